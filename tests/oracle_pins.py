@@ -1,0 +1,359 @@
+"""Pins that tie the fp64 oracle to facts other than itself.
+
+Each ``pin_*`` function takes an oracle handle (``oracle.Oracle``) and raises
+``AssertionError`` when the oracle disagrees with:
+  * a library routine on a special case (torch's scaled_dot_product_attention
+    in float64 with grouped-query heads, numpy/scipy reductions),
+  * brute force at 50 significant digits (mpmath) on tiny inputs,
+  * closed forms (one token, two tokens, zero query, constant values,
+    saturated softmax, empty list),
+  * invariances (slot order, slot relocation, split-and-merge).
+The same pins run against deliberately broken oracle builds to show that each
+plausible mistake is caught (``test_oracle_mutants.py``).
+"""
+from __future__ import annotations
+
+from fractions import Fraction
+
+import mpmath
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+import workloads
+
+TOL = 1e-12
+
+
+def _bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float values to bf16 (nearest-even, via torch) and return the bits."""
+    t = torch.as_tensor(np.asarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return workloads.bits(t)
+
+
+def _widen(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _random_bits(rng, shape, scale=1.0):
+    return _bf16_bits(rng.standard_normal(shape) * scale)
+
+
+def _exact_dot(a_bits, b_bits) -> Fraction:
+    return sum((Fraction(float(x)) * Fraction(float(y))
+                for x, y in zip(_widen(a_bits), _widen(b_bits))), Fraction(0))
+
+
+def _contiguous_case(rng, lengths, Hq, Hkv, D, spare=3):
+    lengths = list(lengths)
+    N = sum(lengths) + spare
+    q = _random_bits(rng, (len(lengths), Hq, D))
+    k = _random_bits(rng, (N, Hkv, D))
+    v = _random_bits(rng, (N, Hkv, D))
+    indptr = np.zeros(len(lengths) + 1, np.int32)
+    indptr[1:] = np.cumsum(lengths)
+    indices = np.arange(sum(lengths), dtype=np.int32) + spare  # slots spare.. (skip the first)
+    return q, k, v, indptr, indices
+
+
+def _scattered_case(rng, lengths, Hq, Hkv, D, N):
+    lengths = list(lengths)
+    q = _random_bits(rng, (len(lengths), Hq, D))
+    k = _random_bits(rng, (N, Hkv, D))
+    v = _random_bits(rng, (N, Hkv, D))
+    indptr = np.zeros(len(lengths) + 1, np.int32)
+    indptr[1:] = np.cumsum(lengths)
+    indices = rng.permutation(N)[: sum(lengths)].astype(np.int32)
+    return q, k, v, indptr, indices
+
+
+# ----------------------------------------------------------------------------
+# decode pins
+# ----------------------------------------------------------------------------
+def pin_sdpa_decode(o):
+    """Contiguous slots: equals torch SDPA (float64, enable_gqa) to 1e-12."""
+    rng = np.random.default_rng(11)
+    for (Hq, Hkv, D, lengths) in [(8, 2, 16, [5, 1, 9]), (4, 4, 8, [3, 7]),
+                                  (8, 1, 32, [6]), (16, 2, 128, [33, 2])]:
+        q, k, v, indptr, indices = _contiguous_case(rng, lengths, Hq, Hkv, D)
+        scale = workloads.softmax_scale(D)
+        out, _ = o.decode(q, k, v, indptr, indices, scale, Hkv)
+        for b in range(len(lengths)):
+            ids = indices[indptr[b]:indptr[b + 1]]
+            qt = torch.from_numpy(_widen(q[b]))[None, :, None, :]            # [1,Hq,1,D]
+            kt = torch.from_numpy(_widen(k[ids])).permute(1, 0, 2)[None]     # [1,Hkv,L,D]
+            vt = torch.from_numpy(_widen(v[ids])).permute(1, 0, 2)[None]
+            ref = F.scaled_dot_product_attention(qt, kt, vt, scale=scale, enable_gqa=True)
+            err = np.abs(out[b] - ref[0, :, 0, :].numpy()).max()
+            assert err < TOL, f"sdpa mismatch {err} (Hq={Hq} Hkv={Hkv} D={D} b={b})"
+
+
+def pin_bruteforce_tiny(o):
+    """Scattered slots, tiny shapes: equals 50-digit brute force (no max shift)."""
+    mpmath.mp.dps = 50
+    rng = np.random.default_rng(12)
+    for (Hq, Hkv, D, lengths, N) in [(4, 2, 4, [1, 3, 5], 16), (2, 1, 6, [4, 2], 9),
+                                     (4, 4, 3, [5], 8)]:
+        q, k, v, indptr, indices = _scattered_case(rng, lengths, Hq, Hkv, D, N)
+        scale = workloads.softmax_scale(D)
+        out, lse = o.decode(q, k, v, indptr, indices, scale, Hkv)
+        g = Hq // Hkv
+        qw, kw, vw = _widen(q), _widen(k), _widen(v)
+        for b in range(len(lengths)):
+            ids = indices[indptr[b]:indptr[b + 1]]
+            for h in range(Hq):
+                kh = h // g
+                e = []
+                for s in ids:
+                    dot = mpmath.fsum(mpmath.mpf(float(qw[b, h, d])) * mpmath.mpf(float(kw[s, kh, d]))
+                                      for d in range(D))
+                    e.append(mpmath.exp(mpmath.mpf(float(np.float32(scale))) * dot))
+                z = mpmath.fsum(e)
+                for d in range(D):
+                    ref = mpmath.fsum(e[j] * mpmath.mpf(float(vw[s, kh, d]))
+                                      for j, s in enumerate(ids)) / z
+                    assert abs(out[b, h, d] - float(ref)) < 1e-14, "brute-force out mismatch"
+                assert abs(lse[b, h] - float(mpmath.log(z))) < 1e-13, "brute-force lse mismatch"
+
+
+def pin_slot_order(o):
+    """Shuffling each list, or moving rows to other slots, changes nothing (1e-12)."""
+    rng = np.random.default_rng(13)
+    N = 200
+    q, k, v, indptr, indices = _scattered_case(rng, [17, 40, 3], 8, 2, 16, N)
+    scale = workloads.softmax_scale(16)
+    base, base_lse = o.decode(q, k, v, indptr, indices, scale, 2)
+    shuffled = indices.copy()
+    for b in range(3):
+        seg = shuffled[indptr[b]:indptr[b + 1]]
+        shuffled[indptr[b]:indptr[b + 1]] = rng.permutation(seg)
+    out, lse = o.decode(q, k, v, indptr, shuffled, scale, 2)
+    assert np.abs(out - base).max() < TOL and np.abs(lse - base_lse).max() < TOL, "slot order"
+    move = rng.permutation(N)                    # row at slot s moves to slot move[s]
+    k2, v2 = np.empty_like(k), np.empty_like(v)
+    k2[move], v2[move] = k, v
+    out, lse = o.decode(q, k2, v2, indptr, move[indices].astype(np.int32), scale, 2)
+    assert np.abs(out - base).max() < TOL and np.abs(lse - base_lse).max() < TOL, "relocation"
+
+
+def pin_single_token(o):
+    """L = 1: out is the value row exactly; lse is the scaled dot product."""
+    rng = np.random.default_rng(14)
+    q, k, v, indptr, indices = _scattered_case(rng, [1, 1, 1], 8, 2, 32, 50)
+    scale = workloads.softmax_scale(32)
+    out, lse = o.decode(q, k, v, indptr, indices, scale, 2)
+    for b in range(3):
+        s = indices[b]
+        for h in range(8):
+            assert np.array_equal(out[b, h], _widen(v[s, h // 4])), "L=1 must return V exactly"
+            ref = float(Fraction(float(np.float32(scale))) * _exact_dot(q[b, h], k[s, h // 4]))
+            assert abs(lse[b, h] - ref) < TOL, "L=1 lse"
+
+
+def pin_two_tokens(o):
+    """L = 2: out = sigmoid(s1-s0) v1 + (1 - sigmoid(s1-s0)) v0, lse = logaddexp(s0, s1)."""
+    rng = np.random.default_rng(15)
+    q, k, v, indptr, indices = _scattered_case(rng, [2, 2], 4, 2, 16, 30)
+    scale = workloads.softmax_scale(16)
+    out, lse = o.decode(q, k, v, indptr, indices, scale, 2)
+    sc = Fraction(float(np.float32(scale)))
+    for b in range(2):
+        s0_slot, s1_slot = indices[indptr[b]], indices[indptr[b] + 1]
+        for h in range(4):
+            kh = h // 2
+            s0 = float(sc * _exact_dot(q[b, h], k[s0_slot, kh]))
+            s1 = float(sc * _exact_dot(q[b, h], k[s1_slot, kh]))
+            w1 = 1.0 / (1.0 + np.exp(-(s1 - s0)))
+            ref = w1 * _widen(v[s1_slot, kh]) + (1.0 - w1) * _widen(v[s0_slot, kh])
+            assert np.abs(out[b, h] - ref).max() < TOL, "two-token closed form"
+            assert abs(lse[b, h] - np.logaddexp(s0, s1)) < TOL, "two-token lse"
+
+
+def pin_zero_query(o):
+    """q = 0 (or scale 0): out is the arithmetic mean of the value rows, lse = ln L."""
+    rng = np.random.default_rng(16)
+    q, k, v, indptr, indices = _scattered_case(rng, [7, 1, 30], 4, 1, 8, 64)
+    zq = np.zeros_like(q)
+    for qq, scale in [(zq, 0.125), (q, 0.0)]:
+        out, lse = o.decode(qq, k, v, indptr, indices, scale, 1)
+        for b in range(3):
+            ids = indices[indptr[b]:indptr[b + 1]]
+            ref = _widen(v[ids, 0]).mean(axis=0)
+            assert np.abs(out[b] - ref[None]).max() < TOL, "zero query: mean of V"
+            assert np.abs(lse[b] - np.log(len(ids))).max() < TOL, "zero query: lse = ln L"
+
+
+def pin_constant_values(o):
+    """All listed value rows equal: out equals that row whatever the weights."""
+    rng = np.random.default_rng(17)
+    q, k, v, indptr, indices = _scattered_case(rng, [9, 4], 8, 2, 16, 40)
+    row = _random_bits(rng, (2, 16))
+    v = v.copy()
+    v[indices] = row
+    out, _ = o.decode(q, k, v, indptr, indices, workloads.softmax_scale(16), 2)
+    for h in range(8):
+        assert np.abs(out[:, h] - _widen(row[h // 4])[None]).max() < TOL, "constant V"
+
+
+def pin_saturated_softmax(o):
+    """One key far above the rest: out is that key's value row; lse its score.
+
+    The top score (2048) exceeds every other by more than the double exponent
+    range, so an exponent taken without the right shift overflows."""
+    rng = np.random.default_rng(18)
+    D = 8
+    q, k, v, indptr, indices = _scattered_case(rng, [6], 2, 1, D, 20)
+    q = _bf16_bits(np.full((1, 2, D), 16.0))
+    k = k.copy()
+    star = indices[3]
+    k[star] = _bf16_bits(np.full((1, D), 16.0))
+    others = indices[indices != star]
+    k[others] = _bf16_bits(np.clip(_widen(k[others]), -4, 4) * 0.5)
+    out, lse = o.decode(q, k, v, indptr, indices, 1.0, 1)
+    for h in range(2):
+        assert np.isfinite(out[0, h]).all(), "saturated softmax must stay finite"
+        assert np.abs(out[0, h] - _widen(v[star, 0])).max() < TOL, "saturated softmax"
+        assert abs(lse[0, h] - 16.0 * 16.0 * D) < 1e-9, "saturated lse"
+
+
+def pin_empty_list(o):
+    """An empty list gives out = 0 and lse = -inf, and leaves its neighbours alone."""
+    rng = np.random.default_rng(19)
+    q, k, v, indptr, indices = _scattered_case(rng, [0, 5, 0], 4, 2, 8, 20)
+    scale = workloads.softmax_scale(8)
+    out, lse = o.decode(q, k, v, indptr, indices, scale, 2)
+    for b in (0, 2):
+        assert np.all(out[b] == 0.0) and np.all(np.isneginf(lse[b])), "empty list"
+    ref, ref_lse = o.decode(q[1:2], k, v, np.array([0, 5], np.int32), indices, scale, 2)
+    assert np.abs(out[1] - ref[0]).max() < TOL and np.abs(lse[1] - ref_lse[0]).max() < TOL
+
+
+def pin_duplicate_slots(o):
+    """A slot listed twice counts twice: equals SDPA over the duplicated rows."""
+    rng = np.random.default_rng(20)
+    D, Hq, Hkv = 16, 4, 2
+    q = _random_bits(rng, (1, Hq, D))
+    k = _random_bits(rng, (10, Hkv, D))
+    v = _random_bits(rng, (10, Hkv, D))
+    ids = np.array([4, 4, 7, 1, 4], np.int32)
+    scale = workloads.softmax_scale(D)
+    out, _ = o.decode(q, k, v, np.array([0, 5], np.int32), ids, scale, Hkv)
+    qt = torch.from_numpy(_widen(q[0]))[None, :, None, :]
+    kt = torch.from_numpy(_widen(k[ids])).permute(1, 0, 2)[None]
+    vt = torch.from_numpy(_widen(v[ids])).permute(1, 0, 2)[None]
+    ref = F.scaled_dot_product_attention(qt, kt, vt, scale=scale, enable_gqa=True)
+    assert np.abs(out[0] - ref[0, :, 0, :].numpy()).max() < TOL, "duplicate slots"
+
+
+def pin_row_selection(o):
+    """Computing a subset of rows gives the same values as computing all rows."""
+    rng = np.random.default_rng(21)
+    q, k, v, indptr, indices = _scattered_case(rng, [5, 9, 2], 8, 2, 16, 40)
+    scale = workloads.softmax_scale(16)
+    full, full_lse = o.decode(q, k, v, indptr, indices, scale, 2)
+    sel = [0, 9, 23, 17]
+    part, part_lse = o.decode(q, k, v, indptr, indices, scale, 2, sel=sel)
+    fo, po = full.reshape(-1, 16), part.reshape(-1, 16)
+    assert np.array_equal(fo[sel], po[sel]), "row selection"
+    assert np.array_equal(full_lse.reshape(-1)[sel], part_lse.reshape(-1)[sel])
+    others = [r for r in range(24) if r not in sel]
+    assert np.isnan(po[others]).all(), "unselected rows untouched"
+
+
+# ----------------------------------------------------------------------------
+# merge pins
+# ----------------------------------------------------------------------------
+def pin_merge_of_splits(o):
+    """Decode over parts of a list, merged, equals decode over the whole list."""
+    rng = np.random.default_rng(22)
+    D, Hq, Hkv = 16, 4, 2
+    q, k, v, indptr, indices = _scattered_case(rng, [23], Hq, Hkv, D, 60)
+    scale = workloads.softmax_scale(D)
+    whole, whole_lse = o.decode(q, k, v, indptr, indices, scale, Hkv)
+    for cuts in ([0, 23], [0, 11, 23], [0, 1, 2, 9, 9, 22, 23], list(range(24))):
+        n = len(cuts) - 1
+        parts = [o.decode(q, k, v, np.array([0, cuts[i + 1] - cuts[i]], np.int32),
+                          indices[cuts[i]:cuts[i + 1]], scale, Hkv) for i in range(n)]
+        for h in range(Hq):
+            op = np.stack([p[0][0, h] for p in parts])
+            lp = np.array([p[1][0, h] for p in parts])
+            mo, ml = o.merge(op, lp)
+            assert np.abs(mo - whole[0, h]).max() < TOL, f"merge out ({n} parts)"
+            assert abs(ml - whole_lse[0, h]) < TOL, f"merge lse ({n} parts)"
+
+
+def pin_merge_special_cases(o):
+    """One part returns itself; equal lse averages; all-empty gives 0 / -inf."""
+    rng = np.random.default_rng(23)
+    a = rng.standard_normal((1, 8))
+    mo, ml = o.merge(a, np.array([0.7]))
+    assert np.abs(mo - a[0]).max() < TOL and abs(ml - 0.7) < TOL, "single part"
+    b = rng.standard_normal((2, 8))
+    mo, ml = o.merge(b, np.array([1.5, 1.5]))
+    assert np.abs(mo - b.mean(axis=0)).max() < TOL and abs(ml - (1.5 + np.log(2))) < TOL
+    mo, ml = o.merge(b, np.array([-np.inf, 2.0]))
+    assert np.abs(mo - b[1]).max() < TOL and abs(ml - 2.0) < TOL, "empty part ignored"
+    mo, ml = o.merge(b, np.array([-np.inf, -np.inf]))
+    assert np.all(mo == 0) and np.isneginf(ml), "all parts empty"
+
+
+# ----------------------------------------------------------------------------
+# prefill pins
+# ----------------------------------------------------------------------------
+def _prefill_case(rng, cached, chunks, Hq, Hkv, D, N):
+    lengths = [p + c for p, c in zip(cached, chunks)]
+    _, k, v, indptr, indices = _scattered_case(rng, lengths, Hq, Hkv, D, N)
+    qo = np.zeros(len(chunks) + 1, np.int32)
+    qo[1:] = np.cumsum(chunks)
+    q = _random_bits(rng, (int(qo[-1]), Hq, D))
+    return q, k, v, qo, indptr, indices
+
+
+def pin_prefill_sdpa(o):
+    """Contiguous slots: equals SDPA with an explicit bottom-right causal mask."""
+    rng = np.random.default_rng(24)
+    for (Hq, Hkv, D, cached, chunks) in [(8, 2, 16, [5, 0, 3], [4, 3, 1]), (4, 1, 32, [9], [6])]:
+        lengths = [p + c for p, c in zip(cached, chunks)]
+        _, k, v, indptr, indices = _contiguous_case(rng, lengths, Hq, Hkv, D)
+        qo = np.zeros(len(chunks) + 1, np.int32)
+        qo[1:] = np.cumsum(chunks)
+        q = _random_bits(rng, (int(qo[-1]), Hq, D))
+        scale = workloads.softmax_scale(D)
+        out, _ = o.prefill(q, k, v, qo, indptr, indices, scale, Hkv)
+        for b, (P, C) in enumerate(zip(cached, chunks)):
+            ids = indices[indptr[b]:indptr[b + 1]]
+            L = P + C
+            qt = torch.from_numpy(_widen(q[qo[b]:qo[b + 1]])).permute(1, 0, 2)[None]  # [1,Hq,C,D]
+            kt = torch.from_numpy(_widen(k[ids])).permute(1, 0, 2)[None]
+            vt = torch.from_numpy(_widen(v[ids])).permute(1, 0, 2)[None]
+            mask = torch.ones(C, L, dtype=torch.bool).tril(diagonal=P)
+            ref = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=scale,
+                                                 enable_gqa=True)
+            err = np.abs(out[qo[b]:qo[b + 1]] - ref[0].permute(1, 0, 2).numpy()).max()
+            assert err < TOL, f"prefill sdpa mismatch {err}"
+
+
+def pin_prefill_rows_are_decodes(o):
+    """Chunk row i equals decode over the list's first P+i+1 entries; C = 1 is decode."""
+    rng = np.random.default_rng(25)
+    Hq, Hkv, D = 8, 2, 16
+    q, k, v, qo, indptr, indices = _prefill_case(rng, [6, 0, 11], [5, 2, 1], Hq, Hkv, D, 64)
+    scale = workloads.softmax_scale(D)
+    out, lse = o.prefill(q, k, v, qo, indptr, indices, scale, Hkv)
+    for b in range(3):
+        L = indptr[b + 1] - indptr[b]
+        C = qo[b + 1] - qo[b]
+        for i in range(C):
+            n = L - C + i + 1
+            ref, ref_lse = o.decode(q[qo[b] + i][None], k, v, np.array([0, n], np.int32),
+                                    indices[indptr[b]:indptr[b] + n], scale, Hkv)
+            assert np.abs(out[qo[b] + i] - ref[0]).max() < TOL, "prefill row vs decode"
+            assert np.abs(lse[qo[b] + i] - ref_lse[0]).max() < TOL
+
+
+ALL_PINS = [
+    pin_sdpa_decode, pin_bruteforce_tiny, pin_slot_order, pin_single_token, pin_two_tokens,
+    pin_zero_query, pin_constant_values, pin_saturated_softmax, pin_empty_list,
+    pin_duplicate_slots, pin_row_selection, pin_merge_of_splits, pin_merge_special_cases,
+    pin_prefill_sdpa, pin_prefill_rows_are_decodes,
+]

@@ -1,0 +1,85 @@
+"""Planted mistakes in the oracle are caught by its pins.
+
+Each mutant is a copy of ``oracle/pa_oracle.c`` with one plausible mistake
+(a dropped term, a flipped sign, a wrong index, a transposed operand, an
+off-by-one in the causal window...), compiled on the CPU into a temporary
+library.  The pins must reject every mutant; a surviving mutant means the pins
+leave that part of the oracle unchecked.
+"""
+import os
+
+import pytest
+
+import oracle
+from oracle_pins import ALL_PINS
+
+# (name, [(original text, replacement, occurrence index or None for "the only one")])
+MUTANTS = [
+    ("gqa_modulo_decode", [("int32_t kh = h / group;", "int32_t kh = h % Hkv;", 0)]),
+    ("gqa_modulo_prefill", [("int32_t kh = h / group;", "int32_t kh = h % Hkv;", 1)]),
+    ("scale_dropped", [("s[j] = scale * dot;", "s[j] = dot;", None)]),
+    ("exp_sign_flipped", [("s[j] = exp(s[j] - m);", "s[j] = exp(m - s[j]);", None)]),
+    ("first_weight_dropped_from_z", [("z += s[j];", "if (j) z += s[j];", None)]),
+    ("shift_by_min", [("if (s[j] > m)", "if (s[j] < m)", None)]),
+    ("k_read_from_v_pool", [("const uint16_t *k_row = k_pool", "const uint16_t *k_row = v_pool", None)]),
+    ("values_paired_reversed", [("const uint16_t *v_row = v_pool + (int64_t)slots[j]",
+                                 "const uint16_t *v_row = v_pool + (int64_t)slots[n - 1 - j]", None)]),
+    ("k_head_and_dim_transposed", [
+        ("const uint16_t *k_row = k_pool + (int64_t)slots[j] * slot_stride + (int64_t)kh * D;",
+         "const uint16_t *k_row = k_pool + (int64_t)slots[j] * slot_stride + (int64_t)kh;", None),
+        ("widen_bf16(k_row[d])", "widen_bf16(k_row[(int64_t)d * (slot_stride / D)])", None)]),
+    ("normalised_by_count", [("out[d] /= z;", "out[d] /= (double)n;", None)]),
+    ("lse_without_max", [("*lse = m + log(z);", "*lse = log(z);", None)]),
+    ("lse_without_log", [("*lse = m + log(z);", "*lse = m + z;", None)]),
+    ("empty_lse_zero", [("*lse = -INFINITY;\n        return;", "*lse = 0.0;\n        return;", None)]),
+    ("empty_out_garbage", [("out[d] = 0.0;\n        *lse = -INFINITY;", "out[d] = 1.0;\n        *lse = -INFINITY;", None)]),
+    ("query_head_zero_decode", [("attend_one_row(D, q + row * D,", "attend_one_row(D, q + (row / Hq) * Hq * D,", 0)]),
+    ("query_head_zero_prefill", [("attend_one_row(D, q + row * D,", "attend_one_row(D, q + (row / Hq) * Hq * D,", 1)]),
+    ("decode_list_one_short", [("(int64_t)kv_indptr[b + 1] - kv_indptr[b],\n                           (double)sm_scale",
+                                "(int64_t)kv_indptr[b + 1] - kv_indptr[b] - 1,\n                           (double)sm_scale", None)]),
+    ("causal_window_one_short", [("prefix + i + 1,", "prefix + i,", None)]),
+    ("causal_top_left", [("int64_t prefix = L - chunk;", "int64_t prefix = 0;", None)]),
+    ("causal_ignored", [("prefix + i + 1,", "L,", None)]),
+    ("prefill_row_in_chunk_wrong", [("int64_t i = t - qo_indptr[b];", "int64_t i = t - qo_indptr[b] - (b > 0);", None)]),
+    ("merge_weight_sign", [("double w = exp(lse_parts[i] - M);", "double w = exp(M - lse_parts[i]);", None)]),
+    ("merge_lse_without_log", [("*lse = M + log(wsum);", "*lse = M;", None)]),
+    ("merge_first_part_dropped", [("for (int32_t i = 0; i < n; i++) {\n        double w",
+                                   "for (int32_t i = 1; i < n; i++) {\n        double w", None)]),
+    ("merge_unnormalised", [("out[d] /= wsum;", "out[d] /= (double)n;", None)]),
+]
+
+
+def _mutate(src: str, edits):
+    for old, new, occurrence in edits:
+        count = src.count(old)
+        if occurrence is None:
+            assert count == 1, f"mutation anchor must be unique: {old!r} ({count})"
+            src = src.replace(old, new)
+        else:
+            assert count > occurrence, f"mutation anchor occurrence missing: {old!r}"
+            pos = -1
+            for _ in range(occurrence + 1):
+                pos = src.index(old, pos + 1)
+            src = src[:pos] + new + src[pos + len(old):]
+    return src
+
+
+@pytest.mark.parametrize("name,edits", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, name, edits):
+    with open(oracle.SOURCE) as f:
+        src = f.read()
+    mutated = _mutate(src, edits)
+    assert mutated != src
+    c_path = os.path.join(tmp_path, f"{name}.c")
+    so_path = os.path.join(tmp_path, f"lib{name}.so")
+    with open(c_path, "w") as f:
+        f.write(mutated)
+    oracle.build(c_path, so_path)
+    mutant = oracle.Oracle(so_path)
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin(mutant)
+        except (AssertionError, oracle.OracleError) as e:
+            caught.append(f"{pin.__name__}: {str(e)[:60]}")
+    assert caught, f"mutant {name} survived every pin"
