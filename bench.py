@@ -1,0 +1,271 @@
+#!/usr/bin/env python3
+"""Benchmark of the decode hot path on one MI355X.
+
+Workload: batch-64 paged GQA decode (32 query heads over 8 KV heads, head_dim
+128), slot-list lengths uniform in [2048, 8192], 16 groups of 4 requests
+sharing a 1024-slot prefix, scattered slots in a 600k-slot bf16 pool, and 36
+layers per step with one pa_plan reused by all of them; every layer has its
+own pools, so caches cannot serve one layer's K/V to the next.  Inputs are
+seeded synthetic data (workloads.py), resident in HBM before timing starts.
+
+A step = pa_plan (host partition + one async upload) + 36 x pa_decode_run.
+The JSON line reports:
+  value            algorithmic HBM bytes of the step / step time (GB/s)
+  us_per_step_layer  step time / 36
+  roofline         the decode kernel alone: algorithmic bytes per launch /
+                   its average duration from HIP events recorded around each
+                   launch on the launch stream, against 8 TB/s; `traffic` comes
+                   from committed rocprofv3 counters when they were taken on
+                   the current kernel source, else null
+  cpu_baseline     the fp64 oracle on the host cores, on layer 0 of the same
+                   workload (all rows), repeated for about --cpu-seconds
+Algorithmic bytes per layer = unique slots x Hkv x D x 2 (K) x 2 (V) + list
+entries x 4 (slot ids) + B x Hq x D x 2 (q) + B x Hq x D x 4 (out) + (B+1) x 4.
+
+`--workload copy --copy-gib N` runs a plain device copy of N GiB instead (for
+calibrating the HBM counters).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-attn µs/step/layer + achieved HBM GB/s (% of MI355X peak), batch 64"
+HBM_PEAK_GBS = 8000.0
+COUNTERS = os.path.join(ROOT, "profiles", "decode_b64_counters.json")
+KERNEL_SOURCE = os.path.join(ROOT, "paged_gqa_decode_pa_amd", "csrc", "decode.hip")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(spec, kv_indptr, kv_indices) -> int:
+    import numpy as np
+    B, Hq, Hkv, D = spec.batch, spec.num_qo_heads, spec.num_kv_heads, spec.head_dim
+    unique = int(np.unique(kv_indices).size)
+    return (unique * Hkv * D * 2 * 2 + int(kv_indptr[-1]) * 4 + B * Hq * D * 2 + B * Hq * D * 4
+            + (B + 1) * 4)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in ("decode.hip", "pa_internal.h"):
+        with open(os.path.join(os.path.dirname(KERNEL_SOURCE), name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_per_launch():
+    """HBM bytes per decode launch from committed counters, if they match the kernel."""
+    if not os.path.exists(COUNTERS):
+        return None
+    with open(COUNTERS) as f:
+        c = json.load(f)
+    if c.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return int((c["fetch_kib_per_dispatch"] * c["fetch_scale"] +
+                c["write_kib_per_dispatch"] * c["write_scale"]) * 1024)
+
+
+def run_copy(gib: float, steps: int):
+    import torch
+    n = int(gib * (1 << 30)) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    log(f"copy {gib} GiB: {dt * 1e3:.3f} ms, {2 * n * 4 / dt / 1e9:.1f} GB/s (read+write)")
+
+
+def cpu_baseline(case, spec, bytes_per_layer, seconds, gpu_out_layer0):
+    import numpy as np
+
+    import oracle
+    import workloads as W
+    ref = oracle.load()
+    qb = W.bits(case.q)
+    kb = W.bits(case.k_pools[0])
+    vb = W.bits(case.v_pools[0])
+    reps = 0
+    t0 = time.perf_counter()
+    out = None
+    while True:
+        out, _ = ref.decode(qb, kb, vb, case.kv_indptr, case.kv_indices, case.sm_scale,
+                            spec.num_kv_heads)
+        reps += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    err = float(np.abs(gpu_out_layer0 - out).max())
+    return {
+        "value": round(bytes_per_layer * reps / dt / 1e9, 3),
+        "unit": "GB/s",
+        "cores": ref.num_threads(),
+        "kind": "oracle",
+        "us_per_layer": round(dt / reps * 1e6, 1),
+        "sample": f"layer 0 of the same workload, all {spec.batch}x{spec.num_qo_heads} rows, "
+                  f"{reps} repetition(s), {dt:.1f} s",
+    }, err
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--layers", type=int, default=None, help="layers per step (default: 36)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--flags", type=int, default=0, help="pa_plan flags")
+    ap.add_argument("--workload", default="batch64", choices=["batch64", "copy"])
+    ap.add_argument("--copy-gib", type=float, default=4.0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the decode path is built and measured on a single "
+              "MI355X (its multi-GPU sharding is a design note, not a measured configuration). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    if args.workload == "copy":
+        run_copy(args.copy_gib, args.steps)
+        return
+
+    import paged_gqa_decode_pa_amd as pa
+    import workloads as W
+
+    spec = W.BATCH64_SHARED_PREFIX
+    layers = args.layers or spec.num_layers
+    dev = torch.device("cuda", 0)
+    log(f"generating {spec.name}: {layers} layers of {spec.num_slots}-slot pools")
+    t0 = time.perf_counter()
+    case = W.make_decode_case(spec, dev, layers=layers)
+    torch.cuda.synchronize()
+    log(f"inputs ready in {time.perf_counter() - t0:.1f} s "
+        f"({torch.cuda.memory_allocated() / 2**30:.1f} GiB on device)")
+    idx = torch.as_tensor(case.kv_indices, device=dev)
+    B, Hq, Hkv, D = spec.batch, spec.num_qo_heads, spec.num_kv_heads, spec.head_dim
+    bytes_per_layer = algorithmic_bytes(spec, case.kv_indptr, case.kv_indices)
+    outs = [torch.empty((B, Hq, D), dtype=torch.float32, device=dev) for _ in range(layers)]
+    plan = pa.Plan(B, int(case.kv_indptr[-1]), Hq, Hkv, D)
+    stream = torch.cuda.current_stream(dev)
+    plan_host_s = []
+
+    def step():
+        t = time.perf_counter()
+        plan.plan(case.kv_indptr, flags=args.flags, stream=stream)
+        plan_host_s.append(time.perf_counter() - t)
+        for layer in range(layers):
+            plan.decode(case.q, case.k_pools[layer], case.v_pools[layer], idx, case.sm_scale,
+                        outs[layer], stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("warmup done")
+
+    # timed region: K steps, HIP events on the launch stream around every
+    # decode kernel (recorded by the library) and around the whole region
+    pa.pa_profile_begin(plan.handle, args.steps * layers)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    plan_host_s.clear()
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(end) / args.steps
+    kernel_ms, launches = pa.pa_profile_end(plan.handle)
+    kernel_avg_ms = kernel_ms / max(1, launches)
+    log(f"step {ms_per_step:.3f} ms, decode kernel avg {kernel_avg_ms * 1e3:.1f} us over {launches} launches")
+
+    # the same region again without kernel events, to show their cost
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step_plain = start.elapsed_time(end) / args.steps
+    log(f"step without kernel events {ms_per_step_plain:.3f} ms")
+
+    step_bytes = bytes_per_layer * layers
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = bytes_per_layer / (kernel_avg_ms * 1e-3) / 1e9
+    traffic = traffic_per_launch()
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": spec.name,
+            "batch": B, "num_qo_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
+            "layers_per_step": layers,
+            "kv_len": f"uniform [{spec.len_lo}, {spec.len_hi}]",
+            "shared_prefix": f"{spec.batch // spec.prefix_group_size} groups x "
+                             f"{spec.prefix_group_size} requests x {spec.prefix_len} slots",
+            "list_entries": int(case.kv_indptr[-1]),
+            "unique_slots": int(np.unique(case.kv_indices).size),
+            "pool_slots": spec.num_slots,
+            "plan_flags": args.flags,
+        },
+        "us_per_step_layer": round(ms_per_step * 1e3 / layers, 2),
+        "frac_of_peak": round(value / HBM_PEAK_GBS, 4),
+        "ms_per_step_without_kernel_events": round(ms_per_step_plain, 4),
+        "plan_host_us": round(1e6 * float(np.median(plan_host_s)), 1),
+        "algorithmic_bytes_per_layer": bytes_per_layer,
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": "decode_kernel<128,4> (pa_decode_run)",
+            "kernel_avg_us": round(kernel_avg_ms * 1e3, 2),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: fp64 oracle on layer 0 for ~{args.cpu_seconds:.0f} s")
+        torch.cuda.synchronize()
+        cpu, err = cpu_baseline(case, spec, bytes_per_layer, args.cpu_seconds, outs[0].cpu().numpy())
+        result["cpu_baseline"] = cpu
+        result["parity_layer0_max_abs_err"] = err
+        log(f"cpu baseline {cpu['value']} GB/s on {cpu['cores']} threads; layer-0 max|d| {err:.3g}")
+    plan.close()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

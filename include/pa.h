@@ -1,0 +1,238 @@
+/*
+ * pa.h -- C ABI of libpa: batched grouped-query decode attention over a
+ * token-granular paged KV pool on AMD Instinct MI355X (gfx950), with a
+ * chunked-prefill variant over the same pool.
+ *
+ * Sources.  The pool follows the Agent-Infer page ("Agent-Infer: 纯 Rust 编写的
+ * 高性能 LLM 推理引擎"), section "分页 KV 缓存": one pool slot per token (page
+ * size 1), shared by every request so that decode batches across requests,
+ * with a plan computed once per decode step and reused by every layer, over
+ * buffers allocated up front (same section, and stages 2-3 of the table in
+ * "优化历程").  The head geometry follows the Pegainfer page ("Pegainfer:
+ * 纯Rust+CUDA构建的LLM推理引擎"), section "关键技术实现", items 1-2 (GQA with
+ * 32 query heads over 8 KV heads and head_dim 128; head_dim 256 for Qwen3.5's
+ * full-attention layers).  Chunked prefill follows the Agent-Infer page,
+ * section "连续批处理" (chunks of 512 tokens, 64 while decodes run).  The pages
+ * call the kernels through a plain C FFI (Pegainfer page, "核心组件概览",
+ * ffi.rs); this header is that kind of boundary.
+ *
+ * What is computed (the pages name the operation but do not write it out;
+ * this is the textbook reading):
+ *   g = Hq / Hkv; query head h reads KV head h / g.
+ *   For request b, S = kv_indices[kv_indptr[b] .. kv_indptr[b+1]) in list order.
+ *   s_j = sm_scale * <q[b,h,:], K[S_j, h/g, :]>
+ *   out[b,h,:] = sum_j exp(s_j - m) V[S_j, h/g, :] / sum_j exp(s_j - m),  m = max_j s_j
+ *   lse[b,h]   = m + ln(sum_j exp(s_j - m))
+ *   An empty list gives out = 0 and lse = -inf.  A slot listed twice counts
+ *   twice.  Lists of different requests may share slots.
+ *   Prefill: request b brings C_b = qo_indptr[b+1]-qo_indptr[b] query rows,
+ *   which are the last C_b entries of its slot list (L_b >= C_b); chunk row i
+ *   attends to list positions 0 .. (L_b - C_b) + i (causal inside the chunk).
+ *
+ * Data layout (all device pointers unless said otherwise):
+ *   q        bf16, [B, Hq, D] for decode, [T, Hq, D] for prefill, contiguous,
+ *            16-byte aligned.
+ *   k_pool,  bf16; the row of slot s and KV head kh starts at element
+ *   v_pool   s * slot_stride + kh * D and holds D contiguous values.
+ *            slot_stride (elements) is >= Hkv*D and a multiple of 8, so a
+ *            [slots, Hkv, D] pool has slot_stride = Hkv*D (pass 0 for that),
+ *            and a fused [slots, 2, Hkv, D] buffer passes 2*Hkv*D with
+ *            v_pool = k_pool + Hkv*D.  Both pools 16-byte aligned.  Pools may
+ *            exceed 4 GiB; offsets are computed in 64 bits when they do.
+ *   kv_indices int32 slot ids, 0 <= id < num_slots; read on the device.
+ *   kv_indptr / qo_indptr int32 CSR offsets, read on the HOST by pa_plan.
+ *   out      fp32, [B, Hq, D] (decode) or [T, Hq, D] (prefill), contiguous.
+ *   lse      fp32, [B, Hq] or [T, Hq], natural log; may be NULL.
+ *
+ * Precision: bf16 inputs, fp32 arithmetic (the prefill variant multiplies
+ * bf16 tiles on the matrix cores with fp32 accumulation), fp32 outputs.
+ *
+ * Streams: every entry point that touches the GPU takes a hipStream_t passed
+ * as pa_stream_t (NULL = the null stream) and is asynchronous on it.  The run
+ * entry points never allocate and never synchronise, so they can be captured
+ * into a HIP graph.  Runs must be ordered after the pa_plan call whose
+ * result they read (same stream, or an event); kv_indices must not change
+ * between that pa_plan and the last run of the step.
+ *
+ * Errors: every call returns a pa_status; no exception crosses the ABI.
+ * Argument errors are detected on the host before any GPU work is enqueued,
+ * and then nothing is enqueued.  A HIP failure returns PA_ERR_HIP; faults of
+ * kernels already enqueued surface from a later call or at the caller's
+ * synchronisation.  pa_last_error_detail() describes the last failure of the
+ * calling thread.  Slot ids outside [0, num_slots) are not checked on the
+ * device: they are the caller's error and their result is undefined.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct pa_plan pa_plan_t;
+typedef void *pa_stream_t; /* a hipStream_t */
+
+typedef enum pa_status {
+    PA_OK = 0,
+    PA_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, bad CSR offsets, bad sizes */
+    PA_ERR_UNSUPPORTED = 2,   /* head_dim not in {128, 256}, Hq/Hkv not in {1, 2, 4, 8} */
+    PA_ERR_CAPACITY = 3,      /* more requests / tokens than the plan was created for */
+    PA_ERR_PLAN_MISMATCH = 4, /* a run that does not match the last pa_plan (mode, heads) */
+    PA_ERR_HIP = 5            /* a HIP runtime call failed */
+} pa_status;
+
+/* pa_plan flags */
+#define PA_PLAN_FORCE_SPLITS_SHIFT 8
+#define PA_PLAN_FORCE_SPLITS_MASK (0xffffu << PA_PLAN_FORCE_SPLITS_SHIFT)
+/* Cut every request's KV list (per KV head) into exactly n parts (1 <= n <=
+ * PA_MAX_FORCED_SPLITS), instead of the automatic split.  Parts may be empty.
+ * Used to test that the result does not depend on the partition. */
+#define PA_PLAN_FORCE_SPLITS(n) (((uint32_t)(n) & 0xffffu) << PA_PLAN_FORCE_SPLITS_SHIFT)
+#define PA_MAX_FORCED_SPLITS 256
+/* Keep the automatic split but do not reorder work for per-XCD cache locality. */
+#define PA_PLAN_NO_XCD_ORDER 0x1u
+
+/*
+ * pa_plan_create: allocate a plan object for up to max_batch requests whose
+ * slot lists hold at most max_kv_total entries in total, and (prefill) at most
+ * max_q_total query rows.  All device and pinned-host memory the plan and its
+ * runs need is allocated here, on the current HIP device, once.
+ *   num_qo_heads % num_kv_heads == 0, group Hq/Hkv in {1, 2, 4, 8};
+ *   head_dim in {128, 256}.
+ * Returns PA_ERR_INVALID_ARG / PA_ERR_UNSUPPORTED for bad sizes, PA_ERR_HIP if
+ * an allocation fails.  *out is set only on success.
+ */
+pa_status pa_plan_create(pa_plan_t **out, int32_t max_batch, int64_t max_kv_total,
+                         int32_t max_q_total, int32_t num_qo_heads,
+                         int32_t num_kv_heads, int32_t head_dim);
+
+/*
+ * pa_plan: partition one step's work; called once per decode (or prefill)
+ * step and reused by every layer's run.
+ *   kv_indptr_host [batch+1], host memory, non-decreasing, kv_indptr[0] = 0,
+ *     kv_indptr[batch] <= max_kv_total.
+ *   qo_indptr_host NULL for a decode plan; for a prefill plan, [batch+1] host
+ *     offsets of each request's chunk rows, non-decreasing, starting at 0, with
+ *     qo_indptr[b+1]-qo_indptr[b] <= kv_indptr[b+1]-kv_indptr[b] and total rows
+ *     <= max_q_total.
+ *   flags: PA_PLAN_* bits.
+ * The partition is computed on the host and uploaded with one asynchronous
+ * copy on `stream` from pinned staging memory owned by the plan (two staging
+ * buffers alternate; a call waits only if the copy of the call before the
+ * previous one has not finished).  The host arrays may be reused as soon as
+ * this returns.
+ */
+pa_status pa_plan(pa_plan_t *plan, const int32_t *kv_indptr_host,
+                  const int32_t *qo_indptr_host, int32_t batch, uint32_t flags,
+                  pa_stream_t stream);
+
+/*
+ * pa_decode_run: decode attention of one layer under a decode plan.
+ *   q [batch, Hq, D] bf16; k_pool / v_pool as above with num_slots slots;
+ *   kv_indices int32 device array with kv_indptr[batch] entries;
+ *   sm_scale: softmax scale (e.g. 1/sqrt(D) as a float);
+ *   out [batch, Hq, D] fp32; lse [batch, Hq] fp32 or NULL.
+ * Requests whose lists were split write partial results into the plan's
+ * workspace and a merge kernel combines them; so two runs of one plan must
+ * not execute concurrently (runs on one stream are fine).
+ */
+pa_status pa_decode_run(const pa_plan_t *plan, const void *q, const void *k_pool,
+                        const void *v_pool, int64_t num_slots, int64_t slot_stride,
+                        const int32_t *kv_indices, float sm_scale, float *out,
+                        float *lse, pa_stream_t stream);
+
+/*
+ * pa_prefill_chunk_run: chunked-prefill attention of one layer under a
+ * prefill plan (pa_plan with qo_indptr_host != NULL).
+ *   q [T, Hq, D] bf16 with T = qo_indptr[batch]; pools and kv_indices as in
+ *   decode (each request's chunk tokens are the last entries of its list,
+ *   already written into the pool); out [T, Hq, D] fp32; lse [T, Hq] or NULL.
+ */
+pa_status pa_prefill_chunk_run(const pa_plan_t *plan, const void *q, const void *k_pool,
+                               const void *v_pool, int64_t num_slots, int64_t slot_stride,
+                               const int32_t *kv_indices, float sm_scale, float *out,
+                               float *lse, pa_stream_t stream);
+
+/* Release everything pa_plan_create allocated.  Waits for the plan's pending
+ * uploads; the caller must not destroy a plan that enqueued runs still use. */
+void pa_plan_destroy(pa_plan_t *plan);
+
+/* Static description of a status code. */
+const char *pa_strerror(pa_status status);
+
+/* Description of the calling thread's last failure ("" if none). */
+const char *pa_last_error_detail(void);
+
+/*
+ * Host-only inspection of the partition (no GPU needed).
+ *
+ * pa_work_unit is one workgroup's share of a plan, as the kernels read it:
+ * KV head kv_head of request `request`, list entries [kv_begin, kv_end)
+ * (absolute offsets into kv_indices), query rows [q_begin, q_end) (prefill;
+ * decode: q_begin = request, q_end = request + 1), and where the result goes:
+ * partial < 0 writes the final output, partial >= 0 writes partial slot
+ * `partial`, later merged.  Units with request < 0 are padding and do nothing.
+ * diag (prefill): query row q_begin + r sees list entries up to offset
+ * diag + r inclusive (the causal window); decode units set diag = kv_end - 1.
+ *
+ * pa_merge_unit: the partial slots [first_partial, first_partial + n_parts)
+ * that make up query rows [q_begin, q_end) of KV head kv_head.
+ */
+typedef struct pa_work_unit {
+    int32_t request;
+    int32_t kv_head;
+    int32_t kv_begin;
+    int32_t kv_end;
+    int32_t q_begin;
+    int32_t q_end;
+    int32_t partial;
+    int32_t diag;
+} pa_work_unit;
+
+typedef struct pa_merge_unit {
+    int32_t request;
+    int32_t kv_head;
+    int32_t q_begin;
+    int32_t q_end;
+    int32_t first_partial;
+    int32_t n_parts;
+    int32_t reserved0;
+    int32_t reserved1;
+} pa_merge_unit;
+
+/*
+ * pa_partition: compute the partition pa_plan would upload, into host arrays.
+ *   Arguments as in pa_plan_create / pa_plan.  units[unit_capacity] and
+ *   merges[merge_capacity] receive the work and merge lists; *n_units,
+ *   *n_merges and *n_partials receive their lengths.  PA_ERR_CAPACITY if an
+ *   array is too small (the counts are still written).
+ */
+pa_status pa_partition(const int32_t *kv_indptr_host, const int32_t *qo_indptr_host,
+                       int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,
+                       int32_t head_dim, uint32_t flags, pa_work_unit *units,
+                       int32_t unit_capacity, pa_merge_unit *merges,
+                       int32_t merge_capacity, int32_t *n_units, int32_t *n_merges,
+                       int32_t *n_partials);
+
+/*
+ * Kernel timing (instrumentation for benchmarks).  pa_profile_begin creates
+ * `capacity` pairs of HIP events (it allocates; call it outside timed or
+ * captured regions) and makes the following runs of this plan record one
+ * pair around their attention kernel, on the run's stream, until the pairs are
+ * used up.  pa_profile_end waits for the recorded events, returns the summed
+ * kernel time in milliseconds and the number of timed launches, and stops
+ * recording.  Merge kernels are not included.  Not for concurrent use.
+ */
+pa_status pa_profile_begin(pa_plan_t *plan, int32_t capacity);
+pa_status pa_profile_end(pa_plan_t *plan, double *total_ms, int32_t *n_launches);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t pa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -1,0 +1,278 @@
+"""Python binding of libpa: paged grouped-query decode attention on MI355X.
+
+Argument marshalling only.  Every step of the computation runs in the HIP
+kernels of ``libpa.so`` behind the C ABI declared in ``include/pa.h``; the
+functions here carry the same names as the C entry points and pass tensors as
+device pointers.  PyTorch provides device memory and streams.
+
+Importing this package loads ``libpa.so`` (built in-tree by
+``paged_gqa_decode_pa_amd.build.build()``) and fails loudly if it is missing.
+torch is imported first so that the library binds to the HIP runtime torch
+already loaded.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+import torch
+
+LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
+
+PA_OK = 0
+PA_ERR_INVALID_ARG = 1
+PA_ERR_UNSUPPORTED = 2
+PA_ERR_CAPACITY = 3
+PA_ERR_PLAN_MISMATCH = 4
+PA_ERR_HIP = 5
+
+PA_PLAN_FORCE_SPLITS_SHIFT = 8
+PA_MAX_FORCED_SPLITS = 256
+PA_PLAN_NO_XCD_ORDER = 0x1
+
+
+def PA_PLAN_FORCE_SPLITS(n: int) -> int:
+    return (int(n) & 0xFFFF) << PA_PLAN_FORCE_SPLITS_SHIFT
+
+
+class pa_work_unit(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("request", "kv_head", "kv_begin", "kv_end", "q_begin", "q_end", "partial", "diag")]
+
+
+class pa_merge_unit(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("request", "kv_head", "q_begin", "q_end", "first_partial", "n_parts",
+                 "reserved0", "reserved1")]
+
+
+WORK_UNIT_DTYPE = np.dtype([(n, np.int32) for n, _ in pa_work_unit._fields_])
+MERGE_UNIT_DTYPE = np.dtype([(n, np.int32) for n, _ in pa_merge_unit._fields_])
+
+
+class PAError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        self.status = status
+        self.detail = detail
+        super().__init__(f"{where}: {pa_strerror(status)} ({detail})")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIBRARY):
+        raise ImportError(f"{LIBRARY} is missing: build it with "
+                          "`python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(LIBRARY)
+    i32, i64, u32, vp, f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_float
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    lib.pa_plan_create.argtypes = [ctypes.POINTER(vp), i32, i64, i32, i32, i32, i32]
+    lib.pa_plan_create.restype = ctypes.c_int
+    lib.pa_plan.argtypes = [vp, i32p, i32p, i32, u32, vp]
+    lib.pa_plan.restype = ctypes.c_int
+    run = [vp, vp, vp, vp, i64, i64, vp, f32, vp, vp, vp]
+    lib.pa_decode_run.argtypes = run
+    lib.pa_decode_run.restype = ctypes.c_int
+    lib.pa_prefill_chunk_run.argtypes = run
+    lib.pa_prefill_chunk_run.restype = ctypes.c_int
+    lib.pa_plan_destroy.argtypes = [vp]
+    lib.pa_plan_destroy.restype = None
+    lib.pa_strerror.argtypes = [ctypes.c_int]
+    lib.pa_strerror.restype = ctypes.c_char_p
+    lib.pa_last_error_detail.argtypes = []
+    lib.pa_last_error_detail.restype = ctypes.c_char_p
+    lib.pa_version.argtypes = []
+    lib.pa_version.restype = i32
+    lib.pa_partition.argtypes = [i32p, i32p, i32, i32, i32, i32, u32,
+                                 ctypes.POINTER(pa_work_unit), i32,
+                                 ctypes.POINTER(pa_merge_unit), i32, i32p, i32p, i32p]
+    lib.pa_partition.restype = ctypes.c_int
+    lib.pa_profile_begin.argtypes = [vp, i32]
+    lib.pa_profile_begin.restype = ctypes.c_int
+    lib.pa_profile_end.argtypes = [vp, ctypes.POINTER(ctypes.c_double), i32p]
+    lib.pa_profile_end.restype = ctypes.c_int
+    return lib
+
+
+_lib = _load()
+
+
+def pa_strerror(status: int) -> str:
+    return _lib.pa_strerror(int(status)).decode()
+
+
+def pa_last_error_detail() -> str:
+    return _lib.pa_last_error_detail().decode()
+
+
+def pa_version() -> int:
+    return int(_lib.pa_version())
+
+
+def _check(status: int, where: str):
+    if status != PA_OK:
+        raise PAError(status, where, pa_last_error_detail())
+
+
+def _host_i32(a) -> Optional[np.ndarray]:
+    if a is None:
+        return None
+    if isinstance(a, torch.Tensor):
+        a = a.detach().cpu().numpy()
+    return np.ascontiguousarray(np.asarray(a), dtype=np.int32)
+
+
+def _i32p(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        stream = stream.cuda_stream
+    return ctypes.c_void_p(int(stream))
+
+
+def _dev_ptr(t: Optional[torch.Tensor], name: str, dtype=None) -> ctypes.c_void_p:
+    if t is None:
+        return ctypes.c_void_p(0)
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _pool_stride(k_pool: torch.Tensor, v_pool: torch.Tensor, head_dim: int) -> int:
+    """Slot stride (elements) of a pool whose rows are [.., Hkv, D] with contiguous heads."""
+    for name, p in (("k_pool", k_pool), ("v_pool", v_pool)):
+        if p.dim() < 2 or p.stride(-1) != 1 or (p.dim() >= 3 and p.stride(-2) != head_dim):
+            raise ValueError(f"{name}: each slot must hold its Hkv rows of D contiguous values")
+    if k_pool.stride(0) != v_pool.stride(0):
+        raise ValueError("k_pool and v_pool must have the same slot stride")
+    return int(k_pool.stride(0))
+
+
+# ----------------------------------------------------------------------------
+# C entry points
+# ----------------------------------------------------------------------------
+def pa_plan_create(max_batch: int, max_kv_total: int, max_q_total: int,
+                   num_qo_heads: int, num_kv_heads: int, head_dim: int) -> ctypes.c_void_p:
+    handle = ctypes.c_void_p()
+    _check(_lib.pa_plan_create(ctypes.byref(handle), max_batch, max_kv_total, max_q_total,
+                               num_qo_heads, num_kv_heads, head_dim), "pa_plan_create")
+    return handle
+
+
+def pa_plan(plan, kv_indptr, qo_indptr=None, flags: int = 0, stream=None) -> None:
+    kv = _host_i32(kv_indptr)
+    qo = _host_i32(qo_indptr)
+    batch = kv.size - 1
+    _check(_lib.pa_plan(plan, _i32p(kv), _i32p(qo), batch, flags, _stream(stream)), "pa_plan")
+
+
+def _run(fn, where, plan, q, k_pool, v_pool, kv_indices, sm_scale, out, lse,
+         num_slots, slot_stride, stream):
+    head_dim = q.shape[-1]
+    if slot_stride is None:
+        slot_stride = _pool_stride(k_pool, v_pool, head_dim)
+    if num_slots is None:
+        num_slots = k_pool.shape[0]
+    if kv_indices.dtype != torch.int32:
+        raise TypeError("kv_indices must be int32")
+    if out.dtype != torch.float32 or not out.is_contiguous():
+        raise TypeError("out must be a contiguous float32 tensor")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
+        raise TypeError("lse must be a contiguous float32 tensor")
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    _check(fn(plan, _dev_ptr(q, "q", torch.bfloat16), _dev_ptr(k_pool, "k_pool", torch.bfloat16),
+              _dev_ptr(v_pool, "v_pool", torch.bfloat16), int(num_slots), int(slot_stride),
+              _dev_ptr(kv_indices, "kv_indices"), float(sm_scale), _dev_ptr(out, "out"),
+              _dev_ptr(lse, "lse"), _stream(stream)), where)
+
+
+def pa_decode_run(plan, q, k_pool, v_pool, kv_indices, sm_scale, out, lse=None,
+                  num_slots=None, slot_stride=None, stream=None) -> None:
+    _run(_lib.pa_decode_run, "pa_decode_run", plan, q, k_pool, v_pool, kv_indices, sm_scale,
+         out, lse, num_slots, slot_stride, stream)
+
+
+def pa_prefill_chunk_run(plan, q, k_pool, v_pool, kv_indices, sm_scale, out, lse=None,
+                         num_slots=None, slot_stride=None, stream=None) -> None:
+    _run(_lib.pa_prefill_chunk_run, "pa_prefill_chunk_run", plan, q, k_pool, v_pool,
+         kv_indices, sm_scale, out, lse, num_slots, slot_stride, stream)
+
+
+def pa_plan_destroy(plan) -> None:
+    _lib.pa_plan_destroy(plan)
+
+
+def pa_partition(kv_indptr, qo_indptr, num_qo_heads: int, num_kv_heads: int, head_dim: int,
+                 flags: int = 0):
+    """Host-only: the partition pa_plan would upload -> (units, merges, n_partials)."""
+    kv = _host_i32(kv_indptr)
+    qo = _host_i32(qo_indptr)
+    n_u, n_m, n_p = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    st = _lib.pa_partition(_i32p(kv), _i32p(qo), kv.size - 1, num_qo_heads, num_kv_heads,
+                           head_dim, flags, None, 0, None, 0,
+                           ctypes.byref(n_u), ctypes.byref(n_m), ctypes.byref(n_p))
+    if st not in (PA_OK, PA_ERR_CAPACITY):
+        _check(st, "pa_partition")
+    units = (pa_work_unit * max(1, n_u.value))()
+    merges = (pa_merge_unit * max(1, n_m.value))()
+    _check(_lib.pa_partition(_i32p(kv), _i32p(qo), kv.size - 1, num_qo_heads, num_kv_heads,
+                             head_dim, flags, units, n_u.value, merges, n_m.value,
+                             ctypes.byref(n_u), ctypes.byref(n_m), ctypes.byref(n_p)),
+           "pa_partition")
+    u = np.frombuffer(bytes(units), dtype=WORK_UNIT_DTYPE)[: n_u.value].copy()
+    m = np.frombuffer(bytes(merges), dtype=MERGE_UNIT_DTYPE)[: n_m.value].copy()
+    return u, m, n_p.value
+
+
+def pa_profile_begin(plan, capacity: int) -> None:
+    _check(_lib.pa_profile_begin(plan, int(capacity)), "pa_profile_begin")
+
+
+def pa_profile_end(plan):
+    """-> (total kernel milliseconds, number of timed launches)."""
+    ms, n = ctypes.c_double(), ctypes.c_int32()
+    _check(_lib.pa_profile_end(plan, ctypes.byref(ms), ctypes.byref(n)), "pa_profile_end")
+    return ms.value, n.value
+
+
+class Plan:
+    """Owns one pa_plan_t (workspace allocated once; pa_plan once per step)."""
+
+    def __init__(self, max_batch: int, max_kv_total: int, num_qo_heads: int, num_kv_heads: int,
+                 head_dim: int, max_q_total: int = 0):
+        self.num_qo_heads, self.num_kv_heads, self.head_dim = num_qo_heads, num_kv_heads, head_dim
+        self.handle = pa_plan_create(max_batch, max_kv_total, max_q_total, num_qo_heads,
+                                     num_kv_heads, head_dim)
+
+    def plan(self, kv_indptr, qo_indptr=None, flags: int = 0, stream=None) -> None:
+        pa_plan(self.handle, kv_indptr, qo_indptr, flags, stream)
+
+    def decode(self, q, k_pool, v_pool, kv_indices, sm_scale, out, lse=None, **kw) -> None:
+        pa_decode_run(self.handle, q, k_pool, v_pool, kv_indices, sm_scale, out, lse, **kw)
+
+    def prefill(self, q, k_pool, v_pool, kv_indices, sm_scale, out, lse=None, **kw) -> None:
+        pa_prefill_chunk_run(self.handle, q, k_pool, v_pool, kv_indices, sm_scale, out, lse, **kw)
+
+    def close(self) -> None:
+        if self.handle is not None and self.handle.value:
+            pa_plan_destroy(self.handle)
+        self.handle = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,427 @@
+// api.cpp -- the C ABI of libpa (declared in include/pa.h): argument checking,
+// the plan object (allocated once, reused every step), upload of the
+// partition, and kernel launches on the caller's stream.
+//
+// Buffers are allocated once at plan creation and a plan is computed once per
+// step and reused by every layer: Agent-Infer page ("Agent-Infer: 纯 Rust 编写的
+// 高性能 LLM 推理引擎"), section "分页 KV 缓存" and stages 2-3 of the table in
+// "优化历程".
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "pa_internal.h"
+
+struct pa_plan {
+    int device = -1;
+    int32_t max_batch = 0;
+    int64_t max_kv_total = 0;
+    int32_t max_q_total = 0;
+    int32_t num_qo_heads = 0, num_kv_heads = 0, head_dim = 0, group = 0;
+    int32_t num_cu = pa::kNumCu, num_xcd = pa::kNumXcd;
+    int64_t unit_cap = 0, merge_cap = 0, partial_rows_cap = 0;
+    // device: [units | merges] packed by the last pa_plan, and partial storage
+    void *d_table = nullptr;
+    float *d_part_o = nullptr;
+    float *d_part_lse = nullptr;
+    // pinned staging, two alternating buffers of (unit_cap + merge_cap) entries
+    void *h_stage[2] = {nullptr, nullptr};
+    hipEvent_t stage_done[2] = {nullptr, nullptr};
+    bool stage_pending[2] = {false, false};
+    int next_stage = 0;
+    // the last partition
+    pa::PlanMode mode = pa::PlanMode::kNone;
+    int32_t batch = 0;
+    int64_t kv_total = 0;
+    int32_t q_total = 0;
+    int32_t n_units = 0, n_merges = 0, n_partials = 0;
+    // kernel timing: event pairs recorded around the attention kernel
+    std::vector<hipEvent_t> prof_events;   // 2 per pair
+    mutable int32_t prof_used = 0;
+    bool prof_on = false;
+};
+
+namespace {
+
+thread_local std::string g_detail;
+
+pa_status fail(pa_status s, const std::string &msg) {
+    g_detail = msg;
+    return s;
+}
+
+pa_status hip_fail(hipError_t e, const char *what) {
+    g_detail = std::string(what) + ": " + hipGetErrorString(e);
+    return PA_ERR_HIP;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+constexpr size_t kEntry = sizeof(pa_work_unit);
+static_assert(sizeof(pa_work_unit) == 32 && sizeof(pa_merge_unit) == 32, "32-byte entries");
+
+void drop_profile(pa_plan_t *p) {
+    for (hipEvent_t e : p->prof_events)
+        (void)hipEventDestroy(e);
+    p->prof_events.clear();
+    p->prof_used = 0;
+    p->prof_on = false;
+}
+
+// Record the start (second = false) or end of a timed kernel.
+hipError_t profile_mark(const pa_plan_t *p, hipStream_t s, bool end) {
+    if (!p->prof_on || (size_t)p->prof_used * 2 >= p->prof_events.size())
+        return hipSuccess;
+    hipError_t e = hipEventRecord(p->prof_events[(size_t)p->prof_used * 2 + (end ? 1 : 0)], s);
+    if (end)
+        p->prof_used++;
+    return e;
+}
+
+void release(pa_plan_t *p) {
+    if (!p)
+        return;
+    drop_profile(p);
+    for (int i = 0; i < 2; i++) {
+        if (p->stage_done[i]) {
+            if (p->stage_pending[i])
+                (void)hipEventSynchronize(p->stage_done[i]);
+            (void)hipEventDestroy(p->stage_done[i]);
+        }
+        if (p->h_stage[i])
+            (void)hipHostFree(p->h_stage[i]);
+    }
+    if (p->d_table)
+        (void)hipFree(p->d_table);
+    if (p->d_part_o)
+        (void)hipFree(p->d_part_o);
+    if (p->d_part_lse)
+        (void)hipFree(p->d_part_lse);
+    delete p;
+}
+
+// Checks shared by the run entry points; fills the launch descriptor.
+pa_status prepare_run(const pa_plan_t *p, pa::PlanMode want, const void *q, const void *k_pool,
+                      const void *v_pool, int64_t num_slots, int64_t slot_stride,
+                      const int32_t *kv_indices, float sm_scale, float *out, float *lse,
+                      pa::DecodeLaunch *l) {
+    if (!p)
+        return fail(PA_ERR_INVALID_ARG, "plan is null");
+    if (p->mode != want)
+        return fail(PA_ERR_PLAN_MISMATCH, p->mode == pa::PlanMode::kNone
+                                              ? "pa_plan has not been called on this plan"
+                                              : "the last pa_plan was for the other mode "
+                                                "(decode: qo_indptr NULL; prefill: non-NULL)");
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetDevice");
+    if (dev != p->device)
+        return fail(PA_ERR_INVALID_ARG, "current HIP device differs from the plan's device");
+    const bool has_rows = (want == pa::PlanMode::kDecode) ? p->batch > 0 : p->q_total > 0;
+    if (has_rows && (!q || !out))
+        return fail(PA_ERR_INVALID_ARG, "q or out is null");
+    if (p->kv_total > 0 && (!k_pool || !v_pool || !kv_indices))
+        return fail(PA_ERR_INVALID_ARG, "k_pool, v_pool or kv_indices is null");
+    if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16))
+        return fail(PA_ERR_INVALID_ARG, "q, k_pool and v_pool must be 16-byte aligned");
+    if (!aligned(kv_indices, 4) || !aligned(out, 4) || !aligned(lse, 4))
+        return fail(PA_ERR_INVALID_ARG, "kv_indices, out and lse must be 4-byte aligned");
+    const int64_t row = (int64_t)p->num_kv_heads * p->head_dim;
+    if (slot_stride == 0)
+        slot_stride = row;
+    if (slot_stride < row || slot_stride % 8 != 0)
+        return fail(PA_ERR_INVALID_ARG, "slot_stride must be >= Hkv*D and a multiple of 8");
+    if (slot_stride * 2 > 0x7fffffffLL)
+        return fail(PA_ERR_INVALID_ARG, "slot_stride too large");
+    if (num_slots < 0 || (p->kv_total > 0 && num_slots == 0))
+        return fail(PA_ERR_INVALID_ARG, "num_slots must be positive");
+    if (!std::isfinite(sm_scale))
+        return fail(PA_ERR_INVALID_ARG, "sm_scale is not finite");
+    const char *tbl = static_cast<const char *>(p->d_table);
+    l->units = reinterpret_cast<const pa_work_unit *>(tbl);
+    l->n_units = p->n_units;
+    l->merges = reinterpret_cast<const pa_merge_unit *>(tbl + (size_t)p->n_units * kEntry);
+    l->n_merges = p->n_merges;
+    l->q = q;
+    l->k_pool = k_pool;
+    l->v_pool = v_pool;
+    l->slot_stride = slot_stride;
+    l->num_slots = num_slots;
+    l->kv_indices = kv_indices;
+    l->sm_scale = sm_scale;
+    l->out = out;
+    l->lse = lse;
+    l->partial_o = p->d_part_o;
+    l->partial_lse = p->d_part_lse;
+    l->num_qo_heads = p->num_qo_heads;
+    l->num_kv_heads = p->num_kv_heads;
+    l->head_dim = p->head_dim;
+    return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *pa_strerror(pa_status s) {
+    switch (s) {
+    case PA_OK: return "ok";
+    case PA_ERR_INVALID_ARG: return "invalid argument";
+    case PA_ERR_UNSUPPORTED: return "unsupported shape";
+    case PA_ERR_CAPACITY: return "plan capacity exceeded";
+    case PA_ERR_PLAN_MISMATCH: return "run does not match the plan";
+    case PA_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char *pa_last_error_detail(void) { return g_detail.c_str(); }
+
+int32_t pa_version(void) { return 100; }
+
+pa_status pa_partition(const int32_t *kv_indptr_host, const int32_t *qo_indptr_host,
+                       int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,
+                       int32_t head_dim, uint32_t flags, pa_work_unit *units,
+                       int32_t unit_capacity, pa_merge_unit *merges, int32_t merge_capacity,
+                       int32_t *n_units, int32_t *n_merges, int32_t *n_partials) {
+    if (!n_units || !n_merges || !n_partials)
+        return fail(PA_ERR_INVALID_ARG, "count pointers must not be null");
+    if ((unit_capacity > 0 && !units) || (merge_capacity > 0 && !merges) || unit_capacity < 0 ||
+        merge_capacity < 0)
+        return fail(PA_ERR_INVALID_ARG, "bad output arrays");
+    pa::PartitionArgs a{kv_indptr_host, qo_indptr_host, batch, num_qo_heads, num_kv_heads,
+                        head_dim, flags, pa::kNumCu, pa::kNumXcd};
+    pa::PartitionResult r;
+    const char *detail = "";
+    pa_status s = pa::partition(a, units, unit_capacity, merges, merge_capacity, &r, &detail);
+    *n_units = r.n_units;
+    *n_merges = r.n_merges;
+    *n_partials = r.n_partials;
+    if (s != PA_OK)
+        return fail(s, detail);
+    return PA_OK;
+}
+
+pa_status pa_plan_create(pa_plan_t **out, int32_t max_batch, int64_t max_kv_total,
+                         int32_t max_q_total, int32_t num_qo_heads, int32_t num_kv_heads,
+                         int32_t head_dim) {
+    if (!out)
+        return fail(PA_ERR_INVALID_ARG, "out is null");
+    if (max_batch < 0 || max_kv_total < 0 || max_q_total < 0)
+        return fail(PA_ERR_INVALID_ARG, "negative capacity");
+    if (max_kv_total > 0x7fffffffLL)
+        return fail(PA_ERR_INVALID_ARG, "max_kv_total above int32 range");
+    if (num_qo_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0)
+        return fail(PA_ERR_INVALID_ARG, "head counts and head_dim must be positive");
+    if (!pa::supported_shape(num_qo_heads, num_kv_heads, head_dim))
+        return fail(PA_ERR_UNSUPPORTED,
+                    "unsupported head shape (need Hq/Hkv in {1,2,4,8} and D in {128,256})");
+    pa_plan_t *p = new (std::nothrow) pa_plan_t;
+    if (!p)
+        return fail(PA_ERR_INVALID_ARG, "host allocation failed");
+    p->max_batch = max_batch;
+    p->max_kv_total = max_kv_total;
+    p->max_q_total = max_q_total;
+    p->num_qo_heads = num_qo_heads;
+    p->num_kv_heads = num_kv_heads;
+    p->head_dim = head_dim;
+    p->group = num_qo_heads / num_kv_heads;
+    hipError_t e = hipGetDevice(&p->device);
+    if (e != hipSuccess) {
+        release(p);
+        return hip_fail(e, "hipGetDevice");
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, p->device) == hipSuccess &&
+        cus > 0)
+        p->num_cu = cus;
+    pa::partition_capacity(max_batch, max_kv_total, max_q_total, num_qo_heads, num_kv_heads,
+                           head_dim, p->num_xcd, &p->unit_cap, &p->merge_cap,
+                           &p->partial_rows_cap);
+    // the capacity bound assumes kNumCu compute units for prefill splitting
+    if (p->num_cu > pa::kNumCu)
+        p->unit_cap = p->unit_cap * p->num_cu / pa::kNumCu + 1;
+    const size_t table_bytes = (size_t)(p->unit_cap + p->merge_cap) * kEntry;
+    const size_t part_o_bytes = (size_t)std::max<int64_t>(1, p->partial_rows_cap) * head_dim * sizeof(float);
+    const size_t part_lse_bytes = (size_t)std::max<int64_t>(1, p->partial_rows_cap) * sizeof(float);
+    if ((e = hipMalloc(&p->d_table, std::max<size_t>(table_bytes, kEntry))) != hipSuccess ||
+        (e = hipMalloc((void **)&p->d_part_o, part_o_bytes)) != hipSuccess ||
+        (e = hipMalloc((void **)&p->d_part_lse, part_lse_bytes)) != hipSuccess) {
+        release(p);
+        return hip_fail(e, "hipMalloc (plan workspace)");
+    }
+    for (int i = 0; i < 2; i++) {
+        if ((e = hipHostMalloc(&p->h_stage[i], std::max<size_t>(table_bytes, kEntry),
+                               hipHostMallocDefault)) != hipSuccess ||
+            (e = hipEventCreateWithFlags(&p->stage_done[i], hipEventDisableTiming)) != hipSuccess) {
+            release(p);
+            return hip_fail(e, "pinned staging / event");
+        }
+    }
+    *out = p;
+    return PA_OK;
+}
+
+void pa_plan_destroy(pa_plan_t *plan) { release(plan); }
+
+pa_status pa_plan(pa_plan_t *p, const int32_t *kv_indptr_host, const int32_t *qo_indptr_host,
+                  int32_t batch, uint32_t flags, pa_stream_t stream) {
+    if (!p)
+        return fail(PA_ERR_INVALID_ARG, "plan is null");
+    if (batch < 0)
+        return fail(PA_ERR_INVALID_ARG, "batch < 0");
+    if (batch > 0 && !kv_indptr_host)
+        return fail(PA_ERR_INVALID_ARG, "kv_indptr_host is null");
+    if (batch > p->max_batch)
+        return fail(PA_ERR_CAPACITY, "batch above the plan's max_batch");
+    const int64_t kv_total = batch > 0 ? kv_indptr_host[batch] : 0;
+    if (kv_total > p->max_kv_total)
+        return fail(PA_ERR_CAPACITY, "total slot-list length above the plan's max_kv_total");
+    int32_t q_total = 0;
+    if (qo_indptr_host) {
+        q_total = batch > 0 ? qo_indptr_host[batch] : 0;
+        if (q_total > p->max_q_total)
+            return fail(PA_ERR_CAPACITY, "total query rows above the plan's max_q_total");
+    }
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetDevice");
+    if (dev != p->device)
+        return fail(PA_ERR_INVALID_ARG, "current HIP device differs from the plan's device");
+
+    const int s = p->next_stage;
+    if (p->stage_pending[s]) {
+        if ((e = hipEventSynchronize(p->stage_done[s])) != hipSuccess)
+            return hip_fail(e, "waiting for an earlier plan upload");
+        p->stage_pending[s] = false;
+    }
+    char *stage = static_cast<char *>(p->h_stage[s]);
+    pa_work_unit *units = reinterpret_cast<pa_work_unit *>(stage);
+    pa_merge_unit *merges = reinterpret_cast<pa_merge_unit *>(stage + (size_t)p->unit_cap * kEntry);
+    pa::PartitionArgs a{kv_indptr_host, qo_indptr_host, batch, p->num_qo_heads, p->num_kv_heads,
+                        p->head_dim, flags, p->num_cu, p->num_xcd};
+    pa::PartitionResult r;
+    const char *detail = "";
+    pa_status st = pa::partition(a, units, (int32_t)std::min<int64_t>(p->unit_cap, 0x7fffffff),
+                                 merges, (int32_t)std::min<int64_t>(p->merge_cap, 0x7fffffff),
+                                 &r, &detail);
+    if (st != PA_OK)
+        return fail(st, detail);
+    const int64_t rows_per_slot = qo_indptr_host ? pa::kPrefillTileRows : p->group;
+    if ((int64_t)r.n_partials * rows_per_slot > p->partial_rows_cap)
+        return fail(PA_ERR_CAPACITY, "partial storage of the plan exceeded");
+    // pack merges right after the units, upload both with one copy
+    if (r.n_merges > 0)
+        std::memmove(stage + (size_t)r.n_units * kEntry, merges, (size_t)r.n_merges * kEntry);
+    const size_t bytes = (size_t)(r.n_units + r.n_merges) * kEntry;
+    if (bytes > 0) {
+        if ((e = hipMemcpyAsync(p->d_table, stage, bytes, hipMemcpyHostToDevice,
+                                (hipStream_t)stream)) != hipSuccess)
+            return hip_fail(e, "plan upload");
+        if ((e = hipEventRecord(p->stage_done[s], (hipStream_t)stream)) != hipSuccess)
+            return hip_fail(e, "plan upload event");
+        p->stage_pending[s] = true;
+    }
+    p->next_stage = s ^ 1;
+    p->mode = qo_indptr_host ? pa::PlanMode::kPrefill : pa::PlanMode::kDecode;
+    p->batch = batch;
+    p->kv_total = kv_total;
+    p->q_total = q_total;
+    p->n_units = r.n_units;
+    p->n_merges = r.n_merges;
+    p->n_partials = r.n_partials;
+    return PA_OK;
+}
+
+pa_status pa_decode_run(const pa_plan_t *p, const void *q, const void *k_pool, const void *v_pool,
+                        int64_t num_slots, int64_t slot_stride, const int32_t *kv_indices,
+                        float sm_scale, float *out, float *lse, pa_stream_t stream) {
+    pa::DecodeLaunch l;
+    pa_status st = prepare_run(p, pa::PlanMode::kDecode, q, k_pool, v_pool, num_slots, slot_stride,
+                               kv_indices, sm_scale, out, lse, &l);
+    if (st != PA_OK)
+        return st;
+    hipError_t e = profile_mark(p, (hipStream_t)stream, false);
+    if (e != hipSuccess)
+        return hip_fail(e, "profile event");
+    int rc = pa::launch_decode(l, stream);
+    if (rc != 0)
+        return hip_fail((hipError_t)rc, "decode kernel launch");
+    if ((e = profile_mark(p, (hipStream_t)stream, true)) != hipSuccess)
+        return hip_fail(e, "profile event");
+    rc = pa::launch_merge(l, stream);
+    if (rc != 0)
+        return hip_fail((hipError_t)rc, "merge kernel launch");
+    return PA_OK;
+}
+
+pa_status pa_prefill_chunk_run(const pa_plan_t *p, const void *q, const void *k_pool,
+                               const void *v_pool, int64_t num_slots, int64_t slot_stride,
+                               const int32_t *kv_indices, float sm_scale, float *out, float *lse,
+                               pa_stream_t stream) {
+    pa::DecodeLaunch l;
+    pa_status st = prepare_run(p, pa::PlanMode::kPrefill, q, k_pool, v_pool, num_slots,
+                               slot_stride, kv_indices, sm_scale, out, lse, &l);
+    if (st != PA_OK)
+        return st;
+    hipError_t e = profile_mark(p, (hipStream_t)stream, false);
+    if (e != hipSuccess)
+        return hip_fail(e, "profile event");
+    int rc = pa::launch_prefill(l, stream);
+    if (rc == (int)hipErrorNotSupported)
+        return fail(PA_ERR_UNSUPPORTED, "prefill kernel not available in this build");
+    if (rc != 0)
+        return hip_fail((hipError_t)rc, "prefill kernel launch");
+    if ((e = profile_mark(p, (hipStream_t)stream, true)) != hipSuccess)
+        return hip_fail(e, "profile event");
+    rc = pa::launch_merge(l, stream);
+    if (rc != 0)
+        return hip_fail((hipError_t)rc, "merge kernel launch");
+    return PA_OK;
+}
+
+pa_status pa_profile_begin(pa_plan_t *p, int32_t capacity) {
+    if (!p || capacity <= 0)
+        return fail(PA_ERR_INVALID_ARG, "plan is null or capacity <= 0");
+    drop_profile(p);
+    p->prof_events.assign((size_t)capacity * 2, nullptr);
+    for (auto &ev : p->prof_events) {
+        hipError_t e = hipEventCreate(&ev);
+        if (e != hipSuccess) {
+            ev = nullptr;
+            drop_profile(p);
+            return hip_fail(e, "hipEventCreate");
+        }
+    }
+    p->prof_on = true;
+    return PA_OK;
+}
+
+pa_status pa_profile_end(pa_plan_t *p, double *total_ms, int32_t *n_launches) {
+    if (!p || !total_ms || !n_launches)
+        return fail(PA_ERR_INVALID_ARG, "null argument");
+    double total = 0.0;
+    for (int32_t i = 0; i < p->prof_used; i++) {
+        hipError_t e = hipEventSynchronize(p->prof_events[(size_t)i * 2 + 1]);
+        float ms = 0.f;
+        if (e == hipSuccess)
+            e = hipEventElapsedTime(&ms, p->prof_events[(size_t)i * 2], p->prof_events[(size_t)i * 2 + 1]);
+        if (e != hipSuccess) {
+            drop_profile(p);
+            return hip_fail(e, "reading profile events");
+        }
+        total += ms;
+    }
+    *total_ms = total;
+    *n_launches = p->prof_used;
+    drop_profile(p);
+    return PA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,531 @@
+// decode.hip -- gfx950 kernels of libpa's decode path: split-KV paged GQA
+// decode attention and the log-sum-exp merge of split partitions.
+//
+// Operation: batched decode attention over a token-granular KV pool (one slot
+// per token, shared by all requests), Agent-Infer page ("Agent-Infer: 纯 Rust
+// 编写的高性能 LLM 推理引擎"), section "分页 KV 缓存"; grouped-query heads,
+// Pegainfer page ("Pegainfer: 纯Rust+CUDA构建的LLM推理引擎"), section
+// "关键技术实现" items 1-2.  The arithmetic is the textbook softmax attention,
+// computed online in the base-2 exponent domain:
+//     s = <q, k> * scale * log2(e);  p = exp2(s - m);  o = sum p v / sum p
+// which gives the same result as exp(<q,k>*scale - m') with m' = m * ln 2.
+//
+// Lane layout of the decode kernel (one workgroup = 4 waves = one work unit:
+// one request, one KV head, a contiguous part of its slot list):
+//   * a K or V row of one head is D bf16 = D*2 bytes; LPR = D/8 lanes load it
+//     with one 16-byte load each (lane chunk c = lane % LPR holds elements
+//     8c..8c+7), so one wave-wide load instruction fetches RPI = 64/LPR whole
+//     rows (4 rows at D = 128, 2 at D = 256): fully coalesced 128-bit loads,
+//     each lane gathering through its own slot id;
+//   * a wave walks the unit in tiles of NI instructions (NI*RPI tokens); the
+//     four waves take every fourth tile; the next tile's slot ids and K/V rows
+//     are loaded while the current one is computed;
+//   * each K row is used by all G query heads of its group straight from the
+//     registers it was loaded into (dot2 bf16 products, fp32 accumulation);
+//     the partial dot products are reduced across the row's lanes with DPP
+//     and the reduction is "transposed": G values per lane go in, and lane c
+//     comes out holding the full score of head c % G, so each (token, head)
+//     exponential is computed by LPR/G lanes instead of LPR;
+//   * softmax is online per (lane row, head) with a lazily moved running
+//     maximum (it moves only when a score exceeds it by more than 8 in the
+//     log2 domain, so weights stay <= 256 and rescaling is rare);
+//   * V rows accumulate into fp32 o[G][8] per lane; at the end the rows of a
+//     wave are combined with cross-lane shuffles, then the four waves through
+//     LDS, and the unit writes either the final output or a partial result
+//     (normalised o and its log2-sum-exp) for the merge kernel.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// Running maxima start here instead of -inf so that exp2(s - m) is never
+// exp2(-inf - -inf); any real score is far above it.
+constexpr float kNoMax = -1.0e30f;
+// Lazy rescale threshold (log2 domain): weights stay below 2^8.
+constexpr float kRescaleSlack = 8.0f;
+
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// DPP lane moves inside 16-lane rows (all sources valid: permutations).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                                 CTRL, 0xf, 0xf, false));
+}
+constexpr int kQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kRowRor4 = 0x124;   // row_ror:4
+constexpr int kRowRor8 = 0x128;   // row_ror:8 (== lane ^ 8 within a row)
+
+__device__ __forceinline__ float shfl_xor(float x, int mask) { return __shfl_xor(x, mask, 64); }
+
+// Hardware base-2 exponential and logarithm (v_exp_f32 / v_log_f32):
+// exp2(-inf) = 0, exp2(0) = 1.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Value of lane `h` of this lane's G-lane group (G <= 4: inside the quad).
+template <int G>
+__device__ __forceinline__ float group_bcast(float x, int h, int lane) {
+    if constexpr (G == 1) {
+        return x;
+    } else if constexpr (G == 2) {
+        // quad_perm [h, h, 2+h, 2+h]
+        return h == 0 ? dpp_mov<0xA0>(x) : dpp_mov<0xF5>(x);
+    } else if constexpr (G == 4) {
+        switch (h) {
+        case 0: return dpp_mov<0x00>(x);
+        case 1: return dpp_mov<0x55>(x);
+        case 2: return dpp_mov<0xAA>(x);
+        default: return dpp_mov<0xFF>(x);
+        }
+    } else {
+        return __shfl(x, (lane & ~7) + h, 64);
+    }
+}
+
+// One exchange step of the transposed reduction across partner lane ^ (1<<BIT):
+// the lane keeps the half of its N values whose head index has bit BIT equal to
+// its own lane bit, and adds the partner's copy of that half.
+template <int BIT, int N>
+__device__ __forceinline__ void exchange_step(float *v, bool upper) {
+#pragma unroll
+    for (int m = 0; m < N / 2; m++) {
+        float keep = upper ? v[2 * m + 1] : v[2 * m];
+        float send = upper ? v[2 * m] : v[2 * m + 1];
+        float recv;
+        if constexpr (BIT == 0)
+            recv = dpp_mov<kQuadXor1>(send);
+        else if constexpr (BIT == 1)
+            recv = dpp_mov<kQuadXor2>(send);
+        else
+            recv = shfl_xor(send, 1 << BIT);
+        v[m] = keep + recv;
+    }
+}
+
+// Sum G per-lane values over the LPR lanes of a row.  On return lane c of the
+// row holds the full sum of value (c % G).
+template <int G, int LPR>
+__device__ __forceinline__ float row_reduce_transposed(float (&v)[G], int lane) {
+    float x;
+    if constexpr (G == 1) {
+        x = v[0];
+        x += dpp_mov<kQuadXor1>(x);
+        x += dpp_mov<kQuadXor2>(x);
+        x += dpp_mov<kRowRor4>(x);
+        x += dpp_mov<kRowRor8>(x);
+    } else if constexpr (G == 2) {
+        exchange_step<0, 2>(v, lane & 1);
+        x = v[0];
+        x += dpp_mov<kQuadXor2>(x);
+        x += dpp_mov<kRowRor4>(x);
+        x += dpp_mov<kRowRor8>(x);
+    } else if constexpr (G == 4) {
+        exchange_step<0, 4>(v, lane & 1);
+        exchange_step<1, 2>(v, (lane >> 1) & 1);
+        x = v[0];
+        x += dpp_mov<kRowRor4>(x);
+        x += dpp_mov<kRowRor8>(x);
+    } else {
+        exchange_step<0, 8>(v, lane & 1);
+        exchange_step<1, 4>(v, (lane >> 1) & 1);
+        exchange_step<2, 2>(v, (lane >> 2) & 1);
+        x = v[0];
+        x += dpp_mov<kRowRor8>(x);
+    }
+    if constexpr (LPR == 32)
+        x += shfl_xor(x, 16);
+    return x;
+}
+
+template <int D>
+struct Geometry {
+    static constexpr int LPR = D / 8;          // lanes per row
+    static constexpr int RPI = 64 / LPR;       // rows per wave instruction
+    static constexpr int NI = 4;               // instructions per tile
+    static constexpr int TILE = NI * RPI;      // tokens per wave tile
+};
+
+// Byte offset of a pool row: 32-bit form (pool below 4 GiB, slot ids and
+// stride below 2^24) or 64-bit form.
+template <bool WIDE>
+struct RowAddr;
+template <>
+struct RowAddr<false> {
+    static __device__ __forceinline__ const uint4 *at(const char *base, int32_t slot,
+                                                      uint32_t stride_bytes, uint32_t lane_off) {
+        uint32_t off = __umul24((uint32_t)slot, stride_bytes) + lane_off;
+        return reinterpret_cast<const uint4 *>(base + off);
+    }
+};
+template <>
+struct RowAddr<true> {
+    static __device__ __forceinline__ const uint4 *at(const char *base, int32_t slot,
+                                                      uint32_t stride_bytes, uint32_t lane_off) {
+        uint64_t off = (uint64_t)(uint32_t)slot * stride_bytes + lane_off;
+        return reinterpret_cast<const uint4 *>(base + off);
+    }
+};
+
+template <int D, int NI>
+struct TileRegs {
+    int32_t slot[NI];
+    uint4 k[NI];
+    uint4 v[NI];
+};
+
+template <int D, int G, bool WIDE>
+__global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
+    const pa_work_unit *__restrict__ units, const uint16_t *__restrict__ q, const char *__restrict__ k_pool,
+    const char *__restrict__ v_pool, uint32_t stride_bytes,
+    const int32_t *__restrict__ kv_indices, float scale_log2, float *__restrict__ out,
+    float *__restrict__ lse, float *__restrict__ part_o, float *__restrict__ part_lse,
+    int32_t num_qo_heads) {
+    using Geo = Geometry<D>;
+    constexpr int LPR = Geo::LPR, RPI = Geo::RPI, NI = Geo::NI, TILE = Geo::TILE;
+    constexpr int WAVES = kDecodeWaves;
+
+    __shared__ float lds_o[WAVES][G][D];
+    __shared__ float lds_m[WAVES][G];
+    __shared__ float lds_l[WAVES][G];
+
+    const pa_work_unit unit = units[blockIdx.x];
+    if (unit.request < 0)
+        return;  // padding unit (uniform over the workgroup)
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int r = lane / LPR;      // row within an instruction
+    const int c = lane % LPR;      // 16-byte chunk of the row
+    const int hsel = lane % G;     // head whose score this lane holds after reduction
+
+    // query rows of the group: q[b, kvh*G + h, 8c .. 8c+7]
+    uint32_t qv[G][4];
+    {
+        const uint16_t *qrow = q + ((int64_t)unit.request * num_qo_heads + (int64_t)unit.kv_head * G) * D + c * 8;
+#pragma unroll
+        for (int h = 0; h < G; h++) {
+            uint4 t = *reinterpret_cast<const uint4 *>(qrow + (int64_t)h * D);
+            qv[h][0] = t.x; qv[h][1] = t.y; qv[h][2] = t.z; qv[h][3] = t.w;
+        }
+    }
+
+    const uint32_t lane_off = (uint32_t)(unit.kv_head * D + c * 8) * 2u;
+    const int32_t kv_begin = unit.kv_begin, kv_end = unit.kv_end;
+    const int32_t n_tiles = (kv_end - kv_begin + TILE - 1) / TILE;
+
+    float m_run = kNoMax, l_run = 0.f;
+    float acc[G][8];
+#pragma unroll
+    for (int h = 0; h < G; h++)
+#pragma unroll
+        for (int e = 0; e < 8; e++)
+            acc[h][e] = 0.f;
+
+    auto load_slots = [&](TileRegs<D, NI> &t, int tile) {
+        const int32_t base = kv_begin + tile * TILE + r;
+#pragma unroll
+        for (int i = 0; i < NI; i++) {
+            int32_t tok = base + i * RPI;
+            tok = tok < kv_end ? tok : kv_end - 1;
+            t.slot[i] = kv_indices[tok];
+        }
+    };
+    auto load_rows = [&](TileRegs<D, NI> &t) {
+#pragma unroll
+        for (int i = 0; i < NI; i++)
+            t.k[i] = *RowAddr<WIDE>::at(k_pool, t.slot[i], stride_bytes, lane_off);
+#pragma unroll
+        for (int i = 0; i < NI; i++)
+            t.v[i] = *RowAddr<WIDE>::at(v_pool, t.slot[i], stride_bytes, lane_off);
+    };
+    auto compute = [&](const TileRegs<D, NI> &t, int tile) {
+        const int32_t base = kv_begin + tile * TILE + r;
+        float s[NI];
+#pragma unroll
+        for (int i = 0; i < NI; i++) {
+            float part[G];
+#pragma unroll
+            for (int h = 0; h < G; h++) {
+                float a = dot2_bf16(qv[h][0], t.k[i].x, 0.f);
+                a = dot2_bf16(qv[h][1], t.k[i].y, a);
+                a = dot2_bf16(qv[h][2], t.k[i].z, a);
+                a = dot2_bf16(qv[h][3], t.k[i].w, a);
+                part[h] = a;
+            }
+            float sc = row_reduce_transposed<G, LPR>(part, lane) * scale_log2;
+            s[i] = (base + i * RPI < kv_end) ? sc : -INFINITY;
+        }
+        float tmax = s[0];
+#pragma unroll
+        for (int i = 1; i < NI; i++)
+            tmax = fmaxf(tmax, s[i]);
+        const bool move = tmax > m_run + kRescaleSlack;
+        if (__any(move)) {
+            const float m_new = move ? tmax : m_run;
+            const float alpha = fast_exp2(m_run - m_new);
+            l_run *= alpha;
+            m_run = m_new;
+#pragma unroll
+            for (int h = 0; h < G; h++) {
+                const float ah = group_bcast<G>(alpha, h, lane);
+#pragma unroll
+                for (int e = 0; e < 8; e++)
+                    acc[h][e] *= ah;
+            }
+        }
+        float p[NI];
+#pragma unroll
+        for (int i = 0; i < NI; i++) {
+            p[i] = fast_exp2(s[i] - m_run);
+            l_run += p[i];
+        }
+#pragma unroll
+        for (int i = 0; i < NI; i++) {
+            float vf[8];
+            vf[0] = bf16_lo(t.v[i].x); vf[1] = bf16_hi(t.v[i].x);
+            vf[2] = bf16_lo(t.v[i].y); vf[3] = bf16_hi(t.v[i].y);
+            vf[4] = bf16_lo(t.v[i].z); vf[5] = bf16_hi(t.v[i].z);
+            vf[6] = bf16_lo(t.v[i].w); vf[7] = bf16_hi(t.v[i].w);
+#pragma unroll
+            for (int h = 0; h < G; h++) {
+                const float ph = group_bcast<G>(p[i], h, lane);
+#pragma unroll
+                for (int e = 0; e < 8; e++)
+                    acc[h][e] = fmaf(ph, vf[e], acc[h][e]);
+            }
+        }
+    };
+
+    // Tiles wave, wave+4, wave+8, ...: two register sets alternate so the
+    // next tile's rows are in flight while the current one is computed.
+    int tile = wave;
+    if (tile < n_tiles) {
+        TileRegs<D, NI> ta, tb;
+        load_slots(ta, tile);
+        load_rows(ta);
+        if (tile + WAVES < n_tiles)
+            load_slots(tb, tile + WAVES);
+        while (true) {
+            // ta holds tile `tile` (rows in flight); tb holds the next tile's slots
+            const bool has_b = tile + WAVES < n_tiles;
+            if (has_b) {
+                load_rows(tb);
+                if (tile + 2 * WAVES < n_tiles)
+                    load_slots(ta, tile + 2 * WAVES);  // slots only; ta's rows consumed below first
+            }
+            // ta.slot may have been overwritten above, but compute() reads only ta.k / ta.v
+            compute(ta, tile);
+            tile += WAVES;
+            if (!has_b)
+                break;
+            const bool has_a = tile + WAVES < n_tiles;
+            if (has_a) {
+                load_rows(ta);
+                if (tile + 2 * WAVES < n_tiles)
+                    load_slots(tb, tile + 2 * WAVES);
+            }
+            compute(tb, tile);
+            tile += WAVES;
+            if (!has_a)
+                break;
+        }
+    }
+
+    // ---- combine the rows of this wave (same head: lanes with equal lane % G)
+    float mm = m_run;
+#pragma unroll
+    for (int x = LPR; x < 64; x <<= 1)
+        mm = fmaxf(mm, shfl_xor(mm, x));
+    const float f = fast_exp2(m_run - mm);
+    float lsum = l_run * f;
+#pragma unroll
+    for (int x = LPR; x < 64; x <<= 1)
+        lsum += shfl_xor(lsum, x);
+#pragma unroll
+    for (int h = 0; h < G; h++) {
+        const float fh = group_bcast<G>(f, h, lane);
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+            float a = acc[h][e] * fh;
+#pragma unroll
+            for (int x = LPR; x < 64; x <<= 1)
+                a += shfl_xor(a, x);
+            acc[h][e] = a;
+        }
+    }
+    // ---- combine the waves through LDS
+    if (r == 0) {
+#pragma unroll
+        for (int h = 0; h < G; h++) {
+            float4 *dst = reinterpret_cast<float4 *>(&lds_o[wave][h][c * 8]);
+            dst[0] = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+            dst[1] = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
+        }
+        if (c < G) {
+            lds_m[wave][c] = mm;
+            lds_l[wave][c] = lsum;
+        }
+    }
+    __syncthreads();
+
+    const int32_t qrow0 = unit.request * num_qo_heads + unit.kv_head * G;
+    for (int idx = tid; idx < G * D; idx += kDecodeThreads) {
+        const int h = idx / D, d = idx % D;
+        float M = lds_m[0][h];
+#pragma unroll
+        for (int w = 1; w < WAVES; w++)
+            M = fmaxf(M, lds_m[w][h]);
+        float o = 0.f, l = 0.f;
+#pragma unroll
+        for (int w = 0; w < WAVES; w++) {
+            const float wgt = fast_exp2(lds_m[w][h] - M);
+            o = fmaf(wgt, lds_o[w][h][d], o);
+            l = fmaf(wgt, lds_l[w][h], l);
+        }
+        const bool empty = !(l > 0.f);
+        const float res = empty ? 0.f : o / l;
+        const float lse2 = empty ? -INFINITY : M + fast_log2(l);
+        if (unit.partial < 0) {
+            out[(int64_t)(qrow0 + h) * D + d] = res;
+            if (lse && d == 0)
+                lse[qrow0 + h] = lse2 * kLn2;
+        } else {
+            part_o[((int64_t)unit.partial * G + h) * D + d] = res;
+            if (d == 0)
+                part_lse[(int64_t)unit.partial * G + h] = lse2;
+        }
+    }
+}
+
+// Merge unit: partial slots [first, first+n) of query rows [q_begin, q_end)
+// of one KV head.  Each slot holds R rows of D floats (row = (q - q_begin)*G + h)
+// and R log2-sum-exp values.
+template <int D, int G>
+__global__ __launch_bounds__(256) void merge_kernel(const pa_merge_unit *__restrict__ merges,
+                                                    const float *__restrict__ part_o,
+                                                    const float *__restrict__ part_lse,
+                                                    int32_t rows_per_slot, float *__restrict__ out,
+                                                    float *__restrict__ lse, int32_t num_qo_heads) {
+    const pa_merge_unit mu = merges[blockIdx.x];
+    const int32_t rows = (mu.q_end - mu.q_begin) * G;
+    for (int32_t idx = threadIdx.x; idx < rows * D; idx += blockDim.x) {
+        const int32_t row = idx / D, d = idx % D;
+        float M = -INFINITY;
+        for (int32_t i = 0; i < mu.n_parts; i++)
+            M = fmaxf(M, part_lse[(int64_t)(mu.first_partial + i) * rows_per_slot + row]);
+        const int32_t qtok = mu.q_begin + row / G, h = mu.kv_head * G + row % G;
+        const int64_t orow = (int64_t)qtok * num_qo_heads + h;
+        if (M == -INFINITY) {
+            out[orow * D + d] = 0.f;
+            if (lse && d == 0)
+                lse[orow] = -INFINITY;
+            continue;
+        }
+        float o = 0.f, wsum = 0.f;
+        for (int32_t i = 0; i < mu.n_parts; i++) {
+            const int64_t slot_row = (int64_t)(mu.first_partial + i) * rows_per_slot + row;
+            const float w = fast_exp2(part_lse[slot_row] - M);
+            o = fmaf(w, part_o[slot_row * D + d], o);
+            wsum += w;
+        }
+        out[orow * D + d] = o / wsum;
+        if (lse && d == 0)
+            lse[orow] = (M + fast_log2(wsum)) * kLn2;
+    }
+}
+
+template <int D, int G>
+int launch_decode_dg(const DecodeLaunch &l, hipStream_t stream) {
+    const uint32_t stride_bytes = (uint32_t)(l.slot_stride * 2);
+    // the 32-bit row address needs every byte offset below 4 GiB and
+    // operands of the 24-bit multiply below 2^24
+    const uint64_t span = (uint64_t)l.num_slots * stride_bytes;
+    const bool wide = span > 0xFFFF0000ull || l.num_slots > (1 << 24) || stride_bytes >= (1u << 24);
+    const float scale_log2 = l.sm_scale * kLog2e;
+    dim3 grid(l.n_units), block(kDecodeThreads);
+    if (wide)
+        hipLaunchKernelGGL((decode_kernel<D, G, true>), grid, block, 0, stream, l.units,
+                           (const uint16_t *)l.q, (const char *)l.k_pool, (const char *)l.v_pool,
+                           stride_bytes, l.kv_indices, scale_log2, l.out, l.lse, l.partial_o,
+                           l.partial_lse, l.num_qo_heads);
+    else
+        hipLaunchKernelGGL((decode_kernel<D, G, false>), grid, block, 0, stream, l.units,
+                           (const uint16_t *)l.q, (const char *)l.k_pool, (const char *)l.v_pool,
+                           stride_bytes, l.kv_indices, scale_log2, l.out, l.lse, l.partial_o,
+                           l.partial_lse, l.num_qo_heads);
+    return (int)hipGetLastError();
+}
+
+template <int D, int G>
+int launch_merge_dg(const DecodeLaunch &l, int32_t rows_per_slot, hipStream_t stream) {
+    hipLaunchKernelGGL((merge_kernel<D, G>), dim3(l.n_merges), dim3(256), 0, stream, l.merges,
+                       l.partial_o, l.partial_lse, rows_per_slot, l.out, l.lse, l.num_qo_heads);
+    return (int)hipGetLastError();
+}
+
+}  // namespace
+
+int launch_decode(const DecodeLaunch &l, void *stream) {
+    if (l.n_units == 0)
+        return 0;
+    hipStream_t s = (hipStream_t)stream;
+    const int G = l.num_qo_heads / l.num_kv_heads;
+    if (l.head_dim == 128) {
+        switch (G) {
+        case 1: return launch_decode_dg<128, 1>(l, s);
+        case 2: return launch_decode_dg<128, 2>(l, s);
+        case 4: return launch_decode_dg<128, 4>(l, s);
+        case 8: return launch_decode_dg<128, 8>(l, s);
+        }
+    } else if (l.head_dim == 256) {
+        switch (G) {
+        case 1: return launch_decode_dg<256, 1>(l, s);
+        case 2: return launch_decode_dg<256, 2>(l, s);
+        case 4: return launch_decode_dg<256, 4>(l, s);
+        case 8: return launch_decode_dg<256, 8>(l, s);
+        }
+    }
+    return (int)hipErrorInvalidValue;
+}
+
+int launch_merge(const DecodeLaunch &l, void *stream) {
+    if (l.n_merges == 0)
+        return 0;
+    hipStream_t s = (hipStream_t)stream;
+    const int G = l.num_qo_heads / l.num_kv_heads;
+    const int32_t rows = G;  // a decode partial slot holds the group's rows
+    if (l.head_dim == 128) {
+        switch (G) {
+        case 1: return launch_merge_dg<128, 1>(l, rows, s);
+        case 2: return launch_merge_dg<128, 2>(l, rows, s);
+        case 4: return launch_merge_dg<128, 4>(l, rows, s);
+        case 8: return launch_merge_dg<128, 8>(l, rows, s);
+        }
+    } else if (l.head_dim == 256) {
+        switch (G) {
+        case 1: return launch_merge_dg<256, 1>(l, rows, s);
+        case 2: return launch_merge_dg<256, 2>(l, rows, s);
+        case 4: return launch_merge_dg<256, 4>(l, rows, s);
+        case 8: return launch_merge_dg<256, 8>(l, rows, s);
+        }
+    }
+    return (int)hipErrorInvalidValue;
+}
+
+}  // namespace pa

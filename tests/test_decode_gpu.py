@@ -1,0 +1,295 @@
+"""Decode parity: the HIP path (through the C ABI) against the fp64 oracle on
+the same seeded bf16 inputs, element by element, within 2e-3; index handling
+bit-exact.  Needs an AMD GPU."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from gpu_util import TOL, device, max_err, oracle_decode, run_decode, say
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def _lists(lengths, num_slots, seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return W.slot_lists(np.asarray(lengths), num_slots, rng)
+
+
+def _case(lengths, Hq, Hkv, D, num_slots, seed):
+    dev = device()
+    ip, idx = _lists(lengths, num_slots, seed)
+    q = W.normal_bf16((len(lengths), Hq, D), seed * 3 + 1, dev)
+    k, v = W.make_pools(num_slots, Hkv, D, seed * 3 + 2, dev)
+    return ip, idx, q, k, v
+
+
+SMALL = [
+    # (lengths, Hq, Hkv, D) -- tiles of 16 (D=128) / 8 (D=256) tokens per wave, ragged tails
+    ([1, 15, 16, 17, 63, 64, 65, 200, 1023], 32, 8, 128),
+    ([0, 1, 2, 300, 0, 77], 32, 8, 128),
+    ([5, 129, 700], 8, 8, 128),      # group 1
+    ([33, 250], 16, 8, 128),         # group 2
+    ([47, 512], 64, 8, 128),         # group 8
+    ([1, 7, 8, 9, 300, 1500], 16, 4, 256),
+    ([3, 999], 4, 4, 256),
+    ([40, 2], 16, 8, 256),
+    ([100, 31], 32, 4, 256),
+]
+
+
+@pytest.mark.parametrize("lengths,Hq,Hkv,D", SMALL, ids=[f"{c[1]}x{c[2]}x{c[3]}-{i}" for i, c in enumerate(SMALL)])
+def test_small_parity(lengths, Hq, Hkv, D):
+    say(f"small parity lengths={lengths} Hq={Hq} Hkv={Hkv} D={D}")
+    ip, idx, q, k, v = _case(lengths, Hq, Hkv, D, 4096, seed=sum(lengths) + Hq + D)
+    idx_dev = torch.as_tensor(idx, device=device())
+    scale = W.softmax_scale(D)
+    out, lse = run_decode(q, k, v, ip, idx_dev, scale, Hkv)
+    ref, ref_lse = oracle_decode(q, k, v, ip, idx, scale, Hkv)
+    e_out, e_lse = max_err(out, ref), max_err(lse, ref_lse)
+    say(f"  max|d| out={e_out:.3g} lse={e_lse:.3g}")
+    assert e_out <= TOL and e_lse <= TOL
+
+
+@pytest.mark.parametrize("spec", [W.SINGLE_REQUEST_256, W.QWEN3_4B_BATCH8], ids=lambda s: s.name)
+def test_workload_full_parity(spec):
+    say(f"full parity {spec.name}")
+    case = W.make_decode_case(spec, device(), layers=1)
+    idx_dev = torch.as_tensor(case.kv_indices, device=device())
+    out, lse = run_decode(case.q, case.k_pools[0], case.v_pools[0], case.kv_indptr, idx_dev,
+                          case.sm_scale, spec.num_kv_heads)
+    ref, ref_lse = oracle_decode(case.q, case.k_pools[0], case.v_pools[0], case.kv_indptr,
+                                 case.kv_indices, case.sm_scale, spec.num_kv_heads)
+    e_out, e_lse = max_err(out, ref), max_err(lse, ref_lse)
+    say(f"  max|d| out={e_out:.3g} lse={e_lse:.3g}")
+    assert e_out <= TOL and e_lse <= TOL
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("spec,layer", [(W.BATCH64_SHARED_PREFIX, 0), (W.HEADDIM256_BATCH32, 0)],
+                         ids=["batch64_prefix", "headdim256"])
+def test_workload_sampled_parity(spec, layer):
+    """Full-size workloads in the benchmark's launch configuration; the oracle
+    computes a sample of rows (every request, a spread of heads)."""
+    say(f"sampled parity {spec.name} layer {layer}")
+    case = W.make_decode_case(spec, device(), layers=layer + 1)
+    idx_dev = torch.as_tensor(case.kv_indices, device=device())
+    k, v = case.k_pools[layer], case.v_pools[layer]
+    out, lse = run_decode(case.q, k, v, case.kv_indptr, idx_dev, case.sm_scale, spec.num_kv_heads)
+    Hq = spec.num_qo_heads
+    heads = [0, 1, Hq // 2 - 1, Hq // 2, Hq - 1]
+    sel = [b * Hq + h for b in range(spec.batch) for h in heads]
+    ref, ref_lse = oracle_decode(case.q, k, v, case.kv_indptr, case.kv_indices, case.sm_scale,
+                                 spec.num_kv_heads, sel=sel)
+    e_out, e_lse = max_err(out, ref, rows=sel), max_err(lse.reshape(-1, 1), ref_lse.reshape(-1, 1), rows=sel)
+    say(f"  max|d| out={e_out:.3g} lse={e_lse:.3g} over {len(sel)} rows")
+    assert e_out <= TOL and e_lse <= TOL
+    assert np.isfinite(out).all()
+    del case
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("n", [1, 2, 7, 64, 256])
+def test_split_invariance(n):
+    """Forcing any partition count gives the automatic result within 1e-5 and
+    the oracle within 2e-3; parts may be empty."""
+    say(f"forced splits {n}")
+    lengths = [1, 100, 3000, 64, 255]
+    ip, idx, q, k, v = _case(lengths, 32, 8, 128, 8192, seed=7)
+    idx_dev = torch.as_tensor(idx, device=device())
+    scale = W.softmax_scale(128)
+    import paged_gqa_decode_pa_amd as pa
+    auto, auto_lse = run_decode(q, k, v, ip, idx_dev, scale, 8)
+    out, lse = run_decode(q, k, v, ip, idx_dev, scale, 8, flags=pa.PA_PLAN_FORCE_SPLITS(n))
+    assert max_err(out, auto) <= 1e-5 and max_err(lse, auto_lse) <= 1e-5
+    ref, ref_lse = oracle_decode(q, k, v, ip, idx, scale, 8)
+    assert max_err(out, ref) <= TOL and max_err(lse, ref_lse) <= TOL
+
+
+def test_xcd_order_is_result_neutral():
+    import paged_gqa_decode_pa_amd as pa
+    say("xcd order vs natural order")
+    ip, idx, q, k, v = _case([700, 2000, 5, 1300] * 5, 32, 8, 128, 40000, seed=8)
+    idx_dev = torch.as_tensor(idx, device=device())
+    a, la = run_decode(q, k, v, ip, idx_dev, W.softmax_scale(128), 8)
+    b, lb = run_decode(q, k, v, ip, idx_dev, W.softmax_scale(128), 8, flags=pa.PA_PLAN_NO_XCD_ORDER)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+def test_single_token_is_exact():
+    """L = 1: the output is the value row, bit for bit."""
+    say("L=1 exactness")
+    dev = device()
+    B, Hq, Hkv, D, N = 40, 32, 8, 128, 5000
+    ip, idx = _lists([1] * B, N, 11)
+    q = W.normal_bf16((B, Hq, D), 12, dev)
+    k, v = W.make_pools(N, Hkv, D, 13, dev)
+    out, _ = run_decode(q, k, v, ip, torch.as_tensor(idx, device=dev), W.softmax_scale(D), Hkv)
+    vrows = v[torch.as_tensor(idx, device=dev).long()].float().cpu().numpy()   # [B, Hkv, D]
+    want = np.repeat(vrows, Hq // Hkv, axis=1)
+    assert np.array_equal(out, want)
+
+
+def _slot_tag_pool(num_slots, Hkv, D, dev):
+    """V rows whose first three values spell the slot id in base 256 (exact in bf16)."""
+    v = torch.zeros((num_slots, Hkv, D), dtype=torch.bfloat16, device=dev)
+    ids = torch.arange(num_slots, device=dev, dtype=torch.int64)
+    for digit in range(3):
+        v[:, :, digit] = ((ids >> (8 * digit)) & 255).to(torch.bfloat16)[:, None]
+    return v
+
+
+@pytest.mark.parametrize("num_slots,Hq,Hkv,D", [(70000, 32, 8, 128), ((1 << 24) + 1000, 8, 1, 128),
+                                                (2_300_000, 16, 8, 128)],
+                         ids=["small_pool", "over_2^24_slots", "over_4GiB"])
+def test_slot_tags_bit_exact(num_slots, Hq, Hkv, D):
+    """Each single-slot request returns its slot id exactly, including the last
+    slot of pools past 2^24 slots and past 4 GiB (64-bit row offsets)."""
+    dev = device()
+    say(f"slot tags num_slots={num_slots} Hkv={Hkv} ({num_slots * Hkv * D * 2 / 2**30:.2f} GiB per pool)")
+    rng = np.random.Generator(np.random.PCG64(num_slots))
+    chosen = np.concatenate([[num_slots - 1, 0, num_slots - 2], rng.integers(0, num_slots, 61)]).astype(np.int32)
+    B = chosen.size
+    ip = np.arange(B + 1, dtype=np.int32)
+    v = _slot_tag_pool(num_slots, Hkv, D, dev)
+    k = torch.zeros_like(v)
+    q = W.normal_bf16((B, Hq, D), 5, dev)
+    out, _ = run_decode(q, k, v, ip, torch.as_tensor(chosen, device=dev), W.softmax_scale(D), Hkv)
+    digits = np.rint(out[:, :, :3]).astype(np.int64)
+    decoded = digits[..., 0] + 256 * digits[..., 1] + 65536 * digits[..., 2]
+    assert np.array_equal(decoded, np.repeat(chosen[:, None], Hq, axis=1))
+    assert np.array_equal(out[:, :, :3], digits.astype(np.float32))
+    del v, k
+    torch.cuda.empty_cache()
+
+
+def test_poisoned_pool_matches_clean():
+    """NaN in every slot no list references changes nothing (no stray reads)."""
+    say("poisoned pool")
+    lengths = [1, 17, 250, 1000, 3]
+    ip, idx, q, k, v = _case(lengths, 32, 8, 128, 6000, seed=21)
+    idx_dev = torch.as_tensor(idx, device=device())
+    clean, clean_lse = run_decode(q, k, v, ip, idx_dev, W.softmax_scale(128), 8)
+    W.poison_unreferenced(k, idx)
+    W.poison_unreferenced(v, idx)
+    out, lse = run_decode(q, k, v, ip, idx_dev, W.softmax_scale(128), 8)
+    assert np.array_equal(out, clean) and np.array_equal(lse, clean_lse)
+
+
+def test_deterministic():
+    say("run-to-run determinism")
+    ip, idx, q, k, v = _case([3000, 4000, 10], 32, 8, 128, 9000, seed=22)
+    idx_dev = torch.as_tensor(idx, device=device())
+    a = run_decode(q, k, v, ip, idx_dev, W.softmax_scale(128), 8)
+    b = run_decode(q, k, v, ip, idx_dev, W.softmax_scale(128), 8)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_empty_lists():
+    say("empty lists")
+    ip, idx, q, k, v = _case([0, 5, 0, 0], 32, 8, 128, 100, seed=23)
+    out, lse = run_decode(q, k, v, ip, torch.as_tensor(idx, device=device()), W.softmax_scale(128), 8)
+    for b in (0, 2, 3):
+        assert np.all(out[b] == 0) and np.all(np.isneginf(lse[b]))
+    ref, _ = oracle_decode(q, k, v, ip, idx, W.softmax_scale(128), 8)
+    assert max_err(out[1], ref[1]) <= TOL
+
+
+def test_fused_pool_layout():
+    """A [slots, 2, Hkv, D] buffer with slot_stride = 2*Hkv*D gives the same bits."""
+    say("fused KV buffer")
+    dev = device()
+    ip, idx, q, k, v = _case([123, 456], 32, 8, 128, 2000, seed=24)
+    fused = torch.stack([k, v], dim=1).contiguous()          # [N, 2, Hkv, D]
+    idx_dev = torch.as_tensor(idx, device=dev)
+    a = run_decode(q, k, v, ip, idx_dev, W.softmax_scale(128), 8)
+    b = run_decode(q, fused[:, 0], fused[:, 1], ip, idx_dev, W.softmax_scale(128), 8)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_shared_and_duplicate_slots():
+    """Lists overlapping across requests and repeating a slot inside one list."""
+    say("shared and duplicate slots")
+    dev = device()
+    idx = np.array([5, 6, 7, 5, 5, 6, 7, 7, 9, 5, 6], np.int32)
+    ip = np.array([0, 3, 8, 11], np.int32)
+    q = W.normal_bf16((3, 32, 128), 31, dev)
+    k, v = W.make_pools(16, 8, 128, 32, dev)
+    out, lse = run_decode(q, k, v, ip, torch.as_tensor(idx, device=dev), W.softmax_scale(128), 8)
+    ref, ref_lse = oracle_decode(q, k, v, ip, idx, W.softmax_scale(128), 8)
+    assert max_err(out, ref) <= TOL and max_err(lse, ref_lse) <= TOL
+
+
+def test_plan_reused_across_layers():
+    """One pa_plan, several layers with their own pools (one decode step)."""
+    import paged_gqa_decode_pa_amd as pa
+    say("plan reuse over 3 layers")
+    dev = device()
+    spec = W.QWEN3_4B_BATCH8
+    case = W.make_decode_case(spec, dev, layers=3)
+    idx_dev = torch.as_tensor(case.kv_indices, device=dev)
+    outs = []
+    with pa.Plan(spec.batch, int(case.kv_indptr[-1]), 32, 8, 128) as plan:
+        plan.plan(case.kv_indptr)
+        for layer in range(3):
+            o = torch.empty((spec.batch, 32, 128), dtype=torch.float32, device=dev)
+            plan.decode(case.q, case.k_pools[layer], case.v_pools[layer], idx_dev, case.sm_scale, o)
+            outs.append(o)
+        torch.cuda.synchronize()
+    for layer in range(3):
+        ref, _ = oracle_decode(case.q, case.k_pools[layer], case.v_pools[layer], case.kv_indptr,
+                               case.kv_indices, case.sm_scale, 8)
+        assert max_err(outs[layer].cpu().numpy(), ref) <= TOL
+
+
+def test_run_errors_are_reported():
+    import paged_gqa_decode_pa_amd as pa
+    say("error paths")
+    dev = device()
+    ip, idx, q, k, v = _case([10, 20], 32, 8, 128, 100, seed=25)
+    idx_dev = torch.as_tensor(idx, device=dev)
+    out = torch.empty((2, 32, 128), dtype=torch.float32, device=dev)
+    with pa.Plan(2, 30, 32, 8, 128) as plan:
+        with pytest.raises(pa.PAError) as e:                  # no pa_plan yet
+            plan.decode(q, k, v, idx_dev, 0.1, out)
+        assert e.value.status == pa.PA_ERR_PLAN_MISMATCH
+        with pytest.raises(pa.PAError) as e:                  # batch above capacity
+            plan.plan(np.array([0, 1, 2, 3], np.int32))
+        assert e.value.status == pa.PA_ERR_CAPACITY
+        with pytest.raises(pa.PAError) as e:                  # tokens above capacity
+            plan.plan(np.array([0, 20, 31], np.int32))
+        assert e.value.status == pa.PA_ERR_CAPACITY
+        plan.plan(ip)
+        with pytest.raises(pa.PAError) as e:                  # decode plan, prefill run
+            plan.prefill(q, k, v, idx_dev, 0.1, out)
+        assert e.value.status == pa.PA_ERR_PLAN_MISMATCH
+        qflat = torch.empty(q.numel() + 8, dtype=torch.bfloat16, device=dev)
+        q_mis = qflat[1:1 + q.numel()].view(q.shape)          # 2-byte misaligned
+        with pytest.raises(pa.PAError) as e:
+            plan.decode(q_mis, k, v, idx_dev, 0.1, out)
+        assert e.value.status == pa.PA_ERR_INVALID_ARG
+        with pytest.raises(pa.PAError) as e:
+            plan.decode(q, k, v, idx_dev, float("nan"), out)
+        assert e.value.status == pa.PA_ERR_INVALID_ARG
+        with pytest.raises(pa.PAError) as e:
+            plan.decode(q, k, v, idx_dev, 0.1, out, slot_stride=100)
+        assert e.value.status == pa.PA_ERR_INVALID_ARG
+        plan.decode(q, k, v, idx_dev, 0.1, out)                # still usable
+        torch.cuda.synchronize()
+
+
+def test_profile_events():
+    import paged_gqa_decode_pa_amd as pa
+    say("kernel timing events")
+    dev = device()
+    ip, idx, q, k, v = _case([2000] * 8, 32, 8, 128, 20000, seed=26)
+    idx_dev = torch.as_tensor(idx, device=dev)
+    out = torch.empty((8, 32, 128), dtype=torch.float32, device=dev)
+    with pa.Plan(8, int(ip[-1]), 32, 8, 128) as plan:
+        plan.plan(ip)
+        pa.pa_profile_begin(plan.handle, 4)
+        for _ in range(6):
+            plan.decode(q, k, v, idx_dev, 0.1, out)
+        ms, n = pa.pa_profile_end(plan.handle)
+    assert n == 4 and ms > 0

@@ -1,0 +1,195 @@
+"""Host partitioner (pa_partition): coverage, partial/merge bookkeeping, XCD
+placement and determinism.  The partition is one of many valid ones, so the
+tests check what every valid partition must satisfy."""
+from collections import defaultdict
+
+import numpy as np
+import pytest
+
+import paged_gqa_decode_pa_amd as pa
+import workloads as W
+
+XCD = 8
+
+
+def _indptr(lengths):
+    ip = np.zeros(len(lengths) + 1, np.int32)
+    ip[1:] = np.cumsum(lengths)
+    return ip
+
+
+def check_decode(units, merges, n_partials, indptr, Hkv, forced=None):
+    B = indptr.size - 1
+    real = units[units["request"] >= 0]
+    assert np.all(units[units["request"] < 0]["partial"] == -1)
+    by_stream = defaultdict(list)
+    for u in real:
+        b, h = int(u["request"]), int(u["kv_head"])
+        assert 0 <= b < B and 0 <= h < Hkv
+        assert indptr[b] <= u["kv_begin"] <= u["kv_end"] <= indptr[b + 1]
+        assert (u["q_begin"], u["q_end"]) == (b, b + 1)
+        assert u["diag"] == u["kv_end"] - 1
+        by_stream[(b, h)].append(u)
+    assert set(by_stream) == {(b, h) for b in range(B) for h in range(Hkv)}
+    seen_partials = []
+    merge_of = {(int(m["request"]), int(m["kv_head"])): m for m in merges}
+    assert len(merge_of) == len(merges)
+    for (b, h), us in by_stream.items():
+        us = sorted(us, key=lambda u: (u["kv_begin"], u["kv_end"]))
+        # the parts tile the request's list exactly, in order, without overlap
+        pos = indptr[b]
+        for u in us:
+            assert u["kv_begin"] == pos
+            pos = u["kv_end"]
+        assert pos == indptr[b + 1]
+        if forced:
+            assert len(us) == forced
+            sizes = [u["kv_end"] - u["kv_begin"] for u in us]
+            assert max(sizes) - min(sizes) <= 1
+        if len(us) == 1:
+            assert us[0]["partial"] == -1 and (b, h) not in merge_of
+        else:
+            parts = [int(u["partial"]) for u in us]
+            assert min(parts) >= 0
+            m = merge_of[(b, h)]
+            assert m["n_parts"] == len(us)
+            assert sorted(parts) == list(range(m["first_partial"], m["first_partial"] + len(us)))
+            assert (m["q_begin"], m["q_end"]) == (b, b + 1)
+            seen_partials += parts
+    assert sorted(seen_partials) == list(range(n_partials))
+
+
+@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("Hq,Hkv,D", [(32, 8, 128), (16, 4, 256), (8, 8, 128), (64, 8, 256)])
+def test_decode_partition_random(seed, Hq, Hkv, D):
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 40))
+    lengths = rng.integers(0, 3000, size=B)
+    lengths[rng.random(B) < 0.2] = 0
+    ip = _indptr(lengths)
+    for flags in (0, pa.PA_PLAN_NO_XCD_ORDER):
+        units, merges, n_p = pa.pa_partition(ip, None, Hq, Hkv, D, flags)
+        check_decode(units, merges, n_p, ip, Hkv)
+        if flags & pa.PA_PLAN_NO_XCD_ORDER:
+            assert np.all(units["request"] >= 0)
+        else:
+            assert units.size % XCD == 0
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 7, 64, 256])
+def test_forced_splits(n):
+    ip = _indptr([0, 1, 5, 100, 333])
+    units, merges, n_p = pa.pa_partition(ip, None, 32, 8, 128, pa.PA_PLAN_FORCE_SPLITS(n))
+    check_decode(units, merges, n_p, ip, 8, forced=n)
+
+
+def test_forced_split_limit():
+    ip = _indptr([10])
+    with pytest.raises(pa.PAError) as e:
+        pa.pa_partition(ip, None, 32, 8, 128, pa.PA_PLAN_FORCE_SPLITS(257))
+    assert e.value.status == pa.PA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("bad", [[1, 5], [0, 5, 3], [0, -1]])
+def test_bad_indptr(bad):
+    with pytest.raises(pa.PAError) as e:
+        pa.pa_partition(np.array(bad, np.int32), None, 32, 8, 128)
+    assert e.value.status == pa.PA_ERR_INVALID_ARG
+
+
+def test_unknown_flag():
+    with pytest.raises(pa.PAError):
+        pa.pa_partition(_indptr([5]), None, 32, 8, 128, 0x4)
+
+
+def test_deterministic():
+    ip, _ = W.decode_lists(W.BATCH64_SHARED_PREFIX)
+    a = pa.pa_partition(ip, None, 32, 8, 128)
+    b = pa.pa_partition(ip, None, 32, 8, 128)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]) and a[2] == b[2]
+
+
+def test_batch64_partition_shape():
+    """The batch-64 shared-prefix workload: parts are aligned to the same list
+    positions in every request, clusters stay on one XCD, XCD loads balance."""
+    ip, _ = W.decode_lists(W.BATCH64_SHARED_PREFIX)
+    units, merges, n_p = pa.pa_partition(ip, None, 32, 8, 128)
+    check_decode(units, merges, n_p, ip, 8)
+    real = units[units["request"] >= 0]
+    starts = real["kv_begin"] - ip[real["request"]]
+    S = int(np.max(real["kv_end"] - real["kv_begin"]))
+    assert S % 64 == 0 and np.all(starts % S == 0)
+    # the launch holds several workgroups per CU
+    assert real.size >= 256 * 4
+    xcd = np.nonzero(units["request"] >= 0)[0] % XCD
+    cluster = (starts // S) * 1000 + real["kv_head"] * 100 + real["request"] // 16
+    for c in np.unique(cluster):
+        assert np.unique(xcd[cluster == c]).size == 1
+    tokens = np.bincount(xcd, weights=real["kv_end"] - real["kv_begin"], minlength=XCD)
+    assert tokens.max() <= tokens.min() * 1.1 + S * 16
+
+
+def check_prefill(units, merges, n_p, qo, ip, Hkv, group):
+    B = ip.size - 1
+    real = units[units["request"] >= 0]
+    tiles = defaultdict(list)
+    for u in real:
+        tiles[(int(u["request"]), int(u["kv_head"]), int(u["q_begin"]), int(u["q_end"]))].append(u)
+    qt = 128 // group
+    want = set()
+    for b in range(B):
+        C = qo[b + 1] - qo[b]
+        for h in range(Hkv):
+            for t0 in range(0, C, qt):
+                want.add((b, h, qo[b] + t0, qo[b] + min(C, t0 + qt)))
+    assert set(tiles) == want
+    merge_of = {(int(m["request"]), int(m["kv_head"]), int(m["q_begin"])): m for m in merges}
+    all_parts = []
+    for (b, h, q0, q1), us in tiles.items():
+        L = ip[b + 1] - ip[b]
+        C = qo[b + 1] - qo[b]
+        P = L - C
+        t0, t1 = q0 - qo[b], q1 - qo[b]
+        us = sorted(us, key=lambda u: u["kv_begin"])
+        pos = ip[b]
+        for u in us:
+            assert u["kv_begin"] == pos and u["diag"] == ip[b] + P + t0
+            pos = u["kv_end"]
+        assert pos == ip[b] + P + t1  # ends at the last row's causal window
+        if len(us) > 1:
+            m = merge_of[(b, h, q0)]
+            parts = sorted(int(u["partial"]) for u in us)
+            assert parts == list(range(m["first_partial"], m["first_partial"] + len(us)))
+            all_parts += parts
+        else:
+            assert us[0]["partial"] == -1
+    assert sorted(all_parts) == list(range(n_p))
+
+
+@pytest.mark.parametrize("spec", W.PREFILL_SPECS, ids=lambda s: s.name)
+def test_prefill_partition_workloads(spec):
+    qo, ip, _ = W.prefill_lists(spec)
+    units, merges, n_p = pa.pa_partition(ip, qo, spec.num_qo_heads, spec.num_kv_heads, spec.head_dim)
+    check_prefill(units, merges, n_p, qo, ip, spec.num_kv_heads, spec.num_qo_heads // spec.num_kv_heads)
+    real = units[units["request"] >= 0]
+    assert real.size >= 256
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_prefill_partition_random(seed):
+    rng = np.random.default_rng(100 + seed)
+    B = int(rng.integers(1, 6))
+    chunks = rng.integers(0, 300, size=B)
+    cached = rng.integers(0, 2000, size=B)
+    ip = _indptr(chunks + cached)
+    qo = _indptr(chunks)
+    for Hq, Hkv in ((32, 8), (8, 8), (16, 2)):
+        for flags in (0, pa.PA_PLAN_FORCE_SPLITS(3)):
+            units, merges, n_p = pa.pa_partition(ip, qo, Hq, Hkv, 128, flags)
+            check_prefill(units, merges, n_p, qo, ip, Hkv, Hq // Hkv)
+
+
+def test_prefill_chunk_longer_than_list():
+    with pytest.raises(pa.PAError) as e:
+        pa.pa_partition(_indptr([5]), _indptr([6]), 32, 8, 128)
+    assert e.value.status == pa.PA_ERR_INVALID_ARG
