@@ -88,7 +88,10 @@ typedef enum pa_status {
 #define PA_PLAN_FORCE_SPLITS_MASK (0xffffu << PA_PLAN_FORCE_SPLITS_SHIFT)
 /* Cut every request's KV list (per KV head) into exactly n parts (1 <= n <=
  * PA_MAX_FORCED_SPLITS), instead of the automatic split.  Parts may be empty.
- * Used to test that the result does not depend on the partition. */
+ * Used to test that the result does not depend on the partition.  Forced parts
+ * count against the plan's capacity: a plan holds at least
+ * num_kv_heads * (max_batch + max_kv_total / 256) work units, and pa_plan
+ * returns PA_ERR_CAPACITY when batch * n exceeds max_batch + max_kv_total/256. */
 #define PA_PLAN_FORCE_SPLITS(n) (((uint32_t)(n) & 0xffffu) << PA_PLAN_FORCE_SPLITS_SHIFT)
 #define PA_MAX_FORCED_SPLITS 256
 /* Keep the automatic split but do not reorder work for per-XCD cache locality. */

@@ -32,7 +32,9 @@ def run_decode(q, k_pool, v_pool, kv_indptr, kv_indices_dev, sm_scale, num_kv_he
     kv_total = int(kv_indptr[-1])
     out = torch.full((B, Hq, D), float("nan"), dtype=torch.float32, device=q.device)
     lse = torch.full((B, Hq), float("nan"), dtype=torch.float32, device=q.device) if with_lse else None
-    with pa.Plan(max(B, 1), max(kv_total, 1), Hq, num_kv_heads, D) as plan:
+    forced = (flags >> pa.PA_PLAN_FORCE_SPLITS_SHIFT) & 0xFFFF
+    capacity = max(kv_total, 1, B * forced * 256)   # room for the forced parts
+    with pa.Plan(max(B, 1), capacity, Hq, num_kv_heads, D) as plan:
         plan.plan(kv_indptr, flags=flags)
         plan.decode(q, k_pool, v_pool, kv_indices_dev, sm_scale, out, lse,
                     slot_stride=slot_stride, num_slots=num_slots)

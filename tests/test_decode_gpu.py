@@ -132,10 +132,10 @@ def test_single_token_is_exact():
 
 
 def _slot_tag_pool(num_slots, Hkv, D, dev):
-    """V rows whose first three values spell the slot id in base 256 (exact in bf16)."""
+    """V rows whose first four values spell the slot id in base 256 (exact in bf16)."""
     v = torch.zeros((num_slots, Hkv, D), dtype=torch.bfloat16, device=dev)
     ids = torch.arange(num_slots, device=dev, dtype=torch.int64)
-    for digit in range(3):
+    for digit in range(4):
         v[:, :, digit] = ((ids >> (8 * digit)) & 255).to(torch.bfloat16)[:, None]
     return v
 
@@ -156,10 +156,10 @@ def test_slot_tags_bit_exact(num_slots, Hq, Hkv, D):
     k = torch.zeros_like(v)
     q = W.normal_bf16((B, Hq, D), 5, dev)
     out, _ = run_decode(q, k, v, ip, torch.as_tensor(chosen, device=dev), W.softmax_scale(D), Hkv)
-    digits = np.rint(out[:, :, :3]).astype(np.int64)
-    decoded = digits[..., 0] + 256 * digits[..., 1] + 65536 * digits[..., 2]
+    digits = np.rint(out[:, :, :4]).astype(np.int64)
+    decoded = digits[..., 0] + 256 * digits[..., 1] + 65536 * digits[..., 2] + 16777216 * digits[..., 3]
     assert np.array_equal(decoded, np.repeat(chosen[:, None], Hq, axis=1))
-    assert np.array_equal(out[:, :, :3], digits.astype(np.float32))
+    assert np.array_equal(out[:, :, :4], digits.astype(np.float32))
     del v, k
     torch.cuda.empty_cache()
 

@@ -193,3 +193,13 @@ def test_prefill_chunk_longer_than_list():
     with pytest.raises(pa.PAError) as e:
         pa.pa_partition(_indptr([5]), _indptr([6]), 32, 8, 128)
     assert e.value.status == pa.PA_ERR_INVALID_ARG
+
+
+def test_forced_splits_capacity_guarantee():
+    """The documented capacity: Hkv * (max_batch + max_kv_total / 256) units."""
+    from paged_gqa_decode_pa_amd import pa_partition
+    ip = _indptr([10, 20, 30])
+    n = 50
+    units, merges, n_p = pa_partition(ip, None, 32, 8, 128, pa.PA_PLAN_FORCE_SPLITS(n))
+    assert n_p == 3 * 8 * n
+    assert n_p <= 8 * (3 + (3 * n * 256) // 256)
