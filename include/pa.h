@@ -88,13 +88,15 @@ typedef enum pa_status {
 #define PA_PLAN_FORCE_SPLITS_MASK (0xffffu << PA_PLAN_FORCE_SPLITS_SHIFT)
 /* Cut every request's KV list (per KV head) into exactly n parts (1 <= n <=
  * PA_MAX_FORCED_SPLITS), instead of the automatic split.  Parts may be empty.
- * Used to test that the result does not depend on the partition.  Forced parts
- * count against the plan's capacity: a plan holds at least
- * num_kv_heads * (max_batch + max_kv_total / 256) work units, and pa_plan
- * returns PA_ERR_CAPACITY when batch * n exceeds max_batch + max_kv_total/256. */
+ * Used to test that the result does not depend on the partition.  Each part
+ * is then a workgroup of its own.  Forced parts count against the plan's
+ * capacity: a plan holds at least num_kv_heads * (max_batch + max_kv_total /
+ * 256) work units, and pa_plan returns PA_ERR_CAPACITY when batch * n exceeds
+ * max_batch + max_kv_total / 256. */
 #define PA_PLAN_FORCE_SPLITS(n) (((uint32_t)(n) & 0xffffu) << PA_PLAN_FORCE_SPLITS_SHIFT)
 #define PA_MAX_FORCED_SPLITS 256
-/* Keep the automatic split but do not reorder work for per-XCD cache locality. */
+/* Keep the automatic split but place workgroups in plain order instead of
+ * grouping neighbouring requests on one XCD. */
 #define PA_PLAN_NO_XCD_ORDER 0x1u
 
 /*
@@ -137,9 +139,10 @@ pa_status pa_plan(pa_plan_t *plan, const int32_t *kv_indptr_host,
  *   kv_indices int32 device array with kv_indptr[batch] entries;
  *   sm_scale: softmax scale (e.g. 1/sqrt(D) as a float);
  *   out [batch, Hq, D] fp32; lse [batch, Hq] fp32 or NULL.
- * Requests whose lists were split write partial results into the plan's
- * workspace and a merge kernel combines them; so two runs of one plan must
- * not execute concurrently (runs on one stream are fine).
+ * One kernel launch.  Where a list was split, each part writes a partial
+ * result into the plan's workspace and counts its arrival; the part that
+ * arrives last merges them and resets the count.  So two runs of one plan
+ * must not execute concurrently (runs on one stream are fine).
  */
 pa_status pa_decode_run(const pa_plan_t *plan, const void *q, const void *k_pool,
                         const void *v_pool, int64_t num_slots, int64_t slot_stride,
@@ -171,14 +174,19 @@ const char *pa_last_error_detail(void);
 /*
  * Host-only inspection of the partition (no GPU needed).
  *
- * pa_work_unit is one workgroup's share of a plan, as the kernels read it:
- * KV head kv_head of request `request`, list entries [kv_begin, kv_end)
- * (absolute offsets into kv_indices), query rows [q_begin, q_end) (prefill;
- * decode: q_begin = request, q_end = request + 1), and where the result goes:
- * partial < 0 writes the final output, partial >= 0 writes partial slot
- * `partial`, later merged.  Units with request < 0 are padding and do nothing.
+ * A plan is a list of workgroups; workgroup w processes the work units
+ * units[wg_offsets[w] .. wg_offsets[w+1]) one after the other.  Workgroup w is
+ * launched as workgroup id w, which the hardware places on XCD w % 8.
+ *
+ * pa_work_unit is one piece of work as the kernels read it: KV head kv_head of
+ * request `request`, list entries [kv_begin, kv_end) (absolute offsets into
+ * kv_indices), query rows [q_begin, q_end) (prefill; decode: q_begin =
+ * request, q_end = request + 1), and where the result goes: partial < 0 writes
+ * the final output, partial >= 0 writes partial slot `partial`, later merged.
  * diag (prefill): query row q_begin + r sees list entries up to offset
  * diag + r inclusive (the causal window); decode units set diag = kv_end - 1.
+ * merge: index of the pa_merge_unit that combines this unit's partial with
+ * the other parts of its range (-1 when partial < 0).
  *
  * pa_merge_unit: the partial slots [first_partial, first_partial + n_parts)
  * that make up query rows [q_begin, q_end) of KV head kv_head.
@@ -192,6 +200,10 @@ typedef struct pa_work_unit {
     int32_t q_end;
     int32_t partial;
     int32_t diag;
+    int32_t merge;
+    int32_t reserved0;
+    int32_t reserved1;
+    int32_t reserved2;
 } pa_work_unit;
 
 typedef struct pa_merge_unit {
@@ -207,16 +219,21 @@ typedef struct pa_merge_unit {
 
 /*
  * pa_partition: compute the partition pa_plan would upload, into host arrays.
- *   Arguments as in pa_plan_create / pa_plan.  units[unit_capacity] and
- *   merges[merge_capacity] receive the work and merge lists; *n_units,
- *   *n_merges and *n_partials receive their lengths.  PA_ERR_CAPACITY if an
- *   array is too small (the counts are still written).
+ *   Arguments as in pa_plan_create / pa_plan; max_workgroups is the number of
+ *   decode workgroups the GPU holds at once (pa_plan uses the kernel's
+ *   occupancy times the compute-unit count; <= 0 here means 768, three per
+ *   compute unit of an MI355X).
+ *   wg_offsets[wg_capacity], units[unit_capacity] and merges[merge_capacity]
+ *   receive the lists; *n_workgroups, *n_units, *n_merges and *n_partials their
+ *   lengths (wg_offsets holds *n_workgroups + 1 entries).  PA_ERR_CAPACITY if
+ *   an array is too small (the counts are still written).
  */
 pa_status pa_partition(const int32_t *kv_indptr_host, const int32_t *qo_indptr_host,
                        int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,
-                       int32_t head_dim, uint32_t flags, pa_work_unit *units,
-                       int32_t unit_capacity, pa_merge_unit *merges,
-                       int32_t merge_capacity, int32_t *n_units, int32_t *n_merges,
+                       int32_t head_dim, uint32_t flags, int32_t max_workgroups,
+                       int32_t *wg_offsets, int32_t wg_capacity, pa_work_unit *units,
+                       int32_t unit_capacity, pa_merge_unit *merges, int32_t merge_capacity,
+                       int32_t *n_workgroups, int32_t *n_units, int32_t *n_merges,
                        int32_t *n_partials);
 
 /*

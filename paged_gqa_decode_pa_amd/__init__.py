@@ -39,7 +39,8 @@ def PA_PLAN_FORCE_SPLITS(n: int) -> int:
 
 class pa_work_unit(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
-                ("request", "kv_head", "kv_begin", "kv_end", "q_begin", "q_end", "partial", "diag")]
+                ("request", "kv_head", "kv_begin", "kv_end", "q_begin", "q_end", "partial", "diag",
+                 "merge", "reserved0", "reserved1", "reserved2")]
 
 
 class pa_merge_unit(ctypes.Structure):
@@ -83,9 +84,9 @@ def _load() -> ctypes.CDLL:
     lib.pa_last_error_detail.restype = ctypes.c_char_p
     lib.pa_version.argtypes = []
     lib.pa_version.restype = i32
-    lib.pa_partition.argtypes = [i32p, i32p, i32, i32, i32, i32, u32,
+    lib.pa_partition.argtypes = [i32p, i32p, i32, i32, i32, i32, u32, i32, i32p, i32,
                                  ctypes.POINTER(pa_work_unit), i32,
-                                 ctypes.POINTER(pa_merge_unit), i32, i32p, i32p, i32p]
+                                 ctypes.POINTER(pa_merge_unit), i32, i32p, i32p, i32p, i32p]
     lib.pa_partition.restype = ctypes.c_int
     lib.pa_profile_begin.argtypes = [vp, i32]
     lib.pa_profile_begin.restype = ctypes.c_int
@@ -210,25 +211,29 @@ def pa_plan_destroy(plan) -> None:
 
 
 def pa_partition(kv_indptr, qo_indptr, num_qo_heads: int, num_kv_heads: int, head_dim: int,
-                 flags: int = 0):
-    """Host-only: the partition pa_plan would upload -> (units, merges, n_partials)."""
+                 flags: int = 0, max_workgroups: int = 0):
+    """Host-only: the partition pa_plan would upload.
+
+    Returns (wg_offsets int32 [n_workgroups + 1], units, merges, n_partials);
+    workgroup w runs units[wg_offsets[w]:wg_offsets[w + 1]].
+    """
     kv = _host_i32(kv_indptr)
     qo = _host_i32(qo_indptr)
-    n_u, n_m, n_p = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    n_w, n_u, n_m, n_p = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    counts = (ctypes.byref(n_w), ctypes.byref(n_u), ctypes.byref(n_m), ctypes.byref(n_p))
     st = _lib.pa_partition(_i32p(kv), _i32p(qo), kv.size - 1, num_qo_heads, num_kv_heads,
-                           head_dim, flags, None, 0, None, 0,
-                           ctypes.byref(n_u), ctypes.byref(n_m), ctypes.byref(n_p))
+                           head_dim, flags, max_workgroups, None, 0, None, 0, None, 0, *counts)
     if st not in (PA_OK, PA_ERR_CAPACITY):
         _check(st, "pa_partition")
+    offs = np.zeros(n_w.value + 1, np.int32)
     units = (pa_work_unit * max(1, n_u.value))()
     merges = (pa_merge_unit * max(1, n_m.value))()
     _check(_lib.pa_partition(_i32p(kv), _i32p(qo), kv.size - 1, num_qo_heads, num_kv_heads,
-                             head_dim, flags, units, n_u.value, merges, n_m.value,
-                             ctypes.byref(n_u), ctypes.byref(n_m), ctypes.byref(n_p)),
-           "pa_partition")
+                             head_dim, flags, max_workgroups, _i32p(offs), offs.size,
+                             units, n_u.value, merges, n_m.value, *counts), "pa_partition")
     u = np.frombuffer(bytes(units), dtype=WORK_UNIT_DTYPE)[: n_u.value].copy()
     m = np.frombuffer(bytes(merges), dtype=MERGE_UNIT_DTYPE)[: n_m.value].copy()
-    return u, m, n_p.value
+    return offs, u, m, n_p.value
 
 
 def pa_profile_begin(plan, capacity: int) -> None:

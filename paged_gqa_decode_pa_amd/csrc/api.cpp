@@ -23,12 +23,15 @@ struct pa_plan {
     int32_t max_q_total = 0;
     int32_t num_qo_heads = 0, num_kv_heads = 0, head_dim = 0, group = 0;
     int32_t num_cu = pa::kNumCu, num_xcd = pa::kNumXcd;
-    int64_t unit_cap = 0, merge_cap = 0, partial_rows_cap = 0;
-    // device: [units | merges] packed by the last pa_plan, and partial storage
+    int32_t max_workgroups = 0;  // decode workgroups resident at once
+    int64_t wg_cap = 0, unit_cap = 0, merge_cap = 0, partial_rows_cap = 0;
+    // device: [workgroup offsets | units | merges] packed by the last pa_plan,
+    // and partial storage
     void *d_table = nullptr;
     float *d_part_o = nullptr;
     float *d_part_lse = nullptr;
-    // pinned staging, two alternating buffers of (unit_cap + merge_cap) entries
+    int32_t *d_arrivals = nullptr;  // per merge unit, zero between launches
+    // pinned staging, two alternating buffers holding a whole table
     void *h_stage[2] = {nullptr, nullptr};
     hipEvent_t stage_done[2] = {nullptr, nullptr};
     bool stage_pending[2] = {false, false};
@@ -38,7 +41,7 @@ struct pa_plan {
     int32_t batch = 0;
     int64_t kv_total = 0;
     int32_t q_total = 0;
-    int32_t n_units = 0, n_merges = 0, n_partials = 0;
+    int32_t n_workgroups = 0, n_units = 0, n_merges = 0, n_partials = 0;
     // kernel timing: event pairs recorded around the attention kernel
     std::vector<hipEvent_t> prof_events;   // 2 per pair
     mutable int32_t prof_used = 0;
@@ -61,8 +64,19 @@ pa_status hip_fail(hipError_t e, const char *what) {
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-constexpr size_t kEntry = sizeof(pa_work_unit);
-static_assert(sizeof(pa_work_unit) == 32 && sizeof(pa_merge_unit) == 32, "32-byte entries");
+constexpr size_t kUnit = sizeof(pa_work_unit);
+constexpr size_t kMerge = sizeof(pa_merge_unit);
+static_assert(kUnit == 48 && kMerge == 32, "table entry sizes");
+
+// Bytes of the workgroup-offset block of a table with n_workgroups
+// workgroups (n + 1 offsets, rounded up to 64 bytes).
+size_t offsets_bytes(int64_t n_workgroups) {
+    return (size_t)((n_workgroups + 1 + 15) / 16) * 64;
+}
+
+size_t table_bytes(const pa_plan_t *p) {
+    return offsets_bytes(p->wg_cap) + (size_t)p->unit_cap * kUnit + (size_t)p->merge_cap * kMerge;
+}
 
 void drop_profile(pa_plan_t *p) {
     for (hipEvent_t e : p->prof_events)
@@ -101,6 +115,8 @@ void release(pa_plan_t *p) {
         (void)hipFree(p->d_part_o);
     if (p->d_part_lse)
         (void)hipFree(p->d_part_lse);
+    if (p->d_arrivals)
+        (void)hipFree(p->d_arrivals);
     delete p;
 }
 
@@ -143,10 +159,14 @@ pa_status prepare_run(const pa_plan_t *p, pa::PlanMode want, const void *q, cons
     if (!std::isfinite(sm_scale))
         return fail(PA_ERR_INVALID_ARG, "sm_scale is not finite");
     const char *tbl = static_cast<const char *>(p->d_table);
-    l->units = reinterpret_cast<const pa_work_unit *>(tbl);
+    const size_t off_b = offsets_bytes(p->n_workgroups);
+    l->wg_offsets = reinterpret_cast<const int32_t *>(tbl);
+    l->n_workgroups = p->n_workgroups;
+    l->units = reinterpret_cast<const pa_work_unit *>(tbl + off_b);
     l->n_units = p->n_units;
-    l->merges = reinterpret_cast<const pa_merge_unit *>(tbl + (size_t)p->n_units * kEntry);
+    l->merges = reinterpret_cast<const pa_merge_unit *>(tbl + off_b + (size_t)p->n_units * kUnit);
     l->n_merges = p->n_merges;
+    l->arrivals = p->d_arrivals;
     l->q = q;
     l->k_pool = k_pool;
     l->v_pool = v_pool;
@@ -186,19 +206,26 @@ int32_t pa_version(void) { return 100; }
 
 pa_status pa_partition(const int32_t *kv_indptr_host, const int32_t *qo_indptr_host,
                        int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,
-                       int32_t head_dim, uint32_t flags, pa_work_unit *units,
+                       int32_t head_dim, uint32_t flags, int32_t max_workgroups,
+                       int32_t *wg_offsets, int32_t wg_capacity, pa_work_unit *units,
                        int32_t unit_capacity, pa_merge_unit *merges, int32_t merge_capacity,
-                       int32_t *n_units, int32_t *n_merges, int32_t *n_partials) {
-    if (!n_units || !n_merges || !n_partials)
+                       int32_t *n_workgroups, int32_t *n_units, int32_t *n_merges,
+                       int32_t *n_partials) {
+    if (!n_workgroups || !n_units || !n_merges || !n_partials)
         return fail(PA_ERR_INVALID_ARG, "count pointers must not be null");
-    if ((unit_capacity > 0 && !units) || (merge_capacity > 0 && !merges) || unit_capacity < 0 ||
+    if ((wg_capacity > 0 && !wg_offsets) || (unit_capacity > 0 && !units) ||
+        (merge_capacity > 0 && !merges) || wg_capacity < 0 || unit_capacity < 0 ||
         merge_capacity < 0)
         return fail(PA_ERR_INVALID_ARG, "bad output arrays");
+    if (max_workgroups <= 0)
+        max_workgroups = pa::kNumCu * pa::kDefaultWorkgroupsPerCu;
     pa::PartitionArgs a{kv_indptr_host, qo_indptr_host, batch, num_qo_heads, num_kv_heads,
-                        head_dim, flags, pa::kNumCu, pa::kNumXcd};
+                        head_dim, flags, max_workgroups, pa::kNumXcd};
     pa::PartitionResult r;
     const char *detail = "";
-    pa_status s = pa::partition(a, units, unit_capacity, merges, merge_capacity, &r, &detail);
+    pa_status s = pa::partition(a, wg_offsets, wg_capacity, units, unit_capacity, merges,
+                                merge_capacity, &r, &detail);
+    *n_workgroups = r.n_workgroups;
     *n_units = r.n_units;
     *n_merges = r.n_merges;
     *n_partials = r.n_partials;
@@ -240,24 +267,32 @@ pa_status pa_plan_create(pa_plan_t **out, int32_t max_batch, int64_t max_kv_tota
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, p->device) == hipSuccess &&
         cus > 0)
         p->num_cu = cus;
+    int per_cu = pa::decode_workgroups_per_cu(head_dim, p->group);
+    if (per_cu <= 0)
+        per_cu = pa::kDefaultWorkgroupsPerCu;
+    p->max_workgroups = p->num_cu * per_cu;
     pa::partition_capacity(max_batch, max_kv_total, max_q_total, num_qo_heads, num_kv_heads,
-                           head_dim, p->num_xcd, &p->unit_cap, &p->merge_cap,
-                           &p->partial_rows_cap);
-    // the capacity bound assumes kNumCu compute units for prefill splitting
-    if (p->num_cu > pa::kNumCu)
-        p->unit_cap = p->unit_cap * p->num_cu / pa::kNumCu + 1;
-    const size_t table_bytes = (size_t)(p->unit_cap + p->merge_cap) * kEntry;
+                           head_dim, p->max_workgroups, p->num_xcd, &p->wg_cap, &p->unit_cap,
+                           &p->merge_cap, &p->partial_rows_cap);
+    const size_t tbytes = table_bytes(p);
     const size_t part_o_bytes = (size_t)std::max<int64_t>(1, p->partial_rows_cap) * head_dim * sizeof(float);
     const size_t part_lse_bytes = (size_t)std::max<int64_t>(1, p->partial_rows_cap) * sizeof(float);
-    if ((e = hipMalloc(&p->d_table, std::max<size_t>(table_bytes, kEntry))) != hipSuccess ||
+    const size_t arrivals_bytes = (size_t)std::max<int64_t>(1, p->merge_cap) * sizeof(int32_t);
+    if ((e = hipMalloc(&p->d_table, tbytes)) != hipSuccess ||
         (e = hipMalloc((void **)&p->d_part_o, part_o_bytes)) != hipSuccess ||
-        (e = hipMalloc((void **)&p->d_part_lse, part_lse_bytes)) != hipSuccess) {
+        (e = hipMalloc((void **)&p->d_part_lse, part_lse_bytes)) != hipSuccess ||
+        (e = hipMalloc((void **)&p->d_arrivals, arrivals_bytes)) != hipSuccess) {
         release(p);
         return hip_fail(e, "hipMalloc (plan workspace)");
     }
+    // arrival counts start at zero; every launch leaves them at zero again
+    if ((e = hipMemset(p->d_arrivals, 0, arrivals_bytes)) != hipSuccess ||
+        (e = hipDeviceSynchronize()) != hipSuccess) {
+        release(p);
+        return hip_fail(e, "clearing the arrival counts");
+    }
     for (int i = 0; i < 2; i++) {
-        if ((e = hipHostMalloc(&p->h_stage[i], std::max<size_t>(table_bytes, kEntry),
-                               hipHostMallocDefault)) != hipSuccess ||
+        if ((e = hipHostMalloc(&p->h_stage[i], tbytes, hipHostMallocDefault)) != hipSuccess ||
             (e = hipEventCreateWithFlags(&p->stage_done[i], hipEventDisableTiming)) != hipSuccess) {
             release(p);
             return hip_fail(e, "pinned staging / event");
@@ -301,38 +336,43 @@ pa_status pa_plan(pa_plan_t *p, const int32_t *kv_indptr_host, const int32_t *qo
             return hip_fail(e, "waiting for an earlier plan upload");
         p->stage_pending[s] = false;
     }
+    // partition straight into the staging buffer at capacity offsets, then
+    // pack the three lists together and upload them with one copy
     char *stage = static_cast<char *>(p->h_stage[s]);
-    pa_work_unit *units = reinterpret_cast<pa_work_unit *>(stage);
-    pa_merge_unit *merges = reinterpret_cast<pa_merge_unit *>(stage + (size_t)p->unit_cap * kEntry);
+    int32_t *offsets = reinterpret_cast<int32_t *>(stage);
+    const size_t units_at = offsets_bytes(p->wg_cap);
+    pa_work_unit *units = reinterpret_cast<pa_work_unit *>(stage + units_at);
+    pa_merge_unit *merges = reinterpret_cast<pa_merge_unit *>(stage + units_at + (size_t)p->unit_cap * kUnit);
     pa::PartitionArgs a{kv_indptr_host, qo_indptr_host, batch, p->num_qo_heads, p->num_kv_heads,
-                        p->head_dim, flags, p->num_cu, p->num_xcd};
+                        p->head_dim, flags, p->max_workgroups, p->num_xcd};
     pa::PartitionResult r;
     const char *detail = "";
-    pa_status st = pa::partition(a, units, (int32_t)std::min<int64_t>(p->unit_cap, 0x7fffffff),
-                                 merges, (int32_t)std::min<int64_t>(p->merge_cap, 0x7fffffff),
-                                 &r, &detail);
+    auto clamp32 = [](int64_t v) { return (int32_t)std::min<int64_t>(v, 0x7fffffff); };
+    pa_status st = pa::partition(a, offsets, clamp32(p->wg_cap + 1), units, clamp32(p->unit_cap),
+                                 merges, clamp32(p->merge_cap), &r, &detail);
     if (st != PA_OK)
         return fail(st, detail);
     const int64_t rows_per_slot = qo_indptr_host ? pa::kPrefillTileRows : p->group;
     if ((int64_t)r.n_partials * rows_per_slot > p->partial_rows_cap)
         return fail(PA_ERR_CAPACITY, "partial storage of the plan exceeded");
-    // pack merges right after the units, upload both with one copy
+    const size_t off_b = offsets_bytes(r.n_workgroups);
+    if (r.n_units > 0)
+        std::memmove(stage + off_b, units, (size_t)r.n_units * kUnit);
     if (r.n_merges > 0)
-        std::memmove(stage + (size_t)r.n_units * kEntry, merges, (size_t)r.n_merges * kEntry);
-    const size_t bytes = (size_t)(r.n_units + r.n_merges) * kEntry;
-    if (bytes > 0) {
-        if ((e = hipMemcpyAsync(p->d_table, stage, bytes, hipMemcpyHostToDevice,
-                                (hipStream_t)stream)) != hipSuccess)
-            return hip_fail(e, "plan upload");
-        if ((e = hipEventRecord(p->stage_done[s], (hipStream_t)stream)) != hipSuccess)
-            return hip_fail(e, "plan upload event");
-        p->stage_pending[s] = true;
-    }
+        std::memmove(stage + off_b + (size_t)r.n_units * kUnit, merges, (size_t)r.n_merges * kMerge);
+    const size_t bytes = off_b + (size_t)r.n_units * kUnit + (size_t)r.n_merges * kMerge;
+    if ((e = hipMemcpyAsync(p->d_table, stage, bytes, hipMemcpyHostToDevice,
+                            (hipStream_t)stream)) != hipSuccess)
+        return hip_fail(e, "plan upload");
+    if ((e = hipEventRecord(p->stage_done[s], (hipStream_t)stream)) != hipSuccess)
+        return hip_fail(e, "plan upload event");
+    p->stage_pending[s] = true;
     p->next_stage = s ^ 1;
     p->mode = qo_indptr_host ? pa::PlanMode::kPrefill : pa::PlanMode::kDecode;
     p->batch = batch;
     p->kv_total = kv_total;
     p->q_total = q_total;
+    p->n_workgroups = r.n_workgroups;
     p->n_units = r.n_units;
     p->n_merges = r.n_merges;
     p->n_partials = r.n_partials;
@@ -355,9 +395,6 @@ pa_status pa_decode_run(const pa_plan_t *p, const void *q, const void *k_pool, c
         return hip_fail((hipError_t)rc, "decode kernel launch");
     if ((e = profile_mark(p, (hipStream_t)stream, true)) != hipSuccess)
         return hip_fail(e, "profile event");
-    rc = pa::launch_merge(l, stream);
-    if (rc != 0)
-        return hip_fail((hipError_t)rc, "merge kernel launch");
     return PA_OK;
 }
 

@@ -10,16 +10,19 @@
 //     s = <q, k> * scale * log2(e);  p = exp2(s - m);  o = sum p v / sum p
 // which gives the same result as exp(<q,k>*scale - m') with m' = m * ln 2.
 //
-// Lane layout of the decode kernel (one workgroup = 4 waves = one work unit:
-// one request, one KV head, a contiguous part of its slot list):
+// Lane layout of the decode kernel (one workgroup = 4 waves; it runs the work
+// units of its list one after another, each unit being one request, one KV
+// head and a contiguous part of its slot list):
 //   * a K or V row of one head is D bf16 = D*2 bytes; LPR = D/8 lanes load it
 //     with one 16-byte load each (lane chunk c = lane % LPR holds elements
 //     8c..8c+7), so one wave-wide load instruction fetches RPI = 64/LPR whole
 //     rows (4 rows at D = 128, 2 at D = 256): fully coalesced 128-bit loads,
 //     each lane gathering through its own slot id;
 //   * a wave walks the unit in tiles of NI instructions (NI*RPI tokens); the
-//     four waves take every fourth tile; the next tile's slot ids and K/V rows
-//     are loaded while the current one is computed;
+//     four waves take every fourth tile; the next tile's K rows are requested
+//     as soon as the current scores are done with the K registers and its V
+//     rows once the current weighted sum is done with the V registers, so half
+//     a tile is always in flight without a second register set;
 //   * each K row is used by all G query heads of its group straight from the
 //     registers it was loaded into (dot2 bf16 products, fp32 accumulation);
 //     the partial dot products are reduced across the row's lanes with DPP
@@ -32,7 +35,15 @@
 //   * V rows accumulate into fp32 o[G][8] per lane; at the end the rows of a
 //     wave are combined with cross-lane shuffles, then the four waves through
 //     LDS, and the unit writes either the final output or a partial result
-//     (normalised o and its log2-sum-exp) for the merge kernel.
+//     (normalised o and its log2-sum-exp);
+//   * a unit that wrote a partial counts its arrival on its merge unit; the
+//     unit that arrives last merges the parts by log-sum-exp weights, writes
+//     the final output and resets the count to zero for the next launch.
+//     Partials are stored and loaded with agent-scope atomic accesses, which
+//     are coherent across the XCDs' separate L2s, and every store has
+//     completed (vmcnt 0) before the arrival is counted.  Agent-scope fences
+//     would do the same job through whole-L2 writeback and invalidation,
+//     which measured 2.5x slower.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -71,6 +82,17 @@ constexpr int kRowRor4 = 0x124;   // row_ror:4
 constexpr int kRowRor8 = 0x128;   // row_ror:8 (== lane ^ 8 within a row)
 
 __device__ __forceinline__ float shfl_xor(float x, int mask) { return __shfl_xor(x, mask, 64); }
+
+// Agent-scope (all XCDs) coherent 32-bit accesses.
+__device__ __forceinline__ void store_coherent(float *p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float *p) {
+    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until every vector memory access this wave issued has completed
+// (s_waitcnt vmcnt(0); expcnt and lgkmcnt left free).
+__device__ __forceinline__ void wait_vector_memory() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Hardware base-2 exponential and logarithm (v_exp_f32 / v_log_f32):
 // exp2(-inf) = 0, exp2(0) = 1.
@@ -160,8 +182,10 @@ struct Geometry {
     static constexpr int TILE = NI * RPI;      // tokens per wave tile
 };
 
-// Byte offset of a pool row: 32-bit form (pool below 4 GiB, slot ids and
-// stride below 2^24) or 64-bit form.
+// Byte offset of a pool row: 32-bit form or 64-bit form.  The 32-bit form
+// is only used when every row offset is below 2^31: the compiler widens the
+// 24-bit product with a sign extension, so offsets of 2 GiB and more must
+// take the 64-bit form.
 template <bool WIDE>
 struct RowAddr;
 template <>
@@ -181,16 +205,64 @@ struct RowAddr<true> {
     }
 };
 
-template <int D, int NI>
-struct TileRegs {
-    int32_t slot[NI];
-    uint4 k[NI];
-    uint4 v[NI];
-};
+// Log-sum-exp merge of one merge unit: partial slots [first, first+n) of
+// query rows [q_begin, q_end) of one KV head.  Each slot holds rows_per_slot
+// rows of D floats (row = (q - q_begin)*G + h) and their log2-sum-exp values.
+// Threads tid, tid+nthreads, ... of the caller each produce output elements.
+// COHERENT: read the partials with agent-scope coherent loads (partials
+// written by other workgroups of the running kernel).
+template <int D, int G, bool COHERENT>
+__device__ __forceinline__ void merge_rows(const pa_merge_unit &mu, const float *__restrict__ part_o,
+                                           const float *__restrict__ part_lse, int32_t rows_per_slot,
+                                           float *__restrict__ out, float *__restrict__ lse,
+                                           int32_t num_qo_heads, int tid, int nthreads) {
+    const int32_t rows = (mu.q_end - mu.q_begin) * G;
+    for (int32_t idx = tid; idx < rows * D; idx += nthreads) {
+        const int32_t row = idx / D, d = idx % D;
+        float M = -INFINITY;
+
+        for (int32_t i = 0; i < mu.n_parts; i++) {
+            const float *pl = part_lse + (int64_t)(mu.first_partial + i) * rows_per_slot + row;
+            M = fmaxf(M, COHERENT ? load_coherent(pl) : *pl);
+        }
+        const int32_t qtok = mu.q_begin + row / G, h = mu.kv_head * G + row % G;
+        const int64_t orow = (int64_t)qtok * num_qo_heads + h;
+        if (M == -INFINITY) {
+            out[orow * D + d] = 0.f;
+            if (lse && d == 0)
+                lse[orow] = -INFINITY;
+            continue;
+        }
+        float o = 0.f, wsum = 0.f;
+
+        for (int32_t i = 0; i < mu.n_parts; i++) {
+            const int64_t slot_row = (int64_t)(mu.first_partial + i) * rows_per_slot + row;
+            const float l2 = COHERENT ? load_coherent(part_lse + slot_row) : part_lse[slot_row];
+            const float po = COHERENT ? load_coherent(part_o + slot_row * D + d) : part_o[slot_row * D + d];
+            const float w = fast_exp2(l2 - M);
+            o = fmaf(w, po, o);
+            wsum += w;
+        }
+        out[orow * D + d] = o / wsum;
+        if (lse && d == 0)
+            lse[orow] = (M + fast_log2(wsum)) * kLn2;
+    }
+}
+
+// Waves per SIMD the decode kernel is compiled for: three (at most 168
+// VGPRs, room for the rotating K/V registers without spills) for groups of up
+// to four query heads, two for groups of eight.
+template <int G>
+constexpr int decode_waves_per_simd() {
+    return G <= 4 ? 3 : 2;
+}
 
 template <int D, int G, bool WIDE>
-__global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
-    const pa_work_unit *__restrict__ units, const uint16_t *__restrict__ q, const char *__restrict__ k_pool,
+__global__ __launch_bounds__(kDecodeThreads)
+__attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<G>(), 8))) void decode_kernel(
+    const int32_t *__restrict__ wg_offsets, const pa_work_unit *__restrict__ units,
+    const pa_merge_unit *__restrict__ merges, int32_t *__restrict__ arrivals,
+    const uint16_t *__restrict__ q, const char *__restrict__ k_pool,
     const char *__restrict__ v_pool, uint32_t stride_bytes,
     const int32_t *__restrict__ kv_indices, float scale_log2, float *__restrict__ out,
     float *__restrict__ lse, float *__restrict__ part_o, float *__restrict__ part_lse,
@@ -202,10 +274,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     __shared__ float lds_o[WAVES][G][D];
     __shared__ float lds_m[WAVES][G];
     __shared__ float lds_l[WAVES][G];
+    __shared__ int32_t lds_arrived;
 
-    const pa_work_unit unit = units[blockIdx.x];
+    const int32_t unit_begin = wg_offsets[blockIdx.x], unit_end = wg_offsets[blockIdx.x + 1];
+    for (int32_t ui = unit_begin; ui < unit_end; ui++) {
+    const pa_work_unit unit = units[ui];
     if (unit.request < 0)
-        return;  // padding unit (uniform over the workgroup)
+        continue;  // padding unit (uniform over the workgroup)
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -237,40 +312,45 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
         for (int e = 0; e < 8; e++)
             acc[h][e] = 0.f;
 
-    auto load_slots = [&](TileRegs<D, NI> &t, int tile) {
+    auto load_slots = [&](int32_t(&slot)[NI], int tile) {
         const int32_t base = kv_begin + tile * TILE + r;
 #pragma unroll
         for (int i = 0; i < NI; i++) {
             int32_t tok = base + i * RPI;
             tok = tok < kv_end ? tok : kv_end - 1;
-            t.slot[i] = kv_indices[tok];
+            slot[i] = kv_indices[tok];
         }
     };
-    auto load_rows = [&](TileRegs<D, NI> &t) {
+    auto load_k = [&](uint4(&k)[NI], const int32_t(&slot)[NI]) {
 #pragma unroll
         for (int i = 0; i < NI; i++)
-            t.k[i] = *RowAddr<WIDE>::at(k_pool, t.slot[i], stride_bytes, lane_off);
-#pragma unroll
-        for (int i = 0; i < NI; i++)
-            t.v[i] = *RowAddr<WIDE>::at(v_pool, t.slot[i], stride_bytes, lane_off);
+            k[i] = *RowAddr<WIDE>::at(k_pool, slot[i], stride_bytes, lane_off);
     };
-    auto compute = [&](const TileRegs<D, NI> &t, int tile) {
+    auto load_v = [&](uint4(&v)[NI], const int32_t(&slot)[NI]) {
+#pragma unroll
+        for (int i = 0; i < NI; i++)
+            v[i] = *RowAddr<WIDE>::at(v_pool, slot[i], stride_bytes, lane_off);
+    };
+    // scores of this lane's head (lane % G) for the tile's tokens, log2 domain
+    auto qk = [&](const uint4(&k)[NI], float(&s)[NI], int tile) {
         const int32_t base = kv_begin + tile * TILE + r;
-        float s[NI];
 #pragma unroll
         for (int i = 0; i < NI; i++) {
             float part[G];
 #pragma unroll
             for (int h = 0; h < G; h++) {
-                float a = dot2_bf16(qv[h][0], t.k[i].x, 0.f);
-                a = dot2_bf16(qv[h][1], t.k[i].y, a);
-                a = dot2_bf16(qv[h][2], t.k[i].z, a);
-                a = dot2_bf16(qv[h][3], t.k[i].w, a);
+                float a = dot2_bf16(qv[h][0], k[i].x, 0.f);
+                a = dot2_bf16(qv[h][1], k[i].y, a);
+                a = dot2_bf16(qv[h][2], k[i].z, a);
+                a = dot2_bf16(qv[h][3], k[i].w, a);
                 part[h] = a;
             }
-            float sc = row_reduce_transposed<G, LPR>(part, lane) * scale_log2;
+            const float sc = row_reduce_transposed<G, LPR>(part, lane) * scale_log2;
             s[i] = (base + i * RPI < kv_end) ? sc : -INFINITY;
         }
+    };
+    // online softmax: scores -> weights, running max / sum, accumulator rescale
+    auto softmax = [&](const float(&s)[NI], float(&p)[NI]) {
         float tmax = s[0];
 #pragma unroll
         for (int i = 1; i < NI; i++)
@@ -289,19 +369,20 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
                     acc[h][e] *= ah;
             }
         }
-        float p[NI];
 #pragma unroll
         for (int i = 0; i < NI; i++) {
             p[i] = fast_exp2(s[i] - m_run);
             l_run += p[i];
         }
+    };
+    auto pv = [&](const uint4(&v)[NI], const float(&p)[NI]) {
 #pragma unroll
         for (int i = 0; i < NI; i++) {
             float vf[8];
-            vf[0] = bf16_lo(t.v[i].x); vf[1] = bf16_hi(t.v[i].x);
-            vf[2] = bf16_lo(t.v[i].y); vf[3] = bf16_hi(t.v[i].y);
-            vf[4] = bf16_lo(t.v[i].z); vf[5] = bf16_hi(t.v[i].z);
-            vf[6] = bf16_lo(t.v[i].w); vf[7] = bf16_hi(t.v[i].w);
+            vf[0] = bf16_lo(v[i].x); vf[1] = bf16_hi(v[i].x);
+            vf[2] = bf16_lo(v[i].y); vf[3] = bf16_hi(v[i].y);
+            vf[4] = bf16_lo(v[i].z); vf[5] = bf16_hi(v[i].z);
+            vf[6] = bf16_lo(v[i].w); vf[7] = bf16_hi(v[i].w);
 #pragma unroll
             for (int h = 0; h < G; h++) {
                 const float ph = group_bcast<G>(p[i], h, lane);
@@ -312,38 +393,37 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
         }
     };
 
-    // Tiles wave, wave+4, wave+8, ...: two register sets alternate so the
-    // next tile's rows are in flight while the current one is computed.
+    // Tiles wave, wave+4, wave+8, ...  Loads are issued in the order
+    //   S(i) K(i) V(i) S(i+1) | K(i+1) V(i+1) S(i+2) | ...
+    // (S = slot ids): the next tile's K rows are requested as soon as this
+    // tile's scores have consumed the K registers, and its V rows once the
+    // weighted sum has consumed the V registers, so one half of a tile is
+    // always in flight while the other half is computed, without a second
+    // register set.
     int tile = wave;
     if (tile < n_tiles) {
-        TileRegs<D, NI> ta, tb;
-        load_slots(ta, tile);
-        load_rows(ta);
-        if (tile + WAVES < n_tiles)
-            load_slots(tb, tile + WAVES);
+        int32_t slot[NI];
+        uint4 kr[NI], vr[NI];
+        load_slots(slot, tile);
+        load_k(kr, slot);
+        load_v(vr, slot);
+        bool more = tile + WAVES < n_tiles;
+        if (more)
+            load_slots(slot, tile + WAVES);
         while (true) {
-            // ta holds tile `tile` (rows in flight); tb holds the next tile's slots
-            const bool has_b = tile + WAVES < n_tiles;
-            if (has_b) {
-                load_rows(tb);
-                if (tile + 2 * WAVES < n_tiles)
-                    load_slots(ta, tile + 2 * WAVES);  // slots only; ta's rows consumed below first
-            }
-            // ta.slot may have been overwritten above, but compute() reads only ta.k / ta.v
-            compute(ta, tile);
-            tile += WAVES;
-            if (!has_b)
+            float sc[NI], pw[NI];
+            qk(kr, sc, tile);
+            if (more)
+                load_k(kr, slot);
+            softmax(sc, pw);
+            pv(vr, pw);
+            if (!more)
                 break;
-            const bool has_a = tile + WAVES < n_tiles;
-            if (has_a) {
-                load_rows(ta);
-                if (tile + 2 * WAVES < n_tiles)
-                    load_slots(tb, tile + 2 * WAVES);
-            }
-            compute(tb, tile);
+            load_v(vr, slot);
             tile += WAVES;
-            if (!has_a)
-                break;
+            more = tile + WAVES < n_tiles;
+            if (more)
+                load_slots(slot, tile + WAVES);
         }
     }
 
@@ -406,66 +486,69 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
             if (lse && d == 0)
                 lse[qrow0 + h] = lse2 * kLn2;
         } else {
-            part_o[((int64_t)unit.partial * G + h) * D + d] = res;
+            store_coherent(part_o + ((int64_t)unit.partial * G + h) * D + d, res);
             if (d == 0)
-                part_lse[(int64_t)unit.partial * G + h] = lse2;
+                store_coherent(part_lse + (int64_t)unit.partial * G + h, lse2);
         }
+    }
+    if (unit.partial >= 0) {
+        // count this part once its stores have completed; the last to arrive merges
+        wait_vector_memory();
+        __syncthreads();
+        if (tid == 0)
+            lds_arrived = __hip_atomic_fetch_add(arrivals + unit.merge, 1, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        const pa_merge_unit mu = merges[unit.merge];
+        if (lds_arrived == mu.n_parts - 1) {
+            merge_rows<D, G, true>(mu, part_o, part_lse, G, out, lse, num_qo_heads, tid, kDecodeThreads);
+            if (tid == 0)
+                __hip_atomic_store(arrivals + unit.merge, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    if (ui + 1 < unit_end)
+        __syncthreads();  // the next unit rewrites the LDS just read
     }
 }
 
-// Merge unit: partial slots [first, first+n) of query rows [q_begin, q_end)
-// of one KV head.  Each slot holds R rows of D floats (row = (q - q_begin)*G + h)
-// and R log2-sum-exp values.
 template <int D, int G>
 __global__ __launch_bounds__(256) void merge_kernel(const pa_merge_unit *__restrict__ merges,
                                                     const float *__restrict__ part_o,
                                                     const float *__restrict__ part_lse,
                                                     int32_t rows_per_slot, float *__restrict__ out,
                                                     float *__restrict__ lse, int32_t num_qo_heads) {
-    const pa_merge_unit mu = merges[blockIdx.x];
-    const int32_t rows = (mu.q_end - mu.q_begin) * G;
-    for (int32_t idx = threadIdx.x; idx < rows * D; idx += blockDim.x) {
-        const int32_t row = idx / D, d = idx % D;
-        float M = -INFINITY;
-        for (int32_t i = 0; i < mu.n_parts; i++)
-            M = fmaxf(M, part_lse[(int64_t)(mu.first_partial + i) * rows_per_slot + row]);
-        const int32_t qtok = mu.q_begin + row / G, h = mu.kv_head * G + row % G;
-        const int64_t orow = (int64_t)qtok * num_qo_heads + h;
-        if (M == -INFINITY) {
-            out[orow * D + d] = 0.f;
-            if (lse && d == 0)
-                lse[orow] = -INFINITY;
-            continue;
-        }
-        float o = 0.f, wsum = 0.f;
-        for (int32_t i = 0; i < mu.n_parts; i++) {
-            const int64_t slot_row = (int64_t)(mu.first_partial + i) * rows_per_slot + row;
-            const float w = fast_exp2(part_lse[slot_row] - M);
-            o = fmaf(w, part_o[slot_row * D + d], o);
-            wsum += w;
-        }
-        out[orow * D + d] = o / wsum;
-        if (lse && d == 0)
-            lse[orow] = (M + fast_log2(wsum)) * kLn2;
-    }
+    merge_rows<D, G, false>(merges[blockIdx.x], part_o, part_lse, rows_per_slot, out, lse, num_qo_heads,
+                            threadIdx.x, blockDim.x);
 }
+
+}  // namespace
+
+bool row_offsets_fit_32(int64_t num_slots, uint32_t stride_bytes) {
+    // largest offset: (num_slots - 1) * stride + (row start within the slot
+    // + 16-byte chunk), all below num_slots * stride
+    const uint64_t span = (uint64_t)num_slots * stride_bytes;
+    return span <= 0x80000000ull && num_slots <= (1 << 24) && stride_bytes < (1u << 24);
+}
+
+namespace {
 
 template <int D, int G>
 int launch_decode_dg(const DecodeLaunch &l, hipStream_t stream) {
     const uint32_t stride_bytes = (uint32_t)(l.slot_stride * 2);
-    // the 32-bit row address needs every byte offset below 4 GiB and
-    // operands of the 24-bit multiply below 2^24
-    const uint64_t span = (uint64_t)l.num_slots * stride_bytes;
-    const bool wide = span > 0xFFFF0000ull || l.num_slots > (1 << 24) || stride_bytes >= (1u << 24);
+    // the 32-bit row address needs every byte offset below 2^31 (it is
+    // sign-extended into the address) and 24-bit multiply operands
+    const bool wide = !row_offsets_fit_32(l.num_slots, stride_bytes);
     const float scale_log2 = l.sm_scale * kLog2e;
-    dim3 grid(l.n_units), block(kDecodeThreads);
+    dim3 grid(l.n_workgroups), block(kDecodeThreads);
     if (wide)
-        hipLaunchKernelGGL((decode_kernel<D, G, true>), grid, block, 0, stream, l.units,
+        hipLaunchKernelGGL((decode_kernel<D, G, true>), grid, block, 0, stream, l.wg_offsets, l.units,
+                           l.merges, l.arrivals,
                            (const uint16_t *)l.q, (const char *)l.k_pool, (const char *)l.v_pool,
                            stride_bytes, l.kv_indices, scale_log2, l.out, l.lse, l.partial_o,
                            l.partial_lse, l.num_qo_heads);
     else
-        hipLaunchKernelGGL((decode_kernel<D, G, false>), grid, block, 0, stream, l.units,
+        hipLaunchKernelGGL((decode_kernel<D, G, false>), grid, block, 0, stream, l.wg_offsets, l.units,
+                           l.merges, l.arrivals,
                            (const uint16_t *)l.q, (const char *)l.k_pool, (const char *)l.v_pool,
                            stride_bytes, l.kv_indices, scale_log2, l.out, l.lse, l.partial_o,
                            l.partial_lse, l.num_qo_heads);
@@ -479,10 +562,38 @@ int launch_merge_dg(const DecodeLaunch &l, int32_t rows_per_slot, hipStream_t st
     return (int)hipGetLastError();
 }
 
+template <int D, int G>
+int occupancy_dg() {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<D, G, false>, kDecodeThreads, 0) !=
+        hipSuccess)
+        return 0;
+    return n;
+}
+
 }  // namespace
 
+int decode_workgroups_per_cu(int32_t head_dim, int32_t group) {
+    if (head_dim == 128) {
+        switch (group) {
+        case 1: return occupancy_dg<128, 1>();
+        case 2: return occupancy_dg<128, 2>();
+        case 4: return occupancy_dg<128, 4>();
+        case 8: return occupancy_dg<128, 8>();
+        }
+    } else if (head_dim == 256) {
+        switch (group) {
+        case 1: return occupancy_dg<256, 1>();
+        case 2: return occupancy_dg<256, 2>();
+        case 4: return occupancy_dg<256, 4>();
+        case 8: return occupancy_dg<256, 8>();
+        }
+    }
+    return 0;
+}
+
 int launch_decode(const DecodeLaunch &l, void *stream) {
-    if (l.n_units == 0)
+    if (l.n_workgroups == 0)
         return 0;
     hipStream_t s = (hipStream_t)stream;
     const int G = l.num_qo_heads / l.num_kv_heads;

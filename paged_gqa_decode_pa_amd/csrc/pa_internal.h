@@ -22,10 +22,16 @@ constexpr int kTileTokens = 16;
 // Work units hold a multiple of this many tokens (one tile per wave).
 constexpr int kUnitGranule = kDecodeWaves * kTileTokens;
 
-// Automatic split: aim for about this many workgroups per compute unit over
-// the launch, with units of at least this many bytes of K+V.
-constexpr int kTargetUnitsPerCu = 8;
+// Automatic decode split: as many workgroups as the GPU holds at once, each
+// with an equal share of the list entries, never less than kMinUnitBytes of
+// K+V per workgroup.  A piece costs about kPieceOverheadTokens tokens of
+// work beyond its list entries (state setup, the end-of-piece combine and
+// its partial write); pieces are not cut shorter than kMinPieceTokens.
 constexpr int64_t kMinUnitBytes = 128 * 1024;
+constexpr int kPieceOverheadTokens = 128;
+constexpr int kMinPieceTokens = 64;
+// Workgroups per compute unit assumed when the occupancy is not known.
+constexpr int kDefaultWorkgroupsPerCu = 3;
 
 // Prefill kernel geometry (rows of one query tile = chunk tokens x group).
 constexpr int kPrefillTileRows = 128;
@@ -40,35 +46,39 @@ struct PartitionArgs {
     int32_t num_kv_heads;
     int32_t head_dim;
     uint32_t flags;
-    int32_t num_cu;
+    int32_t max_workgroups;  // decode workgroups resident at once
     int32_t num_xcd;
 };
 
 struct PartitionResult {
-    int32_t n_units = 0;     // including padding units
+    int32_t n_workgroups = 0;  // including empty padding workgroups
+    int32_t n_units = 0;
     int32_t n_merges = 0;
-    int32_t n_partials = 0;  // partial slots used
-    int32_t unit_tokens = 0; // automatic split length (tokens per unit), 0 if forced
+    int32_t n_partials = 0;    // partial slots used
 };
 
-// Validates the arguments; fills units/merges up to the capacities.  Returns
-// PA_ERR_CAPACITY (with the counts filled) if a capacity is too small.
-pa_status partition(const PartitionArgs &a, pa_work_unit *units, int32_t unit_capacity,
-                    pa_merge_unit *merges, int32_t merge_capacity, PartitionResult *res,
-                    const char **detail);
+// Validates the arguments; fills wg_offsets (n_workgroups + 1 entries), units
+// and merges up to the capacities.  Returns PA_ERR_CAPACITY (with the counts
+// filled) if a capacity is too small.
+pa_status partition(const PartitionArgs &a, int32_t *wg_offsets, int32_t wg_capacity,
+                    pa_work_unit *units, int32_t unit_capacity, pa_merge_unit *merges,
+                    int32_t merge_capacity, PartitionResult *res, const char **detail);
 
-// Upper bounds on what a plan created with these limits can need: work and
-// merge units, and partial storage in rows of head_dim floats (a decode
-// partial slot holds `group` rows, a prefill slot kPrefillTileRows rows).
+// Upper bounds on what a plan created with these limits can need: workgroup
+// offsets (entries), work and merge units, and partial storage in rows of
+// head_dim floats (a decode partial slot holds `group` rows, a prefill slot
+// kPrefillTileRows rows).
 void partition_capacity(int32_t max_batch, int64_t max_kv_total, int32_t max_q_total,
                         int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
-                        int32_t num_xcd, int64_t *max_units, int64_t *max_merges,
-                        int64_t *max_partial_rows);
+                        int32_t max_workgroups, int32_t num_xcd, int64_t *max_wg_entries,
+                        int64_t *max_units, int64_t *max_merges, int64_t *max_partial_rows);
 
 bool supported_shape(int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim);
 
 // Kernel launchers (decode.hip / prefill.hip).  All asynchronous on `stream`.
 struct DecodeLaunch {
+    const int32_t *wg_offsets;      // device, n_workgroups + 1 entries
+    int32_t n_workgroups;
     const pa_work_unit *units;      // device
     int32_t n_units;
     const pa_merge_unit *merges;    // device
@@ -84,12 +94,18 @@ struct DecodeLaunch {
     float *lse;                     // may be null
     float *partial_o;               // decode: [slots, group, D]; prefill: [slots, tile rows, D]
     float *partial_lse;             // decode: [slots, group];    prefill: [slots, tile rows]
+    int32_t *arrivals;              // per merge unit: parts finished in this launch (zero between launches)
     int32_t num_qo_heads;
     int32_t num_kv_heads;
     int32_t head_dim;
 };
 
 int launch_decode(const DecodeLaunch &l, void *stream);   // returns hipError_t
+// Whether a pool of num_slots slots of stride_bytes bytes can be addressed
+// with 32-bit row offsets (every offset below 2^31).
+bool row_offsets_fit_32(int64_t num_slots, uint32_t stride_bytes);
+// Decode workgroups one compute unit holds at once (0 if unknown).
+int decode_workgroups_per_cu(int32_t head_dim, int32_t group);
 int launch_merge(const DecodeLaunch &l, void *stream);
 int launch_prefill(const DecodeLaunch &l, void *stream);
 

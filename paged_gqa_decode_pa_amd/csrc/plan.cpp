@@ -5,30 +5,30 @@
 // "分页 KV 缓存", and stage 3 of the table in "优化历程").  How the work is cut
 // is not on the pages; this file's policy is:
 //
-// Decode.  The work of request b is Hkv independent streams (one per KV head)
-// of L_b tokens.  A work unit is one workgroup: one (request, KV head) and a
-// contiguous part of the list.  Parts have a fixed length S for the whole
-// step, so part j of every request covers list positions [j*S, (j+1)*S) --
-// requests that share a prompt prefix (radix prefix cache, Agent-Infer page,
-// section "前缀缓存") read the same slots in their part-0 units.  S is chosen
-// so the launch holds about kTargetUnitsPerCu workgroups per compute unit,
-// never below kMinUnitBytes of K+V per unit, rounded to kUnitGranule tokens.
-// A request cut into n > 1 parts writes n partial results that a merge unit
-// combines by log-sum-exp weights.
+// Decode (automatic).  The work of request b is Hkv independent streams
+// ("segments", one per KV head) of L_b list entries.  The launch holds exactly
+// as many workgroups as the GPU keeps resident at once (kernel occupancy x
+// compute units), so every workgroup starts at time zero and none waits for a
+// free slot; each gets an equal budget of list entries (plus a fixed cost per
+// piece of work it handles).  Segments are taken in (KV head, request) order:
+// the first piece of segment i opens workgroup i, so requests that sit next to
+// each other in the batch -- those that share a prompt prefix under a radix
+// prefix cache (Agent-Infer page, section "前缀缓存") -- read their common
+// leading slots at the same moment; the rest of every segment is then streamed
+// over the workgroups in order, cut where a workgroup's budget ends.  A
+// workgroup runs its pieces one after another.  A segment cut into n > 1
+// pieces writes n partial results that a merge unit combines by log-sum-exp
+// weights.  Workgroups are laid out in contiguous blocks per XCD (workgroup id
+// w runs on XCD w % 8, each XCD with its own L2), so neighbouring segments
+// share an L2.
 //
-// Prefill.  A unit is one (request, KV head, tile of chunk rows); the tile
-// stacks the group's query heads so it holds kPrefillTileRows rows.  The KV
-// range of a tile ends at the causal window of its last row.  When there are
-// too few tiles to fill the GPU, the KV range is also cut into parts and
-// merged the same way.
-//
-// XCD order.  Workgroup i runs on XCD i % 8 and each XCD has its own L2.  Units
-// are grouped into clusters (same part, same KV head, 16 consecutive
-// requests), clusters are spread over the XCDs to balance tokens (largest
-// first onto the least loaded XCD), and each XCD's queue is turned into
-// workgroup ids x, x+8, x+16, ...  Units of one cluster therefore run close in
-// time on one XCD, where reads of shared slots can hit its L2.  Queues are
-// padded to equal length with empty units.
+// Decode with forced splits, and prefill.  One unit per workgroup.  Prefill
+// units are (request, KV head, tile of chunk rows); the tile stacks the
+// group's query heads so it holds kPrefillTileRows rows, and its KV range ends
+// at the causal window of its last row.  When the tiles alone cannot fill the
+// GPU, KV ranges are also cut and merged.  Units are grouped into clusters
+// (same part, same KV head, 16 consecutive requests) that are spread over the
+// XCDs by token balance, largest first.
 #include <algorithm>
 #include <cstring>
 #include <numeric>
@@ -48,15 +48,17 @@ struct Unit {
     int64_t tokens;    // list entries the unit reads (for balance)
 };
 
+using Groups = std::vector<std::vector<pa_work_unit>>;  // workgroup id -> its units
+
 int32_t forced_splits(uint32_t flags) {
     return (int32_t)((flags & PA_PLAN_FORCE_SPLITS_MASK) >> PA_PLAN_FORCE_SPLITS_SHIFT);
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Place units on XCD queues and return them in workgroup-id order (with
-// padding units).  `units` are in the natural (request, head, part) order.
-std::vector<pa_work_unit> xcd_order(const std::vector<Unit> &units, int num_xcd) {
+// One unit per workgroup: place units on XCD queues by cluster and return the
+// workgroups in id order (empty workgroups pad the queues to equal depth).
+Groups xcd_order_single(const std::vector<Unit> &units, int num_xcd) {
     if (units.empty())
         return {};
     struct Cluster {
@@ -64,7 +66,6 @@ std::vector<pa_work_unit> xcd_order(const std::vector<Unit> &units, int num_xcd)
         std::vector<int32_t> members;
         int32_t part, head, block;
     };
-    // cluster key: (part, head, request block)
     std::vector<int32_t> order(units.size());
     std::iota(order.begin(), order.end(), 0);
     auto key = [&](int32_t i) {
@@ -88,7 +89,6 @@ std::vector<pa_work_unit> xcd_order(const std::vector<Unit> &units, int num_xcd)
         clusters.back().tokens += std::max<int64_t>(x.tokens, 1);
         clusters.back().members.push_back(i);
     }
-    // largest cluster first onto the least loaded XCD (ties: lower XCD)
     std::vector<int32_t> corder(clusters.size());
     std::iota(corder.begin(), corder.end(), 0);
     std::stable_sort(corder.begin(), corder.end(), [&](int32_t a, int32_t b) {
@@ -105,14 +105,17 @@ std::vector<pa_work_unit> xcd_order(const std::vector<Unit> &units, int num_xcd)
     size_t depth = 0;
     for (auto &q : queue)
         depth = std::max(depth, q.size());
-    pa_work_unit pad;
-    std::memset(&pad, 0, sizeof pad);
-    pad.request = -1;
-    pad.partial = -1;
-    std::vector<pa_work_unit> out(depth * num_xcd, pad);
+    Groups out(depth * num_xcd);
     for (int x = 0; x < num_xcd; x++)
         for (size_t p = 0; p < queue[x].size(); p++)
-            out[p * num_xcd + x] = units[queue[x][p]].u;
+            out[p * num_xcd + x].push_back(units[queue[x][p]].u);
+    return out;
+}
+
+Groups plain_single(const std::vector<Unit> &units) {
+    Groups out(units.size());
+    for (size_t i = 0; i < units.size(); i++)
+        out[i].push_back(units[i].u);
     return out;
 }
 
@@ -120,6 +123,140 @@ pa_status fail(const char **detail, const char *msg, pa_status s) {
     if (detail)
         *detail = msg;
     return s;
+}
+
+int64_t min_unit_tokens(int32_t head_dim) {
+    // K and V rows of one head: 2 * head_dim bf16 values per token
+    return std::max<int64_t>(kUnitGranule, kMinUnitBytes / (4 * (int64_t)head_dim));
+}
+
+int32_t prefill_tile_tokens(int32_t group) { return kPrefillTileRows / group; }
+
+// ---------------------------------------------------------------------------
+// decode, automatic: balanced workgroup bins
+// ---------------------------------------------------------------------------
+void decode_bins(const PartitionArgs &a, Groups *groups, std::vector<pa_merge_unit> *merges,
+                 int32_t *n_partials) {
+    const int32_t B = a.batch, Hkv = a.num_kv_heads;
+    struct Piece {
+        int32_t seg, lo, hi;
+    };
+    const int64_t n_seg = (int64_t)B * Hkv;
+    auto seg_request = [&](int64_t s) { return (int32_t)(s % B); };
+    auto seg_head = [&](int64_t s) { return (int32_t)(s / B); };
+    auto seg_len = [&](int64_t s) {
+        int32_t b = seg_request(s);
+        return a.kv_indptr[b + 1] - a.kv_indptr[b];
+    };
+    const int64_t total = B > 0 ? (int64_t)a.kv_indptr[B] * Hkv : 0;
+    const int64_t max_wg = std::max(1, a.max_workgroups);
+    const int64_t n = std::max<int64_t>(1, std::min(max_wg, ceil_div(total, min_unit_tokens(a.head_dim))));
+    const double ov = kPieceOverheadTokens;
+    const double cap = ((double)total + ov * (double)(n_seg + n)) / (double)n;
+
+    std::vector<std::vector<Piece>> bins(n);
+    std::vector<double> fill(n, 0.0);
+    struct Rest {
+        int32_t seg, from;
+    };
+    std::vector<Rest> rest;
+    rest.reserve(n_seg);
+    // opening pieces: segment i starts workgroup i
+    for (int64_t s = 0; s < n_seg; s++) {
+        const int32_t L = seg_len(s);
+        if (s < n) {
+            const int32_t t = (int32_t)std::min<double>(L, std::max(0.0, cap - ov));
+            bins[s].push_back({(int32_t)s, 0, t});
+            fill[s] += t + ov;
+            if (L > t)
+                rest.push_back({(int32_t)s, t});
+        } else {
+            rest.push_back({(int32_t)s, 0});
+        }
+    }
+    // the rest streams over the workgroups in order
+    int64_t p = 0;
+    for (const Rest &r : rest) {
+        const int32_t L = seg_len(r.seg);
+        int32_t off = r.from;
+        if (L == 0) {  // an empty segment still writes its (empty) result
+            while (p < n - 1 && fill[p] + ov > cap)
+                p++;
+            bins[p].push_back({r.seg, 0, 0});
+            fill[p] += ov;
+            continue;
+        }
+        while (off < L) {
+            while (p < n - 1 && fill[p] + ov + kMinPieceTokens > cap)
+                p++;
+            int32_t take = L - off;
+            if (p < n - 1) {
+                take = std::min<int32_t>(take, (int32_t)(cap - fill[p] - ov));
+                if (L - off - take < kMinPieceTokens)
+                    take = L - off;  // no sliver left for another workgroup
+            }
+            bins[p].push_back({r.seg, off, off + take});
+            fill[p] += take + ov;
+            off += take;
+        }
+    }
+    // partial slots: contiguous per segment, in segment order
+    std::vector<int32_t> pieces_of(n_seg, 0);
+    for (auto &bin : bins)
+        for (const Piece &pc : bin)
+            pieces_of[pc.seg]++;
+    std::vector<int32_t> first(n_seg, -1), next(n_seg, 0);
+    int32_t np = 0;
+    for (int64_t s = 0; s < n_seg; s++) {
+        if (pieces_of[s] > 1) {
+            first[s] = np;
+            np += pieces_of[s];
+        }
+    }
+    *n_partials = np;
+    // merges in (request, head) order
+    std::vector<int32_t> merge_of(n_seg, -1);
+    for (int32_t b = 0; b < B; b++) {
+        for (int32_t h = 0; h < Hkv; h++) {
+            const int64_t s = (int64_t)h * B + b;
+            if (pieces_of[s] > 1) {
+                merge_of[s] = (int32_t)merges->size();
+                pa_merge_unit m;
+                std::memset(&m, 0, sizeof m);
+                m.request = b;
+                m.kv_head = h;
+                m.q_begin = b;
+                m.q_end = b + 1;
+                m.first_partial = first[s];
+                m.n_parts = pieces_of[s];
+                merges->push_back(m);
+            }
+        }
+    }
+    // workgroup ids: bins in contiguous blocks per XCD
+    const bool xcd = !(a.flags & PA_PLAN_NO_XCD_ORDER) && a.num_xcd > 1;
+    const int64_t per_xcd = xcd ? ceil_div(n, a.num_xcd) : n;
+    const int64_t n_wg = xcd ? per_xcd * a.num_xcd : n;
+    groups->assign(n_wg, {});
+    for (int64_t i = 0; i < n; i++) {
+        const int64_t wg = xcd ? (i % per_xcd) * a.num_xcd + i / per_xcd : i;
+        auto &g = (*groups)[wg];
+        for (const Piece &pc : bins[i]) {
+            pa_work_unit u;
+            const int32_t b = seg_request(pc.seg);
+            u.request = b;
+            u.kv_head = seg_head(pc.seg);
+            u.kv_begin = a.kv_indptr[b] + pc.lo;
+            u.kv_end = a.kv_indptr[b] + pc.hi;
+            u.q_begin = b;
+            u.q_end = b + 1;
+            u.partial = pieces_of[pc.seg] > 1 ? first[pc.seg] + next[pc.seg]++ : -1;
+            u.diag = u.kv_end - 1;
+            u.merge = merge_of[pc.seg];
+            u.reserved0 = u.reserved1 = u.reserved2 = 0;
+            g.push_back(u);
+        }
+    }
 }
 
 }  // namespace
@@ -133,41 +270,36 @@ bool supported_shape(int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_di
     return head_dim == 128 || head_dim == 256;
 }
 
-static int64_t min_unit_tokens(int32_t head_dim) {
-    // K and V rows of one head: 2 * head_dim bf16 values per token
-    return std::max<int64_t>(kUnitGranule, kMinUnitBytes / (4 * (int64_t)head_dim));
-}
-
-static int32_t prefill_tile_tokens(int32_t group) { return kPrefillTileRows / group; }
-
 void partition_capacity(int32_t max_batch, int64_t max_kv_total, int32_t max_q_total,
                         int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
-                        int32_t num_xcd, int64_t *max_units, int64_t *max_merges,
-                        int64_t *max_partial_rows) {
-    int32_t g = num_qo_heads / num_kv_heads;
-    // decode, automatic split: ceil(L/S) <= L/S + 1 with S >= the minimum
-    int64_t dec = (int64_t)num_kv_heads * (max_batch + ceil_div(max_kv_total, min_unit_tokens(head_dim)));
+                        int32_t max_workgroups, int32_t num_xcd, int64_t *max_wg_entries,
+                        int64_t *max_units, int64_t *max_merges, int64_t *max_partial_rows) {
+    const int32_t g = num_qo_heads / num_kv_heads;
+    const int64_t segs = (int64_t)num_kv_heads * max_batch;
+    // decode, automatic: an opening piece per segment, one more piece where a
+    // segment continues, one more per workgroup boundary
+    const int64_t dec_auto = 2 * segs + std::max(1, max_workgroups);
+    // decode, forced splits (documented guarantee)
+    const int64_t dec_forced = (int64_t)num_kv_heads * (max_batch + max_kv_total / 256);
+    const int64_t dec = std::max(dec_auto, dec_forced);
     // prefill: tiles, then at most ~4 units per CU after KV splitting
     int64_t tiles = 0, pre = 0;
     if (max_q_total > 0) {
-        int32_t qt = prefill_tile_tokens(g);
+        const int32_t qt = prefill_tile_tokens(g);
         tiles = (int64_t)num_kv_heads * (ceil_div(max_q_total, qt) + max_batch);
-        pre = std::max<int64_t>(tiles, 4LL * kNumCu + tiles);
+        pre = 4LL * kNumCu + tiles;
     }
-    int64_t units = std::max(dec, pre);
-    // padding to equal XCD queues can at worst multiply by the XCD count
-    *max_units = units * num_xcd;
-    *max_merges = std::max(dec, tiles);
-    // partial storage is counted in rows of head_dim floats: a decode partial
-    // slot holds the group's g rows, a prefill slot a whole tile
-    int64_t dec_rows = dec * g;
-    int64_t pre_rows = (max_q_total > 0) ? pre * kPrefillTileRows : 0;
-    *max_partial_rows = std::max(dec_rows, pre_rows);
+    *max_units = std::max(dec, pre);
+    // one-unit workgroups may be padded up to the XCD count times
+    *max_wg_entries = std::max<int64_t>(std::max(1, max_workgroups) + num_xcd,
+                                        std::max(dec_forced, pre) * num_xcd) + 1;
+    *max_merges = std::max(segs, tiles);
+    *max_partial_rows = std::max(dec * g, (max_q_total > 0) ? pre * kPrefillTileRows : 0);
 }
 
-pa_status partition(const PartitionArgs &a, pa_work_unit *units_out, int32_t unit_capacity,
-                    pa_merge_unit *merges_out, int32_t merge_capacity, PartitionResult *res,
-                    const char **detail) {
+pa_status partition(const PartitionArgs &a, int32_t *wg_offsets, int32_t wg_capacity,
+                    pa_work_unit *units_out, int32_t unit_capacity, pa_merge_unit *merges_out,
+                    int32_t merge_capacity, PartitionResult *res, const char **detail) {
     *res = PartitionResult{};
     if (a.batch < 0)
         return fail(detail, "batch < 0", PA_ERR_INVALID_ARG);
@@ -202,34 +334,22 @@ pa_status partition(const PartitionArgs &a, pa_work_unit *units_out, int32_t uni
         }
     }
 
-    std::vector<Unit> units;
+    Groups groups;
     std::vector<pa_merge_unit> merges;
     int32_t n_partials = 0;
+    const bool xcd = !(a.flags & PA_PLAN_NO_XCD_ORDER) && a.num_xcd > 1;
 
-    if (!prefill) {
-        int64_t S = 0;
-        if (!forced) {
-            int64_t total = a.batch > 0 ? a.kv_indptr[a.batch] : 0;
-            int64_t work = total * Hkv;
-            int64_t target = (int64_t)std::max(1, a.num_cu) * kTargetUnitsPerCu;
-            S = std::max(ceil_div(work, target), min_unit_tokens(a.head_dim));
-            S = ceil_div(S, kUnitGranule) * kUnitGranule;
-            res->unit_tokens = (int32_t)S;
-        }
+    if (!prefill && !forced) {
+        decode_bins(a, &groups, &merges, &n_partials);
+    } else if (!prefill) {
+        std::vector<Unit> units;
         for (int32_t b = 0; b < a.batch; b++) {
             const int32_t beg = a.kv_indptr[b], L = a.kv_indptr[b + 1] - a.kv_indptr[b];
-            const int32_t n = forced ? forced : (int32_t)std::max<int64_t>(1, ceil_div(L, S));
+            const int32_t n = forced;
             for (int32_t h = 0; h < Hkv; h++) {
-                int32_t first = n_partials;
+                const int32_t first = n_partials;
                 for (int32_t j = 0; j < n; j++) {
-                    int64_t lo, hi;
-                    if (forced) {
-                        lo = (int64_t)L * j / n;
-                        hi = (int64_t)L * (j + 1) / n;
-                    } else {
-                        lo = std::min<int64_t>(L, j * S);
-                        hi = std::min<int64_t>(L, (j + 1) * S);
-                    }
+                    const int64_t lo = (int64_t)L * j / n, hi = (int64_t)L * (j + 1) / n;
                     Unit x;
                     x.u.request = b;
                     x.u.kv_head = h;
@@ -239,6 +359,8 @@ pa_status partition(const PartitionArgs &a, pa_work_unit *units_out, int32_t uni
                     x.u.q_end = b + 1;
                     x.u.partial = n > 1 ? n_partials++ : -1;
                     x.u.diag = x.u.kv_end - 1;
+                    x.u.merge = n > 1 ? (int32_t)merges.size() : -1;
+                    x.u.reserved0 = x.u.reserved1 = x.u.reserved2 = 0;
                     x.part = j;
                     x.tokens = hi - lo;
                     units.push_back(x);
@@ -256,24 +378,25 @@ pa_status partition(const PartitionArgs &a, pa_work_unit *units_out, int32_t uni
                 }
             }
         }
+        groups = xcd ? xcd_order_single(units, a.num_xcd) : plain_single(units);
     } else {
         const int32_t qt = prefill_tile_tokens(g);
-        // tiles: (request, head, chunk-row tile)
         int64_t n_tiles = 0;
         for (int32_t b = 0; b < a.batch; b++)
             n_tiles += (int64_t)Hkv * ceil_div(a.qo_indptr[b + 1] - a.qo_indptr[b], qt);
         // cut KV ranges only when the tiles alone cannot fill the GPU
         int64_t part_len = 0;  // 0 = no cut
-        if (forced == 0 && n_tiles > 0 && n_tiles < 2LL * a.num_cu) {
+        if (forced == 0 && n_tiles > 0 && n_tiles < 2LL * kNumCu) {
             int64_t kv_work = 0;
             for (int32_t b = 0; b < a.batch; b++) {
-                int64_t C = a.qo_indptr[b + 1] - a.qo_indptr[b];
+                const int64_t C = a.qo_indptr[b + 1] - a.qo_indptr[b];
                 if (C > 0)
                     kv_work += (int64_t)Hkv * ceil_div(C, qt) * (a.kv_indptr[b + 1] - a.kv_indptr[b]);
             }
-            part_len = std::max<int64_t>(256, ceil_div(kv_work, 4LL * a.num_cu));
+            part_len = std::max<int64_t>(256, ceil_div(kv_work, 4LL * kNumCu));
             part_len = ceil_div(part_len, 64) * 64;
         }
+        std::vector<Unit> units;
         for (int32_t b = 0; b < a.batch; b++) {
             const int32_t kv0 = a.kv_indptr[b];
             const int32_t L = a.kv_indptr[b + 1] - kv0;
@@ -289,7 +412,7 @@ pa_status partition(const PartitionArgs &a, pa_work_unit *units_out, int32_t uni
                         n = forced;
                     else if (part_len)
                         n = (int32_t)std::max<int64_t>(1, ceil_div(visible, part_len));
-                    int32_t first = n_partials;
+                    const int32_t first = n_partials;
                     for (int32_t j = 0; j < n; j++) {
                         int64_t lo = visible * j / n, hi = visible * (j + 1) / n;
                         if (!forced && part_len) {
@@ -305,6 +428,8 @@ pa_status partition(const PartitionArgs &a, pa_work_unit *units_out, int32_t uni
                         x.u.q_end = q0 + t1;
                         x.u.partial = n > 1 ? n_partials++ : -1;
                         x.u.diag = kv0 + P + t0;
+                        x.u.merge = n > 1 ? (int32_t)merges.size() : -1;
+                        x.u.reserved0 = x.u.reserved1 = x.u.reserved2 = 0;
                         x.part = j;
                         x.tokens = (hi - lo) * (t1 - t0);
                         units.push_back(x);
@@ -323,24 +448,26 @@ pa_status partition(const PartitionArgs &a, pa_work_unit *units_out, int32_t uni
                 }
             }
         }
+        groups = xcd ? xcd_order_single(units, a.num_xcd) : plain_single(units);
     }
 
-    std::vector<pa_work_unit> ordered;
-    if ((a.flags & PA_PLAN_NO_XCD_ORDER) || a.num_xcd <= 1) {
-        ordered.reserve(units.size());
-        for (auto &x : units)
-            ordered.push_back(x.u);
-    } else {
-        ordered = xcd_order(units, a.num_xcd);
-    }
-
-    res->n_units = (int32_t)ordered.size();
+    int64_t n_units = 0;
+    for (auto &gr : groups)
+        n_units += (int64_t)gr.size();
+    res->n_workgroups = (int32_t)groups.size();
+    res->n_units = (int32_t)n_units;
     res->n_merges = (int32_t)merges.size();
     res->n_partials = n_partials;
-    if (res->n_units > unit_capacity || res->n_merges > merge_capacity)
+    if ((int64_t)groups.size() + 1 > wg_capacity || n_units > unit_capacity ||
+        (int64_t)merges.size() > merge_capacity)
         return fail(detail, "plan capacity exceeded", PA_ERR_CAPACITY);
-    if (!ordered.empty())
-        std::memcpy(units_out, ordered.data(), ordered.size() * sizeof(pa_work_unit));
+    int32_t pos = 0;
+    for (size_t w = 0; w < groups.size(); w++) {
+        wg_offsets[w] = pos;
+        for (const pa_work_unit &u : groups[w])
+            units_out[pos++] = u;
+    }
+    wg_offsets[groups.size()] = pos;
     if (!merges.empty())
         std::memcpy(merges_out, merges.data(), merges.size() * sizeof(pa_merge_unit));
     return PA_OK;

@@ -141,11 +141,14 @@ def _slot_tag_pool(num_slots, Hkv, D, dev):
 
 
 @pytest.mark.parametrize("num_slots,Hq,Hkv,D", [(70000, 32, 8, 128), ((1 << 24) + 1000, 8, 1, 128),
-                                                (2_300_000, 16, 8, 128)],
-                         ids=["small_pool", "over_2^24_slots", "over_4GiB"])
+                                                (2_300_000, 16, 8, 128), (1_048_575, 32, 8, 128),
+                                                (1_600_000, 32, 8, 128)],
+                         ids=["small_pool", "over_2^24_slots", "over_4GiB", "just_below_2GiB",
+                              "between_2_and_4GiB"])
 def test_slot_tags_bit_exact(num_slots, Hq, Hkv, D):
     """Each single-slot request returns its slot id exactly, including the last
-    slot of pools past 2^24 slots and past 4 GiB (64-bit row offsets)."""
+    slot of pools on both sides of 2 GiB (where row offsets stop fitting a
+    signed 32-bit offset), past 4 GiB and past 2^24 slots."""
     dev = device()
     say(f"slot tags num_slots={num_slots} Hkv={Hkv} ({num_slots * Hkv * D * 2 / 2**30:.2f} GiB per pool)")
     rng = np.random.Generator(np.random.PCG64(num_slots))
@@ -293,3 +296,30 @@ def test_profile_events():
             plan.decode(q, k, v, idx_dev, 0.1, out)
         ms, n = pa.pa_profile_end(plan.handle)
     assert n == 4 and ms > 0
+
+
+@pytest.mark.parametrize("flags_n", [0, 7, 64])
+def test_merge_protocol_repeatable(flags_n):
+    """Split lists are merged in-kernel by the part that arrives last.  Many
+    back-to-back launches (arrival counts reset by the kernels themselves)
+    must give bit-identical results, equal to the oracle within 2e-3."""
+    import paged_gqa_decode_pa_amd as pa
+    say(f"in-kernel merge repeatability, forced splits {flags_n}")
+    dev = device()
+    spec = W.QWEN3_4B_BATCH8
+    case = W.make_decode_case(spec, dev, layers=1)
+    idx = torch.as_tensor(case.kv_indices, device=dev)
+    flags = pa.PA_PLAN_FORCE_SPLITS(flags_n) if flags_n else 0
+    capacity = max(int(case.kv_indptr[-1]), spec.batch * flags_n * 256)
+    outs = [torch.empty((spec.batch, 32, 128), dtype=torch.float32, device=dev) for _ in range(40)]
+    with pa.Plan(spec.batch, capacity, 32, 8, 128) as plan:
+        plan.plan(case.kv_indptr, flags=flags)
+        for o in outs:
+            plan.decode(case.q, case.k_pools[0], case.v_pools[0], idx, case.sm_scale, o)
+        torch.cuda.synchronize()
+    first = outs[0].cpu().numpy()
+    for o in outs[1:]:
+        assert np.array_equal(o.cpu().numpy(), first)
+    ref, _ = oracle_decode(case.q, case.k_pools[0], case.v_pools[0], case.kv_indptr,
+                           case.kv_indices, case.sm_scale, 8)
+    assert max_err(first, ref) <= TOL

@@ -18,10 +18,14 @@ def _indptr(lengths):
     return ip
 
 
+def check_offsets(offs, units):
+    assert offs[0] == 0 and offs[-1] == units.size and np.all(np.diff(offs) >= 0)
+
+
 def check_decode(units, merges, n_partials, indptr, Hkv, forced=None):
     B = indptr.size - 1
     real = units[units["request"] >= 0]
-    assert np.all(units[units["request"] < 0]["partial"] == -1)
+    assert real.size == units.size, "no padding units"
     by_stream = defaultdict(list)
     for u in real:
         b, h = int(u["request"]), int(u["kv_head"])
@@ -68,18 +72,24 @@ def test_decode_partition_random(seed, Hq, Hkv, D):
     lengths[rng.random(B) < 0.2] = 0
     ip = _indptr(lengths)
     for flags in (0, pa.PA_PLAN_NO_XCD_ORDER):
-        units, merges, n_p = pa.pa_partition(ip, None, Hq, Hkv, D, flags)
-        check_decode(units, merges, n_p, ip, Hkv)
-        if flags & pa.PA_PLAN_NO_XCD_ORDER:
-            assert np.all(units["request"] >= 0)
-        else:
-            assert units.size % XCD == 0
+        for max_wg in (0, 1, 37, 2048):
+            offs, units, merges, n_p = pa.pa_partition(ip, None, Hq, Hkv, D, flags, max_wg)
+            check_offsets(offs, units)
+            check_decode(units, merges, n_p, ip, Hkv)
+            n_wg = offs.size - 1
+            limit = max_wg if max_wg > 0 else 768
+            if flags & pa.PA_PLAN_NO_XCD_ORDER:
+                assert n_wg <= limit
+            else:
+                assert n_wg % XCD == 0 and n_wg <= limit + XCD
 
 
 @pytest.mark.parametrize("n", [1, 2, 3, 7, 64, 256])
 def test_forced_splits(n):
     ip = _indptr([0, 1, 5, 100, 333])
-    units, merges, n_p = pa.pa_partition(ip, None, 32, 8, 128, pa.PA_PLAN_FORCE_SPLITS(n))
+    offs, units, merges, n_p = pa.pa_partition(ip, None, 32, 8, 128, pa.PA_PLAN_FORCE_SPLITS(n))
+    check_offsets(offs, units)
+    assert np.all(np.diff(offs) <= 1), "forced parts run one per workgroup"
     check_decode(units, merges, n_p, ip, 8, forced=n)
 
 
@@ -106,32 +116,48 @@ def test_deterministic():
     ip, _ = W.decode_lists(W.BATCH64_SHARED_PREFIX)
     a = pa.pa_partition(ip, None, 32, 8, 128)
     b = pa.pa_partition(ip, None, 32, 8, 128)
-    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]) and a[2] == b[2]
+    assert all(np.array_equal(x, y) for x, y in zip(a[:3], b[:3])) and a[3] == b[3]
 
 
 def test_batch64_partition_shape():
-    """The batch-64 shared-prefix workload: parts are aligned to the same list
-    positions in every request, clusters stay on one XCD, XCD loads balance."""
+    """The batch-64 shared-prefix workload: one workgroup per resident slot,
+    equal budgets, each (head, request) list opening its own workgroup, and
+    requests of one prefix group opened side by side on one XCD."""
     ip, _ = W.decode_lists(W.BATCH64_SHARED_PREFIX)
-    units, merges, n_p = pa.pa_partition(ip, None, 32, 8, 128)
+    max_wg = 768
+    offs, units, merges, n_p = pa.pa_partition(ip, None, 32, 8, 128, 0, max_wg)
+    check_offsets(offs, units)
     check_decode(units, merges, n_p, ip, 8)
-    real = units[units["request"] >= 0]
-    starts = real["kv_begin"] - ip[real["request"]]
-    S = int(np.max(real["kv_end"] - real["kv_begin"]))
-    assert S % 64 == 0 and np.all(starts % S == 0)
-    # the launch holds several workgroups per CU
-    assert real.size >= 256 * 4
-    xcd = np.nonzero(units["request"] >= 0)[0] % XCD
-    cluster = (starts // S) * 1000 + real["kv_head"] * 100 + real["request"] // 16
-    for c in np.unique(cluster):
-        assert np.unique(xcd[cluster == c]).size == 1
-    tokens = np.bincount(xcd, weights=real["kv_end"] - real["kv_begin"], minlength=XCD)
-    assert tokens.max() <= tokens.min() * 1.1 + S * 16
+    n_wg = offs.size - 1
+    assert n_wg == max_wg
+    cost = np.array([(units["kv_end"][offs[w]:offs[w + 1]] - units["kv_begin"][offs[w]:offs[w + 1]]).sum()
+                     + 128 * (offs[w + 1] - offs[w]) for w in range(n_wg)])
+    assert cost.max() <= cost.mean() * 1.05
+    # the first unit of workgroup id wg(i) opens segment i = head * B + request
+    per_xcd = n_wg // XCD
+    B = ip.size - 1
+    for i in range(8 * B):
+        wg = (i % per_xcd) * XCD + i // per_xcd
+        first = units[offs[wg]]
+        h, b = divmod(i, B)
+        assert (first["request"], first["kv_head"], first["kv_begin"]) == (b, h, ip[b])
+        if b % 4 == 3:   # the group b-3..b sits on one XCD
+            xcds = {((i - k) // per_xcd) for k in range(4)}
+            assert len(xcds) == 1
+
+
+def test_decode_small_batch_uses_fewer_workgroups():
+    """A small step does not spread below the minimum useful piece."""
+    ip = _indptr([256])
+    offs, units, merges, n_p = pa.pa_partition(ip, None, 32, 8, 128, pa.PA_PLAN_NO_XCD_ORDER, 768)
+    assert offs.size - 1 == 8          # 8 heads x 256 tokens, 256-token minimum
+    check_decode(units, merges, n_p, ip, 8)
 
 
 def check_prefill(units, merges, n_p, qo, ip, Hkv, group):
     B = ip.size - 1
     real = units[units["request"] >= 0]
+    assert real.size == units.size
     tiles = defaultdict(list)
     for u in real:
         tiles[(int(u["request"]), int(u["kv_head"]), int(u["q_begin"]), int(u["q_end"]))].append(u)
@@ -169,7 +195,9 @@ def check_prefill(units, merges, n_p, qo, ip, Hkv, group):
 @pytest.mark.parametrize("spec", W.PREFILL_SPECS, ids=lambda s: s.name)
 def test_prefill_partition_workloads(spec):
     qo, ip, _ = W.prefill_lists(spec)
-    units, merges, n_p = pa.pa_partition(ip, qo, spec.num_qo_heads, spec.num_kv_heads, spec.head_dim)
+    offs, units, merges, n_p = pa.pa_partition(ip, qo, spec.num_qo_heads, spec.num_kv_heads, spec.head_dim)
+    check_offsets(offs, units)
+    assert np.all(np.diff(offs) <= 1)
     check_prefill(units, merges, n_p, qo, ip, spec.num_kv_heads, spec.num_qo_heads // spec.num_kv_heads)
     real = units[units["request"] >= 0]
     assert real.size >= 256
@@ -185,7 +213,8 @@ def test_prefill_partition_random(seed):
     qo = _indptr(chunks)
     for Hq, Hkv in ((32, 8), (8, 8), (16, 2)):
         for flags in (0, pa.PA_PLAN_FORCE_SPLITS(3)):
-            units, merges, n_p = pa.pa_partition(ip, qo, Hq, Hkv, 128, flags)
+            offs, units, merges, n_p = pa.pa_partition(ip, qo, Hq, Hkv, 128, flags)
+            check_offsets(offs, units)
             check_prefill(units, merges, n_p, qo, ip, Hkv, Hq // Hkv)
 
 
@@ -200,6 +229,6 @@ def test_forced_splits_capacity_guarantee():
     from paged_gqa_decode_pa_amd import pa_partition
     ip = _indptr([10, 20, 30])
     n = 50
-    units, merges, n_p = pa_partition(ip, None, 32, 8, 128, pa.PA_PLAN_FORCE_SPLITS(n))
+    offs, units, merges, n_p = pa_partition(ip, None, 32, 8, 128, pa.PA_PLAN_FORCE_SPLITS(n))
     assert n_p == 3 * 8 * n
     assert n_p <= 8 * (3 + (3 * n * 256) // 256)
