@@ -41,6 +41,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode-attn µs/step/layer + achieved HBM GB/s (% of MI355X peak), batch 64"
 HBM_PEAK_GBS = 8000.0
+PREFILL_METRIC = "chunked-prefill attention TFLOP/s (% of MI355X dense bf16 MFMA peak)"
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+PREFILL_LAYERS = 8
 COUNTERS = os.path.join(ROOT, "profiles", "decode_b64_counters.json")
 KERNEL_SOURCE = os.path.join(ROOT, "paged_gqa_decode_pa_amd", "csrc", "decode.hip")
 
@@ -124,6 +127,153 @@ def cpu_baseline(case, spec, bytes_per_layer, seconds, gpu_out_layer0):
     }, err
 
 
+def prefill_flops(spec, qo_indptr, kv_indptr) -> int:
+    """4*D flops (QK^T and PV) per (query row, visible list entry)."""
+    total = 0
+    for b in range(spec.batch):
+        C = int(qo_indptr[b + 1] - qo_indptr[b])
+        L = int(kv_indptr[b + 1] - kv_indptr[b])
+        P = L - C
+        total += C * (P + 1) + C * (C - 1) // 2   # row i sees P + i + 1 entries
+    return total * spec.num_qo_heads * 4 * spec.head_dim
+
+
+def prefill_bytes(spec, qo_indptr, kv_indices) -> int:
+    import numpy as np
+    T = int(qo_indptr[-1])
+    unique = int(np.unique(kv_indices).size)
+    Hq, Hkv, D = spec.num_qo_heads, spec.num_kv_heads, spec.head_dim
+    return unique * Hkv * D * 2 * 2 + int(kv_indices.size) * 4 + T * Hq * D * (2 + 4)
+
+
+def cpu_baseline_prefill(case, spec, flops_per_row_entry, seconds):
+    """fp64 oracle on a bounded sample of rows: the last chunk token of every
+    request, all heads (the rows that see the most entries), repeated."""
+    import numpy as np
+
+    import oracle
+    import workloads as W
+    ref = oracle.load()
+    qb, kb, vb = W.bits(case.q), W.bits(case.k_pool), W.bits(case.v_pool)
+    Hq = spec.num_qo_heads
+    rows = []
+    entries = 0
+    for b in range(spec.batch):
+        t = int(case.qo_indptr[b + 1]) - 1
+        L = int(case.kv_indptr[b + 1] - case.kv_indptr[b])
+        rows.extend(t * Hq + h for h in range(Hq))
+        entries += L * Hq
+    rows = np.asarray(rows, np.int32)
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        ref.prefill(qb, kb, vb, case.qo_indptr, case.kv_indptr, case.kv_indices, case.sm_scale,
+                    spec.num_kv_heads, sel=rows)
+        reps += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {
+        "value": round(entries * flops_per_row_entry * reps / dt / 1e12, 5),
+        "unit": "TFLOP/s",
+        "cores": ref.num_threads(),
+        "kind": "oracle",
+        "sample": f"{rows.size} rows (last chunk token of each request, all heads), "
+                  f"{reps} repetition(s), {dt:.1f} s",
+    }
+
+
+def run_prefill_bench(args):
+    import numpy as np
+    import torch
+
+    import paged_gqa_decode_pa_amd as pa
+    import workloads as W
+
+    spec = W.PREFILL_CHUNK512 if args.workload == "prefill_chunk512" else W.PREFILL_CHUNK64
+    layers = args.layers or PREFILL_LAYERS
+    dev = torch.device("cuda", 0)
+    log(f"generating {spec.name}")
+    case = W.make_prefill_case(spec, dev)
+    T = int(case.qo_indptr[-1])
+    B, Hq, Hkv, D = spec.batch, spec.num_qo_heads, spec.num_kv_heads, spec.head_dim
+    idx = torch.as_tensor(case.kv_indices, device=dev)
+    flops = prefill_flops(spec, case.qo_indptr, case.kv_indptr)
+    nbytes = prefill_bytes(spec, case.qo_indptr, case.kv_indices)
+    outs = [torch.empty((T, Hq, D), dtype=torch.float32, device=dev) for _ in range(layers)]
+    plan = pa.Plan(B, int(case.kv_indptr[-1]), Hq, Hkv, D, max_q_total=T)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        plan.plan(case.kv_indptr, case.qo_indptr, flags=args.flags, stream=stream)
+        for layer in range(layers):
+            plan.prefill(case.q, case.k_pool, case.v_pool, idx, case.sm_scale, outs[layer],
+                         stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(end) / args.steps
+    pa.pa_profile_begin(plan.handle, args.steps * layers)
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    kernel_ms, launches = pa.pa_profile_end(plan.handle)
+    kernel_avg_ms = kernel_ms / max(1, launches)
+    log(f"step {ms_per_step:.3f} ms ({ms_per_step * 1e3 / layers:.1f} us per layer); prefill kernel "
+        f"avg {kernel_avg_ms * 1e3:.1f} us over {launches} launches")
+    value = flops * layers / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (kernel_avg_ms * 1e-3) / 1e12
+    result = {
+        "metric": PREFILL_METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": spec.name,
+            "batch": B, "num_qo_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
+            "cached_len": spec.cached_len, "chunk_len": spec.chunk_len,
+            "layers_per_step": layers, "pool_slots": spec.num_slots, "plan_flags": args.flags,
+        },
+        "us_per_step_layer": round(ms_per_step * 1e3 / layers, 2),
+        "algorithmic_flops_per_layer": flops,
+        "algorithmic_bytes_per_layer": nbytes,
+        "achieved_hbm_gbs": round(nbytes / (kernel_avg_ms * 1e-3) / 1e9, 1),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": BF16_MFMA_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "kernel": f"prefill_kernel<{D},{Hq // Hkv}> (pa_prefill_chunk_run)",
+            "kernel_avg_us": round(kernel_avg_ms * 1e3, 2),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: fp64 oracle on sampled rows for ~{args.cpu_seconds:.0f} s")
+        result["cpu_baseline"] = cpu_baseline_prefill(case, spec, 4 * D, args.cpu_seconds)
+    plan.close()
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -133,7 +283,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--flags", type=int, default=0, help="pa_plan flags")
-    ap.add_argument("--workload", default="batch64", choices=["batch64", "copy"])
+    ap.add_argument("--workload", default="batch64",
+                    choices=["batch64", "prefill_chunk512", "prefill_chunk64", "copy"])
     ap.add_argument("--copy-gib", type=float, default=4.0)
     args = ap.parse_args()
 
@@ -149,6 +300,10 @@ def main():
 
     if args.workload == "copy":
         run_copy(args.copy_gib, args.steps)
+        return
+
+    if args.workload.startswith("prefill"):
+        run_prefill_bench(args)
         return
 
     import paged_gqa_decode_pa_amd as pa

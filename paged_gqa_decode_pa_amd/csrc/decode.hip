@@ -511,16 +511,6 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<G>(), 8))) void decode_
     }
 }
 
-template <int D, int G>
-__global__ __launch_bounds__(256) void merge_kernel(const pa_merge_unit *__restrict__ merges,
-                                                    const float *__restrict__ part_o,
-                                                    const float *__restrict__ part_lse,
-                                                    int32_t rows_per_slot, float *__restrict__ out,
-                                                    float *__restrict__ lse, int32_t num_qo_heads) {
-    merge_rows<D, G, false>(merges[blockIdx.x], part_o, part_lse, rows_per_slot, out, lse, num_qo_heads,
-                            threadIdx.x, blockDim.x);
-}
-
 }  // namespace
 
 bool row_offsets_fit_32(int64_t num_slots, uint32_t stride_bytes) {
@@ -552,13 +542,6 @@ int launch_decode_dg(const DecodeLaunch &l, hipStream_t stream) {
                            (const uint16_t *)l.q, (const char *)l.k_pool, (const char *)l.v_pool,
                            stride_bytes, l.kv_indices, scale_log2, l.out, l.lse, l.partial_o,
                            l.partial_lse, l.num_qo_heads);
-    return (int)hipGetLastError();
-}
-
-template <int D, int G>
-int launch_merge_dg(const DecodeLaunch &l, int32_t rows_per_slot, hipStream_t stream) {
-    hipLaunchKernelGGL((merge_kernel<D, G>), dim3(l.n_merges), dim3(256), 0, stream, l.merges,
-                       l.partial_o, l.partial_lse, rows_per_slot, l.out, l.lse, l.num_qo_heads);
     return (int)hipGetLastError();
 }
 
@@ -610,30 +593,6 @@ int launch_decode(const DecodeLaunch &l, void *stream) {
         case 2: return launch_decode_dg<256, 2>(l, s);
         case 4: return launch_decode_dg<256, 4>(l, s);
         case 8: return launch_decode_dg<256, 8>(l, s);
-        }
-    }
-    return (int)hipErrorInvalidValue;
-}
-
-int launch_merge(const DecodeLaunch &l, void *stream) {
-    if (l.n_merges == 0)
-        return 0;
-    hipStream_t s = (hipStream_t)stream;
-    const int G = l.num_qo_heads / l.num_kv_heads;
-    const int32_t rows = G;  // a decode partial slot holds the group's rows
-    if (l.head_dim == 128) {
-        switch (G) {
-        case 1: return launch_merge_dg<128, 1>(l, rows, s);
-        case 2: return launch_merge_dg<128, 2>(l, rows, s);
-        case 4: return launch_merge_dg<128, 4>(l, rows, s);
-        case 8: return launch_merge_dg<128, 8>(l, rows, s);
-        }
-    } else if (l.head_dim == 256) {
-        switch (G) {
-        case 1: return launch_merge_dg<256, 1>(l, rows, s);
-        case 2: return launch_merge_dg<256, 2>(l, rows, s);
-        case 4: return launch_merge_dg<256, 4>(l, rows, s);
-        case 8: return launch_merge_dg<256, 8>(l, rows, s);
         }
     }
     return (int)hipErrorInvalidValue;

@@ -106,7 +106,8 @@ int launch_decode(const DecodeLaunch &l, void *stream);   // returns hipError_t
 bool row_offsets_fit_32(int64_t num_slots, uint32_t stride_bytes);
 // Decode workgroups one compute unit holds at once (0 if unknown).
 int decode_workgroups_per_cu(int32_t head_dim, int32_t group);
-int launch_merge(const DecodeLaunch &l, void *stream);
 int launch_prefill(const DecodeLaunch &l, void *stream);
+// Log-sum-exp merge of the prefill partials (no-op without merge units).
+int launch_prefill_merge(const DecodeLaunch &l, void *stream);
 
 }  // namespace pa

@@ -1,14 +1,481 @@
 // prefill.hip -- gfx950 chunked-prefill kernel of libpa (matrix-core path).
+//
+// Operation: a request whose prompt is processed in chunks (Agent-Infer page,
+// "Agent-Infer: 纯 Rust 编写的高性能 LLM 推理引擎", sections "调度器" and
+// "优化历程": chunks of 512 tokens, 64 while decodes run) has a slot list of
+// L entries whose last C entries are the chunk's own tokens, already written
+// into the pool; chunk token i (0-based) attends to list entries 0 .. L-C+i
+// (its cached prefix plus the chunk up to itself).  Scores, softmax and the
+// weighted sum are the textbook ones, in the base-2 exponent domain as in the
+// decode kernel.
+//
+// One workgroup (4 waves) runs one work unit: one request, one KV head, a
+// tile of up to 128/G chunk tokens whose G query heads are stacked into 128
+// rows (row r = token * G + head, so wave w owns rows 32w .. 32w+31), and a
+// contiguous range of the list.  Per tile of KT list entries:
+//   * all 256 threads gather the KT K rows and V rows of the KV head (16-byte
+//     loads, one slot id per row) into registers one tile ahead, and write
+//     them into a double-buffered LDS stage (row-major, rows padded so that
+//     the reads below hit distinct banks);
+//   * each wave computes its 32 x KT score block transposed, S^T = K Q^T,
+//     with v_mfma_f32_32x32x16_bf16 (K rows from LDS as the A operand, the
+//     wave's 32 query rows held in registers as the B operand for the whole
+//     unit), so every lane ends up owning 16 x (KT/32) scores of ONE query
+//     row and the row statistics need a single cross-half exchange;
+//   * online softmax in fp32 with a lazily moved maximum (as in decode);
+//   * the weights P are split into two bf16 terms, P = hi + lo (lo = the
+//     rounding residue of hi), and O^T += V^T hi^T + V^T lo^T, so the weighted
+//     sum keeps about 16 bits of each weight instead of bf16's 8; the V^T
+//     operand is read straight from the row-major LDS tile with the
+//     transposing read ds_read_b64_tr_b16, and the P^T operand is regrouped
+//     from the score layout with two v_permlane32_swap per 16 entries;
+//   * O^T accumulates in the MFMA's fp32 registers: a lane holds D/2 values
+//     of its own row, so rescaling is a per-lane multiply.
+// The unit writes the final rows, or a partial result (normalised O and its
+// log2-sum-exp) that the merge kernel combines.
 #include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
 
 #include "pa_internal.h"
 
 namespace pa {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNoMax = -1.0e30f;
+constexpr float kRescaleSlack = 8.0f;
+constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+
+template <int D>
+struct PrefillGeo {
+    static constexpr int KT = D == 128 ? 64 : 32;     // list entries per tile
+    // LDS row pitches.  K rows are read 16 bytes per lane down a column of
+    // rows; a 16-byte pad moves each row by 4 banks.  V rows are read by the
+    // transposing read, 8 bytes per lane, 4 rows x 32 bytes per 16 lanes; a
+    // 32-byte pad moves each row by 8 banks.
+    static constexpr int KROW = D * 2 + 16;
+    static constexpr int VROW = D * 2 + 32;
+    static constexpr int STAGE = KT * (KROW + VROW);  // one buffer: K tile then V tile
+    static constexpr int TPR = D / 8;                  // staging threads per row (16 B each)
+    static constexpr int RPP = kThreads / TPR;         // rows per staging pass
+    static constexpr int PASSES = KT / RPP;
+    static constexpr int DS = D / 16;                  // MFMA k-steps over D (QK^T)
+    static constexpr int DB = D / 32;                  // 32-wide column blocks of O
+    static constexpr int SB = KT / 32;                 // 32-entry score blocks
+    static constexpr int KS = KT / 16;                 // MFMA k-steps over entries (PV)
+    static_assert(PASSES * RPP == KT, "staging passes must cover the tile");
+};
+
+template <int D>
+constexpr int prefill_waves_per_simd() {
+    return D == 128 ? 2 : 1;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Value of x held by lane (l + 32) % 64.
+__device__ __forceinline__ float other_half(float x) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(__lane_id() < 32 ? p[1] : p[0]);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    const f32x2_t v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+// Splits weights (a, b) into bf16 pairs hi and lo with a + b = hi + lo up to
+// the rounding of lo (2^-16 relative).
+__device__ __forceinline__ void split_pair(float a, float b, uint32_t &hi, uint32_t &lo) {
+    hi = pack_bf16(a, b);
+    const float ha = __uint_as_float(hi << 16), hb = __uint_as_float(hi & 0xffff0000u);
+    lo = pack_bf16(a - ha, b - hb);
+}
+
+// B operand (P^T, 16 entries x 32 rows) of one k-step from the score layout.
+// x0, x1: this lane's weights of entries 4h..4h+3 of the k-step (h = lane/32)
+// packed in pairs; y0, y1: entries 8+4h..8+4h+3.  Lane l < 32 needs entries
+// 0..7 (its own x and the x of lane l+32), lane l >= 32 entries 8..15 (the y
+// of lane l-32 and its own y): one half-wave swap per dword does both.
+__device__ __forceinline__ bf16x8_t regroup(uint32_t x0, uint32_t x1, uint32_t y0, uint32_t y1) {
+    const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
+    const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
+    const uint4 v = {s0[0], s1[0], s0[1], s1[1]};
+    return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// s_waitcnt vmcnt(0): every vector-memory load of this wave has returned.
+__device__ __forceinline__ void wait_vector_memory() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+__device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int D, int G, bool SPLIT>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(prefill_waves_per_simd<D>(), prefill_waves_per_simd<D>()))) void
+prefill_kernel(const int32_t *__restrict__ wg_offsets, const pa_work_unit *__restrict__ units,
+               const uint16_t *__restrict__ q, const char *__restrict__ k_pool,
+               const char *__restrict__ v_pool, uint64_t stride_bytes,
+               const int32_t *__restrict__ kv_indices, float scale_log2, float *__restrict__ out,
+               float *__restrict__ lse, float *__restrict__ part_o, float *__restrict__ part_lse,
+               int32_t num_qo_heads) {
+    using Geo = PrefillGeo<D>;
+    constexpr int KT = Geo::KT, KROW = Geo::KROW, VROW = Geo::VROW, STAGE = Geo::STAGE;
+    constexpr int TPR = Geo::TPR, RPP = Geo::RPP, PASSES = Geo::PASSES;
+    constexpr int DS = Geo::DS, DB = Geo::DB, SB = Geo::SB, KS = Geo::KS;
+    static_assert(kWaves * 32 == kPrefillTileRows, "one 32-row block per wave");
+
+    __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 31, half = lane >> 5;
+    const int row = wave * 32 + col;       // tile row of this lane's scores and output
+    const int tt = row / G, g = row % G;   // its chunk token (within the tile) and head
+    // staging: this thread moves 16-byte chunk `chunk` of rows srow + p*RPP
+    const int srow = tid / TPR, chunk = tid % TPR;
+    // LDS byte offsets of this lane's MFMA operands within a stage
+    const int k_lane = col * KROW + half * 16;
+    const int gi = lane >> 4, e4 = (lane & 15) >> 2, q4 = lane & 3;
+    const int v_lane = KT * KROW + (8 * (gi >> 1) + e4) * VROW + (16 * (gi & 1) + 4 * q4) * 2;
+    // Scores are scaled after taking their maximum, which needs a positive
+    // scale: a negative scale is applied as |scale| to -q (bf16 negation is
+    // exact), a zero scale as 1 to q = 0 (every score 0, as it should be).
+    const uint32_t q_sign = scale_log2 < 0.f ? 0x80008000u : 0u;
+    const bool q_zero = scale_log2 == 0.f;
+    const float c_exp = q_zero ? 1.f : fabsf(scale_log2);
+
+    const int32_t unit_begin = wg_offsets[blockIdx.x], unit_end = wg_offsets[blockIdx.x + 1];
+    for (int32_t ui = unit_begin; ui < unit_end; ui++) {
+        const pa_work_unit unit = units[ui];
+        if (unit.request < 0)
+            continue;  // padding unit (uniform over the workgroup)
+        __syncthreads();  // the previous unit's last tile is no longer read
+
+        const int32_t n_tok = unit.q_end - unit.q_begin;
+        const bool row_valid = tt < n_tok;
+        bf16x8_t qf[DS];
+        {
+            const int64_t qrow = ((int64_t)(unit.q_begin + tt) * num_qo_heads + unit.kv_head * G + g) * D;
+            const uint4 *qp = reinterpret_cast<const uint4 *>(q + qrow + 8 * half);
+#pragma unroll
+            for (int s = 0; s < DS; s++) {
+                uint4 v = (row_valid && !q_zero) ? qp[2 * s] : uint4{0, 0, 0, 0};
+                v.x ^= q_sign;
+                v.y ^= q_sign;
+                v.z ^= q_sign;
+                v.w ^= q_sign;
+                qf[s] = __builtin_bit_cast(bf16x8_t, v);
+            }
+        }
+        // the query operand stays in registers for the whole unit; waiting for
+        // it here keeps the tile loop from waiting on every load in flight
+        wait_vector_memory();
+
+        const int32_t kv0 = unit.kv_begin, kv1 = unit.kv_end;
+        const int32_t n_tiles = (kv1 - kv0 + KT - 1) / KT;
+        const uint64_t head_off = (uint64_t)unit.kv_head * D * 2 + chunk * 16;
+
+        int32_t slot[PASSES];
+        uint4 kreg[PASSES], vreg[PASSES];
+        auto load_slots = [&](int32_t tile) {
+#pragma unroll
+            for (int p = 0; p < PASSES; p++) {
+                const int32_t idx = kv0 + tile * KT + p * RPP + srow;
+                slot[p] = idx < kv1 ? kv_indices[idx] : -1;
+            }
+        };
+        auto load_rows = [&]() {
+#pragma unroll
+            for (int p = 0; p < PASSES; p++) {
+                if (slot[p] >= 0) {
+                    const uint64_t off = (uint64_t)(uint32_t)slot[p] * stride_bytes + head_off;
+                    kreg[p] = *reinterpret_cast<const uint4 *>(k_pool + off);
+                    vreg[p] = *reinterpret_cast<const uint4 *>(v_pool + off);
+                } else {
+                    kreg[p] = uint4{0, 0, 0, 0};
+                    vreg[p] = uint4{0, 0, 0, 0};
+                }
+            }
+        };
+        auto store_rows = [&](int buf) {
+            char *st = smem + buf * STAGE;
+#pragma unroll
+            for (int p = 0; p < PASSES; p++) {
+                const int r = p * RPP + srow;
+                *reinterpret_cast<uint4 *>(st + r * KROW + chunk * 16) = kreg[p];
+                *reinterpret_cast<uint4 *>(st + KT * KROW + r * VROW + chunk * 16) = vreg[p];
+            }
+        };
+
+        float m = kNoMax, l = 0.f;
+        f32x16_t o[DB];
+#pragma unroll
+        for (int b = 0; b < DB; b++)
+            o[b] = f32x16_t{};
+
+        if (n_tiles > 0) {
+            load_slots(0);
+            load_rows();
+            if (n_tiles > 1)
+                load_slots(1);
+            store_rows(0);
+        }
+        // row limit: the last list entry (absolute offset) this row may see
+        const int32_t row_last = min(kv1 - 1, unit.diag + tt);
+        const int32_t unit_last = min(kv1 - 1, unit.diag);  // smallest row limit of the unit
+
+        // one tile: entries kv0 + it*KT ...; MASK: some entry lies beyond a row's limit
+        auto step = [&](int32_t it, auto mask_tag) {
+            constexpr bool MASK = decltype(mask_tag)::value;
+            const int buf = it & 1;
+            if (it + 1 < n_tiles) {
+                load_rows();  // tile it+1, slots fetched one iteration earlier
+                if (it + 2 < n_tiles)
+                    load_slots(it + 2);
+            }
+            __syncthreads();  // stage `buf` written by every thread
+
+            const char *st = smem + buf * STAGE;
+            // S^T = K Q^T, one 32x32 block per 32 entries; entry of s[b][i]:
+            // b*32 + 8*(i/4) + 4*half + i%4 within the tile
+            f32x16_t s[SB];
+#pragma unroll
+            for (int b = 0; b < SB; b++) {
+                uint4 ka[DS];
+#pragma unroll
+                for (int d = 0; d < DS; d++)
+                    ka[d] = *reinterpret_cast<const uint4 *>(st + k_lane + b * 32 * KROW + d * 32);
+                s[b] = mfma(__builtin_bit_cast(bf16x8_t, ka[0]), qf[0], f32x16_t{});
+#pragma unroll
+                for (int d = 1; d < DS; d++)
+                    s[b] = mfma(__builtin_bit_cast(bf16x8_t, ka[d]), qf[d], s[b]);
+            }
+            if (MASK) {
+                const int32_t lim = row_last - (kv0 + it * KT) - 4 * half;
+#pragma unroll
+                for (int b = 0; b < SB; b++)
+#pragma unroll
+                    for (int i = 0; i < 16; i++)
+                        if (b * 32 + 8 * (i / 4) + (i % 4) > lim)
+                            s[b][i] = -INFINITY;
+            }
+            float tmax = -INFINITY;
+#pragma unroll
+            for (int b = 0; b < SB; b++)
+#pragma unroll
+                for (int i = 0; i < 16; i++)
+                    tmax = fmaxf(tmax, s[b][i]);
+            tmax *= c_exp;
+            tmax = fmaxf(tmax, other_half(tmax));
+            const bool move = tmax > m + kRescaleSlack;
+            if (__builtin_amdgcn_ballot_w64(move)) {
+                const float m_new = move ? tmax : m;
+                const float alpha = fast_exp2(m - m_new);
+                l *= alpha;
+#pragma unroll
+                for (int b = 0; b < DB; b++)
+#pragma unroll
+                    for (int i = 0; i < 16; i++)
+                        o[b][i] *= alpha;
+                m = m_new;
+            }
+            // weights (<= 2^8), their row sum, and the split into bf16 hi + lo
+            uint32_t ph[SB][8], pl[SB][8];
+#pragma unroll
+            for (int b = 0; b < SB; b++)
+#pragma unroll
+                for (int i = 0; i < 16; i += 2) {
+                    const float p0 = fast_exp2(fmaf(s[b][i], c_exp, -m));
+                    const float p1 = fast_exp2(fmaf(s[b][i + 1], c_exp, -m));
+                    l += p0 + p1;
+                    if (SPLIT)
+                        split_pair(p0, p1, ph[b][i / 2], pl[b][i / 2]);
+                    else
+                        ph[b][i / 2] = pack_bf16(p0, p1);
+                }
+            // O^T += V^T P^T, 16 entries per k-step
+#pragma unroll
+            for (int k = 0; k < KS; k++) {
+                const int b = k / 2, w0 = 4 * (k % 2);  // dword index of entries 16*(k%2) + 4*half
+                const bf16x8_t bh = regroup(ph[b][w0], ph[b][w0 + 1], ph[b][w0 + 2], ph[b][w0 + 3]);
+                bf16x8_t bl;
+                if (SPLIT)
+                    bl = regroup(pl[b][w0], pl[b][w0 + 1], pl[b][w0 + 2], pl[b][w0 + 3]);
+#pragma unroll
+                for (int db = 0; db < DB; db++) {
+                    const int off = v_lane + k * 16 * VROW + db * 64;
+                    const i16x4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(st + off));
+                    const i16x4_t hi4 =
+                        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(st + off + 4 * VROW));
+                    const bf16x8_t a = __builtin_bit_cast(
+                        bf16x8_t, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+                    o[db] = mfma(a, bh, o[db]);
+                    if (SPLIT)
+                        o[db] = mfma(a, bl, o[db]);
+                }
+            }
+            if (it + 1 < n_tiles)
+                store_rows(buf ^ 1);
+        };
+        // tiles that lie entirely within every row's window need no mask
+        const int32_t n_open = max(0, min(n_tiles, (unit_last - kv0 + 1) / KT));
+        for (int32_t it = 0; it < n_open; it++)
+            step(it, std::false_type{});
+        for (int32_t it = n_open; it < n_tiles; it++)
+            step(it, std::true_type{});
+
+        // the two lanes of a row hold disjoint halves of its entries
+        const float l_row = l + other_half(l);
+        const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
+        const float lse2 = l_row > 0.f ? m + fast_log2(l_row) : -INFINITY;
+        float *dst;
+        if (unit.partial < 0) {
+            if (!row_valid)
+                continue;
+            const int64_t orow = (int64_t)(unit.q_begin + tt) * num_qo_heads + unit.kv_head * G + g;
+            dst = out + orow * D;
+            if (lse && half == 0)
+                lse[orow] = lse2 * kLn2;
+        } else {
+            if (!row_valid)
+                continue;
+            const int64_t prow = (int64_t)unit.partial * kPrefillTileRows + row;
+            dst = part_o + prow * D;
+            if (half == 0)
+                part_lse[prow] = lse2;
+        }
+        // O^T element i of block db: column db*32 + 8*(i/4) + 4*half + i%4
+#pragma unroll
+        for (int db = 0; db < DB; db++)
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const float4 v = {o[db][4 * j] * inv, o[db][4 * j + 1] * inv, o[db][4 * j + 2] * inv,
+                                  o[db][4 * j + 3] * inv};
+                *reinterpret_cast<float4 *>(dst + db * 32 + 8 * j + 4 * half) = v;
+            }
+    }
+}
+
+// Log-sum-exp merge of prefill partials: workgroup (x, y) combines rows
+// y*RPW .. y*RPW+RPW-1 of merge unit x; a row's D values are spread over
+// D/4 threads with one float4 each, so every part's row is one coalesced read.
+template <int D, int G>
+__global__ __launch_bounds__(kThreads) void prefill_merge_kernel(
+    const pa_merge_unit *__restrict__ merges, const float *__restrict__ part_o,
+    const float *__restrict__ part_lse, float *__restrict__ out, float *__restrict__ lse,
+    int32_t num_qo_heads) {
+    constexpr int TPR = D / 4, RPW = kThreads / TPR;
+    const pa_merge_unit mu = merges[blockIdx.x];
+    const int row = blockIdx.y * RPW + threadIdx.x / TPR, c = threadIdx.x % TPR;
+    if (row >= (mu.q_end - mu.q_begin) * G)
+        return;
+    float M = -INFINITY;
+    for (int32_t i = 0; i < mu.n_parts; i++)
+        M = fmaxf(M, part_lse[(int64_t)(mu.first_partial + i) * kPrefillTileRows + row]);
+    const int64_t orow = (int64_t)(mu.q_begin + row / G) * num_qo_heads + mu.kv_head * G + row % G;
+    float4 acc = {0.f, 0.f, 0.f, 0.f};
+    float wsum = 0.f;
+    if (M != -INFINITY) {
+        for (int32_t i = 0; i < mu.n_parts; i++) {
+            const int64_t prow = (int64_t)(mu.first_partial + i) * kPrefillTileRows + row;
+            const float w = fast_exp2(part_lse[prow] - M);
+            const float4 v = *reinterpret_cast<const float4 *>(part_o + prow * D + 4 * c);
+            acc.x = fmaf(w, v.x, acc.x);
+            acc.y = fmaf(w, v.y, acc.y);
+            acc.z = fmaf(w, v.z, acc.z);
+            acc.w = fmaf(w, v.w, acc.w);
+            wsum += w;
+        }
+        const float inv = 1.f / wsum;
+        acc.x *= inv;
+        acc.y *= inv;
+        acc.z *= inv;
+        acc.w *= inv;
+    }
+    *reinterpret_cast<float4 *>(out + orow * D + 4 * c) = acc;
+    if (lse && c == 0)
+        lse[orow] = M == -INFINITY ? -INFINITY : (M + fast_log2(wsum)) * kLn2;
+}
+
+template <int D, int G>
+int launch_prefill_merge_dg(const DecodeLaunch &l, hipStream_t stream) {
+    constexpr int RPW = kThreads / (D / 4);
+    hipLaunchKernelGGL((prefill_merge_kernel<D, G>), dim3(l.n_merges, kPrefillTileRows / RPW),
+                       dim3(kThreads), 0, stream, l.merges, l.partial_o, l.partial_lse, l.out, l.lse,
+                       l.num_qo_heads);
+    return (int)hipGetLastError();
+}
+
+template <int D, int G>
+int launch_prefill_dg(const DecodeLaunch &l, hipStream_t stream) {
+    const uint64_t stride_bytes = (uint64_t)l.slot_stride * 2;
+    hipLaunchKernelGGL((prefill_kernel<D, G, true>), dim3(l.n_workgroups), dim3(kThreads), 0, stream,
+                       l.wg_offsets, l.units, (const uint16_t *)l.q, (const char *)l.k_pool,
+                       (const char *)l.v_pool, stride_bytes, l.kv_indices, l.sm_scale * kLog2e, l.out,
+                       l.lse, l.partial_o, l.partial_lse, l.num_qo_heads);
+    return (int)hipGetLastError();
+}
+
+}  // namespace
 
 int launch_prefill(const DecodeLaunch &l, void *stream) {
-    (void)l;
-    (void)stream;
-    return (int)hipErrorNotSupported;
+    if (l.n_workgroups == 0)
+        return 0;
+    hipStream_t s = (hipStream_t)stream;
+    const int G = l.num_qo_heads / l.num_kv_heads;
+    if (l.head_dim == 128) {
+        switch (G) {
+        case 1: return launch_prefill_dg<128, 1>(l, s);
+        case 2: return launch_prefill_dg<128, 2>(l, s);
+        case 4: return launch_prefill_dg<128, 4>(l, s);
+        case 8: return launch_prefill_dg<128, 8>(l, s);
+        }
+    } else if (l.head_dim == 256) {
+        switch (G) {
+        case 1: return launch_prefill_dg<256, 1>(l, s);
+        case 2: return launch_prefill_dg<256, 2>(l, s);
+        case 4: return launch_prefill_dg<256, 4>(l, s);
+        case 8: return launch_prefill_dg<256, 8>(l, s);
+        }
+    }
+    return (int)hipErrorInvalidValue;
+}
+
+int launch_prefill_merge(const DecodeLaunch &l, void *stream) {
+    if (l.n_merges == 0)
+        return 0;
+    hipStream_t s = (hipStream_t)stream;
+    const int G = l.num_qo_heads / l.num_kv_heads;
+    if (l.head_dim == 128) {
+        switch (G) {
+        case 1: return launch_prefill_merge_dg<128, 1>(l, s);
+        case 2: return launch_prefill_merge_dg<128, 2>(l, s);
+        case 4: return launch_prefill_merge_dg<128, 4>(l, s);
+        case 8: return launch_prefill_merge_dg<128, 8>(l, s);
+        }
+    } else if (l.head_dim == 256) {
+        switch (G) {
+        case 1: return launch_prefill_merge_dg<256, 1>(l, s);
+        case 2: return launch_prefill_merge_dg<256, 2>(l, s);
+        case 4: return launch_prefill_merge_dg<256, 4>(l, s);
+        case 8: return launch_prefill_merge_dg<256, 8>(l, s);
+        }
+    }
+    return (int)hipErrorInvalidValue;
 }
 
 }  // namespace pa

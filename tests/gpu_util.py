@@ -56,3 +56,26 @@ def max_err(gpu: np.ndarray, ref: np.ndarray, rows=None) -> float:
     both_inf = np.isneginf(g) & np.isneginf(r)
     d = np.where(both_inf, 0.0, np.abs(g.astype(np.float64) - r))
     return float(np.nanmax(d)) if d.size else 0.0
+
+
+def run_prefill(q, k_pool, v_pool, qo_indptr, kv_indptr, kv_indices_dev, sm_scale, num_kv_heads,
+                flags=0, with_lse=True):
+    """HIP chunked prefill through the C ABI -> (out [T,Hq,D], lse [T,Hq]) on the host."""
+    import paged_gqa_decode_pa_amd as pa
+    T, Hq, D = q.shape
+    B = len(kv_indptr) - 1
+    out = torch.full((T, Hq, D), float("nan"), dtype=torch.float32, device=q.device)
+    lse = torch.full((T, Hq), float("nan"), dtype=torch.float32, device=q.device) if with_lse else None
+    with pa.Plan(max(B, 1), max(int(kv_indptr[-1]), 1), Hq, num_kv_heads, D,
+                 max_q_total=max(T, 1)) as plan:
+        plan.plan(kv_indptr, qo_indptr, flags=flags)
+        plan.prefill(q, k_pool, v_pool, kv_indices_dev, sm_scale, out, lse)
+        torch.cuda.synchronize()
+    return out.cpu().numpy(), (lse.cpu().numpy() if with_lse else None)
+
+
+def oracle_prefill(q, k_pool, v_pool, qo_indptr, kv_indptr, kv_indices, sm_scale, num_kv_heads,
+                   sel=None):
+    ref = oracle.load()
+    return ref.prefill(W.bits(q), W.bits(k_pool), W.bits(v_pool), qo_indptr, kv_indptr,
+                       np.asarray(kv_indices, np.int32), sm_scale, num_kv_heads, sel=sel)

@@ -1,0 +1,156 @@
+"""Chunked-prefill parity: the HIP matrix-core path (through the C ABI) against
+the fp64 oracle on the same seeded bf16 inputs, within 2e-3.  Needs an AMD GPU."""
+import numpy as np
+import pytest
+import torch
+
+import paged_gqa_decode_pa_amd as pa
+import workloads as W
+from gpu_util import (TOL, device, max_err, oracle_decode, oracle_prefill, run_decode, run_prefill,
+                      say)
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def _case(reqs, Hq, Hkv, D, num_slots, seed):
+    """reqs: [(list length L, chunk length C)] -> (qo_indptr, kv_indptr, kv_indices, q, k, v)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lengths = np.asarray([L for L, _ in reqs])
+    kv_indptr, kv_indices = W.slot_lists(lengths, num_slots, rng)
+    qo_indptr = np.concatenate([[0], np.cumsum([C for _, C in reqs])]).astype(np.int32)
+    dev = device()
+    q = W.normal_bf16((int(qo_indptr[-1]), Hq, D), seed * 5 + 1, dev)
+    k, v = W.make_pools(num_slots, Hkv, D, seed * 5 + 2, dev)
+    return qo_indptr, kv_indptr, kv_indices, q, k, v
+
+
+def _check(reqs, Hq, Hkv, D, seed, flags=0, num_slots=8192):
+    qo, ip, idx, q, k, v = _case(reqs, Hq, Hkv, D, num_slots, seed)
+    scale = W.softmax_scale(D)
+    out, lse = run_prefill(q, k, v, qo, ip, torch.as_tensor(idx, device=device()), scale, Hkv,
+                           flags=flags)
+    ref, ref_lse = oracle_prefill(q, k, v, qo, ip, idx, scale, Hkv)
+    e_out, e_lse = max_err(out, ref), max_err(lse, ref_lse)
+    say(f"  max|d| out={e_out:.3g} lse={e_lse:.3g}")
+    assert e_out <= TOL and e_lse <= TOL
+    return out, lse
+
+
+SMALL = [
+    # ([(L, C)], Hq, Hkv, D): tiles of 128/G chunk tokens, KV tiles of 64 (D=128) / 32 (D=256)
+    ([(1, 1), (5, 5), (40, 33), (300, 64), (700, 129), (100, 0)], 32, 8, 128),
+    ([(200, 200), (513, 130)], 8, 8, 128),          # group 1: 128-token tiles
+    ([(64, 17), (1000, 300)], 16, 8, 128),          # group 2
+    ([(90, 40), (333, 16), (2, 1)], 64, 8, 128),    # group 8: 16-token tiles
+    ([(50, 50), (400, 100)], 16, 4, 256),
+    ([(120, 7), (260, 200)], 8, 8, 256),
+    ([(77, 77), (31, 3)], 32, 4, 256),
+]
+
+
+@pytest.mark.parametrize("reqs,Hq,Hkv,D", SMALL,
+                         ids=[f"{c[1]}x{c[2]}x{c[3]}-{i}" for i, c in enumerate(SMALL)])
+def test_prefill_small_parity(reqs, Hq, Hkv, D):
+    say(f"prefill small parity reqs={reqs} Hq={Hq} Hkv={Hkv} D={D}")
+    _check(reqs, Hq, Hkv, D, seed=11 + Hq + D + len(reqs))
+
+
+@pytest.mark.parametrize("n", [2, 5, 16])
+def test_prefill_forced_splits(n):
+    say(f"prefill forced splits n={n}")
+    reqs = [(300, 64), (700, 129), (9, 9)]
+    base, base_lse = _check(reqs, 32, 8, 128, seed=7)
+    out, lse = _check(reqs, 32, 8, 128, seed=7, flags=pa.PA_PLAN_FORCE_SPLITS(n))
+    assert max_err(out, base.astype(np.float64)) <= TOL
+
+
+def test_prefill_xcd_order_neutral_and_deterministic():
+    say("prefill xcd order / determinism")
+    reqs = [(500, 200), (1200, 64)]
+    qo, ip, idx, q, k, v = _case(reqs, 32, 8, 128, 8192, 3)
+    idx_dev = torch.as_tensor(idx, device=device())
+    scale = W.softmax_scale(128)
+    a, _ = run_prefill(q, k, v, qo, ip, idx_dev, scale, 8)
+    b, _ = run_prefill(q, k, v, qo, ip, idx_dev, scale, 8)
+    c, _ = run_prefill(q, k, v, qo, ip, idx_dev, scale, 8, flags=pa.PA_PLAN_NO_XCD_ORDER)
+    assert np.array_equal(a, b)
+    assert np.array_equal(a, c)  # one unit per workgroup: placement does not change the sums
+
+
+def test_prefill_chunk_of_one_equals_decode():
+    say("prefill C=1 vs decode")
+    reqs = [(1, 1), (77, 1), (600, 1)]
+    qo, ip, idx, q, k, v = _case(reqs, 32, 8, 128, 4096, 5)
+    idx_dev = torch.as_tensor(idx, device=device())
+    scale = W.softmax_scale(128)
+    out_p, lse_p = run_prefill(q, k, v, qo, ip, idx_dev, scale, 8)
+    out_d, lse_d = run_decode(q, k, v, ip, idx_dev, scale, 8)
+    ref, ref_lse = oracle_decode(q, k, v, ip, idx, scale, 8)
+    assert max_err(out_p, ref) <= TOL and max_err(lse_p, ref_lse) <= TOL
+    assert max_err(out_p, out_d.astype(np.float64)) <= TOL
+
+
+def test_prefill_poisoned_pool():
+    say("prefill poisoned pool")
+    reqs = [(150, 40), (333, 100)]
+    qo, ip, idx, q, k, v = _case(reqs, 32, 8, 128, 8192, 9)
+    idx_dev = torch.as_tensor(idx, device=device())
+    scale = W.softmax_scale(128)
+    clean, _ = run_prefill(q, k, v, qo, ip, idx_dev, scale, 8)
+    W.poison_unreferenced(k, idx)
+    W.poison_unreferenced(v, idx)
+    dirty, _ = run_prefill(q, k, v, qo, ip, idx_dev, scale, 8)
+    assert np.array_equal(clean, dirty)
+
+
+def test_prefill_large_pool_offsets():
+    """Slots beyond 2^31 bytes of pool address (64-bit row offsets)."""
+    say("prefill large pool: 2,300,000 slots x 8 heads x 128")
+    num_slots = 2_300_000
+    dev = device()
+    rng = np.random.Generator(np.random.PCG64(21))
+    lengths = np.asarray([700, 260])
+    ip, idx = W.slot_lists(lengths, num_slots, rng)
+    idx[:64] = num_slots - 1 - np.arange(64)   # touch the very end of the pool
+    qo = np.asarray([0, 200, 330], np.int32)
+    q = W.normal_bf16((330, 32, 128), 22, dev)
+    k, v = W.make_pools(num_slots, 8, 128, 23, dev)
+    scale = W.softmax_scale(128)
+    out, lse = run_prefill(q, k, v, qo, ip, torch.as_tensor(idx, device=dev), scale, 8)
+    ref, ref_lse = oracle_prefill(q, k, v, qo, ip, idx, scale, 8)
+    assert max_err(out, ref) <= TOL and max_err(lse, ref_lse) <= TOL
+    del k, v
+    torch.cuda.empty_cache()
+
+
+def _sample_rows(qo, Hq, n_random, seed):
+    """Flat rows t*Hq + h: first and last chunk token of every request (all
+    heads), plus random rows."""
+    rows = []
+    for b in range(len(qo) - 1):
+        if qo[b + 1] > qo[b]:
+            for t in (qo[b], qo[b + 1] - 1):
+                rows.extend(int(t) * Hq + h for h in range(Hq))
+    rng = np.random.Generator(np.random.PCG64(seed))
+    rows.extend(rng.integers(0, int(qo[-1]) * Hq, n_random).tolist())
+    return np.unique(np.asarray(rows, np.int32))
+
+
+@pytest.mark.parametrize("spec", W.PREFILL_SPECS, ids=lambda s: s.name)
+def test_prefill_workload_sampled_parity(spec):
+    say(f"prefill workload {spec.name}: sampled rows")
+    dev = device()
+    case = W.make_prefill_case(spec, dev)
+    Hq, D = spec.num_qo_heads, spec.head_dim
+    idx_dev = torch.as_tensor(case.kv_indices, device=dev)
+    out, lse = run_prefill(case.q, case.k_pool, case.v_pool, case.qo_indptr, case.kv_indptr, idx_dev,
+                           case.sm_scale, spec.num_kv_heads)
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    rows = _sample_rows(case.qo_indptr, Hq, 768, spec.seed)
+    ref, ref_lse = oracle_prefill(case.q, case.k_pool, case.v_pool, case.qo_indptr, case.kv_indptr,
+                                  case.kv_indices, case.sm_scale, spec.num_kv_heads, sel=rows)
+    e_out = max_err(out.reshape(-1, D), ref.reshape(-1, D), rows=rows)
+    e_lse = max_err(lse.reshape(-1), ref_lse.reshape(-1), rows=rows)
+    say(f"  {rows.size} rows: max|d| out={e_out:.3g} lse={e_lse:.3g}")
+    assert e_out <= TOL and e_lse <= TOL
