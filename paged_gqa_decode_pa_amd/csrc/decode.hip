@@ -73,8 +73,8 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 // DPP lane moves inside 16-lane rows (all sources valid: permutations).
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
-                                                                 CTRL, 0xf, 0xf, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xf, 0xf,
+                                                              true));
 }
 constexpr int kQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]
 constexpr int kQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]
@@ -283,7 +283,8 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<G>(), 8))) void decode_
         continue;  // padding unit (uniform over the workgroup)
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    // wave index as a scalar: the tile loop below is uniform per wave
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int r = lane / LPR;      // row within an instruction
     const int c = lane % LPR;      // 16-byte chunk of the row
@@ -393,37 +394,49 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<G>(), 8))) void decode_
         }
     };
 
-    // Tiles wave, wave+4, wave+8, ...  Loads are issued in the order
-    //   S(i) K(i) V(i) S(i+1) | K(i+1) V(i+1) S(i+2) | ...
-    // (S = slot ids): the next tile's K rows are requested as soon as this
-    // tile's scores have consumed the K registers, and its V rows once the
-    // weighted sum has consumed the V registers, so one half of a tile is
-    // always in flight while the other half is computed, without a second
-    // register set.
+    // Tiles wave, wave+4, wave+8, ... (t0, t1, ...) alternate between two
+    // register sets A and B: while the tile in one set is computed, the next
+    // tile's K and V rows are in flight into the other, and a set is refilled
+    // (two tiles ahead) as soon as its tile is done.  Slot ids are fetched two
+    // tiles ahead of their rows.  Every load is unconditional (slot ids of
+    // tiles past the end are clamped to the last entry and re-read one row),
+    // so each set is refilled in place.
     int tile = wave;
     if (tile < n_tiles) {
-        int32_t slot[NI];
-        uint4 kr[NI], vr[NI];
-        load_slots(slot, tile);
-        load_k(kr, slot);
-        load_v(vr, slot);
-        bool more = tile + WAVES < n_tiles;
-        if (more)
-            load_slots(slot, tile + WAVES);
-        while (true) {
+        int32_t sa[NI], sb[NI];
+        uint4 ka[NI], va[NI], kb[NI], vb[NI];
+        load_slots(sa, tile);
+        load_slots(sb, tile + WAVES);
+        load_k(ka, sa);
+        load_v(va, sa);
+        load_k(kb, sb);
+        load_v(vb, sb);
+        load_slots(sa, tile + 2 * WAVES);
+        load_slots(sb, tile + 3 * WAVES);
+        auto compute = [&](const uint4(&k)[NI], const uint4(&v)[NI]) {
             float sc[NI], pw[NI];
-            qk(kr, sc, tile);
-            if (more)
-                load_k(kr, slot);
+            qk(k, sc, tile);
             softmax(sc, pw);
-            pv(vr, pw);
-            if (!more)
-                break;
-            load_v(vr, slot);
+            pv(v, pw);
+        };
+        while (true) {
+            compute(ka, va);
+            // refills stay behind the last use of the registers they overwrite
+            __builtin_amdgcn_sched_barrier(0);
+            load_k(ka, sa);
+            load_v(va, sa);
+            load_slots(sa, tile + 4 * WAVES);
             tile += WAVES;
-            more = tile + WAVES < n_tiles;
-            if (more)
-                load_slots(slot, tile + WAVES);
+            if (tile >= n_tiles)
+                break;
+            compute(kb, vb);
+            __builtin_amdgcn_sched_barrier(0);
+            load_k(kb, sb);
+            load_v(vb, sb);
+            load_slots(sb, tile + 4 * WAVES);
+            tile += WAVES;
+            if (tile >= n_tiles)
+                break;
         }
     }
 
