@@ -99,9 +99,14 @@ typedef enum pa_status {
  * grouping neighbouring requests on one XCD. */
 #define PA_PLAN_NO_XCD_ORDER 0x1u
 
+/* Largest max_kv_total a plan accepts: list entries are addressed with 32-bit
+ * byte offsets. */
+#define PA_MAX_KV_TOTAL (1LL << 29)
+
 /*
  * pa_plan_create: allocate a plan object for up to max_batch requests whose
- * slot lists hold at most max_kv_total entries in total, and (prefill) at most
+ * slot lists hold at most max_kv_total (<= PA_MAX_KV_TOTAL) entries in total,
+ * and (prefill) at most
  * max_q_total query rows.  All device and pinned-host memory the plan and its
  * runs need is allocated here, on the current HIP device, once.
  *   num_qo_heads % num_kv_heads == 0, group Hq/Hkv in {1, 2, 4, 8};
@@ -247,6 +252,14 @@ pa_status pa_partition(const int32_t *kv_indptr_host, const int32_t *qo_indptr_h
  */
 pa_status pa_profile_begin(pa_plan_t *plan, int32_t capacity);
 pa_status pa_profile_end(pa_plan_t *plan, double *total_ms, int32_t *n_launches);
+
+/*
+ * Host time of the last successful pa_plan call on this plan, measured inside
+ * the library with a steady clock: *total_us is the whole call, *wait_us the
+ * part spent waiting for the upload of two calls back to finish (its pinned
+ * staging buffer is reused).  PA_ERR_INVALID_ARG for null pointers.
+ */
+pa_status pa_plan_host_timing(const pa_plan_t *plan, double *total_us, double *wait_us);
 
 /* Library version as major*10000 + minor*100 + patch. */
 int32_t pa_version(void);

@@ -30,6 +30,7 @@ PA_ERR_HIP = 5
 
 PA_PLAN_FORCE_SPLITS_SHIFT = 8
 PA_MAX_FORCED_SPLITS = 256
+PA_MAX_KV_TOTAL = 1 << 29
 PA_PLAN_NO_XCD_ORDER = 0x1
 
 
@@ -92,6 +93,9 @@ def _load() -> ctypes.CDLL:
     lib.pa_profile_begin.restype = ctypes.c_int
     lib.pa_profile_end.argtypes = [vp, ctypes.POINTER(ctypes.c_double), i32p]
     lib.pa_profile_end.restype = ctypes.c_int
+    lib.pa_plan_host_timing.argtypes = [vp, ctypes.POINTER(ctypes.c_double),
+                                        ctypes.POINTER(ctypes.c_double)]
+    lib.pa_plan_host_timing.restype = ctypes.c_int
     return lib
 
 
@@ -234,6 +238,15 @@ def pa_partition(kv_indptr, qo_indptr, num_qo_heads: int, num_kv_heads: int, hea
     u = np.frombuffer(bytes(units), dtype=WORK_UNIT_DTYPE)[: n_u.value].copy()
     m = np.frombuffer(bytes(merges), dtype=MERGE_UNIT_DTYPE)[: n_m.value].copy()
     return offs, u, m, n_p.value
+
+
+def pa_plan_host_timing(plan):
+    """-> (host microseconds of the last pa_plan call, of which waiting for an
+    earlier upload)."""
+    tot, wait = ctypes.c_double(), ctypes.c_double()
+    _check(_lib.pa_plan_host_timing(plan, ctypes.byref(tot), ctypes.byref(wait)),
+           "pa_plan_host_timing")
+    return tot.value, wait.value
 
 
 def pa_profile_begin(plan, capacity: int) -> None:

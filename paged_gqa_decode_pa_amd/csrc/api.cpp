@@ -8,6 +8,7 @@
 // "优化历程".
 #include <hip/hip_runtime.h>
 
+#include <chrono>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -42,6 +43,8 @@ struct pa_plan {
     int64_t kv_total = 0;
     int32_t q_total = 0;
     int32_t n_workgroups = 0, n_units = 0, n_merges = 0, n_partials = 0;
+    pa::PartitionScratch scratch;  // host working arrays of the partition
+    double plan_total_us = 0.0, plan_wait_us = 0.0;  // host time of the last pa_plan
     // kernel timing: event pairs recorded around the attention kernel
     std::vector<hipEvent_t> prof_events;   // 2 per pair
     mutable int32_t prof_used = 0;
@@ -223,7 +226,7 @@ pa_status pa_partition(const int32_t *kv_indptr_host, const int32_t *qo_indptr_h
                         head_dim, flags, max_workgroups, pa::kNumXcd};
     pa::PartitionResult r;
     const char *detail = "";
-    pa_status s = pa::partition(a, wg_offsets, wg_capacity, units, unit_capacity, merges,
+    pa_status s = pa::partition(a, nullptr, wg_offsets, wg_capacity, units, unit_capacity, merges,
                                 merge_capacity, &r, &detail);
     *n_workgroups = r.n_workgroups;
     *n_units = r.n_units;
@@ -241,8 +244,8 @@ pa_status pa_plan_create(pa_plan_t **out, int32_t max_batch, int64_t max_kv_tota
         return fail(PA_ERR_INVALID_ARG, "out is null");
     if (max_batch < 0 || max_kv_total < 0 || max_q_total < 0)
         return fail(PA_ERR_INVALID_ARG, "negative capacity");
-    if (max_kv_total > 0x7fffffffLL)
-        return fail(PA_ERR_INVALID_ARG, "max_kv_total above int32 range");
+    if (max_kv_total > PA_MAX_KV_TOTAL)
+        return fail(PA_ERR_INVALID_ARG, "max_kv_total above PA_MAX_KV_TOTAL");
     if (num_qo_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0)
         return fail(PA_ERR_INVALID_ARG, "head counts and head_dim must be positive");
     if (!pa::supported_shape(num_qo_heads, num_kv_heads, head_dim))
@@ -306,6 +309,8 @@ void pa_plan_destroy(pa_plan_t *plan) { release(plan); }
 
 pa_status pa_plan(pa_plan_t *p, const int32_t *kv_indptr_host, const int32_t *qo_indptr_host,
                   int32_t batch, uint32_t flags, pa_stream_t stream) {
+    using clock = std::chrono::steady_clock;
+    const clock::time_point t_start = clock::now();
     if (!p)
         return fail(PA_ERR_INVALID_ARG, "plan is null");
     if (batch < 0)
@@ -331,11 +336,13 @@ pa_status pa_plan(pa_plan_t *p, const int32_t *kv_indptr_host, const int32_t *qo
         return fail(PA_ERR_INVALID_ARG, "current HIP device differs from the plan's device");
 
     const int s = p->next_stage;
+    const clock::time_point t_wait = clock::now();
     if (p->stage_pending[s]) {
         if ((e = hipEventSynchronize(p->stage_done[s])) != hipSuccess)
             return hip_fail(e, "waiting for an earlier plan upload");
         p->stage_pending[s] = false;
     }
+    const clock::time_point t_waited = clock::now();
     // partition straight into the staging buffer at capacity offsets, then
     // pack the three lists together and upload them with one copy
     char *stage = static_cast<char *>(p->h_stage[s]);
@@ -348,7 +355,8 @@ pa_status pa_plan(pa_plan_t *p, const int32_t *kv_indptr_host, const int32_t *qo
     pa::PartitionResult r;
     const char *detail = "";
     auto clamp32 = [](int64_t v) { return (int32_t)std::min<int64_t>(v, 0x7fffffff); };
-    pa_status st = pa::partition(a, offsets, clamp32(p->wg_cap + 1), units, clamp32(p->unit_cap),
+    pa_status st = pa::partition(a, &p->scratch, offsets, clamp32(p->wg_cap + 1), units,
+                                 clamp32(p->unit_cap),
                                  merges, clamp32(p->merge_cap), &r, &detail);
     if (st != PA_OK)
         return fail(st, detail);
@@ -376,6 +384,16 @@ pa_status pa_plan(pa_plan_t *p, const int32_t *kv_indptr_host, const int32_t *qo
     p->n_units = r.n_units;
     p->n_merges = r.n_merges;
     p->n_partials = r.n_partials;
+    p->plan_wait_us = std::chrono::duration<double, std::micro>(t_waited - t_wait).count();
+    p->plan_total_us = std::chrono::duration<double, std::micro>(clock::now() - t_start).count();
+    return PA_OK;
+}
+
+pa_status pa_plan_host_timing(const pa_plan_t *p, double *total_us, double *wait_us) {
+    if (!p || !total_us || !wait_us)
+        return fail(PA_ERR_INVALID_ARG, "null argument");
+    *total_us = p->plan_total_us;
+    *wait_us = p->plan_wait_us;
     return PA_OK;
 }
 

@@ -19,16 +19,22 @@
 //     rows (4 rows at D = 128, 2 at D = 256): fully coalesced 128-bit loads,
 //     each lane gathering through its own slot id;
 //   * a wave walks the unit in tiles of NI instructions (NI*RPI tokens); the
-//     four waves take every fourth tile; the next tile's K rows are requested
-//     as soon as the current scores are done with the K registers and its V
-//     rows once the current weighted sum is done with the V registers, so half
-//     a tile is always in flight without a second register set;
+//     four waves take every fourth tile; tiles alternate between two register
+//     sets, so one tile's K and V rows are in flight while the other's are
+//     used;
+//   * slot ids are read through a buffer descriptor whose range ends at the
+//     unit's last entry: an id past it reads as 0 (a valid slot, whose row
+//     the masked scores ignore), so the loads of the look-ahead need no
+//     clamping;
 //   * each K row is used by all G query heads of its group straight from the
 //     registers it was loaded into (dot2 bf16 products, fp32 accumulation);
 //     the partial dot products are reduced across the row's lanes with DPP
 //     and the reduction is "transposed": G values per lane go in, and lane c
 //     comes out holding the full score of head c % G, so each (token, head)
-//     exponential is computed by LPR/G lanes instead of LPR;
+//     exponential is computed by LPR/G lanes instead of LPR.  Lane c keeps
+//     its query heads in the order h ^ (c % G), so that at every exchange
+//     step a lane adds its partner's value at a fixed register index (no
+//     per-lane selects);
 //   * softmax is online per (lane row, head) with a lazily moved running
 //     maximum (it moves only when a score exceeds it by more than 8 in the
 //     log2 domain, so weights stay <= 256 and rescaling is rare);
@@ -61,6 +67,9 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNoMax = -1.0e30f;
 // Lazy rescale threshold (log2 domain): weights stay below 2^8.
 constexpr float kRescaleSlack = 8.0f;
+// Word 3 of a raw buffer descriptor: 32-bit data format, no swizzle, no
+// index stride.
+constexpr int32_t kBufferWord3 = 0x00020000;
 
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
@@ -119,59 +128,57 @@ __device__ __forceinline__ float group_bcast(float x, int h, int lane) {
     }
 }
 
-// One exchange step of the transposed reduction across partner lane ^ (1<<BIT):
-// the lane keeps the half of its N values whose head index has bit BIT equal to
-// its own lane bit, and adds the partner's copy of that half.
-template <int BIT, int N>
-__device__ __forceinline__ void exchange_step(float *v, bool upper) {
-#pragma unroll
-    for (int m = 0; m < N / 2; m++) {
-        float keep = upper ? v[2 * m + 1] : v[2 * m];
-        float send = upper ? v[2 * m] : v[2 * m + 1];
-        float recv;
-        if constexpr (BIT == 0)
-            recv = dpp_mov<kQuadXor1>(send);
-        else if constexpr (BIT == 1)
-            recv = dpp_mov<kQuadXor2>(send);
-        else
-            recv = shfl_xor(send, 1 << BIT);
-        v[m] = keep + recv;
-    }
-}
-
-// Sum G per-lane values over the LPR lanes of a row.  On return lane c of the
-// row holds the full sum of value (c % G).
+// Score partials of one K row for the G heads, reduced across the row's LPR
+// lanes (the reduction is "transposed": lane c returns the full dot product
+// of head c % G).  Lane c holds, at index j, the query of head j ^ (c % G).
+// Exchange step k pairs lane c with c ^ 2^k: the partner's value at index
+// 2m+1 belongs to the same head as this lane's value at 2m, so
+// v[m] = v[2m] + partner(v[2m+1]) halves the values while keeping the head of
+// index m equal to (m << (k+1)) ^ (c % G); after log2(G) steps lane c holds
+// head c % G, and the remaining steps add the lanes of the row that hold the
+// same head.  In the first step the partner's value is the starting value of
+// the dot-product chain of index 2m, which saves the add and the zeroing of
+// that chain's accumulator.
 template <int G, int LPR>
-__device__ __forceinline__ float row_reduce_transposed(float (&v)[G], int lane) {
+__device__ __forceinline__ float row_scores(const uint32_t (&qv)[G][4], const uint4 &k) {
+    auto chain = [&](int j, float c) {
+        float a = dot2_bf16(qv[j][0], k.x, c);
+        a = dot2_bf16(qv[j][1], k.y, a);
+        a = dot2_bf16(qv[j][2], k.z, a);
+        return dot2_bf16(qv[j][3], k.w, a);
+    };
     float x;
     if constexpr (G == 1) {
-        x = v[0];
+        x = chain(0, 0.f);
         x += dpp_mov<kQuadXor1>(x);
         x += dpp_mov<kQuadXor2>(x);
-        x += dpp_mov<kRowRor4>(x);
-        x += dpp_mov<kRowRor8>(x);
-    } else if constexpr (G == 2) {
-        exchange_step<0, 2>(v, lane & 1);
-        x = v[0];
-        x += dpp_mov<kQuadXor2>(x);
-        x += dpp_mov<kRowRor4>(x);
-        x += dpp_mov<kRowRor8>(x);
-    } else if constexpr (G == 4) {
-        exchange_step<0, 4>(v, lane & 1);
-        exchange_step<1, 2>(v, (lane >> 1) & 1);
-        x = v[0];
-        x += dpp_mov<kRowRor4>(x);
-        x += dpp_mov<kRowRor8>(x);
     } else {
-        exchange_step<0, 8>(v, lane & 1);
-        exchange_step<1, 4>(v, (lane >> 1) & 1);
-        exchange_step<2, 2>(v, (lane >> 2) & 1);
+        float v[G / 2];
+#pragma unroll
+        for (int m = 0; m < G / 2; m++)
+            v[m] = chain(2 * m, dpp_mov<kQuadXor1>(chain(2 * m + 1, 0.f)));
+        if constexpr (G >= 4) {
+#pragma unroll
+            for (int m = 0; m < G / 4; m++)
+                v[m] = v[2 * m] + dpp_mov<kQuadXor2>(v[2 * m + 1]);
+        }
+        if constexpr (G >= 8)
+            v[0] = v[0] + shfl_xor(v[1], 4);
         x = v[0];
-        x += dpp_mov<kRowRor8>(x);
+        if constexpr (G == 2)
+            x += dpp_mov<kQuadXor2>(x);
     }
+    if constexpr (G <= 4)
+        x += dpp_mov<kRowRor4>(x);
+    x += dpp_mov<kRowRor8>(x);
     if constexpr (LPR == 32)
         x += shfl_xor(x, 16);
     return x;
+}
+
+// Buffer descriptor over 4-byte elements [0, n) of p.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t index_rsrc(const int32_t *p, int32_t n) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t *>(p), (short)0, n * 4, kBufferWord3);
 }
 
 template <int D>
@@ -290,14 +297,14 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<G>(), 8))) void decode_
     const int c = lane % LPR;      // 16-byte chunk of the row
     const int hsel = lane % G;     // head whose score this lane holds after reduction
 
-    // query rows of the group: q[b, kvh*G + h, 8c .. 8c+7]
+    // query rows of the group: qv[j] = q[b, kvh*G + (j ^ hsel), 8c .. 8c+7]
     uint32_t qv[G][4];
     {
         const uint16_t *qrow = q + ((int64_t)unit.request * num_qo_heads + (int64_t)unit.kv_head * G) * D + c * 8;
 #pragma unroll
-        for (int h = 0; h < G; h++) {
-            uint4 t = *reinterpret_cast<const uint4 *>(qrow + (int64_t)h * D);
-            qv[h][0] = t.x; qv[h][1] = t.y; qv[h][2] = t.z; qv[h][3] = t.w;
+        for (int j = 0; j < G; j++) {
+            uint4 t = *reinterpret_cast<const uint4 *>(qrow + (int64_t)(j ^ hsel) * D);
+            qv[j][0] = t.x; qv[j][1] = t.y; qv[j][2] = t.z; qv[j][3] = t.w;
         }
     }
 
@@ -313,14 +320,20 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<G>(), 8))) void decode_
         for (int e = 0; e < 8; e++)
             acc[h][e] = 0.f;
 
+    // slot ids of a tile: entries kv_begin + tile*TILE + r + i*RPI of the
+    // list.  Entries at or past kv_end (the tail of the last tile and the
+    // tiles the look-ahead requests past the end) are clamped to the unit's
+    // last entry, so every row read is one the unit references.  In bytes:
+    // min(e + 4*i*RPI, last) = min(e, last - 4*i*RPI) + 4*i*RPI, whose
+    // constant term goes into the load's immediate offset.
+    const __amdgpu_buffer_rsrc_t slot_rsrc = index_rsrc(kv_indices + kv_begin, kv_end - kv_begin);
+    const int32_t last4 = (kv_end - kv_begin - 1) * 4;
     auto load_slots = [&](int32_t(&slot)[NI], int tile) {
-        const int32_t base = kv_begin + tile * TILE + r;
+        const int32_t e4 = (tile * TILE + r) * 4;
 #pragma unroll
-        for (int i = 0; i < NI; i++) {
-            int32_t tok = base + i * RPI;
-            tok = tok < kv_end ? tok : kv_end - 1;
-            slot[i] = kv_indices[tok];
-        }
+        for (int i = 0; i < NI; i++)
+            slot[i] = __builtin_amdgcn_raw_buffer_load_b32(
+                slot_rsrc, min(e4, last4 - i * RPI * 4) + i * RPI * 4, 0, 0);
     };
     auto load_k = [&](uint4(&k)[NI], const int32_t(&slot)[NI]) {
 #pragma unroll
@@ -334,20 +347,12 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<G>(), 8))) void decode_
     };
     // scores of this lane's head (lane % G) for the tile's tokens, log2 domain
     auto qk = [&](const uint4(&k)[NI], float(&s)[NI], int tile) {
-        const int32_t base = kv_begin + tile * TILE + r;
+        // entries of the tile left in the unit (uniform)
+        const int32_t left = kv_end - kv_begin - tile * TILE;
 #pragma unroll
         for (int i = 0; i < NI; i++) {
-            float part[G];
-#pragma unroll
-            for (int h = 0; h < G; h++) {
-                float a = dot2_bf16(qv[h][0], k[i].x, 0.f);
-                a = dot2_bf16(qv[h][1], k[i].y, a);
-                a = dot2_bf16(qv[h][2], k[i].z, a);
-                a = dot2_bf16(qv[h][3], k[i].w, a);
-                part[h] = a;
-            }
-            const float sc = row_reduce_transposed<G, LPR>(part, lane) * scale_log2;
-            s[i] = (base + i * RPI < kv_end) ? sc : -INFINITY;
+            const float sc = row_scores<G, LPR>(qv, k[i]) * scale_log2;
+            s[i] = (r + i * RPI < left) ? sc : -INFINITY;
         }
     };
     // online softmax: scores -> weights, running max / sum, accumulator rescale

@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <stddef.h>
 
+#include <vector>
+
 #include "pa.h"
 
 namespace pa {
@@ -57,12 +59,25 @@ struct PartitionResult {
     int32_t n_partials = 0;    // partial slots used
 };
 
+// Working arrays of the automatic decode partition, kept by a plan between
+// steps so that a step's partition allocates nothing once they have grown.
+struct PartitionScratch {
+    struct Piece {
+        int32_t seg, lo, hi;  // segment (KV head * batch + request), list range
+        int32_t ordinal;      // index of the piece within its segment
+    };
+    std::vector<int32_t> seg_request, seg_pieces, seg_first, seg_merge, bin_stream;
+    std::vector<Piece> stream;
+};
+
 // Validates the arguments; fills wg_offsets (n_workgroups + 1 entries), units
 // and merges up to the capacities.  Returns PA_ERR_CAPACITY (with the counts
-// filled) if a capacity is too small.
-pa_status partition(const PartitionArgs &a, int32_t *wg_offsets, int32_t wg_capacity,
-                    pa_work_unit *units, int32_t unit_capacity, pa_merge_unit *merges,
-                    int32_t merge_capacity, PartitionResult *res, const char **detail);
+// filled) if a capacity is too small.  scratch may be null (then a temporary
+// one is used).
+pa_status partition(const PartitionArgs &a, PartitionScratch *scratch, int32_t *wg_offsets,
+                    int32_t wg_capacity, pa_work_unit *units, int32_t unit_capacity,
+                    pa_merge_unit *merges, int32_t merge_capacity, PartitionResult *res,
+                    const char **detail);
 
 // Upper bounds on what a plan created with these limits can need: workgroup
 // offsets (entries), work and merge units, and partial storage in rows of

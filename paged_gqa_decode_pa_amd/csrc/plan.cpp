@@ -135,17 +135,27 @@ int32_t prefill_tile_tokens(int32_t group) { return kPrefillTileRows / group; }
 // ---------------------------------------------------------------------------
 // decode, automatic: balanced workgroup bins
 // ---------------------------------------------------------------------------
-void decode_bins(const PartitionArgs &a, Groups *groups, std::vector<pa_merge_unit> *merges,
-                 int32_t *n_partials) {
+// Segment s = h * B + b is KV head h of request b.  Bin i (one workgroup)
+// holds the opening piece of segment i (i < number of segments), then a run
+// of the "stream": the remainders of all segments in segment order, cut into
+// pieces where a bin's budget ends.  Pass 1 cuts the stream; pass 2 numbers
+// partial slots and merge units; pass 3 writes the units workgroup by
+// workgroup.  Linear in segments + bins; the arrays live in the caller's
+// workspace, which only grows.
+pa_status decode_bins(const PartitionArgs &a, PartitionScratch &ws, int32_t *wg_offsets,
+                      int32_t wg_capacity, pa_work_unit *units_out, int32_t unit_capacity,
+                      pa_merge_unit *merges_out, int32_t merge_capacity, PartitionResult *res,
+                      const char **detail) {
     const int32_t B = a.batch, Hkv = a.num_kv_heads;
-    struct Piece {
-        int32_t seg, lo, hi;
-    };
     const int64_t n_seg = (int64_t)B * Hkv;
-    auto seg_request = [&](int64_t s) { return (int32_t)(s % B); };
-    auto seg_head = [&](int64_t s) { return (int32_t)(s / B); };
+    // request of each segment, filled without divisions (segments are few,
+    // but one integer division per piece would dominate the partition)
+    ws.seg_request.resize(n_seg);
+    for (int32_t h = 0, s = 0; h < Hkv; h++)
+        for (int32_t b = 0; b < B; b++)
+            ws.seg_request[s++] = b;
     auto seg_len = [&](int64_t s) {
-        int32_t b = seg_request(s);
+        const int32_t b = ws.seg_request[s];
         return a.kv_indptr[b + 1] - a.kv_indptr[b];
     };
     const int64_t total = B > 0 ? (int64_t)a.kv_indptr[B] * Hkv : 0;
@@ -153,110 +163,132 @@ void decode_bins(const PartitionArgs &a, Groups *groups, std::vector<pa_merge_un
     const int64_t n = std::max<int64_t>(1, std::min(max_wg, ceil_div(total, min_unit_tokens(a.head_dim))));
     const double ov = kPieceOverheadTokens;
     const double cap = ((double)total + ov * (double)(n_seg + n)) / (double)n;
-
-    std::vector<std::vector<Piece>> bins(n);
-    std::vector<double> fill(n, 0.0);
-    struct Rest {
-        int32_t seg, from;
+    // entries of the opening piece of segment s < n
+    auto open_len = [&](int64_t s) {
+        return (int32_t)std::min<double>(seg_len(s), std::max(0.0, cap - ov));
     };
-    std::vector<Rest> rest;
-    rest.reserve(n_seg);
-    // opening pieces: segment i starts workgroup i
+
+    ws.seg_pieces.assign(n_seg, 0);
+    ws.seg_first.resize(n_seg);
+    ws.seg_merge.resize(n_seg);
+    ws.bin_stream.resize(n + 1);
+    ws.stream.clear();
+
+    // pass 1: cut the stream over the bins
+    int64_t p = 0;
+    double fill = (0 < n_seg) ? open_len(0) + ov : 0.0;  // fill of bin p
+    ws.bin_stream[0] = 0;
+    auto advance = [&]() {
+        p++;
+        ws.bin_stream[p] = (int32_t)ws.stream.size();
+        fill = (p < n_seg) ? open_len(p) + ov : 0.0;
+    };
     for (int64_t s = 0; s < n_seg; s++) {
         const int32_t L = seg_len(s);
+        int32_t off = 0;
         if (s < n) {
-            const int32_t t = (int32_t)std::min<double>(L, std::max(0.0, cap - ov));
-            bins[s].push_back({(int32_t)s, 0, t});
-            fill[s] += t + ov;
-            if (L > t)
-                rest.push_back({(int32_t)s, t});
-        } else {
-            rest.push_back({(int32_t)s, 0});
+            ws.seg_pieces[s] = 1;  // the opening piece
+            off = open_len(s);
+            if (off >= L)
+                continue;
         }
-    }
-    // the rest streams over the workgroups in order
-    int64_t p = 0;
-    for (const Rest &r : rest) {
-        const int32_t L = seg_len(r.seg);
-        int32_t off = r.from;
         if (L == 0) {  // an empty segment still writes its (empty) result
-            while (p < n - 1 && fill[p] + ov > cap)
-                p++;
-            bins[p].push_back({r.seg, 0, 0});
-            fill[p] += ov;
+            while (p < n - 1 && fill + ov > cap)
+                advance();
+            ws.stream.push_back({(int32_t)s, 0, 0, ws.seg_pieces[s]++});
+            fill += ov;
             continue;
         }
         while (off < L) {
-            while (p < n - 1 && fill[p] + ov + kMinPieceTokens > cap)
-                p++;
+            while (p < n - 1 && fill + ov + kMinPieceTokens > cap)
+                advance();
             int32_t take = L - off;
             if (p < n - 1) {
-                take = std::min<int32_t>(take, (int32_t)(cap - fill[p] - ov));
+                take = std::min<int32_t>(take, (int32_t)(cap - fill - ov));
                 if (L - off - take < kMinPieceTokens)
                     take = L - off;  // no sliver left for another workgroup
             }
-            bins[p].push_back({r.seg, off, off + take});
-            fill[p] += take + ov;
+            ws.stream.push_back({(int32_t)s, off, off + take, ws.seg_pieces[s]++});
+            fill += take + ov;
             off += take;
         }
     }
-    // partial slots: contiguous per segment, in segment order
-    std::vector<int32_t> pieces_of(n_seg, 0);
-    for (auto &bin : bins)
-        for (const Piece &pc : bin)
-            pieces_of[pc.seg]++;
-    std::vector<int32_t> first(n_seg, -1), next(n_seg, 0);
+    while (p < n)
+        advance();  // bin_stream[i] for the bins after the last used one, and [n]
+
+    // pass 2: partial slots contiguous per segment in segment order; merge
+    // units in (request, head) order
     int32_t np = 0;
     for (int64_t s = 0; s < n_seg; s++) {
-        if (pieces_of[s] > 1) {
-            first[s] = np;
-            np += pieces_of[s];
-        }
+        ws.seg_first[s] = ws.seg_pieces[s] > 1 ? np : -1;
+        np += ws.seg_pieces[s] > 1 ? ws.seg_pieces[s] : 0;
     }
-    *n_partials = np;
-    // merges in (request, head) order
-    std::vector<int32_t> merge_of(n_seg, -1);
-    for (int32_t b = 0; b < B; b++) {
+    int32_t n_merges = 0;
+    for (int32_t b = 0; b < B; b++)
         for (int32_t h = 0; h < Hkv; h++) {
             const int64_t s = (int64_t)h * B + b;
-            if (pieces_of[s] > 1) {
-                merge_of[s] = (int32_t)merges->size();
-                pa_merge_unit m;
-                std::memset(&m, 0, sizeof m);
-                m.request = b;
-                m.kv_head = h;
-                m.q_begin = b;
-                m.q_end = b + 1;
-                m.first_partial = first[s];
-                m.n_parts = pieces_of[s];
-                merges->push_back(m);
-            }
+            ws.seg_merge[s] = ws.seg_pieces[s] > 1 ? n_merges++ : -1;
         }
-    }
-    // workgroup ids: bins in contiguous blocks per XCD
+
     const bool xcd = !(a.flags & PA_PLAN_NO_XCD_ORDER) && a.num_xcd > 1;
     const int64_t per_xcd = xcd ? ceil_div(n, a.num_xcd) : n;
     const int64_t n_wg = xcd ? per_xcd * a.num_xcd : n;
-    groups->assign(n_wg, {});
-    for (int64_t i = 0; i < n; i++) {
-        const int64_t wg = xcd ? (i % per_xcd) * a.num_xcd + i / per_xcd : i;
-        auto &g = (*groups)[wg];
-        for (const Piece &pc : bins[i]) {
-            pa_work_unit u;
-            const int32_t b = seg_request(pc.seg);
-            u.request = b;
-            u.kv_head = seg_head(pc.seg);
-            u.kv_begin = a.kv_indptr[b] + pc.lo;
-            u.kv_end = a.kv_indptr[b] + pc.hi;
-            u.q_begin = b;
-            u.q_end = b + 1;
-            u.partial = pieces_of[pc.seg] > 1 ? first[pc.seg] + next[pc.seg]++ : -1;
-            u.diag = u.kv_end - 1;
-            u.merge = merge_of[pc.seg];
-            u.reserved0 = u.reserved1 = u.reserved2 = 0;
-            g.push_back(u);
+    const int64_t n_units = std::min<int64_t>(n, n_seg) + (int64_t)ws.stream.size();
+    res->n_workgroups = (int32_t)n_wg;
+    res->n_units = (int32_t)n_units;
+    res->n_merges = n_merges;
+    res->n_partials = np;
+    if (n_wg + 1 > wg_capacity || n_units > unit_capacity || n_merges > merge_capacity)
+        return fail(detail, "plan capacity exceeded", PA_ERR_CAPACITY);
+
+    for (int32_t b = 0; b < B; b++)
+        for (int32_t h = 0; h < Hkv; h++) {
+            const int64_t s = (int64_t)h * B + b;
+            if (ws.seg_merge[s] < 0)
+                continue;
+            pa_merge_unit &m = merges_out[ws.seg_merge[s]];
+            std::memset(&m, 0, sizeof m);
+            m.request = b;
+            m.kv_head = h;
+            m.q_begin = b;
+            m.q_end = b + 1;
+            m.first_partial = ws.seg_first[s];
+            m.n_parts = ws.seg_pieces[s];
+        }
+
+    // pass 3: workgroup ids hold the bins in contiguous blocks per XCD
+    // (bin i runs as workgroup (i % per_xcd) * num_xcd + i / per_xcd)
+    auto emit = [&](pa_work_unit &u, int32_t seg, int32_t lo, int32_t hi, int32_t ordinal) {
+        const int32_t b = ws.seg_request[seg];
+        u.request = b;
+        u.kv_head = (seg - b) / B;
+        u.kv_begin = a.kv_indptr[b] + lo;
+        u.kv_end = a.kv_indptr[b] + hi;
+        u.q_begin = b;
+        u.q_end = b + 1;
+        u.partial = ws.seg_first[seg] >= 0 ? ws.seg_first[seg] + ordinal : -1;
+        u.diag = u.kv_end - 1;
+        u.merge = ws.seg_merge[seg];
+        u.reserved0 = u.reserved1 = u.reserved2 = 0;
+    };
+    const int64_t stride = xcd ? a.num_xcd : 1;   // workgroup w = k * stride + x
+    int32_t pos = 0;
+    for (int64_t k = 0, w = 0; k < n_wg / stride; k++) {
+        for (int64_t x = 0; x < stride; x++, w++) {
+            wg_offsets[w] = pos;
+            const int64_t i = x * per_xcd + k;
+            if (i >= n)
+                continue;  // padding workgroup
+            if (i < n_seg)
+                emit(units_out[pos++], (int32_t)i, 0, open_len(i), 0);
+            for (int32_t j = ws.bin_stream[i]; j < ws.bin_stream[i + 1]; j++) {
+                const PartitionScratch::Piece &pc = ws.stream[j];
+                emit(units_out[pos++], pc.seg, pc.lo, pc.hi, pc.ordinal);
+            }
         }
     }
+    wg_offsets[n_wg] = pos;
+    return PA_OK;
 }
 
 }  // namespace
@@ -297,9 +329,10 @@ void partition_capacity(int32_t max_batch, int64_t max_kv_total, int32_t max_q_t
     *max_partial_rows = std::max(dec * g, (max_q_total > 0) ? pre * kPrefillTileRows : 0);
 }
 
-pa_status partition(const PartitionArgs &a, int32_t *wg_offsets, int32_t wg_capacity,
-                    pa_work_unit *units_out, int32_t unit_capacity, pa_merge_unit *merges_out,
-                    int32_t merge_capacity, PartitionResult *res, const char **detail) {
+pa_status partition(const PartitionArgs &a, PartitionScratch *scratch, int32_t *wg_offsets,
+                    int32_t wg_capacity, pa_work_unit *units_out, int32_t unit_capacity,
+                    pa_merge_unit *merges_out, int32_t merge_capacity, PartitionResult *res,
+                    const char **detail) {
     *res = PartitionResult{};
     if (a.batch < 0)
         return fail(detail, "batch < 0", PA_ERR_INVALID_ARG);
@@ -340,7 +373,9 @@ pa_status partition(const PartitionArgs &a, int32_t *wg_offsets, int32_t wg_capa
     const bool xcd = !(a.flags & PA_PLAN_NO_XCD_ORDER) && a.num_xcd > 1;
 
     if (!prefill && !forced) {
-        decode_bins(a, &groups, &merges, &n_partials);
+        PartitionScratch local;
+        return decode_bins(a, scratch ? *scratch : local, wg_offsets, wg_capacity, units_out,
+                           unit_capacity, merges_out, merge_capacity, res, detail);
     } else if (!prefill) {
         std::vector<Unit> units;
         for (int32_t b = 0; b < a.batch; b++) {

@@ -47,6 +47,7 @@ def test_status_strings():
     ((-1, 1000, 0, 32, 8, 128), pa.PA_ERR_INVALID_ARG),
     ((4, -5, 0, 32, 8, 128), pa.PA_ERR_INVALID_ARG),
     ((4, 1 << 40, 0, 32, 8, 128), pa.PA_ERR_INVALID_ARG),
+    ((4, pa.PA_MAX_KV_TOTAL + 1, 0, 32, 8, 128), pa.PA_ERR_INVALID_ARG),
 ])
 def test_plan_create_rejects_on_host(args, status):
     with pytest.raises(pa.PAError) as e:
