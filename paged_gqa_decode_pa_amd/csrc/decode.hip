@@ -284,6 +284,33 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<G>(), 8))) void decode_
     __shared__ int32_t lds_arrived;
 
     const int32_t unit_begin = wg_offsets[blockIdx.x], unit_end = wg_offsets[blockIdx.x + 1];
+
+    // Issue priority by remaining work.  Workgroups that share a compute unit
+    // start with equal budgets, but the instruction arbiter prefers older
+    // waves, so without this the first workgroup placed on a unit runs ahead
+    // and the last one is left alone at the end.  A wave's priority is the
+    // number of quarters of its workgroup's list entries still ahead of it
+    // (3 .. 0): a wave that has run ahead yields issue slots to those behind.
+    int32_t wg_total = 0;
+    for (int32_t ui = unit_begin; ui < unit_end; ui++)
+        if (units[ui].request >= 0)
+            wg_total += units[ui].kv_end - units[ui].kv_begin;
+    const int32_t quarter1 = wg_total / 4, quarter2 = wg_total / 2, quarter3 = wg_total - wg_total / 4;
+    int32_t done_before = 0;   // entries of the units finished
+    int priority = -1;
+    auto set_priority = [&](int32_t remaining) {
+        const int level = (remaining > quarter1) + (remaining > quarter2) + (remaining > quarter3);
+        if (level != priority) {
+            priority = level;
+            switch (level) {
+            case 0: __builtin_amdgcn_s_setprio(0); break;
+            case 1: __builtin_amdgcn_s_setprio(1); break;
+            case 2: __builtin_amdgcn_s_setprio(2); break;
+            default: __builtin_amdgcn_s_setprio(3); break;
+            }
+        }
+    };
+
     for (int32_t ui = unit_begin; ui < unit_end; ui++) {
     const pa_work_unit unit = units[ui];
     if (unit.request < 0)
@@ -425,6 +452,7 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<G>(), 8))) void decode_
             pv(v, pw);
         };
         while (true) {
+            set_priority(wg_total - done_before - tile * TILE);
             compute(ka, va);
             // refills stay behind the last use of the registers they overwrite
             __builtin_amdgcn_sched_barrier(0);
@@ -524,6 +552,7 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<G>(), 8))) void decode_
                 __hip_atomic_store(arrivals + unit.merge, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
+    done_before += kv_end - kv_begin;
     if (ui + 1 < unit_end)
         __syncthreads();  // the next unit rewrites the LDS just read
     }
