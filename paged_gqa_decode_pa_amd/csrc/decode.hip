@@ -90,7 +90,47 @@ constexpr int kQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]
 constexpr int kRowRor4 = 0x124;   // row_ror:4
 constexpr int kRowRor8 = 0x128;   // row_ror:8 (== lane ^ 8 within a row)
 
-__device__ __forceinline__ float shfl_xor(float x, int mask) { return __shfl_xor(x, mask, 64); }
+// Cross-row exchanges without lane-index arithmetic.  v_permlane16_swap
+// (v_permlane32_swap) with both operands x returns, in its two results, the
+// lane's own x and that of lane ^ 16 (lane ^ 32), in an order that depends
+// on the lane; sums and maxima do not care about the order.
+__device__ __forceinline__ float sum_xor16(float x) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float max_xor16(float x) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+// ds_swizzle in bit mode inside 32-lane halves: source lane =
+// ((lane & AND) | OR) ^ XOR.
+template <int AND, int OR, int XOR>
+__device__ __forceinline__ float swizzle(float x) {
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), AND | (OR << 5) | (XOR << 10)));
+}
+// Sum (max) over the rows of a wave instruction: lanes that hold the same
+// 16-byte chunk of different rows (lane ^ 16, lane ^ 32 at 16 lanes per row;
+// lane ^ 32 at 32).
+template <int LPR>
+__device__ __forceinline__ float sum_rows(float x) {
+    if constexpr (LPR <= 16)
+        x = sum_xor16(x);
+    return sum_xor32(x);
+}
+template <int LPR>
+__device__ __forceinline__ float max_rows(float x) {
+    if constexpr (LPR <= 16)
+        x = max_xor16(x);
+    return max_xor32(x);
+}
 
 // Agent-scope (all XCDs) coherent 32-bit accesses.
 __device__ __forceinline__ void store_coherent(float *p, float v) {
@@ -108,7 +148,8 @@ __device__ __forceinline__ void wait_vector_memory() { __builtin_amdgcn_s_waitcn
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// Value of lane `h` of this lane's G-lane group (G <= 4: inside the quad).
+// Value of lane `h` of this lane's G-lane group (G <= 4: inside the quad;
+// G = 8: a swizzle over groups of 8 lanes).
 template <int G>
 __device__ __forceinline__ float group_bcast(float x, int h, int lane) {
     if constexpr (G == 1) {
@@ -124,7 +165,16 @@ __device__ __forceinline__ float group_bcast(float x, int h, int lane) {
         default: return dpp_mov<0xFF>(x);
         }
     } else {
-        return __shfl(x, (lane & ~7) + h, 64);
+        switch (h) {
+        case 0: return swizzle<0x18, 0, 0>(x);
+        case 1: return swizzle<0x18, 1, 0>(x);
+        case 2: return swizzle<0x18, 2, 0>(x);
+        case 3: return swizzle<0x18, 3, 0>(x);
+        case 4: return swizzle<0x18, 4, 0>(x);
+        case 5: return swizzle<0x18, 5, 0>(x);
+        case 6: return swizzle<0x18, 6, 0>(x);
+        default: return swizzle<0x18, 7, 0>(x);
+        }
     }
 }
 
@@ -163,7 +213,7 @@ __device__ __forceinline__ float row_scores(const uint32_t (&qv)[G][4], const ui
                 v[m] = v[2 * m] + dpp_mov<kQuadXor2>(v[2 * m + 1]);
         }
         if constexpr (G >= 8)
-            v[0] = v[0] + shfl_xor(v[1], 4);
+            v[0] = v[0] + swizzle<0x1f, 0, 4>(v[1]);
         x = v[0];
         if constexpr (G == 2)
             x += dpp_mov<kQuadXor2>(x);
@@ -172,8 +222,30 @@ __device__ __forceinline__ float row_scores(const uint32_t (&qv)[G][4], const ui
         x += dpp_mov<kRowRor4>(x);
     x += dpp_mov<kRowRor8>(x);
     if constexpr (LPR == 32)
-        x += shfl_xor(x, 16);
+        x = sum_xor16(x);
     return x;
+}
+
+// The plan tables are read-only during a launch.  Reading them through the
+// constant address space lets the compiler use scalar loads even after the
+// kernel's own stores and atomics (with generic pointers those would be
+// vector loads, whose waits also wait for the K/V rows in flight).
+using ConstantI32 = const __attribute__((address_space(4))) int32_t *;
+__device__ __forceinline__ ConstantI32 constant_view(const int32_t *p) { return (ConstantI32)p; }
+__device__ __forceinline__ pa_work_unit load_unit(const pa_work_unit *units, int32_t i) {
+    const ConstantI32 w = (ConstantI32)(units + i);
+    pa_work_unit u;
+    u.request = w[0]; u.kv_head = w[1]; u.kv_begin = w[2]; u.kv_end = w[3];
+    u.q_begin = w[4]; u.q_end = w[5]; u.partial = w[6]; u.diag = w[7];
+    u.merge = w[8]; u.reserved0 = u.reserved1 = u.reserved2 = 0;
+    return u;
+}
+__device__ __forceinline__ pa_merge_unit load_merge(const pa_merge_unit *merges, int32_t i) {
+    const ConstantI32 w = (ConstantI32)(merges + i);
+    pa_merge_unit m;
+    m.request = w[0]; m.kv_head = w[1]; m.q_begin = w[2]; m.q_end = w[3];
+    m.first_partial = w[4]; m.n_parts = w[5]; m.reserved0 = m.reserved1 = 0;
+    return m;
 }
 
 // Buffer descriptor over 4-byte elements [0, n) of p.
@@ -283,7 +355,8 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<G>(), 8))) void decode_
     __shared__ float lds_l[WAVES][G];
     __shared__ int32_t lds_arrived;
 
-    const int32_t unit_begin = wg_offsets[blockIdx.x], unit_end = wg_offsets[blockIdx.x + 1];
+    const int32_t unit_begin = constant_view(wg_offsets)[blockIdx.x];
+    const int32_t unit_end = constant_view(wg_offsets)[blockIdx.x + 1];
 
     // Issue priority by remaining work.  Workgroups that share a compute unit
     // start with equal budgets, but the instruction arbiter prefers older
@@ -292,9 +365,11 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<G>(), 8))) void decode_
     // number of quarters of its workgroup's list entries still ahead of it
     // (3 .. 0): a wave that has run ahead yields issue slots to those behind.
     int32_t wg_total = 0;
-    for (int32_t ui = unit_begin; ui < unit_end; ui++)
-        if (units[ui].request >= 0)
-            wg_total += units[ui].kv_end - units[ui].kv_begin;
+    for (int32_t ui = unit_begin; ui < unit_end; ui++) {
+        const pa_work_unit u = load_unit(units, ui);
+        if (u.request >= 0)
+            wg_total += u.kv_end - u.kv_begin;
+    }
     const int32_t quarter1 = wg_total / 4, quarter2 = wg_total / 2, quarter3 = wg_total - wg_total / 4;
     int32_t done_before = 0;   // entries of the units finished
     int priority = -1;
@@ -312,7 +387,7 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<G>(), 8))) void decode_
     };
 
     for (int32_t ui = unit_begin; ui < unit_end; ui++) {
-    const pa_work_unit unit = units[ui];
+    const pa_work_unit unit = load_unit(units, ui);
     if (unit.request < 0)
         continue;  // padding unit (uniform over the workgroup)
 
@@ -474,26 +549,15 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<G>(), 8))) void decode_
     }
 
     // ---- combine the rows of this wave (same head: lanes with equal lane % G)
-    float mm = m_run;
-#pragma unroll
-    for (int x = LPR; x < 64; x <<= 1)
-        mm = fmaxf(mm, shfl_xor(mm, x));
+    const float mm = max_rows<LPR>(m_run);
     const float f = fast_exp2(m_run - mm);
-    float lsum = l_run * f;
-#pragma unroll
-    for (int x = LPR; x < 64; x <<= 1)
-        lsum += shfl_xor(lsum, x);
+    const float lsum = sum_rows<LPR>(l_run * f);
 #pragma unroll
     for (int h = 0; h < G; h++) {
         const float fh = group_bcast<G>(f, h, lane);
 #pragma unroll
-        for (int e = 0; e < 8; e++) {
-            float a = acc[h][e] * fh;
-#pragma unroll
-            for (int x = LPR; x < 64; x <<= 1)
-                a += shfl_xor(a, x);
-            acc[h][e] = a;
-        }
+        for (int e = 0; e < 8; e++)
+            acc[h][e] = sum_rows<LPR>(acc[h][e] * fh);
     }
     // ---- combine the waves through LDS
     if (r == 0) {
@@ -545,7 +609,7 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<G>(), 8))) void decode_
             lds_arrived = __hip_atomic_fetch_add(arrivals + unit.merge, 1, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT);
         __syncthreads();
-        const pa_merge_unit mu = merges[unit.merge];
+        const pa_merge_unit mu = load_merge(merges, unit.merge);
         if (lds_arrived == mu.n_parts - 1) {
             merge_rows<D, G, true>(mu, part_o, part_lse, G, out, lse, num_qo_heads, tid, kDecodeThreads);
             if (tid == 0)
