@@ -24,8 +24,14 @@ The JSON line reports:
 Algorithmic bytes per layer = unique slots x Hkv x D x 2 (K) x 2 (V) + list
 entries x 4 (slot ids) + B x Hq x D x 2 (q) + B x Hq x D x 4 (out) + (B+1) x 4.
 
-`--workload copy --copy-gib N` runs a plain device copy of N GiB instead (for
-calibrating the HBM counters).
+Other decode workloads (`--workload single_request | batch8 | hd256`): one
+request of 256 slots; 8 requests of 512..4096 slots (Qwen3-4B head shapes);
+32 requests of 1024..16384 slots at head_dim 256 -- each 36 layers per step
+with per-layer pools.  `--graph` replays each step's 36 layer runs from one
+captured HIP graph (pa_plan stays outside the graph).
+`--workload prefill_chunk512 | prefill_chunk64` measures the chunked-prefill
+kernel (MFMA roofline); `--workload copy --copy-gib N` runs a plain device
+copy of N GiB (for calibrating the HBM counters).
 """
 from __future__ import annotations
 
@@ -284,7 +290,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--flags", type=int, default=0, help="pa_plan flags")
     ap.add_argument("--workload", default="batch64",
-                    choices=["batch64", "prefill_chunk512", "prefill_chunk64", "copy"])
+                    choices=["batch64", "single_request", "batch8", "hd256",
+                             "prefill_chunk512", "prefill_chunk64", "copy"])
+    ap.add_argument("--graph", action="store_true",
+                    help="decode: replay each step's layer runs from a captured HIP graph")
     ap.add_argument("--copy-gib", type=float, default=4.0)
     args = ap.parse_args()
 
@@ -309,8 +318,10 @@ def main():
     import paged_gqa_decode_pa_amd as pa
     import workloads as W
 
-    spec = W.BATCH64_SHARED_PREFIX
-    layers = args.layers or spec.num_layers
+    spec = {"batch64": W.BATCH64_SHARED_PREFIX, "single_request": W.SINGLE_REQUEST_256,
+            "batch8": W.QWEN3_4B_BATCH8, "hd256": W.HEADDIM256_BATCH32}[args.workload]
+    # every decode workload runs 36 layers per step, each with its own pools
+    layers = args.layers or 36
     dev = torch.device("cuda", 0)
     log(f"generating {spec.name}: {layers} layers of {spec.num_slots}-slot pools")
     t0 = time.perf_counter()
@@ -326,12 +337,35 @@ def main():
     stream = torch.cuda.current_stream(dev)
     plan_host_s = []
 
-    def step():
-        plan.plan(case.kv_indptr, flags=args.flags, stream=stream)
-        plan_host_s.append(pa.pa_plan_host_timing(plan.handle))
+    def layer_runs(s):
         for layer in range(layers):
             plan.decode(case.q, case.k_pools[layer], case.v_pools[layer], idx, case.sm_scale,
-                        outs[layer], stream=stream)
+                        outs[layer], stream=s)
+
+    graph = None
+    if args.graph:
+        # the step's layer runs captured once; every step's pa_plan rewrites
+        # the same device tables (same lists, hence the same grid), which the
+        # replayed kernels read
+        plan.plan(case.kv_indptr, flags=args.flags, stream=stream)
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            layer_runs(side)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            layer_runs(side)
+        torch.cuda.synchronize()
+
+    def step(eager=False):
+        plan.plan(case.kv_indptr, flags=args.flags, stream=stream)
+        plan_host_s.append(pa.pa_plan_host_timing(plan.handle))
+        if graph is not None and not eager:
+            graph.replay()
+        else:
+            layer_runs(stream)
 
     for _ in range(args.warmup):
         step()
@@ -359,7 +393,7 @@ def main():
     torch.cuda.synchronize()
     start.record(stream)
     for _ in range(args.steps):
-        step()
+        step(eager=True)
     end.record(stream)
     torch.cuda.synchronize()
     ms_per_step_events = start.elapsed_time(end) / args.steps
@@ -386,10 +420,12 @@ def main():
     step_bytes = bytes_per_layer * layers
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = bytes_per_layer / (kernel_avg_ms * 1e-3) / 1e9
-    traffic = traffic_per_launch()
+    traffic = traffic_per_launch() if spec is W.BATCH64_SHARED_PREFIX else None
 
+    G = Hq // Hkv
     result = {
-        "metric": METRIC,
+        "metric": METRIC if spec is W.BATCH64_SHARED_PREFIX else
+        f"decode-attn µs/step/layer + achieved HBM GB/s (% of MI355X peak), {spec.name}",
         "value": round(value, 1),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -406,8 +442,10 @@ def main():
             "batch": B, "num_qo_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
             "layers_per_step": layers,
             "kv_len": f"uniform [{spec.len_lo}, {spec.len_hi}]",
-            "shared_prefix": f"{spec.batch // spec.prefix_group_size} groups x "
-                             f"{spec.prefix_group_size} requests x {spec.prefix_len} slots",
+            "shared_prefix": (f"{spec.batch // spec.prefix_group_size} groups x "
+                              f"{spec.prefix_group_size} requests x {spec.prefix_len} slots"
+                              if spec.prefix_group_size else "none"),
+            "layer_runs": "hip graph replay" if graph is not None else "eager",
             "list_entries": int(case.kv_indptr[-1]),
             "unique_slots": int(np.unique(case.kv_indices).size),
             "pool_slots": spec.num_slots,
@@ -426,7 +464,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": "decode_kernel<128,4> (pa_decode_run)",
+            "kernel": f"decode_kernel<{D},{G}> (pa_decode_run)",
             "kernel_avg_us": round(kernel_avg_ms * 1e3, 2),
         },
         "cpu_baseline": None,

@@ -1,0 +1,97 @@
+"""Capture of a multi-layer step in a HIP graph.
+
+A plan is computed once per step and every layer's run reads the plan's
+device tables, so the runs of one step can be captured once and replayed
+(the plan/run split of the Agent-Infer page, section "分页 KV 缓存"; graph
+capture of the decode step is stage 5 of the table in its section "优化历程").
+Runs allocate nothing and reset their own arrival counters, so a replay must
+give the eager result bit for bit.  Each replay follows eager work (the
+outputs are poisoned) and a synchronisation, and every replay is checked."""
+import numpy as np
+import pytest
+import torch
+
+import paged_gqa_decode_pa_amd as pa
+import workloads as W
+from gpu_util import TOL, device, max_err, oracle_decode, oracle_prefill, say
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+LAYERS = 4
+
+
+def _replay_and_check(step, outs, eager, replays=3):
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(g, stream=s):
+        step(s)
+    torch.cuda.synchronize()
+    for rep in range(replays):
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, e in zip(outs, eager):
+            assert np.array_equal(o.cpu().numpy(), e, equal_nan=True), f"replay {rep} differs"
+    del g
+
+
+@pytest.mark.parametrize("splits", [0, 3], ids=["auto", "forced3"])
+def test_decode_layers_graph_replay(splits):
+    say(f"graph capture: {LAYERS}-layer decode step, B=8, splits={splits}")
+    dev = device()
+    rng = np.random.Generator(np.random.PCG64(31))
+    B, Hq, Hkv, D, N = 8, 32, 8, 128, 65536
+    ip, idx = W.slot_lists(rng.integers(512, 4097, B), N, rng)
+    q = W.normal_bf16((B, Hq, D), 32, dev)
+    pools = [W.make_pools(N, Hkv, D, 40 + l, dev) for l in range(LAYERS)]
+    idx_dev = torch.as_tensor(idx, device=dev)
+    scale = W.softmax_scale(D)
+    outs = [torch.empty((B, Hq, D), dtype=torch.float32, device=dev) for _ in range(LAYERS)]
+    lses = [torch.empty((B, Hq), dtype=torch.float32, device=dev) for _ in range(LAYERS)]
+    with pa.Plan(B, int(ip[-1]), Hq, Hkv, D) as plan:
+        plan.plan(ip, flags=pa.PA_PLAN_FORCE_SPLITS(splits) if splits else 0)
+
+        def step(stream):
+            for l in range(LAYERS):
+                plan.decode(q, pools[l][0], pools[l][1], idx_dev, scale, outs[l], lses[l], stream=stream)
+
+        step(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        eager = [o.cpu().numpy() for o in outs] + [x.cpu().numpy() for x in lses]
+        ref, ref_lse = oracle_decode(q, pools[0][0], pools[0][1], ip, idx, scale, Hkv)
+        assert max_err(eager[0], ref) <= TOL and max_err(eager[LAYERS], ref_lse) <= TOL
+        _replay_and_check(step, outs + lses, eager)
+
+
+def test_prefill_layers_graph_replay():
+    say(f"graph capture: {LAYERS}-layer prefill step with split KV ranges")
+    dev = device()
+    rng = np.random.Generator(np.random.PCG64(37))
+    Hq, Hkv, D, N = 32, 8, 128, 16384
+    reqs = [(700, 64), (1500, 16)]     # few tiles: KV ranges are cut and merged
+    ip, idx = W.slot_lists(np.asarray([L for L, _ in reqs]), N, rng)
+    qo = np.concatenate([[0], np.cumsum([C for _, C in reqs])]).astype(np.int32)
+    T = int(qo[-1])
+    q = W.normal_bf16((T, Hq, D), 38, dev)
+    pools = [W.make_pools(N, Hkv, D, 50 + l, dev) for l in range(LAYERS)]
+    idx_dev = torch.as_tensor(idx, device=dev)
+    scale = W.softmax_scale(D)
+    outs = [torch.empty((T, Hq, D), dtype=torch.float32, device=dev) for _ in range(LAYERS)]
+    lses = [torch.empty((T, Hq), dtype=torch.float32, device=dev) for _ in range(LAYERS)]
+    with pa.Plan(len(reqs), int(ip[-1]), Hq, Hkv, D, max_q_total=T) as plan:
+        plan.plan(ip, qo)
+
+        def step(stream):
+            for l in range(LAYERS):
+                plan.prefill(q, pools[l][0], pools[l][1], idx_dev, scale, outs[l], lses[l], stream=stream)
+
+        step(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        eager = [o.cpu().numpy() for o in outs] + [x.cpu().numpy() for x in lses]
+        ref, ref_lse = oracle_prefill(q, pools[0][0], pools[0][1], qo, ip, idx, scale, Hkv)
+        assert max_err(eager[0], ref) <= TOL and max_err(eager[LAYERS], ref_lse) <= TOL
+        _replay_and_check(step, outs + lses, eager)
