@@ -290,19 +290,50 @@ struct RowAddr<true> {
 // Threads tid, tid+nthreads, ... of the caller each produce output elements.
 // COHERENT: read the partials with agent-scope coherent loads (partials
 // written by other workgroups of the running kernel).
+// The parts are read kMergeBatch at a time (all loads of a batch in flight
+// together, one memory round trip per batch) and folded in with a running
+// maximum; for up to kMergeBatch parts this is the plain two-pass formula
+// o = sum_i 2^(lse_i - M) o_i / sum_i 2^(lse_i - M), M = max_i lse_i.
+constexpr int kMergeBatch = 8;
+
 template <int D, int G, bool COHERENT>
 __device__ __forceinline__ void merge_rows(const pa_merge_unit &mu, const float *__restrict__ part_o,
                                            const float *__restrict__ part_lse, int32_t rows_per_slot,
                                            float *__restrict__ out, float *__restrict__ lse,
                                            int32_t num_qo_heads, int tid, int nthreads) {
     const int32_t rows = (mu.q_end - mu.q_begin) * G;
+    const int32_t n = mu.n_parts;
     for (int32_t idx = tid; idx < rows * D; idx += nthreads) {
         const int32_t row = idx / D, d = idx % D;
-        float M = -INFINITY;
-
-        for (int32_t i = 0; i < mu.n_parts; i++) {
-            const float *pl = part_lse + (int64_t)(mu.first_partial + i) * rows_per_slot + row;
-            M = fmaxf(M, COHERENT ? load_coherent(pl) : *pl);
+        float M = -INFINITY, o = 0.f, wsum = 0.f;
+        for (int32_t i0 = 0; i0 < n; i0 += kMergeBatch) {
+            float l[kMergeBatch], v[kMergeBatch];
+#pragma unroll
+            for (int j = 0; j < kMergeBatch; j++) {
+                const int32_t i = min(i0 + j, n - 1);   // past the end: re-read the last part
+                const int64_t slot_row = (int64_t)(mu.first_partial + i) * rows_per_slot + row;
+                l[j] = COHERENT ? load_coherent(part_lse + slot_row) : part_lse[slot_row];
+                v[j] = COHERENT ? load_coherent(part_o + slot_row * D + d) : part_o[slot_row * D + d];
+            }
+            float m = M;
+#pragma unroll
+            for (int j = 0; j < kMergeBatch; j++) {
+                if (i0 + j >= n)
+                    l[j] = -INFINITY;
+                m = fmaxf(m, l[j]);
+            }
+            if (m == -INFINITY)
+                continue;  // only empty parts so far
+            const float a = fast_exp2(M - m);  // 0 while M is -inf
+            o *= a;
+            wsum *= a;
+#pragma unroll
+            for (int j = 0; j < kMergeBatch; j++) {
+                const float w = fast_exp2(l[j] - m);
+                o = fmaf(w, v[j], o);
+                wsum += w;
+            }
+            M = m;
         }
         const int32_t qtok = mu.q_begin + row / G, h = mu.kv_head * G + row % G;
         const int64_t orow = (int64_t)qtok * num_qo_heads + h;
@@ -310,21 +341,11 @@ __device__ __forceinline__ void merge_rows(const pa_merge_unit &mu, const float 
             out[orow * D + d] = 0.f;
             if (lse && d == 0)
                 lse[orow] = -INFINITY;
-            continue;
+        } else {
+            out[orow * D + d] = o / wsum;
+            if (lse && d == 0)
+                lse[orow] = (M + fast_log2(wsum)) * kLn2;
         }
-        float o = 0.f, wsum = 0.f;
-
-        for (int32_t i = 0; i < mu.n_parts; i++) {
-            const int64_t slot_row = (int64_t)(mu.first_partial + i) * rows_per_slot + row;
-            const float l2 = COHERENT ? load_coherent(part_lse + slot_row) : part_lse[slot_row];
-            const float po = COHERENT ? load_coherent(part_o + slot_row * D + d) : part_o[slot_row * D + d];
-            const float w = fast_exp2(l2 - M);
-            o = fmaf(w, po, o);
-            wsum += w;
-        }
-        out[orow * D + d] = o / wsum;
-        if (lse && d == 0)
-            lse[orow] = (M + fast_log2(wsum)) * kLn2;
     }
 }
 

@@ -373,6 +373,7 @@ prefill_kernel(const int32_t *__restrict__ wg_offsets, const pa_work_unit *__res
 // Log-sum-exp merge of prefill partials: workgroup (x, y) combines rows
 // y*RPW .. y*RPW+RPW-1 of merge unit x; a row's D values are spread over
 // D/4 threads with one float4 each, so every part's row is one coalesced read.
+constexpr int kMergeBatch = 8;   // parts read per memory round trip
 template <int D, int G>
 __global__ __launch_bounds__(kThreads) void prefill_merge_kernel(
     const pa_merge_unit *__restrict__ merges, const float *__restrict__ part_o,
@@ -383,23 +384,49 @@ __global__ __launch_bounds__(kThreads) void prefill_merge_kernel(
     const int row = blockIdx.y * RPW + threadIdx.x / TPR, c = threadIdx.x % TPR;
     if (row >= (mu.q_end - mu.q_begin) * G)
         return;
-    float M = -INFINITY;
-    for (int32_t i = 0; i < mu.n_parts; i++)
-        M = fmaxf(M, part_lse[(int64_t)(mu.first_partial + i) * kPrefillTileRows + row]);
-    const int64_t orow = (int64_t)(mu.q_begin + row / G) * num_qo_heads + mu.kv_head * G + row % G;
+    // parts read kMergeBatch at a time (one memory round trip per batch) and
+    // folded in with a running maximum; for up to kMergeBatch parts this is
+    // the plain two-pass log-sum-exp merge
+    const int32_t n = mu.n_parts;
+    float M = -INFINITY, wsum = 0.f;
     float4 acc = {0.f, 0.f, 0.f, 0.f};
-    float wsum = 0.f;
-    if (M != -INFINITY) {
-        for (int32_t i = 0; i < mu.n_parts; i++) {
-            const int64_t prow = (int64_t)(mu.first_partial + i) * kPrefillTileRows + row;
-            const float w = fast_exp2(part_lse[prow] - M);
-            const float4 v = *reinterpret_cast<const float4 *>(part_o + prow * D + 4 * c);
-            acc.x = fmaf(w, v.x, acc.x);
-            acc.y = fmaf(w, v.y, acc.y);
-            acc.z = fmaf(w, v.z, acc.z);
-            acc.w = fmaf(w, v.w, acc.w);
+    for (int32_t i0 = 0; i0 < n; i0 += kMergeBatch) {
+        float l[kMergeBatch];
+        float4 v[kMergeBatch];
+#pragma unroll
+        for (int j = 0; j < kMergeBatch; j++) {
+            const int64_t prow = (int64_t)(mu.first_partial + min(i0 + j, n - 1)) * kPrefillTileRows + row;
+            l[j] = part_lse[prow];
+            v[j] = *reinterpret_cast<const float4 *>(part_o + prow * D + 4 * c);
+        }
+        float m = M;
+#pragma unroll
+        for (int j = 0; j < kMergeBatch; j++) {
+            if (i0 + j >= n)
+                l[j] = -INFINITY;
+            m = fmaxf(m, l[j]);
+        }
+        if (m == -INFINITY)
+            continue;
+        const float a = fast_exp2(M - m);   // 0 while M is -inf
+        acc.x *= a;
+        acc.y *= a;
+        acc.z *= a;
+        acc.w *= a;
+        wsum *= a;
+#pragma unroll
+        for (int j = 0; j < kMergeBatch; j++) {
+            const float w = fast_exp2(l[j] - m);
+            acc.x = fmaf(w, v[j].x, acc.x);
+            acc.y = fmaf(w, v[j].y, acc.y);
+            acc.z = fmaf(w, v[j].z, acc.z);
+            acc.w = fmaf(w, v[j].w, acc.w);
             wsum += w;
         }
+        M = m;
+    }
+    const int64_t orow = (int64_t)(mu.q_begin + row / G) * num_qo_heads + mu.kv_head * G + row % G;
+    if (M != -INFINITY) {
         const float inv = 1.f / wsum;
         acc.x *= inv;
         acc.y *= inv;
