@@ -1,4 +1,5 @@
-"""fp64 CPU oracle for paged grouped-query decode attention.
+"""fp64 CPU oracle for paged grouped-query decode attention (and the rotary
+position embedding of the rows appended to the pool).
 
 TEST INFRASTRUCTURE ONLY: the test-suite, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` are the only code that may import this
@@ -80,6 +81,9 @@ class Oracle:
             _i32p, _i32p, _i32p, ctypes.c_float, _f64p, _f64p, _i32p, ctypes.c_int64]
         lib.pa_oracle_merge.restype = ctypes.c_int
         lib.pa_oracle_merge.argtypes = [ctypes.c_int32, ctypes.c_int32, _f64p, _f64p, _f64p, _f64p]
+        lib.pa_oracle_rope.restype = ctypes.c_int
+        lib.pa_oracle_rope.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _u16p, _i32p,
+                                       ctypes.c_double, _f64p]
         lib.pa_oracle_num_threads.restype = ctypes.c_int
         lib.pa_oracle_num_threads.argtypes = []
         self._lib = lib
@@ -170,6 +174,22 @@ class Oracle:
             ctypes.c_float(sm_scale), _ptr(out, _f64p), _ptr(lse, _f64p), sel_p, n_sel)
         self._check(rc)
         return out, lse
+
+    def rope(self, x_bits, positions, theta: float) -> np.ndarray:
+        """Rotary position embedding (rotate-half pairs i, i + D/2) of bf16 rows.
+
+        x_bits: uint16 [T, H, D]; positions: int32 [T].  Returns float64
+        [T, H, D], not rounded.
+        """
+        x = _as(x_bits, np.uint16)
+        T, H, D = x.shape
+        pos = _as(positions, np.int32)
+        if pos.shape != (T,):
+            raise OracleError("positions must hold one entry per token")
+        y = np.zeros((T, H, D), np.float64)
+        self._check(self._lib.pa_oracle_rope(T, H, D, _ptr(x, _u16p), _ptr(pos, _i32p),
+                                             float(theta), _ptr(y, _f64p)))
+        return y
 
     def merge(self, o_parts, lse_parts):
         """Log-sum-exp merge of partial results of one row: o_parts [n, D], lse_parts [n]."""

@@ -40,6 +40,17 @@
  *         M = max_i lse_i,  w_i = exp(lse_i - M),
  *         o = sum_i w_i o_i / sum_i w_i,  lse = M + ln(sum_i w_i).
  *
+ *   - Rotary position embedding of the rows appended to the pool (the step
+ *     before attention: new tokens' K/V rows are written to their slots, K
+ *     stored already rotated).  Pegainfer page, section "核心组件概览" (RoPE is
+ *     one of the GPU operators of ops.rs); the appended slots are the
+ *     TokenToKVPool slots of the Agent-Infer page, section "分页 KV 缓存".  The
+ *     pages do not write RoPE out.  Reading (the rotate-half form used by the
+ *     Qwen3 family): for head dimension D, pair i < D/2 couples elements i and
+ *     i + D/2 and turns them by the angle pos * theta^(-2i/D):
+ *         y[i]       = x[i] cos(a_i) - x[i + D/2] sin(a_i)
+ *         y[i + D/2] = x[i + D/2] cos(a_i) + x[i] sin(a_i)
+ *
  * All arithmetic is in double precision.  bf16 inputs are widened exactly
  * (a bf16 bit pattern is the upper half of an IEEE binary32).  The softmax
  * scale is given as a float and widened, so both sides use the same value.
@@ -317,6 +328,34 @@ int pa_oracle_merge(int32_t n, int32_t D, const double *o_parts,
 }
 
 /* Threads an OpenMP region of this library uses (1 without OpenMP). */
+/*
+ * Rotary position embedding of n rows of D bf16 values (rows of `heads`
+ * consecutive heads per token): row r belongs to token r / heads, whose
+ * position is positions[r / heads].  Output: n * D doubles (not rounded).
+ */
+int pa_oracle_rope(int64_t tokens, int32_t heads, int32_t D, const uint16_t *x_bits,
+                   const int32_t *positions, double theta, double *y)
+{
+    if (tokens < 0 || heads <= 0 || D <= 0 || D % 2 != 0 || !(theta > 0.0))
+        return ORACLE_BAD_SHAPE;
+    const int half = D / 2;
+    for (int64_t t = 0; t < tokens; t++) {
+        for (int32_t h = 0; h < heads; h++) {
+            const uint16_t *x = x_bits + (t * heads + h) * (int64_t)D;
+            double *out = y + (t * heads + h) * (int64_t)D;
+            for (int i = 0; i < half; i++) {
+                const double inv_freq = pow(theta, -2.0 * (double)i / (double)D);
+                const double a = (double)positions[t] * inv_freq;
+                const double c = cos(a), sn = sin(a);
+                const double x1 = widen_bf16(x[i]), x2 = widen_bf16(x[i + half]);
+                out[i] = x1 * c - x2 * sn;
+                out[i + half] = x2 * c + x1 * sn;
+            }
+        }
+    }
+    return ORACLE_OK;
+}
+
 int pa_oracle_num_threads(void)
 {
 #ifdef _OPENMP

@@ -6,8 +6,10 @@ Each ``pin_*`` function takes an oracle handle (``oracle.Oracle``) and raises
     in float64 with grouped-query heads, numpy/scipy reductions),
   * brute force at 50 significant digits (mpmath) on tiny inputs,
   * closed forms (one token, two tokens, zero query, constant values,
-    saturated softmax, empty list),
-  * invariances (slot order, slot relocation, split-and-merge).
+    saturated softmax, empty list; RoPE of unit vectors),
+  * invariances (slot order, slot relocation, split-and-merge; RoPE's
+    relative-position property and pair norms), and for RoPE numpy complex
+    multiplication.
 The same pins run against deliberately broken oracle builds to show that each
 plausible mistake is caught (``test_oracle_mutants.py``).
 """
@@ -351,9 +353,78 @@ def pin_prefill_rows_are_decodes(o):
             assert np.abs(lse[qo[b] + i] - ref_lse[0]).max() < TOL
 
 
+# ----------------------------------------------------------------------------
+# rotary position embedding pins (the append step)
+# ----------------------------------------------------------------------------
+def pin_rope_complex_rotation(o):
+    """Rotate-half RoPE is the complex product (x_i + j x_{i+D/2}) e^{j p theta^(-2i/D)}:
+    numpy complex arithmetic agrees to 1e-12."""
+    rng = np.random.default_rng(41)
+    for (T, H, D, theta) in [(5, 3, 8, 10000.0), (4, 2, 128, 1e6), (3, 1, 256, 5e5)]:
+        x = _random_bits(rng, (T, H, D))
+        pos = rng.integers(0, 40000, T).astype(np.int32)
+        y = o.rope(x, pos, theta)
+        xw = _widen(x)
+        half = D // 2
+        z = xw[..., :half] + 1j * xw[..., half:]
+        ang = pos[:, None, None].astype(np.float64) * theta ** (-2.0 * np.arange(half) / D)[None, None, :]
+        r = z * np.exp(1j * ang)
+        ref = np.concatenate([r.real, r.imag], axis=-1)
+        assert np.abs(y - ref).max() < 1e-12 * max(1.0, np.abs(ref).max()), "rope != complex rotation"
+
+
+def pin_rope_closed_form(o):
+    """D = 4, x = e_0 (pair 0) or e_1 (pair 1): y = (cos a, 0, sin a, 0) with
+    a = p, and (0, cos b, 0, sin b) with b = p / sqrt(theta)."""
+    theta = 10000.0
+    for p in (0, 1, 7, 1234):
+        e0 = _bf16_bits(np.array([[[1.0, 0.0, 0.0, 0.0]]]))
+        e1 = _bf16_bits(np.array([[[0.0, 1.0, 0.0, 0.0]]]))
+        y0 = o.rope(e0, np.array([p], np.int32), theta)[0, 0]
+        y1 = o.rope(e1, np.array([p], np.int32), theta)[0, 0]
+        a, b = float(p), float(p) / np.sqrt(theta)
+        assert np.allclose(y0, [np.cos(a), 0, np.sin(a), 0], atol=1e-13), "pair 0 closed form"
+        assert np.allclose(y1, [0, np.cos(b), 0, np.sin(b)], atol=1e-13), "pair 1 closed form"
+
+
+def pin_rope_position_zero(o):
+    """Position 0 leaves every row unchanged, exactly."""
+    rng = np.random.default_rng(42)
+    x = _random_bits(rng, (6, 4, 128))
+    y = o.rope(x, np.zeros(6, np.int32), 1e6)
+    assert np.array_equal(y, _widen(x)), "position 0 must be the identity"
+
+
+def pin_rope_relative_position(o):
+    """<R(m) q, R(n) k> depends on m - n only: equal to <R(m - n) q, k> (1e-9 relative)."""
+    rng = np.random.default_rng(43)
+    D, theta = 64, 1e4
+    q = _random_bits(rng, (1, 1, D))
+    k = _random_bits(rng, (1, 1, D))
+    for (m, n) in [(5, 2), (1000, 37), (30000, 29999), (17, 17)]:
+        lhs = float(np.dot(o.rope(q, np.array([m], np.int32), theta)[0, 0],
+                           o.rope(k, np.array([n], np.int32), theta)[0, 0]))
+        rhs = float(np.dot(o.rope(q, np.array([m - n], np.int32), theta)[0, 0], _widen(k)[0, 0]))
+        assert abs(lhs - rhs) <= 1e-9 * max(1.0, abs(rhs)), f"relative position ({m}, {n})"
+
+
+def pin_rope_norm(o):
+    """Each pair (i, i + D/2) keeps its length."""
+    rng = np.random.default_rng(44)
+    D = 128
+    x = _random_bits(rng, (8, 2, D))
+    y = o.rope(x, rng.integers(0, 1 << 20, 8).astype(np.int32), 1e6)
+    xw = _widen(x)
+    nx = np.hypot(xw[..., :D // 2], xw[..., D // 2:])
+    ny = np.hypot(y[..., :D // 2], y[..., D // 2:])
+    assert np.abs(nx - ny).max() < 1e-12, "rotation changed a pair's length"
+
+
 ALL_PINS = [
     pin_sdpa_decode, pin_bruteforce_tiny, pin_slot_order, pin_single_token, pin_two_tokens,
     pin_zero_query, pin_constant_values, pin_saturated_softmax, pin_empty_list,
     pin_duplicate_slots, pin_row_selection, pin_merge_of_splits, pin_merge_special_cases,
     pin_prefill_sdpa, pin_prefill_rows_are_decodes,
+    pin_rope_complex_rotation, pin_rope_closed_form, pin_rope_position_zero,
+    pin_rope_relative_position, pin_rope_norm,
 ]

@@ -46,6 +46,12 @@ MUTANTS = [
     ("merge_first_part_dropped", [("for (int32_t i = 0; i < n; i++) {\n        double w",
                                    "for (int32_t i = 1; i < n; i++) {\n        double w", None)]),
     ("merge_unnormalised", [("out[d] /= wsum;", "out[d] /= (double)n;", None)]),
+    ("rope_adjacent_pairs", [("widen_bf16(x[i]), x2 = widen_bf16(x[i + half]);",
+                              "widen_bf16(x[(2 * i) % D]), x2 = widen_bf16(x[(2 * i + 1) % D]);", None)]),
+    ("rope_sign_flipped", [("out[i] = x1 * c - x2 * sn;", "out[i] = x1 * c + x2 * sn;", None)]),
+    ("rope_frequency_exponent", [("pow(theta, -2.0 * (double)i / (double)D)", "pow(theta, -(double)i / (double)D)", None)]),
+    ("rope_second_half_unrotated", [("out[i + half] = x2 * c + x1 * sn;", "out[i + half] = x2;", None)]),
+    ("rope_position_off_by_one", [("(double)positions[t] * inv_freq", "(double)(positions[t] + 1) * inv_freq", None)]),
 ]
 
 
