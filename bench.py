@@ -280,6 +280,67 @@ def run_prefill_bench(args):
     print(json.dumps(result), flush=True)
 
 
+def run_append_bench(args):
+    """The append step of a batch-64 decode step: 64 new tokens' K/V rows
+    (Hkv=8, D=128) written to scattered slots of a 600k-slot pool, K and the
+    32 query heads rotated by RoPE; 36 calls (one per layer) per step, the
+    query rows rotated again by every call (the arithmetic is the same)."""
+    import numpy as np
+    import torch
+
+    import paged_gqa_decode_pa_amd as pa
+    import workloads as W
+    dev = torch.device("cuda", 0)
+    T, Hq, Hkv, D, N, layers = 64, 32, 8, 128, 600_000, args.layers or 36
+    rng = np.random.Generator(np.random.PCG64(1006))
+    k_pools = [W.make_pools(N, Hkv, D, 1006 + l, dev) for l in range(min(layers, 4))]
+    k_new = W.normal_bf16((T, Hkv, D), 7, dev)
+    v_new = W.normal_bf16((T, Hkv, D), 8, dev)
+    q = W.normal_bf16((T, Hq, D), 9, dev)
+    loc = torch.as_tensor(rng.permutation(N)[:T].astype(np.int32), device=dev)
+    pos = torch.as_tensor(rng.integers(2048, 8193, T).astype(np.int32), device=dev)
+
+    def calls(stream):
+        for l in range(layers):
+            kp, vp = k_pools[l % len(k_pools)]
+            pa.pa_kv_append(k_new, v_new, loc, kp, vp, positions=pos, rope_theta=1e6, q=q,
+                            stream=stream)
+
+    # the 36 calls of a step replayed from a HIP graph, so the time is the
+    # GPU's and not the Python binding's
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        calls(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        calls(side)
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        graph.replay()
+    end.record()
+    torch.cuda.synchronize()
+    us = start.elapsed_time(end) * 1e3 / (args.steps * layers)
+    moved = 2 * (2 * T * Hkv * D * 2 + T * Hq * D * 2) + 2 * T * 4   # K, V, Q read + written; ids
+    log(f"append: {us:.2f} us per call ({moved / (us * 1e-6) / 1e9:.1f} GB/s)")
+    print(json.dumps({
+        "metric": "append + RoPE µs per layer call, batch-64 decode step", "value": round(us, 3),
+        "unit": "us", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "higher_is_better": False, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "append_rope_b64_hkv8_hq32_d128", "tokens": T, "layers_per_step": layers},
+        "bytes_per_call": moved, "vs_baseline": None,
+        "roofline": {"bound": "hbm", "achieved": round(moved / (us * 1e-6) / 1e9, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(moved / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 5), "traffic": None,
+                     "kernel": "append_kernel (pa_kv_append)"},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -291,7 +352,7 @@ def main():
     ap.add_argument("--flags", type=int, default=0, help="pa_plan flags")
     ap.add_argument("--workload", default="batch64",
                     choices=["batch64", "single_request", "batch8", "hd256",
-                             "prefill_chunk512", "prefill_chunk64", "copy"])
+                             "prefill_chunk512", "prefill_chunk64", "append", "copy"])
     ap.add_argument("--graph", action="store_true",
                     help="decode: replay each step's layer runs from a captured HIP graph")
     ap.add_argument("--copy-gib", type=float, default=4.0)
@@ -313,6 +374,9 @@ def main():
 
     if args.workload.startswith("prefill"):
         run_prefill_bench(args)
+        return
+    if args.workload == "append":
+        run_append_bench(args)
         return
 
     import paged_gqa_decode_pa_amd as pa

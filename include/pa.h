@@ -223,6 +223,32 @@ typedef struct pa_merge_unit {
 } pa_merge_unit;
 
 /*
+ * pa_kv_append: the step before attention.  Writes the K and V rows of
+ * num_tokens new tokens into their slots of the token-granular pool (one slot
+ * per token: Agent-Infer page, section "分页 KV 缓存"), rotating K by rotary
+ * position embedding (an operator named on the Pegainfer page, section
+ * "核心组件概览") when rope_theta > 0, and, if q is not NULL, rotating the
+ * tokens' query rows in place with the same positions.  Rotation: pair
+ * i < D/2 couples elements i and i + D/2 and turns them by the angle
+ * positions[t] * rope_theta^(-2i/D) (computed in double precision, rounded
+ * once to bf16, nearest-even).  rope_theta <= 0: K is copied unrotated and q
+ * is left alone.
+ *   k_new, v_new   device bf16 [num_tokens, num_kv_heads, head_dim], 16-byte aligned
+ *   q              device bf16 [num_tokens, num_qo_heads, head_dim] or NULL
+ *   positions      device int32 [num_tokens] (may be NULL when rope_theta <= 0)
+ *   out_loc        device int32 [num_tokens]: the slot of each token, distinct;
+ *                  a token whose slot is outside [0, num_slots) is not written
+ *   k_pool, v_pool device bf16 pools as for the runs (slot_stride 0 = Hkv*D)
+ * Asynchronous on `stream`; allocates nothing.  Overlapping slots between
+ * tokens of one call race.  PA_ERR_INVALID_ARG for null or misaligned
+ * pointers and bad sizes, PA_ERR_UNSUPPORTED for head_dim not in {128, 256}.
+ */
+pa_status pa_kv_append(const void *k_new, const void *v_new, void *q, const int32_t *positions,
+                       const int32_t *out_loc, int32_t num_tokens, int32_t num_qo_heads,
+                       int32_t num_kv_heads, int32_t head_dim, float rope_theta, void *k_pool,
+                       void *v_pool, int64_t num_slots, int64_t slot_stride, pa_stream_t stream);
+
+/*
  * pa_partition: compute the partition pa_plan would upload, into host arrays.
  *   Arguments as in pa_plan_create / pa_plan; max_workgroups is the number of
  *   decode workgroups the GPU holds at once (pa_plan uses the kernel's

@@ -96,6 +96,8 @@ def _load() -> ctypes.CDLL:
     lib.pa_plan_host_timing.argtypes = [vp, ctypes.POINTER(ctypes.c_double),
                                         ctypes.POINTER(ctypes.c_double)]
     lib.pa_plan_host_timing.restype = ctypes.c_int
+    lib.pa_kv_append.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp, vp, i64, i64, vp]
+    lib.pa_kv_append.restype = ctypes.c_int
     return lib
 
 
@@ -208,6 +210,37 @@ def pa_prefill_chunk_run(plan, q, k_pool, v_pool, kv_indices, sm_scale, out, lse
                          num_slots=None, slot_stride=None, stream=None) -> None:
     _run(_lib.pa_prefill_chunk_run, "pa_prefill_chunk_run", plan, q, k_pool, v_pool,
          kv_indices, sm_scale, out, lse, num_slots, slot_stride, stream)
+
+
+def pa_kv_append(k_new, v_new, out_loc, k_pool, v_pool, positions=None, rope_theta: float = 0.0,
+                 q=None, num_slots=None, slot_stride=None, stream=None) -> None:
+    """Write the new tokens' K/V rows [T, Hkv, D] to slots out_loc [T] of the
+    pools, K rotated by RoPE (and q [T, Hq, D] rotated in place, if given)
+    when rope_theta > 0."""
+    T, Hkv, D = k_new.shape
+    if tuple(v_new.shape) != (T, Hkv, D):
+        raise ValueError("v_new must have the shape of k_new")
+    for name, t in (("k_new", k_new), ("v_new", v_new), ("q", q)):
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    Hq = Hkv
+    if q is not None:
+        if q.dim() != 3 or q.shape[0] != T or q.shape[2] != D:
+            raise ValueError("q must be [T, Hq, D]")
+        Hq = q.shape[1]
+    for name, t in (("out_loc", out_loc), ("positions", positions)):
+        if t is not None and (t.dtype != torch.int32 or t.numel() != T):
+            raise TypeError(f"{name} must be int32 with one entry per token")
+    if slot_stride is None:
+        slot_stride = _pool_stride(k_pool, v_pool, D)
+    if num_slots is None:
+        num_slots = k_pool.shape[0]
+    _check(_lib.pa_kv_append(_dev_ptr(k_new, "k_new", torch.bfloat16), _dev_ptr(v_new, "v_new", torch.bfloat16),
+                             _dev_ptr(q, "q", torch.bfloat16), _dev_ptr(positions, "positions"),
+                             _dev_ptr(out_loc, "out_loc"), T, Hq, Hkv, D, float(rope_theta),
+                             _dev_ptr(k_pool, "k_pool", torch.bfloat16),
+                             _dev_ptr(v_pool, "v_pool", torch.bfloat16), int(num_slots),
+                             int(slot_stride), _stream(stream)), "pa_kv_append")
 
 
 def pa_plan_destroy(plan) -> None:

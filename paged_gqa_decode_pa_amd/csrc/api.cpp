@@ -389,6 +389,52 @@ pa_status pa_plan(pa_plan_t *p, const int32_t *kv_indptr_host, const int32_t *qo
     return PA_OK;
 }
 
+pa_status pa_kv_append(const void *k_new, const void *v_new, void *q, const int32_t *positions,
+                       const int32_t *out_loc, int32_t num_tokens, int32_t num_qo_heads,
+                       int32_t num_kv_heads, int32_t head_dim, float rope_theta, void *k_pool,
+                       void *v_pool, int64_t num_slots, int64_t slot_stride, pa_stream_t stream) {
+    if (num_tokens < 0 || num_qo_heads <= 0 || num_kv_heads <= 0)
+        return fail(PA_ERR_INVALID_ARG, "bad token or head count");
+    if (head_dim != 128 && head_dim != 256)
+        return fail(PA_ERR_UNSUPPORTED, "head_dim must be 128 or 256");
+    if (!std::isfinite(rope_theta))
+        return fail(PA_ERR_INVALID_ARG, "rope_theta is not finite");
+    if (num_tokens == 0)
+        return PA_OK;
+    const bool rotate = rope_theta > 0.f;
+    if (!k_new || !v_new || !out_loc || !k_pool || !v_pool || (rotate && !positions))
+        return fail(PA_ERR_INVALID_ARG, "null pointer");
+    if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
+        !aligned(q, 4) || !aligned(positions, 4) || !aligned(out_loc, 4))
+        return fail(PA_ERR_INVALID_ARG, "k_new, v_new and the pools must be 16-byte aligned");
+    const int64_t row = (int64_t)num_kv_heads * head_dim;
+    if (slot_stride == 0)
+        slot_stride = row;
+    if (slot_stride < row || slot_stride % 8 != 0)
+        return fail(PA_ERR_INVALID_ARG, "slot_stride must be >= Hkv*D and a multiple of 8");
+    if (num_slots <= 0)
+        return fail(PA_ERR_INVALID_ARG, "num_slots must be positive");
+    pa::AppendLaunch l;
+    l.k_new = k_new;
+    l.v_new = v_new;
+    l.q = q;
+    l.positions = positions;
+    l.out_loc = out_loc;
+    l.num_tokens = num_tokens;
+    l.num_qo_heads = num_qo_heads;
+    l.num_kv_heads = num_kv_heads;
+    l.head_dim = head_dim;
+    l.rope_theta = rope_theta;
+    l.k_pool = k_pool;
+    l.v_pool = v_pool;
+    l.num_slots = num_slots;
+    l.slot_stride = slot_stride;
+    const int rc = pa::launch_append(l, stream);
+    if (rc != 0)
+        return hip_fail((hipError_t)rc, "append kernel launch");
+    return PA_OK;
+}
+
 pa_status pa_plan_host_timing(const pa_plan_t *p, double *total_us, double *wait_us) {
     if (!p || !total_us || !wait_us)
         return fail(PA_ERR_INVALID_ARG, "null argument");

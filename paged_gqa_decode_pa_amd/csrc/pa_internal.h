@@ -125,4 +125,19 @@ int launch_prefill(const DecodeLaunch &l, void *stream);
 // Log-sum-exp merge of the prefill partials (no-op without merge units).
 int launch_prefill_merge(const DecodeLaunch &l, void *stream);
 
+// The append step: new tokens' K/V rows written to their slots, K (and the
+// query rows, in place, if q is not null) rotated by RoPE when rope_theta > 0.
+struct AppendLaunch {
+    const void *k_new;          // bf16 [tokens, Hkv, D]
+    const void *v_new;          // bf16 [tokens, Hkv, D]
+    void *q;                    // bf16 [tokens, Hq, D] or null
+    const int32_t *positions;   // device [tokens] (unused when rope_theta <= 0)
+    const int32_t *out_loc;     // device [tokens]
+    int32_t num_tokens, num_qo_heads, num_kv_heads, head_dim;
+    float rope_theta;
+    void *k_pool, *v_pool;
+    int64_t num_slots, slot_stride;   // elements
+};
+int launch_append(const AppendLaunch &l, void *stream);   // returns hipError_t
+
 }  // namespace pa
