@@ -84,6 +84,11 @@ class Oracle:
         lib.pa_oracle_rope.restype = ctypes.c_int
         lib.pa_oracle_rope.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _u16p, _i32p,
                                        ctypes.c_double, _f64p]
+        _u8p = ctypes.POINTER(ctypes.c_uint8)
+        lib.pa_oracle_e4m3_to_bf16.restype = ctypes.c_int
+        lib.pa_oracle_e4m3_to_bf16.argtypes = [ctypes.c_int64, _u8p, _u16p]
+        lib.pa_oracle_e4m3_values.restype = ctypes.c_int
+        lib.pa_oracle_e4m3_values.argtypes = [ctypes.c_int64, _u8p, _f64p]
         lib.pa_oracle_num_threads.restype = ctypes.c_int
         lib.pa_oracle_num_threads.argtypes = []
         self._lib = lib
@@ -190,6 +195,34 @@ class Oracle:
         self._check(self._lib.pa_oracle_rope(T, H, D, _ptr(x, _u16p), _ptr(pos, _i32p),
                                              float(theta), _ptr(y, _f64p)))
         return y
+
+    def e4m3_values(self, codes) -> np.ndarray:
+        """float64 values of OCP FP8 E4M3 codes (uint8)."""
+        c = _as(codes, np.uint8)
+        out = np.zeros(c.shape, np.float64)
+        self._check(self._lib.pa_oracle_e4m3_values(c.size, c.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)),
+                                                    _ptr(out, _f64p)))
+        return out
+
+    def e4m3_to_bf16(self, codes) -> np.ndarray:
+        """bf16 bit patterns (uint16) of the values of E4M3 codes (exact)."""
+        c = _as(codes, np.uint8)
+        out = np.zeros(c.shape, np.uint16)
+        self._check(self._lib.pa_oracle_e4m3_to_bf16(c.size, c.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)),
+                                                     _ptr(out, _u16p)))
+        return out
+
+    def decode_fp8(self, q_bits, k_codes, v_codes, kv_indptr, kv_indices, sm_scale: float,
+                   k_scale: float, v_scale: float, num_kv_heads: int, sel=None):
+        """Decode over E4M3 pools with per-pool scales: the decode of the
+        widened codes with softmax scale sm_scale * k_scale (fp32 product, as
+        the caller's scale is fp32) and the output times v_scale.  The pools
+        are widened in full (use small pools, or `sel` for sampled rows)."""
+        kb = self.e4m3_to_bf16(k_codes)
+        vb = self.e4m3_to_bf16(v_codes)
+        scale = float(np.float32(np.float32(sm_scale) * np.float32(k_scale)))
+        out, lse = self.decode(q_bits, kb, vb, kv_indptr, kv_indices, scale, num_kv_heads, sel=sel)
+        return out * float(np.float32(v_scale)), lse
 
     def merge(self, o_parts, lse_parts):
         """Log-sum-exp merge of partial results of one row: o_parts [n, D], lse_parts [n]."""

@@ -51,6 +51,15 @@
  *         y[i]       = x[i] cos(a_i) - x[i + D/2] sin(a_i)
  *         y[i + D/2] = x[i + D/2] cos(a_i) + x[i] sin(a_i)
  *
+ *   - 8-bit floating-point KV pool (quantisation, FP8 among them, is on the
+ *     Agent-Infer page's roadmap, section "未来规划"; the pages give no format).
+ *     Reading: K and V rows stored as OCP FP8 E4M3 codes (1 sign bit, 4
+ *     exponent bits with bias 7, 3 mantissa bits; no infinities; exponent and
+ *     mantissa all ones is NaN), with one scale per pool: the row values are
+ *     k_scale * code and v_scale * code.  Every E4M3 value is exactly a bf16
+ *     value, so the fp8 decode is the decode above on the widened codes, with
+ *     the softmax scale multiplied by k_scale and the output by v_scale.
+ *
  * All arithmetic is in double precision.  bf16 inputs are widened exactly
  * (a bf16 bit pattern is the upper half of an IEEE binary32).  The softmax
  * scale is given as a float and widened, so both sides use the same value.
@@ -353,6 +362,46 @@ int pa_oracle_rope(int64_t tokens, int32_t heads, int32_t D, const uint16_t *x_b
             }
         }
     }
+    return ORACLE_OK;
+}
+
+/*
+ * Value of an OCP FP8 E4M3 code: (-1)^s * 2^(e - 7) * (1 + m/8) for e > 0,
+ * (-1)^s * 2^-6 * (m/8) for e = 0 (subnormals), NaN for e = 15, m = 7.
+ */
+static double e4m3_value(uint8_t code)
+{
+    const int sign = code >> 7, e = (code >> 3) & 0xF, m = code & 0x7;
+    if (e == 0xF && m == 0x7)
+        return NAN;
+    const double mag = (e == 0) ? ldexp((double)m / 8.0, -6) : ldexp(1.0 + (double)m / 8.0, e - 7);
+    return sign ? -mag : mag;
+}
+
+/*
+ * E4M3 codes -> the bf16 bit patterns of the same values (exact: 3 mantissa
+ * bits and exponents 2^-9 .. 2^8 all fit bf16).  NaN codes give a bf16 NaN.
+ */
+int pa_oracle_e4m3_to_bf16(int64_t n, const uint8_t *codes, uint16_t *bits)
+{
+    if (n < 0)
+        return ORACLE_BAD_SHAPE;
+    for (int64_t i = 0; i < n; i++) {
+        const float f = (float)e4m3_value(codes[i]);
+        uint32_t u;
+        memcpy(&u, &f, sizeof u);
+        bits[i] = (uint16_t)(u >> 16);   /* exact: the low 16 bits are zero */
+    }
+    return ORACLE_OK;
+}
+
+/* Values of n E4M3 codes (for the pins). */
+int pa_oracle_e4m3_values(int64_t n, const uint8_t *codes, double *values)
+{
+    if (n < 0)
+        return ORACLE_BAD_SHAPE;
+    for (int64_t i = 0; i < n; i++)
+        values[i] = e4m3_value(codes[i]);
     return ORACLE_OK;
 }
 

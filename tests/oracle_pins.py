@@ -420,6 +420,65 @@ def pin_rope_norm(o):
     assert np.abs(nx - ny).max() < 1e-12, "rotation changed a pair's length"
 
 
+# ----------------------------------------------------------------------------
+# 8-bit (OCP FP8 E4M3) pool pins
+# ----------------------------------------------------------------------------
+_ALL_CODES = np.arange(256, dtype=np.uint8)
+
+
+def pin_e4m3_matches_torch(o):
+    """All 256 E4M3 codes decode to torch's float8_e4m3fn values (NaN codes included)."""
+    ours = o.e4m3_values(_ALL_CODES)
+    ref = torch.from_numpy(_ALL_CODES.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(ours), np.isnan(ref)), "NaN codes differ"
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ours[ok], ref[ok]), "E4M3 values differ from torch"
+
+
+def pin_e4m3_closed_forms(o):
+    """1.0, the largest finite value 448, the smallest normal 2^-6 and
+    subnormal 2^-9, signed zero, and the NaN codes."""
+    v = o.e4m3_values(np.array([0x38, 0x7E, 0x08, 0x01, 0x00, 0x80, 0xB8, 0x7F, 0xFF], np.uint8))
+    assert list(v[:4]) == [1.0, 448.0, 2.0 ** -6, 2.0 ** -9], "E4M3 closed forms"
+    assert v[4] == 0.0 and v[5] == 0.0 and np.signbit(v[5]) and v[6] == -1.0, "E4M3 signs"
+    assert np.isnan(v[7]) and np.isnan(v[8]), "E4M3 NaN codes"
+
+
+def pin_e4m3_widening_exact(o):
+    """The bf16 patterns the fp8 decode attends over hold the codes' values exactly."""
+    vals = o.e4m3_values(_ALL_CODES)
+    wid = _widen(o.e4m3_to_bf16(_ALL_CODES))
+    ok = ~np.isnan(vals)
+    assert np.array_equal(wid[ok], vals[ok]) and np.all(np.isnan(wid[~ok])), "widening not exact"
+
+
+def pin_decode_fp8_sdpa(o):
+    """fp8 pools with per-pool scales: torch SDPA (float64) on scale * torch's
+    float8_e4m3fn values, contiguous slots, to 1e-12."""
+    rng = np.random.default_rng(51)
+    Hq, Hkv, D, lengths = 8, 2, 16, [5, 1, 12]
+    k_scale, v_scale = 0.5, 0.25
+    N = sum(lengths) + 2
+    q = _random_bits(rng, (len(lengths), Hq, D))
+    kc = torch.from_numpy(rng.standard_normal((N, Hkv, D)) * 2).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    vc = torch.from_numpy(rng.standard_normal((N, Hkv, D)) * 4).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    indptr = np.zeros(len(lengths) + 1, np.int32)
+    indptr[1:] = np.cumsum(lengths)
+    indices = np.arange(sum(lengths), dtype=np.int32) + 2
+    scale = workloads.softmax_scale(D)
+    out, lse = o.decode_fp8(q, kc, vc, indptr, indices, scale, k_scale, v_scale, Hkv)
+    kf = torch.from_numpy(kc.copy()).view(torch.float8_e4m3fn).to(torch.float64) * k_scale
+    vf = torch.from_numpy(vc.copy()).view(torch.float8_e4m3fn).to(torch.float64) * v_scale
+    sm = float(np.float32(scale))   # scales are powers of two: every product is exact
+    for b in range(len(lengths)):
+        ids = torch.from_numpy(indices[indptr[b]:indptr[b + 1]].astype(np.int64))
+        qt = torch.from_numpy(_widen(q[b]))[None, :, None, :]
+        ref = F.scaled_dot_product_attention(qt, kf[ids].permute(1, 0, 2)[None], vf[ids].permute(1, 0, 2)[None],
+                                             scale=sm, enable_gqa=True)
+        err = np.abs(out[b] - ref[0, :, 0, :].numpy()).max()
+        assert err < TOL, f"fp8 decode vs sdpa {err}"
+
+
 ALL_PINS = [
     pin_sdpa_decode, pin_bruteforce_tiny, pin_slot_order, pin_single_token, pin_two_tokens,
     pin_zero_query, pin_constant_values, pin_saturated_softmax, pin_empty_list,
@@ -427,4 +486,5 @@ ALL_PINS = [
     pin_prefill_sdpa, pin_prefill_rows_are_decodes,
     pin_rope_complex_rotation, pin_rope_closed_form, pin_rope_position_zero,
     pin_rope_relative_position, pin_rope_norm,
+    pin_e4m3_matches_torch, pin_e4m3_closed_forms, pin_e4m3_widening_exact, pin_decode_fp8_sdpa,
 ]

@@ -51,6 +51,11 @@ MUTANTS = [
     ("rope_sign_flipped", [("out[i] = x1 * c - x2 * sn;", "out[i] = x1 * c + x2 * sn;", None)]),
     ("rope_frequency_exponent", [("pow(theta, -2.0 * (double)i / (double)D)", "pow(theta, -(double)i / (double)D)", None)]),
     ("rope_second_half_unrotated", [("out[i + half] = x2 * c + x1 * sn;", "out[i + half] = x2;", None)]),
+    ("e4m3_bias_8", [("ldexp(1.0 + (double)m / 8.0, e - 7)", "ldexp(1.0 + (double)m / 8.0, e - 8)", None)]),
+    ("e4m3_subnormal_scale", [("ldexp((double)m / 8.0, -6)", "ldexp((double)m / 8.0, -7)", None)]),
+    ("e4m3_mantissa_width", [("ldexp(1.0 + (double)m / 8.0, e - 7)", "ldexp(1.0 + (double)m / 16.0, e - 7)", None)]),
+    ("e4m3_sign_ignored", [("return sign ? -mag : mag;", "return mag;", None)]),
+    ("e4m3_no_nan", [("if (e == 0xF && m == 0x7)\n        return NAN;", "if (0)\n        return NAN;", None)]),
     ("rope_position_off_by_one", [("(double)positions[t] * inv_freq", "(double)(positions[t] + 1) * inv_freq", None)]),
 ]
 
