@@ -58,12 +58,12 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes(spec, kv_indptr, kv_indices) -> int:
+def algorithmic_bytes(spec, kv_indptr, kv_indices, kv_elem_bytes: int = 2) -> int:
     import numpy as np
     B, Hq, Hkv, D = spec.batch, spec.num_qo_heads, spec.num_kv_heads, spec.head_dim
     unique = int(np.unique(kv_indices).size)
-    return (unique * Hkv * D * 2 * 2 + int(kv_indptr[-1]) * 4 + B * Hq * D * 2 + B * Hq * D * 4
-            + (B + 1) * 4)
+    return (unique * Hkv * D * kv_elem_bytes * 2 + int(kv_indptr[-1]) * 4 + B * Hq * D * 2
+            + B * Hq * D * 4 + (B + 1) * 4)
 
 
 def kernel_source_hash() -> str:
@@ -249,10 +249,10 @@ def run_prefill_bench(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8-e4m3 KV, bf16 q, fp32 math" if fp8 else "bf16",
         "data": "synthetic",
         "config": {
-            "workload": spec.name,
+            "workload": spec.name + ("_fp8kv" if fp8 else ""),
             "batch": B, "num_qo_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
             "cached_len": spec.cached_len, "chunk_len": spec.chunk_len,
             "layers_per_step": layers, "pool_slots": spec.num_slots, "plan_flags": args.flags,
@@ -353,6 +353,8 @@ def main():
     ap.add_argument("--workload", default="batch64",
                     choices=["batch64", "single_request", "batch8", "hd256",
                              "prefill_chunk512", "prefill_chunk64", "append", "copy"])
+    ap.add_argument("--kv", default="bf16", choices=["bf16", "fp8"],
+                    help="decode: pool element type (fp8 = OCP E4M3 codes with per-pool scales)")
     ap.add_argument("--graph", action="store_true",
                     help="decode: replay each step's layer runs from a captured HIP graph")
     ap.add_argument("--copy-gib", type=float, default=4.0)
@@ -389,13 +391,22 @@ def main():
     dev = torch.device("cuda", 0)
     log(f"generating {spec.name}: {layers} layers of {spec.num_slots}-slot pools")
     t0 = time.perf_counter()
-    case = W.make_decode_case(spec, dev, layers=layers)
+    fp8 = args.kv == "fp8"
+    if fp8:   # the same lists and queries over 8-bit pools
+        case = W.make_decode_case(spec, dev, layers=0)
+        for layer in range(layers):
+            k, v = W.make_pools_e4m3(spec.num_slots, spec.num_kv_heads, spec.head_dim,
+                                     W.layer_seed(spec.seed, layer), dev)
+            case.k_pools.append(k)
+            case.v_pools.append(v)
+    else:
+        case = W.make_decode_case(spec, dev, layers=layers)
     torch.cuda.synchronize()
     log(f"inputs ready in {time.perf_counter() - t0:.1f} s "
         f"({torch.cuda.memory_allocated() / 2**30:.1f} GiB on device)")
     idx = torch.as_tensor(case.kv_indices, device=dev)
     B, Hq, Hkv, D = spec.batch, spec.num_qo_heads, spec.num_kv_heads, spec.head_dim
-    bytes_per_layer = algorithmic_bytes(spec, case.kv_indptr, case.kv_indices)
+    bytes_per_layer = algorithmic_bytes(spec, case.kv_indptr, case.kv_indices, 1 if fp8 else 2)
     outs = [torch.empty((B, Hq, D), dtype=torch.float32, device=dev) for _ in range(layers)]
     plan = pa.Plan(B, int(case.kv_indptr[-1]), Hq, Hkv, D)
     stream = torch.cuda.current_stream(dev)
@@ -403,8 +414,12 @@ def main():
 
     def layer_runs(s):
         for layer in range(layers):
-            plan.decode(case.q, case.k_pools[layer], case.v_pools[layer], idx, case.sm_scale,
-                        outs[layer], stream=s)
+            if fp8:
+                plan.decode_fp8(case.q, case.k_pools[layer], case.v_pools[layer], idx, case.sm_scale,
+                                W.FP8_K_SCALE, W.FP8_V_SCALE, outs[layer], stream=s)
+            else:
+                plan.decode(case.q, case.k_pools[layer], case.v_pools[layer], idx, case.sm_scale,
+                            outs[layer], stream=s)
 
     graph = None
     if args.graph:
@@ -484,12 +499,12 @@ def main():
     step_bytes = bytes_per_layer * layers
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = bytes_per_layer / (kernel_avg_ms * 1e-3) / 1e9
-    traffic = traffic_per_launch() if spec is W.BATCH64_SHARED_PREFIX else None
+    traffic = traffic_per_launch() if spec is W.BATCH64_SHARED_PREFIX and not fp8 else None
 
     G = Hq // Hkv
     result = {
-        "metric": METRIC if spec is W.BATCH64_SHARED_PREFIX else
-        f"decode-attn µs/step/layer + achieved HBM GB/s (% of MI355X peak), {spec.name}",
+        "metric": METRIC if spec is W.BATCH64_SHARED_PREFIX and not fp8 else
+        f"decode-attn µs/step/layer + achieved HBM GB/s (% of MI355X peak), {spec.name}, {args.kv} KV",
         "value": round(value, 1),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -499,10 +514,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8-e4m3 KV, bf16 q, fp32 math" if fp8 else "bf16",
         "data": "synthetic",
         "config": {
-            "workload": spec.name,
+            "workload": spec.name + ("_fp8kv" if fp8 else ""),
             "batch": B, "num_qo_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
             "layers_per_step": layers,
             "kv_len": f"uniform [{spec.len_lo}, {spec.len_hi}]",
@@ -528,12 +543,13 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": f"decode_kernel<{D},{G}> (pa_decode_run)",
+            "kernel": f"decode_kernel<{D},{G},{'e4m3' if fp8 else 'bf16'}> "
+                      f"({'pa_decode_run_fp8' if fp8 else 'pa_decode_run'})",
             "kernel_avg_us": round(kernel_avg_ms * 1e3, 2),
         },
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not fp8:
         log(f"cpu baseline: fp64 oracle on layer 0 for ~{args.cpu_seconds:.0f} s")
         torch.cuda.synchronize()
         cpu, err = cpu_baseline(case, spec, bytes_per_layer, args.cpu_seconds, outs[0].cpu().numpy())

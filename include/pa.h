@@ -155,6 +155,22 @@ pa_status pa_decode_run(const pa_plan_t *plan, const void *q, const void *k_pool
                         float *lse, pa_stream_t stream);
 
 /*
+ * pa_decode_run_fp8: pa_decode_run over 8-bit pools.  The pools hold OCP FP8
+ * E4M3 codes (1 byte per element, same [slots, Hkv, D] layout and slot
+ * stride in elements = bytes), and the row values are k_scale * code and
+ * v_scale * code (one scale per pool).  Quantised KV is on the Agent-Infer
+ * page's roadmap (section "未来规划": FP8 among the quantisation formats); the
+ * format and the per-pool scales are this library's reading.  Same plan,
+ * arguments, output and errors as pa_decode_run, plus PA_ERR_INVALID_ARG for
+ * a non-finite scale.  Code 0x7F / 0xFF (NaN) in a referenced row makes the
+ * results NaN; unreferenced rows are never read.
+ */
+pa_status pa_decode_run_fp8(const pa_plan_t *plan, const void *q, const void *k_pool,
+                            const void *v_pool, int64_t num_slots, int64_t slot_stride,
+                            const int32_t *kv_indices, float sm_scale, float k_scale,
+                            float v_scale, float *out, float *lse, pa_stream_t stream);
+
+/*
  * pa_prefill_chunk_run: chunked-prefill attention of one layer under a
  * prefill plan (pa_plan with qo_indptr_host != NULL).
  *   q [T, Hq, D] bf16 with T = qo_indptr[batch]; pools and kv_indices as in

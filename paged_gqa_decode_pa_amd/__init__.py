@@ -96,6 +96,8 @@ def _load() -> ctypes.CDLL:
     lib.pa_plan_host_timing.argtypes = [vp, ctypes.POINTER(ctypes.c_double),
                                         ctypes.POINTER(ctypes.c_double)]
     lib.pa_plan_host_timing.restype = ctypes.c_int
+    lib.pa_decode_run_fp8.argtypes = [vp, vp, vp, vp, i64, i64, vp, f32, f32, f32, vp, vp, vp]
+    lib.pa_decode_run_fp8.restype = ctypes.c_int
     lib.pa_kv_append.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp, vp, i64, i64, vp]
     lib.pa_kv_append.restype = ctypes.c_int
     return lib
@@ -206,6 +208,32 @@ def pa_decode_run(plan, q, k_pool, v_pool, kv_indices, sm_scale, out, lse=None,
          out, lse, num_slots, slot_stride, stream)
 
 
+def pa_decode_run_fp8(plan, q, k_pool, v_pool, kv_indices, sm_scale, k_scale, v_scale, out, lse=None,
+                      num_slots=None, slot_stride=None, stream=None) -> None:
+    """Decode over E4M3 pools (torch.float8_e4m3fn or uint8 [slots, Hkv, D])."""
+    head_dim = q.shape[-1]
+    for name, t in (("k_pool", k_pool), ("v_pool", v_pool)):
+        if t.dtype not in (torch.float8_e4m3fn, torch.uint8):
+            raise TypeError(f"{name} must hold E4M3 codes (float8_e4m3fn or uint8)")
+    if slot_stride is None:
+        slot_stride = _pool_stride(k_pool, v_pool, head_dim)
+    if num_slots is None:
+        num_slots = k_pool.shape[0]
+    if kv_indices.dtype != torch.int32:
+        raise TypeError("kv_indices must be int32")
+    if out.dtype != torch.float32 or not out.is_contiguous():
+        raise TypeError("out must be a contiguous float32 tensor")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
+        raise TypeError("lse must be a contiguous float32 tensor")
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    _check(_lib.pa_decode_run_fp8(plan, _dev_ptr(q, "q", torch.bfloat16), _dev_ptr(k_pool, "k_pool"),
+                                  _dev_ptr(v_pool, "v_pool"), int(num_slots), int(slot_stride),
+                                  _dev_ptr(kv_indices, "kv_indices"), float(sm_scale), float(k_scale),
+                                  float(v_scale), _dev_ptr(out, "out"), _dev_ptr(lse, "lse"),
+                                  _stream(stream)), "pa_decode_run_fp8")
+
+
 def pa_prefill_chunk_run(plan, q, k_pool, v_pool, kv_indices, sm_scale, out, lse=None,
                          num_slots=None, slot_stride=None, stream=None) -> None:
     _run(_lib.pa_prefill_chunk_run, "pa_prefill_chunk_run", plan, q, k_pool, v_pool,
@@ -307,6 +335,11 @@ class Plan:
 
     def decode(self, q, k_pool, v_pool, kv_indices, sm_scale, out, lse=None, **kw) -> None:
         pa_decode_run(self.handle, q, k_pool, v_pool, kv_indices, sm_scale, out, lse, **kw)
+
+    def decode_fp8(self, q, k_pool, v_pool, kv_indices, sm_scale, k_scale, v_scale, out, lse=None,
+                   **kw) -> None:
+        pa_decode_run_fp8(self.handle, q, k_pool, v_pool, kv_indices, sm_scale, k_scale, v_scale, out,
+                          lse, **kw)
 
     def prefill(self, q, k_pool, v_pool, kv_indices, sm_scale, out, lse=None, **kw) -> None:
         pa_prefill_chunk_run(self.handle, q, k_pool, v_pool, kv_indices, sm_scale, out, lse, **kw)

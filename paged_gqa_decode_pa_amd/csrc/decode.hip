@@ -71,8 +71,6 @@ constexpr float kRescaleSlack = 8.0f;
 // index stride.
 constexpr int32_t kBufferWord3 = 0x00020000;
 
-__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
@@ -269,18 +267,61 @@ template <bool WIDE>
 struct RowAddr;
 template <>
 struct RowAddr<false> {
-    static __device__ __forceinline__ const uint4 *at(const char *base, int32_t slot,
-                                                      uint32_t stride_bytes, uint32_t lane_off) {
+    static __device__ __forceinline__ const char *at(const char *base, int32_t slot,
+                                                     uint32_t stride_bytes, uint32_t lane_off) {
         uint32_t off = __umul24((uint32_t)slot, stride_bytes) + lane_off;
-        return reinterpret_cast<const uint4 *>(base + off);
+        return base + off;
     }
 };
 template <>
 struct RowAddr<true> {
-    static __device__ __forceinline__ const uint4 *at(const char *base, int32_t slot,
-                                                      uint32_t stride_bytes, uint32_t lane_off) {
+    static __device__ __forceinline__ const char *at(const char *base, int32_t slot,
+                                                     uint32_t stride_bytes, uint32_t lane_off) {
         uint64_t off = (uint64_t)(uint32_t)slot * stride_bytes + lane_off;
-        return reinterpret_cast<const uint4 *>(base + off);
+        return base + off;
+    }
+};
+
+// Element type of the pools.  bf16: a lane's 8 elements of a row are one
+// 16-byte load, already in the dot-product and FMA operand formats.  OCP FP8
+// E4M3 (8-bit pools): the same 8 elements are one 8-byte load; K codes are
+// widened to bf16 pairs (exact: every E4M3 value is a bf16 value) for the
+// dot products and V codes to fp32 for the weighted sum, with
+// v_cvt_scalef32_pk_bf16_fp8 / v_cvt_pk_f32_fp8 (scale 1: the pools' scales
+// are applied to the softmax scale and to the output).
+template <bool KV8>
+struct PoolRow;
+template <>
+struct PoolRow<false> {
+    using T = uint4;
+    static constexpr uint32_t kElemBytes = 2;
+    static __device__ __forceinline__ uint4 k_bf16(const uint4 &x) { return x; }
+    static __device__ __forceinline__ void v_f32(const uint4 &x, float (&f)[8]) {
+        // a bf16 value is the upper half of the fp32 with the same value
+        f[0] = __uint_as_float(x.x << 16); f[1] = __uint_as_float(x.x & 0xffff0000u);
+        f[2] = __uint_as_float(x.y << 16); f[3] = __uint_as_float(x.y & 0xffff0000u);
+        f[4] = __uint_as_float(x.z << 16); f[5] = __uint_as_float(x.z & 0xffff0000u);
+        f[6] = __uint_as_float(x.w << 16); f[7] = __uint_as_float(x.w & 0xffff0000u);
+    }
+};
+template <>
+struct PoolRow<true> {
+    using T = uint2;
+    static constexpr uint32_t kElemBytes = 1;
+    static __device__ __forceinline__ uint32_t pair(uint32_t w, bool hi) {
+        return hi ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true))
+                  : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+    }
+    static __device__ __forceinline__ uint4 k_bf16(const uint2 &x) {
+        return make_uint4(pair(x.x, false), pair(x.x, true), pair(x.y, false), pair(x.y, true));
+    }
+    static __device__ __forceinline__ void v_f32(const uint2 &x, float (&f)[8]) {
+        const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(x.x, false);
+        const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(x.x, true);
+        const auto c = __builtin_amdgcn_cvt_pk_f32_fp8(x.y, false);
+        const auto d = __builtin_amdgcn_cvt_pk_f32_fp8(x.y, true);
+        f[0] = a[0]; f[1] = a[1]; f[2] = b[0]; f[3] = b[1];
+        f[4] = c[0]; f[5] = c[1]; f[6] = d[0]; f[7] = d[1];
     }
 };
 
@@ -357,17 +398,19 @@ constexpr int decode_waves_per_simd() {
     return G <= 4 ? 3 : 2;
 }
 
-template <int D, int G, bool WIDE>
+template <int D, int G, bool WIDE, bool KV8>
 __global__ __launch_bounds__(kDecodeThreads)
 __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<G>(), 8))) void decode_kernel(
     const int32_t *__restrict__ wg_offsets, const pa_work_unit *__restrict__ units,
     const pa_merge_unit *__restrict__ merges, int32_t *__restrict__ arrivals,
     const uint16_t *__restrict__ q, const char *__restrict__ k_pool,
     const char *__restrict__ v_pool, uint32_t stride_bytes,
-    const int32_t *__restrict__ kv_indices, float scale_log2, float *__restrict__ out,
+    const int32_t *__restrict__ kv_indices, float scale_log2, float out_scale, float *__restrict__ out,
     float *__restrict__ lse, float *__restrict__ part_o, float *__restrict__ part_lse,
     int32_t num_qo_heads) {
     using Geo = Geometry<D>;
+    using PR = PoolRow<KV8>;
+    using Row = typename PR::T;
     constexpr int LPR = Geo::LPR, RPI = Geo::RPI, NI = Geo::NI, TILE = Geo::TILE;
     constexpr int WAVES = kDecodeWaves;
 
@@ -431,7 +474,7 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<G>(), 8))) void decode_
         }
     }
 
-    const uint32_t lane_off = (uint32_t)(unit.kv_head * D + c * 8) * 2u;
+    const uint32_t lane_off = (uint32_t)(unit.kv_head * D + c * 8) * PR::kElemBytes;
     const int32_t kv_begin = unit.kv_begin, kv_end = unit.kv_end;
     const int32_t n_tiles = (kv_end - kv_begin + TILE - 1) / TILE;
 
@@ -458,23 +501,23 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<G>(), 8))) void decode_
             slot[i] = __builtin_amdgcn_raw_buffer_load_b32(
                 slot_rsrc, min(e4, last4 - i * RPI * 4) + i * RPI * 4, 0, 0);
     };
-    auto load_k = [&](uint4(&k)[NI], const int32_t(&slot)[NI]) {
+    auto load_k = [&](Row(&k)[NI], const int32_t(&slot)[NI]) {
 #pragma unroll
         for (int i = 0; i < NI; i++)
-            k[i] = *RowAddr<WIDE>::at(k_pool, slot[i], stride_bytes, lane_off);
+            k[i] = *reinterpret_cast<const Row *>(RowAddr<WIDE>::at(k_pool, slot[i], stride_bytes, lane_off));
     };
-    auto load_v = [&](uint4(&v)[NI], const int32_t(&slot)[NI]) {
+    auto load_v = [&](Row(&v)[NI], const int32_t(&slot)[NI]) {
 #pragma unroll
         for (int i = 0; i < NI; i++)
-            v[i] = *RowAddr<WIDE>::at(v_pool, slot[i], stride_bytes, lane_off);
+            v[i] = *reinterpret_cast<const Row *>(RowAddr<WIDE>::at(v_pool, slot[i], stride_bytes, lane_off));
     };
     // scores of this lane's head (lane % G) for the tile's tokens, log2 domain
-    auto qk = [&](const uint4(&k)[NI], float(&s)[NI], int tile) {
+    auto qk = [&](const Row(&k)[NI], float(&s)[NI], int tile) {
         // entries of the tile left in the unit (uniform)
         const int32_t left = kv_end - kv_begin - tile * TILE;
 #pragma unroll
         for (int i = 0; i < NI; i++) {
-            const float sc = row_scores<G, LPR>(qv, k[i]) * scale_log2;
+            const float sc = row_scores<G, LPR>(qv, PR::k_bf16(k[i])) * scale_log2;
             s[i] = (r + i * RPI < left) ? sc : -INFINITY;
         }
     };
@@ -504,14 +547,11 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<G>(), 8))) void decode_
             l_run += p[i];
         }
     };
-    auto pv = [&](const uint4(&v)[NI], const float(&p)[NI]) {
+    auto pv = [&](const Row(&v)[NI], const float(&p)[NI]) {
 #pragma unroll
         for (int i = 0; i < NI; i++) {
             float vf[8];
-            vf[0] = bf16_lo(v[i].x); vf[1] = bf16_hi(v[i].x);
-            vf[2] = bf16_lo(v[i].y); vf[3] = bf16_hi(v[i].y);
-            vf[4] = bf16_lo(v[i].z); vf[5] = bf16_hi(v[i].z);
-            vf[6] = bf16_lo(v[i].w); vf[7] = bf16_hi(v[i].w);
+            PR::v_f32(v[i], vf);
 #pragma unroll
             for (int h = 0; h < G; h++) {
                 const float ph = group_bcast<G>(p[i], h, lane);
@@ -532,7 +572,7 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<G>(), 8))) void decode_
     int tile = wave;
     if (tile < n_tiles) {
         int32_t sa[NI], sb[NI];
-        uint4 ka[NI], va[NI], kb[NI], vb[NI];
+        Row ka[NI], va[NI], kb[NI], vb[NI];
         load_slots(sa, tile);
         load_slots(sb, tile + WAVES);
         load_k(ka, sa);
@@ -541,7 +581,7 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<G>(), 8))) void decode_
         load_v(vb, sb);
         load_slots(sa, tile + 2 * WAVES);
         load_slots(sb, tile + 3 * WAVES);
-        auto compute = [&](const uint4(&k)[NI], const uint4(&v)[NI]) {
+        auto compute = [&](const Row(&k)[NI], const Row(&v)[NI]) {
             float sc[NI], pw[NI];
             qk(k, sc, tile);
             softmax(sc, pw);
@@ -610,7 +650,7 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<G>(), 8))) void decode_
             l = fmaf(wgt, lds_l[w][h], l);
         }
         const bool empty = !(l > 0.f);
-        const float res = empty ? 0.f : o / l;
+        const float res = empty ? 0.f : o / l * out_scale;
         const float lse2 = empty ? -INFINITY : M + fast_log2(l);
         if (unit.partial < 0) {
             out[(int64_t)(qrow0 + h) * D + d] = res;
@@ -654,33 +694,40 @@ bool row_offsets_fit_32(int64_t num_slots, uint32_t stride_bytes) {
 
 namespace {
 
-template <int D, int G>
-int launch_decode_dg(const DecodeLaunch &l, hipStream_t stream) {
-    const uint32_t stride_bytes = (uint32_t)(l.slot_stride * 2);
+template <int D, int G, bool KV8>
+int launch_decode_dgk(const DecodeLaunch &l, hipStream_t stream) {
+    const uint32_t stride_bytes = (uint32_t)(l.slot_stride * PoolRow<KV8>::kElemBytes);
     // the 32-bit row address needs every byte offset below 2^31 (it is
     // sign-extended into the address) and 24-bit multiply operands
     const bool wide = !row_offsets_fit_32(l.num_slots, stride_bytes);
-    const float scale_log2 = l.sm_scale * kLog2e;
+    // 8-bit pools: K = k_scale * code enters the scores, V = v_scale * code the output
+    const float scale_log2 = (KV8 ? l.sm_scale * l.k_scale : l.sm_scale) * kLog2e;
+    const float out_scale = KV8 ? l.v_scale : 1.0f;
     dim3 grid(l.n_workgroups), block(kDecodeThreads);
     if (wide)
-        hipLaunchKernelGGL((decode_kernel<D, G, true>), grid, block, 0, stream, l.wg_offsets, l.units,
+        hipLaunchKernelGGL((decode_kernel<D, G, true, KV8>), grid, block, 0, stream, l.wg_offsets, l.units,
                            l.merges, l.arrivals,
                            (const uint16_t *)l.q, (const char *)l.k_pool, (const char *)l.v_pool,
-                           stride_bytes, l.kv_indices, scale_log2, l.out, l.lse, l.partial_o,
+                           stride_bytes, l.kv_indices, scale_log2, out_scale, l.out, l.lse, l.partial_o,
                            l.partial_lse, l.num_qo_heads);
     else
-        hipLaunchKernelGGL((decode_kernel<D, G, false>), grid, block, 0, stream, l.wg_offsets, l.units,
+        hipLaunchKernelGGL((decode_kernel<D, G, false, KV8>), grid, block, 0, stream, l.wg_offsets, l.units,
                            l.merges, l.arrivals,
                            (const uint16_t *)l.q, (const char *)l.k_pool, (const char *)l.v_pool,
-                           stride_bytes, l.kv_indices, scale_log2, l.out, l.lse, l.partial_o,
+                           stride_bytes, l.kv_indices, scale_log2, out_scale, l.out, l.lse, l.partial_o,
                            l.partial_lse, l.num_qo_heads);
     return (int)hipGetLastError();
 }
 
 template <int D, int G>
+int launch_decode_dg(const DecodeLaunch &l, hipStream_t stream) {
+    return l.kv_fp8 ? launch_decode_dgk<D, G, true>(l, stream) : launch_decode_dgk<D, G, false>(l, stream);
+}
+
+template <int D, int G>
 int occupancy_dg() {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<D, G, false>, kDecodeThreads, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<D, G, false, false>, kDecodeThreads, 0) !=
         hipSuccess)
         return 0;
     return n;

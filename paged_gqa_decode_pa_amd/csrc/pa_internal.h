@@ -113,6 +113,8 @@ struct DecodeLaunch {
     int32_t num_qo_heads;
     int32_t num_kv_heads;
     int32_t head_dim;
+    bool kv_fp8 = false;             // pools of OCP FP8 E4M3 codes (decode only)
+    float k_scale = 1.f, v_scale = 1.f;   // their per-pool scales
 };
 
 int launch_decode(const DecodeLaunch &l, void *stream);   // returns hipError_t

@@ -1,0 +1,145 @@
+"""Decode over 8-bit (OCP FP8 E4M3) pools with per-pool scales, through the
+C ABI (pa_decode_run_fp8), against the fp64 oracle on the same codes.  Needs
+an AMD GPU."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_gqa_decode_pa_amd as pa
+import workloads as W
+from gpu_util import TOL, device, max_err, run_decode, say
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+KS, VS = W.FP8_K_SCALE, W.FP8_V_SCALE
+
+
+def run_fp8(q, k, v, ip, idx_dev, scale, Hkv, flags=0, k_scale=KS, v_scale=VS):
+    B, Hq, D = q.shape
+    out = torch.full((B, Hq, D), float("nan"), dtype=torch.float32, device=q.device)
+    lse = torch.full((B, Hq), float("nan"), dtype=torch.float32, device=q.device)
+    forced = (flags >> pa.PA_PLAN_FORCE_SPLITS_SHIFT) & 0xFFFF
+    with pa.Plan(max(B, 1), max(int(ip[-1]), 1, B * forced * 256), Hq, Hkv, D) as plan:
+        plan.plan(ip, flags=flags)
+        plan.decode_fp8(q, k, v, idx_dev, scale, k_scale, v_scale, out, lse)
+        torch.cuda.synchronize()
+    return out.cpu().numpy(), lse.cpu().numpy()
+
+
+def _case(lengths, Hq, Hkv, D, N, seed):
+    dev = device()
+    rng = np.random.Generator(np.random.PCG64(seed))
+    ip, idx = W.slot_lists(np.asarray(lengths), N, rng)
+    q = W.normal_bf16((len(lengths), Hq, D), seed + 1, dev)
+    k, v = W.make_pools_e4m3(N, Hkv, D, seed + 2, dev)
+    return ip, idx, q, k, v
+
+
+def _oracle(q, k, v, ip, idx, scale, Hkv, sel=None, k_scale=KS, v_scale=VS):
+    return oracle.load().decode_fp8(W.bits(q), W.codes(k), W.codes(v), ip, idx, scale, k_scale, v_scale,
+                                    Hkv, sel=sel)
+
+
+CASES = [
+    ([1, 7, 64, 300, 1025], 32, 8, 128),
+    ([0, 2, 513], 32, 8, 128),
+    ([100, 2000], 8, 8, 128),
+    ([33, 700], 16, 8, 128),
+    ([50, 900, 3], 64, 8, 128),
+    ([17, 1500], 16, 4, 256),
+    ([400, 5], 8, 8, 256),
+]
+
+
+@pytest.mark.parametrize("lengths,Hq,Hkv,D", CASES, ids=[f"{c[1]}x{c[2]}x{c[3]}-{i}" for i, c in enumerate(CASES)])
+def test_fp8_small_parity(lengths, Hq, Hkv, D):
+    say(f"fp8 decode parity lengths={lengths} Hq={Hq} Hkv={Hkv} D={D}")
+    ip, idx, q, k, v = _case(lengths, Hq, Hkv, D, 8192, 300 + Hq + D + len(lengths))
+    scale = W.softmax_scale(D)
+    out, lse = run_fp8(q, k, v, ip, torch.as_tensor(idx, device=device()), scale, Hkv)
+    ref, ref_lse = _oracle(q, k, v, ip, idx, scale, Hkv)
+    e, el = max_err(out, ref), max_err(lse, ref_lse)
+    say(f"  max|d| out={e:.3g} lse={el:.3g}")
+    assert e <= TOL and el <= TOL
+
+
+@pytest.mark.parametrize("n", [2, 7])
+def test_fp8_forced_splits_agree(n):
+    say(f"fp8 forced splits n={n}")
+    ip, idx, q, k, v = _case([300, 1025, 9], 32, 8, 128, 8192, 71)
+    idx_dev = torch.as_tensor(idx, device=device())
+    scale = W.softmax_scale(128)
+    base, _ = run_fp8(q, k, v, ip, idx_dev, scale, 8)
+    out, _ = run_fp8(q, k, v, ip, idx_dev, scale, 8, flags=pa.PA_PLAN_FORCE_SPLITS(n))
+    assert max_err(out, base.astype(np.float64)) <= 1e-5
+
+
+def test_fp8_equals_bf16_path_on_the_same_values():
+    """With unit scales, decode over E4M3 codes equals (bit for bit) the bf16
+    decode over pools holding the codes' values: the codes widen exactly."""
+    say("fp8 vs bf16 path on identical values")
+    ip, idx, q, k, v = _case([1, 90, 600, 2049], 32, 8, 128, 8192, 81)
+    idx_dev = torch.as_tensor(idx, device=device())
+    scale = W.softmax_scale(128)
+    out8, lse8 = run_fp8(q, k, v, ip, idx_dev, scale, 8, k_scale=1.0, v_scale=1.0)
+    kb, vb = k.to(torch.bfloat16), v.to(torch.bfloat16)
+    out16, lse16 = run_decode(q, kb, vb, ip, idx_dev, scale, 8)
+    assert np.array_equal(out8, out16) and np.array_equal(lse8, lse16)
+
+
+def test_fp8_poisoned_pool():
+    """NaN codes in every unreferenced slot change nothing."""
+    say("fp8 poisoned pool")
+    dev = device()
+    ip, idx, q, k, v = _case([150, 333, 2], 32, 8, 128, 4096, 91)
+    idx_dev = torch.as_tensor(idx, device=dev)
+    scale = W.softmax_scale(128)
+    clean, _ = run_fp8(q, k, v, ip, idx_dev, scale, 8)
+    keep = torch.zeros(k.shape[0], dtype=torch.bool, device=dev)
+    keep[torch.as_tensor(idx.astype(np.int64), device=dev)] = True
+    for pool in (k, v):
+        pool.view(torch.uint8)[~keep] = 0x7F
+    dirty, _ = run_fp8(q, k, v, ip, idx_dev, scale, 8)
+    assert np.array_equal(clean, dirty)
+
+
+def test_fp8_large_pool_offsets():
+    """Rows past 2^31 bytes of an 8-bit pool (64-bit row offsets)."""
+    say("fp8 large pool: 2,300,000 slots x 8 heads x 128")
+    dev = device()
+    N = 2_300_000
+    rng = np.random.Generator(np.random.PCG64(101))
+    ip, idx = W.slot_lists(np.asarray([700, 260]), N, rng)
+    idx[:64] = N - 1 - np.arange(64)
+    q = W.normal_bf16((2, 32, 128), 102, dev)
+    k, v = W.make_pools_e4m3(N, 8, 128, 103, dev)
+    scale = W.softmax_scale(128)
+    out, lse = run_fp8(q, k, v, ip, torch.as_tensor(idx, device=dev), scale, 8)
+    ref, ref_lse = _oracle(q, k, v, ip, idx, scale, 8)
+    assert max_err(out, ref) <= TOL and max_err(lse, ref_lse) <= TOL
+    del k, v
+    torch.cuda.empty_cache()
+
+
+def test_fp8_batch64_workload_sampled():
+    """The batch-64 shared-prefix workload over 8-bit pools, sampled rows."""
+    spec = W.BATCH64_SHARED_PREFIX
+    say(f"fp8 workload {spec.name}: sampled rows")
+    dev = device()
+    ip, idx = W.decode_lists(spec)
+    q = W.normal_bf16((spec.batch, spec.num_qo_heads, spec.head_dim), spec.seed, dev)
+    k, v = W.make_pools_e4m3(spec.num_slots, spec.num_kv_heads, spec.head_dim, W.layer_seed(spec.seed, 0), dev)
+    scale = W.softmax_scale(spec.head_dim)
+    out, lse = run_fp8(q, k, v, ip, torch.as_tensor(idx, device=dev), scale, spec.num_kv_heads)
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    rng = np.random.Generator(np.random.PCG64(5))
+    rows = np.unique(np.concatenate([np.arange(spec.num_qo_heads),
+                                     rng.integers(0, spec.batch * spec.num_qo_heads, 300)])).astype(np.int32)
+    ref, ref_lse = _oracle(q, k, v, ip, idx, scale, spec.num_kv_heads, sel=rows)
+    D = spec.head_dim
+    e = max_err(out.reshape(-1, D), ref.reshape(-1, D), rows=rows)
+    el = max_err(lse.reshape(-1), ref_lse.reshape(-1), rows=rows)
+    say(f"  {rows.size} rows: max|d| out={e:.3g} lse={el:.3g}")
+    assert e <= TOL and el <= TOL

@@ -197,6 +197,38 @@ def make_pools(num_slots: int, num_kv_heads: int, head_dim: int, seed: int, devi
     return k, v
 
 
+# Per-pool scales of the 8-bit workloads: codes hold value / scale.
+FP8_K_SCALE = 0.25
+FP8_V_SCALE = 0.5
+
+
+def normal_e4m3(shape, seed: int, scale: float, device="cpu", chunk_elems: int = 1 << 28):
+    """OCP FP8 E4M3 codes (torch.float8_e4m3fn) of N(0,1) float32 draws divided
+    by `scale`, rounded to nearest-even, filled in chunks."""
+    out = torch.empty(shape, dtype=torch.float8_e4m3fn, device=device)
+    flat = out.view(-1)
+    g = _generator(device, seed)
+    n = flat.numel()
+    for start in range(0, n, chunk_elems):
+        stop = min(n, start + chunk_elems)
+        x = torch.randn(stop - start, generator=g, device=device, dtype=torch.float32)
+        flat[start:stop] = (x / scale).to(torch.float8_e4m3fn)
+    return out
+
+
+def make_pools_e4m3(num_slots: int, num_kv_heads: int, head_dim: int, seed: int, device="cpu",
+                    k_scale: float = FP8_K_SCALE, v_scale: float = FP8_V_SCALE):
+    """(K, V) pools of E4M3 codes, each [num_slots, Hkv, D]."""
+    k = normal_e4m3((num_slots, num_kv_heads, head_dim), seed * 2 + 0, k_scale, device)
+    v = normal_e4m3((num_slots, num_kv_heads, head_dim), seed * 2 + 1, v_scale, device)
+    return k, v
+
+
+def codes(t: "torch.Tensor") -> np.ndarray:
+    """uint8 codes of an E4M3 tensor, on the host."""
+    return t.detach().contiguous().view(torch.uint8).cpu().numpy()
+
+
 def layer_seed(seed: int, layer: int) -> int:
     return seed * 1000 + 1 + layer
 
