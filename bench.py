@@ -249,10 +249,10 @@ def run_prefill_bench(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8-e4m3 KV, bf16 q, fp32 math" if fp8 else "bf16",
+        "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": spec.name + ("_fp8kv" if fp8 else ""),
+            "workload": spec.name,
             "batch": B, "num_qo_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
             "cached_len": spec.cached_len, "chunk_len": spec.chunk_len,
             "layers_per_step": layers, "pool_slots": spec.num_slots, "plan_flags": args.flags,
