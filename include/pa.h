@@ -98,6 +98,19 @@ typedef enum pa_status {
 /* Keep the automatic split but place workgroups in plain order instead of
  * grouping neighbouring requests on one XCD. */
 #define PA_PLAN_NO_XCD_ORDER 0x1u
+/* Balance the automatic decode partition over the XCDs by their measured
+ * speed.  The decode launches of a plan computed with this flag record, per
+ * XCD, how long its workgroups ran (one atomic add per workgroup).  A later
+ * pa_plan call with the flag reads those records without waiting (each call
+ * starts an asynchronous copy that a following call consumes once it has
+ * completed) and moves each XCD's share of the next partition towards the
+ * rate its workgroups achieved: the XCDs of one GPU run at unequal speeds
+ * that change from run to run, and an equal split leaves the fast ones idle
+ * while the slowest finishes.  Ignored for prefill and forced splits.  For a
+ * fixed plan the results are deterministic; two steps with identical inputs
+ * may be cut differently and so differ by rounding (within the usual
+ * tolerance).  The weights in use are read with pa_plan_xcd_weights. */
+#define PA_PLAN_XCD_FEEDBACK 0x2u
 
 /* Largest max_kv_total a plan accepts: list entries are addressed with 32-bit
  * byte offsets. */
@@ -282,6 +295,39 @@ pa_status pa_partition(const int32_t *kv_indptr_host, const int32_t *qo_indptr_h
                        int32_t unit_capacity, pa_merge_unit *merges, int32_t merge_capacity,
                        int32_t *n_workgroups, int32_t *n_units, int32_t *n_merges,
                        int32_t *n_partials);
+
+/*
+ * pa_partition_weighted: pa_partition with per-XCD work weights: in the
+ * automatic decode split the workgroups placed on XCD x (workgroup id w runs
+ * on XCD w % 8) get xcd_weights[x] times the budget of an equal split.
+ * n_weights must be 8 (the XCDs of an MI355X) and every weight in
+ * [0.25, 4]; they need not average 1 (the budgets are rescaled to the work).
+ * xcd_weights = NULL is pa_partition.  Other modes ignore the weights.
+ */
+pa_status pa_partition_weighted(const int32_t *kv_indptr_host, const int32_t *qo_indptr_host,
+                                int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,
+                                int32_t head_dim, uint32_t flags, int32_t max_workgroups,
+                                const float *xcd_weights, int32_t n_weights,
+                                int32_t *wg_offsets, int32_t wg_capacity, pa_work_unit *units,
+                                int32_t unit_capacity, pa_merge_unit *merges,
+                                int32_t merge_capacity, int32_t *n_workgroups, int32_t *n_units,
+                                int32_t *n_merges, int32_t *n_partials);
+
+/*
+ * pa_plan_xcd_weights: the per-XCD weights the plan's next automatic decode
+ * partition will use (share of an XCD's workgroups relative to an equal
+ * split; they average 1).  *n_xcd receives the XCD count and
+ * min(capacity, *n_xcd) weights are written to `weights` (which may be NULL
+ * when capacity is 0).  They start at 1 and change only through
+ * pa_plan_set_xcd_weights or the measurements of PA_PLAN_XCD_FEEDBACK.
+ *
+ * pa_plan_set_xcd_weights: set them.  n must equal the XCD count and every
+ * weight be finite and in [0.25, 4]; they are rescaled to average 1.  Used by
+ * callers that know their XCDs' speeds, or to pin a partition.
+ */
+pa_status pa_plan_xcd_weights(const pa_plan_t *plan, float *weights, int32_t capacity,
+                              int32_t *n_xcd);
+pa_status pa_plan_set_xcd_weights(pa_plan_t *plan, const float *weights, int32_t n);
 
 /*
  * Kernel timing (instrumentation for benchmarks).  pa_profile_begin creates

@@ -45,6 +45,18 @@ struct pa_plan {
     int32_t n_workgroups = 0, n_units = 0, n_merges = 0, n_partials = 0;
     pa::PartitionScratch scratch;  // host working arrays of the partition
     double plan_total_us = 0.0, plan_wait_us = 0.0;  // host time of the last pa_plan
+    // per-XCD work weights of the automatic decode split, and their feedback
+    // (PA_PLAN_XCD_FEEDBACK): the decode kernel adds each workgroup's run
+    // time to d_xcd_clock; pa_plan copies the counters to h_xcd_clock and a
+    // later call turns the difference of two copies into new weights
+    float xcd_weight[pa::kMaxXcd];
+    uint64_t *d_xcd_clock = nullptr;     // device, one 256-byte line per XCD
+    uint64_t *h_xcd_clock = nullptr;     // pinned copy of those lines
+    hipEvent_t clock_done = nullptr;
+    bool clock_pending = false;          // a copy is in flight or unread
+    uint64_t clock_last[pa::kMaxXcd] = {};       // the copy read last
+    float clock_weight[pa::kMaxXcd];     // weights of the launches the pending copy covers
+    bool clock_record = false;           // the last plan's decode launches record
     // kernel timing: event pairs recorded around the attention kernel
     std::vector<hipEvent_t> prof_events;   // 2 per pair
     mutable int32_t prof_used = 0;
@@ -103,6 +115,15 @@ void release(pa_plan_t *p) {
     if (!p)
         return;
     drop_profile(p);
+    if (p->clock_done) {
+        if (p->clock_pending)
+            (void)hipEventSynchronize(p->clock_done);
+        (void)hipEventDestroy(p->clock_done);
+    }
+    if (p->h_xcd_clock)
+        (void)hipHostFree(p->h_xcd_clock);
+    if (p->d_xcd_clock)
+        (void)hipFree(p->d_xcd_clock);
     for (int i = 0; i < 2; i++) {
         if (p->stage_done[i]) {
             if (p->stage_pending[i])
@@ -124,6 +145,54 @@ void release(pa_plan_t *p) {
 }
 
 // Checks shared by the run entry points; fills the launch descriptor.
+// Bounds of the weights the feedback moves to, and the fraction of the way
+// from the current weights to the measured rates taken per update.
+constexpr float kFeedbackMinWeight = 0.5f, kFeedbackMaxWeight = 1.5f;
+constexpr double kFeedbackGain = 0.5;
+
+// Rescale weights to average 1 over the plan's XCDs.
+void normalise_weights(float *w, int n) {
+    double sum = 0.0;
+    for (int x = 0; x < n; x++)
+        sum += w[x];
+    for (int x = 0; x < n; x++)
+        w[x] = (float)(w[x] * n / sum);
+}
+
+// Turn the counters of the completed clock copy into new weights.  The
+// launches since the copy before it gave each workgroup of XCD x a budget
+// proportional to clock_weight[x] and took mean_x ticks per workgroup, so the
+// XCD's workgroups ran at clock_weight[x] / mean_x; an even finish gives each
+// XCD a share proportional to that rate.
+void update_xcd_weights(pa_plan_t *p) {
+    const int nx = p->num_xcd;
+    const uint64_t time_mask = (1ull << pa::kXcdClockCountShift) - 1;
+    double rate[pa::kMaxXcd];
+    bool complete = true;
+    for (int x = 0; x < nx; x++) {
+        const uint64_t now = p->h_xcd_clock[(size_t)x * pa::kXcdClockStride];
+        const uint64_t diff = now - p->clock_last[x];
+        p->clock_last[x] = now;
+        const uint64_t count = diff >> pa::kXcdClockCountShift, ticks = diff & time_mask;
+        if (count == 0 || ticks == 0) {
+            complete = false;
+            continue;
+        }
+        rate[x] = p->clock_weight[x] / ((double)ticks / (double)count);
+    }
+    if (!complete)
+        return;   // some XCD ran none of the recorded workgroups
+    double mean_rate = 0.0;
+    for (int x = 0; x < nx; x++)
+        mean_rate += rate[x] / nx;
+    for (int x = 0; x < nx; x++) {
+        const double target = rate[x] / mean_rate;
+        const double w = (1.0 - kFeedbackGain) * p->xcd_weight[x] + kFeedbackGain * target;
+        p->xcd_weight[x] = std::min(kFeedbackMaxWeight, std::max(kFeedbackMinWeight, (float)w));
+    }
+    normalise_weights(p->xcd_weight, nx);
+}
+
 pa_status prepare_run(const pa_plan_t *p, pa::PlanMode want, const void *q, const void *k_pool,
                       const void *v_pool, int64_t num_slots, int64_t slot_stride,
                       const int32_t *kv_indices, float sm_scale, float *out, float *lse,
@@ -184,6 +253,8 @@ pa_status prepare_run(const pa_plan_t *p, pa::PlanMode want, const void *q, cons
     l->num_qo_heads = p->num_qo_heads;
     l->num_kv_heads = p->num_kv_heads;
     l->head_dim = p->head_dim;
+    l->xcd_clock = (want == pa::PlanMode::kDecode && p->clock_record) ? p->d_xcd_clock : nullptr;
+    l->num_xcd = p->num_xcd;
     return PA_OK;
 }
 
@@ -214,6 +285,22 @@ pa_status pa_partition(const int32_t *kv_indptr_host, const int32_t *qo_indptr_h
                        int32_t unit_capacity, pa_merge_unit *merges, int32_t merge_capacity,
                        int32_t *n_workgroups, int32_t *n_units, int32_t *n_merges,
                        int32_t *n_partials) {
+    return pa_partition_weighted(kv_indptr_host, qo_indptr_host, batch, num_qo_heads, num_kv_heads,
+                                 head_dim, flags, max_workgroups, nullptr, 0, wg_offsets,
+                                 wg_capacity, units, unit_capacity, merges, merge_capacity,
+                                 n_workgroups, n_units, n_merges, n_partials);
+}
+
+pa_status pa_partition_weighted(const int32_t *kv_indptr_host, const int32_t *qo_indptr_host,
+                                int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,
+                                int32_t head_dim, uint32_t flags, int32_t max_workgroups,
+                                const float *xcd_weights, int32_t n_weights,
+                                int32_t *wg_offsets, int32_t wg_capacity, pa_work_unit *units,
+                                int32_t unit_capacity, pa_merge_unit *merges,
+                                int32_t merge_capacity, int32_t *n_workgroups, int32_t *n_units,
+                                int32_t *n_merges, int32_t *n_partials) {
+    if (xcd_weights && n_weights != pa::kNumXcd)
+        return fail(PA_ERR_INVALID_ARG, "n_weights must equal the XCD count (8)");
     if (!n_workgroups || !n_units || !n_merges || !n_partials)
         return fail(PA_ERR_INVALID_ARG, "count pointers must not be null");
     if ((wg_capacity > 0 && !wg_offsets) || (unit_capacity > 0 && !units) ||
@@ -223,7 +310,7 @@ pa_status pa_partition(const int32_t *kv_indptr_host, const int32_t *qo_indptr_h
     if (max_workgroups <= 0)
         max_workgroups = pa::kNumCu * pa::kDefaultWorkgroupsPerCu;
     pa::PartitionArgs a{kv_indptr_host, qo_indptr_host, batch, num_qo_heads, num_kv_heads,
-                        head_dim, flags, max_workgroups, pa::kNumXcd};
+                        head_dim, flags, max_workgroups, pa::kNumXcd, xcd_weights};
     pa::PartitionResult r;
     const char *detail = "";
     pa_status s = pa::partition(a, nullptr, wg_offsets, wg_capacity, units, unit_capacity, merges,
@@ -234,6 +321,33 @@ pa_status pa_partition(const int32_t *kv_indptr_host, const int32_t *qo_indptr_h
     *n_partials = r.n_partials;
     if (s != PA_OK)
         return fail(s, detail);
+    return PA_OK;
+}
+
+pa_status pa_plan_xcd_weights(const pa_plan_t *p, float *weights, int32_t capacity,
+                              int32_t *n_xcd) {
+    if (!p || !n_xcd || capacity < 0 || (capacity > 0 && !weights))
+        return fail(PA_ERR_INVALID_ARG, "null argument or negative capacity");
+    *n_xcd = p->num_xcd;
+    for (int32_t x = 0; x < std::min(capacity, p->num_xcd); x++)
+        weights[x] = p->xcd_weight[x];
+    return PA_OK;
+}
+
+pa_status pa_plan_set_xcd_weights(pa_plan_t *p, const float *weights, int32_t n) {
+    if (!p || !weights)
+        return fail(PA_ERR_INVALID_ARG, "null argument");
+    if (n != p->num_xcd)
+        return fail(PA_ERR_INVALID_ARG, "n must equal the plan's XCD count");
+    for (int32_t x = 0; x < n; x++)
+        if (!(weights[x] >= pa::kMinXcdWeight && weights[x] <= pa::kMaxXcdWeight))
+            return fail(PA_ERR_INVALID_ARG, "XCD weight not finite or outside [0.25, 4]");
+    float w[pa::kMaxXcd];
+    std::memcpy(w, weights, sizeof(float) * (size_t)n);
+    normalise_weights(w, n);
+    for (int32_t x = 0; x < n; x++)   // the rescaled set must still be accepted
+        w[x] = std::min(pa::kMaxXcdWeight, std::max(pa::kMinXcdWeight, w[x]));
+    std::memcpy(p->xcd_weight, w, sizeof(float) * (size_t)n);
     return PA_OK;
 }
 
@@ -254,6 +368,8 @@ pa_status pa_plan_create(pa_plan_t **out, int32_t max_batch, int64_t max_kv_tota
     pa_plan_t *p = new (std::nothrow) pa_plan_t;
     if (!p)
         return fail(PA_ERR_INVALID_ARG, "host allocation failed");
+    for (int x = 0; x < pa::kMaxXcd; x++)
+        p->xcd_weight[x] = p->clock_weight[x] = 1.0f;
     p->max_batch = max_batch;
     p->max_kv_total = max_kv_total;
     p->max_q_total = max_q_total;
@@ -281,15 +397,19 @@ pa_status pa_plan_create(pa_plan_t **out, int32_t max_batch, int64_t max_kv_tota
     const size_t part_o_bytes = (size_t)std::max<int64_t>(1, p->partial_rows_cap) * head_dim * sizeof(float);
     const size_t part_lse_bytes = (size_t)std::max<int64_t>(1, p->partial_rows_cap) * sizeof(float);
     const size_t arrivals_bytes = (size_t)std::max<int64_t>(1, p->merge_cap) * sizeof(int32_t);
+    const size_t clock_bytes = (size_t)p->num_xcd * pa::kXcdClockStride * sizeof(uint64_t);
     if ((e = hipMalloc(&p->d_table, tbytes)) != hipSuccess ||
         (e = hipMalloc((void **)&p->d_part_o, part_o_bytes)) != hipSuccess ||
         (e = hipMalloc((void **)&p->d_part_lse, part_lse_bytes)) != hipSuccess ||
-        (e = hipMalloc((void **)&p->d_arrivals, arrivals_bytes)) != hipSuccess) {
+        (e = hipMalloc((void **)&p->d_arrivals, arrivals_bytes)) != hipSuccess ||
+        (e = hipMalloc((void **)&p->d_xcd_clock, clock_bytes)) != hipSuccess) {
         release(p);
         return hip_fail(e, "hipMalloc (plan workspace)");
     }
-    // arrival counts start at zero; every launch leaves them at zero again
+    // arrival counts start at zero; every launch leaves them at zero again.
+    // The XCD clock counters only grow (readers take differences).
     if ((e = hipMemset(p->d_arrivals, 0, arrivals_bytes)) != hipSuccess ||
+        (e = hipMemset(p->d_xcd_clock, 0, clock_bytes)) != hipSuccess ||
         (e = hipDeviceSynchronize()) != hipSuccess) {
         release(p);
         return hip_fail(e, "clearing the arrival counts");
@@ -300,6 +420,11 @@ pa_status pa_plan_create(pa_plan_t **out, int32_t max_batch, int64_t max_kv_tota
             release(p);
             return hip_fail(e, "pinned staging / event");
         }
+    }
+    if ((e = hipHostMalloc((void **)&p->h_xcd_clock, clock_bytes, hipHostMallocDefault)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&p->clock_done, hipEventDisableTiming)) != hipSuccess) {
+        release(p);
+        return hip_fail(e, "pinned XCD clock copy / event");
     }
     *out = p;
     return PA_OK;
@@ -335,6 +460,26 @@ pa_status pa_plan(pa_plan_t *p, const int32_t *kv_indptr_host, const int32_t *qo
     if (dev != p->device)
         return fail(PA_ERR_INVALID_ARG, "current HIP device differs from the plan's device");
 
+    const bool auto_decode = !qo_indptr_host &&
+                             ((flags & PA_PLAN_FORCE_SPLITS_MASK) >> PA_PLAN_FORCE_SPLITS_SHIFT) == 0;
+    const bool feedback = (flags & PA_PLAN_XCD_FEEDBACK) && auto_decode;
+    // weights of the plans since the last clock copy (they change only here)
+    float interval_weight[pa::kMaxXcd];
+    std::memcpy(interval_weight, p->xcd_weight, sizeof interval_weight);
+    if (feedback && p->clock_pending) {
+        const hipError_t before = hipPeekAtLastError();
+        e = hipEventQuery(p->clock_done);
+        if (e == hipSuccess) {
+            p->clock_pending = false;
+            update_xcd_weights(p);
+        } else if (e == hipErrorNotReady) {
+            if (before == hipSuccess)
+                (void)hipGetLastError();  // not an error: the copy is still in flight
+        } else {
+            return hip_fail(e, "XCD clock copy");
+        }
+    }
+
     const int s = p->next_stage;
     const clock::time_point t_wait = clock::now();
     if (p->stage_pending[s]) {
@@ -351,7 +496,7 @@ pa_status pa_plan(pa_plan_t *p, const int32_t *kv_indptr_host, const int32_t *qo
     pa_work_unit *units = reinterpret_cast<pa_work_unit *>(stage + units_at);
     pa_merge_unit *merges = reinterpret_cast<pa_merge_unit *>(stage + units_at + (size_t)p->unit_cap * kUnit);
     pa::PartitionArgs a{kv_indptr_host, qo_indptr_host, batch, p->num_qo_heads, p->num_kv_heads,
-                        p->head_dim, flags, p->max_workgroups, p->num_xcd};
+                        p->head_dim, flags, p->max_workgroups, p->num_xcd, p->xcd_weight};
     pa::PartitionResult r;
     const char *detail = "";
     auto clamp32 = [](int64_t v) { return (int32_t)std::min<int64_t>(v, 0x7fffffff); };
@@ -376,6 +521,19 @@ pa_status pa_plan(pa_plan_t *p, const int32_t *kv_indptr_host, const int32_t *qo
         return hip_fail(e, "plan upload event");
     p->stage_pending[s] = true;
     p->next_stage = s ^ 1;
+    if (feedback && !p->clock_pending) {
+        // the counters as of the end of the launches enqueued so far: those
+        // since the previous copy all used interval_weight
+        if ((e = hipMemcpyAsync(p->h_xcd_clock, p->d_xcd_clock,
+                                (size_t)p->num_xcd * pa::kXcdClockStride * sizeof(uint64_t),
+                                hipMemcpyDeviceToHost, (hipStream_t)stream)) != hipSuccess ||
+            (e = hipEventRecord(p->clock_done, (hipStream_t)stream)) != hipSuccess)
+            return hip_fail(e, "XCD clock copy");
+        std::memcpy(p->clock_weight, interval_weight, sizeof interval_weight);
+        p->clock_pending = true;
+    }
+    // only launches that fill the GPU measure the XCDs' speeds
+    p->clock_record = feedback && r.n_workgroups >= p->max_workgroups;
     p->mode = qo_indptr_host ? pa::PlanMode::kPrefill : pa::PlanMode::kDecode;
     p->batch = batch;
     p->kv_total = kv_total;

@@ -10,7 +10,9 @@
 // as many workgroups as the GPU keeps resident at once (kernel occupancy x
 // compute units), so every workgroup starts at time zero and none waits for a
 // free slot; each gets an equal budget of list entries (plus a fixed cost per
-// piece of work it handles).  Segments are taken in (KV head, request) order:
+// piece of work it handles), scaled by its XCD's weight when the caller gives
+// per-XCD weights (XCDs of one GPU run at unequal speeds; see
+// PA_PLAN_XCD_FEEDBACK in pa.h).  Segments are taken in (KV head, request) order:
 // the first piece of segment i opens workgroup i, so requests that sit next to
 // each other in the batch -- those that share a prompt prefix under a radix
 // prefix cache (Agent-Infer page, section "前缀缓存") -- read their common
@@ -162,10 +164,22 @@ pa_status decode_bins(const PartitionArgs &a, PartitionScratch &ws, int32_t *wg_
     const int64_t max_wg = std::max(1, a.max_workgroups);
     const int64_t n = std::max<int64_t>(1, std::min(max_wg, ceil_div(total, min_unit_tokens(a.head_dim))));
     const double ov = kPieceOverheadTokens;
-    const double cap = ((double)total + ov * (double)(n_seg + n)) / (double)n;
+    const bool xcd = !(a.flags & PA_PLAN_NO_XCD_ORDER) && a.num_xcd > 1;
+    const int64_t per_xcd = xcd ? ceil_div(n, a.num_xcd) : n;
+    // Bin i runs on XCD i / per_xcd.  Its budget is base * (weight of that
+    // XCD); the budgets add up to the whole work.
+    double wsum = 0.0;
+    for (int64_t x = 0; x * per_xcd < n; x++) {
+        const double w = (xcd && a.xcd_weights) ? a.xcd_weights[x] : 1.0;
+        wsum += w * (double)(std::min(n, (x + 1) * per_xcd) - x * per_xcd);
+    }
+    const double base = ((double)total + ov * (double)(n_seg + n)) / wsum;
+    auto cap_of = [&](int64_t i) {
+        return (xcd && a.xcd_weights) ? base * a.xcd_weights[i / per_xcd] : base;
+    };
     // entries of the opening piece of segment s < n
     auto open_len = [&](int64_t s) {
-        return (int32_t)std::min<double>(seg_len(s), std::max(0.0, cap - ov));
+        return (int32_t)std::min<double>(seg_len(s), std::max(0.0, cap_of(s) - ov));
     };
 
     ws.seg_pieces.assign(n_seg, 0);
@@ -177,11 +191,14 @@ pa_status decode_bins(const PartitionArgs &a, PartitionScratch &ws, int32_t *wg_
     // pass 1: cut the stream over the bins
     int64_t p = 0;
     double fill = (0 < n_seg) ? open_len(0) + ov : 0.0;  // fill of bin p
+    double cap = cap_of(0);                               // its budget
     ws.bin_stream[0] = 0;
     auto advance = [&]() {
         p++;
         ws.bin_stream[p] = (int32_t)ws.stream.size();
         fill = (p < n_seg) ? open_len(p) + ov : 0.0;
+        if (p < n)
+            cap = cap_of(p);
     };
     for (int64_t s = 0; s < n_seg; s++) {
         const int32_t L = seg_len(s);
@@ -230,8 +247,6 @@ pa_status decode_bins(const PartitionArgs &a, PartitionScratch &ws, int32_t *wg_
             ws.seg_merge[s] = ws.seg_pieces[s] > 1 ? n_merges++ : -1;
         }
 
-    const bool xcd = !(a.flags & PA_PLAN_NO_XCD_ORDER) && a.num_xcd > 1;
-    const int64_t per_xcd = xcd ? ceil_div(n, a.num_xcd) : n;
     const int64_t n_wg = xcd ? per_xcd * a.num_xcd : n;
     const int64_t n_units = std::min<int64_t>(n, n_seg) + (int64_t)ws.stream.size();
     res->n_workgroups = (int32_t)n_wg;
@@ -346,8 +361,14 @@ pa_status partition(const PartitionArgs &a, PartitionScratch *scratch, int32_t *
     const int32_t forced = forced_splits(a.flags);
     if (forced > PA_MAX_FORCED_SPLITS)
         return fail(detail, "forced split count above PA_MAX_FORCED_SPLITS", PA_ERR_INVALID_ARG);
-    if ((a.flags & ~(PA_PLAN_FORCE_SPLITS_MASK | PA_PLAN_NO_XCD_ORDER)) != 0)
+    if ((a.flags & ~(PA_PLAN_FORCE_SPLITS_MASK | PA_PLAN_NO_XCD_ORDER | PA_PLAN_XCD_FEEDBACK)) != 0)
         return fail(detail, "unknown flag bits", PA_ERR_INVALID_ARG);
+    if (a.num_xcd < 1 || a.num_xcd > kMaxXcd)
+        return fail(detail, "XCD count out of range", PA_ERR_INVALID_ARG);
+    if (a.xcd_weights)
+        for (int32_t x = 0; x < a.num_xcd; x++)
+            if (!(a.xcd_weights[x] >= kMinXcdWeight && a.xcd_weights[x] <= kMaxXcdWeight))
+                return fail(detail, "XCD weight outside [0.25, 4]", PA_ERR_INVALID_ARG);
     if (a.batch > 0) {
         if (a.kv_indptr[0] != 0)
             return fail(detail, "kv_indptr[0] != 0", PA_ERR_INVALID_ARG);

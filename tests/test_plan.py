@@ -146,6 +146,68 @@ def test_batch64_partition_shape():
             assert len(xcds) == 1
 
 
+def _wg_costs(offs, units):
+    return np.array([(units["kv_end"][offs[w]:offs[w + 1]] - units["kv_begin"][offs[w]:offs[w + 1]]).sum()
+                     + 128 * (offs[w + 1] - offs[w]) for w in range(offs.size - 1)])
+
+
+def test_unit_weights_give_the_unweighted_partition():
+    ip, _ = W.decode_lists(W.BATCH64_SHARED_PREFIX)
+    a = pa.pa_partition(ip, None, 32, 8, 128)
+    b = pa.pa_partition(ip, None, 32, 8, 128, xcd_weights=np.ones(XCD))
+    assert all(np.array_equal(x, y) for x, y in zip(a[:3], b[:3])) and a[3] == b[3]
+    # the feedback flag is a pa_plan matter: the partition ignores it
+    c = pa.pa_partition(ip, None, 32, 8, 128, pa.PA_PLAN_XCD_FEEDBACK)
+    assert all(np.array_equal(x, y) for x, y in zip(a[:3], c[:3]))
+
+
+def test_weighted_partition_budgets():
+    """Workgroups on XCD x get weight_x times an equal share; every
+    partition invariant still holds."""
+    ip, _ = W.decode_lists(W.BATCH64_SHARED_PREFIX)
+    w = np.array([0.7, 1.3, 1.0, 1.1, 0.9, 1.25, 0.8, 0.95])
+    offs, units, merges, n_p = pa.pa_partition(ip, None, 32, 8, 128, 0, 768, xcd_weights=w)
+    check_offsets(offs, units)
+    check_decode(units, merges, n_p, ip, 8)
+    cost = _wg_costs(offs, units)
+    assert cost.size == 768
+    xcd_of = np.arange(cost.size) % XCD
+    per_xcd = np.array([cost[xcd_of == x].mean() for x in range(XCD)])
+    share = per_xcd / per_xcd.mean()
+    np.testing.assert_allclose(share, w / w.mean(), rtol=0.03)
+    base = cost.sum() / (w[xcd_of]).sum()
+    assert np.all(cost <= base * w[xcd_of] * 1.05 + 128)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_weighted_partition_random(seed):
+    rng = np.random.default_rng(100 + seed)
+    B = int(rng.integers(1, 70))
+    lengths = rng.integers(0, 6000, size=B)
+    lengths[rng.random(B) < 0.2] = 0
+    ip = _indptr(lengths)
+    w = rng.uniform(0.25, 4.0, size=XCD)
+    for flags in (0, pa.PA_PLAN_NO_XCD_ORDER, pa.PA_PLAN_FORCE_SPLITS(3)):
+        for max_wg in (0, 37, 768):
+            offs, units, merges, n_p = pa.pa_partition(ip, None, 32, 8, 128, flags, max_wg,
+                                                       xcd_weights=w)
+            check_offsets(offs, units)
+            check_decode(units, merges, n_p, ip, 8, forced=3 if flags & 0xFF00 else None)
+    # weights are ignored where the split is not the automatic XCD-ordered one
+    for flags in (pa.PA_PLAN_NO_XCD_ORDER, pa.PA_PLAN_FORCE_SPLITS(3)):
+        a = pa.pa_partition(ip, None, 32, 8, 128, flags, 768)
+        b = pa.pa_partition(ip, None, 32, 8, 128, flags, 768, xcd_weights=w)
+        assert all(np.array_equal(x, y) for x, y in zip(a[:3], b[:3]))
+
+
+@pytest.mark.parametrize("w", [[1.0] * 7, [1.0] * 9, [1.0] * 7 + [0.2], [1.0] * 7 + [4.5],
+                               [1.0] * 7 + [float("nan")], [1.0] * 7 + [float("inf")]])
+def test_bad_weights(w):
+    with pytest.raises(pa.PAError) as e:
+        pa.pa_partition(_indptr([100, 200]), None, 32, 8, 128, xcd_weights=w)
+    assert e.value.status == pa.PA_ERR_INVALID_ARG
+
+
 def test_decode_small_batch_uses_fewer_workgroups():
     """A small step does not spread below the minimum useful piece."""
     ip = _indptr([256])
