@@ -350,7 +350,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--flags", type=int, default=0x2,
-                    help="pa_plan flags (default PA_PLAN_XCD_FEEDBACK: per-XCD budgets from measured speed)")
+                    help="pa_plan flags (default PA_PLAN_SPEED_FEEDBACK: per-compute-unit budgets from measured speed)")
     ap.add_argument("--workload", default="batch64",
                     choices=["batch64", "single_request", "batch8", "hd256",
                              "prefill_chunk512", "prefill_chunk64", "append", "copy"])
@@ -465,9 +465,11 @@ def main():
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(end) / args.steps
     log(f"step {ms_per_step:.3f} ms ({ms_per_step * 1e3 / layers:.1f} us per layer)")
-    xcd_weights = [round(float(x), 3) for x in plan.xcd_weights()]
-    if args.flags & pa.PA_PLAN_XCD_FEEDBACK:
-        log(f"XCD weights after the timed steps: {xcd_weights}")
+    wgw = plan.workgroup_weights()
+    wg_weight_range = [round(float(wgw.min()), 3), round(float(wgw.max()), 3)]
+    if args.flags & pa.PA_PLAN_SPEED_FEEDBACK:
+        log(f"workgroup weights after the timed steps: min {wgw.min():.3f} max {wgw.max():.3f} "
+            f"std {wgw.std():.3f}")
 
     # the same K steps again with HIP events recorded by the library around
     # every decode kernel on the launch stream; the events themselves keep
@@ -533,7 +535,7 @@ def main():
             "unique_slots": int(np.unique(case.kv_indices).size),
             "pool_slots": spec.num_slots,
             "plan_flags": args.flags,
-            "xcd_weights": xcd_weights,
+            "workgroup_weight_range": wg_weight_range,
         },
         "us_per_step_layer": round(ms_per_step * 1e3 / layers, 2),
         "frac_of_peak": round(value / HBM_PEAK_GBS, 4),

@@ -98,19 +98,22 @@ typedef enum pa_status {
 /* Keep the automatic split but place workgroups in plain order instead of
  * grouping neighbouring requests on one XCD. */
 #define PA_PLAN_NO_XCD_ORDER 0x1u
-/* Balance the automatic decode partition over the XCDs by their measured
- * speed.  The decode launches of a plan computed with this flag record, per
- * XCD, how long its workgroups ran (one atomic add per workgroup).  A later
- * pa_plan call with the flag reads those records without waiting (each call
- * starts an asynchronous copy that a following call consumes once it has
- * completed) and moves each XCD's share of the next partition towards the
- * rate its workgroups achieved: the XCDs of one GPU run at unequal speeds
- * that change from run to run, and an equal split leaves the fast ones idle
- * while the slowest finishes.  Ignored for prefill and forced splits.  For a
- * fixed plan the results are deterministic; two steps with identical inputs
- * may be cut differently and so differ by rounding (within the usual
- * tolerance).  The weights in use are read with pa_plan_xcd_weights. */
-#define PA_PLAN_XCD_FEEDBACK 0x2u
+/* Balance the automatic decode partition by the measured speed of the
+ * compute units.  The decode launches of a plan computed with this flag (when
+ * they fill the GPU) record how long each workgroup ran (one atomic add per
+ * workgroup).  A later pa_plan call with the flag reads those records without
+ * waiting (each call starts an asynchronous copy that a following call
+ * consumes once it has completed) and moves each compute unit's share of the
+ * next partition towards the rate it achieved.  A launch that fills the GPU
+ * places workgroup ids w, w + C, w + 2C, ... on one compute unit (C = compute
+ * units), every launch alike, and the units of one GPU do not run at equal
+ * speeds (which are slow changes from run to run, and between XCDs), so an
+ * equal split leaves the fast ones idle while the slowest finish.  Ignored for
+ * prefill and forced splits.  For a fixed plan the results are deterministic;
+ * two steps with identical inputs may be cut differently and so differ by
+ * rounding (within the usual tolerance).  The weights in use are read with
+ * pa_plan_workgroup_weights. */
+#define PA_PLAN_SPEED_FEEDBACK 0x2u
 
 /* Largest max_kv_total a plan accepts: list entries are addressed with 32-bit
  * byte offsets. */
@@ -297,17 +300,20 @@ pa_status pa_partition(const int32_t *kv_indptr_host, const int32_t *qo_indptr_h
                        int32_t *n_partials);
 
 /*
- * pa_partition_weighted: pa_partition with per-XCD work weights: in the
- * automatic decode split the workgroups placed on XCD x (workgroup id w runs
- * on XCD w % 8) get xcd_weights[x] times the budget of an equal split.
- * n_weights must be 8 (the XCDs of an MI355X) and every weight in
- * [0.25, 4]; they need not average 1 (the budgets are rescaled to the work).
- * xcd_weights = NULL is pa_partition.  Other modes ignore the weights.
+ * pa_partition_weighted: pa_partition with work weights for the automatic
+ * decode split: the workgroup that bin i runs as (id w, on XCD w % 8) gets
+ * xcd_weights[w % 8] * wg_weights[w] times the budget of an equal split
+ * (ids at or beyond n_wg_weights weigh 1).  n_xcd_weights must be 8 (the XCDs
+ * of an MI355X); every weight must be in [0.25, 4]; they need not average 1
+ * (the budgets are rescaled to the work).  NULL weights weigh 1; both NULL is
+ * pa_partition.  XCD weights apply only to the XCD-ordered placement; other
+ * modes (prefill, forced splits) ignore all weights.
  */
 pa_status pa_partition_weighted(const int32_t *kv_indptr_host, const int32_t *qo_indptr_host,
                                 int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,
                                 int32_t head_dim, uint32_t flags, int32_t max_workgroups,
-                                const float *xcd_weights, int32_t n_weights,
+                                const float *xcd_weights, int32_t n_xcd_weights,
+                                const float *wg_weights, int32_t n_wg_weights,
                                 int32_t *wg_offsets, int32_t wg_capacity, pa_work_unit *units,
                                 int32_t unit_capacity, pa_merge_unit *merges,
                                 int32_t merge_capacity, int32_t *n_workgroups, int32_t *n_units,
@@ -319,7 +325,7 @@ pa_status pa_partition_weighted(const int32_t *kv_indptr_host, const int32_t *qo
  * split; they average 1).  *n_xcd receives the XCD count and
  * min(capacity, *n_xcd) weights are written to `weights` (which may be NULL
  * when capacity is 0).  They start at 1 and change only through
- * pa_plan_set_xcd_weights or the measurements of PA_PLAN_XCD_FEEDBACK.
+ * pa_plan_set_xcd_weights.
  *
  * pa_plan_set_xcd_weights: set them.  n must equal the XCD count and every
  * weight be finite and in [0.25, 4]; they are rescaled to average 1.  Used by
@@ -328,6 +334,16 @@ pa_status pa_partition_weighted(const int32_t *kv_indptr_host, const int32_t *qo
 pa_status pa_plan_xcd_weights(const pa_plan_t *plan, float *weights, int32_t capacity,
                               int32_t *n_xcd);
 pa_status pa_plan_set_xcd_weights(pa_plan_t *plan, const float *weights, int32_t n);
+
+/*
+ * pa_plan_workgroup_weights: the per-workgroup-id weights that
+ * PA_PLAN_SPEED_FEEDBACK has measured (1 until it has; id w weighs what its
+ * compute unit w % C does; they multiply the XCD weights and average 1 over
+ * the units that recorded).  *n receives their number and min(capacity, *n)
+ * are written to `weights` (which may be NULL when capacity is 0).
+ */
+pa_status pa_plan_workgroup_weights(const pa_plan_t *plan, float *weights, int32_t capacity,
+                                    int32_t *n);
 
 /*
  * Kernel timing (instrumentation for benchmarks).  pa_profile_begin creates

@@ -32,7 +32,7 @@ PA_PLAN_FORCE_SPLITS_SHIFT = 8
 PA_MAX_FORCED_SPLITS = 256
 PA_MAX_KV_TOTAL = 1 << 29
 PA_PLAN_NO_XCD_ORDER = 0x1
-PA_PLAN_XCD_FEEDBACK = 0x2
+PA_PLAN_SPEED_FEEDBACK = 0x2
 PA_NUM_XCD = 8
 
 
@@ -93,7 +93,7 @@ def _load() -> ctypes.CDLL:
     lib.pa_partition.restype = ctypes.c_int
     f32p = ctypes.POINTER(ctypes.c_float)
     lib.pa_partition_weighted.argtypes = [i32p, i32p, i32, i32, i32, i32, u32, i32, f32p, i32,
-                                          i32p, i32, ctypes.POINTER(pa_work_unit), i32,
+                                          f32p, i32, i32p, i32, ctypes.POINTER(pa_work_unit), i32,
                                           ctypes.POINTER(pa_merge_unit), i32, i32p, i32p, i32p,
                                           i32p]
     lib.pa_partition_weighted.restype = ctypes.c_int
@@ -101,6 +101,8 @@ def _load() -> ctypes.CDLL:
     lib.pa_plan_xcd_weights.restype = ctypes.c_int
     lib.pa_plan_set_xcd_weights.argtypes = [vp, f32p, i32]
     lib.pa_plan_set_xcd_weights.restype = ctypes.c_int
+    lib.pa_plan_workgroup_weights.argtypes = [vp, f32p, i32, i32p]
+    lib.pa_plan_workgroup_weights.restype = ctypes.c_int
     lib.pa_profile_begin.argtypes = [vp, i32]
     lib.pa_profile_begin.restype = ctypes.c_int
     lib.pa_profile_end.argtypes = [vp, ctypes.POINTER(ctypes.c_double), i32p]
@@ -288,33 +290,35 @@ def pa_plan_destroy(plan) -> None:
 
 
 def pa_partition(kv_indptr, qo_indptr, num_qo_heads: int, num_kv_heads: int, head_dim: int,
-                 flags: int = 0, max_workgroups: int = 0, xcd_weights=None):
-    """Host-only: the partition pa_plan would upload (pa_partition, or
-    pa_partition_weighted when xcd_weights holds one weight per XCD).
+                 flags: int = 0, max_workgroups: int = 0, xcd_weights=None, wg_weights=None):
+    """Host-only: the partition pa_plan would upload (pa_partition_weighted:
+    xcd_weights one weight per XCD, wg_weights one per workgroup id).
 
     Returns (wg_offsets int32 [n_workgroups + 1], units, merges, n_partials);
     workgroup w runs units[wg_offsets[w]:wg_offsets[w + 1]].
     """
     kv = _host_i32(kv_indptr)
     qo = _host_i32(qo_indptr)
-    if xcd_weights is None:
-        wp, nw = None, 0
-    else:
-        w = np.ascontiguousarray(np.asarray(xcd_weights, dtype=np.float32))
-        wp, nw = w.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), int(w.size)
+    def _f32(a):
+        if a is None:
+            return None, 0, None
+        arr = np.ascontiguousarray(np.asarray(a, dtype=np.float32))
+        return arr.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), int(arr.size), arr
+    wp, nw, _keep_x = _f32(xcd_weights)
+    gp, ng, _keep_g = _f32(wg_weights)
     n_w, n_u, n_m, n_p = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
     counts = (ctypes.byref(n_w), ctypes.byref(n_u), ctypes.byref(n_m), ctypes.byref(n_p))
     st = _lib.pa_partition_weighted(_i32p(kv), _i32p(qo), kv.size - 1, num_qo_heads, num_kv_heads,
-                                    head_dim, flags, max_workgroups, wp, nw, None, 0, None, 0,
-                                    None, 0, *counts)
+                                    head_dim, flags, max_workgroups, wp, nw, gp, ng, None, 0,
+                                    None, 0, None, 0, *counts)
     if st not in (PA_OK, PA_ERR_CAPACITY):
         _check(st, "pa_partition")
     offs = np.zeros(n_w.value + 1, np.int32)
     units = (pa_work_unit * max(1, n_u.value))()
     merges = (pa_merge_unit * max(1, n_m.value))()
     _check(_lib.pa_partition_weighted(_i32p(kv), _i32p(qo), kv.size - 1, num_qo_heads,
-                                      num_kv_heads, head_dim, flags, max_workgroups, wp, nw,
-                                      _i32p(offs), offs.size, units, n_u.value, merges,
+                                      num_kv_heads, head_dim, flags, max_workgroups, wp, nw, gp,
+                                      ng, _i32p(offs), offs.size, units, n_u.value, merges,
                                       n_m.value, *counts), "pa_partition")
     u = np.frombuffer(bytes(units), dtype=WORK_UNIT_DTYPE)[: n_u.value].copy()
     m = np.frombuffer(bytes(merges), dtype=MERGE_UNIT_DTYPE)[: n_m.value].copy()
@@ -328,6 +332,18 @@ def pa_plan_xcd_weights(plan) -> np.ndarray:
     w = np.zeros(n.value, np.float32)
     _check(_lib.pa_plan_xcd_weights(plan, w.ctypes.data_as(ctypes.POINTER(ctypes.c_float)),
                                     w.size, ctypes.byref(n)), "pa_plan_xcd_weights")
+    return w
+
+
+def pa_plan_workgroup_weights(plan) -> np.ndarray:
+    """The per-workgroup-id weights measured by PA_PLAN_SPEED_FEEDBACK (id w
+    weighs what its compute unit w % C does)."""
+    n = ctypes.c_int32()
+    _check(_lib.pa_plan_workgroup_weights(plan, None, 0, ctypes.byref(n)),
+           "pa_plan_workgroup_weights")
+    w = np.zeros(n.value, np.float32)
+    _check(_lib.pa_plan_workgroup_weights(plan, w.ctypes.data_as(ctypes.POINTER(ctypes.c_float)),
+                                          w.size, ctypes.byref(n)), "pa_plan_workgroup_weights")
     return w
 
 
@@ -374,6 +390,9 @@ class Plan:
 
     def set_xcd_weights(self, weights) -> None:
         pa_plan_set_xcd_weights(self.handle, weights)
+
+    def workgroup_weights(self) -> np.ndarray:
+        return pa_plan_workgroup_weights(self.handle)
 
     def decode(self, q, k_pool, v_pool, kv_indices, sm_scale, out, lse=None, **kw) -> None:
         pa_decode_run(self.handle, q, k_pool, v_pool, kv_indices, sm_scale, out, lse, **kw)

@@ -8,6 +8,7 @@
 // "优化历程".
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <chrono>
 #include <cmath>
 #include <cstdio>
@@ -45,17 +46,23 @@ struct pa_plan {
     int32_t n_workgroups = 0, n_units = 0, n_merges = 0, n_partials = 0;
     pa::PartitionScratch scratch;  // host working arrays of the partition
     double plan_total_us = 0.0, plan_wait_us = 0.0;  // host time of the last pa_plan
-    // per-XCD work weights of the automatic decode split, and their feedback
-    // (PA_PLAN_XCD_FEEDBACK): the decode kernel adds each workgroup's run
-    // time to d_xcd_clock; pa_plan copies the counters to h_xcd_clock and a
-    // later call turns the difference of two copies into new weights
+    // work weights of the automatic decode split: per XCD (set by the
+    // caller) and per workgroup id (PA_PLAN_SPEED_FEEDBACK).  With the
+    // feedback the decode kernel adds each workgroup's run time to
+    // d_wg_clock; pa_plan copies the counters to h_wg_clock and a later call
+    // turns the difference of two copies into new workgroup weights
     float xcd_weight[pa::kMaxXcd];
-    uint64_t *d_xcd_clock = nullptr;     // device, one 256-byte line per XCD
-    uint64_t *h_xcd_clock = nullptr;     // pinned copy of those lines
+    int32_t n_clock = 0;                 // workgroup ids with a counter
+    std::vector<float> wg_weight;        // n_clock entries, from cu_weight
+    std::vector<float> cu_weight;        // num_cu entries
+    std::vector<double> cu_busy;         // update_cu_weights' working array
+    uint64_t *d_wg_clock = nullptr;      // device, n_clock counters, kClockStride apart
+    uint64_t *h_wg_clock = nullptr;      // pinned copy
     hipEvent_t clock_done = nullptr;
     bool clock_pending = false;          // a copy is in flight or unread
-    uint64_t clock_last[pa::kMaxXcd] = {};       // the copy read last
-    float clock_weight[pa::kMaxXcd];     // weights of the launches the pending copy covers
+    std::vector<uint64_t> clock_last;    // the counters of the copy read last
+    std::vector<float> clock_weight;     // unit weights of the launches the pending copy covers
+    std::vector<float> interval_weight;  // pa_plan's copy of the unit weights before it updates them
     bool clock_record = false;           // the last plan's decode launches record
     // kernel timing: event pairs recorded around the attention kernel
     std::vector<hipEvent_t> prof_events;   // 2 per pair
@@ -120,10 +127,10 @@ void release(pa_plan_t *p) {
             (void)hipEventSynchronize(p->clock_done);
         (void)hipEventDestroy(p->clock_done);
     }
-    if (p->h_xcd_clock)
-        (void)hipHostFree(p->h_xcd_clock);
-    if (p->d_xcd_clock)
-        (void)hipFree(p->d_xcd_clock);
+    if (p->h_wg_clock)
+        (void)hipHostFree(p->h_wg_clock);
+    if (p->d_wg_clock)
+        (void)hipFree(p->d_wg_clock);
     for (int i = 0; i < 2; i++) {
         if (p->stage_done[i]) {
             if (p->stage_pending[i])
@@ -150,7 +157,7 @@ void release(pa_plan_t *p) {
 constexpr float kFeedbackMinWeight = 0.5f, kFeedbackMaxWeight = 1.5f;
 constexpr double kFeedbackGain = 0.5;
 
-// Rescale weights to average 1 over the plan's XCDs.
+// Rescale weights to average 1.
 void normalise_weights(float *w, int n) {
     double sum = 0.0;
     for (int x = 0; x < n; x++)
@@ -159,38 +166,52 @@ void normalise_weights(float *w, int n) {
         w[x] = (float)(w[x] * n / sum);
 }
 
-// Turn the counters of the completed clock copy into new weights.  The
-// launches since the copy before it gave each workgroup of XCD x a budget
-// proportional to clock_weight[x] and took mean_x ticks per workgroup, so the
-// XCD's workgroups ran at clock_weight[x] / mean_x; an even finish gives each
-// XCD a share proportional to that rate.
-void update_xcd_weights(pa_plan_t *p) {
-    const int nx = p->num_xcd;
-    const uint64_t time_mask = (1ull << pa::kXcdClockCountShift) - 1;
-    double rate[pa::kMaxXcd];
-    bool complete = true;
-    for (int x = 0; x < nx; x++) {
-        const uint64_t now = p->h_xcd_clock[(size_t)x * pa::kXcdClockStride];
-        const uint64_t diff = now - p->clock_last[x];
-        p->clock_last[x] = now;
-        const uint64_t count = diff >> pa::kXcdClockCountShift, ticks = diff & time_mask;
-        if (count == 0 || ticks == 0) {
-            complete = false;
-            continue;
+// Turn the counters of the completed clock copy into new weights.  A launch
+// that fills the GPU places workgroup ids w, w + C, w + 2C, ... (C = compute
+// units) on one compute unit, and the unit is done when the last of them is,
+// so the weights are kept per unit: the launches since the copy before it
+// gave unit c a budget proportional to clock_weight[c] and it was busy for
+// busy_c = the largest mean run time of its workgroups, so it ran at
+// clock_weight[c] / busy_c; an even finish gives each unit a share
+// proportional to that rate.  Units whose workgroups recorded nothing keep
+// their weights.  Workgroup id w then weighs cu_weight[w % C].
+void update_cu_weights(pa_plan_t *p) {
+    const uint64_t time_mask = (1ull << pa::kClockCountShift) - 1;
+    const int32_t C = p->num_cu;
+    std::vector<double> &busy = p->cu_busy;
+    std::fill(busy.begin(), busy.end(), 0.0);
+    for (int32_t w = 0; w < p->n_clock; w++) {
+        const uint64_t now = p->h_wg_clock[(size_t)w * pa::kClockStride];
+        const uint64_t diff = now - p->clock_last[w];
+        p->clock_last[w] = now;
+        const uint64_t count = diff >> pa::kClockCountShift, ticks = diff & time_mask;
+        if (count > 0)
+            busy[w % C] = std::max(busy[w % C], (double)ticks / (double)count);
+    }
+    double sum = 0.0;
+    int active = 0;
+    for (int32_t c = 0; c < C; c++)
+        if (busy[c] > 0.0) {
+            busy[c] = p->clock_weight[c] / busy[c];   // now the unit's rate
+            sum += busy[c];
+            active++;
         }
-        rate[x] = p->clock_weight[x] / ((double)ticks / (double)count);
+    if (active == 0)
+        return;
+    const double mean_rate = sum / active;
+    double wsum = 0.0;
+    for (int32_t c = 0; c < C; c++) {
+        if (busy[c] == 0.0)
+            continue;
+        const double v = (1.0 - kFeedbackGain) * p->cu_weight[c] + kFeedbackGain * busy[c] / mean_rate;
+        p->cu_weight[c] = std::min(kFeedbackMaxWeight, std::max(kFeedbackMinWeight, (float)v));
+        wsum += p->cu_weight[c];
     }
-    if (!complete)
-        return;   // some XCD ran none of the recorded workgroups
-    double mean_rate = 0.0;
-    for (int x = 0; x < nx; x++)
-        mean_rate += rate[x] / nx;
-    for (int x = 0; x < nx; x++) {
-        const double target = rate[x] / mean_rate;
-        const double w = (1.0 - kFeedbackGain) * p->xcd_weight[x] + kFeedbackGain * target;
-        p->xcd_weight[x] = std::min(kFeedbackMaxWeight, std::max(kFeedbackMinWeight, (float)w));
-    }
-    normalise_weights(p->xcd_weight, nx);
+    for (int32_t c = 0; c < C; c++)   // mean 1 over the units that ran
+        if (busy[c] != 0.0)
+            p->cu_weight[c] = (float)(p->cu_weight[c] * active / wsum);
+    for (int32_t w = 0; w < p->n_clock; w++)
+        p->wg_weight[w] = p->cu_weight[w % C];
 }
 
 pa_status prepare_run(const pa_plan_t *p, pa::PlanMode want, const void *q, const void *k_pool,
@@ -253,8 +274,7 @@ pa_status prepare_run(const pa_plan_t *p, pa::PlanMode want, const void *q, cons
     l->num_qo_heads = p->num_qo_heads;
     l->num_kv_heads = p->num_kv_heads;
     l->head_dim = p->head_dim;
-    l->xcd_clock = (want == pa::PlanMode::kDecode && p->clock_record) ? p->d_xcd_clock : nullptr;
-    l->num_xcd = p->num_xcd;
+    l->wg_clock = (want == pa::PlanMode::kDecode && p->clock_record) ? p->d_wg_clock : nullptr;
     return PA_OK;
 }
 
@@ -286,7 +306,7 @@ pa_status pa_partition(const int32_t *kv_indptr_host, const int32_t *qo_indptr_h
                        int32_t *n_workgroups, int32_t *n_units, int32_t *n_merges,
                        int32_t *n_partials) {
     return pa_partition_weighted(kv_indptr_host, qo_indptr_host, batch, num_qo_heads, num_kv_heads,
-                                 head_dim, flags, max_workgroups, nullptr, 0, wg_offsets,
+                                 head_dim, flags, max_workgroups, nullptr, 0, nullptr, 0, wg_offsets,
                                  wg_capacity, units, unit_capacity, merges, merge_capacity,
                                  n_workgroups, n_units, n_merges, n_partials);
 }
@@ -294,13 +314,16 @@ pa_status pa_partition(const int32_t *kv_indptr_host, const int32_t *qo_indptr_h
 pa_status pa_partition_weighted(const int32_t *kv_indptr_host, const int32_t *qo_indptr_host,
                                 int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,
                                 int32_t head_dim, uint32_t flags, int32_t max_workgroups,
-                                const float *xcd_weights, int32_t n_weights,
+                                const float *xcd_weights, int32_t n_xcd_weights,
+                                const float *wg_weights, int32_t n_wg_weights,
                                 int32_t *wg_offsets, int32_t wg_capacity, pa_work_unit *units,
                                 int32_t unit_capacity, pa_merge_unit *merges,
                                 int32_t merge_capacity, int32_t *n_workgroups, int32_t *n_units,
                                 int32_t *n_merges, int32_t *n_partials) {
-    if (xcd_weights && n_weights != pa::kNumXcd)
-        return fail(PA_ERR_INVALID_ARG, "n_weights must equal the XCD count (8)");
+    if (xcd_weights && n_xcd_weights != pa::kNumXcd)
+        return fail(PA_ERR_INVALID_ARG, "n_xcd_weights must equal the XCD count (8)");
+    if (n_wg_weights < 0 || (n_wg_weights > 0 && !wg_weights))
+        return fail(PA_ERR_INVALID_ARG, "bad workgroup weights");
     if (!n_workgroups || !n_units || !n_merges || !n_partials)
         return fail(PA_ERR_INVALID_ARG, "count pointers must not be null");
     if ((wg_capacity > 0 && !wg_offsets) || (unit_capacity > 0 && !units) ||
@@ -310,7 +333,8 @@ pa_status pa_partition_weighted(const int32_t *kv_indptr_host, const int32_t *qo
     if (max_workgroups <= 0)
         max_workgroups = pa::kNumCu * pa::kDefaultWorkgroupsPerCu;
     pa::PartitionArgs a{kv_indptr_host, qo_indptr_host, batch, num_qo_heads, num_kv_heads,
-                        head_dim, flags, max_workgroups, pa::kNumXcd, xcd_weights};
+                        head_dim, flags, max_workgroups, pa::kNumXcd, xcd_weights,
+                        n_wg_weights > 0 ? wg_weights : nullptr, n_wg_weights};
     pa::PartitionResult r;
     const char *detail = "";
     pa_status s = pa::partition(a, nullptr, wg_offsets, wg_capacity, units, unit_capacity, merges,
@@ -331,6 +355,16 @@ pa_status pa_plan_xcd_weights(const pa_plan_t *p, float *weights, int32_t capaci
     *n_xcd = p->num_xcd;
     for (int32_t x = 0; x < std::min(capacity, p->num_xcd); x++)
         weights[x] = p->xcd_weight[x];
+    return PA_OK;
+}
+
+pa_status pa_plan_workgroup_weights(const pa_plan_t *p, float *weights, int32_t capacity,
+                                    int32_t *n) {
+    if (!p || !n || capacity < 0 || (capacity > 0 && !weights))
+        return fail(PA_ERR_INVALID_ARG, "null argument or negative capacity");
+    *n = p->n_clock;
+    for (int32_t w = 0; w < std::min(capacity, p->n_clock); w++)
+        weights[w] = p->wg_weight[w];
     return PA_OK;
 }
 
@@ -369,7 +403,7 @@ pa_status pa_plan_create(pa_plan_t **out, int32_t max_batch, int64_t max_kv_tota
     if (!p)
         return fail(PA_ERR_INVALID_ARG, "host allocation failed");
     for (int x = 0; x < pa::kMaxXcd; x++)
-        p->xcd_weight[x] = p->clock_weight[x] = 1.0f;
+        p->xcd_weight[x] = 1.0f;
     p->max_batch = max_batch;
     p->max_kv_total = max_kv_total;
     p->max_q_total = max_q_total;
@@ -397,19 +431,31 @@ pa_status pa_plan_create(pa_plan_t **out, int32_t max_batch, int64_t max_kv_tota
     const size_t part_o_bytes = (size_t)std::max<int64_t>(1, p->partial_rows_cap) * head_dim * sizeof(float);
     const size_t part_lse_bytes = (size_t)std::max<int64_t>(1, p->partial_rows_cap) * sizeof(float);
     const size_t arrivals_bytes = (size_t)std::max<int64_t>(1, p->merge_cap) * sizeof(int32_t);
-    const size_t clock_bytes = (size_t)p->num_xcd * pa::kXcdClockStride * sizeof(uint64_t);
+    p->n_clock = p->max_workgroups + pa::kMaxXcd;   // ids of the automatic decode split
+    try {
+        p->wg_weight.assign((size_t)p->n_clock, 1.0f);
+        p->cu_weight.assign((size_t)p->num_cu, 1.0f);
+        p->cu_busy.assign((size_t)p->num_cu, 0.0);
+        p->clock_weight.assign((size_t)p->num_cu, 1.0f);
+        p->interval_weight.assign((size_t)p->num_cu, 1.0f);
+        p->clock_last.assign((size_t)p->n_clock, 0);
+    } catch (...) {
+        release(p);
+        return fail(PA_ERR_INVALID_ARG, "host allocation failed");
+    }
+    const size_t clock_bytes = (size_t)p->n_clock * pa::kClockStride * sizeof(uint64_t);
     if ((e = hipMalloc(&p->d_table, tbytes)) != hipSuccess ||
         (e = hipMalloc((void **)&p->d_part_o, part_o_bytes)) != hipSuccess ||
         (e = hipMalloc((void **)&p->d_part_lse, part_lse_bytes)) != hipSuccess ||
         (e = hipMalloc((void **)&p->d_arrivals, arrivals_bytes)) != hipSuccess ||
-        (e = hipMalloc((void **)&p->d_xcd_clock, clock_bytes)) != hipSuccess) {
+        (e = hipMalloc((void **)&p->d_wg_clock, clock_bytes)) != hipSuccess) {
         release(p);
         return hip_fail(e, "hipMalloc (plan workspace)");
     }
     // arrival counts start at zero; every launch leaves them at zero again.
-    // The XCD clock counters only grow (readers take differences).
+    // The clock counters only grow (readers take differences).
     if ((e = hipMemset(p->d_arrivals, 0, arrivals_bytes)) != hipSuccess ||
-        (e = hipMemset(p->d_xcd_clock, 0, clock_bytes)) != hipSuccess ||
+        (e = hipMemset(p->d_wg_clock, 0, clock_bytes)) != hipSuccess ||
         (e = hipDeviceSynchronize()) != hipSuccess) {
         release(p);
         return hip_fail(e, "clearing the arrival counts");
@@ -421,10 +467,10 @@ pa_status pa_plan_create(pa_plan_t **out, int32_t max_batch, int64_t max_kv_tota
             return hip_fail(e, "pinned staging / event");
         }
     }
-    if ((e = hipHostMalloc((void **)&p->h_xcd_clock, clock_bytes, hipHostMallocDefault)) != hipSuccess ||
+    if ((e = hipHostMalloc((void **)&p->h_wg_clock, clock_bytes, hipHostMallocDefault)) != hipSuccess ||
         (e = hipEventCreateWithFlags(&p->clock_done, hipEventDisableTiming)) != hipSuccess) {
         release(p);
-        return hip_fail(e, "pinned XCD clock copy / event");
+        return hip_fail(e, "pinned clock copy / event");
     }
     *out = p;
     return PA_OK;
@@ -462,21 +508,23 @@ pa_status pa_plan(pa_plan_t *p, const int32_t *kv_indptr_host, const int32_t *qo
 
     const bool auto_decode = !qo_indptr_host &&
                              ((flags & PA_PLAN_FORCE_SPLITS_MASK) >> PA_PLAN_FORCE_SPLITS_SHIFT) == 0;
-    const bool feedback = (flags & PA_PLAN_XCD_FEEDBACK) && auto_decode;
-    // weights of the plans since the last clock copy (they change only here)
-    float interval_weight[pa::kMaxXcd];
-    std::memcpy(interval_weight, p->xcd_weight, sizeof interval_weight);
+    const bool feedback = (flags & PA_PLAN_SPEED_FEEDBACK) && auto_decode;
+    // the weights of the plans since the last clock copy (they change only
+    // below, when a copy is read, and a copy is started only when none is
+    // pending)
+    if (feedback)
+        std::copy(p->cu_weight.begin(), p->cu_weight.end(), p->interval_weight.begin());
     if (feedback && p->clock_pending) {
         const hipError_t before = hipPeekAtLastError();
         e = hipEventQuery(p->clock_done);
         if (e == hipSuccess) {
             p->clock_pending = false;
-            update_xcd_weights(p);
+            update_cu_weights(p);
         } else if (e == hipErrorNotReady) {
             if (before == hipSuccess)
                 (void)hipGetLastError();  // not an error: the copy is still in flight
         } else {
-            return hip_fail(e, "XCD clock copy");
+            return hip_fail(e, "clock copy");
         }
     }
 
@@ -496,7 +544,8 @@ pa_status pa_plan(pa_plan_t *p, const int32_t *kv_indptr_host, const int32_t *qo
     pa_work_unit *units = reinterpret_cast<pa_work_unit *>(stage + units_at);
     pa_merge_unit *merges = reinterpret_cast<pa_merge_unit *>(stage + units_at + (size_t)p->unit_cap * kUnit);
     pa::PartitionArgs a{kv_indptr_host, qo_indptr_host, batch, p->num_qo_heads, p->num_kv_heads,
-                        p->head_dim, flags, p->max_workgroups, p->num_xcd, p->xcd_weight};
+                        p->head_dim, flags, p->max_workgroups, p->num_xcd, p->xcd_weight,
+                        p->wg_weight.data(), p->n_clock};
     pa::PartitionResult r;
     const char *detail = "";
     auto clamp32 = [](int64_t v) { return (int32_t)std::min<int64_t>(v, 0x7fffffff); };
@@ -524,16 +573,17 @@ pa_status pa_plan(pa_plan_t *p, const int32_t *kv_indptr_host, const int32_t *qo
     if (feedback && !p->clock_pending) {
         // the counters as of the end of the launches enqueued so far: those
         // since the previous copy all used interval_weight
-        if ((e = hipMemcpyAsync(p->h_xcd_clock, p->d_xcd_clock,
-                                (size_t)p->num_xcd * pa::kXcdClockStride * sizeof(uint64_t),
+        if ((e = hipMemcpyAsync(p->h_wg_clock, p->d_wg_clock,
+                                (size_t)p->n_clock * pa::kClockStride * sizeof(uint64_t),
                                 hipMemcpyDeviceToHost, (hipStream_t)stream)) != hipSuccess ||
             (e = hipEventRecord(p->clock_done, (hipStream_t)stream)) != hipSuccess)
-            return hip_fail(e, "XCD clock copy");
-        std::memcpy(p->clock_weight, interval_weight, sizeof interval_weight);
+            return hip_fail(e, "clock copy");
+        std::copy(p->interval_weight.begin(), p->interval_weight.end(), p->clock_weight.begin());
         p->clock_pending = true;
     }
-    // only launches that fill the GPU measure the XCDs' speeds
-    p->clock_record = feedback && r.n_workgroups >= p->max_workgroups;
+    // only launches that fill the GPU measure the workgroups' speeds
+    p->clock_record = feedback && r.n_workgroups >= p->max_workgroups &&
+                      r.n_workgroups <= p->n_clock;
     p->mode = qo_indptr_host ? pa::PlanMode::kPrefill : pa::PlanMode::kDecode;
     p->batch = batch;
     p->kv_total = kv_total;

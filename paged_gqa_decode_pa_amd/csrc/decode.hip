@@ -407,7 +407,7 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<G>(), 8))) void decode_
     const char *__restrict__ v_pool, uint32_t stride_bytes,
     const int32_t *__restrict__ kv_indices, float scale_log2, float out_scale, float *__restrict__ out,
     float *__restrict__ lse, float *__restrict__ part_o, float *__restrict__ part_lse,
-    int32_t num_qo_heads, uint64_t *__restrict__ xcd_clock, int32_t num_xcd) {
+    int32_t num_qo_heads, uint64_t *__restrict__ wg_clock) {
     using Geo = Geometry<D>;
     using PR = PoolRow<KV8>;
     using Row = typename PR::T;
@@ -420,7 +420,7 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<G>(), 8))) void decode_
     __shared__ int32_t lds_arrived;
 
     // start of the workgroup's run on the 100 MHz real-time counter
-    const uint64_t t_begin = xcd_clock ? __builtin_amdgcn_s_memrealtime() : 0;
+    const uint64_t t_begin = wg_clock ? __builtin_amdgcn_s_memrealtime() : 0;
     const int32_t unit_begin = constant_view(wg_offsets)[blockIdx.x];
     const int32_t unit_end = constant_view(wg_offsets)[blockIdx.x + 1];
 
@@ -683,12 +683,12 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<G>(), 8))) void decode_
     if (ui + 1 < unit_end)
         __syncthreads();  // the next unit rewrites the LDS just read
     }
-    // add this workgroup's run time and a count of one to its XCD's record
-    // (wave 0 leaves after the last combine, which waits for every wave)
-    if (xcd_clock && wg_total > 0 && threadIdx.x == 0) {
+    // add this workgroup's run time and a count of one to its record (wave 0
+    // leaves after the last combine, which waits for every wave)
+    if (wg_clock && wg_total > 0 && threadIdx.x == 0) {
         const uint64_t ticks = __builtin_amdgcn_s_memrealtime() - t_begin;
-        __hip_atomic_fetch_add(xcd_clock + (blockIdx.x % num_xcd) * kXcdClockStride,
-                               (1ull << kXcdClockCountShift) + ticks, __ATOMIC_RELAXED,
+        __hip_atomic_fetch_add(wg_clock + (size_t)blockIdx.x * kClockStride,
+                               (1ull << kClockCountShift) + ticks, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
     }
 }
@@ -719,13 +719,13 @@ int launch_decode_dgk(const DecodeLaunch &l, hipStream_t stream) {
                            l.merges, l.arrivals,
                            (const uint16_t *)l.q, (const char *)l.k_pool, (const char *)l.v_pool,
                            stride_bytes, l.kv_indices, scale_log2, out_scale, l.out, l.lse, l.partial_o,
-                           l.partial_lse, l.num_qo_heads, l.xcd_clock, l.num_xcd);
+                           l.partial_lse, l.num_qo_heads, l.wg_clock);
     else
         hipLaunchKernelGGL((decode_kernel<D, G, false, KV8>), grid, block, 0, stream, l.wg_offsets, l.units,
                            l.merges, l.arrivals,
                            (const uint16_t *)l.q, (const char *)l.k_pool, (const char *)l.v_pool,
                            stride_bytes, l.kv_indices, scale_log2, out_scale, l.out, l.lse, l.partial_o,
-                           l.partial_lse, l.num_qo_heads, l.xcd_clock, l.num_xcd);
+                           l.partial_lse, l.num_qo_heads, l.wg_clock);
     return (int)hipGetLastError();
 }
 

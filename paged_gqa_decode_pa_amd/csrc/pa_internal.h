@@ -20,14 +20,14 @@ constexpr int kMaxXcd = 64;
 // Accepted range of the per-XCD work weights of the automatic decode split.
 constexpr float kMinXcdWeight = 0.25f, kMaxXcdWeight = 4.0f;
 
-// Per-XCD run-time record of the decode kernel (PA_PLAN_XCD_FEEDBACK): one
-// 64-bit counter per XCD, each in a 256-byte line of its own, to which every
-// workgroup with work adds (1 << kXcdClockCountShift) + its run time in ticks
-// of the 100 MHz real-time counter.  The count bits and the time bits are
+// Per-workgroup run-time record of the decode kernel (PA_PLAN_SPEED_FEEDBACK):
+// one 64-bit counter per workgroup id, each in a 64-byte line of its own, to
+// which the workgroup adds (1 << kClockCountShift) + its run time in ticks of
+// the 100 MHz real-time counter.  The count bits and the time bits are
 // separated by subtracting two readings: the time added between them must
 // stay below 2^40 ticks (about three hours of workgroup time).
-constexpr int kXcdClockStride = 32;   // uint64_t per line
-constexpr int kXcdClockCountShift = 40;
+constexpr int kClockStride = 8;   // uint64_t per counter
+constexpr int kClockCountShift = 40;
 
 // Decode kernel geometry: 4 waves of 64 lanes per workgroup; a wave walks its
 // share of a work unit in tiles of kTileTokens tokens.
@@ -66,6 +66,10 @@ struct PartitionArgs {
     // automatic decode: share of the work of each XCD's workgroups relative
     // to an equal split (num_xcd entries, positive); nullptr = equal
     const float *xcd_weights = nullptr;
+    // and of each workgroup id (n_wg_weights entries, positive; ids beyond
+    // them weigh 1), multiplied with its XCD's weight
+    const float *wg_weights = nullptr;
+    int32_t n_wg_weights = 0;
 };
 
 struct PartitionResult {
@@ -131,8 +135,7 @@ struct DecodeLaunch {
     int32_t head_dim;
     bool kv_fp8 = false;             // pools of OCP FP8 E4M3 codes (decode only)
     float k_scale = 1.f, v_scale = 1.f;   // their per-pool scales
-    uint64_t *xcd_clock = nullptr;   // decode: per-XCD run-time record, or null
-    int32_t num_xcd = 1;             // workgroup w runs on XCD w % num_xcd
+    uint64_t *wg_clock = nullptr;    // decode: per-workgroup run-time record, or null
 };
 
 int launch_decode(const DecodeLaunch &l, void *stream);   // returns hipError_t

@@ -11,8 +11,8 @@
 // compute units), so every workgroup starts at time zero and none waits for a
 // free slot; each gets an equal budget of list entries (plus a fixed cost per
 // piece of work it handles), scaled by its XCD's weight when the caller gives
-// per-XCD weights (XCDs of one GPU run at unequal speeds; see
-// PA_PLAN_XCD_FEEDBACK in pa.h).  Segments are taken in (KV head, request) order:
+// per-XCD or per-workgroup weights (the XCDs and compute units of one GPU do
+// not run at equal speeds; see PA_PLAN_SPEED_FEEDBACK in pa.h).  Segments are taken in (KV head, request) order:
 // the first piece of segment i opens workgroup i, so requests that sit next to
 // each other in the batch -- those that share a prompt prefix under a radix
 // prefix cache (Agent-Infer page, section "前缀缓存") -- read their common
@@ -166,17 +166,28 @@ pa_status decode_bins(const PartitionArgs &a, PartitionScratch &ws, int32_t *wg_
     const double ov = kPieceOverheadTokens;
     const bool xcd = !(a.flags & PA_PLAN_NO_XCD_ORDER) && a.num_xcd > 1;
     const int64_t per_xcd = xcd ? ceil_div(n, a.num_xcd) : n;
-    // Bin i runs on XCD i / per_xcd.  Its budget is base * (weight of that
-    // XCD); the budgets add up to the whole work.
-    double wsum = 0.0;
-    for (int64_t x = 0; x * per_xcd < n; x++) {
-        const double w = (xcd && a.xcd_weights) ? a.xcd_weights[x] : 1.0;
-        wsum += w * (double)(std::min(n, (x + 1) * per_xcd) - x * per_xcd);
+    // Bin i runs as workgroup wg_of(i), on XCD i / per_xcd when placed by
+    // XCD.  Its budget is base * (weight of that XCD) * (weight of that
+    // workgroup id); the budgets add up to the whole work.
+    auto wg_of = [&](int64_t i) {
+        return xcd ? (i % per_xcd) * a.num_xcd + i / per_xcd : i;
+    };
+    auto weight_of = [&](int64_t i) {
+        double w = (xcd && a.xcd_weights) ? a.xcd_weights[i / per_xcd] : 1.0;
+        const int64_t id = wg_of(i);
+        if (a.wg_weights && id < a.n_wg_weights)
+            w *= a.wg_weights[id];
+        return w;
+    };
+    const bool weighted = (xcd && a.xcd_weights) || a.wg_weights;
+    double wsum = (double)n;
+    if (weighted) {
+        wsum = 0.0;
+        for (int64_t i = 0; i < n; i++)
+            wsum += weight_of(i);
     }
     const double base = ((double)total + ov * (double)(n_seg + n)) / wsum;
-    auto cap_of = [&](int64_t i) {
-        return (xcd && a.xcd_weights) ? base * a.xcd_weights[i / per_xcd] : base;
-    };
+    auto cap_of = [&](int64_t i) { return weighted ? base * weight_of(i) : base; };
     // entries of the opening piece of segment s < n
     auto open_len = [&](int64_t s) {
         return (int32_t)std::min<double>(seg_len(s), std::max(0.0, cap_of(s) - ov));
@@ -361,7 +372,7 @@ pa_status partition(const PartitionArgs &a, PartitionScratch *scratch, int32_t *
     const int32_t forced = forced_splits(a.flags);
     if (forced > PA_MAX_FORCED_SPLITS)
         return fail(detail, "forced split count above PA_MAX_FORCED_SPLITS", PA_ERR_INVALID_ARG);
-    if ((a.flags & ~(PA_PLAN_FORCE_SPLITS_MASK | PA_PLAN_NO_XCD_ORDER | PA_PLAN_XCD_FEEDBACK)) != 0)
+    if ((a.flags & ~(PA_PLAN_FORCE_SPLITS_MASK | PA_PLAN_NO_XCD_ORDER | PA_PLAN_SPEED_FEEDBACK)) != 0)
         return fail(detail, "unknown flag bits", PA_ERR_INVALID_ARG);
     if (a.num_xcd < 1 || a.num_xcd > kMaxXcd)
         return fail(detail, "XCD count out of range", PA_ERR_INVALID_ARG);
@@ -369,6 +380,10 @@ pa_status partition(const PartitionArgs &a, PartitionScratch *scratch, int32_t *
         for (int32_t x = 0; x < a.num_xcd; x++)
             if (!(a.xcd_weights[x] >= kMinXcdWeight && a.xcd_weights[x] <= kMaxXcdWeight))
                 return fail(detail, "XCD weight outside [0.25, 4]", PA_ERR_INVALID_ARG);
+    if (a.wg_weights)
+        for (int32_t w = 0; w < a.n_wg_weights; w++)
+            if (!(a.wg_weights[w] >= kMinXcdWeight && a.wg_weights[w] <= kMaxXcdWeight))
+                return fail(detail, "workgroup weight outside [0.25, 4]", PA_ERR_INVALID_ARG);
     if (a.batch > 0) {
         if (a.kv_indptr[0] != 0)
             return fail(detail, "kv_indptr[0] != 0", PA_ERR_INVALID_ARG);

@@ -1,8 +1,9 @@
-"""Per-XCD work weights of the automatic decode split and their run-time
-feedback (PA_PLAN_XCD_FEEDBACK): a weighted partition gives the unweighted
-result up to summation order and the oracle within 2e-3, the feedback keeps
-every step's result within the same bounds while it moves the weights, and
-the weights stay in their documented range.  Needs an AMD GPU."""
+"""Work weights of the automatic decode split (per XCD, set by the caller;
+per workgroup, measured by PA_PLAN_SPEED_FEEDBACK): a weighted partition
+gives the unweighted result up to summation order and the oracle within
+2e-3, the feedback keeps every step's result within the same bounds while it
+moves the weights, and the weights stay in their documented range.  Needs an
+AMD GPU."""
 import numpy as np
 import pytest
 import torch
@@ -41,6 +42,8 @@ def test_weights_roundtrip_and_validation():
     with pa.Plan(4, 1000, HQ, HKV, D) as plan:
         w = plan.xcd_weights()
         assert w.size == pa.PA_NUM_XCD and np.all(w == 1.0)
+        ww = plan.workgroup_weights()
+        assert ww.size >= 256 and np.all(ww == 1.0)
         plan.set_xcd_weights([2.0, 2.0, 2.0, 2.0, 1.0, 1.0, 1.0, 1.0])
         got = plan.xcd_weights()
         np.testing.assert_allclose(got, [4 / 3] * 4 + [2 / 3] * 4, rtol=1e-6)
@@ -75,10 +78,10 @@ def test_weighted_partition_parity():
 def test_feedback_over_steps():
     """Eight decode steps of two layers with the feedback on: every step's
     output matches the first within 1e-5 (only the cut points move), the
-    first and last match the oracle, the weights leave 1 once the clock
-    copies arrive and stay within [0.5, 1.5] with mean 1."""
+    first and last match the oracle, the workgroup weights leave 1 once the
+    clock copies arrive and stay within bounds with mean 1."""
     import paged_gqa_decode_pa_amd as pa
-    say("xcd feedback over 8 steps")
+    say("speed feedback over 8 steps")
     ip, idx, q, k, v = _fill_case(33)
     k2, v2 = W.make_pools(120000, HKV, D, 99, device())
     idx_dev = torch.as_tensor(idx, device=device())
@@ -86,14 +89,15 @@ def test_feedback_over_steps():
     outs, weights = [], []
     with pa.Plan(16, int(ip[-1]), HQ, HKV, D) as plan:
         for step in range(8):
-            plan.plan(ip, flags=pa.PA_PLAN_XCD_FEEDBACK)
-            weights.append(plan.xcd_weights())
+            plan.plan(ip, flags=pa.PA_PLAN_SPEED_FEEDBACK)
+            weights.append(plan.workgroup_weights())
             o0, l0 = _run(plan, q, k, v, idx_dev, scale)
             o1, _ = _run(plan, q, k2, v2, idx_dev, scale)
             torch.cuda.synchronize()
             outs.append((o0.cpu().numpy(), l0.cpu().numpy(), o1.cpu().numpy()))
-        final = plan.xcd_weights()
-    say(f"  weights per step: {[np.round(w, 3).tolist() for w in weights]}")
+        final = plan.workgroup_weights()
+        assert np.all(plan.xcd_weights() == 1.0)   # the feedback leaves the XCD weights alone
+    say(f"  weight spread per step: {[(round(float(w.min()), 3), round(float(w.max()), 3)) for w in weights]}")
     for o0, l0, o1 in outs[1:]:
         assert max_err(o0, outs[0][0]) <= 1e-5 and max_err(l0, outs[0][1]) <= 1e-5
         assert max_err(o1, outs[0][2]) <= 1e-5
@@ -101,7 +105,7 @@ def test_feedback_over_steps():
     for o0, l0, _ in (outs[0], outs[-1]):
         assert max_err(o0, ref) <= TOL and max_err(l0, ref_lse) <= TOL
     assert np.all(weights[0] == 1.0)
-    assert np.any(final != 1.0), "no XCD clock record reached the plan"
+    assert np.any(final != 1.0), "no clock record reached the plan"
     for w in weights + [final]:
         assert np.all(w >= 0.5 / 1.5 - 1e-6) and np.all(w <= 1.5 * 1.5 + 1e-6)
-        assert abs(float(w.mean()) - 1.0) < 1e-4
+        assert abs(float(w.mean()) - 1.0) < 1e-3

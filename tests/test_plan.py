@@ -157,7 +157,7 @@ def test_unit_weights_give_the_unweighted_partition():
     b = pa.pa_partition(ip, None, 32, 8, 128, xcd_weights=np.ones(XCD))
     assert all(np.array_equal(x, y) for x, y in zip(a[:3], b[:3])) and a[3] == b[3]
     # the feedback flag is a pa_plan matter: the partition ignores it
-    c = pa.pa_partition(ip, None, 32, 8, 128, pa.PA_PLAN_XCD_FEEDBACK)
+    c = pa.pa_partition(ip, None, 32, 8, 128, pa.PA_PLAN_SPEED_FEEDBACK)
     assert all(np.array_equal(x, y) for x, y in zip(a[:3], c[:3]))
 
 
@@ -200,12 +200,40 @@ def test_weighted_partition_random(seed):
         assert all(np.array_equal(x, y) for x, y in zip(a[:3], b[:3]))
 
 
+def test_workgroup_weighted_budgets():
+    """Workgroup id w gets wg_weights[w] (times its XCD's weight) of an equal
+    share, whichever bin lands on it."""
+    ip, _ = W.decode_lists(W.BATCH64_SHARED_PREFIX)
+    rng = np.random.default_rng(5)
+    ww = rng.uniform(0.6, 1.4, size=768)
+    xw = np.array([1.1, 0.9, 1.0, 1.0, 1.2, 0.8, 1.0, 1.0])
+    offs, units, merges, n_p = pa.pa_partition(ip, None, 32, 8, 128, 0, 768, xcd_weights=xw,
+                                               wg_weights=ww)
+    check_offsets(offs, units)
+    check_decode(units, merges, n_p, ip, 8)
+    cost = _wg_costs(offs, units)
+    want = ww * xw[np.arange(768) % XCD]
+    ratio = (cost / cost.sum()) / (want / want.sum())
+    assert np.percentile(np.abs(ratio - 1), 95) < 0.05 and ratio.max() < 1.1
+    # short weight arrays: ids beyond them weigh 1; plain order ignores XCD weights
+    for flags, x in ((0, None), (pa.PA_PLAN_NO_XCD_ORDER, xw)):
+        for nw in (1, 100, 768, 1000):
+            o2, u2, m2, p2 = pa.pa_partition(ip, None, 32, 8, 128, flags, 768, xcd_weights=x,
+                                             wg_weights=np.full(nw, 0.7))
+            check_offsets(o2, u2)
+            check_decode(u2, m2, p2, ip, 8)
+
+
 @pytest.mark.parametrize("w", [[1.0] * 7, [1.0] * 9, [1.0] * 7 + [0.2], [1.0] * 7 + [4.5],
                                [1.0] * 7 + [float("nan")], [1.0] * 7 + [float("inf")]])
 def test_bad_weights(w):
     with pytest.raises(pa.PAError) as e:
         pa.pa_partition(_indptr([100, 200]), None, 32, 8, 128, xcd_weights=w)
     assert e.value.status == pa.PA_ERR_INVALID_ARG
+    if len(w) == 8:
+        with pytest.raises(pa.PAError) as e:
+            pa.pa_partition(_indptr([100, 200]), None, 32, 8, 128, wg_weights=w)
+        assert e.value.status == pa.PA_ERR_INVALID_ARG
 
 
 def test_decode_small_batch_uses_fewer_workgroups():
