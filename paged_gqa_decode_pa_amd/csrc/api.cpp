@@ -55,6 +55,7 @@ struct pa_plan {
     int32_t n_clock = 0;                 // workgroup ids with a counter
     std::vector<float> wg_weight;        // n_clock entries, from cu_weight
     std::vector<float> cu_weight;        // num_cu entries
+    bool xcd_weighted = false, wg_weighted = false;   // some weight differs from 1
     std::vector<double> cu_busy;         // update_cu_weights' working array
     uint64_t *d_wg_clock = nullptr;      // device, n_clock counters, kClockStride apart
     uint64_t *h_wg_clock = nullptr;      // pinned copy
@@ -212,6 +213,7 @@ void update_cu_weights(pa_plan_t *p) {
             p->cu_weight[c] = (float)(p->cu_weight[c] * active / wsum);
     for (int32_t w = 0; w < p->n_clock; w++)
         p->wg_weight[w] = p->cu_weight[w % C];
+    p->wg_weighted = true;
 }
 
 pa_status prepare_run(const pa_plan_t *p, pa::PlanMode want, const void *q, const void *k_pool,
@@ -382,6 +384,9 @@ pa_status pa_plan_set_xcd_weights(pa_plan_t *p, const float *weights, int32_t n)
     for (int32_t x = 0; x < n; x++)   // the rescaled set must still be accepted
         w[x] = std::min(pa::kMaxXcdWeight, std::max(pa::kMinXcdWeight, w[x]));
     std::memcpy(p->xcd_weight, w, sizeof(float) * (size_t)n);
+    p->xcd_weighted = false;
+    for (int32_t x = 0; x < n; x++)
+        p->xcd_weighted |= w[x] != 1.0f;
     return PA_OK;
 }
 
@@ -544,8 +549,9 @@ pa_status pa_plan(pa_plan_t *p, const int32_t *kv_indptr_host, const int32_t *qo
     pa_work_unit *units = reinterpret_cast<pa_work_unit *>(stage + units_at);
     pa_merge_unit *merges = reinterpret_cast<pa_merge_unit *>(stage + units_at + (size_t)p->unit_cap * kUnit);
     pa::PartitionArgs a{kv_indptr_host, qo_indptr_host, batch, p->num_qo_heads, p->num_kv_heads,
-                        p->head_dim, flags, p->max_workgroups, p->num_xcd, p->xcd_weight,
-                        p->wg_weight.data(), p->n_clock};
+                        p->head_dim, flags, p->max_workgroups, p->num_xcd,
+                        p->xcd_weighted ? p->xcd_weight : nullptr,
+                        p->wg_weighted ? p->wg_weight.data() : nullptr, p->n_clock};
     pa::PartitionResult r;
     const char *detail = "";
     auto clamp32 = [](int64_t v) { return (int32_t)std::min<int64_t>(v, 0x7fffffff); };

@@ -88,6 +88,7 @@ struct PartitionScratch {
     };
     std::vector<int32_t> seg_request, seg_pieces, seg_first, seg_merge, bin_stream;
     std::vector<Piece> stream;
+    std::vector<double> bin_cap;   // budget of each bin when weighted
 };
 
 // Validates the arguments; fills wg_offsets (n_workgroups + 1 entries), units

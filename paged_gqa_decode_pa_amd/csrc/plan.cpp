@@ -182,12 +182,18 @@ pa_status decode_bins(const PartitionArgs &a, PartitionScratch &ws, int32_t *wg_
     const bool weighted = (xcd && a.xcd_weights) || a.wg_weights;
     double wsum = (double)n;
     if (weighted) {
+        ws.bin_cap.resize(n);
         wsum = 0.0;
-        for (int64_t i = 0; i < n; i++)
-            wsum += weight_of(i);
+        for (int64_t i = 0; i < n; i++) {
+            ws.bin_cap[i] = weight_of(i);
+            wsum += ws.bin_cap[i];
+        }
     }
     const double base = ((double)total + ov * (double)(n_seg + n)) / wsum;
-    auto cap_of = [&](int64_t i) { return weighted ? base * weight_of(i) : base; };
+    if (weighted)
+        for (int64_t i = 0; i < n; i++)
+            ws.bin_cap[i] *= base;
+    auto cap_of = [&](int64_t i) { return weighted ? ws.bin_cap[i] : base; };
     // entries of the opening piece of segment s < n
     auto open_len = [&](int64_t s) {
         return (int32_t)std::min<double>(seg_len(s), std::max(0.0, cap_of(s) - ov));
