@@ -500,7 +500,8 @@ def main():
     torch.cuda.synchronize()
     plan_host_us = float(np.median(idle))
     log(f"pa_plan host {plan_host_us:.1f} us (idle GPU); inside the timed steps "
-        f"{np.median(in_step[:, 0]):.1f} us of which waiting {np.median(in_step[:, 1]):.1f} us")
+        f"{np.median(in_step[:, 0] - in_step[:, 1]):.1f} us of work, plus "
+        f"{np.median(in_step[:, 1]):.1f} us waiting for the GPU (the host runs two steps ahead)")
 
     step_bytes = bytes_per_layer * layers
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
@@ -541,7 +542,10 @@ def main():
         "frac_of_peak": round(value / HBM_PEAK_GBS, 4),
         "ms_per_step_with_kernel_events": round(ms_per_step_events, 4),
         "plan_host_us": round(plan_host_us, 1),
-        "plan_host_us_in_step": round(float(np.median(in_step[:, 0])), 1),
+        # the plan's own work inside the timed steps, and separately the time
+        # it blocked because the host was two steps ahead of the GPU
+        "plan_host_us_in_step": round(float(np.median(in_step[:, 0] - in_step[:, 1])), 1),
+        "plan_backpressure_wait_us_in_step": round(float(np.median(in_step[:, 1])), 1),
         "algorithmic_bytes_per_layer": bytes_per_layer,
         "roofline": {
             "bound": "hbm",
