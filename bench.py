@@ -352,12 +352,14 @@ def main():
     ap.add_argument("--flags", type=int, default=0x2,
                     help="pa_plan flags (default PA_PLAN_SPEED_FEEDBACK: per-compute-unit budgets from measured speed)")
     ap.add_argument("--workload", default="batch64",
-                    choices=["batch64", "single_request", "batch8", "hd256",
+                    choices=["batch64", "single_request", "batch8", "hd256", "system_prompt",
                              "prefill_chunk512", "prefill_chunk64", "append", "copy"])
     ap.add_argument("--kv", default="bf16", choices=["bf16", "fp8"],
                     help="decode: pool element type (fp8 = OCP E4M3 codes with per-pool scales)")
     ap.add_argument("--graph", action="store_true",
                     help="decode: replay each step's layer runs from a captured HIP graph")
+    ap.add_argument("--cascade", action="store_true",
+                    help="decode: plan with pa_plan_cascade over the workload's shared-prefix groups")
     ap.add_argument("--copy-gib", type=float, default=4.0)
     args = ap.parse_args()
 
@@ -386,7 +388,8 @@ def main():
     import workloads as W
 
     spec = {"batch64": W.BATCH64_SHARED_PREFIX, "single_request": W.SINGLE_REQUEST_256,
-            "batch8": W.QWEN3_4B_BATCH8, "hd256": W.HEADDIM256_BATCH32}[args.workload]
+            "batch8": W.QWEN3_4B_BATCH8, "hd256": W.HEADDIM256_BATCH32,
+            "system_prompt": W.SYSTEM_PROMPT_B64}[args.workload]
     # every decode workload runs 36 layers per step, each with its own pools
     layers = args.layers or 36
     dev = torch.device("cuda", 0)
@@ -412,6 +415,20 @@ def main():
     plan = pa.Plan(B, int(case.kv_indptr[-1]), Hq, Hkv, D)
     stream = torch.cuda.current_stream(dev)
     plan_host_s = []
+    if args.cascade and not spec.prefix_group_size:
+        raise SystemExit(f"--cascade needs a workload with shared prefixes ({spec.name} has none)")
+    if args.cascade:
+        # the workload's prefix groups: consecutive requests sharing their
+        # leading slot ids (what a radix prefix cache reports)
+        group_indptr = np.arange(0, B + 1, spec.prefix_group_size, dtype=np.int32)
+        prefix_len = np.full(group_indptr.size - 1, spec.prefix_len, np.int32)
+
+    def do_plan():
+        if args.cascade:
+            plan.plan_cascade(case.kv_indptr, group_indptr, prefix_len, flags=args.flags,
+                              stream=stream)
+        else:
+            plan.plan(case.kv_indptr, flags=args.flags, stream=stream)
 
     def layer_runs(s):
         for layer in range(layers):
@@ -427,7 +444,7 @@ def main():
         # the step's layer runs captured once; every step's pa_plan rewrites
         # the same device tables (same lists, hence the same grid), which the
         # replayed kernels read
-        plan.plan(case.kv_indptr, flags=args.flags, stream=stream)
+        do_plan()
         side = torch.cuda.Stream(dev)
         side.wait_stream(stream)
         with torch.cuda.stream(side):
@@ -440,7 +457,7 @@ def main():
         torch.cuda.synchronize()
 
     def step(eager=False):
-        plan.plan(case.kv_indptr, flags=args.flags, stream=stream)
+        do_plan()
         plan_host_s.append(pa.pa_plan_host_timing(plan.handle))
         if graph is not None and not eager:
             graph.replay()
@@ -495,7 +512,7 @@ def main():
     idle = []
     for _ in range(50):
         torch.cuda.synchronize()
-        plan.plan(case.kv_indptr, flags=args.flags, stream=stream)
+        do_plan()
         idle.append(pa.pa_plan_host_timing(plan.handle)[0])
     torch.cuda.synchronize()
     plan_host_us = float(np.median(idle))
@@ -532,6 +549,7 @@ def main():
                               f"{spec.prefix_group_size} requests x {spec.prefix_len} slots"
                               if spec.prefix_group_size else "none"),
             "layer_runs": "hip graph replay" if graph is not None else "eager",
+            "plan": "pa_plan_cascade (shared prefixes read once per group)" if args.cascade else "pa_plan",
             "list_entries": int(case.kv_indptr[-1]),
             "unique_slots": int(np.unique(case.kv_indices).size),
             "pool_slots": spec.num_slots,
@@ -555,7 +573,8 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
             "kernel": f"decode_kernel<{D},{G},{'e4m3' if fp8 else 'bf16'}> "
-                      f"({'pa_decode_run_fp8' if fp8 else 'pa_decode_run'})",
+                      f"({'pa_decode_run_fp8' if fp8 else 'pa_decode_run'})"
+                      + (" after the cascade prefix units (prefill_kernel); time of both" if args.cascade else ""),
             "kernel_avg_us": round(kernel_avg_ms * 1e3, 2),
         },
         "cpu_baseline": None,

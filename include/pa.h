@@ -114,6 +114,12 @@ typedef enum pa_status {
  * rounding (within the usual tolerance).  The weights in use are read with
  * pa_plan_workgroup_weights. */
 #define PA_PLAN_SPEED_FEEDBACK 0x2u
+/* pa_plan_cascade: give every group with a prefix its prefix units.  Without
+ * it, groups whose member query rows (members x Hq/Hkv) number fewer than 64
+ * are decoded as if they had no prefix: their members read the shared slots
+ * at the same moment and share them through the L2 cache, which measured
+ * faster than a separate prefix pass over so few rows. */
+#define PA_PLAN_CASCADE_ALL 0x4u
 
 /* Largest max_kv_total a plan accepts: list entries are addressed with 32-bit
  * byte offsets. */
@@ -153,6 +159,32 @@ pa_status pa_plan_create(pa_plan_t **out, int32_t max_batch, int64_t max_kv_tota
 pa_status pa_plan(pa_plan_t *plan, const int32_t *kv_indptr_host,
                   const int32_t *qo_indptr_host, int32_t batch, uint32_t flags,
                   pa_stream_t stream);
+
+/*
+ * pa_plan_cascade: a decode plan that reads each group's shared prompt prefix
+ * once for the whole group (cascade decode; the radix prefix cache that makes
+ * requests share leading slots is on the Agent-Infer page, section "前缀缓存").
+ *   kv_indptr_host, batch, flags, stream: as in pa_plan (decode);
+ *   group_indptr_host [num_groups + 1]: group g is requests
+ *     [group_indptr[g], group_indptr[g+1]); group_indptr[0] = 0,
+ *     nondecreasing, group_indptr[num_groups] = batch;
+ *   prefix_len_host [num_groups]: the first prefix_len[g] entries of every
+ *     member's list are the same slot ids (the caller guarantees it; they are
+ *     read from the first member's list), 0 <= prefix_len[g] <= the shortest
+ *     member list.
+ * pa_decode_run under this plan launches two kernels: the prefix units
+ * (matrix-core attention of all member query rows over the shared prefix,
+ * at most 128 / (Hq/Hkv) requests per unit, the prefix cut into up to 32
+ * parts) writing partial results, then the decode kernel over the rest of
+ * every list, whose merges fold the prefix partials in.  The result equals
+ * pa_decode_run under pa_plan up to summation order.  Groups with
+ * prefix_len 0 and singleton groups cost nothing extra.  Errors: as pa_plan,
+ * plus PA_ERR_INVALID_ARG for inconsistent groups or prefix lengths.
+ * pa_decode_run_fp8 does not take cascade plans (PA_ERR_UNSUPPORTED).
+ */
+pa_status pa_plan_cascade(pa_plan_t *plan, const int32_t *kv_indptr_host, int32_t batch,
+                          const int32_t *group_indptr_host, int32_t num_groups,
+                          const int32_t *prefix_len_host, uint32_t flags, pa_stream_t stream);
 
 /*
  * pa_decode_run: decode attention of one layer under a decode plan.
@@ -223,10 +255,17 @@ const char *pa_last_error_detail(void);
  * diag (prefill): query row q_begin + r sees list entries up to offset
  * diag + r inclusive (the causal window); decode units set diag = kv_end - 1.
  * merge: index of the pa_merge_unit that combines this unit's partial with
- * the other parts of its range (-1 when partial < 0).
+ * the other parts of its range (-1 when partial < 0).  part_stride (prefix
+ * units of a cascade plan, see pa_plan_cascade): query row q_begin + t of the
+ * unit writes partial slot partial + t * part_stride; 0 for every other unit
+ * (a prefill unit's rows then fill slot `partial` of the prefill layout).
  *
  * pa_merge_unit: the partial slots [first_partial, first_partial + n_parts)
- * that make up query rows [q_begin, q_end) of KV head kv_head.
+ * that make up query rows [q_begin, q_end) of KV head kv_head, plus, in a
+ * cascade plan, the slots [prefix_first, prefix_first + prefix_parts) written
+ * by the prefix units of the request's group before the decode kernel runs
+ * (prefix_parts = 0 otherwise).  Decode and prefix partial slots hold one row
+ * per query head of the KV head's group.
  */
 typedef struct pa_work_unit {
     int32_t request;
@@ -238,7 +277,7 @@ typedef struct pa_work_unit {
     int32_t partial;
     int32_t diag;
     int32_t merge;
-    int32_t reserved0;
+    int32_t part_stride;
     int32_t reserved1;
     int32_t reserved2;
 } pa_work_unit;
@@ -250,8 +289,8 @@ typedef struct pa_merge_unit {
     int32_t q_end;
     int32_t first_partial;
     int32_t n_parts;
-    int32_t reserved0;
-    int32_t reserved1;
+    int32_t prefix_first;
+    int32_t prefix_parts;
 } pa_merge_unit;
 
 /*
@@ -318,6 +357,24 @@ pa_status pa_partition_weighted(const int32_t *kv_indptr_host, const int32_t *qo
                                 int32_t unit_capacity, pa_merge_unit *merges,
                                 int32_t merge_capacity, int32_t *n_workgroups, int32_t *n_units,
                                 int32_t *n_merges, int32_t *n_partials);
+
+/*
+ * pa_partition_cascade: the partition pa_plan_cascade would upload, into host
+ * arrays (arguments as in pa_plan_cascade and pa_partition).  The decode part
+ * is returned as by pa_partition; prefix_units[prefix_capacity] receives the
+ * prefix units (*n_prefix_units of them; prefix unit i runs as workgroup i of
+ * the prefix launch).  *n_partials counts decode and prefix slots.
+ * PA_ERR_CAPACITY if an array is too small (the counts are still written).
+ */
+pa_status pa_partition_cascade(const int32_t *kv_indptr_host, int32_t batch,
+                               const int32_t *group_indptr_host, int32_t num_groups,
+                               const int32_t *prefix_len_host, int32_t num_qo_heads,
+                               int32_t num_kv_heads, int32_t head_dim, uint32_t flags,
+                               int32_t max_workgroups, int32_t *wg_offsets, int32_t wg_capacity,
+                               pa_work_unit *units, int32_t unit_capacity, pa_merge_unit *merges,
+                               int32_t merge_capacity, pa_work_unit *prefix_units,
+                               int32_t prefix_capacity, int32_t *n_workgroups, int32_t *n_units,
+                               int32_t *n_merges, int32_t *n_partials, int32_t *n_prefix_units);
 
 /*
  * pa_plan_xcd_weights: the per-XCD weights the plan's next automatic decode

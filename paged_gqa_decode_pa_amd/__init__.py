@@ -33,6 +33,7 @@ PA_MAX_FORCED_SPLITS = 256
 PA_MAX_KV_TOTAL = 1 << 29
 PA_PLAN_NO_XCD_ORDER = 0x1
 PA_PLAN_SPEED_FEEDBACK = 0x2
+PA_PLAN_CASCADE_ALL = 0x4
 PA_NUM_XCD = 8
 
 
@@ -43,13 +44,13 @@ def PA_PLAN_FORCE_SPLITS(n: int) -> int:
 class pa_work_unit(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("request", "kv_head", "kv_begin", "kv_end", "q_begin", "q_end", "partial", "diag",
-                 "merge", "reserved0", "reserved1", "reserved2")]
+                 "merge", "part_stride", "reserved1", "reserved2")]
 
 
 class pa_merge_unit(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("request", "kv_head", "q_begin", "q_end", "first_partial", "n_parts",
-                 "reserved0", "reserved1")]
+                 "prefix_first", "prefix_parts")]
 
 
 WORK_UNIT_DTYPE = np.dtype([(n, np.int32) for n, _ in pa_work_unit._fields_])
@@ -101,6 +102,13 @@ def _load() -> ctypes.CDLL:
     lib.pa_plan_xcd_weights.restype = ctypes.c_int
     lib.pa_plan_set_xcd_weights.argtypes = [vp, f32p, i32]
     lib.pa_plan_set_xcd_weights.restype = ctypes.c_int
+    lib.pa_plan_cascade.argtypes = [vp, i32p, i32, i32p, i32, i32p, u32, vp]
+    lib.pa_plan_cascade.restype = ctypes.c_int
+    wup, mup = ctypes.POINTER(pa_work_unit), ctypes.POINTER(pa_merge_unit)
+    lib.pa_partition_cascade.argtypes = [i32p, i32, i32p, i32, i32p, i32, i32, i32, u32, i32,
+                                         i32p, i32, wup, i32, mup, i32, wup, i32,
+                                         i32p, i32p, i32p, i32p, i32p]
+    lib.pa_partition_cascade.restype = ctypes.c_int
     lib.pa_plan_workgroup_weights.argtypes = [vp, f32p, i32, i32p]
     lib.pa_plan_workgroup_weights.restype = ctypes.c_int
     lib.pa_profile_begin.argtypes = [vp, i32]
@@ -193,6 +201,16 @@ def pa_plan(plan, kv_indptr, qo_indptr=None, flags: int = 0, stream=None) -> Non
     qo = _host_i32(qo_indptr)
     batch = kv.size - 1
     _check(_lib.pa_plan(plan, _i32p(kv), _i32p(qo), batch, flags, _stream(stream)), "pa_plan")
+
+
+def pa_plan_cascade(plan, kv_indptr, group_indptr, prefix_len, flags: int = 0,
+                    stream=None) -> None:
+    kv = _host_i32(kv_indptr)
+    gi = _host_i32(group_indptr)
+    pl = _host_i32(prefix_len)
+    ng = 0 if gi is None else gi.size - 1
+    _check(_lib.pa_plan_cascade(plan, _i32p(kv), kv.size - 1, _i32p(gi), ng, _i32p(pl), flags,
+                                _stream(stream)), "pa_plan_cascade")
 
 
 def _run(fn, where, plan, q, k_pool, v_pool, kv_indices, sm_scale, out, lse,
@@ -325,6 +343,39 @@ def pa_partition(kv_indptr, qo_indptr, num_qo_heads: int, num_kv_heads: int, hea
     return offs, u, m, n_p.value
 
 
+def pa_partition_cascade(kv_indptr, group_indptr, prefix_len, num_qo_heads: int,
+                         num_kv_heads: int, head_dim: int, flags: int = 0,
+                         max_workgroups: int = 0):
+    """Host-only: the partition pa_plan_cascade would upload.
+
+    Returns (wg_offsets, units, merges, n_partials, prefix_units).
+    """
+    kv = _host_i32(kv_indptr)
+    gi = _host_i32(group_indptr)
+    pl = _host_i32(prefix_len)
+    ng = 0 if gi is None else gi.size - 1
+    cnt = [ctypes.c_int32() for _ in range(5)]
+    refs = [ctypes.byref(c) for c in cnt]
+    st = _lib.pa_partition_cascade(_i32p(kv), kv.size - 1, _i32p(gi), ng, _i32p(pl), num_qo_heads,
+                                   num_kv_heads, head_dim, flags, max_workgroups, None, 0, None, 0,
+                                   None, 0, None, 0, *refs)
+    if st not in (PA_OK, PA_ERR_CAPACITY):
+        _check(st, "pa_partition_cascade")
+    n_w, n_u, n_m, n_p, n_x = (c.value for c in cnt)
+    offs = np.zeros(n_w + 1, np.int32)
+    units = (pa_work_unit * max(1, n_u))()
+    merges = (pa_merge_unit * max(1, n_m))()
+    pre = (pa_work_unit * max(1, n_x))()
+    _check(_lib.pa_partition_cascade(_i32p(kv), kv.size - 1, _i32p(gi), ng, _i32p(pl), num_qo_heads,
+                                     num_kv_heads, head_dim, flags, max_workgroups, _i32p(offs),
+                                     offs.size, units, n_u, merges, n_m, pre, n_x, *refs),
+           "pa_partition_cascade")
+    u = np.frombuffer(bytes(units), dtype=WORK_UNIT_DTYPE)[:n_u].copy()
+    m = np.frombuffer(bytes(merges), dtype=MERGE_UNIT_DTYPE)[:n_m].copy()
+    x = np.frombuffer(bytes(pre), dtype=WORK_UNIT_DTYPE)[:n_x].copy()
+    return offs, u, m, cnt[3].value, x
+
+
 def pa_plan_xcd_weights(plan) -> np.ndarray:
     """The per-XCD weights the plan's next automatic decode partition uses."""
     n = ctypes.c_int32()
@@ -393,6 +444,10 @@ class Plan:
 
     def workgroup_weights(self) -> np.ndarray:
         return pa_plan_workgroup_weights(self.handle)
+
+    def plan_cascade(self, kv_indptr, group_indptr, prefix_len, flags: int = 0,
+                     stream=None) -> None:
+        pa_plan_cascade(self.handle, kv_indptr, group_indptr, prefix_len, flags, stream)
 
     def decode(self, q, k_pool, v_pool, kv_indices, sm_scale, out, lse=None, **kw) -> None:
         pa_decode_run(self.handle, q, k_pool, v_pool, kv_indices, sm_scale, out, lse, **kw)

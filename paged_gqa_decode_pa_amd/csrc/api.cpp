@@ -27,6 +27,7 @@ struct pa_plan {
     int32_t num_cu = pa::kNumCu, num_xcd = pa::kNumXcd;
     int32_t max_workgroups = 0;  // decode workgroups resident at once
     int64_t wg_cap = 0, unit_cap = 0, merge_cap = 0, partial_rows_cap = 0;
+    int64_t prefix_cap = 0;       // cascade prefix units
     // device: [workgroup offsets | units | merges] packed by the last pa_plan,
     // and partial storage
     void *d_table = nullptr;
@@ -44,6 +45,7 @@ struct pa_plan {
     int64_t kv_total = 0;
     int32_t q_total = 0;
     int32_t n_workgroups = 0, n_units = 0, n_merges = 0, n_partials = 0;
+    int32_t n_prefix_units = 0;   // cascade plan: prefix units after the merges
     pa::PartitionScratch scratch;  // host working arrays of the partition
     double plan_total_us = 0.0, plan_wait_us = 0.0;  // host time of the last pa_plan
     // work weights of the automatic decode split: per XCD (set by the
@@ -97,8 +99,11 @@ size_t offsets_bytes(int64_t n_workgroups) {
     return (size_t)((n_workgroups + 1 + 15) / 16) * 64;
 }
 
+// Table layout (device and staging): [workgroup offsets | units | merges |
+// prefix workgroup offsets | prefix units]; the last two only in cascade plans.
 size_t table_bytes(const pa_plan_t *p) {
-    return offsets_bytes(p->wg_cap) + (size_t)p->unit_cap * kUnit + (size_t)p->merge_cap * kMerge;
+    return offsets_bytes(p->wg_cap) + (size_t)p->unit_cap * kUnit + (size_t)p->merge_cap * kMerge +
+           offsets_bytes(p->prefix_cap) + (size_t)p->prefix_cap * kUnit;
 }
 
 void drop_profile(pa_plan_t *p) {
@@ -216,6 +221,23 @@ void update_cu_weights(pa_plan_t *p) {
     p->wg_weighted = true;
 }
 
+// The launch of a cascade plan's prefix units: the decode launch l with the
+// prefix workgroup offsets and units of the table (packed after the merges).
+pa::DecodeLaunch prefix_launch(const pa_plan_t *p, const pa::DecodeLaunch &l) {
+    pa::DecodeLaunch x = l;
+    const char *tbl = static_cast<const char *>(p->d_table);
+    const size_t at = offsets_bytes(p->n_workgroups) + (size_t)p->n_units * kUnit +
+                      (size_t)p->n_merges * kMerge;
+    x.wg_offsets = reinterpret_cast<const int32_t *>(tbl + at);
+    x.n_workgroups = p->n_prefix_units;
+    x.units = reinterpret_cast<const pa_work_unit *>(tbl + at + offsets_bytes(p->n_prefix_units));
+    x.n_units = p->n_prefix_units;
+    x.merges = nullptr;
+    x.n_merges = 0;
+    x.wg_clock = nullptr;
+    return x;
+}
+
 pa_status prepare_run(const pa_plan_t *p, pa::PlanMode want, const void *q, const void *k_pool,
                       const void *v_pool, int64_t num_slots, int64_t slot_stride,
                       const int32_t *kv_indices, float sm_scale, float *out, float *lse,
@@ -282,6 +304,147 @@ pa_status prepare_run(const pa_plan_t *p, pa::PlanMode want, const void *q, cons
 
 }  // namespace
 
+// pa_plan and pa_plan_cascade (casc != nullptr).
+static pa_status plan_impl(pa_plan_t *p, const int32_t *kv_indptr_host, const int32_t *qo_indptr_host,
+                           int32_t batch, uint32_t flags, pa_stream_t stream,
+                           const pa::CascadeArgs *casc) {
+    using clock = std::chrono::steady_clock;
+    const clock::time_point t_start = clock::now();
+    if (!p)
+        return fail(PA_ERR_INVALID_ARG, "plan is null");
+    if (batch < 0)
+        return fail(PA_ERR_INVALID_ARG, "batch < 0");
+    if (batch > 0 && !kv_indptr_host)
+        return fail(PA_ERR_INVALID_ARG, "kv_indptr_host is null");
+    if (batch > p->max_batch)
+        return fail(PA_ERR_CAPACITY, "batch above the plan's max_batch");
+    const int64_t kv_total = batch > 0 ? kv_indptr_host[batch] : 0;
+    if (kv_total > p->max_kv_total)
+        return fail(PA_ERR_CAPACITY, "total slot-list length above the plan's max_kv_total");
+    int32_t q_total = 0;
+    if (qo_indptr_host) {
+        q_total = batch > 0 ? qo_indptr_host[batch] : 0;
+        if (q_total > p->max_q_total)
+            return fail(PA_ERR_CAPACITY, "total query rows above the plan's max_q_total");
+    }
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetDevice");
+    if (dev != p->device)
+        return fail(PA_ERR_INVALID_ARG, "current HIP device differs from the plan's device");
+
+    const bool auto_decode = !qo_indptr_host &&
+                             ((flags & PA_PLAN_FORCE_SPLITS_MASK) >> PA_PLAN_FORCE_SPLITS_SHIFT) == 0;
+    const bool feedback = (flags & PA_PLAN_SPEED_FEEDBACK) && auto_decode;
+    // the weights of the plans since the last clock copy (they change only
+    // below, when a copy is read, and a copy is started only when none is
+    // pending)
+    if (feedback)
+        std::copy(p->cu_weight.begin(), p->cu_weight.end(), p->interval_weight.begin());
+    if (feedback && p->clock_pending) {
+        const hipError_t before = hipPeekAtLastError();
+        e = hipEventQuery(p->clock_done);
+        if (e == hipSuccess) {
+            p->clock_pending = false;
+            update_cu_weights(p);
+        } else if (e == hipErrorNotReady) {
+            if (before == hipSuccess)
+                (void)hipGetLastError();  // not an error: the copy is still in flight
+        } else {
+            return hip_fail(e, "clock copy");
+        }
+    }
+
+    const int s = p->next_stage;
+    const clock::time_point t_wait = clock::now();
+    if (p->stage_pending[s]) {
+        if ((e = hipEventSynchronize(p->stage_done[s])) != hipSuccess)
+            return hip_fail(e, "waiting for an earlier plan upload");
+        p->stage_pending[s] = false;
+    }
+    const clock::time_point t_waited = clock::now();
+    // partition straight into the staging buffer at capacity offsets, then
+    // pack the three lists together and upload them with one copy
+    char *stage = static_cast<char *>(p->h_stage[s]);
+    int32_t *offsets = reinterpret_cast<int32_t *>(stage);
+    const size_t units_at = offsets_bytes(p->wg_cap);
+    pa_work_unit *units = reinterpret_cast<pa_work_unit *>(stage + units_at);
+    pa_merge_unit *merges = reinterpret_cast<pa_merge_unit *>(stage + units_at + (size_t)p->unit_cap * kUnit);
+    pa::PartitionArgs a{kv_indptr_host, qo_indptr_host, batch, p->num_qo_heads, p->num_kv_heads,
+                        p->head_dim, flags, p->max_workgroups, p->num_xcd,
+                        p->xcd_weighted ? p->xcd_weight : nullptr,
+                        p->wg_weighted ? p->wg_weight.data() : nullptr, p->n_clock};
+    pa::PartitionResult r;
+    const char *detail = "";
+    auto clamp32 = [](int64_t v) { return (int32_t)std::min<int64_t>(v, 0x7fffffff); };
+    const size_t prefix_at = units_at + (size_t)p->unit_cap * kUnit + (size_t)p->merge_cap * kMerge;
+    pa_work_unit *prefix_units =
+        reinterpret_cast<pa_work_unit *>(stage + prefix_at + offsets_bytes(p->prefix_cap));
+    pa_status st = casc ? pa::cascade_partition(a, *casc, &p->scratch, offsets, clamp32(p->wg_cap + 1),
+                                                units, clamp32(p->unit_cap), merges,
+                                                clamp32(p->merge_cap), prefix_units,
+                                                clamp32(p->prefix_cap), &r, &detail)
+                        : pa::partition(a, &p->scratch, offsets, clamp32(p->wg_cap + 1), units,
+                                        clamp32(p->unit_cap), merges, clamp32(p->merge_cap), &r,
+                                        &detail);
+    if (st != PA_OK)
+        return fail(st, detail);
+    const int64_t rows_per_slot = qo_indptr_host ? pa::kPrefillTileRows : p->group;
+    if ((int64_t)r.n_partials * rows_per_slot > p->partial_rows_cap)
+        return fail(PA_ERR_CAPACITY, "partial storage of the plan exceeded");
+    // pack: [offsets | units | merges | prefix offsets | prefix units]
+    const size_t off_b = offsets_bytes(r.n_workgroups);
+    if (r.n_units > 0)
+        std::memmove(stage + off_b, units, (size_t)r.n_units * kUnit);
+    if (r.n_merges > 0)
+        std::memmove(stage + off_b + (size_t)r.n_units * kUnit, merges, (size_t)r.n_merges * kMerge);
+    size_t bytes = off_b + (size_t)r.n_units * kUnit + (size_t)r.n_merges * kMerge;
+    if (r.n_prefix_units > 0) {
+        // one prefix unit per workgroup (packed after the merges, so the
+        // prefix offsets are written last: they may overlap the old units)
+        const size_t pre_off_b = offsets_bytes(r.n_prefix_units);
+        std::memmove(stage + bytes + pre_off_b, prefix_units, (size_t)r.n_prefix_units * kUnit);
+        int32_t *po = reinterpret_cast<int32_t *>(stage + bytes);
+        for (int32_t w = 0; w <= r.n_prefix_units; w++)
+            po[w] = w;
+        bytes += pre_off_b + (size_t)r.n_prefix_units * kUnit;
+    }
+    if ((e = hipMemcpyAsync(p->d_table, stage, bytes, hipMemcpyHostToDevice,
+                            (hipStream_t)stream)) != hipSuccess)
+        return hip_fail(e, "plan upload");
+    if ((e = hipEventRecord(p->stage_done[s], (hipStream_t)stream)) != hipSuccess)
+        return hip_fail(e, "plan upload event");
+    p->stage_pending[s] = true;
+    p->next_stage = s ^ 1;
+    if (feedback && !p->clock_pending) {
+        // the counters as of the end of the launches enqueued so far: those
+        // since the previous copy all used interval_weight
+        if ((e = hipMemcpyAsync(p->h_wg_clock, p->d_wg_clock,
+                                (size_t)p->n_clock * pa::kClockStride * sizeof(uint64_t),
+                                hipMemcpyDeviceToHost, (hipStream_t)stream)) != hipSuccess ||
+            (e = hipEventRecord(p->clock_done, (hipStream_t)stream)) != hipSuccess)
+            return hip_fail(e, "clock copy");
+        std::copy(p->interval_weight.begin(), p->interval_weight.end(), p->clock_weight.begin());
+        p->clock_pending = true;
+    }
+    // only launches that fill the GPU measure the workgroups' speeds
+    p->clock_record = feedback && r.n_workgroups >= p->max_workgroups &&
+                      r.n_workgroups <= p->n_clock;
+    p->mode = qo_indptr_host ? pa::PlanMode::kPrefill : pa::PlanMode::kDecode;
+    p->batch = batch;
+    p->kv_total = kv_total;
+    p->q_total = q_total;
+    p->n_workgroups = r.n_workgroups;
+    p->n_units = r.n_units;
+    p->n_merges = r.n_merges;
+    p->n_partials = r.n_partials;
+    p->n_prefix_units = r.n_prefix_units;
+    p->plan_wait_us = std::chrono::duration<double, std::micro>(t_waited - t_wait).count();
+    p->plan_total_us = std::chrono::duration<double, std::micro>(clock::now() - t_start).count();
+    return PA_OK;
+}
+
 extern "C" {
 
 const char *pa_strerror(pa_status s) {
@@ -345,6 +508,44 @@ pa_status pa_partition_weighted(const int32_t *kv_indptr_host, const int32_t *qo
     *n_units = r.n_units;
     *n_merges = r.n_merges;
     *n_partials = r.n_partials;
+    if (s != PA_OK)
+        return fail(s, detail);
+    return PA_OK;
+}
+
+pa_status pa_partition_cascade(const int32_t *kv_indptr_host, int32_t batch,
+                               const int32_t *group_indptr_host, int32_t num_groups,
+                               const int32_t *prefix_len_host, int32_t num_qo_heads,
+                               int32_t num_kv_heads, int32_t head_dim, uint32_t flags,
+                               int32_t max_workgroups, int32_t *wg_offsets, int32_t wg_capacity,
+                               pa_work_unit *units, int32_t unit_capacity, pa_merge_unit *merges,
+                               int32_t merge_capacity, pa_work_unit *prefix_units,
+                               int32_t prefix_capacity, int32_t *n_workgroups, int32_t *n_units,
+                               int32_t *n_merges, int32_t *n_partials, int32_t *n_prefix_units) {
+    if (!n_workgroups || !n_units || !n_merges || !n_partials || !n_prefix_units)
+        return fail(PA_ERR_INVALID_ARG, "count pointers must not be null");
+    if ((wg_capacity > 0 && !wg_offsets) || (unit_capacity > 0 && !units) ||
+        (merge_capacity > 0 && !merges) || (prefix_capacity > 0 && !prefix_units) ||
+        wg_capacity < 0 || unit_capacity < 0 || merge_capacity < 0 || prefix_capacity < 0)
+        return fail(PA_ERR_INVALID_ARG, "bad output arrays");
+    if (num_groups < 0 || (num_groups > 0 && (!group_indptr_host || !prefix_len_host)) ||
+        (batch > 0 && !group_indptr_host))
+        return fail(PA_ERR_INVALID_ARG, "group arrays are null or num_groups < 0");
+    if (max_workgroups <= 0)
+        max_workgroups = pa::kNumCu * pa::kDefaultWorkgroupsPerCu;
+    pa::PartitionArgs a{kv_indptr_host, nullptr, batch, num_qo_heads, num_kv_heads,
+                        head_dim, flags, max_workgroups, pa::kNumXcd};
+    const pa::CascadeArgs c{group_indptr_host, num_groups, prefix_len_host};
+    pa::PartitionResult r;
+    const char *detail = "";
+    pa_status s = pa::cascade_partition(a, c, nullptr, wg_offsets, wg_capacity, units,
+                                        unit_capacity, merges, merge_capacity, prefix_units,
+                                        prefix_capacity, &r, &detail);
+    *n_workgroups = r.n_workgroups;
+    *n_units = r.n_units;
+    *n_merges = r.n_merges;
+    *n_partials = r.n_partials;
+    *n_prefix_units = r.n_prefix_units;
     if (s != PA_OK)
         return fail(s, detail);
     return PA_OK;
@@ -431,7 +632,7 @@ pa_status pa_plan_create(pa_plan_t **out, int32_t max_batch, int64_t max_kv_tota
     p->max_workgroups = p->num_cu * per_cu;
     pa::partition_capacity(max_batch, max_kv_total, max_q_total, num_qo_heads, num_kv_heads,
                            head_dim, p->max_workgroups, p->num_xcd, &p->wg_cap, &p->unit_cap,
-                           &p->merge_cap, &p->partial_rows_cap);
+                           &p->merge_cap, &p->partial_rows_cap, &p->prefix_cap);
     const size_t tbytes = table_bytes(p);
     const size_t part_o_bytes = (size_t)std::max<int64_t>(1, p->partial_rows_cap) * head_dim * sizeof(float);
     const size_t part_lse_bytes = (size_t)std::max<int64_t>(1, p->partial_rows_cap) * sizeof(float);
@@ -485,122 +686,19 @@ void pa_plan_destroy(pa_plan_t *plan) { release(plan); }
 
 pa_status pa_plan(pa_plan_t *p, const int32_t *kv_indptr_host, const int32_t *qo_indptr_host,
                   int32_t batch, uint32_t flags, pa_stream_t stream) {
-    using clock = std::chrono::steady_clock;
-    const clock::time_point t_start = clock::now();
-    if (!p)
-        return fail(PA_ERR_INVALID_ARG, "plan is null");
-    if (batch < 0)
-        return fail(PA_ERR_INVALID_ARG, "batch < 0");
-    if (batch > 0 && !kv_indptr_host)
-        return fail(PA_ERR_INVALID_ARG, "kv_indptr_host is null");
-    if (batch > p->max_batch)
-        return fail(PA_ERR_CAPACITY, "batch above the plan's max_batch");
-    const int64_t kv_total = batch > 0 ? kv_indptr_host[batch] : 0;
-    if (kv_total > p->max_kv_total)
-        return fail(PA_ERR_CAPACITY, "total slot-list length above the plan's max_kv_total");
-    int32_t q_total = 0;
-    if (qo_indptr_host) {
-        q_total = batch > 0 ? qo_indptr_host[batch] : 0;
-        if (q_total > p->max_q_total)
-            return fail(PA_ERR_CAPACITY, "total query rows above the plan's max_q_total");
-    }
-    int dev = -1;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess)
-        return hip_fail(e, "hipGetDevice");
-    if (dev != p->device)
-        return fail(PA_ERR_INVALID_ARG, "current HIP device differs from the plan's device");
+    return plan_impl(p, kv_indptr_host, qo_indptr_host, batch, flags, stream, nullptr);
+}
 
-    const bool auto_decode = !qo_indptr_host &&
-                             ((flags & PA_PLAN_FORCE_SPLITS_MASK) >> PA_PLAN_FORCE_SPLITS_SHIFT) == 0;
-    const bool feedback = (flags & PA_PLAN_SPEED_FEEDBACK) && auto_decode;
-    // the weights of the plans since the last clock copy (they change only
-    // below, when a copy is read, and a copy is started only when none is
-    // pending)
-    if (feedback)
-        std::copy(p->cu_weight.begin(), p->cu_weight.end(), p->interval_weight.begin());
-    if (feedback && p->clock_pending) {
-        const hipError_t before = hipPeekAtLastError();
-        e = hipEventQuery(p->clock_done);
-        if (e == hipSuccess) {
-            p->clock_pending = false;
-            update_cu_weights(p);
-        } else if (e == hipErrorNotReady) {
-            if (before == hipSuccess)
-                (void)hipGetLastError();  // not an error: the copy is still in flight
-        } else {
-            return hip_fail(e, "clock copy");
-        }
-    }
-
-    const int s = p->next_stage;
-    const clock::time_point t_wait = clock::now();
-    if (p->stage_pending[s]) {
-        if ((e = hipEventSynchronize(p->stage_done[s])) != hipSuccess)
-            return hip_fail(e, "waiting for an earlier plan upload");
-        p->stage_pending[s] = false;
-    }
-    const clock::time_point t_waited = clock::now();
-    // partition straight into the staging buffer at capacity offsets, then
-    // pack the three lists together and upload them with one copy
-    char *stage = static_cast<char *>(p->h_stage[s]);
-    int32_t *offsets = reinterpret_cast<int32_t *>(stage);
-    const size_t units_at = offsets_bytes(p->wg_cap);
-    pa_work_unit *units = reinterpret_cast<pa_work_unit *>(stage + units_at);
-    pa_merge_unit *merges = reinterpret_cast<pa_merge_unit *>(stage + units_at + (size_t)p->unit_cap * kUnit);
-    pa::PartitionArgs a{kv_indptr_host, qo_indptr_host, batch, p->num_qo_heads, p->num_kv_heads,
-                        p->head_dim, flags, p->max_workgroups, p->num_xcd,
-                        p->xcd_weighted ? p->xcd_weight : nullptr,
-                        p->wg_weighted ? p->wg_weight.data() : nullptr, p->n_clock};
-    pa::PartitionResult r;
-    const char *detail = "";
-    auto clamp32 = [](int64_t v) { return (int32_t)std::min<int64_t>(v, 0x7fffffff); };
-    pa_status st = pa::partition(a, &p->scratch, offsets, clamp32(p->wg_cap + 1), units,
-                                 clamp32(p->unit_cap),
-                                 merges, clamp32(p->merge_cap), &r, &detail);
-    if (st != PA_OK)
-        return fail(st, detail);
-    const int64_t rows_per_slot = qo_indptr_host ? pa::kPrefillTileRows : p->group;
-    if ((int64_t)r.n_partials * rows_per_slot > p->partial_rows_cap)
-        return fail(PA_ERR_CAPACITY, "partial storage of the plan exceeded");
-    const size_t off_b = offsets_bytes(r.n_workgroups);
-    if (r.n_units > 0)
-        std::memmove(stage + off_b, units, (size_t)r.n_units * kUnit);
-    if (r.n_merges > 0)
-        std::memmove(stage + off_b + (size_t)r.n_units * kUnit, merges, (size_t)r.n_merges * kMerge);
-    const size_t bytes = off_b + (size_t)r.n_units * kUnit + (size_t)r.n_merges * kMerge;
-    if ((e = hipMemcpyAsync(p->d_table, stage, bytes, hipMemcpyHostToDevice,
-                            (hipStream_t)stream)) != hipSuccess)
-        return hip_fail(e, "plan upload");
-    if ((e = hipEventRecord(p->stage_done[s], (hipStream_t)stream)) != hipSuccess)
-        return hip_fail(e, "plan upload event");
-    p->stage_pending[s] = true;
-    p->next_stage = s ^ 1;
-    if (feedback && !p->clock_pending) {
-        // the counters as of the end of the launches enqueued so far: those
-        // since the previous copy all used interval_weight
-        if ((e = hipMemcpyAsync(p->h_wg_clock, p->d_wg_clock,
-                                (size_t)p->n_clock * pa::kClockStride * sizeof(uint64_t),
-                                hipMemcpyDeviceToHost, (hipStream_t)stream)) != hipSuccess ||
-            (e = hipEventRecord(p->clock_done, (hipStream_t)stream)) != hipSuccess)
-            return hip_fail(e, "clock copy");
-        std::copy(p->interval_weight.begin(), p->interval_weight.end(), p->clock_weight.begin());
-        p->clock_pending = true;
-    }
-    // only launches that fill the GPU measure the workgroups' speeds
-    p->clock_record = feedback && r.n_workgroups >= p->max_workgroups &&
-                      r.n_workgroups <= p->n_clock;
-    p->mode = qo_indptr_host ? pa::PlanMode::kPrefill : pa::PlanMode::kDecode;
-    p->batch = batch;
-    p->kv_total = kv_total;
-    p->q_total = q_total;
-    p->n_workgroups = r.n_workgroups;
-    p->n_units = r.n_units;
-    p->n_merges = r.n_merges;
-    p->n_partials = r.n_partials;
-    p->plan_wait_us = std::chrono::duration<double, std::micro>(t_waited - t_wait).count();
-    p->plan_total_us = std::chrono::duration<double, std::micro>(clock::now() - t_start).count();
-    return PA_OK;
+pa_status pa_plan_cascade(pa_plan_t *p, const int32_t *kv_indptr_host, int32_t batch,
+                          const int32_t *group_indptr_host, int32_t num_groups,
+                          const int32_t *prefix_len_host, uint32_t flags, pa_stream_t stream) {
+    if (num_groups < 0 || (num_groups > 0 && (!group_indptr_host || !prefix_len_host)) ||
+        (batch > 0 && !group_indptr_host))
+        return fail(PA_ERR_INVALID_ARG, "group arrays are null or num_groups < 0");
+    if (p && num_groups > std::max(p->max_batch, 1))
+        return fail(PA_ERR_CAPACITY, "more groups than the plan's max_batch");
+    const pa::CascadeArgs c{group_indptr_host, num_groups, prefix_len_host};
+    return plan_impl(p, kv_indptr_host, nullptr, batch, flags, stream, &c);
 }
 
 pa_status pa_kv_append(const void *k_new, const void *v_new, void *q, const int32_t *positions,
@@ -668,6 +766,15 @@ pa_status pa_decode_run(const pa_plan_t *p, const void *q, const void *k_pool, c
     hipError_t e = profile_mark(p, (hipStream_t)stream, false);
     if (e != hipSuccess)
         return hip_fail(e, "profile event");
+    if (p->n_prefix_units > 0) {
+        // cascade: the shared prefixes first; their partials are complete
+        // when the decode kernel's merges read them (same stream)
+        int rc = pa::launch_prefill(prefix_launch(p, l), stream);
+        if (rc == (int)hipErrorNotSupported)
+            return fail(PA_ERR_UNSUPPORTED, "prefill kernel not available in this build");
+        if (rc != 0)
+            return hip_fail((hipError_t)rc, "cascade prefix kernel launch");
+    }
     int rc = pa::launch_decode(l, stream);
     if (rc != 0)
         return hip_fail((hipError_t)rc, "decode kernel launch");
@@ -687,6 +794,8 @@ pa_status pa_decode_run_fp8(const pa_plan_t *p, const void *q, const void *k_poo
         return st;
     if (!std::isfinite(k_scale) || !std::isfinite(v_scale))
         return fail(PA_ERR_INVALID_ARG, "k_scale and v_scale must be finite");
+    if (p->n_prefix_units > 0)
+        return fail(PA_ERR_UNSUPPORTED, "cascade plans are bf16 only");
     l.kv_fp8 = true;
     l.k_scale = k_scale;
     l.v_scale = v_scale;

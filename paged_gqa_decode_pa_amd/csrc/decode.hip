@@ -235,14 +235,14 @@ __device__ __forceinline__ pa_work_unit load_unit(const pa_work_unit *units, int
     pa_work_unit u;
     u.request = w[0]; u.kv_head = w[1]; u.kv_begin = w[2]; u.kv_end = w[3];
     u.q_begin = w[4]; u.q_end = w[5]; u.partial = w[6]; u.diag = w[7];
-    u.merge = w[8]; u.reserved0 = u.reserved1 = u.reserved2 = 0;
+    u.merge = w[8]; u.part_stride = w[9]; u.reserved1 = u.reserved2 = 0;
     return u;
 }
 __device__ __forceinline__ pa_merge_unit load_merge(const pa_merge_unit *merges, int32_t i) {
     const ConstantI32 w = (ConstantI32)(merges + i);
     pa_merge_unit m;
     m.request = w[0]; m.kv_head = w[1]; m.q_begin = w[2]; m.q_end = w[3];
-    m.first_partial = w[4]; m.n_parts = w[5]; m.reserved0 = m.reserved1 = 0;
+    m.first_partial = w[4]; m.n_parts = w[5]; m.prefix_first = w[6]; m.prefix_parts = w[7];
     return m;
 }
 
@@ -343,7 +343,10 @@ __device__ __forceinline__ void merge_rows(const pa_merge_unit &mu, const float 
                                            float *__restrict__ out, float *__restrict__ lse,
                                            int32_t num_qo_heads, int tid, int nthreads) {
     const int32_t rows = (mu.q_end - mu.q_begin) * G;
-    const int32_t n = mu.n_parts;
+    // the parts: slots first_partial .. + n_parts, then (cascade) the prefix
+    // slots prefix_first .. + prefix_parts
+    const int32_t n_own = mu.n_parts, n = mu.n_parts + mu.prefix_parts;
+    const int32_t prefix_shift = mu.prefix_first - n_own;
     for (int32_t idx = tid; idx < rows * D; idx += nthreads) {
         const int32_t row = idx / D, d = idx % D;
         float M = -INFINITY, o = 0.f, wsum = 0.f;
@@ -352,7 +355,8 @@ __device__ __forceinline__ void merge_rows(const pa_merge_unit &mu, const float 
 #pragma unroll
             for (int j = 0; j < kMergeBatch; j++) {
                 const int32_t i = min(i0 + j, n - 1);   // past the end: re-read the last part
-                const int64_t slot_row = (int64_t)(mu.first_partial + i) * rows_per_slot + row;
+                const int32_t slot = i < n_own ? mu.first_partial + i : prefix_shift + i;
+                const int64_t slot_row = (int64_t)slot * rows_per_slot + row;
                 l[j] = COHERENT ? load_coherent(part_lse + slot_row) : part_lse[slot_row];
                 v[j] = COHERENT ? load_coherent(part_o + slot_row * D + d) : part_o[slot_row * D + d];
             }

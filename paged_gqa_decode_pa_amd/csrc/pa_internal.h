@@ -70,13 +70,34 @@ struct PartitionArgs {
     // them weigh 1), multiplied with its XCD's weight
     const float *wg_weights = nullptr;
     int32_t n_wg_weights = 0;
+    // automatic decode: entries at the start of each request's list that its
+    // decode units skip (read by cascade prefix units); nullptr = none
+    const int32_t *kv_skip = nullptr;
 };
+
+// Shared-prefix groups of a cascade decode plan (pa_plan_cascade).
+struct CascadeArgs {
+    const int32_t *group_indptr;   // [num_groups + 1] over requests
+    int32_t num_groups;
+    const int32_t *prefix_len;     // [num_groups]
+};
+
+// Cascade prefix units: a prefix is cut into parts of at least
+// kCascadeMinPartEntries entries, at most kMaxCascadeParts of them, as many as
+// it takes for the prefix units to number about as many as the decode
+// workgroups (they run one per workgroup, and short ones are latency bound).
+constexpr int kCascadeMinPartEntries = 64;
+// Groups with fewer member query rows than this get no prefix units unless
+// PA_PLAN_CASCADE_ALL is set.
+constexpr int kCascadeMinRows = 64;
+constexpr int kMaxCascadeParts = 32;
 
 struct PartitionResult {
     int32_t n_workgroups = 0;  // including empty padding workgroups
     int32_t n_units = 0;
     int32_t n_merges = 0;
-    int32_t n_partials = 0;    // partial slots used
+    int32_t n_partials = 0;    // partial slots used (cascade: decode and prefix slots)
+    int32_t n_prefix_units = 0;   // cascade: prefix units, one workgroup each
 };
 
 // Working arrays of the automatic decode partition, kept by a plan between
@@ -89,6 +110,7 @@ struct PartitionScratch {
     std::vector<int32_t> seg_request, seg_pieces, seg_first, seg_merge, bin_stream;
     std::vector<Piece> stream;
     std::vector<double> bin_cap;   // budget of each bin when weighted
+    std::vector<int32_t> kv_skip;  // cascade: per request, entries of its group's prefix
 };
 
 // Validates the arguments; fills wg_offsets (n_workgroups + 1 entries), units
@@ -100,6 +122,16 @@ pa_status partition(const PartitionArgs &a, PartitionScratch *scratch, int32_t *
                     pa_merge_unit *merges, int32_t merge_capacity, PartitionResult *res,
                     const char **detail);
 
+// Cascade decode partition: the automatic decode split of every list after
+// its group's shared prefix (with a merge for every request that has one),
+// then the prefix units into prefix_units[prefix_capacity]; merges carry the
+// prefix slots.  Returns PA_ERR_CAPACITY if an array is too small.
+pa_status cascade_partition(const PartitionArgs &a, const CascadeArgs &c, PartitionScratch *scratch,
+                            int32_t *wg_offsets, int32_t wg_capacity, pa_work_unit *units,
+                            int32_t unit_capacity, pa_merge_unit *merges, int32_t merge_capacity,
+                            pa_work_unit *prefix_units, int32_t prefix_capacity,
+                            PartitionResult *res, const char **detail);
+
 // Upper bounds on what a plan created with these limits can need: workgroup
 // offsets (entries), work and merge units, and partial storage in rows of
 // head_dim floats (a decode partial slot holds `group` rows, a prefill slot
@@ -107,7 +139,8 @@ pa_status partition(const PartitionArgs &a, PartitionScratch *scratch, int32_t *
 void partition_capacity(int32_t max_batch, int64_t max_kv_total, int32_t max_q_total,
                         int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
                         int32_t max_workgroups, int32_t num_xcd, int64_t *max_wg_entries,
-                        int64_t *max_units, int64_t *max_merges, int64_t *max_partial_rows);
+                        int64_t *max_units, int64_t *max_merges, int64_t *max_partial_rows,
+                        int64_t *max_prefix_units);
 
 bool supported_shape(int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim);
 

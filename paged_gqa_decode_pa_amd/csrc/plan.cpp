@@ -156,11 +156,20 @@ pa_status decode_bins(const PartitionArgs &a, PartitionScratch &ws, int32_t *wg_
     for (int32_t h = 0, s = 0; h < Hkv; h++)
         for (int32_t b = 0; b < B; b++)
             ws.seg_request[s++] = b;
+    // entries a request's decode units skip at the start of its list (the
+    // shared prefix of a cascade plan, read by the prefix units)
+    auto skip_of = [&](int32_t b) { return a.kv_skip ? a.kv_skip[b] : 0; };
     auto seg_len = [&](int64_t s) {
         const int32_t b = ws.seg_request[s];
-        return a.kv_indptr[b + 1] - a.kv_indptr[b];
+        return a.kv_indptr[b + 1] - a.kv_indptr[b] - skip_of(b);
     };
-    const int64_t total = B > 0 ? (int64_t)a.kv_indptr[B] * Hkv : 0;
+    int64_t total = B > 0 ? (int64_t)a.kv_indptr[B] * Hkv : 0;
+    if (a.kv_skip)
+        for (int32_t b = 0; b < B; b++)
+            total -= (int64_t)a.kv_skip[b] * Hkv;
+    // a segment whose request has a cascade prefix always writes a partial:
+    // its merge folds the prefix parts in
+    auto must_merge = [&](int64_t s) { return skip_of(ws.seg_request[s]) > 0; };
     const int64_t max_wg = std::max(1, a.max_workgroups);
     const int64_t n = std::max<int64_t>(1, std::min(max_wg, ceil_div(total, min_unit_tokens(a.head_dim))));
     const double ov = kPieceOverheadTokens;
@@ -254,14 +263,15 @@ pa_status decode_bins(const PartitionArgs &a, PartitionScratch &ws, int32_t *wg_
     // units in (request, head) order
     int32_t np = 0;
     for (int64_t s = 0; s < n_seg; s++) {
-        ws.seg_first[s] = ws.seg_pieces[s] > 1 ? np : -1;
-        np += ws.seg_pieces[s] > 1 ? ws.seg_pieces[s] : 0;
+        const bool merged = ws.seg_pieces[s] > 1 || must_merge(s);
+        ws.seg_first[s] = merged ? np : -1;
+        np += merged ? ws.seg_pieces[s] : 0;
     }
     int32_t n_merges = 0;
     for (int32_t b = 0; b < B; b++)
         for (int32_t h = 0; h < Hkv; h++) {
             const int64_t s = (int64_t)h * B + b;
-            ws.seg_merge[s] = ws.seg_pieces[s] > 1 ? n_merges++ : -1;
+            ws.seg_merge[s] = ws.seg_first[s] >= 0 ? n_merges++ : -1;
         }
 
     const int64_t n_wg = xcd ? per_xcd * a.num_xcd : n;
@@ -294,14 +304,14 @@ pa_status decode_bins(const PartitionArgs &a, PartitionScratch &ws, int32_t *wg_
         const int32_t b = ws.seg_request[seg];
         u.request = b;
         u.kv_head = (seg - b) / B;
-        u.kv_begin = a.kv_indptr[b] + lo;
-        u.kv_end = a.kv_indptr[b] + hi;
+        u.kv_begin = a.kv_indptr[b] + skip_of(b) + lo;
+        u.kv_end = a.kv_indptr[b] + skip_of(b) + hi;
         u.q_begin = b;
         u.q_end = b + 1;
         u.partial = ws.seg_first[seg] >= 0 ? ws.seg_first[seg] + ordinal : -1;
         u.diag = u.kv_end - 1;
         u.merge = ws.seg_merge[seg];
-        u.reserved0 = u.reserved1 = u.reserved2 = 0;
+        u.part_stride = u.reserved1 = u.reserved2 = 0;
     };
     const int64_t stride = xcd ? a.num_xcd : 1;   // workgroup w = k * stride + x
     int32_t pos = 0;
@@ -337,7 +347,8 @@ bool supported_shape(int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_di
 void partition_capacity(int32_t max_batch, int64_t max_kv_total, int32_t max_q_total,
                         int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
                         int32_t max_workgroups, int32_t num_xcd, int64_t *max_wg_entries,
-                        int64_t *max_units, int64_t *max_merges, int64_t *max_partial_rows) {
+                        int64_t *max_units, int64_t *max_merges, int64_t *max_partial_rows,
+                        int64_t *max_prefix_units) {
     const int32_t g = num_qo_heads / num_kv_heads;
     const int64_t segs = (int64_t)num_kv_heads * max_batch;
     // decode, automatic: an opening piece per segment, one more piece where a
@@ -358,7 +369,144 @@ void partition_capacity(int32_t max_batch, int64_t max_kv_total, int32_t max_q_t
     *max_wg_entries = std::max<int64_t>(std::max(1, max_workgroups) + num_xcd,
                                         std::max(dec_forced, pre) * num_xcd) + 1;
     *max_merges = std::max(segs, tiles);
-    *max_partial_rows = std::max(dec * g, (max_q_total > 0) ? pre * kPrefillTileRows : 0);
+    // cascade: at most one subgroup per request, each with up to
+    // kMaxCascadeParts prefix units per KV head and one slot per member,
+    // head and part
+    const int64_t prefix_slots = segs * kMaxCascadeParts;
+    *max_prefix_units = prefix_slots;
+    *max_partial_rows = std::max((dec + prefix_slots) * g, (max_q_total > 0) ? pre * kPrefillTileRows : 0);
+}
+
+pa_status cascade_partition(const PartitionArgs &a, const CascadeArgs &c, PartitionScratch *scratch,
+                            int32_t *wg_offsets, int32_t wg_capacity, pa_work_unit *units,
+                            int32_t unit_capacity, pa_merge_unit *merges, int32_t merge_capacity,
+                            pa_work_unit *prefix_units, int32_t prefix_capacity,
+                            PartitionResult *res, const char **detail) {
+    *res = PartitionResult{};
+    if (a.qo_indptr || forced_splits(a.flags))
+        return fail(detail, "a cascade plan is an automatic decode plan", PA_ERR_INVALID_ARG);
+    if (c.num_groups < 0 || (a.batch > 0 && (!c.group_indptr || !c.prefix_len)))
+        return fail(detail, "group arrays are null or num_groups < 0", PA_ERR_INVALID_ARG);
+    if (c.num_groups > 0 && !c.group_indptr)
+        return fail(detail, "group_indptr is null", PA_ERR_INVALID_ARG);
+    if ((c.num_groups > 0 || a.batch > 0) &&
+        (c.group_indptr[0] != 0 || c.group_indptr[c.num_groups] != a.batch))
+        return fail(detail, "group_indptr must run from 0 to batch", PA_ERR_INVALID_ARG);
+    PartitionScratch local;
+    PartitionScratch &ws = scratch ? *scratch : local;
+    ws.kv_skip.assign(std::max(0, a.batch), 0);
+    // the checks partition() makes, before the lists are read
+    if (a.batch < 0)
+        return fail(detail, "batch < 0", PA_ERR_INVALID_ARG);
+    if (!supported_shape(a.num_qo_heads, a.num_kv_heads, a.head_dim))
+        return fail(detail, "unsupported head shape (need Hq/Hkv in {1,2,4,8}, D in {128,256})",
+                    PA_ERR_UNSUPPORTED);
+    if ((a.flags & ~(PA_PLAN_NO_XCD_ORDER | PA_PLAN_SPEED_FEEDBACK | PA_PLAN_CASCADE_ALL)) != 0)
+        return fail(detail, "unknown flag bits", PA_ERR_INVALID_ARG);
+    if (a.num_xcd < 1 || a.num_xcd > kMaxXcd)
+        return fail(detail, "XCD count out of range", PA_ERR_INVALID_ARG);
+    if (a.batch > 0) {
+        if (!a.kv_indptr)
+            return fail(detail, "kv_indptr is null", PA_ERR_INVALID_ARG);
+        if (a.kv_indptr[0] != 0)
+            return fail(detail, "kv_indptr[0] != 0", PA_ERR_INVALID_ARG);
+        for (int32_t b = 0; b < a.batch; b++)
+            if (a.kv_indptr[b + 1] < a.kv_indptr[b])
+                return fail(detail, "kv_indptr decreases", PA_ERR_INVALID_ARG);
+    }
+    for (int32_t gi = 0; gi < c.num_groups; gi++) {
+        const int32_t b0 = c.group_indptr[gi], b1 = c.group_indptr[gi + 1];
+        if (b1 < b0)
+            return fail(detail, "group_indptr decreases", PA_ERR_INVALID_ARG);
+        const int32_t plen = c.prefix_len[gi];
+        if (plen < 0)
+            return fail(detail, "negative prefix length", PA_ERR_INVALID_ARG);
+        if (plen > 0 && b1 == b0)
+            return fail(detail, "a prefix for an empty group", PA_ERR_INVALID_ARG);
+        for (int32_t b = b0; b < b1; b++)
+            if (plen > a.kv_indptr[b + 1] - a.kv_indptr[b])
+                return fail(detail, "prefix longer than a member's list", PA_ERR_INVALID_ARG);
+    }
+    // the prefixes that get prefix units
+    const int32_t g = a.num_qo_heads / a.num_kv_heads, Hkv = a.num_kv_heads;
+    auto used_prefix = [&](int32_t gi) {
+        const int32_t members = c.group_indptr[gi + 1] - c.group_indptr[gi];
+        const bool big = (int64_t)members * g >= kCascadeMinRows || (a.flags & PA_PLAN_CASCADE_ALL);
+        return big ? c.prefix_len[gi] : 0;
+    };
+    for (int32_t gi = 0; gi < c.num_groups; gi++)
+        for (int32_t b = c.group_indptr[gi]; b < c.group_indptr[gi + 1]; b++)
+            ws.kv_skip[b] = used_prefix(gi);
+    PartitionArgs d = a;
+    d.kv_skip = ws.kv_skip.data();
+    // on PA_ERR_CAPACITY the counts are still wanted: go on counting
+    pa_status st = decode_bins(d, ws, wg_offsets, wg_capacity, units, unit_capacity, merges,
+                               merge_capacity, res, detail);
+    if (st != PA_OK && st != PA_ERR_CAPACITY)
+        return st;
+    const bool decode_fits = st == PA_OK;
+    if (!decode_fits)
+        merge_capacity = 0;   // the merges were not written
+
+    // prefix units: per group, subgroups of up to kPrefillTileRows / g members
+    // (one query tile), per KV head, the prefix cut into K parts; part k of
+    // member t of (subgroup, head) writes slot base + t * K + k
+    const int32_t max_members = kPrefillTileRows / g;
+    int64_t pairs = 0;   // (subgroup, KV head) pairs with a prefix
+    for (int32_t gi = 0; gi < c.num_groups; gi++)
+        if (used_prefix(gi) > 0)
+            pairs += Hkv * ceil_div(c.group_indptr[gi + 1] - c.group_indptr[gi], max_members);
+    const int64_t want_parts = pairs > 0 ? ceil_div(std::max(1, a.max_workgroups), pairs) : 1;
+    int32_t n_prefix = 0, slot = res->n_partials;
+    for (int32_t gi = 0; gi < c.num_groups; gi++) {
+        const int32_t plen = used_prefix(gi);
+        if (plen == 0)
+            continue;
+        const int32_t K = (int32_t)std::max<int64_t>(
+            1, std::min<int64_t>({(int64_t)kMaxCascadeParts, want_parts,
+                                  ceil_div(plen, kCascadeMinPartEntries)}));
+        for (int32_t s0 = c.group_indptr[gi]; s0 < c.group_indptr[gi + 1]; s0 += max_members) {
+            const int32_t m = std::min(max_members, c.group_indptr[gi + 1] - s0);
+            for (int32_t h = 0; h < Hkv; h++) {
+                const int32_t base = slot;
+                slot += m * K;
+                for (int32_t k = 0; k < K; k++) {
+                    const int32_t lo = (int32_t)((int64_t)plen * k / K);
+                    const int32_t hi = (int32_t)((int64_t)plen * (k + 1) / K);
+                    if (n_prefix < prefix_capacity) {
+                        pa_work_unit &u = prefix_units[n_prefix];
+                        u.request = s0;
+                        u.kv_head = h;
+                        u.kv_begin = a.kv_indptr[s0] + lo;
+                        u.kv_end = a.kv_indptr[s0] + hi;
+                        u.q_begin = s0;
+                        u.q_end = s0 + m;
+                        u.partial = base + k;
+                        u.diag = u.kv_end - 1;   // every member row sees the whole part
+                        u.merge = -1;
+                        u.part_stride = K;
+                        u.reserved1 = u.reserved2 = 0;
+                    }
+                    n_prefix++;
+                }
+                for (int32_t t = 0; t < m; t++) {
+                    // with a prefix, every (request, head) segment has a merge
+                    const int32_t mi = ws.seg_merge[(int64_t)h * a.batch + s0 + t];
+                    if (mi >= 0 && mi < merge_capacity) {
+                        merges[mi].prefix_first = base + t * K;
+                        merges[mi].prefix_parts = K;
+                    }
+                }
+            }
+        }
+    }
+    res->n_prefix_units = n_prefix;
+    res->n_partials = slot;
+    if (!decode_fits)
+        return st;
+    if (n_prefix > prefix_capacity)
+        return fail(detail, "plan capacity exceeded (prefix units)", PA_ERR_CAPACITY);
+    return PA_OK;
 }
 
 pa_status partition(const PartitionArgs &a, PartitionScratch *scratch, int32_t *wg_offsets,
@@ -378,7 +526,8 @@ pa_status partition(const PartitionArgs &a, PartitionScratch *scratch, int32_t *
     const int32_t forced = forced_splits(a.flags);
     if (forced > PA_MAX_FORCED_SPLITS)
         return fail(detail, "forced split count above PA_MAX_FORCED_SPLITS", PA_ERR_INVALID_ARG);
-    if ((a.flags & ~(PA_PLAN_FORCE_SPLITS_MASK | PA_PLAN_NO_XCD_ORDER | PA_PLAN_SPEED_FEEDBACK)) != 0)
+    if ((a.flags & ~(PA_PLAN_FORCE_SPLITS_MASK | PA_PLAN_NO_XCD_ORDER | PA_PLAN_SPEED_FEEDBACK |
+                     PA_PLAN_CASCADE_ALL)) != 0)
         return fail(detail, "unknown flag bits", PA_ERR_INVALID_ARG);
     if (a.num_xcd < 1 || a.num_xcd > kMaxXcd)
         return fail(detail, "XCD count out of range", PA_ERR_INVALID_ARG);
@@ -437,7 +586,7 @@ pa_status partition(const PartitionArgs &a, PartitionScratch *scratch, int32_t *
                     x.u.partial = n > 1 ? n_partials++ : -1;
                     x.u.diag = x.u.kv_end - 1;
                     x.u.merge = n > 1 ? (int32_t)merges.size() : -1;
-                    x.u.reserved0 = x.u.reserved1 = x.u.reserved2 = 0;
+                    x.u.part_stride = x.u.reserved1 = x.u.reserved2 = 0;
                     x.part = j;
                     x.tokens = hi - lo;
                     units.push_back(x);
@@ -506,7 +655,7 @@ pa_status partition(const PartitionArgs &a, PartitionScratch *scratch, int32_t *
                         x.u.partial = n > 1 ? n_partials++ : -1;
                         x.u.diag = kv0 + P + t0;
                         x.u.merge = n > 1 ? (int32_t)merges.size() : -1;
-                        x.u.reserved0 = x.u.reserved1 = x.u.reserved2 = 0;
+                        x.u.part_stride = x.u.reserved1 = x.u.reserved2 = 0;
                         x.part = j;
                         x.tokens = (hi - lo) * (t1 - t0);
                         units.push_back(x);

@@ -353,7 +353,12 @@ prefill_kernel(const int32_t *__restrict__ wg_offsets, const pa_work_unit *__res
         } else {
             if (!row_valid)
                 continue;
-            const int64_t prow = (int64_t)unit.partial * kPrefillTileRows + row;
+            // a cascade prefix unit writes query token tt's rows into slot
+            // partial + tt * part_stride (G rows per slot, the decode layout);
+            // other units fill slot `partial` of the tile layout
+            const int64_t prow = unit.part_stride > 0
+                                     ? ((int64_t)unit.partial + (int64_t)tt * unit.part_stride) * G + g
+                                     : (int64_t)unit.partial * kPrefillTileRows + row;
             dst = part_o + prow * D;
             if (half == 0)
                 part_lse[prow] = lse2;

@@ -109,7 +109,7 @@ def test_bad_indptr(bad):
 
 def test_unknown_flag():
     with pytest.raises(pa.PAError):
-        pa.pa_partition(_indptr([5]), None, 32, 8, 128, 0x4)
+        pa.pa_partition(_indptr([5]), None, 32, 8, 128, 0x80)
 
 
 def test_deterministic():

@@ -88,6 +88,12 @@ BATCH64_SHARED_PREFIX = DecodeSpec(
 HEADDIM256_BATCH32 = DecodeSpec(
     "hd256_b32_l1024_16384", batch=32, num_qo_heads=16, num_kv_heads=4, head_dim=256,
     num_slots=400_000, len_lo=1024, len_hi=16384, seed=1003)
+# Not one of the benchmark configurations: one system prompt shared by a whole
+# batch, the case a cascade plan (shared prefix read once) is made for.
+SYSTEM_PROMPT_B64 = DecodeSpec(
+    "b64_system_prompt4096_suffix256_2048", batch=64, num_qo_heads=32, num_kv_heads=8,
+    head_dim=128, num_slots=250_000, len_lo=4096 + 256, len_hi=4096 + 2048, seed=1006,
+    prefix_group_size=64, prefix_len=4096, num_layers=36)
 PREFILL_CHUNK512 = PrefillSpec(
     "prefill_8x4096_chunk512", batch=8, num_qo_heads=32, num_kv_heads=8, head_dim=128,
     num_slots=131072, cached_len=4096, chunk_len=512, seed=1004)
