@@ -174,7 +174,7 @@ pa_status pa_plan(pa_plan_t *plan, const int32_t *kv_indptr_host,
  *     member list.
  * pa_decode_run under this plan launches two kernels: the prefix units
  * (matrix-core attention of all member query rows over the shared prefix,
- * at most 128 / (Hq/Hkv) requests per unit, the prefix cut into up to 32
+ * at most 128 / (Hq/Hkv) requests per unit, the prefix cut into up to 16
  * parts) writing partial results, then the decode kernel over the rest of
  * every list, whose merges fold the prefix partials in.  The result equals
  * pa_decode_run under pa_plan up to summation order.  Groups with

@@ -90,7 +90,7 @@ constexpr int kCascadeMinPartEntries = 64;
 // Groups with fewer member query rows than this get no prefix units unless
 // PA_PLAN_CASCADE_ALL is set.
 constexpr int kCascadeMinRows = 64;
-constexpr int kMaxCascadeParts = 32;
+constexpr int kMaxCascadeParts = 16;
 
 struct PartitionResult {
     int32_t n_workgroups = 0;  // including empty padding workgroups

@@ -11,7 +11,7 @@ import pytest
 import paged_gqa_decode_pa_amd as pa
 import workloads as W
 
-MAX_PARTS = 32
+MAX_PARTS = 16
 
 
 def _indptr(lengths):
@@ -113,7 +113,7 @@ def test_system_prompt_groups():
     gi = np.array([0, 64], np.int32)
     pl = np.array([4096], np.int32)
     offs, units, merges, n_p, pre = check_cascade(ip, gi, pl, 32, 8, max_wg=768)
-    assert pre.size == 2 * 8 * 32       # subgroups of 32, 32 parts of 128 entries
+    assert pre.size == 2 * 8 * 16       # subgroups of 32, 16 parts of 256 entries
 
 
 @pytest.mark.parametrize("seed", range(10))
