@@ -60,12 +60,16 @@ constexpr int kWaves = 4;
 template <int D>
 struct PrefillGeo {
     static constexpr int KT = D == 128 ? 64 : 32;     // list entries per tile
-    // LDS row pitches.  K rows are read 16 bytes per lane down a column of
-    // rows; a 16-byte pad moves each row by 4 banks.  V rows are read by the
-    // transposing read, 8 bytes per lane, 4 rows x 32 bytes per 16 lanes; a
-    // 32-byte pad moves each row by 8 banks.
+    // LDS row pitches (64 banks of 4 bytes).  K rows are read 16 bytes per
+    // lane down a column of rows; a 16-byte pad moves each row by 4 banks, so
+    // 16 consecutive rows hit distinct banks.  V rows are read by the
+    // transposing read, 8 bytes per lane, 4 rows x 32 bytes per 16 lanes and
+    // two column blocks per 32 lanes; a 64-byte pad moves each row by 16
+    // banks, so the 32 lanes of a read cycle hit 64 distinct banks (a 32-byte
+    // pad left 25% of the LDS cycles in bank conflicts, rocprofv3
+    // SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE; this one none).
     static constexpr int KROW = D * 2 + 16;
-    static constexpr int VROW = D * 2 + 32;
+    static constexpr int VROW = D * 2 + 64;
     static constexpr int STAGE = KT * (KROW + VROW);  // one buffer: K tile then V tile
     static constexpr int TPR = D / 8;                  // staging threads per row (16 B each)
     static constexpr int RPP = kThreads / TPR;         // rows per staging pass
