@@ -62,3 +62,17 @@ def test_null_plan_rejected():
         == pa.PA_ERR_INVALID_ARG
     assert pa._lib.pa_plan(null, None, None, 0, 0, None) == pa.PA_ERR_INVALID_ARG
     pa.pa_plan_destroy(null)  # no-op
+
+
+@pytest.mark.parametrize("lang,std", [("c", "c99"), ("c++", "c++17")])
+def test_header_compiles_standalone(lang, std, tmp_path):
+    """include/pa.h is a plain C header: it compiles on its own, warning-free,
+    as C99 and as C++17 (no HIP or torch types in the signatures)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc" if lang == "c" else "g++")
+    if cc is None:
+        pytest.skip("no host compiler")
+    r = subprocess.run([cc, "-fsyntax-only", "-x", lang, f"-std={std}", "-Wall", "-Wextra",
+                        "-pedantic", "-Werror", HEADER], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
