@@ -251,6 +251,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t index_rsrc(const int32_t *p, i
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t *>(p), (short)0, n * 4, kBufferWord3);
 }
 
+// Load of a gathered K or V row, marked non-temporal (the instruction's nt
+// bit: the L2 keeps the line at the eviction end of its set).  A pool row is
+// read once per launch, or by a prefix group's few requests at about the
+// same moment; marking the stream keeps it from evicting the lines that are
+// still in use (slot ids, shared-prefix rows, partials).  Measured on the
+// batch-64 workload: 195.9-199.5 us per layer against 205.5-208.4 us with
+// ordinary loads.
+template <typename T>
+__device__ __forceinline__ T load_streamed(const T *p) {
+    typedef unsigned int V __attribute__((ext_vector_type(sizeof(T) / 4)));
+    return __builtin_bit_cast(T, __builtin_nontemporal_load(reinterpret_cast<const V *>(p)));
+}
+
 template <int D>
 struct Geometry {
     static constexpr int LPR = D / 8;          // lanes per row
@@ -510,12 +523,12 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<G>(), 8))) void decode_
     auto load_k = [&](Row(&k)[NI], const int32_t(&slot)[NI]) {
 #pragma unroll
         for (int i = 0; i < NI; i++)
-            k[i] = *reinterpret_cast<const Row *>(RowAddr<WIDE>::at(k_pool, slot[i], stride_bytes, lane_off));
+            k[i] = load_streamed(reinterpret_cast<const Row *>(RowAddr<WIDE>::at(k_pool, slot[i], stride_bytes, lane_off)));
     };
     auto load_v = [&](Row(&v)[NI], const int32_t(&slot)[NI]) {
 #pragma unroll
         for (int i = 0; i < NI; i++)
-            v[i] = *reinterpret_cast<const Row *>(RowAddr<WIDE>::at(v_pool, slot[i], stride_bytes, lane_off));
+            v[i] = load_streamed(reinterpret_cast<const Row *>(RowAddr<WIDE>::at(v_pool, slot[i], stride_bytes, lane_off)));
     };
     // scores of this lane's head (lane % G) for the tile's tokens, log2 domain
     auto qk = [&](const Row(&k)[NI], float(&s)[NI], int tile) {
