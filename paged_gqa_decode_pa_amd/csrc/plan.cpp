@@ -369,11 +369,15 @@ void partition_capacity(int32_t max_batch, int64_t max_kv_total, int32_t max_q_t
     *max_wg_entries = std::max<int64_t>(std::max(1, max_workgroups) + num_xcd,
                                         std::max(dec_forced, pre) * num_xcd) + 1;
     *max_merges = std::max(segs, tiles);
-    // cascade: at most one subgroup per request, each with up to
-    // kMaxCascadeParts prefix units per KV head and one slot per member,
-    // head and part
-    const int64_t prefix_slots = segs * kMaxCascadeParts;
-    *max_prefix_units = prefix_slots;
+    // cascade: a (subgroup, KV head) pair has K prefix units and K slots per
+    // member, K <= kMaxCascadeParts, and K > 1 only while the pairs number
+    // fewer than the decode workgroups (K <= ceil(max_workgroups / pairs)):
+    // so at most max(pairs, 2 * max_workgroups) units and max(segments,
+    // 2 * (members per pair) * max_workgroups) slots, pairs <= segments
+    const int64_t max_wg = std::max(1, max_workgroups);
+    const int64_t prefix_slots =
+        std::max(segs, std::min<int64_t>(segs * kMaxCascadeParts, 2 * (int64_t)(kPrefillTileRows / g) * max_wg));
+    *max_prefix_units = std::max(segs, std::min<int64_t>(segs * kMaxCascadeParts, 2 * max_wg));
     *max_partial_rows = std::max((dec + prefix_slots) * g, (max_q_total > 0) ? pre * kPrefillTileRows : 0);
 }
 

@@ -203,3 +203,22 @@ def test_graph_replay():
             graph.replay()
             torch.cuda.synchronize()
             assert torch.equal(out, eager)
+
+
+@pytest.mark.parametrize("layout", ["singletons", "one_big_group"])
+def test_capacity_extremes(layout):
+    """The most prefix units or slots a plan has to hold: 64 one-request groups
+    (pairs < workgroups, two parts each) and one group of 128 requests (four
+    subgroups, 16 parts each: exactly the reserved slots)."""
+    import paged_gqa_decode_pa_amd as pa
+    say(f"cascade capacity {layout}")
+    if layout == "singletons":
+        lengths, gsize, plen = [700 + 13 * i for i in range(64)], 1, 600
+    else:
+        lengths, gsize, plen = [1200 + 7 * i for i in range(128)], 128, 1100
+    ip, idx, q, k, v = _case(lengths, gsize, plen, 32, 8, 128, 200000, seed=len(lengths))
+    gi = _groups(len(lengths), gsize)
+    pl = np.full(gi.size - 1, plen, np.int32)
+    Hq = 32
+    sel = [b * Hq + h for b in range(0, len(lengths), 9) for h in (0, 17, 31)]
+    _check(ip, idx, q, k, v, 8, gi, pl, sel=sel)

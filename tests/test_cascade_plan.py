@@ -174,3 +174,26 @@ def test_forced_splits_rejected():
     with pytest.raises(pa.PAError):
         pa.pa_partition_cascade(ip, np.array([0, 2], np.int32), np.array([50], np.int32), 32, 8,
                                 128, pa.PA_PLAN_FORCE_SPLITS(2))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_prefix_counts_within_plan_capacity(seed):
+    """The prefix units and slots of any cascade partition stay within what a
+    plan reserves: units <= max(segments, min(16*segments, 2*W)) and slots <=
+    max(segments, min(16*segments, 2*(128/g)*W)), W = decode workgroups."""
+    rng = np.random.default_rng(500 + seed)
+    Hq, Hkv = [(32, 8), (64, 8), (16, 4), (8, 8)][seed % 4]
+    g = Hq // Hkv
+    B = int(rng.integers(1, 200))
+    lengths = rng.integers(64, 3000, size=B)
+    cuts = sorted(set(rng.integers(1, B, size=int(rng.integers(0, max(1, B // 3)))).tolist()) | {0, B})
+    gi = np.array(cuts, np.int32)
+    pl = np.array([int(lengths[gi[k]:gi[k + 1]].min()) for k in range(gi.size - 1)], np.int32)
+    W = 768
+    offs, units, merges, n_p, pre = pa.pa_partition_cascade(ip := _indptr(lengths), gi, pl, Hq, Hkv,
+                                                            128, pa.PA_PLAN_CASCADE_ALL, W)
+    segs = B * Hkv
+    decode_slots = sum(int(m["n_parts"]) for m in merges)
+    prefix_slots = n_p - decode_slots
+    assert pre.size <= max(segs, min(16 * segs, 2 * W))
+    assert prefix_slots <= max(segs, min(16 * segs, 2 * (128 // g) * W))
