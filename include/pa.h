@@ -259,6 +259,10 @@ const char *pa_last_error_detail(void);
  * units of a cascade plan, see pa_plan_cascade): query row q_begin + t of the
  * unit writes partial slot partial + t * part_stride; 0 for every other unit
  * (a prefill unit's rows then fill slot `partial` of the prefill layout).
+ * cached_end (decode units): list entries before this absolute offset are
+ * read with ordinary loads that stay in the L2 for other requests (the shared
+ * prefix of a small group in a cascade plan); the rest are streamed
+ * (non-temporal loads).  0 in every other unit.
  *
  * pa_merge_unit: the partial slots [first_partial, first_partial + n_parts)
  * that make up query rows [q_begin, q_end) of KV head kv_head, plus, in a
@@ -278,7 +282,7 @@ typedef struct pa_work_unit {
     int32_t diag;
     int32_t merge;
     int32_t part_stride;
-    int32_t reserved1;
+    int32_t cached_end;
     int32_t reserved2;
 } pa_work_unit;
 

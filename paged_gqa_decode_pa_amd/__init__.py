@@ -44,7 +44,7 @@ def PA_PLAN_FORCE_SPLITS(n: int) -> int:
 class pa_work_unit(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("request", "kv_head", "kv_begin", "kv_end", "q_begin", "q_end", "partial", "diag",
-                 "merge", "part_stride", "reserved1", "reserved2")]
+                 "merge", "part_stride", "cached_end", "reserved2")]
 
 
 class pa_merge_unit(ctypes.Structure):

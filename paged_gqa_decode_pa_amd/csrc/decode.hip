@@ -53,6 +53,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "pa_internal.h"
 
 namespace pa {
@@ -235,7 +237,7 @@ __device__ __forceinline__ pa_work_unit load_unit(const pa_work_unit *units, int
     pa_work_unit u;
     u.request = w[0]; u.kv_head = w[1]; u.kv_begin = w[2]; u.kv_end = w[3];
     u.q_begin = w[4]; u.q_end = w[5]; u.partial = w[6]; u.diag = w[7];
-    u.merge = w[8]; u.part_stride = w[9]; u.reserved1 = u.reserved2 = 0;
+    u.merge = w[8]; u.part_stride = w[9]; u.cached_end = w[10]; u.reserved2 = 0;
     return u;
 }
 __device__ __forceinline__ pa_merge_unit load_merge(const pa_merge_unit *merges, int32_t i) {
@@ -520,15 +522,17 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<G>(), 8))) void decode_
             slot[i] = __builtin_amdgcn_raw_buffer_load_b32(
                 slot_rsrc, min(e4, last4 - i * RPI * 4) + i * RPI * 4, 0, 0);
     };
-    auto load_k = [&](Row(&k)[NI], const int32_t(&slot)[NI]) {
+    // rows of the streamed range: non-temporal; of the cached range (a shared
+    // prefix other requests read too): ordinary loads
+    auto load_rows = [&](auto stream, Row(&x)[NI], const char *pool, const int32_t(&slot)[NI]) {
 #pragma unroll
-        for (int i = 0; i < NI; i++)
-            k[i] = load_streamed(reinterpret_cast<const Row *>(RowAddr<WIDE>::at(k_pool, slot[i], stride_bytes, lane_off)));
-    };
-    auto load_v = [&](Row(&v)[NI], const int32_t(&slot)[NI]) {
-#pragma unroll
-        for (int i = 0; i < NI; i++)
-            v[i] = load_streamed(reinterpret_cast<const Row *>(RowAddr<WIDE>::at(v_pool, slot[i], stride_bytes, lane_off)));
+        for (int i = 0; i < NI; i++) {
+            const Row *p = reinterpret_cast<const Row *>(RowAddr<WIDE>::at(pool, slot[i], stride_bytes, lane_off));
+            if constexpr (decltype(stream)::value)
+                x[i] = load_streamed(p);
+            else
+                x[i] = *p;
+        }
     };
     // scores of this lane's head (lane % G) for the tile's tokens, log2 domain
     auto qk = [&](const Row(&k)[NI], float(&s)[NI], int tile) {
@@ -588,18 +592,25 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<G>(), 8))) void decode_
     // tiles ahead of their rows.  Every load is unconditional (slot ids of
     // tiles past the end are clamped to the last entry and re-read one row),
     // so each set is refilled in place.
-    int tile = wave;
-    if (tile < n_tiles) {
+    // The wave's tiles t_first, t_first + WAVES, ... below t_end, in the same
+    // order in either range.  The look-ahead runs two tiles past t_end: in
+    // the cached range those are the streamed range's first tiles (which
+    // then find them in the L2), past the unit's end the slot ids clamp to
+    // its last entry.
+    auto run_tiles = [&](auto stream, int tile, int t_end) {
+        if (tile >= t_end)
+            return;
+        auto ahead = [](int t) { return t; };
         int32_t sa[NI], sb[NI];
         Row ka[NI], va[NI], kb[NI], vb[NI];
         load_slots(sa, tile);
-        load_slots(sb, tile + WAVES);
-        load_k(ka, sa);
-        load_v(va, sa);
-        load_k(kb, sb);
-        load_v(vb, sb);
-        load_slots(sa, tile + 2 * WAVES);
-        load_slots(sb, tile + 3 * WAVES);
+        load_slots(sb, ahead(tile + WAVES));
+        load_rows(stream, ka, k_pool, sa);
+        load_rows(stream, va, v_pool, sa);
+        load_rows(stream, kb, k_pool, sb);
+        load_rows(stream, vb, v_pool, sb);
+        load_slots(sa, ahead(tile + 2 * WAVES));
+        load_slots(sb, ahead(tile + 3 * WAVES));
         auto compute = [&](const Row(&k)[NI], const Row(&v)[NI]) {
             float sc[NI], pw[NI];
             qk(k, sc, tile);
@@ -611,21 +622,32 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<G>(), 8))) void decode_
             compute(ka, va);
             // refills stay behind the last use of the registers they overwrite
             __builtin_amdgcn_sched_barrier(0);
-            load_k(ka, sa);
-            load_v(va, sa);
-            load_slots(sa, tile + 4 * WAVES);
+            load_rows(stream, ka, k_pool, sa);
+            load_rows(stream, va, v_pool, sa);
+            load_slots(sa, ahead(tile + 4 * WAVES));
             tile += WAVES;
-            if (tile >= n_tiles)
+            if (tile >= t_end)
                 break;
             compute(kb, vb);
             __builtin_amdgcn_sched_barrier(0);
-            load_k(kb, sb);
-            load_v(vb, sb);
-            load_slots(sb, tile + 4 * WAVES);
+            load_rows(stream, kb, k_pool, sb);
+            load_rows(stream, vb, v_pool, sb);
+            load_slots(sb, ahead(tile + 4 * WAVES));
             tile += WAVES;
-            if (tile >= n_tiles)
+            if (tile >= t_end)
                 break;
         }
+    };
+    // tiles that hold entries before cached_end: cached loads; the rest streamed
+    const int32_t n_cached =
+        unit.cached_end > kv_begin ? min(n_tiles, (unit.cached_end - kv_begin + TILE - 1) / TILE) : 0;
+    if (n_cached > 0) {
+        run_tiles(std::false_type{}, wave, n_cached);
+        // the wave's first tile of the streamed range
+        const int first = wave + (n_cached - wave + WAVES - 1) / WAVES * WAVES;
+        run_tiles(std::true_type{}, first, n_tiles);
+    } else {
+        run_tiles(std::true_type{}, wave, n_tiles);
     }
 
     // ---- combine the rows of this wave (same head: lanes with equal lane % G)

@@ -73,6 +73,10 @@ struct PartitionArgs {
     // automatic decode: entries at the start of each request's list that its
     // decode units skip (read by cascade prefix units); nullptr = none
     const int32_t *kv_skip = nullptr;
+    // automatic decode: entries at the start of each request's list that its
+    // decode units read with cached loads (a shared prefix left to the L2);
+    // nullptr = none
+    const int32_t *kv_cached = nullptr;
 };
 
 // Shared-prefix groups of a cascade decode plan (pa_plan_cascade).
@@ -111,6 +115,7 @@ struct PartitionScratch {
     std::vector<Piece> stream;
     std::vector<double> bin_cap;   // budget of each bin when weighted
     std::vector<int32_t> kv_skip;  // cascade: per request, entries of its group's prefix
+    std::vector<int32_t> kv_cached;  // cascade: per request, shared entries read cached
 };
 
 // Validates the arguments; fills wg_offsets (n_workgroups + 1 entries), units

@@ -311,7 +311,8 @@ pa_status decode_bins(const PartitionArgs &a, PartitionScratch &ws, int32_t *wg_
         u.partial = ws.seg_first[seg] >= 0 ? ws.seg_first[seg] + ordinal : -1;
         u.diag = u.kv_end - 1;
         u.merge = ws.seg_merge[seg];
-        u.part_stride = u.reserved1 = u.reserved2 = 0;
+        u.part_stride = u.reserved2 = 0;
+        u.cached_end = a.kv_cached && a.kv_cached[b] > 0 ? a.kv_indptr[b] + a.kv_cached[b] : 0;
     };
     const int64_t stride = xcd ? a.num_xcd : 1;   // workgroup w = k * stride + x
     int32_t pos = 0;
@@ -438,11 +439,20 @@ pa_status cascade_partition(const PartitionArgs &a, const CascadeArgs &c, Partit
         const bool big = (int64_t)members * g >= kCascadeMinRows || (a.flags & PA_PLAN_CASCADE_ALL);
         return big ? c.prefix_len[gi] : 0;
     };
-    for (int32_t gi = 0; gi < c.num_groups; gi++)
-        for (int32_t b = c.group_indptr[gi]; b < c.group_indptr[gi + 1]; b++)
+    // a shared prefix without prefix units is left to the L2: its members'
+    // decode units read it with cached loads (they stream everything else)
+    ws.kv_cached.assign(std::max(0, a.batch), 0);
+    for (int32_t gi = 0; gi < c.num_groups; gi++) {
+        const int32_t members = c.group_indptr[gi + 1] - c.group_indptr[gi];
+        const bool shared_in_l2 = used_prefix(gi) == 0 && members > 1;
+        for (int32_t b = c.group_indptr[gi]; b < c.group_indptr[gi + 1]; b++) {
             ws.kv_skip[b] = used_prefix(gi);
+            ws.kv_cached[b] = shared_in_l2 ? c.prefix_len[gi] : 0;
+        }
+    }
     PartitionArgs d = a;
     d.kv_skip = ws.kv_skip.data();
+    d.kv_cached = ws.kv_cached.data();
     // on PA_ERR_CAPACITY the counts are still wanted: go on counting
     pa_status st = decode_bins(d, ws, wg_offsets, wg_capacity, units, unit_capacity, merges,
                                merge_capacity, res, detail);
@@ -489,7 +499,7 @@ pa_status cascade_partition(const PartitionArgs &a, const CascadeArgs &c, Partit
                         u.diag = u.kv_end - 1;   // every member row sees the whole part
                         u.merge = -1;
                         u.part_stride = K;
-                        u.reserved1 = u.reserved2 = 0;
+                        u.cached_end = u.reserved2 = 0;
                     }
                     n_prefix++;
                 }
@@ -590,7 +600,7 @@ pa_status partition(const PartitionArgs &a, PartitionScratch *scratch, int32_t *
                     x.u.partial = n > 1 ? n_partials++ : -1;
                     x.u.diag = x.u.kv_end - 1;
                     x.u.merge = n > 1 ? (int32_t)merges.size() : -1;
-                    x.u.part_stride = x.u.reserved1 = x.u.reserved2 = 0;
+                    x.u.part_stride = x.u.cached_end = x.u.reserved2 = 0;
                     x.part = j;
                     x.tokens = hi - lo;
                     units.push_back(x);
@@ -659,7 +669,7 @@ pa_status partition(const PartitionArgs &a, PartitionScratch *scratch, int32_t *
                         x.u.partial = n > 1 ? n_partials++ : -1;
                         x.u.diag = kv0 + P + t0;
                         x.u.merge = n > 1 ? (int32_t)merges.size() : -1;
-                        x.u.part_stride = x.u.reserved1 = x.u.reserved2 = 0;
+                        x.u.part_stride = x.u.cached_end = x.u.reserved2 = 0;
                         x.part = j;
                         x.tokens = (hi - lo) * (t1 - t0);
                         units.push_back(x);

@@ -25,17 +25,23 @@ def check_cascade(ip, gi, pl, Hq, Hkv, flags=0, max_wg=0):
     B, g = ip.size - 1, Hq // Hkv
     assert offs[0] == 0 and offs[-1] == units.size
     skip = np.zeros(B, np.int64)
+    cached = np.zeros(B, np.int64)
     for k in range(gi.size - 1):
         # groups with fewer than 64 member query rows get no prefix units
-        # unless every group is asked for
-        if (gi[k + 1] - gi[k]) * g >= 64 or flags & pa.PA_PLAN_CASCADE_ALL:
+        # unless every group is asked for; their shared prefix is read with
+        # cached loads instead (when there is someone to share it with)
+        members = gi[k + 1] - gi[k]
+        if members * g >= 64 or flags & pa.PA_PLAN_CASCADE_ALL:
             skip[gi[k]:gi[k + 1]] = pl[k]
+        elif members > 1:
+            cached[gi[k]:gi[k + 1]] = pl[k]
     written = defaultdict(int)          # partial slot -> times written
     # decode units: the list after the prefix, in order, once
     by_seg = defaultdict(list)
     for u in units:
         b, h = int(u["request"]), int(u["kv_head"])
         assert u["part_stride"] == 0 and (u["q_begin"], u["q_end"]) == (b, b + 1)
+        assert u["cached_end"] == (ip[b] + cached[b] if cached[b] > 0 else 0)
         by_seg[(b, h)].append(u)
     merge_of = {(int(m["request"]), int(m["kv_head"])): m for m in merges}
     assert len(merge_of) == merges.size
@@ -101,7 +107,12 @@ def test_batch64_groups():
     offs, units, merges, n_p, pre = check_cascade(ip, gi, pl, 32, 8, max_wg=768)
     assert pre.size == 0
     plain = pa.pa_partition(ip, None, 32, 8, 128, 0, 768)
-    assert all(np.array_equal(x, y) for x, y in zip(plain[:3], (offs, units, merges)))
+    # the same split; only the prefix entries are marked for cached loads
+    assert np.array_equal(plain[0], offs) and np.array_equal(plain[2], merges)
+    fields = [f for f in units.dtype.names if f != "cached_end"]
+    assert all(np.array_equal(plain[1][f], units[f]) for f in fields)
+    assert np.all(plain[1]["cached_end"] == 0)
+    assert np.all(units["cached_end"] == ip[units["request"]] + 1024)
     # ... unless every group is asked for
     offs, units, merges, n_p, pre = check_cascade(ip, gi, pl, 32, 8, pa.PA_PLAN_CASCADE_ALL, 768)
     assert pre.size == 16 * 8 * 6       # 1024 entries in 6 parts: ~768 prefix units
@@ -151,6 +162,7 @@ def test_no_prefix_is_plain_decode():
     a = pa.pa_partition(ip, None, 32, 8, 128)
     b = pa.pa_partition_cascade(ip, gi, np.zeros(2, np.int32), 32, 8, 128)
     assert all(np.array_equal(x, y) for x, y in zip(a[:3], b[:3])) and a[3] == b[3]
+    assert np.all(b[1]["cached_end"] == 0)
     assert b[4].size == 0
 
 
