@@ -116,9 +116,11 @@ typedef enum pa_status {
 #define PA_PLAN_SPEED_FEEDBACK 0x2u
 /* pa_plan_cascade: give every group with a prefix its prefix units.  Without
  * it, groups whose member query rows (members x Hq/Hkv) number fewer than 64
- * are decoded as if they had no prefix: their members read the shared slots
- * at the same moment and share them through the L2 cache, which measured
- * faster than a separate prefix pass over so few rows. */
+ * get no prefix units: the plain split decodes their lists, the members read
+ * the shared slots at the same moment, and those rows are loaded so that
+ * they stay in the L2 cache for the other members (every other row is
+ * streamed), which measured faster than a separate prefix pass over so few
+ * rows. */
 #define PA_PLAN_CASCADE_ALL 0x4u
 
 /* Largest max_kv_total a plan accepts: list entries are addressed with 32-bit
