@@ -102,21 +102,29 @@ def run_copy(gib: float, steps: int):
     log(f"copy {gib} GiB: {dt * 1e3:.3f} ms, {2 * n * 4 / dt / 1e9:.1f} GB/s (read+write)")
 
 
-def cpu_baseline(case, spec, bytes_per_layer, seconds, gpu_out_layer0):
+def cpu_baseline(case, spec, bytes_per_layer, seconds, gpu_out_layer0, fp8=False):
     import numpy as np
 
     import oracle
     import workloads as W
     ref = oracle.load()
     qb = W.bits(case.q)
-    kb = W.bits(case.k_pools[0])
-    vb = W.bits(case.v_pools[0])
+    if fp8:   # E4M3 code pools, widened by the oracle inside the timed loop
+        kc = W.codes(case.k_pools[0])
+        vc = W.codes(case.v_pools[0])
+    else:
+        kb = W.bits(case.k_pools[0])
+        vb = W.bits(case.v_pools[0])
     reps = 0
     t0 = time.perf_counter()
     out = None
     while True:
-        out, _ = ref.decode(qb, kb, vb, case.kv_indptr, case.kv_indices, case.sm_scale,
-                            spec.num_kv_heads)
+        if fp8:
+            out, _ = ref.decode_fp8(qb, kc, vc, case.kv_indptr, case.kv_indices, case.sm_scale,
+                                    W.FP8_K_SCALE, W.FP8_V_SCALE, spec.num_kv_heads)
+        else:
+            out, _ = ref.decode(qb, kb, vb, case.kv_indptr, case.kv_indices, case.sm_scale,
+                                spec.num_kv_heads)
         reps += 1
         if time.perf_counter() - t0 >= seconds:
             break
@@ -129,7 +137,8 @@ def cpu_baseline(case, spec, bytes_per_layer, seconds, gpu_out_layer0):
         "kind": "oracle",
         "us_per_layer": round(dt / reps * 1e6, 1),
         "sample": f"layer 0 of the same workload, all {spec.batch}x{spec.num_qo_heads} rows, "
-                  f"{reps} repetition(s), {dt:.1f} s",
+                  f"{reps} repetition(s), {dt:.1f} s"
+                  + (" (each widening the whole E4M3 pools first)" if fp8 else ""),
     }, err
 
 
@@ -328,6 +337,10 @@ def run_append_bench(args):
     us = start.elapsed_time(end) * 1e3 / (args.steps * layers)
     moved = 2 * (2 * T * Hkv * D * 2 + T * Hq * D * 2) + 2 * T * 4   # K, V, Q read + written; ids
     log(f"append: {us:.2f} us per call ({moved / (us * 1e-6) / 1e9:.1f} GB/s)")
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_append(k_new, v_new, q, loc, pos, N, args.cpu_seconds)
+        log(f"cpu baseline {cpu['value']} us per call on {cpu['cores']} threads")
     print(json.dumps({
         "metric": "append + RoPE µs per layer call, batch-64 decode step", "value": round(us, 3),
         "unit": "us", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -338,7 +351,37 @@ def run_append_bench(args):
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(moved / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 5), "traffic": None,
                      "kernel": "append_kernel (pa_kv_append)"},
+        "cpu_baseline": cpu,
     }), flush=True)
+
+
+def cpu_baseline_append(k_new, v_new, q, loc, pos, num_slots, seconds):
+    """The oracle's RoPE of the call's K and query rows, and the K and V rows
+    stored at their slots of host pools (float64, allocated lazily)."""
+    import numpy as np
+
+    import oracle
+    import workloads as W
+    ref = oracle.load()
+    kb, vb, qb = W.bits(k_new), W.bits(v_new), W.bits(q)
+    slots = loc.cpu().numpy()
+    positions = pos.cpu().numpy()
+    T, Hkv, D = kb.shape
+    k_pool = np.zeros((num_slots, Hkv, D))
+    v_pool = np.zeros((num_slots, Hkv, D))
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        k_pool[slots] = ref.rope(kb, positions, 1e6)
+        v_pool[slots] = (vb.astype(np.uint32) << 16).view(np.float32)   # V rows as they are
+        ref.rope(qb, positions, 1e6)
+        reps += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(dt / reps * 1e6, 2), "unit": "us", "cores": ref.num_threads(), "kind": "oracle",
+            "sample": f"one call of the same shape ({T} tokens, {q.shape[1]} query and {Hkv} KV heads, "
+                      f"D={D}), {reps} repetitions, {dt:.1f} s"}
 
 
 def main():
@@ -579,10 +622,11 @@ def main():
         },
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline and not fp8:
+    if not args.no_cpu_baseline:
         log(f"cpu baseline: fp64 oracle on layer 0 for ~{args.cpu_seconds:.0f} s")
         torch.cuda.synchronize()
-        cpu, err = cpu_baseline(case, spec, bytes_per_layer, args.cpu_seconds, outs[0].cpu().numpy())
+        cpu, err = cpu_baseline(case, spec, bytes_per_layer, args.cpu_seconds, outs[0].cpu().numpy(),
+                                fp8=fp8)
         result["cpu_baseline"] = cpu
         result["parity_layer0_max_abs_err"] = err
         log(f"cpu baseline {cpu['value']} GB/s on {cpu['cores']} threads; layer-0 max|d| {err:.3g}")

@@ -291,6 +291,11 @@ def bits(t: "torch.Tensor") -> np.ndarray:
     return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
+def codes(t: "torch.Tensor") -> np.ndarray:
+    """uint8 codes of an 8-bit (E4M3) tensor, on the host."""
+    return t.detach().contiguous().view(torch.uint8).cpu().numpy()
+
+
 def poison_unreferenced(pool: "torch.Tensor", kv_indices) -> None:
     """Write NaN into every slot of ``pool`` that no list references."""
     idx = torch.as_tensor(np.asarray(kv_indices, dtype=np.int64), device=pool.device)
