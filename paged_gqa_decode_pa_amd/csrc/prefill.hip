@@ -48,6 +48,7 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 constexpr float kLn2 = 0.6931471805599453f;
@@ -193,26 +194,23 @@ prefill_kernel(const int32_t *__restrict__ wg_offsets, const pa_work_unit *__res
         const int32_t n_tiles = (kv1 - kv0 + KT - 1) / KT;
         const uint64_t head_off = (uint64_t)unit.kv_head * D * 2 + chunk * 16;
 
+        // Entries at or past kv1 (the tail of the last tile) are clamped to
+        // the range's last entry, so every row read is one the unit
+        // references and the loads need no branch; the causal mask gives
+        // those entries weight 0 (their row limit is at most kv1 - 1).
         int32_t slot[PASSES];
-        uint4 kreg[PASSES], vreg[PASSES];
+        u32x4_t kreg[PASSES], vreg[PASSES];
         auto load_slots = [&](int32_t tile) {
 #pragma unroll
-            for (int p = 0; p < PASSES; p++) {
-                const int32_t idx = kv0 + tile * KT + p * RPP + srow;
-                slot[p] = idx < kv1 ? kv_indices[idx] : -1;
-            }
+            for (int p = 0; p < PASSES; p++)
+                slot[p] = kv_indices[min(kv0 + tile * KT + p * RPP + srow, kv1 - 1)];
         };
         auto load_rows = [&]() {
 #pragma unroll
             for (int p = 0; p < PASSES; p++) {
-                if (slot[p] >= 0) {
-                    const uint64_t off = (uint64_t)(uint32_t)slot[p] * stride_bytes + head_off;
-                    kreg[p] = *reinterpret_cast<const uint4 *>(k_pool + off);
-                    vreg[p] = *reinterpret_cast<const uint4 *>(v_pool + off);
-                } else {
-                    kreg[p] = uint4{0, 0, 0, 0};
-                    vreg[p] = uint4{0, 0, 0, 0};
-                }
+                const uint64_t off = (uint64_t)(uint32_t)slot[p] * stride_bytes + head_off;
+                kreg[p] = *reinterpret_cast<const u32x4_t *>(k_pool + off);
+                vreg[p] = *reinterpret_cast<const u32x4_t *>(v_pool + off);
             }
         };
         auto store_rows = [&](int buf) {
@@ -220,8 +218,8 @@ prefill_kernel(const int32_t *__restrict__ wg_offsets, const pa_work_unit *__res
 #pragma unroll
             for (int p = 0; p < PASSES; p++) {
                 const int r = p * RPP + srow;
-                *reinterpret_cast<uint4 *>(st + r * KROW + chunk * 16) = kreg[p];
-                *reinterpret_cast<uint4 *>(st + KT * KROW + r * VROW + chunk * 16) = vreg[p];
+                *reinterpret_cast<u32x4_t *>(st + r * KROW + chunk * 16) = kreg[p];
+                *reinterpret_cast<u32x4_t *>(st + KT * KROW + r * VROW + chunk * 16) = vreg[p];
             }
         };
 
