@@ -50,8 +50,14 @@ HBM_PEAK_GBS = 8000.0
 PREFILL_METRIC = "chunked-prefill attention TFLOP/s (% of MI355X dense bf16 MFMA peak)"
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 PREFILL_LAYERS = 8
+CSRC = os.path.join(ROOT, "paged_gqa_decode_pa_amd", "csrc")
 COUNTERS = os.path.join(ROOT, "profiles", "decode_b64_counters.json")
-KERNEL_SOURCE = os.path.join(ROOT, "paged_gqa_decode_pa_amd", "csrc", "decode.hip")
+DECODE_SOURCES = ("decode.hip", "pa_internal.h")
+PREFILL_COUNTERS = {
+    "prefill_8x4096_chunk512": os.path.join(ROOT, "profiles", "prefill_chunk512_counters.json"),
+    "prefill_8x4096_chunk64": os.path.join(ROOT, "profiles", "prefill_chunk64_counters.json"),
+}
+PREFILL_SOURCES = ("prefill.hip", "pa_internal.h")
 
 
 def log(msg):
@@ -66,21 +72,21 @@ def algorithmic_bytes(spec, kv_indptr, kv_indices, kv_elem_bytes: int = 2) -> in
             + B * Hq * D * 4 + (B + 1) * 4)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(names=DECODE_SOURCES) -> str:
     h = hashlib.sha256()
-    for name in ("decode.hip", "pa_internal.h"):
-        with open(os.path.join(os.path.dirname(KERNEL_SOURCE), name), "rb") as f:
+    for name in names:
+        with open(os.path.join(CSRC, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def traffic_per_launch():
-    """HBM bytes per decode launch from committed counters, if they match the kernel."""
-    if not os.path.exists(COUNTERS):
+def traffic_per_launch(path=COUNTERS, sources=DECODE_SOURCES):
+    """HBM bytes per launch from committed counters, if they match the kernel source."""
+    if path is None or not os.path.exists(path):
         return None
-    with open(COUNTERS) as f:
+    with open(path) as f:
         c = json.load(f)
-    if c.get("kernel_source_sha256") != kernel_source_hash():
+    if c.get("kernel_source_sha256") != kernel_source_hash(sources):
         return None
     return int((c["fetch_kib_per_dispatch"] * c["fetch_scale"] +
                 c["write_kib_per_dispatch"] * c["write_scale"]) * 1024)
@@ -276,7 +282,7 @@ def run_prefill_bench(args):
             "peak": BF16_MFMA_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4),
-            "traffic": None,
+            "traffic": traffic_per_launch(PREFILL_COUNTERS.get(spec.name), PREFILL_SOURCES),
             "kernel": f"prefill_kernel<{D},{Hq // Hkv}> (pa_prefill_chunk_run)",
             "kernel_avg_us": round(kernel_avg_ms * 1e3, 2),
         },
