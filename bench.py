@@ -57,7 +57,8 @@ PREFILL_COUNTERS = {
     "prefill_8x4096_chunk512": os.path.join(ROOT, "profiles", "prefill_chunk512_counters.json"),
     "prefill_8x4096_chunk64": os.path.join(ROOT, "profiles", "prefill_chunk64_counters.json"),
 }
-PREFILL_SOURCES = ("prefill.hip", "pa_internal.h")
+# the partition decides how many partial rows a prefill launch writes
+PREFILL_SOURCES = ("prefill.hip", "pa_internal.h", "plan.cpp")
 
 
 def log(msg):

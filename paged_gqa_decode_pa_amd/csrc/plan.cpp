@@ -624,7 +624,11 @@ pa_status partition(const PartitionArgs &a, PartitionScratch *scratch, int32_t *
         int64_t n_tiles = 0;
         for (int32_t b = 0; b < a.batch; b++)
             n_tiles += (int64_t)Hkv * ceil_div(a.qo_indptr[b + 1] - a.qo_indptr[b], qt);
-        // cut KV ranges only when the tiles alone cannot fill the GPU
+        // Cut KV ranges only when the tiles alone cannot fill the GPU (two
+        // prefill workgroups per compute unit at head_dim 128), and then into
+        // about that many parts: every part runs in the first round, and more
+        // parts only add partial rows to write and merge (8 x 4096 cached +
+        // 64-token chunks: 4 parts per tile 79-80 us per layer, 8 parts 92-93).
         int64_t part_len = 0;  // 0 = no cut
         if (forced == 0 && n_tiles > 0 && n_tiles < 2LL * kNumCu) {
             int64_t kv_work = 0;
@@ -633,7 +637,7 @@ pa_status partition(const PartitionArgs &a, PartitionScratch *scratch, int32_t *
                 if (C > 0)
                     kv_work += (int64_t)Hkv * ceil_div(C, qt) * (a.kv_indptr[b + 1] - a.kv_indptr[b]);
             }
-            part_len = std::max<int64_t>(256, ceil_div(kv_work, 4LL * kNumCu));
+            part_len = std::max<int64_t>(256, ceil_div(kv_work, 2LL * kNumCu));
             part_len = ceil_div(part_len, 64) * 64;
         }
         std::vector<Unit> units;
