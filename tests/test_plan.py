@@ -322,3 +322,26 @@ def test_forced_splits_capacity_guarantee():
     offs, units, merges, n_p = pa_partition(ip, None, 32, 8, 128, pa.PA_PLAN_FORCE_SPLITS(n))
     assert n_p == 3 * 8 * n
     assert n_p <= 8 * (3 + (3 * n * 256) // 256)
+
+
+def test_prefill_kv_cut_one_round():
+    """Chunk tiles that cannot fill the GPU get their KV ranges cut into about
+    two parts per compute unit (one round of the resident prefill
+    workgroups); tiles that fill it alone are not cut.  Every part of a tile
+    covers a disjoint, contiguous piece of its causal window."""
+    for spec, n_units, n_merges in ((W.PREFILL_CHUNK512, 1024, 0), (W.PREFILL_CHUNK64, 512, 128)):
+        qo, ip, idx = W.prefill_lists(spec)
+        offs, units, merges, n_p = pa.pa_partition(ip, qo, spec.num_qo_heads, spec.num_kv_heads,
+                                                   spec.head_dim)
+        assert len(units) == n_units and len(merges) == n_merges
+        for m in merges:
+            parts = units[(units["request"] == m["request"]) & (units["kv_head"] == m["kv_head"])
+                          & (units["q_begin"] == m["q_begin"])]
+            parts = np.sort(parts, order="kv_begin")
+            assert len(parts) == m["n_parts"]
+            assert parts["kv_begin"][0] == ip[m["request"]]
+            assert np.all(parts["kv_begin"][1:] == parts["kv_end"][:-1])
+            # the last part ends at the window of the tile's last row
+            t1 = m["q_end"] - qo[m["request"]]
+            P = (ip[m["request"] + 1] - ip[m["request"]]) - (qo[m["request"] + 1] - qo[m["request"]])
+            assert parts["kv_end"][-1] == ip[m["request"]] + P + t1
