@@ -128,7 +128,7 @@ __device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-template <int D, int G, bool SPLIT>
+template <int D, int G, bool WIDE>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(prefill_waves_per_simd<D>(), prefill_waves_per_simd<D>()))) void
 prefill_kernel(const int32_t *__restrict__ wg_offsets, const pa_work_unit *__restrict__ units,
@@ -198,19 +198,28 @@ prefill_kernel(const int32_t *__restrict__ wg_offsets, const pa_work_unit *__res
         // the range's last entry, so every row read is one the unit
         // references and the loads need no branch; the causal mask gives
         // those entries weight 0 (their row limit is at most kv1 - 1).
+        const int32_t *const unit_ids = kv_indices + kv0;   // the unit's entries, uniform base
         int32_t slot[PASSES];
         u32x4_t kreg[PASSES], vreg[PASSES];
         auto load_slots = [&](int32_t tile) {
 #pragma unroll
             for (int p = 0; p < PASSES; p++)
-                slot[p] = kv_indices[min(kv0 + tile * KT + p * RPP + srow, kv1 - 1)];
+                slot[p] = unit_ids[(uint32_t)min(tile * KT + p * RPP + srow, kv1 - kv0 - 1)];
         };
         auto load_rows = [&]() {
 #pragma unroll
             for (int p = 0; p < PASSES; p++) {
-                const uint64_t off = (uint64_t)(uint32_t)slot[p] * stride_bytes + head_off;
-                kreg[p] = *reinterpret_cast<const u32x4_t *>(k_pool + off);
-                vreg[p] = *reinterpret_cast<const u32x4_t *>(v_pool + off);
+                // pools whose byte offsets stay below 2^31 (the host checks)
+                // take a 32-bit offset, shared by the K and V loads
+                if constexpr (WIDE) {
+                    const uint64_t off = (uint64_t)(uint32_t)slot[p] * stride_bytes + head_off;
+                    kreg[p] = *reinterpret_cast<const u32x4_t *>(k_pool + off);
+                    vreg[p] = *reinterpret_cast<const u32x4_t *>(v_pool + off);
+                } else {
+                    const uint32_t off = __umul24((uint32_t)slot[p], (uint32_t)stride_bytes) + (uint32_t)head_off;
+                    kreg[p] = *reinterpret_cast<const u32x4_t *>(k_pool + off);
+                    vreg[p] = *reinterpret_cast<const u32x4_t *>(v_pool + off);
+                }
             }
         };
         auto store_rows = [&](int buf) {
@@ -304,19 +313,14 @@ prefill_kernel(const int32_t *__restrict__ wg_offsets, const pa_work_unit *__res
                     const float p0 = fast_exp2(fmaf(s[b][i], c_exp, -m));
                     const float p1 = fast_exp2(fmaf(s[b][i + 1], c_exp, -m));
                     l += p0 + p1;
-                    if (SPLIT)
-                        split_pair(p0, p1, ph[b][i / 2], pl[b][i / 2]);
-                    else
-                        ph[b][i / 2] = pack_bf16(p0, p1);
+                    split_pair(p0, p1, ph[b][i / 2], pl[b][i / 2]);
                 }
             // O^T += V^T P^T, 16 entries per k-step
 #pragma unroll
             for (int k = 0; k < KS; k++) {
                 const int b = k / 2, w0 = 4 * (k % 2);  // dword index of entries 16*(k%2) + 4*half
                 const bf16x8_t bh = regroup(ph[b][w0], ph[b][w0 + 1], ph[b][w0 + 2], ph[b][w0 + 3]);
-                bf16x8_t bl;
-                if (SPLIT)
-                    bl = regroup(pl[b][w0], pl[b][w0 + 1], pl[b][w0 + 2], pl[b][w0 + 3]);
+                const bf16x8_t bl = regroup(pl[b][w0], pl[b][w0 + 1], pl[b][w0 + 2], pl[b][w0 + 3]);
 #pragma unroll
                 for (int db = 0; db < DB; db++) {
                     const int off = v_lane + k * 16 * VROW + db * 64;
@@ -326,8 +330,7 @@ prefill_kernel(const int32_t *__restrict__ wg_offsets, const pa_work_unit *__res
                     const bf16x8_t a = __builtin_bit_cast(
                         bf16x8_t, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
                     o[db] = mfma(a, bh, o[db]);
-                    if (SPLIT)
-                        o[db] = mfma(a, bl, o[db]);
+                    o[db] = mfma(a, bl, o[db]);
                 }
             }
             if (it + 1 < n_tiles)
@@ -457,10 +460,17 @@ int launch_prefill_merge_dg(const DecodeLaunch &l, hipStream_t stream) {
 template <int D, int G>
 int launch_prefill_dg(const DecodeLaunch &l, hipStream_t stream) {
     const uint64_t stride_bytes = (uint64_t)l.slot_stride * 2;
-    hipLaunchKernelGGL((prefill_kernel<D, G, true>), dim3(l.n_workgroups), dim3(kThreads), 0, stream,
-                       l.wg_offsets, l.units, (const uint16_t *)l.q, (const char *)l.k_pool,
-                       (const char *)l.v_pool, stride_bytes, l.kv_indices, l.sm_scale * kLog2e, l.out,
-                       l.lse, l.partial_o, l.partial_lse, l.num_qo_heads);
+    const bool wide = stride_bytes >= (1u << 24) || !row_offsets_fit_32(l.num_slots, (uint32_t)stride_bytes);
+    if (wide)
+        hipLaunchKernelGGL((prefill_kernel<D, G, true>), dim3(l.n_workgroups), dim3(kThreads), 0, stream,
+                           l.wg_offsets, l.units, (const uint16_t *)l.q, (const char *)l.k_pool,
+                           (const char *)l.v_pool, stride_bytes, l.kv_indices, l.sm_scale * kLog2e, l.out,
+                           l.lse, l.partial_o, l.partial_lse, l.num_qo_heads);
+    else
+        hipLaunchKernelGGL((prefill_kernel<D, G, false>), dim3(l.n_workgroups), dim3(kThreads), 0, stream,
+                           l.wg_offsets, l.units, (const uint16_t *)l.q, (const char *)l.k_pool,
+                           (const char *)l.v_pool, stride_bytes, l.kv_indices, l.sm_scale * kLog2e, l.out,
+                           l.lse, l.partial_o, l.partial_lse, l.num_qo_heads);
     return (int)hipGetLastError();
 }
 
