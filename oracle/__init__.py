@@ -89,6 +89,12 @@ class Oracle:
         lib.pa_oracle_e4m3_to_bf16.argtypes = [ctypes.c_int64, _u8p, _u16p]
         lib.pa_oracle_e4m3_values.restype = ctypes.c_int
         lib.pa_oracle_e4m3_values.argtypes = [ctypes.c_int64, _u8p, _f64p]
+        lib.pa_oracle_decode_e4m3.restype = ctypes.c_int
+        lib.pa_oracle_decode_e4m3.argtypes = [
+            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+            _u16p, _u8p, _u8p, ctypes.c_int64, ctypes.c_int64,
+            _i32p, _i32p, ctypes.c_float, ctypes.c_float, ctypes.c_float,
+            _f64p, _f64p, _i32p, ctypes.c_int64]
         lib.pa_oracle_num_threads.restype = ctypes.c_int
         lib.pa_oracle_num_threads.argtypes = []
         self._lib = lib
@@ -214,15 +220,43 @@ class Oracle:
 
     def decode_fp8(self, q_bits, k_codes, v_codes, kv_indptr, kv_indices, sm_scale: float,
                    k_scale: float, v_scale: float, num_kv_heads: int, sel=None):
-        """Decode over E4M3 pools with per-pool scales: the decode of the
-        widened codes with softmax scale sm_scale * k_scale (fp32 product, as
-        the caller's scale is fp32) and the output times v_scale.  The pools
-        are widened in full (use small pools, or `sel` for sampled rows)."""
-        kb = self.e4m3_to_bf16(k_codes)
-        vb = self.e4m3_to_bf16(v_codes)
-        scale = float(np.float32(np.float32(sm_scale) * np.float32(k_scale)))
-        out, lse = self.decode(q_bits, kb, vb, kv_indptr, kv_indices, scale, num_kv_heads, sel=sel)
-        return out * float(np.float32(v_scale)), lse
+        """Decode over E4M3 pools with per-pool scales: the attention of
+        ``decode`` on the row values k_scale * value(code) and
+        v_scale * value(code), formed in double precision from the codes
+        (uint8 [N, Hkv, D]); the three scales are float32 values, widened.
+        Returns (out float64 [B, Hq, D], lse float64 [B, Hq])."""
+        q = _as(q_bits, np.uint16)
+        k = _as(k_codes, np.uint8)
+        v = _as(v_codes, np.uint8)
+        B, Hq, D = q.shape
+        if v.shape != k.shape:
+            raise OracleError("k and v pools differ in shape")
+        num_slots = k.shape[0]
+        slot_stride = int(np.prod(k.shape[1:])) if k.ndim > 1 else 0
+        indptr = _as(kv_indptr, np.int32)
+        indices = _as(kv_indices, np.int32)
+        if indptr.shape != (B + 1,):
+            raise OracleError("kv_indptr must have batch+1 entries")
+        if indices.shape[0] < indptr[-1]:
+            raise OracleError("kv_indices shorter than kv_indptr[-1]")
+        if indices.size == 0:
+            indices = np.zeros(1, np.int32)
+        out = np.full((B, Hq, D), np.nan)
+        lse = np.full((B, Hq), np.nan)
+        if sel is None:
+            sel_arr, n_sel, sel_p = None, 0, None
+        else:
+            sel_arr = _as(sel, np.int32)
+            n_sel = sel_arr.size
+            sel_p = _ptr(sel_arr, _i32p)
+        u8p = ctypes.POINTER(ctypes.c_uint8)
+        rc = self._lib.pa_oracle_decode_e4m3(
+            B, Hq, num_kv_heads, D, _ptr(q, _u16p), _ptr(k, u8p), _ptr(v, u8p),
+            num_slots, slot_stride, _ptr(indptr, _i32p), _ptr(indices, _i32p),
+            ctypes.c_float(sm_scale), ctypes.c_float(k_scale), ctypes.c_float(v_scale),
+            _ptr(out, _f64p), _ptr(lse, _f64p), sel_p, n_sel)
+        self._check(rc)
+        return out, lse
 
     def merge(self, o_parts, lse_parts):
         """Log-sum-exp merge of partial results of one row: o_parts [n, D], lse_parts [n]."""

@@ -51,14 +51,16 @@
  *         y[i]       = x[i] cos(a_i) - x[i + D/2] sin(a_i)
  *         y[i + D/2] = x[i + D/2] cos(a_i) + x[i] sin(a_i)
  *
- *   - 8-bit floating-point KV pool (quantisation, FP8 among them, is on the
- *     Agent-Infer page's roadmap, section "未来规划"; the pages give no format).
- *     Reading: K and V rows stored as OCP FP8 E4M3 codes (1 sign bit, 4
- *     exponent bits with bias 7, 3 mantissa bits; no infinities; exponent and
- *     mantissa all ones is NaN), with one scale per pool: the row values are
- *     k_scale * code and v_scale * code.  Every E4M3 value is exactly a bf16
- *     value, so the fp8 decode is the decode above on the widened codes, with
- *     the softmax scale multiplied by k_scale and the output by v_scale.
+ *   - 8-bit floating-point KV pool (quantisation, FP8 among the formats, is
+ *     on the Agent-Infer page's roadmap, section "模型支持与发展路线图"; the
+ *     pages give no format).  Reading: K and V rows stored as OCP FP8 E4M3
+ *     codes (1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits; no
+ *     infinities; exponent and mantissa all ones is NaN), with one scale per
+ *     pool: the row values are k_scale * value(code) and v_scale * value(code),
+ *     formed in double precision, and the attention above runs on those
+ *     values unchanged:
+ *         s_j = scale * <q, k_scale * value(Kcode[S_j])>
+ *         out = sum_j exp(s_j - m) * v_scale * value(Vcode[S_j]) / sum_j exp(s_j - m)
  *
  * All arithmetic is in double precision.  bf16 inputs are widened exactly
  * (a bf16 bit pattern is the upper half of an IEEE binary32).  The softmax
@@ -336,7 +338,6 @@ int pa_oracle_merge(int32_t n, int32_t D, const double *o_parts,
     return ORACLE_OK;
 }
 
-/* Threads an OpenMP region of this library uses (1 without OpenMP). */
 /*
  * Rotary position embedding of n rows of D bf16 values (rows of `heads`
  * consecutive heads per token): row r belongs to token r / heads, whose
@@ -405,6 +406,103 @@ int pa_oracle_e4m3_values(int64_t n, const uint8_t *codes, double *values)
     return ORACLE_OK;
 }
 
+/*
+ * Softmax attention of one query row over n slots of E4M3 pools: the same
+ * formula as attend_one_row, on the values k_scale * value(code) and
+ * v_scale * value(code), all in double precision.
+ */
+static void attend_one_row_e4m3(int D, const uint16_t *q_row,
+                                const uint8_t *k_codes, const uint8_t *v_codes,
+                                int64_t slot_stride, int kh,
+                                const int32_t *slots, int64_t n, double scale,
+                                double k_scale, double v_scale,
+                                double *w, double *out, double *lse)
+{
+    if (n == 0) {
+        for (int d = 0; d < D; d++)
+            out[d] = 0.0;
+        *lse = -INFINITY;
+        return;
+    }
+    for (int64_t j = 0; j < n; j++) {
+        const uint8_t *kc = k_codes + (int64_t)slots[j] * slot_stride + (int64_t)kh * D;
+        double acc = 0.0;
+        for (int d = 0; d < D; d++)
+            acc += widen_bf16(q_row[d]) * (k_scale * e4m3_value(kc[d]));
+        w[j] = scale * acc;
+    }
+    double top = w[0];
+    for (int64_t j = 1; j < n; j++)
+        top = w[j] > top ? w[j] : top;
+    double total = 0.0;
+    for (int64_t j = 0; j < n; j++) {
+        w[j] = exp(w[j] - top);
+        total += w[j];
+    }
+    for (int d = 0; d < D; d++)
+        out[d] = 0.0;
+    for (int64_t j = 0; j < n; j++) {
+        const uint8_t *vc = v_codes + (int64_t)slots[j] * slot_stride + (int64_t)kh * D;
+        for (int d = 0; d < D; d++)
+            out[d] += w[j] * (v_scale * e4m3_value(vc[d]));
+    }
+    for (int d = 0; d < D; d++)
+        out[d] = out[d] / total;
+    *lse = top + log(total);
+}
+
+/*
+ * Decode over E4M3 pools with per-pool scales (codes: 1 byte per element,
+ * slot s, head kh row at s*slot_stride + kh*D).  Arguments otherwise as
+ * pa_oracle_decode; the scales are given as floats and widened.
+ */
+int pa_oracle_decode_e4m3(int32_t batch, int32_t Hq, int32_t Hkv, int32_t D,
+                          const uint16_t *q,
+                          const uint8_t *k_codes, const uint8_t *v_codes,
+                          int64_t num_slots, int64_t slot_stride,
+                          const int32_t *kv_indptr, const int32_t *kv_indices,
+                          float sm_scale, float k_scale, float v_scale,
+                          double *out, double *lse,
+                          const int32_t *sel, int64_t n_sel)
+{
+    int rc = check_common(batch, Hq, Hkv, D, num_slots, slot_stride, kv_indptr, kv_indices);
+    if (rc != ORACLE_OK)
+        return rc;
+    const int32_t per_kv_head = Hq / Hkv;
+    const int64_t n_rows = sel ? n_sel : (int64_t)batch * Hq;
+    const int64_t longest = longest_list(batch, kv_indptr);
+    int failed = 0;
+    for (int64_t r = 0; r < n_rows; r++) {
+        int64_t row = sel ? sel[r] : r;
+        if (row < 0 || row >= (int64_t)batch * Hq)
+            return ORACLE_BAD_SHAPE;
+    }
+#pragma omp parallel
+    {
+        double *w = (double *)malloc(sizeof(double) * (size_t)longest);
+        if (!w) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t r = 0; r < n_rows; r++) {
+            if (!w)
+                continue;
+            const int64_t row = sel ? sel[r] : r;
+            const int32_t b = (int32_t)(row / Hq);
+            const int32_t head = (int32_t)(row % Hq);
+            attend_one_row_e4m3(D, q + row * D, k_codes, v_codes, slot_stride,
+                                head / per_kv_head, kv_indices + kv_indptr[b],
+                                (int64_t)kv_indptr[b + 1] - kv_indptr[b],
+                                (double)sm_scale, (double)k_scale, (double)v_scale,
+                                w, out + row * D, lse + row);
+        }
+        free(w);
+    }
+    return failed ? ORACLE_NO_MEMORY : ORACLE_OK;
+}
+
+/* Threads an OpenMP region of this library uses (1 without OpenMP). */
 int pa_oracle_num_threads(void)
 {
 #ifdef _OPENMP

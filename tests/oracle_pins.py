@@ -452,31 +452,87 @@ def pin_e4m3_widening_exact(o):
     assert np.array_equal(wid[ok], vals[ok]) and np.all(np.isnan(wid[~ok])), "widening not exact"
 
 
-def pin_decode_fp8_sdpa(o):
-    """fp8 pools with per-pool scales: torch SDPA (float64) on scale * torch's
-    float8_e4m3fn values, contiguous slots, to 1e-12."""
-    rng = np.random.default_rng(51)
-    Hq, Hkv, D, lengths = 8, 2, 16, [5, 1, 12]
-    k_scale, v_scale = 0.5, 0.25
-    N = sum(lengths) + 2
+def _fp8_case(rng, lengths, Hq, Hkv, D, spare=2):
+    N = sum(lengths) + spare
     q = _random_bits(rng, (len(lengths), Hq, D))
     kc = torch.from_numpy(rng.standard_normal((N, Hkv, D)) * 2).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     vc = torch.from_numpy(rng.standard_normal((N, Hkv, D)) * 4).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     indptr = np.zeros(len(lengths) + 1, np.int32)
     indptr[1:] = np.cumsum(lengths)
-    indices = np.arange(sum(lengths), dtype=np.int32) + 2
-    scale = workloads.softmax_scale(D)
+    indices = np.arange(sum(lengths), dtype=np.int32) + spare
+    return q, kc, vc, indptr, indices
+
+
+def _f32(x: float) -> float:
+    return float(np.float32(x))
+
+
+def pin_decode_fp8_sdpa(o):
+    """fp8 pools with per-pool scales that are not powers of two (0.37, 1.3)
+    and a softmax scale 1/sqrt(32) that is not one either: torch SDPA
+    (float64) on the values scale * torch's float8_e4m3fn value, contiguous
+    slots, to 1e-12.  Every product is formed in double; a float32 product
+    of two scales moves the scores by ~1e-8 and fails this pin."""
+    rng = np.random.default_rng(51)
+    for Hq, Hkv, D, lengths, k_scale, v_scale in [(8, 2, 32, [5, 1, 12], 0.37, 1.3),
+                                                  (4, 4, 16, [3, 9], 0.5, 0.25)]:
+        q, kc, vc, indptr, indices = _fp8_case(rng, lengths, Hq, Hkv, D)
+        scale = workloads.softmax_scale(D)
+        out, lse = o.decode_fp8(q, kc, vc, indptr, indices, scale, k_scale, v_scale, Hkv)
+        kf = torch.from_numpy(kc.copy()).view(torch.float8_e4m3fn).to(torch.float64) * _f32(k_scale)
+        vf = torch.from_numpy(vc.copy()).view(torch.float8_e4m3fn).to(torch.float64) * _f32(v_scale)
+        sm = _f32(scale)
+        for b in range(len(lengths)):
+            ids = torch.from_numpy(indices[indptr[b]:indptr[b + 1]].astype(np.int64))
+            qt = torch.from_numpy(_widen(q[b]))[None, :, None, :]
+            kt = kf[ids].permute(1, 0, 2)[None].contiguous()
+            vt = vf[ids].permute(1, 0, 2)[None].contiguous()
+            ref = F.scaled_dot_product_attention(qt, kt, vt, scale=sm, enable_gqa=True)
+            err = np.abs(out[b] - ref[0, :, 0, :].numpy()).max()
+            assert err < TOL, f"fp8 decode vs sdpa {err} (scales {k_scale}, {v_scale})"
+            g = Hq // Hkv
+            s = sm * torch.einsum("hd,khd->hk", qt[0, :, 0, :],
+                                  kt[0].permute(1, 0, 2).repeat_interleave(g, dim=1))
+            ref_lse = torch.logsumexp(s, dim=1).numpy()
+            err = np.abs(lse[b] - ref_lse).max()
+            assert err < TOL, f"fp8 decode lse vs logsumexp {err}"
+
+
+def pin_decode_fp8_single_token(o):
+    """One listed slot: the output is v_scale times the code's value, exactly
+    (the rounding of that one double product), and lse is the scaled dot
+    product of q with k_scale times the K codes' values, summed exactly; an
+    empty list gives out = 0 and lse = -inf."""
+    rng = np.random.default_rng(52)
+    Hq, Hkv, D = 4, 2, 8
+    q, kc, vc, indptr, indices = _fp8_case(rng, [1, 1, 0], Hq, Hkv, D, spare=5)
+    indices = np.array([3, 6], np.int32)
+    k_scale, v_scale, scale = 0.37, 1.3, 0.3
     out, lse = o.decode_fp8(q, kc, vc, indptr, indices, scale, k_scale, v_scale, Hkv)
-    kf = torch.from_numpy(kc.copy()).view(torch.float8_e4m3fn).to(torch.float64) * k_scale
-    vf = torch.from_numpy(vc.copy()).view(torch.float8_e4m3fn).to(torch.float64) * v_scale
-    sm = float(np.float32(scale))   # scales are powers of two: every product is exact
-    for b in range(len(lengths)):
-        ids = torch.from_numpy(indices[indptr[b]:indptr[b + 1]].astype(np.int64))
-        qt = torch.from_numpy(_widen(q[b]))[None, :, None, :]
-        ref = F.scaled_dot_product_attention(qt, kf[ids].permute(1, 0, 2)[None], vf[ids].permute(1, 0, 2)[None],
-                                             scale=sm, enable_gqa=True)
-        err = np.abs(out[b] - ref[0, :, 0, :].numpy()).max()
-        assert err < TOL, f"fp8 decode vs sdpa {err}"
+    assert np.all(out[2] == 0.0) and np.all(np.isneginf(lse[2])), "fp8 empty list"
+    kval = o.e4m3_values(kc)
+    vval = o.e4m3_values(vc)
+    for b in range(2):
+        for h in range(Hq):
+            kh = h // (Hq // Hkv)
+            want = _f32(v_scale) * vval[indices[b], kh]
+            assert np.array_equal(out[b, h], want), "fp8 L=1 output is not v_scale * value"
+            dot = sum((Fraction(float(x)) * Fraction(_f32(k_scale) * float(y))
+                       for x, y in zip(_widen(q[b, h]), kval[indices[b], kh])), Fraction(0))
+            assert abs(lse[b, h] - _f32(scale) * float(dot)) < 1e-14, "fp8 L=1 lse"
+
+
+def pin_decode_fp8_unit_scales_equal_bf16(o):
+    """With unit scales the fp8 decode equals the bf16 decode over pools that
+    hold the codes' values (every E4M3 value is a bf16 value)."""
+    rng = np.random.default_rng(53)
+    q, kc, vc, indptr, indices = _fp8_case(rng, [7, 30, 2], 8, 2, 16)
+    scale = workloads.softmax_scale(16)
+    out8, lse8 = o.decode_fp8(q, kc, vc, indptr, indices, scale, 1.0, 1.0, 2)
+    kb = _bf16_bits(torch.from_numpy(kc.copy()).view(torch.float8_e4m3fn).to(torch.float32).numpy())
+    vb = _bf16_bits(torch.from_numpy(vc.copy()).view(torch.float8_e4m3fn).to(torch.float32).numpy())
+    out, lse = o.decode(q, kb, vb, indptr, indices, scale, 2)
+    assert np.abs(out8 - out).max() < TOL and np.abs(lse8 - lse).max() < TOL, "fp8 vs bf16 decode"
 
 
 ALL_PINS = [
@@ -487,4 +543,5 @@ ALL_PINS = [
     pin_rope_complex_rotation, pin_rope_closed_form, pin_rope_position_zero,
     pin_rope_relative_position, pin_rope_norm,
     pin_e4m3_matches_torch, pin_e4m3_closed_forms, pin_e4m3_widening_exact, pin_decode_fp8_sdpa,
+    pin_decode_fp8_single_token, pin_decode_fp8_unit_scales_equal_bf16,
 ]

@@ -31,8 +31,10 @@ MUTANTS = [
     ("normalised_by_count", [("out[d] /= z;", "out[d] /= (double)n;", None)]),
     ("lse_without_max", [("*lse = m + log(z);", "*lse = log(z);", None)]),
     ("lse_without_log", [("*lse = m + log(z);", "*lse = m + z;", None)]),
-    ("empty_lse_zero", [("*lse = -INFINITY;\n        return;", "*lse = 0.0;\n        return;", None)]),
-    ("empty_out_garbage", [("out[d] = 0.0;\n        *lse = -INFINITY;", "out[d] = 1.0;\n        *lse = -INFINITY;", None)]),
+    ("empty_lse_zero", [("*lse = -INFINITY;\n        return;", "*lse = 0.0;\n        return;", 0)]),
+    ("empty_out_garbage", [("out[d] = 0.0;\n        *lse = -INFINITY;", "out[d] = 1.0;\n        *lse = -INFINITY;", 0)]),
+    ("fp8_empty_lse_zero", [("*lse = -INFINITY;\n        return;", "*lse = 0.0;\n        return;", 1)]),
+    ("fp8_empty_out_garbage", [("out[d] = 0.0;\n        *lse = -INFINITY;", "out[d] = 1.0;\n        *lse = -INFINITY;", 1)]),
     ("query_head_zero_decode", [("attend_one_row(D, q + row * D,", "attend_one_row(D, q + (row / Hq) * Hq * D,", 0)]),
     ("query_head_zero_prefill", [("attend_one_row(D, q + row * D,", "attend_one_row(D, q + (row / Hq) * Hq * D,", 1)]),
     ("decode_list_one_short", [("(int64_t)kv_indptr[b + 1] - kv_indptr[b],\n                           (double)sm_scale",
@@ -56,6 +58,16 @@ MUTANTS = [
     ("e4m3_mantissa_width", [("ldexp(1.0 + (double)m / 8.0, e - 7)", "ldexp(1.0 + (double)m / 16.0, e - 7)", None)]),
     ("e4m3_sign_ignored", [("return sign ? -mag : mag;", "return mag;", None)]),
     ("e4m3_no_nan", [("if (e == 0xF && m == 0x7)\n        return NAN;", "if (0)\n        return NAN;", None)]),
+    ("fp8_k_scale_dropped", [("acc += widen_bf16(q_row[d]) * (k_scale * e4m3_value(kc[d]));",
+                              "acc += widen_bf16(q_row[d]) * e4m3_value(kc[d]);", None)]),
+    ("fp8_v_scale_dropped", [("out[d] += w[j] * (v_scale * e4m3_value(vc[d]));",
+                              "out[d] += w[j] * e4m3_value(vc[d]);", None)]),
+    ("fp8_values_from_k_codes", [("const uint8_t *vc = v_codes", "const uint8_t *vc = k_codes", None)]),
+    ("fp8_scales_as_float_product", [("(double)sm_scale, (double)k_scale, (double)v_scale,",
+                                      "(double)(float)(sm_scale * k_scale), 1.0, (double)v_scale,", None)]),
+    ("fp8_lse_without_max", [("*lse = top + log(total);", "*lse = log(total);", None)]),
+    ("fp8_exp_unshifted", [("w[j] = exp(w[j] - top);", "w[j] = exp(w[j]);", None)]),
+    ("fp8_gqa_modulo", [("head / per_kv_head, kv_indices", "head % Hkv, kv_indices", None)]),
     ("rope_position_off_by_one", [("(double)positions[t] * inv_freq", "(double)(positions[t] + 1) * inv_freq", None)]),
 ]
 
