@@ -1,8 +1,8 @@
 // prefill.hip -- gfx950 chunked-prefill kernel of libpa (matrix-core path).
 //
 // Operation: a request whose prompt is processed in chunks (Agent-Infer page,
-// "Agent-Infer: 纯 Rust 编写的高性能 LLM 推理引擎", sections "调度器" and
-// "优化历程": chunks of 512 tokens, 64 while decodes run) has a slot list of
+// "Agent-Infer: 纯 Rust 编写的高性能 LLM 推理引擎", section "连续批处理":
+// chunks of 512 tokens, 64 while decodes run) has a slot list of
 // L entries whose last C entries are the chunk's own tokens, already written
 // into the pool; chunk token i (0-based) attends to list entries 0 .. L-C+i
 // (its cached prefix plus the chunk up to itself).  Scores, softmax and the

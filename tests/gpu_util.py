@@ -49,13 +49,41 @@ def oracle_decode(q, k_pool, v_pool, kv_indptr, kv_indices, sm_scale, num_kv_hea
 
 
 def max_err(gpu: np.ndarray, ref: np.ndarray, rows=None) -> float:
-    g = gpu.reshape(-1, gpu.shape[-1]) if gpu.ndim > 1 else gpu.reshape(-1, 1)
-    r = ref.reshape(g.shape)
+    """Largest |gpu - ref| over the compared rows (float64).
+
+    The arrays are viewed as rows of their last axis (a 1-D array as rows of
+    one value); ``rows`` selects flat row indices to compare (None: all).
+    Rows are picked by index, never skipped because a value is NaN: a GPU
+    value that is NaN or infinite where the oracle's is finite (an output row
+    the kernel never wrote keeps the NaN it was filled with) and a finite GPU
+    value where the oracle's is not (a row the oracle did not compute, or a
+    result that should be infinite) both count as an infinite error.  The one
+    non-finite agreement accepted is -inf on both sides (the lse of an empty
+    list)."""
+    g = np.asarray(gpu)
+    r = np.asarray(ref)
+    if g.size != r.size:
+        raise ValueError(f"gpu and oracle sizes differ: {g.shape} vs {r.shape}")
+    g = g.reshape(-1, g.shape[-1]) if g.ndim > 1 else g.reshape(-1, 1)
+    r = r.reshape(g.shape)
     if rows is not None:
-        g, r = g[rows], r[rows]
-    both_inf = np.isneginf(g) & np.isneginf(r)
-    d = np.where(both_inf, 0.0, np.abs(g.astype(np.float64) - r))
-    return float(np.nanmax(d)) if d.size else 0.0
+        idx = np.asarray(rows, dtype=np.int64).reshape(-1)
+        g, r = g[idx], r[idx]
+    if g.size == 0:
+        return 0.0
+    g = g.astype(np.float64)
+    finite = np.isfinite(g) & np.isfinite(r)
+    agree = np.isneginf(g) & np.isneginf(r)
+    if not np.all(finite | agree):
+        return float("inf")
+    d = np.abs(g[finite] - r[finite])
+    return float(d.max()) if d.size else 0.0
+
+
+def all_rows_written(gpu: np.ndarray) -> bool:
+    """True when no output value is NaN (outputs are filled with NaN before a
+    run, so a NaN left over is a row the kernel did not write)."""
+    return not np.isnan(np.asarray(gpu)).any()
 
 
 def run_prefill(q, k_pool, v_pool, qo_indptr, kv_indptr, kv_indices_dev, sm_scale, num_kv_heads,

@@ -1,8 +1,9 @@
 """The append step (pa_kv_append): new tokens' K/V rows written to their
 slots, K (and optionally Q) rotated by RoPE, against the fp64 oracle's
-rotation on the same bf16 bits.  Slot placement and V are bit-exact; rotated
-values are the oracle's rounded to bf16 within one bf16 unit in the last
-place (the GPU rounds its own double-precision rotation once).  Needs a GPU."""
+rotation on the same bf16 bits.  Slot placement and V are bit-exact; a
+rotated value must equal the oracle's double-precision rotation rounded once
+to bf16 (nearest-even, no float32 step), bit for bit: the kernel also rounds
+its double-precision rotation once.  Needs a GPU."""
 import numpy as np
 import pytest
 import torch
@@ -19,8 +20,20 @@ THETA = 1e6   # Qwen3's RoPE base
 
 
 def _bf16_round(x64: np.ndarray) -> np.ndarray:
-    """float64 -> bf16 bits, nearest-even (through float32)."""
-    return W.bits(torch.as_tensor(x64).to(torch.float32).to(torch.bfloat16))
+    """float64 -> bf16 bits, rounded once to nearest-even straight from the
+    double (no float32 step, so no double rounding).  Values must be zero or
+    normal in bf16 (|x| >= 2^-126), as every rotated N(0, 1) value here is."""
+    x = np.ascontiguousarray(x64, dtype=np.float64)
+    mag = np.abs(x)
+    assert np.all((mag == 0) | ((mag >= 2.0 ** -126) & (mag < 3.0e38))), "outside bf16's normal range"
+    u = x.view(np.uint64)
+    # keep 7 of the double's 52 fraction bits: add half an ulp of the kept
+    # part (minus one when the kept part is even: ties go to even), truncate
+    drop = np.uint64(45)
+    lsb = (u >> drop) & np.uint64(1)
+    r = ((u + (np.uint64(1) << np.uint64(44)) - np.uint64(1) + lsb) >> drop) << drop
+    f32 = r.view(np.float64).astype(np.float32)   # exact: r holds a bf16 value
+    return (f32.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
 
 
 def _ulp_distance(a_bits: np.ndarray, b_bits: np.ndarray) -> np.ndarray:
@@ -62,13 +75,13 @@ def _check_append(T, Hq, Hkv, D, N, seed, theta=THETA, with_q=True, positions_hi
     exp_k = _bf16_round(k_ref) if theta > 0 else kb
     dk = _ulp_distance(k_after[out_loc], exp_k)
     say(f"  K: max ulp {dk.max()}, exact {np.mean(dk == 0) * 100:.4f}%")
-    assert dk.max() <= 1
+    assert dk.max() == 0
     if with_q:
         q_after = W.bits(q)
         if theta > 0:
             dq = _ulp_distance(q_after, _bf16_round(ref.rope(q_before, positions, theta)))
             say(f"  Q: max ulp {dq.max()}, exact {np.mean(dq == 0) * 100:.4f}%")
-            assert dq.max() <= 1
+            assert dq.max() == 0
         else:
             assert np.array_equal(q_after, q_before)
     return k_pool, v_pool, k_ref, out_loc, positions
@@ -153,7 +166,7 @@ def test_append_then_decode_attends_rotated_keys():
     pa.pa_kv_append(k_new, v_new, torch.as_tensor(new_slots, device=dev), k_pool, v_pool,
                     positions=torch.as_tensor(positions, device=dev), rope_theta=THETA, q=q)
     scale = W.softmax_scale(D)
-    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    out = torch.full((B, Hq, D), float("nan"), dtype=torch.float32, device=dev)
     with pa.Plan(B, int(ip[-1]), Hq, Hkv, D) as plan:
         plan.plan(ip)
         plan.decode(q, k_pool, v_pool, torch.as_tensor(idx, device=dev), scale, out)
@@ -164,7 +177,7 @@ def test_append_then_decode_attends_rotated_keys():
     k_exp[new_slots] = _bf16_round(ref_o.rope(W.bits(k_new), positions, THETA))
     q_exp = _bf16_round(ref_o.rope(q_raw, positions, THETA))
     d = _ulp_distance(W.bits(k_pool), k_exp).max()
-    assert d <= 1
+    assert d == 0
     ref, _ = ref_o.decode(q_exp, k_exp, W.bits(v_pool), ip, idx, scale, Hkv)
     assert max_err(out.cpu().numpy(), ref) <= TOL
 
@@ -187,6 +200,6 @@ def test_append_large_pool_offsets():
     got_v = W.bits(v_pool[torch.as_tensor(loc, device=dev, dtype=torch.int64)])
     assert np.array_equal(got_v, W.bits(v_new))
     exp_k = _bf16_round(oracle.load().rope(W.bits(k_new), pos, THETA))
-    assert _ulp_distance(got_k, exp_k).max() <= 1
+    assert _ulp_distance(got_k, exp_k).max() == 0
     del k_pool, v_pool
     torch.cuda.empty_cache()

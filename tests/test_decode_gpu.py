@@ -6,7 +6,7 @@ import pytest
 import torch
 
 import workloads as W
-from gpu_util import TOL, device, max_err, oracle_decode, run_decode, say
+from gpu_util import TOL, all_rows_written, device, max_err, oracle_decode, run_decode, say
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -66,27 +66,58 @@ def test_workload_full_parity(spec):
     assert e_out <= TOL and e_lse <= TOL
 
 
+def _bench_config_layers(spec, layers, warm_steps=6):
+    """Decode the given layers of a full-size workload as the benchmark does:
+    one plan object with the speed feedback on (its weights moved by a few
+    warm steps first), one pa_plan, then every layer's run reusing it.
+    Returns {layer: (out, lse, k, v)} with the outputs on the host."""
+    import paged_gqa_decode_pa_amd as pa
+    dev = device()
+    ip, idx = W.decode_lists(spec)
+    q = W.normal_bf16((spec.batch, spec.num_qo_heads, spec.head_dim), spec.seed, dev)
+    idx_dev = torch.as_tensor(idx, device=dev)
+    scale = W.softmax_scale(spec.head_dim)
+    pools = {l: W.make_pools(spec.num_slots, spec.num_kv_heads, spec.head_dim,
+                             W.layer_seed(spec.seed, l), dev) for l in layers}
+    shape = (spec.batch, spec.num_qo_heads, spec.head_dim)
+    res = {}
+    with pa.Plan(spec.batch, int(ip[-1]), spec.num_qo_heads, spec.num_kv_heads, spec.head_dim) as plan:
+        warm = torch.empty(shape, dtype=torch.float32, device=dev)
+        for _ in range(warm_steps):
+            plan.plan(ip, flags=pa.PA_PLAN_SPEED_FEEDBACK)
+            for l in layers:
+                plan.decode(q, pools[l][0], pools[l][1], idx_dev, scale, warm)
+            torch.cuda.synchronize()
+        plan.plan(ip, flags=pa.PA_PLAN_SPEED_FEEDBACK)
+        outs = {l: (torch.full(shape, float("nan"), dtype=torch.float32, device=dev),
+                    torch.full(shape[:2], float("nan"), dtype=torch.float32, device=dev)) for l in layers}
+        for l in layers:
+            plan.decode(q, pools[l][0], pools[l][1], idx_dev, scale, outs[l][0], outs[l][1])
+        torch.cuda.synchronize()
+        say(f"  workgroup weights in use: {plan.workgroup_weights().min():.3f} .. "
+            f"{plan.workgroup_weights().max():.3f}")
+    for l in layers:
+        res[l] = (outs[l][0].cpu().numpy(), outs[l][1].cpu().numpy(), pools[l][0], pools[l][1])
+    return ip, idx, q, scale, res
+
+
 @pytest.mark.slow
-@pytest.mark.parametrize("spec,layer", [(W.BATCH64_SHARED_PREFIX, 0), (W.HEADDIM256_BATCH32, 0)],
-                         ids=["batch64_prefix", "headdim256"])
-def test_workload_sampled_parity(spec, layer):
-    """Full-size workloads in the benchmark's launch configuration; the oracle
-    computes a sample of rows (every request, a spread of heads)."""
-    say(f"sampled parity {spec.name} layer {layer}")
-    case = W.make_decode_case(spec, device(), layers=layer + 1)
-    idx_dev = torch.as_tensor(case.kv_indices, device=device())
-    k, v = case.k_pools[layer], case.v_pools[layer]
-    out, lse = run_decode(case.q, k, v, case.kv_indptr, idx_dev, case.sm_scale, spec.num_kv_heads)
-    Hq = spec.num_qo_heads
-    heads = [0, 1, Hq // 2 - 1, Hq // 2, Hq - 1]
-    sel = [b * Hq + h for b in range(spec.batch) for h in heads]
-    ref, ref_lse = oracle_decode(case.q, k, v, case.kv_indptr, case.kv_indices, case.sm_scale,
-                                 spec.num_kv_heads, sel=sel)
-    e_out, e_lse = max_err(out, ref, rows=sel), max_err(lse.reshape(-1, 1), ref_lse.reshape(-1, 1), rows=sel)
-    say(f"  max|d| out={e_out:.3g} lse={e_lse:.3g} over {len(sel)} rows")
-    assert e_out <= TOL and e_lse <= TOL
-    assert np.isfinite(out).all()
-    del case
+@pytest.mark.parametrize("spec,layers", [(W.BATCH64_SHARED_PREFIX, (0, 17, 35)),
+                                         (W.HEADDIM256_BATCH32, (0,))],
+                         ids=["batch64_prefix_layers_0_17_35", "headdim256"])
+def test_workload_full_rows(spec, layers):
+    """Full-size workloads in the benchmark's launch configuration (one plan
+    with the speed feedback, reused by every layer): every row of every
+    listed layer against the oracle."""
+    say(f"full-row parity {spec.name} layers {layers}")
+    ip, idx, q, scale, res = _bench_config_layers(spec, layers)
+    for l in layers:
+        out, lse, k, v = res[l]
+        ref, ref_lse = oracle_decode(q, k, v, ip, idx, scale, spec.num_kv_heads)
+        e_out, e_lse = max_err(out, ref), max_err(lse, ref_lse)
+        say(f"  layer {l}: max|d| out={e_out:.3g} lse={e_lse:.3g} over all {out.shape[0] * out.shape[1]} rows")
+        assert e_out <= TOL and e_lse <= TOL
+    del res
     torch.cuda.empty_cache()
 
 
@@ -128,7 +159,7 @@ def test_single_token_is_exact():
     out, _ = run_decode(q, k, v, ip, torch.as_tensor(idx, device=dev), W.softmax_scale(D), Hkv)
     vrows = v[torch.as_tensor(idx, device=dev).long()].float().cpu().numpy()   # [B, Hkv, D]
     want = np.repeat(vrows, Hq // Hkv, axis=1)
-    assert np.array_equal(out, want)
+    assert all_rows_written(out) and np.array_equal(out, want)
 
 
 def _slot_tag_pool(num_slots, Hkv, D, dev):
@@ -236,7 +267,7 @@ def test_plan_reused_across_layers():
     with pa.Plan(spec.batch, int(case.kv_indptr[-1]), 32, 8, 128) as plan:
         plan.plan(case.kv_indptr)
         for layer in range(3):
-            o = torch.empty((spec.batch, 32, 128), dtype=torch.float32, device=dev)
+            o = torch.full((spec.batch, 32, 128), float("nan"), dtype=torch.float32, device=dev)
             plan.decode(case.q, case.k_pools[layer], case.v_pools[layer], idx_dev, case.sm_scale, o)
             outs.append(o)
         torch.cuda.synchronize()
@@ -311,7 +342,8 @@ def test_merge_protocol_repeatable(flags_n):
     idx = torch.as_tensor(case.kv_indices, device=dev)
     flags = pa.PA_PLAN_FORCE_SPLITS(flags_n) if flags_n else 0
     capacity = max(int(case.kv_indptr[-1]), spec.batch * flags_n * 256)
-    outs = [torch.empty((spec.batch, 32, 128), dtype=torch.float32, device=dev) for _ in range(40)]
+    outs = [torch.full((spec.batch, 32, 128), float("nan"), dtype=torch.float32, device=dev)
+            for _ in range(40)]
     with pa.Plan(spec.batch, capacity, 32, 8, 128) as plan:
         plan.plan(case.kv_indptr, flags=flags)
         for o in outs:
@@ -323,3 +355,51 @@ def test_merge_protocol_repeatable(flags_n):
     ref, _ = oracle_decode(case.q, case.k_pools[0], case.v_pools[0], case.kv_indptr,
                            case.kv_indices, case.sm_scale, 8)
     assert max_err(first, ref) <= TOL
+
+
+def test_plan_info_and_binding_shape_checks():
+    """pa_plan_info reports the last plan; the binding rejects tensors that do
+    not match it before anything reaches the C ABI."""
+    import paged_gqa_decode_pa_amd as pa
+    say("plan info and binding shape checks")
+    dev = device()
+    ip, idx, q, k, v = _case([10, 20, 30], 32, 8, 128, 100, seed=27)
+    idx_dev = torch.as_tensor(idx, device=dev)
+    out = torch.full((3, 32, 128), float("nan"), dtype=torch.float32, device=dev)
+    with pa.Plan(4, 100, 32, 8, 128) as plan:
+        assert plan.info()["mode"] == 0
+        plan.plan(ip)
+        assert plan.info() == dict(mode=1, rows=3, num_qo_heads=32, num_kv_heads=8, head_dim=128)
+        with pytest.raises(ValueError):                      # q of another batch
+            plan.decode(q[:2].contiguous(), k, v, idx_dev, 0.1, out[:2])
+        with pytest.raises(ValueError):                      # out too small
+            plan.decode(q, k, v, idx_dev, 0.1, out[:2])
+        with pytest.raises(ValueError):                      # strided slot ids
+            plan.decode(q, k, v, torch.as_tensor(np.repeat(idx, 2), device=dev)[::2], 0.1, out)
+        with pytest.raises(ValueError):                      # V pool shorter than num_slots
+            plan.decode(q, k, v[:50], idx_dev, 0.1, out, num_slots=100)
+        plan.decode(q, k, v, idx_dev, W.softmax_scale(128), out)
+        torch.cuda.synchronize()
+    ref, ref_lse = oracle_decode(q, k, v, ip, idx, W.softmax_scale(128), 8)
+    assert max_err(out.cpu().numpy(), ref) <= TOL
+
+
+def test_index_check_debug_mode(monkeypatch):
+    """With the PA_CHECK debug option, a run whose slot list holds an id
+    outside the pool is refused on the host (the kernel never sees it)."""
+    import paged_gqa_decode_pa_amd as pa
+    say("PA_CHECK debug mode")
+    monkeypatch.setattr(pa, "CHECK_INDICES", True)
+    dev = device()
+    ip, idx, q, k, v = _case([10, 20], 32, 8, 128, 100, seed=28)
+    bad = idx.copy()
+    bad[13] = 100
+    out = torch.full((2, 32, 128), float("nan"), dtype=torch.float32, device=dev)
+    with pa.Plan(2, 30, 32, 8, 128) as plan:
+        plan.plan(ip)
+        with pytest.raises(pa.PAError) as e:
+            plan.decode(q, k, v, torch.as_tensor(bad, device=dev), 0.1, out)
+        assert e.value.status == pa.PA_ERR_INVALID_ARG and "kv_indices[13]" in e.value.detail
+        plan.decode(q, k, v, torch.as_tensor(idx, device=dev), W.softmax_scale(128), out)
+        torch.cuda.synchronize()
+    assert all_rows_written(out.cpu().numpy())

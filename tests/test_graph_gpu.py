@@ -3,7 +3,7 @@
 A plan is computed once per step and every layer's run reads the plan's
 device tables, so the runs of one step can be captured once and replayed
 (the plan/run split of the Agent-Infer page, section "分页 KV 缓存"; graph
-capture of the decode step is stage 5 of the table in its section "优化历程").
+capture of the decode step is stage 6 of the table in its section "优化历程").
 Runs allocate nothing and reset their own arrival counters, so a replay must
 give the eager result bit for bit.  Each replay follows eager work (the
 outputs are poisoned) and a synchronisation, and every replay is checked."""
@@ -50,8 +50,8 @@ def test_decode_layers_graph_replay(splits):
     pools = [W.make_pools(N, Hkv, D, 40 + l, dev) for l in range(LAYERS)]
     idx_dev = torch.as_tensor(idx, device=dev)
     scale = W.softmax_scale(D)
-    outs = [torch.empty((B, Hq, D), dtype=torch.float32, device=dev) for _ in range(LAYERS)]
-    lses = [torch.empty((B, Hq), dtype=torch.float32, device=dev) for _ in range(LAYERS)]
+    outs = [torch.full((B, Hq, D), float("nan"), dtype=torch.float32, device=dev) for _ in range(LAYERS)]
+    lses = [torch.full((B, Hq), float("nan"), dtype=torch.float32, device=dev) for _ in range(LAYERS)]
     with pa.Plan(B, int(ip[-1]), Hq, Hkv, D) as plan:
         plan.plan(ip, flags=pa.PA_PLAN_FORCE_SPLITS(splits) if splits else 0)
 
@@ -62,8 +62,9 @@ def test_decode_layers_graph_replay(splits):
         step(torch.cuda.current_stream())
         torch.cuda.synchronize()
         eager = [o.cpu().numpy() for o in outs] + [x.cpu().numpy() for x in lses]
-        ref, ref_lse = oracle_decode(q, pools[0][0], pools[0][1], ip, idx, scale, Hkv)
-        assert max_err(eager[0], ref) <= TOL and max_err(eager[LAYERS], ref_lse) <= TOL
+        for l in range(LAYERS):
+            ref, ref_lse = oracle_decode(q, pools[l][0], pools[l][1], ip, idx, scale, Hkv)
+            assert max_err(eager[l], ref) <= TOL and max_err(eager[LAYERS + l], ref_lse) <= TOL
         _replay_and_check(step, outs + lses, eager)
 
 
@@ -80,8 +81,8 @@ def test_prefill_layers_graph_replay():
     pools = [W.make_pools(N, Hkv, D, 50 + l, dev) for l in range(LAYERS)]
     idx_dev = torch.as_tensor(idx, device=dev)
     scale = W.softmax_scale(D)
-    outs = [torch.empty((T, Hq, D), dtype=torch.float32, device=dev) for _ in range(LAYERS)]
-    lses = [torch.empty((T, Hq), dtype=torch.float32, device=dev) for _ in range(LAYERS)]
+    outs = [torch.full((T, Hq, D), float("nan"), dtype=torch.float32, device=dev) for _ in range(LAYERS)]
+    lses = [torch.full((T, Hq), float("nan"), dtype=torch.float32, device=dev) for _ in range(LAYERS)]
     with pa.Plan(len(reqs), int(ip[-1]), Hq, Hkv, D, max_q_total=T) as plan:
         plan.plan(ip, qo)
 
@@ -92,6 +93,7 @@ def test_prefill_layers_graph_replay():
         step(torch.cuda.current_stream())
         torch.cuda.synchronize()
         eager = [o.cpu().numpy() for o in outs] + [x.cpu().numpy() for x in lses]
-        ref, ref_lse = oracle_prefill(q, pools[0][0], pools[0][1], qo, ip, idx, scale, Hkv)
-        assert max_err(eager[0], ref) <= TOL and max_err(eager[LAYERS], ref_lse) <= TOL
+        for l in range(LAYERS):
+            ref, ref_lse = oracle_prefill(q, pools[l][0], pools[l][1], qo, ip, idx, scale, Hkv)
+            assert max_err(eager[l], ref) <= TOL and max_err(eager[LAYERS + l], ref_lse) <= TOL
         _replay_and_check(step, outs + lses, eager)

@@ -85,6 +85,12 @@ BATCH64_SHARED_PREFIX = DecodeSpec(
     "b64_l2048_8192_prefix16x4x1024_36layers", batch=64, num_qo_heads=32, num_kv_heads=8,
     head_dim=128, num_slots=600_000, len_lo=2048, len_hi=8192, seed=1002,
     prefix_group_size=4, prefix_len=1024, num_layers=36)
+# The batch-64 workload with every list in the 4k-8k range (the same shared
+# prefixes and pool): the spec point of batch 64 at 4-8k context.
+BATCH64_4K_8K = DecodeSpec(
+    "b64_l4096_8192_prefix16x4x1024_36layers", batch=64, num_qo_heads=32, num_kv_heads=8,
+    head_dim=128, num_slots=600_000, len_lo=4096, len_hi=8192, seed=1007,
+    prefix_group_size=4, prefix_len=1024, num_layers=36)
 HEADDIM256_BATCH32 = DecodeSpec(
     "hd256_b32_l1024_16384", batch=32, num_qo_heads=16, num_kv_heads=4, head_dim=256,
     num_slots=400_000, len_lo=1024, len_hi=16384, seed=1003)
@@ -101,7 +107,7 @@ PREFILL_CHUNK64 = PrefillSpec(
     "prefill_8x4096_chunk64", batch=8, num_qo_heads=32, num_kv_heads=8, head_dim=128,
     num_slots=131072, cached_len=4096, chunk_len=64, seed=1005)
 
-DECODE_SPECS = [SINGLE_REQUEST_256, QWEN3_4B_BATCH8, BATCH64_SHARED_PREFIX, HEADDIM256_BATCH32]
+DECODE_SPECS = [SINGLE_REQUEST_256, QWEN3_4B_BATCH8, BATCH64_SHARED_PREFIX, BATCH64_4K_8K, HEADDIM256_BATCH32]
 PREFILL_SPECS = [PREFILL_CHUNK512, PREFILL_CHUNK64]
 
 
@@ -228,11 +234,6 @@ def make_pools_e4m3(num_slots: int, num_kv_heads: int, head_dim: int, seed: int,
     k = normal_e4m3((num_slots, num_kv_heads, head_dim), seed * 2 + 0, k_scale, device)
     v = normal_e4m3((num_slots, num_kv_heads, head_dim), seed * 2 + 1, v_scale, device)
     return k, v
-
-
-def codes(t: "torch.Tensor") -> np.ndarray:
-    """uint8 codes of an E4M3 tensor, on the host."""
-    return t.detach().contiguous().view(torch.uint8).cpu().numpy()
 
 
 def layer_seed(seed: int, layer: int) -> int:
