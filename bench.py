@@ -65,6 +65,19 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), or the platform's."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def algorithmic_bytes(spec, kv_indptr, kv_indices, kv_elem_bytes: int = 2) -> int:
     import numpy as np
     B, Hq, Hkv, D = spec.batch, spec.num_qo_heads, spec.num_kv_heads, spec.head_dim
@@ -141,11 +154,13 @@ def cpu_baseline(case, spec, bytes_per_layer, seconds, gpu_out_layer0, fp8=False
         "value": round(bytes_per_layer * reps / dt / 1e9, 3),
         "unit": "GB/s",
         "cores": ref.num_threads(),
+        "cpu_model": cpu_model(),
+        "host_cpus": os.cpu_count(),
         "kind": "oracle",
         "us_per_layer": round(dt / reps * 1e6, 1),
         "sample": f"layer 0 of the same workload, all {spec.batch}x{spec.num_qo_heads} rows, "
                   f"{reps} repetition(s), {dt:.1f} s"
-                  + (" (each widening the whole E4M3 pools first)" if fp8 else ""),
+                  + (" (the oracle reads the E4M3 codes directly)" if fp8 else ""),
     }, err
 
 
@@ -199,6 +214,8 @@ def cpu_baseline_prefill(case, spec, flops_per_row_entry, seconds):
         "value": round(entries * flops_per_row_entry * reps / dt / 1e12, 5),
         "unit": "TFLOP/s",
         "cores": ref.num_threads(),
+        "cpu_model": cpu_model(),
+        "host_cpus": os.cpu_count(),
         "kind": "oracle",
         "sample": f"{rows.size} rows (last chunk token of each request, all heads), "
                   f"{reps} repetition(s), {dt:.1f} s",
@@ -386,7 +403,8 @@ def cpu_baseline_append(k_new, v_new, q, loc, pos, num_slots, seconds):
         if time.perf_counter() - t0 >= seconds:
             break
     dt = time.perf_counter() - t0
-    return {"value": round(dt / reps * 1e6, 2), "unit": "us", "cores": ref.num_threads(), "kind": "oracle",
+    return {"value": round(dt / reps * 1e6, 2), "unit": "us", "cores": ref.num_threads(),
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(), "kind": "oracle",
             "sample": f"one call of the same shape ({T} tokens, {q.shape[1]} query and {Hkv} KV heads, "
                       f"D={D}), {reps} repetitions, {dt:.1f} s"}
 
@@ -402,7 +420,7 @@ def main():
     ap.add_argument("--flags", type=int, default=0x2,
                     help="pa_plan flags (default PA_PLAN_SPEED_FEEDBACK: per-compute-unit budgets from measured speed)")
     ap.add_argument("--workload", default="batch64",
-                    choices=["batch64", "single_request", "batch8", "hd256", "system_prompt",
+                    choices=["batch64", "batch64_4k8k", "single_request", "batch8", "hd256", "system_prompt",
                              "prefill_chunk512", "prefill_chunk64", "append", "copy"])
     ap.add_argument("--kv", default="bf16", choices=["bf16", "fp8"],
                     help="decode: pool element type (fp8 = OCP E4M3 codes with per-pool scales)")
@@ -437,7 +455,8 @@ def main():
     import paged_gqa_decode_pa_amd as pa
     import workloads as W
 
-    spec = {"batch64": W.BATCH64_SHARED_PREFIX, "single_request": W.SINGLE_REQUEST_256,
+    spec = {"batch64": W.BATCH64_SHARED_PREFIX, "batch64_4k8k": W.BATCH64_4K_8K,
+            "single_request": W.SINGLE_REQUEST_256,
             "batch8": W.QWEN3_4B_BATCH8, "hd256": W.HEADDIM256_BATCH32,
             "system_prompt": W.SYSTEM_PROMPT_B64}[args.workload]
     # every decode workload runs 36 layers per step, each with its own pools
@@ -514,24 +533,33 @@ def main():
         else:
             layer_runs(stream)
 
-    for _ in range(args.warmup):
+    wmarks = [torch.cuda.Event(enable_timing=True) for _ in range(args.warmup + 1)]
+    wmarks[0].record(stream)
+    for i in range(args.warmup):
         step()
+        wmarks[i + 1].record(stream)
     torch.cuda.synchronize()
-    log("warmup done")
+    log("warmup done; per-step ms: " + " ".join(f"{wmarks[i].elapsed_time(wmarks[i + 1]):.3f}"
+                                                for i in range(args.warmup)))
 
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
 
-    # timed region: K steps bracketed by HIP events on the launch stream
+    # timed region: K steps bracketed by HIP events on the launch stream, with
+    # one more event between consecutive steps for the per-step spread
     plan_host_s.clear()
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    start.record(stream)
-    for _ in range(args.steps):
+    marks[0].record(stream)
+    for i in range(args.steps):
         step()
-    end.record(stream)
+        marks[i + 1].record(stream)
     torch.cuda.synchronize()
-    ms_per_step = start.elapsed_time(end) / args.steps
-    log(f"step {ms_per_step:.3f} ms ({ms_per_step * 1e3 / layers:.1f} us per layer)")
+    ms_per_step = marks[0].elapsed_time(marks[-1]) / args.steps
+    step_ms = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)])
+    log(f"step {ms_per_step:.3f} ms ({ms_per_step * 1e3 / layers:.1f} us per layer); per step "
+        f"median {np.median(step_ms):.3f} min {step_ms.min():.3f} max {step_ms.max():.3f} ms")
+    log("per-step ms: " + " ".join(f"{t:.3f}" for t in step_ms))
     wgw = plan.workgroup_weights()
     wg_weight_range = [round(float(wgw.min()), 3), round(float(wgw.max()), 3)]
     if args.flags & pa.PA_PLAN_SPEED_FEEDBACK:
@@ -607,6 +635,9 @@ def main():
             "workgroup_weight_range": wg_weight_range,
         },
         "us_per_step_layer": round(ms_per_step * 1e3 / layers, 2),
+        "step_ms": {"mean": round(ms_per_step, 4), "median": round(float(np.median(step_ms)), 4),
+                    "min": round(float(step_ms.min()), 4), "max": round(float(step_ms.max()), 4)},
+        "us_per_step_layer_median": round(float(np.median(step_ms)) * 1e3 / layers, 2),
         "frac_of_peak": round(value / HBM_PEAK_GBS, 4),
         "ms_per_step_with_kernel_events": round(ms_per_step_events, 4),
         "plan_host_us": round(plan_host_us, 1),

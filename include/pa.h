@@ -209,7 +209,8 @@ pa_status pa_decode_run(const pa_plan_t *plan, const void *q, const void *k_pool
  * E4M3 codes (1 byte per element, same [slots, Hkv, D] layout and slot
  * stride in elements = bytes), and the row values are k_scale * code and
  * v_scale * code (one scale per pool).  Quantised KV is on the Agent-Infer
- * page's roadmap (section "未来规划": FP8 among the quantisation formats); the
+ * page's roadmap (section "模型支持与发展路线图": FP8 among the quantisation
+ * formats); the
  * format and the per-pool scales are this library's reading.  Same plan,
  * arguments, output and errors as pa_decode_run, plus PA_ERR_INVALID_ARG for
  * a non-finite scale.  Code 0x7F / 0xFF (NaN) in a referenced row makes the
@@ -427,6 +428,37 @@ pa_status pa_profile_end(pa_plan_t *plan, double *total_ms, int32_t *n_launches)
  * staging buffer is reused).  PA_ERR_INVALID_ARG for null pointers.
  */
 pa_status pa_plan_host_timing(const pa_plan_t *plan, double *total_us, double *wait_us);
+
+/*
+ * pa_plan_info: what the last successful pa_plan / pa_plan_cascade call on
+ * this plan set up, so that a caller can size its tensors for the runs.
+ *   *mode: 0 no plan yet, 1 decode, 2 prefill;
+ *   *rows: query rows a run reads and writes (decode: batch; prefill: the
+ *          total chunk rows qo_indptr[batch]);
+ *   *num_qo_heads, *num_kv_heads, *head_dim: as given to pa_plan_create.
+ * A run reads q [rows, Hq, D] and writes out [rows, Hq, D] and lse [rows, Hq].
+ * Any output pointer may be NULL.  PA_ERR_INVALID_ARG for a null plan.
+ */
+pa_status pa_plan_info(const pa_plan_t *plan, int32_t *mode, int32_t *rows,
+                       int32_t *num_qo_heads, int32_t *num_kv_heads, int32_t *head_dim);
+
+/*
+ * pa_check_kv_indices: opt-in bounds check of a step's slot lists on the
+ * host (the runs do not check slot ids on the device: an id outside
+ * [0, num_slots) is undefined behaviour there).  For callers that keep a host
+ * copy of the lists, or debug runs that copy them back.
+ *   kv_indptr_host [batch+1] and kv_indices_host [kv_indptr[batch]], host
+ *   memory, as passed to pa_plan and the runs; num_slots as for the runs.
+ * Returns PA_OK when kv_indptr is a valid CSR offset array (starts at 0,
+ * non-decreasing) and every id is in [0, num_slots).  Otherwise
+ * PA_ERR_INVALID_ARG, with *first_bad (if not NULL) set to the position in
+ * kv_indices of the first out-of-range id (-1 for a bad kv_indptr), and
+ * pa_last_error_detail() naming the request, the position and the id.
+ * Reads only its arguments; no GPU work.
+ */
+pa_status pa_check_kv_indices(const int32_t *kv_indptr_host, int32_t batch,
+                              const int32_t *kv_indices_host, int64_t num_slots,
+                              int64_t *first_bad);
 
 /* Library version as major*10000 + minor*100 + patch. */
 int32_t pa_version(void);

@@ -9,6 +9,12 @@ Importing this package loads ``libpa.so`` (built in-tree by
 ``paged_gqa_decode_pa_amd.build.build()``) and fails loudly if it is missing.
 torch is imported first so that the library binds to the HIP runtime torch
 already loaded.
+
+Debug option: with the environment variable ``PA_CHECK=1`` set when the
+package is imported, every run made through a ``Plan`` object first copies
+``kv_indices`` to the host and checks it against the plan's slot lists and
+the pool size with ``pa_check_kv_indices`` (a host synchronisation per run;
+off by default, since the kernels do not check slot ids).
 """
 from __future__ import annotations
 
@@ -122,10 +128,16 @@ def _load() -> ctypes.CDLL:
     lib.pa_decode_run_fp8.restype = ctypes.c_int
     lib.pa_kv_append.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp, vp, i64, i64, vp]
     lib.pa_kv_append.restype = ctypes.c_int
+    lib.pa_plan_info.argtypes = [vp, i32p, i32p, i32p, i32p, i32p]
+    lib.pa_plan_info.restype = ctypes.c_int
+    lib.pa_check_kv_indices.argtypes = [i32p, i32, i32p, i64, ctypes.POINTER(ctypes.c_int64)]
+    lib.pa_check_kv_indices.restype = ctypes.c_int
     return lib
 
 
 _lib = _load()
+
+CHECK_INDICES = os.environ.get("PA_CHECK", "0") not in ("", "0")
 
 
 def pa_strerror(status: int) -> str:
@@ -213,21 +225,65 @@ def pa_plan_cascade(plan, kv_indptr, group_indptr, prefix_len, flags: int = 0,
                                 _stream(stream)), "pa_plan_cascade")
 
 
+def pa_plan_info(plan):
+    """-> dict(mode, rows, num_qo_heads, num_kv_heads, head_dim) of the last
+    pa_plan on this plan (mode 0: none, 1: decode, 2: prefill; a run reads
+    q [rows, Hq, D] and writes out [rows, Hq, D], lse [rows, Hq])."""
+    vals = [ctypes.c_int32() for _ in range(5)]
+    _check(_lib.pa_plan_info(plan, *[ctypes.byref(v) for v in vals]), "pa_plan_info")
+    return dict(zip(("mode", "rows", "num_qo_heads", "num_kv_heads", "head_dim"),
+                    (v.value for v in vals)))
+
+
+def pa_check_kv_indices(kv_indptr, kv_indices, num_slots: int) -> None:
+    """Host-side bounds check of slot lists: raises PAError (PA_ERR_INVALID_ARG,
+    naming the request, position and id) if an id is outside [0, num_slots)
+    or kv_indptr is not a valid CSR offset array.  kv_indices may be a device
+    tensor (copied to the host)."""
+    ip = _host_i32(kv_indptr)
+    idx = _host_i32(kv_indices)
+    if idx.size < int(ip[-1]):
+        raise ValueError("kv_indices shorter than kv_indptr[-1]")
+    bad = ctypes.c_int64()
+    _check(_lib.pa_check_kv_indices(_i32p(ip), ip.size - 1, _i32p(idx), int(num_slots),
+                                    ctypes.byref(bad)), "pa_check_kv_indices")
+
+
+def _check_run_shapes(plan, q, k_pool, v_pool, kv_indices, out, lse, num_slots):
+    """Sizes the C ABI cannot see: the tensors must match the last pa_plan
+    (rows x Hq x D), the pools must hold num_slots slots, and kv_indices must
+    be one packed int32 array."""
+    info = pa_plan_info(plan)
+    rows, Hq, D = info["rows"], info["num_qo_heads"], info["head_dim"]
+    if kv_indices.dtype != torch.int32:
+        raise TypeError("kv_indices must be int32")
+    if kv_indices.dim() != 1 or not kv_indices.is_contiguous():
+        raise ValueError("kv_indices must be a contiguous 1-D tensor")
+    if info["mode"] != 0:
+        if q.dim() != 3 or tuple(q.shape) != (rows, Hq, D):
+            raise ValueError(f"q must be [{rows}, {Hq}, {D}] for this plan, got {tuple(q.shape)}")
+        if out.numel() != rows * Hq * D:
+            raise ValueError(f"out must hold {rows}x{Hq}x{D} values, has {out.numel()}")
+        if lse is not None and lse.numel() != rows * Hq:
+            raise ValueError(f"lse must hold {rows}x{Hq} values, has {lse.numel()}")
+    if min(k_pool.shape[0], v_pool.shape[0]) < num_slots:
+        raise ValueError(f"the pools hold fewer than num_slots={num_slots} slots")
+
+
 def _run(fn, where, plan, q, k_pool, v_pool, kv_indices, sm_scale, out, lse,
          num_slots, slot_stride, stream):
     head_dim = q.shape[-1]
     if slot_stride is None:
         slot_stride = _pool_stride(k_pool, v_pool, head_dim)
     if num_slots is None:
-        num_slots = k_pool.shape[0]
-    if kv_indices.dtype != torch.int32:
-        raise TypeError("kv_indices must be int32")
+        num_slots = min(k_pool.shape[0], v_pool.shape[0])
     if out.dtype != torch.float32 or not out.is_contiguous():
         raise TypeError("out must be a contiguous float32 tensor")
     if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
         raise TypeError("lse must be a contiguous float32 tensor")
     if not q.is_contiguous():
         raise ValueError("q must be contiguous")
+    _check_run_shapes(plan, q, k_pool, v_pool, kv_indices, out, lse, num_slots)
     _check(fn(plan, _dev_ptr(q, "q", torch.bfloat16), _dev_ptr(k_pool, "k_pool", torch.bfloat16),
               _dev_ptr(v_pool, "v_pool", torch.bfloat16), int(num_slots), int(slot_stride),
               _dev_ptr(kv_indices, "kv_indices"), float(sm_scale), _dev_ptr(out, "out"),
@@ -250,15 +306,14 @@ def pa_decode_run_fp8(plan, q, k_pool, v_pool, kv_indices, sm_scale, k_scale, v_
     if slot_stride is None:
         slot_stride = _pool_stride(k_pool, v_pool, head_dim)
     if num_slots is None:
-        num_slots = k_pool.shape[0]
-    if kv_indices.dtype != torch.int32:
-        raise TypeError("kv_indices must be int32")
+        num_slots = min(k_pool.shape[0], v_pool.shape[0])
     if out.dtype != torch.float32 or not out.is_contiguous():
         raise TypeError("out must be a contiguous float32 tensor")
     if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
         raise TypeError("lse must be a contiguous float32 tensor")
     if not q.is_contiguous():
         raise ValueError("q must be contiguous")
+    _check_run_shapes(plan, q, k_pool, v_pool, kv_indices, out, lse, num_slots)
     _check(_lib.pa_decode_run_fp8(plan, _dev_ptr(q, "q", torch.bfloat16), _dev_ptr(k_pool, "k_pool"),
                                   _dev_ptr(v_pool, "v_pool"), int(num_slots), int(slot_stride),
                                   _dev_ptr(kv_indices, "kv_indices"), float(sm_scale), float(k_scale),
@@ -435,6 +490,15 @@ class Plan:
 
     def plan(self, kv_indptr, qo_indptr=None, flags: int = 0, stream=None) -> None:
         pa_plan(self.handle, kv_indptr, qo_indptr, flags, stream)
+        self._kv_indptr = _host_i32(kv_indptr) if CHECK_INDICES else None
+
+    def info(self) -> dict:
+        return pa_plan_info(self.handle)
+
+    def _debug_check(self, kv_indices, k_pool, kw) -> None:
+        if CHECK_INDICES and getattr(self, "_kv_indptr", None) is not None:
+            n = kw.get("num_slots")
+            pa_check_kv_indices(self._kv_indptr, kv_indices, k_pool.shape[0] if n is None else n)
 
     def xcd_weights(self) -> np.ndarray:
         return pa_plan_xcd_weights(self.handle)
@@ -448,16 +512,20 @@ class Plan:
     def plan_cascade(self, kv_indptr, group_indptr, prefix_len, flags: int = 0,
                      stream=None) -> None:
         pa_plan_cascade(self.handle, kv_indptr, group_indptr, prefix_len, flags, stream)
+        self._kv_indptr = _host_i32(kv_indptr) if CHECK_INDICES else None
 
     def decode(self, q, k_pool, v_pool, kv_indices, sm_scale, out, lse=None, **kw) -> None:
+        self._debug_check(kv_indices, k_pool, kw)
         pa_decode_run(self.handle, q, k_pool, v_pool, kv_indices, sm_scale, out, lse, **kw)
 
     def decode_fp8(self, q, k_pool, v_pool, kv_indices, sm_scale, k_scale, v_scale, out, lse=None,
                    **kw) -> None:
+        self._debug_check(kv_indices, k_pool, kw)
         pa_decode_run_fp8(self.handle, q, k_pool, v_pool, kv_indices, sm_scale, k_scale, v_scale, out,
                           lse, **kw)
 
     def prefill(self, q, k_pool, v_pool, kv_indices, sm_scale, out, lse=None, **kw) -> None:
+        self._debug_check(kv_indices, k_pool, kw)
         pa_prefill_chunk_run(self.handle, q, k_pool, v_pool, kv_indices, sm_scale, out, lse, **kw)
 
     def close(self) -> None:

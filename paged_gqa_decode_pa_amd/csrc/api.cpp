@@ -747,6 +747,58 @@ pa_status pa_kv_append(const void *k_new, const void *v_new, void *q, const int3
     return PA_OK;
 }
 
+pa_status pa_plan_info(const pa_plan_t *p, int32_t *mode, int32_t *rows, int32_t *num_qo_heads,
+                       int32_t *num_kv_heads, int32_t *head_dim) {
+    if (!p)
+        return fail(PA_ERR_INVALID_ARG, "plan is null");
+    if (mode)
+        *mode = (int32_t)p->mode;
+    if (rows)
+        *rows = p->mode == pa::PlanMode::kPrefill ? p->q_total
+                                                   : (p->mode == pa::PlanMode::kDecode ? p->batch : 0);
+    if (num_qo_heads)
+        *num_qo_heads = p->num_qo_heads;
+    if (num_kv_heads)
+        *num_kv_heads = p->num_kv_heads;
+    if (head_dim)
+        *head_dim = p->head_dim;
+    return PA_OK;
+}
+
+pa_status pa_check_kv_indices(const int32_t *kv_indptr_host, int32_t batch,
+                              const int32_t *kv_indices_host, int64_t num_slots,
+                              int64_t *first_bad) {
+    if (first_bad)
+        *first_bad = -1;
+    if (batch < 0 || num_slots < 0)
+        return fail(PA_ERR_INVALID_ARG, "batch and num_slots must be >= 0");
+    if (batch == 0)
+        return PA_OK;
+    if (!kv_indptr_host)
+        return fail(PA_ERR_INVALID_ARG, "kv_indptr_host is null");
+    if (kv_indptr_host[0] != 0)
+        return fail(PA_ERR_INVALID_ARG, "kv_indptr[0] is not 0");
+    for (int32_t b = 0; b < batch; b++)
+        if (kv_indptr_host[b + 1] < kv_indptr_host[b])
+            return fail(PA_ERR_INVALID_ARG,
+                        "kv_indptr decreases at request " + std::to_string(b));
+    if (kv_indptr_host[batch] > 0 && !kv_indices_host)
+        return fail(PA_ERR_INVALID_ARG, "kv_indices_host is null");
+    for (int32_t b = 0; b < batch; b++)
+        for (int32_t j = kv_indptr_host[b]; j < kv_indptr_host[b + 1]; j++) {
+            const int32_t id = kv_indices_host[j];
+            if (id < 0 || (int64_t)id >= num_slots) {
+                if (first_bad)
+                    *first_bad = j;
+                return fail(PA_ERR_INVALID_ARG,
+                            "slot id " + std::to_string(id) + " at kv_indices[" + std::to_string(j) +
+                                "] (request " + std::to_string(b) + ") is outside [0, " +
+                                std::to_string(num_slots) + ")");
+            }
+        }
+    return PA_OK;
+}
+
 pa_status pa_plan_host_timing(const pa_plan_t *p, double *total_us, double *wait_us) {
     if (!p || !total_us || !wait_us)
         return fail(PA_ERR_INVALID_ARG, "null argument");

@@ -4,6 +4,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import paged_gqa_decode_pa_amd as pa
@@ -76,3 +77,37 @@ def test_header_compiles_standalone(lang, std, tmp_path):
     r = subprocess.run([cc, "-fsyntax-only", "-x", lang, f"-std={std}", "-Wall", "-Wextra",
                         "-pedantic", "-Werror", HEADER], capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
+
+
+def test_check_kv_indices_accepts_valid_lists():
+    ip = np.array([0, 3, 3, 7], np.int32)
+    idx = np.array([0, 9, 4, 1, 2, 3, 9], np.int32)
+    pa.pa_check_kv_indices(ip, idx, 10)
+    pa.pa_check_kv_indices(np.array([0], np.int32), np.zeros(0, np.int32), 0)   # empty batch
+
+
+@pytest.mark.parametrize("bad_pos,bad_id", [(0, -1), (4, 10), (6, 1 << 30), (2, -2147483648)])
+def test_check_kv_indices_reports_the_first_bad_id(bad_pos, bad_id):
+    ip = np.array([0, 3, 3, 7], np.int32)
+    idx = np.array([0, 9, 4, 1, 2, 3, 9], np.int32)
+    idx[bad_pos] = bad_id
+    with pytest.raises(pa.PAError) as e:
+        pa.pa_check_kv_indices(ip, idx, 10)
+    assert e.value.status == pa.PA_ERR_INVALID_ARG
+    assert f"kv_indices[{bad_pos}]" in e.value.detail and str(bad_id) in e.value.detail
+    first = ctypes.c_int64()
+    st = pa._lib.pa_check_kv_indices(pa._i32p(ip), 3, pa._i32p(idx), 10, ctypes.byref(first))
+    assert st == pa.PA_ERR_INVALID_ARG and first.value == bad_pos
+
+
+@pytest.mark.parametrize("ip", [[1, 3], [0, 3, 2]])
+def test_check_kv_indices_rejects_bad_offsets(ip):
+    ip = np.asarray(ip, np.int32)
+    first = ctypes.c_int64(99)
+    idx = np.zeros(8, np.int32)
+    st = pa._lib.pa_check_kv_indices(pa._i32p(ip), ip.size - 1, pa._i32p(idx), 10, ctypes.byref(first))
+    assert st == pa.PA_ERR_INVALID_ARG and first.value == -1
+
+
+def test_plan_info_null_plan():
+    assert pa._lib.pa_plan_info(ctypes.c_void_p(0), None, None, None, None, None) == pa.PA_ERR_INVALID_ARG
