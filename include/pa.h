@@ -233,6 +233,37 @@ pa_status pa_prefill_chunk_run(const pa_plan_t *plan, const void *q, const void 
                                const int32_t *kv_indices, float sm_scale, float *out,
                                float *lse, pa_stream_t stream);
 
+/*
+ * pa_decode_run_noalloc: pa_decode_run without a plan object and without any
+ * allocation, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).  The
+ * split of the lists over workgroups is computed on the device on every call
+ * (an equal split of the (KV head, request) entries, no XCD placement or
+ * speed feedback), and the work table, partial results and arrival counters
+ * live in a workspace inside the library: a device array of about 9.4 MiB
+ * that each GPU the library runs on holds until the process ends.
+ *   q, k_pool, v_pool, num_slots, slot_stride, kv_indices, sm_scale, out,
+ *   lse: as in pa_decode_run (same layout, same result up to summation
+ *   order, out and lse written for every request);
+ *   kv_indptr: DEVICE int32 [batch + 1] CSR offsets (kv_indptr[0] = 0,
+ *   non-decreasing, kv_indptr[batch] <= PA_MAX_KV_TOTAL); offsets that break
+ *   these rules are detected on the device and give NaN in out and lse;
+ *   batch <= 4096, batch * num_kv_heads <= 16384; head shapes as in
+ *   pa_plan_create.
+ * Two kernels on `stream`; nothing is allocated, freed or synchronised.
+ * Every call on one GPU uses that GPU's single workspace, so calls that can
+ * run at the same time on one GPU (other streams, or other host threads) race
+ * and must be ordered by the caller; calls on one stream are fine.  Errors:
+ * PA_ERR_INVALID_ARG / PA_ERR_UNSUPPORTED as pa_plan_create and
+ * pa_decode_run, PA_ERR_CAPACITY above the limits (nothing is enqueued),
+ * PA_ERR_HIP if the workspace cannot be located on the current device.
+ */
+pa_status pa_decode_run_noalloc(const void *q, const void *k_pool, const void *v_pool,
+                                int64_t num_slots, int64_t slot_stride, const int32_t *kv_indptr,
+                                const int32_t *kv_indices, int32_t batch, int32_t num_qo_heads,
+                                int32_t num_kv_heads, int32_t head_dim, float sm_scale, float *out,
+                                float *lse, pa_stream_t stream);
+
 /* Release everything pa_plan_create allocated.  Waits for the plan's pending
  * uploads; the caller must not destroy a plan that enqueued runs still use. */
 void pa_plan_destroy(pa_plan_t *plan);

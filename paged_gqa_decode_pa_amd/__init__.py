@@ -132,6 +132,8 @@ def _load() -> ctypes.CDLL:
     lib.pa_plan_info.restype = ctypes.c_int
     lib.pa_check_kv_indices.argtypes = [i32p, i32, i32p, i64, ctypes.POINTER(ctypes.c_int64)]
     lib.pa_check_kv_indices.restype = ctypes.c_int
+    lib.pa_decode_run_noalloc.argtypes = [vp, vp, vp, i64, i64, vp, vp, i32, i32, i32, i32, f32, vp, vp, vp]
+    lib.pa_decode_run_noalloc.restype = ctypes.c_int
     return lib
 
 
@@ -319,6 +321,41 @@ def pa_decode_run_fp8(plan, q, k_pool, v_pool, kv_indices, sm_scale, k_scale, v_
                                   _dev_ptr(kv_indices, "kv_indices"), float(sm_scale), float(k_scale),
                                   float(v_scale), _dev_ptr(out, "out"), _dev_ptr(lse, "lse"),
                                   _stream(stream)), "pa_decode_run_fp8")
+
+
+def pa_decode_run_noalloc(q, k_pool, v_pool, kv_indptr, kv_indices, sm_scale, out, lse=None,
+                          num_kv_heads=None, num_slots=None, slot_stride=None, stream=None) -> None:
+    """Decode without a plan and without allocation: kv_indptr is a device
+    int32 tensor [B + 1]; the split is computed on the device into the
+    library's own workspace.  q [B, Hq, D] bf16, pools [slots, Hkv, D] bf16."""
+    if q.dim() != 3:
+        raise ValueError("q must be [B, Hq, D]")
+    B, Hq, D = q.shape
+    if num_kv_heads is None:
+        num_kv_heads = k_pool.shape[-2]
+    if slot_stride is None:
+        slot_stride = _pool_stride(k_pool, v_pool, D)
+    if num_slots is None:
+        num_slots = min(k_pool.shape[0], v_pool.shape[0])
+    for name, t in (("kv_indptr", kv_indptr), ("kv_indices", kv_indices)):
+        if t.dtype != torch.int32 or t.dim() != 1 or not t.is_contiguous():
+            raise TypeError(f"{name} must be a contiguous 1-D int32 tensor")
+    if kv_indptr.numel() != B + 1:
+        raise ValueError(f"kv_indptr must hold batch + 1 = {B + 1} offsets")
+    if out.dtype != torch.float32 or not out.is_contiguous() or out.numel() != B * Hq * D:
+        raise ValueError(f"out must be a contiguous float32 tensor of {B}x{Hq}x{D} values")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or lse.numel() != B * Hq):
+        raise ValueError(f"lse must be a contiguous float32 tensor of {B}x{Hq} values")
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    if min(k_pool.shape[0], v_pool.shape[0]) < num_slots:
+        raise ValueError(f"the pools hold fewer than num_slots={num_slots} slots")
+    _check(_lib.pa_decode_run_noalloc(
+        _dev_ptr(q, "q", torch.bfloat16), _dev_ptr(k_pool, "k_pool", torch.bfloat16),
+        _dev_ptr(v_pool, "v_pool", torch.bfloat16), int(num_slots), int(slot_stride),
+        _dev_ptr(kv_indptr, "kv_indptr"), _dev_ptr(kv_indices, "kv_indices"), int(B), int(Hq),
+        int(num_kv_heads), int(D), float(sm_scale), _dev_ptr(out, "out"), _dev_ptr(lse, "lse"),
+        _stream(stream)), "pa_decode_run_noalloc")
 
 
 def pa_prefill_chunk_run(plan, q, k_pool, v_pool, kv_indices, sm_scale, out, lse=None,

@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIBRARY = os.path.join(PKG, "libpa.so")
-SOURCES = ["api.cpp", "plan.cpp", "decode.hip", "prefill.hip", "append.hip"]
+SOURCES = ["api.cpp", "plan.cpp", "decode.hip", "prefill.hip", "append.hip", "noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -887,6 +887,75 @@ pa_status pa_prefill_chunk_run(const pa_plan_t *p, const void *q, const void *k_
     return PA_OK;
 }
 
+pa_status pa_decode_run_noalloc(const void *q, const void *k_pool, const void *v_pool,
+                                int64_t num_slots, int64_t slot_stride, const int32_t *kv_indptr,
+                                const int32_t *kv_indices, int32_t batch, int32_t num_qo_heads,
+                                int32_t num_kv_heads, int32_t head_dim, float sm_scale, float *out,
+                                float *lse, pa_stream_t stream) {
+    if (num_qo_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0)
+        return fail(PA_ERR_INVALID_ARG, "head counts and head_dim must be positive");
+    if (!pa::supported_shape(num_qo_heads, num_kv_heads, head_dim))
+        return fail(PA_ERR_UNSUPPORTED,
+                    "unsupported head shape (need Hq/Hkv in {1,2,4,8} and D in {128,256})");
+    if (batch < 0)
+        return fail(PA_ERR_INVALID_ARG, "batch < 0");
+    if (batch > pa::kNoAllocMaxBatch || (int64_t)batch * num_kv_heads > pa::kNoAllocMaxSegments)
+        return fail(PA_ERR_CAPACITY, "batch above " + std::to_string(pa::kNoAllocMaxBatch) +
+                                         " or batch * num_kv_heads above " +
+                                         std::to_string(pa::kNoAllocMaxSegments));
+    if (batch == 0)
+        return PA_OK;
+    if (!q || !out || !k_pool || !v_pool || !kv_indices || !kv_indptr)
+        return fail(PA_ERR_INVALID_ARG, "null pointer");
+    if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16))
+        return fail(PA_ERR_INVALID_ARG, "q, k_pool and v_pool must be 16-byte aligned");
+    if (!aligned(kv_indices, 4) || !aligned(kv_indptr, 4) || !aligned(out, 4) || !aligned(lse, 4))
+        return fail(PA_ERR_INVALID_ARG, "kv_indptr, kv_indices, out and lse must be 4-byte aligned");
+    const int64_t row = (int64_t)num_kv_heads * head_dim;
+    if (slot_stride == 0)
+        slot_stride = row;
+    if (slot_stride < row || slot_stride % 8 != 0)
+        return fail(PA_ERR_INVALID_ARG, "slot_stride must be >= Hkv*D and a multiple of 8");
+    if (slot_stride * 2 > 0x7fffffffLL)
+        return fail(PA_ERR_INVALID_ARG, "slot_stride too large");
+    if (num_slots <= 0)
+        return fail(PA_ERR_INVALID_ARG, "num_slots must be positive");
+    if (!std::isfinite(sm_scale))
+        return fail(PA_ERR_INVALID_ARG, "sm_scale is not finite");
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetDevice");
+    const int32_t group = num_qo_heads / num_kv_heads;
+    pa::NoAllocLaunch a;
+    int rc = pa::noalloc_setup(dev, head_dim, group, &a.scratch, &a.workgroups);
+    if (rc != 0)
+        return hip_fail((hipError_t)rc, "workspace set-up (hipGetSymbolAddress)");
+    if (a.workgroups > pa::kNoAllocMaxWorkgroups ||
+        2LL * a.workgroups * group * head_dim > pa::kNoAllocPartialFloats ||
+        2LL * a.workgroups * group > pa::kNoAllocPartialLseFloats)
+        return fail(PA_ERR_CAPACITY, "this GPU's decode workgroups (" + std::to_string(a.workgroups) +
+                                         ") need more partial storage than the workspace holds");
+    a.kv_indptr = kv_indptr;
+    a.kv_indices = kv_indices;
+    a.batch = batch;
+    a.num_qo_heads = num_qo_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.head_dim = head_dim;
+    a.q = q;
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.num_slots = num_slots;
+    a.slot_stride = slot_stride;
+    a.sm_scale = sm_scale;
+    a.out = out;
+    a.lse = lse;
+    rc = pa::launch_decode_noalloc(a, stream);
+    if (rc != 0)
+        return hip_fail((hipError_t)rc, "no-allocation decode launch");
+    return PA_OK;
+}
+
 pa_status pa_profile_begin(pa_plan_t *p, int32_t capacity) {
     if (!p || capacity <= 0)
         return fail(PA_ERR_INVALID_ARG, "plan is null or capacity <= 0");

@@ -187,6 +187,43 @@ int launch_prefill(const DecodeLaunch &l, void *stream);
 // Log-sum-exp merge of the prefill partials (no-op without merge units).
 int launch_prefill_merge(const DecodeLaunch &l, void *stream);
 
+// Decode without allocation (pa_decode_run_noalloc): the work table,
+// partial results and arrival counters live in a file-scope device array of
+// kNoAllocScratchBytes per GPU.  Limits: batch <= kNoAllocMaxBatch, batch *
+// Hkv <= kNoAllocMaxSegments, the GPU's decode workgroups (occupancy x
+// compute units) <= kNoAllocMaxWorkgroups, and 2 x workgroups x G x D <=
+// kNoAllocPartialFloats (2 partial slots per workgroup at most).
+constexpr int kNoAllocMaxBatch = 4096;
+constexpr int kNoAllocMaxSegments = 16384;
+constexpr int kNoAllocMaxWorkgroups = 1024;
+constexpr int64_t kNoAllocPartialFloats = 1 << 21;
+constexpr int64_t kNoAllocPartialLseFloats = 2 * kNoAllocMaxWorkgroups * 8;
+constexpr size_t noalloc_round256(size_t x) { return (x + 255) / 256 * 256; }
+constexpr size_t kNoAllocScratchBytes =
+    noalloc_round256((size_t)(kNoAllocMaxWorkgroups + 1) * 4) +
+    noalloc_round256((size_t)(kNoAllocMaxWorkgroups + kNoAllocMaxSegments) * sizeof(pa_work_unit)) +
+    noalloc_round256((size_t)kNoAllocMaxSegments * sizeof(pa_merge_unit)) +
+    noalloc_round256((size_t)kNoAllocMaxSegments * 4) + noalloc_round256((size_t)kNoAllocPartialLseFloats * 4) +
+    (size_t)kNoAllocPartialFloats * 4;
+
+struct NoAllocLaunch {
+    void *scratch;                  // device address of the workspace array
+    int32_t workgroups;             // decode workgroups launched (bins)
+    const int32_t *kv_indptr;       // device [batch + 1]
+    const int32_t *kv_indices;      // device
+    int32_t batch, num_qo_heads, num_kv_heads, head_dim;
+    const void *q, *k_pool, *v_pool;
+    int64_t num_slots, slot_stride;
+    float sm_scale;
+    float *out, *lse;
+};
+// Once per device (later calls return the cached values): the device address
+// of the workspace and the decode workgroups the device holds at once for
+// this head shape.  Returns a hipError_t.
+int noalloc_setup(int device, int32_t head_dim, int32_t group, void **scratch_ptr, int32_t *workgroups);
+// The planner kernel, then the decode kernel, on `stream`.  Returns a hipError_t.
+int launch_decode_noalloc(const NoAllocLaunch &a, void *stream);
+
 // The append step: new tokens' K/V rows written to their slots, K (and the
 // query rows, in place, if q is not null) rotated by RoPE when rope_theta > 0.
 struct AppendLaunch {
