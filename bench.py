@@ -36,6 +36,7 @@ copy of N GiB (for calibrating the HBM counters).
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -249,17 +250,20 @@ def run_prefill_bench(args):
             plan.prefill(case.q, case.k_pool, case.v_pool, idx, case.sm_scale, outs[layer],
                          stream=stream)
 
+    gc.collect()
+    gc.disable()   # no collector pauses while steps are issued (see the decode bench)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(args.steps):
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    marks[0].record(stream)
+    for i in range(args.steps):
         step()
-    end.record(stream)
+        marks[i + 1].record(stream)
     torch.cuda.synchronize()
-    ms_per_step = start.elapsed_time(end) / args.steps
+    gc.enable()
+    ms_per_step = marks[0].elapsed_time(marks[-1]) / args.steps
+    step_ms = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)])
     pa.pa_profile_begin(plan.handle, args.steps * layers)
     torch.cuda.synchronize()
     for _ in range(args.steps):
@@ -291,6 +295,8 @@ def run_prefill_bench(args):
             "layers_per_step": layers, "pool_slots": spec.num_slots, "plan_flags": args.flags,
         },
         "us_per_step_layer": round(ms_per_step * 1e3 / layers, 2),
+        "step_ms": {"mean": round(ms_per_step, 4), "median": round(float(np.median(step_ms)), 4),
+                    "min": round(float(step_ms.min()), 4), "max": round(float(step_ms.max()), 4)},
         "algorithmic_flops_per_layer": flops,
         "algorithmic_bytes_per_layer": nbytes,
         "achieved_hbm_gbs": round(nbytes / (kernel_avg_ms * 1e-3) / 1e9, 1),
@@ -533,6 +539,12 @@ def main():
         else:
             layer_runs(stream)
 
+    # Python's cyclic garbage collector pauses the host for several
+    # milliseconds every few hundred steps (measured: one step in 40 took
+    # 13 ms instead of 7), long enough to starve the GPU, which the host
+    # otherwise keeps two steps ahead of; it stays off while steps are issued
+    gc.collect()
+    gc.disable()
     wmarks = [torch.cuda.Event(enable_timing=True) for _ in range(args.warmup + 1)]
     wmarks[0].record(stream)
     for i in range(args.warmup):
@@ -546,17 +558,19 @@ def main():
     end = torch.cuda.Event(enable_timing=True)
 
     # timed region: K steps bracketed by HIP events on the launch stream, with
-    # one more event between consecutive steps for the per-step spread
+    # one more event between consecutive steps for the per-step spread (events
+    # around every launch would slow the step down: they are taken in a
+    # second pass below)
     plan_host_s.clear()
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    step_marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    marks[0].record(stream)
+    step_marks[0].record(stream)
     for i in range(args.steps):
         step()
-        marks[i + 1].record(stream)
+        step_marks[i + 1].record(stream)
     torch.cuda.synchronize()
-    ms_per_step = marks[0].elapsed_time(marks[-1]) / args.steps
-    step_ms = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)])
+    ms_per_step = step_marks[0].elapsed_time(step_marks[-1]) / args.steps
+    step_ms = np.array([step_marks[i].elapsed_time(step_marks[i + 1]) for i in range(args.steps)])
     log(f"step {ms_per_step:.3f} ms ({ms_per_step * 1e3 / layers:.1f} us per layer); per step "
         f"median {np.median(step_ms):.3f} min {step_ms.min():.3f} max {step_ms.max():.3f} ms")
     log("per-step ms: " + " ".join(f"{t:.3f}" for t in step_ms))
@@ -566,9 +580,10 @@ def main():
         log(f"workgroup weights after the timed steps: min {wgw.min():.3f} max {wgw.max():.3f} "
             f"std {wgw.std():.3f}")
 
-    # the same K steps again with HIP events recorded by the library around
-    # every decode kernel on the launch stream; the events themselves keep
-    # consecutive kernels from overlapping, so this region only times kernels
+    # the same K steps again with HIP events recorded by the library in pairs
+    # around every decode kernel on the launch stream: the kernel's own
+    # duration (the pairs add a few microseconds between launches, so this
+    # pass's step time is not the headline)
     pa.pa_profile_begin(plan.handle, args.steps * layers)
     torch.cuda.synchronize()
     start.record(stream)
@@ -580,7 +595,9 @@ def main():
     kernel_ms, launches = pa.pa_profile_end(plan.handle)
     kernel_avg_ms = kernel_ms / max(1, launches)
     log(f"decode kernel avg {kernel_avg_ms * 1e3:.1f} us over {launches} launches "
-        f"(step with kernel events {ms_per_step_events:.3f} ms)")
+        f"(step with kernel event pairs {ms_per_step_events:.3f} ms)")
+
+    gc.enable()
 
     # pa_plan's own host time (inside the library): within the timed steps the
     # call also waits for the upload of two steps back, so the host cost is
@@ -639,7 +656,7 @@ def main():
                     "min": round(float(step_ms.min()), 4), "max": round(float(step_ms.max()), 4)},
         "us_per_step_layer_median": round(float(np.median(step_ms)) * 1e3 / layers, 2),
         "frac_of_peak": round(value / HBM_PEAK_GBS, 4),
-        "ms_per_step_with_kernel_events": round(ms_per_step_events, 4),
+        "ms_per_step_with_kernel_event_pairs": round(ms_per_step_events, 4),
         "plan_host_us": round(plan_host_us, 1),
         # the plan's own work inside the timed steps, and separately the time
         # it blocked because the host was two steps ahead of the GPU
@@ -657,6 +674,8 @@ def main():
                       f"({'pa_decode_run_fp8' if fp8 else 'pa_decode_run'})"
                       + (" after the cascade prefix units (prefill_kernel); time of both" if args.cascade else ""),
             "kernel_avg_us": round(kernel_avg_ms * 1e3, 2),
+            "kernel_timing": f"HIP event pairs around each of {launches} launches, second pass of the "
+                             "timed steps",
         },
         "cpu_baseline": None,
     }
