@@ -45,6 +45,8 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
@@ -100,25 +102,36 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
     const f32x2_t v = {a, b};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
-
-// Splits weights (a, b) into bf16 pairs hi and lo with a + b = hi + lo up to
-// the rounding of lo (2^-16 relative).
-__device__ __forceinline__ void split_pair(float a, float b, uint32_t &hi, uint32_t &lo) {
-    hi = pack_bf16(a, b);
-    const float ha = __uint_as_float(hi << 16), hb = __uint_as_float(hi & 0xffff0000u);
-    lo = pack_bf16(a - ha, b - hb);
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+    const f32x2_t v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
 }
+// A bf16 pair as an fp16 pair (exact for magnitudes in [2^-14, 65520); below,
+// fp16's subnormals keep an absolute error under 2^-25), and the running
+// largest magnitude, which tells whether any value overflowed fp16.
+__device__ __forceinline__ uint32_t bf16_pair_to_f16(uint32_t u, float &vmax) {
+    const float a = __uint_as_float(u << 16), b = __uint_as_float(u & 0xffff0000u);
+    vmax = fmaxf(vmax, fmaxf(fabsf(a), fabsf(b)));
+    return pack_f16(a, b);
+}
+// The same, with both values multiplied by 2^-shift first (exact unless the
+// product falls below fp16's normal range).
+__device__ __forceinline__ uint32_t bf16_pair_to_f16_scaled(uint32_t u, int shift) {
+    const float a = __uint_as_float(u << 16), b = __uint_as_float(u & 0xffff0000u);
+    return pack_f16(__builtin_amdgcn_ldexpf(a, -shift), __builtin_amdgcn_ldexpf(b, -shift));
+}
+// Smallest magnitude that fp16 rounds to infinity.
+constexpr float kF16Overflow = 65520.0f;
 
 // B operand (P^T, 16 entries x 32 rows) of one k-step from the score layout.
 // x0, x1: this lane's weights of entries 4h..4h+3 of the k-step (h = lane/32)
 // packed in pairs; y0, y1: entries 8+4h..8+4h+3.  Lane l < 32 needs entries
 // 0..7 (its own x and the x of lane l+32), lane l >= 32 entries 8..15 (the y
 // of lane l-32 and its own y): one half-wave swap per dword does both.
-__device__ __forceinline__ bf16x8_t regroup(uint32_t x0, uint32_t x1, uint32_t y0, uint32_t y1) {
+__device__ __forceinline__ uint4 regroup(uint32_t x0, uint32_t x1, uint32_t y0, uint32_t y1) {
     const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
     const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
-    const uint4 v = {s0[0], s1[0], s0[1], s1[1]};
-    return __builtin_bit_cast(bf16x8_t, v);
+    return uint4{s0[0], s1[0], s0[1], s1[1]};
 }
 
 // s_waitcnt vmcnt(0): every vector-memory load of this wave has returned.
@@ -126,6 +139,9 @@ __device__ __forceinline__ void wait_vector_memory() { __builtin_amdgcn_s_waitcn
 
 __device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16_t mfma_f16(f16x8_t a, f16x8_t b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
 template <int D, int G, bool WIDE>
@@ -144,6 +160,7 @@ prefill_kernel(const int32_t *__restrict__ wg_offsets, const pa_work_unit *__res
     static_assert(kWaves * 32 == kPrefillTileRows, "one 32-row block per wave");
 
     __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+    __shared__ float vmax_lds[kWaves];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -168,7 +185,6 @@ prefill_kernel(const int32_t *__restrict__ wg_offsets, const pa_work_unit *__res
         const pa_work_unit unit = units[ui];
         if (unit.request < 0)
             continue;  // padding unit (uniform over the workgroup)
-        __syncthreads();  // the previous unit's last tile is no longer read
 
         const int32_t n_tok = unit.q_end - unit.q_begin;
         const bool row_valid = tt < n_tok;
@@ -193,190 +209,241 @@ prefill_kernel(const int32_t *__restrict__ wg_offsets, const pa_work_unit *__res
         const int32_t kv0 = unit.kv_begin, kv1 = unit.kv_end;
         const int32_t n_tiles = (kv1 - kv0 + KT - 1) / KT;
         const uint64_t head_off = (uint64_t)unit.kv_head * D * 2 + chunk * 16;
-
-        // Entries at or past kv1 (the tail of the last tile) are clamped to
-        // the range's last entry, so every row read is one the unit
-        // references and the loads need no branch; the causal mask gives
-        // those entries weight 0 (their row limit is at most kv1 - 1).
-        const int32_t *const unit_ids = kv_indices + kv0;   // the unit's entries, uniform base
-        int32_t slot[PASSES];
-        u32x4_t kreg[PASSES], vreg[PASSES];
-        auto load_slots = [&](int32_t tile) {
-#pragma unroll
-            for (int p = 0; p < PASSES; p++)
-                slot[p] = unit_ids[(uint32_t)min(tile * KT + p * RPP + srow, kv1 - kv0 - 1)];
-        };
-        auto load_rows = [&]() {
-#pragma unroll
-            for (int p = 0; p < PASSES; p++) {
-                // pools whose byte offsets stay below 2^31 (the host checks)
-                // take a 32-bit offset, shared by the K and V loads
-                if constexpr (WIDE) {
-                    const uint64_t off = (uint64_t)(uint32_t)slot[p] * stride_bytes + head_off;
-                    kreg[p] = *reinterpret_cast<const u32x4_t *>(k_pool + off);
-                    vreg[p] = *reinterpret_cast<const u32x4_t *>(v_pool + off);
-                } else {
-                    const uint32_t off = __umul24((uint32_t)slot[p], (uint32_t)stride_bytes) + (uint32_t)head_off;
-                    kreg[p] = *reinterpret_cast<const u32x4_t *>(k_pool + off);
-                    vreg[p] = *reinterpret_cast<const u32x4_t *>(v_pool + off);
-                }
-            }
-        };
-        auto store_rows = [&](int buf) {
-            char *st = smem + buf * STAGE;
-#pragma unroll
-            for (int p = 0; p < PASSES; p++) {
-                const int r = p * RPP + srow;
-                *reinterpret_cast<u32x4_t *>(st + r * KROW + chunk * 16) = kreg[p];
-                *reinterpret_cast<u32x4_t *>(st + KT * KROW + r * VROW + chunk * 16) = vreg[p];
-            }
-        };
-
-        float m = kNoMax, l = 0.f;
-        f32x16_t o[DB];
-#pragma unroll
-        for (int b = 0; b < DB; b++)
-            o[b] = f32x16_t{};
-
-        if (n_tiles > 0) {
-            load_slots(0);
-            load_rows();
-            if (n_tiles > 1)
-                load_slots(1);
-            store_rows(0);
-        }
         // row limit: the last list entry (absolute offset) this row may see
         const int32_t row_last = min(kv1 - 1, unit.diag + tt);
         const int32_t unit_last = min(kv1 - 1, unit.diag);  // smallest row limit of the unit
+        // tiles that lie entirely within every row's window need no mask
+        const int32_t n_open = max(0, min(n_tiles, (unit_last - kv0 + 1) / KT));
 
-        // one tile: entries kv0 + it*KT ...; MASK: some entry lies beyond a row's limit
-        auto step = [&](int32_t it, auto mask_tag) {
-            constexpr bool MASK = decltype(mask_tag)::value;
-            const int buf = it & 1;
-            if (it + 1 < n_tiles) {
-                load_rows();  // tile it+1, slots fetched one iteration earlier
-                if (it + 2 < n_tiles)
-                    load_slots(it + 2);
-            }
-            __syncthreads();  // stage `buf` written by every thread
+        // One pass over the unit, V staged in fp16 as V * 2^-vshift.  The
+        // first pass takes vshift = 0 and watches the largest |V| it stages;
+        // if a finite V value overflowed fp16 the pass writes nothing and
+        // returns true, with *retry the power of two that brings every V of
+        // the unit below 2^15, and the unit runs again with it (the result is
+        // scaled back by 2^vshift).  Infinite or NaN V values are not
+        // retried: they make the result infinite or NaN either way.
+        auto run_unit = [&](const int vshift, int *retry) -> bool {
+            __syncthreads();  // the previous unit's (or pass's) last tile is no longer read
 
-            const char *st = smem + buf * STAGE;
-            // S^T = K Q^T, one 32x32 block per 32 entries; entry of s[b][i]:
-            // b*32 + 8*(i/4) + 4*half + i%4 within the tile
-            f32x16_t s[SB];
+            // Entries at or past kv1 (the tail of the last tile) are clamped
+            // to the range's last entry, so every row read is one the unit
+            // references and the loads need no branch; the causal mask gives
+            // those entries weight 0 (their row limit is at most kv1 - 1).
+            const int32_t *const unit_ids = kv_indices + kv0;   // the unit's entries, uniform base
+            int32_t slot[PASSES];
+            u32x4_t kreg[PASSES], vreg[PASSES];
+            float vmax = 0.f;   // largest |V| this thread staged (first pass)
+            auto load_slots = [&](int32_t tile) {
 #pragma unroll
-            for (int b = 0; b < SB; b++) {
-                uint4 ka[DS];
+                for (int p = 0; p < PASSES; p++)
+                    slot[p] = unit_ids[(uint32_t)min(tile * KT + p * RPP + srow, kv1 - kv0 - 1)];
+            };
+            auto load_rows = [&]() {
 #pragma unroll
-                for (int d = 0; d < DS; d++)
-                    ka[d] = *reinterpret_cast<const uint4 *>(st + k_lane + b * 32 * KROW + d * 32);
-                s[b] = mfma(__builtin_bit_cast(bf16x8_t, ka[0]), qf[0], f32x16_t{});
+                for (int p = 0; p < PASSES; p++) {
+                    // pools whose byte offsets stay below 2^31 (the host
+                    // checks) take a 32-bit offset, shared by the K and V loads
+                    if constexpr (WIDE) {
+                        const uint64_t off = (uint64_t)(uint32_t)slot[p] * stride_bytes + head_off;
+                        kreg[p] = *reinterpret_cast<const u32x4_t *>(k_pool + off);
+                        vreg[p] = *reinterpret_cast<const u32x4_t *>(v_pool + off);
+                    } else {
+                        const uint32_t off =
+                            __umul24((uint32_t)slot[p], (uint32_t)stride_bytes) + (uint32_t)head_off;
+                        kreg[p] = *reinterpret_cast<const u32x4_t *>(k_pool + off);
+                        vreg[p] = *reinterpret_cast<const u32x4_t *>(v_pool + off);
+                    }
+                }
+            };
+            // K rows as they are (bf16), V rows converted to fp16 (one uniform
+            // branch for the whole stage: the scaled form is the rare retry)
+            auto store_rows = [&](int buf) {
+                char *st = smem + buf * STAGE;
+                u32x4_t v[PASSES];
+                if (vshift == 0) {
 #pragma unroll
-                for (int d = 1; d < DS; d++)
-                    s[b] = mfma(__builtin_bit_cast(bf16x8_t, ka[d]), qf[d], s[b]);
+                    for (int p = 0; p < PASSES; p++)
+#pragma unroll
+                        for (int j = 0; j < 4; j++)
+                            v[p][j] = bf16_pair_to_f16(vreg[p][j], vmax);
+                } else {
+#pragma unroll
+                    for (int p = 0; p < PASSES; p++)
+#pragma unroll
+                        for (int j = 0; j < 4; j++)
+                            v[p][j] = bf16_pair_to_f16_scaled(vreg[p][j], vshift);
+                }
+#pragma unroll
+                for (int p = 0; p < PASSES; p++) {
+                    const int r = p * RPP + srow;
+                    *reinterpret_cast<u32x4_t *>(st + r * KROW + chunk * 16) = kreg[p];
+                    *reinterpret_cast<u32x4_t *>(st + KT * KROW + r * VROW + chunk * 16) = v[p];
+                }
+            };
+
+            float m = kNoMax, l = 0.f;
+            f32x16_t o[DB];
+#pragma unroll
+            for (int b = 0; b < DB; b++)
+                o[b] = f32x16_t{};
+
+            if (n_tiles > 0) {
+                load_slots(0);
+                load_rows();
+                if (n_tiles > 1)
+                    load_slots(1);
+                store_rows(0);
             }
-            if (MASK) {
-                const int32_t lim = row_last - (kv0 + it * KT) - 4 * half;
+
+            // one tile: entries kv0 + it*KT ...; MASK: some entry lies beyond a row's limit
+            auto step = [&](int32_t it, auto mask_tag) {
+                constexpr bool MASK = decltype(mask_tag)::value;
+                const int buf = it & 1;
+                if (it + 1 < n_tiles) {
+                    load_rows();  // tile it+1, slots fetched one iteration earlier
+                    if (it + 2 < n_tiles)
+                        load_slots(it + 2);
+                }
+                __syncthreads();  // stage `buf` written by every thread
+
+                const char *st = smem + buf * STAGE;
+                // S^T = K Q^T, one 32x32 block per 32 entries; entry of s[b][i]:
+                // b*32 + 8*(i/4) + 4*half + i%4 within the tile
+                f32x16_t s[SB];
+#pragma unroll
+                for (int b = 0; b < SB; b++) {
+                    uint4 ka[DS];
+#pragma unroll
+                    for (int d = 0; d < DS; d++)
+                        ka[d] = *reinterpret_cast<const uint4 *>(st + k_lane + b * 32 * KROW + d * 32);
+                    s[b] = mfma(__builtin_bit_cast(bf16x8_t, ka[0]), qf[0], f32x16_t{});
+#pragma unroll
+                    for (int d = 1; d < DS; d++)
+                        s[b] = mfma(__builtin_bit_cast(bf16x8_t, ka[d]), qf[d], s[b]);
+                }
+                if (MASK) {
+                    const int32_t lim = row_last - (kv0 + it * KT) - 4 * half;
+#pragma unroll
+                    for (int b = 0; b < SB; b++)
+#pragma unroll
+                        for (int i = 0; i < 16; i++)
+                            if (b * 32 + 8 * (i / 4) + (i % 4) > lim)
+                                s[b][i] = -INFINITY;
+                }
+                float tmax = -INFINITY;
 #pragma unroll
                 for (int b = 0; b < SB; b++)
 #pragma unroll
                     for (int i = 0; i < 16; i++)
-                        if (b * 32 + 8 * (i / 4) + (i % 4) > lim)
-                            s[b][i] = -INFINITY;
-            }
-            float tmax = -INFINITY;
+                        tmax = fmaxf(tmax, s[b][i]);
+                tmax *= c_exp;
+                tmax = fmaxf(tmax, other_half(tmax));
+                const bool move = tmax > m + kRescaleSlack;
+                if (__builtin_amdgcn_ballot_w64(move)) {
+                    const float m_new = move ? tmax : m;
+                    const float alpha = fast_exp2(m - m_new);
+                    l *= alpha;
 #pragma unroll
-            for (int b = 0; b < SB; b++)
+                    for (int b = 0; b < DB; b++)
 #pragma unroll
-                for (int i = 0; i < 16; i++)
-                    tmax = fmaxf(tmax, s[b][i]);
-            tmax *= c_exp;
-            tmax = fmaxf(tmax, other_half(tmax));
-            const bool move = tmax > m + kRescaleSlack;
-            if (__builtin_amdgcn_ballot_w64(move)) {
-                const float m_new = move ? tmax : m;
-                const float alpha = fast_exp2(m - m_new);
-                l *= alpha;
-#pragma unroll
-                for (int b = 0; b < DB; b++)
-#pragma unroll
-                    for (int i = 0; i < 16; i++)
-                        o[b][i] *= alpha;
-                m = m_new;
-            }
-            // weights (<= 2^8), their row sum, and the split into bf16 hi + lo
-            uint32_t ph[SB][8], pl[SB][8];
-#pragma unroll
-            for (int b = 0; b < SB; b++)
-#pragma unroll
-                for (int i = 0; i < 16; i += 2) {
-                    const float p0 = fast_exp2(fmaf(s[b][i], c_exp, -m));
-                    const float p1 = fast_exp2(fmaf(s[b][i + 1], c_exp, -m));
-                    l += p0 + p1;
-                    split_pair(p0, p1, ph[b][i / 2], pl[b][i / 2]);
+                        for (int i = 0; i < 16; i++)
+                            o[b][i] *= alpha;
+                    m = m_new;
                 }
-            // O^T += V^T P^T, 16 entries per k-step
+                // weights (<= 2^8) rounded once to fp16; the row sum adds the
+                // rounded weights, so the result is the exact weighted mean of V
+                // under them
+                const f16x2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
+                uint32_t ph[SB][8];
 #pragma unroll
-            for (int k = 0; k < KS; k++) {
-                const int b = k / 2, w0 = 4 * (k % 2);  // dword index of entries 16*(k%2) + 4*half
-                const bf16x8_t bh = regroup(ph[b][w0], ph[b][w0 + 1], ph[b][w0 + 2], ph[b][w0 + 3]);
-                const bf16x8_t bl = regroup(pl[b][w0], pl[b][w0 + 1], pl[b][w0 + 2], pl[b][w0 + 3]);
+                for (int b = 0; b < SB; b++)
 #pragma unroll
-                for (int db = 0; db < DB; db++) {
-                    const int off = v_lane + k * 16 * VROW + db * 64;
-                    const i16x4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(st + off));
-                    const i16x4_t hi4 =
-                        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(st + off + 4 * VROW));
-                    const bf16x8_t a = __builtin_bit_cast(
-                        bf16x8_t, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-                    o[db] = mfma(a, bh, o[db]);
-                    o[db] = mfma(a, bl, o[db]);
+                    for (int i = 0; i < 16; i += 2) {
+                        const float p0 = fast_exp2(fmaf(s[b][i], c_exp, -m));
+                        const float p1 = fast_exp2(fmaf(s[b][i + 1], c_exp, -m));
+                        ph[b][i / 2] = pack_f16(p0, p1);
+                        l = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, ph[b][i / 2]), ones, l, false);
+                    }
+                // O^T += V^T P^T, 16 entries per k-step
+#pragma unroll
+                for (int k = 0; k < KS; k++) {
+                    const int b = k / 2, w0 = 4 * (k % 2);  // dword index of entries 16*(k%2) + 4*half
+                    const f16x8_t bh = __builtin_bit_cast(
+                        f16x8_t, regroup(ph[b][w0], ph[b][w0 + 1], ph[b][w0 + 2], ph[b][w0 + 3]));
+#pragma unroll
+                    for (int db = 0; db < DB; db++) {
+                        const int off = v_lane + k * 16 * VROW + db * 64;
+                        const i16x4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(st + off));
+                        const i16x4_t hi4 =
+                            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(st + off + 4 * VROW));
+                        const f16x8_t a = __builtin_bit_cast(
+                            f16x8_t, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+                        o[db] = mfma_f16(a, bh, o[db]);
+                    }
                 }
-            }
-            if (it + 1 < n_tiles)
-                store_rows(buf ^ 1);
-        };
-        // tiles that lie entirely within every row's window need no mask
-        const int32_t n_open = max(0, min(n_tiles, (unit_last - kv0 + 1) / KT));
-        for (int32_t it = 0; it < n_open; it++)
-            step(it, std::false_type{});
-        for (int32_t it = n_open; it < n_tiles; it++)
-            step(it, std::true_type{});
+                if (it + 1 < n_tiles)
+                    store_rows(buf ^ 1);
+            };
+            for (int32_t it = 0; it < n_open; it++)
+                step(it, std::false_type{});
+            for (int32_t it = n_open; it < n_tiles; it++)
+                step(it, std::true_type{});
 
-        // the two lanes of a row hold disjoint halves of its entries
-        const float l_row = l + other_half(l);
-        const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
-        const float lse2 = l_row > 0.f ? m + fast_log2(l_row) : -INFINITY;
-        float *dst;
-        if (unit.partial < 0) {
-            if (!row_valid)
-                continue;
-            const int64_t orow = (int64_t)(unit.q_begin + tt) * num_qo_heads + unit.kv_head * G + g;
-            dst = out + orow * D;
-            if (lse && half == 0)
-                lse[orow] = lse2 * kLn2;
-        } else {
-            if (!row_valid)
-                continue;
-            // a cascade prefix unit writes query token tt's rows into slot
-            // partial + tt * part_stride (G rows per slot, the decode layout);
-            // other units fill slot `partial` of the tile layout
-            const int64_t prow = unit.part_stride > 0
-                                     ? ((int64_t)unit.partial + (int64_t)tt * unit.part_stride) * G + g
-                                     : (int64_t)unit.partial * kPrefillTileRows + row;
-            dst = part_o + prow * D;
-            if (half == 0)
-                part_lse[prow] = lse2;
-        }
-        // O^T element i of block db: column db*32 + 8*(i/4) + 4*half + i%4
+            if (vshift == 0) {
+                // largest finite |V| of the unit: run again if fp16 overflowed
 #pragma unroll
-        for (int db = 0; db < DB; db++)
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-                const float4 v = {o[db][4 * j] * inv, o[db][4 * j + 1] * inv, o[db][4 * j + 2] * inv,
-                                  o[db][4 * j + 3] * inv};
-                *reinterpret_cast<float4 *>(dst + db * 32 + 8 * j + 4 * half) = v;
+                for (int off = 32; off > 0; off >>= 1)
+                    vmax = fmaxf(vmax, __shfl_xor(vmax, off));
+                if (lane == 0)
+                    vmax_lds[wave] = vmax;
+                __syncthreads();
+                const float wmax = fmaxf(fmaxf(vmax_lds[0], vmax_lds[1]), fmaxf(vmax_lds[2], vmax_lds[3]));
+                if (wmax >= kF16Overflow && wmax <= 3.4028235e38f) {
+                    // 2^e <= wmax < 2^(e+1): wmax * 2^-(e-14) < 2^15
+                    *retry = __builtin_amdgcn_readfirstlane((int)((__float_as_uint(wmax) >> 23) & 0xff) - 127 - 14);
+                    return true;
+                }
             }
+
+            // the two lanes of a row hold disjoint halves of its entries
+            const float l_row = l + other_half(l);
+            const float inv = l_row > 0.f ? __builtin_amdgcn_ldexpf(1.f / l_row, vshift) : 0.f;
+            const float lse2 = l_row > 0.f ? m + fast_log2(l_row) : -INFINITY;
+            if (!row_valid)
+                return false;
+            float *dst;
+            if (unit.partial < 0) {
+                const int64_t orow = (int64_t)(unit.q_begin + tt) * num_qo_heads + unit.kv_head * G + g;
+                dst = out + orow * D;
+                if (lse && half == 0)
+                    lse[orow] = lse2 * kLn2;
+            } else {
+                // a cascade prefix unit writes query token tt's rows into slot
+                // partial + tt * part_stride (G rows per slot, the decode layout);
+                // other units fill slot `partial` of the tile layout
+                const int64_t prow = unit.part_stride > 0
+                                         ? ((int64_t)unit.partial + (int64_t)tt * unit.part_stride) * G + g
+                                         : (int64_t)unit.partial * kPrefillTileRows + row;
+                dst = part_o + prow * D;
+                if (half == 0)
+                    part_lse[prow] = lse2;
+            }
+            // O^T element i of block db: column db*32 + 8*(i/4) + 4*half + i%4
+#pragma unroll
+            for (int db = 0; db < DB; db++)
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const float4 v = {o[db][4 * j] * inv, o[db][4 * j + 1] * inv, o[db][4 * j + 2] * inv,
+                                      o[db][4 * j + 3] * inv};
+                    *reinterpret_cast<float4 *>(dst + db * 32 + 8 * j + 4 * half) = v;
+                }
+            return false;
+        };
+        // one call site (a loop) keeps the pass inlined once; vshift is
+        // uniform over the workgroup
+        int vshift = 0;
+        for (int pass = 0; pass < 2 && run_unit(vshift, &vshift); pass++) {
+        }
     }
 }
 

@@ -1,7 +1,7 @@
 """Cascade decode (pa_plan_cascade): each group's shared prefix is attended
 once by the matrix-core prefix units and merged into the decode kernel's
 results.  The output must match the fp64 oracle on the full lists within
-2e-3 and the plain decode plan within 1e-5.  Needs an AMD GPU."""
+2e-3 and the plain decode plan within 5e-4.  Needs an AMD GPU."""
 import numpy as np
 import pytest
 import torch
@@ -11,6 +11,12 @@ from gpu_util import TOL, device, max_err, oracle_decode, say
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+# Cascade and plain decode of the same lists agree to this (the bar against
+# the oracle stays 2e-3): the prefix units weight V on fp16 matrix cores,
+# each weight rounded once to fp16 (relative error <= 2^-11), where the decode
+# kernel keeps fp32 weights.
+CASCADE_VS_PLAIN = 5e-4
 
 
 def _groups(B, size):
@@ -50,7 +56,7 @@ def _check(ip, idx, q, k, v, Hkv, gi, pl):
     ref, ref_lse = oracle_decode(q, k, v, ip, idx, W.softmax_scale(q.shape[-1]), Hkv)
     e = max_err(cas, ref), max_err(cas_lse, ref_lse)
     say(f"  vs plain {d_plain:.3g}; vs oracle out {e[0]:.3g} lse {e[1]:.3g} (all rows)")
-    assert d_plain <= 1e-5
+    assert d_plain <= CASCADE_VS_PLAIN
     assert e[0] <= TOL and e[1] <= TOL
 
 
@@ -114,7 +120,7 @@ def test_system_prompt_workload_full_rows():
                         case.kv_indices, q, k, v, spec.num_kv_heads)
     plain, plain_lse = _run(lambda p: p.plan(case.kv_indptr), case.kv_indptr, case.kv_indices,
                             q, k, v, spec.num_kv_heads)
-    assert max_err(cas, plain) <= 1e-5 and max_err(cas_lse, plain_lse) <= 1e-5
+    assert max_err(cas, plain) <= CASCADE_VS_PLAIN and max_err(cas_lse, plain_lse) <= CASCADE_VS_PLAIN
     ref, ref_lse = oracle_decode(q, k, v, case.kv_indptr, case.kv_indices, case.sm_scale,
                                  spec.num_kv_heads)
     e = max_err(cas, ref), max_err(cas_lse, ref_lse)
@@ -162,7 +168,7 @@ def test_plan_modes_alternate():
         assert e.value.status == pa.PA_ERR_UNSUPPORTED
         torch.cuda.synchronize()
     a, b, c = (o.cpu().numpy() for o in outs)
-    assert np.array_equal(a, c) and max_err(a, b) <= 1e-5
+    assert np.array_equal(a, c) and max_err(a, b) <= CASCADE_VS_PLAIN
 
 
 def test_graph_replay():

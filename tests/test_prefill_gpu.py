@@ -140,3 +140,26 @@ def test_prefill_workload_full_rows(spec):
     e_out, e_lse = max_err(out, ref), max_err(lse, ref_lse)
     say(f"  {out.shape[0] * out.shape[1]} rows: max|d| out={e_out:.3g} lse={e_lse:.3g}")
     assert e_out <= TOL and e_lse <= TOL
+
+
+@pytest.mark.parametrize("log2_scale", [16, 100])
+def test_prefill_values_beyond_fp16_range(log2_scale):
+    """The weighted sum runs on fp16 matrix cores; a unit whose V values
+    overflow fp16 is run again with V scaled by a power of two.  V = 2^s x
+    N(0, 1) (exact in bf16) must give 2^s x the result for N(0, 1), and the
+    oracle within 2e-3 x 2^s."""
+    say(f"prefill with V scaled by 2^{log2_scale}")
+    reqs = [(300, 64), (700, 129), (40, 33)]
+    qo, ip, idx, q, k, v = _case(reqs, 32, 8, 128, 8192, seed=41)
+    idx_dev = torch.as_tensor(idx, device=device())
+    scale = W.softmax_scale(128)
+    base, base_lse = run_prefill(q, k, v, qo, ip, idx_dev, scale, 8)
+    f = 2.0 ** log2_scale
+    big = (v.float() * f).to(torch.bfloat16)
+    assert torch.equal(big.float(), v.float() * f)   # the scaling is exact
+    out, lse = run_prefill(q, k, big, qo, ip, idx_dev, scale, 8)
+    ref, ref_lse = oracle_prefill(q, k, big, qo, ip, idx, scale, 8)
+    e = max_err(out / f, ref / f), max_err(lse, ref_lse)
+    say(f"  max|d|/2^s vs oracle {e[0]:.3g}, lse {e[1]:.3g}; vs unscaled {max_err(out / f, base):.3g}")
+    assert e[0] <= TOL and e[1] <= TOL
+    assert max_err(out / f, base) <= TOL and max_err(lse, base_lse) <= 1e-6
