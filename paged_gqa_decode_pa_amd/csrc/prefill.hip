@@ -107,12 +107,9 @@ __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
 }
 // A bf16 pair as an fp16 pair (exact for magnitudes in [2^-14, 65520); below,
-// fp16's subnormals keep an absolute error under 2^-25), and the running
-// largest magnitude, which tells whether any value overflowed fp16.
-__device__ __forceinline__ uint32_t bf16_pair_to_f16(uint32_t u, float &vmax) {
-    const float a = __uint_as_float(u << 16), b = __uint_as_float(u & 0xffff0000u);
-    vmax = fmaxf(vmax, fmaxf(fabsf(a), fabsf(b)));
-    return pack_f16(a, b);
+// fp16's subnormals keep an absolute error under 2^-25; from 65520 up, inf).
+__device__ __forceinline__ uint32_t bf16_pair_to_f16(uint32_t u) {
+    return pack_f16(__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u));
 }
 // The same, with both values multiplied by 2^-shift first (exact unless the
 // product falls below fp16's normal range).
@@ -160,7 +157,7 @@ prefill_kernel(const int32_t *__restrict__ wg_offsets, const pa_work_unit *__res
     static_assert(kWaves * 32 == kPrefillTileRows, "one 32-row block per wave");
 
     __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
-    __shared__ float vmax_lds[kWaves];
+    __shared__ float flag_lds[kWaves];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -216,12 +213,14 @@ prefill_kernel(const int32_t *__restrict__ wg_offsets, const pa_work_unit *__res
         const int32_t n_open = max(0, min(n_tiles, (unit_last - kv0 + 1) / KT));
 
         // One pass over the unit, V staged in fp16 as V * 2^-vshift.  The
-        // first pass takes vshift = 0 and watches the largest |V| it stages;
-        // if a finite V value overflowed fp16 the pass writes nothing and
-        // returns true, with *retry the power of two that brings every V of
-        // the unit below 2^15, and the unit runs again with it (the result is
-        // scaled back by 2^vshift).  Infinite or NaN V values are not
-        // retried: they make the result infinite or NaN either way.
+        // first pass takes vshift = 0.  If its result is not finite, a V
+        // value may have overflowed fp16 (or V holds an infinity or NaN): the
+        // unit's largest finite |V| is found by reading its V rows again, and
+        // if it is 65520 or more the pass writes nothing and returns true with
+        // *retry the power of two that brings every V of the unit below 2^15;
+        // the unit then runs again with it (the result scaled back by
+        // 2^vshift).  Otherwise the non-finite result is the right one
+        // (infinite or NaN V make the result infinite or NaN either way).
         auto run_unit = [&](const int vshift, int *retry) -> bool {
             __syncthreads();  // the previous unit's (or pass's) last tile is no longer read
 
@@ -232,7 +231,6 @@ prefill_kernel(const int32_t *__restrict__ wg_offsets, const pa_work_unit *__res
             const int32_t *const unit_ids = kv_indices + kv0;   // the unit's entries, uniform base
             int32_t slot[PASSES];
             u32x4_t kreg[PASSES], vreg[PASSES];
-            float vmax = 0.f;   // largest |V| this thread staged (first pass)
             auto load_slots = [&](int32_t tile) {
 #pragma unroll
                 for (int p = 0; p < PASSES; p++)
@@ -265,7 +263,7 @@ prefill_kernel(const int32_t *__restrict__ wg_offsets, const pa_work_unit *__res
                     for (int p = 0; p < PASSES; p++)
 #pragma unroll
                         for (int j = 0; j < 4; j++)
-                            v[p][j] = bf16_pair_to_f16(vreg[p][j], vmax);
+                            v[p][j] = bf16_pair_to_f16(vreg[p][j]);
                 } else {
 #pragma unroll
                     for (int p = 0; p < PASSES; p++)
@@ -390,18 +388,45 @@ prefill_kernel(const int32_t *__restrict__ wg_offsets, const pa_work_unit *__res
                 step(it, std::true_type{});
 
             if (vshift == 0) {
-                // largest finite |V| of the unit: run again if fp16 overflowed
+                // a non-finite O or row sum anywhere in the workgroup?
+                float chk = l;
 #pragma unroll
-                for (int off = 32; off > 0; off >>= 1)
-                    vmax = fmaxf(vmax, __shfl_xor(vmax, off));
+                for (int db = 0; db < DB; db++)
+#pragma unroll
+                    for (int i = 0; i < 16; i++)
+                        chk += o[db][i];
+                const bool bad = !(fabsf(chk) <= 3.4028235e38f);
                 if (lane == 0)
-                    vmax_lds[wave] = vmax;
+                    flag_lds[wave] = __builtin_amdgcn_ballot_w64(bad) != 0 ? 1.f : 0.f;
                 __syncthreads();
-                const float wmax = fmaxf(fmaxf(vmax_lds[0], vmax_lds[1]), fmaxf(vmax_lds[2], vmax_lds[3]));
-                if (wmax >= kF16Overflow && wmax <= 3.4028235e38f) {
-                    // 2^e <= wmax < 2^(e+1): wmax * 2^-(e-14) < 2^15
-                    *retry = __builtin_amdgcn_readfirstlane((int)((__float_as_uint(wmax) >> 23) & 0xff) - 127 - 14);
-                    return true;
+                if (flag_lds[0] + flag_lds[1] + flag_lds[2] + flag_lds[3] != 0.f) {
+                    // the unit's largest finite |V| (read again: a rare path)
+                    float vm = 0.f;
+                    for (int32_t tile = 0; tile < n_tiles; tile++) {
+                        load_slots(tile);
+                        load_rows();
+#pragma unroll
+                        for (int p = 0; p < PASSES; p++)
+#pragma unroll
+                            for (int j = 0; j < 4; j++) {
+                                const float a = fabsf(__uint_as_float(vreg[p][j] << 16));
+                                const float b = fabsf(__uint_as_float(vreg[p][j] & 0xffff0000u));
+                                vm = fmaxf(vm, fmaxf(a <= 3.4028235e38f ? a : 0.f, b <= 3.4028235e38f ? b : 0.f));
+                            }
+                    }
+#pragma unroll
+                    for (int off = 32; off > 0; off >>= 1)
+                        vm = fmaxf(vm, __shfl_xor(vm, off));
+                    __syncthreads();   // every wave has read the flags
+                    if (lane == 0)
+                        flag_lds[wave] = vm;
+                    __syncthreads();
+                    const float wmax = fmaxf(fmaxf(flag_lds[0], flag_lds[1]), fmaxf(flag_lds[2], flag_lds[3]));
+                    if (wmax >= kF16Overflow) {
+                        // 2^e <= wmax < 2^(e+1): wmax * 2^-(e-14) < 2^15
+                        *retry = __builtin_amdgcn_readfirstlane((int)((__float_as_uint(wmax) >> 23) & 0xff) - 127 - 14);
+                        return true;
+                    }
                 }
             }
 
