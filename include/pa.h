@@ -491,6 +491,13 @@ pa_status pa_check_kv_indices(const int32_t *kv_indptr_host, int32_t batch,
                               const int32_t *kv_indices_host, int64_t num_slots,
                               int64_t *first_bad);
 
+/*
+ * pa_prefill_tile_rows: query rows (chunk tokens x Hq/Hkv) of one prefill
+ * work unit at this head_dim, i.e. the tile height pa_partition uses to cut
+ * chunk rows (0 for an unsupported head_dim).  Host-only.
+ */
+int32_t pa_prefill_tile_rows(int32_t head_dim);
+
 /* Library version as major*10000 + minor*100 + patch. */
 int32_t pa_version(void);
 

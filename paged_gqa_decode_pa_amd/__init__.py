@@ -94,6 +94,8 @@ def _load() -> ctypes.CDLL:
     lib.pa_last_error_detail.restype = ctypes.c_char_p
     lib.pa_version.argtypes = []
     lib.pa_version.restype = i32
+    lib.pa_prefill_tile_rows.argtypes = [i32]
+    lib.pa_prefill_tile_rows.restype = i32
     lib.pa_partition.argtypes = [i32p, i32p, i32, i32, i32, i32, u32, i32, i32p, i32,
                                  ctypes.POINTER(pa_work_unit), i32,
                                  ctypes.POINTER(pa_merge_unit), i32, i32p, i32p, i32p, i32p]
@@ -152,6 +154,11 @@ def pa_last_error_detail() -> str:
 
 def pa_version() -> int:
     return int(_lib.pa_version())
+
+
+def pa_prefill_tile_rows(head_dim: int) -> int:
+    """Query rows of one prefill work unit (chunk tokens x Hq/Hkv) at head_dim."""
+    return int(_lib.pa_prefill_tile_rows(int(head_dim)))
 
 
 def _check(status: int, where: str):

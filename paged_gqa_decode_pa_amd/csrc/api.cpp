@@ -390,7 +390,7 @@ static pa_status plan_impl(pa_plan_t *p, const int32_t *kv_indptr_host, const in
                                         &detail);
     if (st != PA_OK)
         return fail(st, detail);
-    const int64_t rows_per_slot = qo_indptr_host ? pa::kPrefillTileRows : p->group;
+    const int64_t rows_per_slot = qo_indptr_host ? pa::prefill_tile_rows(p->head_dim) : p->group;
     if ((int64_t)r.n_partials * rows_per_slot > p->partial_rows_cap)
         return fail(PA_ERR_CAPACITY, "partial storage of the plan exceeded");
     // pack: [offsets | units | merges | prefix offsets | prefix units]
@@ -462,6 +462,10 @@ const char *pa_strerror(pa_status s) {
 const char *pa_last_error_detail(void) { return g_detail.c_str(); }
 
 int32_t pa_version(void) { return 100; }
+
+int32_t pa_prefill_tile_rows(int32_t head_dim) {
+    return (head_dim == 128 || head_dim == 256) ? pa::prefill_tile_rows(head_dim) : 0;
+}
 
 pa_status pa_partition(const int32_t *kv_indptr_host, const int32_t *qo_indptr_host,
                        int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads,

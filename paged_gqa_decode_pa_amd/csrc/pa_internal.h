@@ -48,8 +48,12 @@ constexpr int kMinPieceTokens = 64;
 // Workgroups per compute unit assumed when the occupancy is not known.
 constexpr int kDefaultWorkgroupsPerCu = 3;
 
-// Prefill kernel geometry (rows of one query tile = chunk tokens x group).
-constexpr int kPrefillTileRows = 128;
+// Prefill kernel geometry: rows of one query tile (chunk tokens x group), one
+// wave per 32 rows; 8 waves (2 per SIMD, one workgroup per compute unit) at
+// head_dim 128, 4 (1 per SIMD) at head_dim 256.
+constexpr int prefill_tile_rows(int head_dim) { return head_dim == 256 ? 128 : 256; }
+// Prefill workgroups one compute unit holds.
+constexpr int kPrefillWorkgroupsPerCu = 1;
 
 enum class PlanMode : int32_t { kNone = 0, kDecode = 1, kPrefill = 2 };
 
@@ -140,7 +144,7 @@ pa_status cascade_partition(const PartitionArgs &a, const CascadeArgs &c, Partit
 // Upper bounds on what a plan created with these limits can need: workgroup
 // offsets (entries), work and merge units, and partial storage in rows of
 // head_dim floats (a decode partial slot holds `group` rows, a prefill slot
-// kPrefillTileRows rows).
+// prefill_tile_rows(head_dim) rows).
 void partition_capacity(int32_t max_batch, int64_t max_kv_total, int32_t max_q_total,
                         int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
                         int32_t max_workgroups, int32_t num_xcd, int64_t *max_wg_entries,

@@ -26,7 +26,7 @@
 //
 // Decode with forced splits, and prefill.  One unit per workgroup.  Prefill
 // units are (request, KV head, tile of chunk rows); the tile stacks the
-// group's query heads so it holds kPrefillTileRows rows, and its KV range ends
+// group's query heads so it holds prefill_tile_rows(head_dim) rows, and its KV range ends
 // at the causal window of its last row.  When the tiles alone cannot fill the
 // GPU, KV ranges are also cut and merged.  Units are grouped into clusters
 // (same part, same KV head, 16 consecutive requests) that are spread over the
@@ -132,7 +132,7 @@ int64_t min_unit_tokens(int32_t head_dim) {
     return std::max<int64_t>(kUnitGranule, kMinUnitBytes / (4 * (int64_t)head_dim));
 }
 
-int32_t prefill_tile_tokens(int32_t group) { return kPrefillTileRows / group; }
+int32_t prefill_tile_tokens(int32_t group, int32_t head_dim) { return prefill_tile_rows(head_dim) / group; }
 
 // ---------------------------------------------------------------------------
 // decode, automatic: balanced workgroup bins
@@ -361,7 +361,7 @@ void partition_capacity(int32_t max_batch, int64_t max_kv_total, int32_t max_q_t
     // prefill: tiles, then at most ~4 units per CU after KV splitting
     int64_t tiles = 0, pre = 0;
     if (max_q_total > 0) {
-        const int32_t qt = prefill_tile_tokens(g);
+        const int32_t qt = prefill_tile_tokens(g, head_dim);
         tiles = (int64_t)num_kv_heads * (ceil_div(max_q_total, qt) + max_batch);
         pre = 4LL * kNumCu + tiles;
     }
@@ -377,9 +377,11 @@ void partition_capacity(int32_t max_batch, int64_t max_kv_total, int32_t max_q_t
     // 2 * (members per pair) * max_workgroups) slots, pairs <= segments
     const int64_t max_wg = std::max(1, max_workgroups);
     const int64_t prefix_slots =
-        std::max(segs, std::min<int64_t>(segs * kMaxCascadeParts, 2 * (int64_t)(kPrefillTileRows / g) * max_wg));
+        std::max(segs, std::min<int64_t>(segs * kMaxCascadeParts,
+                                         2 * (int64_t)(prefill_tile_rows(head_dim) / g) * max_wg));
     *max_prefix_units = std::max(segs, std::min<int64_t>(segs * kMaxCascadeParts, 2 * max_wg));
-    *max_partial_rows = std::max((dec + prefix_slots) * g, (max_q_total > 0) ? pre * kPrefillTileRows : 0);
+    *max_partial_rows =
+        std::max((dec + prefix_slots) * g, (max_q_total > 0) ? pre * prefill_tile_rows(head_dim) : 0);
 }
 
 pa_status cascade_partition(const PartitionArgs &a, const CascadeArgs &c, PartitionScratch *scratch,
@@ -462,10 +464,10 @@ pa_status cascade_partition(const PartitionArgs &a, const CascadeArgs &c, Partit
     if (!decode_fits)
         merge_capacity = 0;   // the merges were not written
 
-    // prefix units: per group, subgroups of up to kPrefillTileRows / g members
+    // prefix units: per group, subgroups of up to prefill_tile_rows / g members
     // (one query tile), per KV head, the prefix cut into K parts; part k of
     // member t of (subgroup, head) writes slot base + t * K + k
-    const int32_t max_members = kPrefillTileRows / g;
+    const int32_t max_members = prefill_tile_rows(a.head_dim) / g;
     int64_t pairs = 0;   // (subgroup, KV head) pairs with a prefix
     for (int32_t gi = 0; gi < c.num_groups; gi++)
         if (used_prefix(gi) > 0)
@@ -620,24 +622,24 @@ pa_status partition(const PartitionArgs &a, PartitionScratch *scratch, int32_t *
         }
         groups = xcd ? xcd_order_single(units, a.num_xcd) : plain_single(units);
     } else {
-        const int32_t qt = prefill_tile_tokens(g);
+        const int32_t qt = prefill_tile_tokens(g, a.head_dim);
         int64_t n_tiles = 0;
         for (int32_t b = 0; b < a.batch; b++)
             n_tiles += (int64_t)Hkv * ceil_div(a.qo_indptr[b + 1] - a.qo_indptr[b], qt);
-        // Cut KV ranges only when the tiles alone cannot fill the GPU (two
-        // prefill workgroups per compute unit at head_dim 128), and then into
-        // about that many parts: every part runs in the first round, and more
-        // parts only add partial rows to write and merge (8 x 4096 cached +
-        // 64-token chunks: 4 parts per tile 79-80 us per layer, 8 parts 92-93).
+        // Cut KV ranges only when the tiles alone cannot fill the GPU (one
+        // prefill workgroup per compute unit), and then into about that many
+        // parts: every part runs in the first round, and more parts only add
+        // partial rows to write and merge.
+        const int64_t resident = (int64_t)kPrefillWorkgroupsPerCu * kNumCu;
         int64_t part_len = 0;  // 0 = no cut
-        if (forced == 0 && n_tiles > 0 && n_tiles < 2LL * kNumCu) {
+        if (forced == 0 && n_tiles > 0 && n_tiles < resident) {
             int64_t kv_work = 0;
             for (int32_t b = 0; b < a.batch; b++) {
                 const int64_t C = a.qo_indptr[b + 1] - a.qo_indptr[b];
                 if (C > 0)
                     kv_work += (int64_t)Hkv * ceil_div(C, qt) * (a.kv_indptr[b + 1] - a.kv_indptr[b]);
             }
-            part_len = std::max<int64_t>(256, ceil_div(kv_work, 2LL * kNumCu));
+            part_len = std::max<int64_t>(256, ceil_div(kv_work, resident));
             part_len = ceil_div(part_len, 64) * 64;
         }
         std::vector<Unit> units;

@@ -57,8 +57,13 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNoMax = -1.0e30f;
 constexpr float kRescaleSlack = 8.0f;
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
+// Waves of a prefill workgroup: one per 32 rows of its query tile (8 at
+// head_dim 128, 4 at 256); they share every staged K/V tile.
+template <int D>
+constexpr int prefill_waves() {
+    return prefill_tile_rows(D) / 32;
+}
+constexpr int kMergeThreads = 256;
 
 template <int D>
 struct PrefillGeo {
@@ -75,7 +80,8 @@ struct PrefillGeo {
     static constexpr int VROW = D * 2 + 64;
     static constexpr int STAGE = KT * (KROW + VROW);  // one buffer: K tile then V tile
     static constexpr int TPR = D / 8;                  // staging threads per row (16 B each)
-    static constexpr int RPP = kThreads / TPR;         // rows per staging pass
+    static constexpr int THREADS = 64 * prefill_waves<D>();
+    static constexpr int RPP = THREADS / TPR;          // rows per staging pass
     static constexpr int PASSES = KT / RPP;
     static constexpr int DS = D / 16;                  // MFMA k-steps over D (QK^T)
     static constexpr int DB = D / 32;                  // 32-wide column blocks of O
@@ -142,7 +148,7 @@ __device__ __forceinline__ f32x16_t mfma_f16(f16x8_t a, f16x8_t b, f32x16_t c) {
 }
 
 template <int D, int G, bool WIDE>
-__global__ __launch_bounds__(kThreads)
+__global__ __launch_bounds__(64 * prefill_waves<D>())
 __attribute__((amdgpu_waves_per_eu(prefill_waves_per_simd<D>(), prefill_waves_per_simd<D>()))) void
 prefill_kernel(const int32_t *__restrict__ wg_offsets, const pa_work_unit *__restrict__ units,
                const uint16_t *__restrict__ q, const char *__restrict__ k_pool,
@@ -154,10 +160,10 @@ prefill_kernel(const int32_t *__restrict__ wg_offsets, const pa_work_unit *__res
     constexpr int KT = Geo::KT, KROW = Geo::KROW, VROW = Geo::VROW, STAGE = Geo::STAGE;
     constexpr int TPR = Geo::TPR, RPP = Geo::RPP, PASSES = Geo::PASSES;
     constexpr int DS = Geo::DS, DB = Geo::DB, SB = Geo::SB, KS = Geo::KS;
-    static_assert(kWaves * 32 == kPrefillTileRows, "one 32-row block per wave");
+    constexpr int WAVES = prefill_waves<D>(), TILE_ROWS = prefill_tile_rows(D);
 
     __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
-    __shared__ float flag_lds[kWaves];
+    __shared__ float flag_lds[WAVES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -399,7 +405,11 @@ prefill_kernel(const int32_t *__restrict__ wg_offsets, const pa_work_unit *__res
                 if (lane == 0)
                     flag_lds[wave] = __builtin_amdgcn_ballot_w64(bad) != 0 ? 1.f : 0.f;
                 __syncthreads();
-                if (flag_lds[0] + flag_lds[1] + flag_lds[2] + flag_lds[3] != 0.f) {
+                float any_bad = 0.f;
+#pragma unroll
+                for (int w = 0; w < WAVES; w++)
+                    any_bad += flag_lds[w];
+                if (any_bad != 0.f) {
                     // the unit's largest finite |V| (read again: a rare path)
                     float vm = 0.f;
                     for (int32_t tile = 0; tile < n_tiles; tile++) {
@@ -421,7 +431,10 @@ prefill_kernel(const int32_t *__restrict__ wg_offsets, const pa_work_unit *__res
                     if (lane == 0)
                         flag_lds[wave] = vm;
                     __syncthreads();
-                    const float wmax = fmaxf(fmaxf(flag_lds[0], flag_lds[1]), fmaxf(flag_lds[2], flag_lds[3]));
+                    float wmax = 0.f;
+#pragma unroll
+                    for (int w = 0; w < WAVES; w++)
+                        wmax = fmaxf(wmax, flag_lds[w]);
                     if (wmax >= kF16Overflow) {
                         // 2^e <= wmax < 2^(e+1): wmax * 2^-(e-14) < 2^15
                         *retry = __builtin_amdgcn_readfirstlane((int)((__float_as_uint(wmax) >> 23) & 0xff) - 127 - 14);
@@ -448,7 +461,7 @@ prefill_kernel(const int32_t *__restrict__ wg_offsets, const pa_work_unit *__res
                 // other units fill slot `partial` of the tile layout
                 const int64_t prow = unit.part_stride > 0
                                          ? ((int64_t)unit.partial + (int64_t)tt * unit.part_stride) * G + g
-                                         : (int64_t)unit.partial * kPrefillTileRows + row;
+                                         : (int64_t)unit.partial * TILE_ROWS + row;
                 dst = part_o + prow * D;
                 if (half == 0)
                     part_lse[prow] = lse2;
@@ -477,11 +490,11 @@ prefill_kernel(const int32_t *__restrict__ wg_offsets, const pa_work_unit *__res
 // D/4 threads with one float4 each, so every part's row is one coalesced read.
 constexpr int kMergeBatch = 8;   // parts read per memory round trip
 template <int D, int G>
-__global__ __launch_bounds__(kThreads) void prefill_merge_kernel(
+__global__ __launch_bounds__(kMergeThreads) void prefill_merge_kernel(
     const pa_merge_unit *__restrict__ merges, const float *__restrict__ part_o,
     const float *__restrict__ part_lse, float *__restrict__ out, float *__restrict__ lse,
     int32_t num_qo_heads) {
-    constexpr int TPR = D / 4, RPW = kThreads / TPR;
+    constexpr int TPR = D / 4, RPW = kMergeThreads / TPR;
     const pa_merge_unit mu = merges[blockIdx.x];
     const int row = blockIdx.y * RPW + threadIdx.x / TPR, c = threadIdx.x % TPR;
     if (row >= (mu.q_end - mu.q_begin) * G)
@@ -497,7 +510,7 @@ __global__ __launch_bounds__(kThreads) void prefill_merge_kernel(
         float4 v[kMergeBatch];
 #pragma unroll
         for (int j = 0; j < kMergeBatch; j++) {
-            const int64_t prow = (int64_t)(mu.first_partial + min(i0 + j, n - 1)) * kPrefillTileRows + row;
+            const int64_t prow = (int64_t)(mu.first_partial + min(i0 + j, n - 1)) * prefill_tile_rows(D) + row;
             l[j] = part_lse[prow];
             v[j] = *reinterpret_cast<const float4 *>(part_o + prow * D + 4 * c);
         }
@@ -542,9 +555,9 @@ __global__ __launch_bounds__(kThreads) void prefill_merge_kernel(
 
 template <int D, int G>
 int launch_prefill_merge_dg(const DecodeLaunch &l, hipStream_t stream) {
-    constexpr int RPW = kThreads / (D / 4);
-    hipLaunchKernelGGL((prefill_merge_kernel<D, G>), dim3(l.n_merges, kPrefillTileRows / RPW),
-                       dim3(kThreads), 0, stream, l.merges, l.partial_o, l.partial_lse, l.out, l.lse,
+    constexpr int RPW = kMergeThreads / (D / 4);
+    hipLaunchKernelGGL((prefill_merge_kernel<D, G>), dim3(l.n_merges, prefill_tile_rows(D) / RPW),
+                       dim3(kMergeThreads), 0, stream, l.merges, l.partial_o, l.partial_lse, l.out, l.lse,
                        l.num_qo_heads);
     return (int)hipGetLastError();
 }
@@ -554,12 +567,12 @@ int launch_prefill_dg(const DecodeLaunch &l, hipStream_t stream) {
     const uint64_t stride_bytes = (uint64_t)l.slot_stride * 2;
     const bool wide = stride_bytes >= (1u << 24) || !row_offsets_fit_32(l.num_slots, (uint32_t)stride_bytes);
     if (wide)
-        hipLaunchKernelGGL((prefill_kernel<D, G, true>), dim3(l.n_workgroups), dim3(kThreads), 0, stream,
+        hipLaunchKernelGGL((prefill_kernel<D, G, true>), dim3(l.n_workgroups), dim3(PrefillGeo<D>::THREADS), 0, stream,
                            l.wg_offsets, l.units, (const uint16_t *)l.q, (const char *)l.k_pool,
                            (const char *)l.v_pool, stride_bytes, l.kv_indices, l.sm_scale * kLog2e, l.out,
                            l.lse, l.partial_o, l.partial_lse, l.num_qo_heads);
     else
-        hipLaunchKernelGGL((prefill_kernel<D, G, false>), dim3(l.n_workgroups), dim3(kThreads), 0, stream,
+        hipLaunchKernelGGL((prefill_kernel<D, G, false>), dim3(l.n_workgroups), dim3(PrefillGeo<D>::THREADS), 0, stream,
                            l.wg_offsets, l.units, (const uint16_t *)l.q, (const char *)l.k_pool,
                            (const char *)l.v_pool, stride_bytes, l.kv_indices, l.sm_scale * kLog2e, l.out,
                            l.lse, l.partial_o, l.partial_lse, l.num_qo_heads);

@@ -67,13 +67,13 @@ def check_cascade(ip, gi, pl, Hq, Hkv, flags=0, max_wg=0):
                     assert m["prefix_parts"] == 0
             else:
                 assert us[0]["partial"] == -1 and (b, h) not in merge_of
-    # prefix units: per group, subgroups of <= 128/g members, each prefix cut
+    # prefix units: per group, subgroups of <= tile rows / g members, each prefix cut
     # into K parts per head; member t of part k writes slot partial + t*K
     covered = defaultdict(list)
     for u in pre:
         s0, m_, h = int(u["q_begin"]), int(u["q_end"] - u["q_begin"]), int(u["kv_head"])
         K = int(u["part_stride"])
-        assert 1 <= m_ <= 128 // g and 1 <= K <= MAX_PARTS
+        assert 1 <= m_ <= pa.pa_prefill_tile_rows(128) // g and 1 <= K <= MAX_PARTS
         assert u["request"] == s0 and u["merge"] == -1 and u["diag"] == u["kv_end"] - 1
         for t in range(m_):
             b = s0 + t
@@ -124,7 +124,8 @@ def test_system_prompt_groups():
     gi = np.array([0, 64], np.int32)
     pl = np.array([4096], np.int32)
     offs, units, merges, n_p, pre = check_cascade(ip, gi, pl, 32, 8, max_wg=768)
-    assert pre.size == 2 * 8 * 16       # subgroups of 32, 16 parts of 256 entries
+    members = pa.pa_prefill_tile_rows(128) // 4          # requests per prefix unit
+    assert pre.size == -(-64 // members) * 8 * 16        # subgroups x KV heads x 16 parts of 256 entries
 
 
 @pytest.mark.parametrize("seed", range(10))
@@ -153,7 +154,8 @@ def test_large_group_is_split():
     offs, units, merges, n_p, pre = check_cascade(ip, gi, np.array([2500], np.int32), 32, 8,
                                                   pa.PA_PLAN_CASCADE_ALL)
     members = sorted(set((int(u["q_begin"]), int(u["q_end"])) for u in pre))
-    assert members == [(0, 32), (32, 64), (64, 70)]
+    m = pa.pa_prefill_tile_rows(128) // 4
+    assert members == [(s0, min(70, s0 + m)) for s0 in range(0, 70, m)]
 
 
 def test_no_prefix_is_plain_decode():
@@ -192,7 +194,7 @@ def test_forced_splits_rejected():
 def test_prefix_counts_within_plan_capacity(seed):
     """The prefix units and slots of any cascade partition stay within what a
     plan reserves: units <= max(segments, min(16*segments, 2*W)) and slots <=
-    max(segments, min(16*segments, 2*(128/g)*W)), W = decode workgroups."""
+    max(segments, min(16*segments, 2*(rows/g)*W)), W = decode workgroups, rows = prefill tile rows."""
     rng = np.random.default_rng(500 + seed)
     Hq, Hkv = [(32, 8), (64, 8), (16, 4), (8, 8)][seed % 4]
     g = Hq // Hkv
@@ -208,4 +210,4 @@ def test_prefix_counts_within_plan_capacity(seed):
     decode_slots = sum(int(m["n_parts"]) for m in merges)
     prefix_slots = n_p - decode_slots
     assert pre.size <= max(segs, min(16 * segs, 2 * W))
-    assert prefix_slots <= max(segs, min(16 * segs, 2 * (128 // g) * W))
+    assert prefix_slots <= max(segs, min(16 * segs, 2 * (pa.pa_prefill_tile_rows(128) // g) * W))

@@ -251,7 +251,7 @@ def check_prefill(units, merges, n_p, qo, ip, Hkv, group):
     tiles = defaultdict(list)
     for u in real:
         tiles[(int(u["request"]), int(u["kv_head"]), int(u["q_begin"]), int(u["q_end"]))].append(u)
-    qt = 128 // group
+    qt = pa.pa_prefill_tile_rows(128) // group
     want = set()
     for b in range(B):
         C = qo[b + 1] - qo[b]
@@ -326,10 +326,15 @@ def test_forced_splits_capacity_guarantee():
 
 def test_prefill_kv_cut_one_round():
     """Chunk tiles that cannot fill the GPU get their KV ranges cut into about
-    two parts per compute unit (one round of the resident prefill
+    one part per compute unit (one round of the resident prefill
     workgroups); tiles that fill it alone are not cut.  Every part of a tile
     covers a disjoint, contiguous piece of its causal window."""
-    for spec, n_units, n_merges in ((W.PREFILL_CHUNK512, 1024, 0), (W.PREFILL_CHUNK64, 512, 128)):
+    rows = pa.pa_prefill_tile_rows(128)
+    tiles512 = 8 * 8 * 512 // (rows // 4)        # requests x KV heads x tiles of rows/4 tokens
+    tiles64 = 8 * 8 * max(1, 64 // (rows // 4))
+    parts64 = -(-256 // tiles64)                # about one part per compute unit
+    for spec, n_units, n_merges in ((W.PREFILL_CHUNK512, tiles512, 0),
+                                    (W.PREFILL_CHUNK64, tiles64 * parts64, tiles64)):
         qo, ip, idx = W.prefill_lists(spec)
         offs, units, merges, n_p = pa.pa_partition(ip, qo, spec.num_qo_heads, spec.num_kv_heads,
                                                    spec.head_dim)
