@@ -885,9 +885,6 @@ pa_status pa_prefill_chunk_run(const pa_plan_t *p, const void *q, const void *k_
         return hip_fail((hipError_t)rc, "prefill kernel launch");
     if ((e = profile_mark(p, (hipStream_t)stream, true)) != hipSuccess)
         return hip_fail(e, "profile event");
-    rc = pa::launch_prefill_merge(l, stream);
-    if (rc != 0)
-        return hip_fail((hipError_t)rc, "merge kernel launch");
     return PA_OK;
 }
 

@@ -170,7 +170,7 @@ struct DecodeLaunch {
     float sm_scale;
     float *out;
     float *lse;                     // may be null
-    float *partial_o;               // decode: [slots, group, D]; prefill: [slots, tile rows, D]
+    float *partial_o;               // decode: [slots, group, D]; prefill: [slots, tile rows x D] in register order
     float *partial_lse;             // decode: [slots, group];    prefill: [slots, tile rows]
     int32_t *arrivals;              // per merge unit: parts finished in this launch (zero between launches)
     int32_t num_qo_heads;
@@ -188,8 +188,6 @@ bool row_offsets_fit_32(int64_t num_slots, uint32_t stride_bytes);
 // Decode workgroups one compute unit holds at once (0 if unknown).
 int decode_workgroups_per_cu(int32_t head_dim, int32_t group);
 int launch_prefill(const DecodeLaunch &l, void *stream);
-// Log-sum-exp merge of the prefill partials (no-op without merge units).
-int launch_prefill_merge(const DecodeLaunch &l, void *stream);
 
 // Decode without allocation (pa_decode_run_noalloc): the work table,
 // partial results and arrival counters live in a file-scope device array of

@@ -9,30 +9,35 @@
 // weighted sum are the textbook ones, in the base-2 exponent domain as in the
 // decode kernel.
 //
-// One workgroup (4 waves) runs one work unit: one request, one KV head, a
-// tile of up to 128/G chunk tokens whose G query heads are stacked into 128
-// rows (row r = token * G + head, so wave w owns rows 32w .. 32w+31), and a
-// contiguous range of the list.  Per tile of KT list entries:
-//   * all 256 threads gather the KT K rows and V rows of the KV head (16-byte
+// One workgroup runs one work unit at a time: one request, one KV head, a
+// tile of chunk tokens whose G query heads are stacked into the tile's rows
+// (row r = token * G + head; 256 rows over 8 waves at head_dim 128, 128 rows
+// over 4 waves at 256; wave w owns rows 32w .. 32w+31), and a contiguous
+// range of the list.  Per tile of KT list entries:
+//   * all threads gather the KT K rows and V rows of the KV head (16-byte
 //     loads, one slot id per row) into registers one tile ahead, and write
 //     them into a double-buffered LDS stage (row-major, rows padded so that
-//     the reads below hit distinct banks);
+//     the reads below hit distinct banks); K stays bf16, V is converted to
+//     fp16 (exact for bf16 magnitudes in [2^-14, 65520));
 //   * each wave computes its 32 x KT score block transposed, S^T = K Q^T,
 //     with v_mfma_f32_32x32x16_bf16 (K rows from LDS as the A operand, the
 //     wave's 32 query rows held in registers as the B operand for the whole
 //     unit), so every lane ends up owning 16 x (KT/32) scores of ONE query
 //     row and the row statistics need a single cross-half exchange;
 //   * online softmax in fp32 with a lazily moved maximum (as in decode);
-//   * the weights P are split into two bf16 terms, P = hi + lo (lo = the
-//     rounding residue of hi), and O^T += V^T hi^T + V^T lo^T, so the weighted
-//     sum keeps about 16 bits of each weight instead of bf16's 8; the V^T
-//     operand is read straight from the row-major LDS tile with the
-//     transposing read ds_read_b64_tr_b16, and the P^T operand is regrouped
-//     from the score layout with two v_permlane32_swap per 16 entries;
+//   * the weights P are rounded once to fp16 and O^T += V^T P^T runs on
+//     v_mfma_f32_32x32x16_f16; the row sum adds the same rounded weights, so
+//     the result is the exact weighted mean of V under them; the V^T operand
+//     is read straight from the row-major LDS tile with the transposing read
+//     ds_read_b64_tr_b16, and the P^T operand is regrouped from the score
+//     layout with two v_permlane32_swap per 16 entries;
 //   * O^T accumulates in the MFMA's fp32 registers: a lane holds D/2 values
 //     of its own row, so rescaling is a per-lane multiply.
-// The unit writes the final rows, or a partial result (normalised O and its
-// log2-sum-exp) that the merge kernel combines.
+// A unit whose V holds a finite value that fp16 cannot represent runs again
+// with V scaled by a power of two.  A unit over a whole range writes the
+// final rows; the parts of a cut range publish normalised rows and their
+// log2-sum-exp, and the last part to finish merges them (no second launch);
+// cascade prefix units write partial rows that the decode kernel merges.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -63,7 +68,6 @@ template <int D>
 constexpr int prefill_waves() {
     return prefill_tile_rows(D) / 32;
 }
-constexpr int kMergeThreads = 256;
 
 template <int D>
 struct PrefillGeo {
@@ -137,8 +141,37 @@ __device__ __forceinline__ uint4 regroup(uint32_t x0, uint32_t x1, uint32_t y0, 
     return uint4{s0[0], s1[0], s0[1], s1[1]};
 }
 
-// s_waitcnt vmcnt(0): every vector-memory load of this wave has returned.
+// s_waitcnt vmcnt(0): every vector-memory access of this wave has completed.
 __device__ __forceinline__ void wait_vector_memory() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Agent-scope (all XCDs) coherent accesses: relaxed atomics, which the
+// compiler emits as plain loads and stores with the coherence bits set, so
+// that they bypass the non-shared L2 of the issuing XCD.
+__device__ __forceinline__ void store_coherent(float *p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float *p) {
+    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// The same coherence for pairs of floats, as raw buffer accesses with the
+// instruction's sc1 bit (cache-policy operand 16), over a descriptor of one
+// partial slot: byte offset = voff (per lane) + soff (uniform).  One 32-bit
+// lane offset instead of a 64-bit address per access keeps the merge's
+// registers within the tile loop's budget.
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+constexpr int kCoherentPolicy = 16;
+constexpr int32_t kBufferWord3 = 0x00020000;   // 32-bit data format, no swizzle or stride
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slot_rsrc(float *p, int32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, bytes, kBufferWord3);
+}
+__device__ __forceinline__ void store_coherent2(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, float a,
+                                                float b) {
+    const u32x2_t v = {__float_as_uint(a), __float_as_uint(b)};
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, voff, soff, kCoherentPolicy);
+}
+__device__ __forceinline__ f32x2_t load_coherent2(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(f32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kCoherentPolicy));
+}
 
 __device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -155,6 +188,7 @@ prefill_kernel(const int32_t *__restrict__ wg_offsets, const pa_work_unit *__res
                const char *__restrict__ v_pool, uint64_t stride_bytes,
                const int32_t *__restrict__ kv_indices, float scale_log2, float *__restrict__ out,
                float *__restrict__ lse, float *__restrict__ part_o, float *__restrict__ part_lse,
+               const pa_merge_unit *__restrict__ merges, int32_t *__restrict__ arrivals,
                int32_t num_qo_heads) {
     using Geo = PrefillGeo<D>;
     constexpr int KT = Geo::KT, KROW = Geo::KROW, VROW = Geo::VROW, STAGE = Geo::STAGE;
@@ -164,6 +198,7 @@ prefill_kernel(const int32_t *__restrict__ wg_offsets, const pa_work_unit *__res
 
     __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
     __shared__ float flag_lds[WAVES];
+    __shared__ int32_t arrived_lds;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -447,34 +482,116 @@ prefill_kernel(const int32_t *__restrict__ wg_offsets, const pa_work_unit *__res
             const float l_row = l + other_half(l);
             const float inv = l_row > 0.f ? __builtin_amdgcn_ldexpf(1.f / l_row, vshift) : 0.f;
             const float lse2 = l_row > 0.f ? m + fast_log2(l_row) : -INFINITY;
-            if (!row_valid)
-                return false;
-            float *dst;
+            // O^T element i of block db: column db*32 + 8*(i/4) + 4*half + i%4
+            auto write_row = [&](float *dst, float f) {
+#pragma unroll
+                for (int db = 0; db < DB; db++)
+#pragma unroll
+                    for (int j = 0; j < 4; j++) {
+                        const float4 v = {o[db][4 * j] * f, o[db][4 * j + 1] * f, o[db][4 * j + 2] * f,
+                                          o[db][4 * j + 3] * f};
+                        *reinterpret_cast<float4 *>(dst + db * 32 + 8 * j + 4 * half) = v;
+                    }
+            };
             if (unit.partial < 0) {
+                if (!row_valid)
+                    return false;
                 const int64_t orow = (int64_t)(unit.q_begin + tt) * num_qo_heads + unit.kv_head * G + g;
-                dst = out + orow * D;
                 if (lse && half == 0)
                     lse[orow] = lse2 * kLn2;
-            } else {
-                // a cascade prefix unit writes query token tt's rows into slot
-                // partial + tt * part_stride (G rows per slot, the decode layout);
-                // other units fill slot `partial` of the tile layout
-                const int64_t prow = unit.part_stride > 0
-                                         ? ((int64_t)unit.partial + (int64_t)tt * unit.part_stride) * G + g
-                                         : (int64_t)unit.partial * TILE_ROWS + row;
-                dst = part_o + prow * D;
+                write_row(out + orow * D, inv);
+                return false;
+            }
+            if (unit.part_stride > 0) {
+                // a cascade prefix unit: query token tt's rows go to slot
+                // partial + tt * part_stride (G rows per slot, the decode
+                // layout), merged by the decode kernel
+                if (!row_valid)
+                    return false;
+                const int64_t prow = ((int64_t)unit.partial + (int64_t)tt * unit.part_stride) * G + g;
                 if (half == 0)
                     part_lse[prow] = lse2;
+                write_row(part_o + prow * D, inv);
+                return false;
             }
-            // O^T element i of block db: column db*32 + 8*(i/4) + 4*half + i%4
+
+            // One of the parts of a cut KV range.  It publishes its normalised
+            // rows and their log2-sum-exp in its partial slot, in register
+            // order (wave w's block of 32 rows, then 8-byte piece k of every
+            // lane in turn: each store and load below is one contiguous 512-byte
+            // run), with agent-scope coherent stores, which write through the
+            // compute unit's own L2 (the 8 XCDs do not share one); once they
+            // have completed (s_waitcnt vmcnt(0) in every wave, then the
+            // barrier) it counts itself in.  The part that arrives last reads
+            // the others with agent-scope coherent loads, issued after it has
+            // seen the count, and merges them with its own rows, still in
+            // registers; it then clears the counter for the next launch.
+            constexpr int32_t SLOT_BYTES = TILE_ROWS * D * 4;
+            // The lane id passes through an empty asm statement, so that the
+            // offsets derived from it are computed here and not hoisted to the
+            // kernel's start, where they would hold registers through the
+            // tile loop.
+            uint32_t lid = lane;
+            asm volatile("" : "+v"(lid));
+            // this lane's byte offset within a slot: its wave's block, its 8 bytes of a piece
+            const uint32_t lane_off = (uint32_t)(wave * (32 * D * 4)) + lid * 8;
+            {
+                const __amdgpu_buffer_rsrc_t slot = slot_rsrc(part_o + (int64_t)unit.partial * (TILE_ROWS * D), SLOT_BYTES);
+                if (half == 0)
+                    store_coherent(part_lse + (int64_t)unit.partial * TILE_ROWS + row, lse2);
+#pragma unroll
+                for (int db = 0; db < DB; db++)
+#pragma unroll
+                    for (int k = 0; k < 8; k++)
+                        store_coherent2(slot, lane_off + (db * 8 + k) * 512, 0, o[db][2 * k] * inv,
+                                        o[db][2 * k + 1] * inv);
+            }
+            wait_vector_memory();
+            __syncthreads();
+            if (tid == 0)
+                arrived_lds = __hip_atomic_fetch_add(arrivals + unit.merge, 1, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();
+            const int32_t first = merges[unit.merge].first_partial, n_parts = merges[unit.merge].n_parts;
+            if (arrived_lds != n_parts - 1)
+                return false;
+            // log-sum-exp merge of the parts in index order with a running
+            // maximum, acc = sum_p 2^(lse_p - M) O_p, wsum = sum_p 2^(lse_p -
+            // M), every part (this one too) read back from its slot: the same
+            // sums whichever part arrives last
+            float M = -INFINITY, wsum = 0.f;
 #pragma unroll
             for (int db = 0; db < DB; db++)
+                o[db] = f32x16_t{};
+            for (int32_t pi = first; pi < first + n_parts; pi++) {
+                const float lp = load_coherent(part_lse + (int64_t)pi * TILE_ROWS + row);
+                const __amdgpu_buffer_rsrc_t src = slot_rsrc(part_o + (int64_t)pi * (TILE_ROWS * D), SLOT_BYTES);
+                const float mx = fmaxf(M, lp);
+                const bool live = mx != -INFINITY;      // some part so far is not empty
+                const float a = live ? fast_exp2(M - mx) : 1.f;   // 0 while M is -inf
+                const float w = live ? fast_exp2(lp - mx) : 0.f;
+                // one column block (16 values of the row) per round trip
 #pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    const float4 v = {o[db][4 * j] * inv, o[db][4 * j + 1] * inv, o[db][4 * j + 2] * inv,
-                                      o[db][4 * j + 3] * inv};
-                    *reinterpret_cast<float4 *>(dst + db * 32 + 8 * j + 4 * half) = v;
+                for (int db = 0; db < DB; db++) {
+                    f32x2_t v[8];
+#pragma unroll
+                    for (int k = 0; k < 8; k++)
+                        v[k] = load_coherent2(src, lane_off + (db * 8 + k) * 512, 0);
+#pragma unroll
+                    for (int i = 0; i < 16; i++)
+                        o[db][i] = fmaf(w, v[i / 2][i % 2], o[db][i] * a);
                 }
+                wsum = fmaf(wsum, a, w);
+                M = live ? mx : M;
+            }
+            if (tid == 0)
+                __hip_atomic_store(arrivals + unit.merge, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (!row_valid)
+                return false;
+            const int64_t orow = (int64_t)(unit.q_begin + tt) * num_qo_heads + unit.kv_head * G + g;
+            if (lse && half == 0)
+                lse[orow] = wsum > 0.f ? (M + fast_log2(wsum)) * kLn2 : -INFINITY;
+            write_row(out + orow * D, wsum > 0.f ? 1.f / wsum : 0.f);
             return false;
         };
         // one call site (a loop) keeps the pass inlined once; vshift is
@@ -485,83 +602,6 @@ prefill_kernel(const int32_t *__restrict__ wg_offsets, const pa_work_unit *__res
     }
 }
 
-// Log-sum-exp merge of prefill partials: workgroup (x, y) combines rows
-// y*RPW .. y*RPW+RPW-1 of merge unit x; a row's D values are spread over
-// D/4 threads with one float4 each, so every part's row is one coalesced read.
-constexpr int kMergeBatch = 8;   // parts read per memory round trip
-template <int D, int G>
-__global__ __launch_bounds__(kMergeThreads) void prefill_merge_kernel(
-    const pa_merge_unit *__restrict__ merges, const float *__restrict__ part_o,
-    const float *__restrict__ part_lse, float *__restrict__ out, float *__restrict__ lse,
-    int32_t num_qo_heads) {
-    constexpr int TPR = D / 4, RPW = kMergeThreads / TPR;
-    const pa_merge_unit mu = merges[blockIdx.x];
-    const int row = blockIdx.y * RPW + threadIdx.x / TPR, c = threadIdx.x % TPR;
-    if (row >= (mu.q_end - mu.q_begin) * G)
-        return;
-    // parts read kMergeBatch at a time (one memory round trip per batch) and
-    // folded in with a running maximum; for up to kMergeBatch parts this is
-    // the plain two-pass log-sum-exp merge
-    const int32_t n = mu.n_parts;
-    float M = -INFINITY, wsum = 0.f;
-    float4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int32_t i0 = 0; i0 < n; i0 += kMergeBatch) {
-        float l[kMergeBatch];
-        float4 v[kMergeBatch];
-#pragma unroll
-        for (int j = 0; j < kMergeBatch; j++) {
-            const int64_t prow = (int64_t)(mu.first_partial + min(i0 + j, n - 1)) * prefill_tile_rows(D) + row;
-            l[j] = part_lse[prow];
-            v[j] = *reinterpret_cast<const float4 *>(part_o + prow * D + 4 * c);
-        }
-        float m = M;
-#pragma unroll
-        for (int j = 0; j < kMergeBatch; j++) {
-            if (i0 + j >= n)
-                l[j] = -INFINITY;
-            m = fmaxf(m, l[j]);
-        }
-        if (m == -INFINITY)
-            continue;
-        const float a = fast_exp2(M - m);   // 0 while M is -inf
-        acc.x *= a;
-        acc.y *= a;
-        acc.z *= a;
-        acc.w *= a;
-        wsum *= a;
-#pragma unroll
-        for (int j = 0; j < kMergeBatch; j++) {
-            const float w = fast_exp2(l[j] - m);
-            acc.x = fmaf(w, v[j].x, acc.x);
-            acc.y = fmaf(w, v[j].y, acc.y);
-            acc.z = fmaf(w, v[j].z, acc.z);
-            acc.w = fmaf(w, v[j].w, acc.w);
-            wsum += w;
-        }
-        M = m;
-    }
-    const int64_t orow = (int64_t)(mu.q_begin + row / G) * num_qo_heads + mu.kv_head * G + row % G;
-    if (M != -INFINITY) {
-        const float inv = 1.f / wsum;
-        acc.x *= inv;
-        acc.y *= inv;
-        acc.z *= inv;
-        acc.w *= inv;
-    }
-    *reinterpret_cast<float4 *>(out + orow * D + 4 * c) = acc;
-    if (lse && c == 0)
-        lse[orow] = M == -INFINITY ? -INFINITY : (M + fast_log2(wsum)) * kLn2;
-}
-
-template <int D, int G>
-int launch_prefill_merge_dg(const DecodeLaunch &l, hipStream_t stream) {
-    constexpr int RPW = kMergeThreads / (D / 4);
-    hipLaunchKernelGGL((prefill_merge_kernel<D, G>), dim3(l.n_merges, prefill_tile_rows(D) / RPW),
-                       dim3(kMergeThreads), 0, stream, l.merges, l.partial_o, l.partial_lse, l.out, l.lse,
-                       l.num_qo_heads);
-    return (int)hipGetLastError();
-}
-
 template <int D, int G>
 int launch_prefill_dg(const DecodeLaunch &l, hipStream_t stream) {
     const uint64_t stride_bytes = (uint64_t)l.slot_stride * 2;
@@ -570,12 +610,12 @@ int launch_prefill_dg(const DecodeLaunch &l, hipStream_t stream) {
         hipLaunchKernelGGL((prefill_kernel<D, G, true>), dim3(l.n_workgroups), dim3(PrefillGeo<D>::THREADS), 0, stream,
                            l.wg_offsets, l.units, (const uint16_t *)l.q, (const char *)l.k_pool,
                            (const char *)l.v_pool, stride_bytes, l.kv_indices, l.sm_scale * kLog2e, l.out,
-                           l.lse, l.partial_o, l.partial_lse, l.num_qo_heads);
+                           l.lse, l.partial_o, l.partial_lse, l.merges, l.arrivals, l.num_qo_heads);
     else
         hipLaunchKernelGGL((prefill_kernel<D, G, false>), dim3(l.n_workgroups), dim3(PrefillGeo<D>::THREADS), 0, stream,
                            l.wg_offsets, l.units, (const uint16_t *)l.q, (const char *)l.k_pool,
                            (const char *)l.v_pool, stride_bytes, l.kv_indices, l.sm_scale * kLog2e, l.out,
-                           l.lse, l.partial_o, l.partial_lse, l.num_qo_heads);
+                           l.lse, l.partial_o, l.partial_lse, l.merges, l.arrivals, l.num_qo_heads);
     return (int)hipGetLastError();
 }
 
@@ -599,29 +639,6 @@ int launch_prefill(const DecodeLaunch &l, void *stream) {
         case 2: return launch_prefill_dg<256, 2>(l, s);
         case 4: return launch_prefill_dg<256, 4>(l, s);
         case 8: return launch_prefill_dg<256, 8>(l, s);
-        }
-    }
-    return (int)hipErrorInvalidValue;
-}
-
-int launch_prefill_merge(const DecodeLaunch &l, void *stream) {
-    if (l.n_merges == 0)
-        return 0;
-    hipStream_t s = (hipStream_t)stream;
-    const int G = l.num_qo_heads / l.num_kv_heads;
-    if (l.head_dim == 128) {
-        switch (G) {
-        case 1: return launch_prefill_merge_dg<128, 1>(l, s);
-        case 2: return launch_prefill_merge_dg<128, 2>(l, s);
-        case 4: return launch_prefill_merge_dg<128, 4>(l, s);
-        case 8: return launch_prefill_merge_dg<128, 8>(l, s);
-        }
-    } else if (l.head_dim == 256) {
-        switch (G) {
-        case 1: return launch_prefill_merge_dg<256, 1>(l, s);
-        case 2: return launch_prefill_merge_dg<256, 2>(l, s);
-        case 4: return launch_prefill_merge_dg<256, 4>(l, s);
-        case 8: return launch_prefill_merge_dg<256, 8>(l, s);
         }
     }
     return (int)hipErrorInvalidValue;
