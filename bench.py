@@ -498,12 +498,15 @@ def main():
         group_indptr = np.arange(0, B + 1, spec.prefix_group_size, dtype=np.int32)
         prefix_len = np.full(group_indptr.size - 1, spec.prefix_len, np.int32)
 
+    # the partition sized for the kernel of the pools' element type
+    plan_flags = args.flags | (pa.PA_PLAN_KV_FP8 if fp8 else 0)
+
     def do_plan():
         if args.cascade:
-            plan.plan_cascade(case.kv_indptr, group_indptr, prefix_len, flags=args.flags,
+            plan.plan_cascade(case.kv_indptr, group_indptr, prefix_len, flags=plan_flags,
                               stream=stream)
         else:
-            plan.plan(case.kv_indptr, flags=args.flags, stream=stream)
+            plan.plan(case.kv_indptr, flags=plan_flags, stream=stream)
 
     def layer_runs(s):
         for layer in range(layers):
@@ -648,7 +651,7 @@ def main():
             "list_entries": int(case.kv_indptr[-1]),
             "unique_slots": int(np.unique(case.kv_indices).size),
             "pool_slots": spec.num_slots,
-            "plan_flags": args.flags,
+            "plan_flags": plan_flags,
             "workgroup_weight_range": wg_weight_range,
         },
         "us_per_step_layer": round(ms_per_step * 1e3 / layers, 2),

@@ -122,6 +122,12 @@ typedef enum pa_status {
  * streamed), which measured faster than a separate prefix pass over so few
  * rows. */
 #define PA_PLAN_CASCADE_ALL 0x4u
+/* Size the decode partition for pa_decode_run_fp8: its kernel keeps fewer
+ * workgroups resident per compute unit than the bf16 one, and the automatic
+ * split cuts the lists for as many workgroups as run at once.  Either run
+ * call accepts a plan made with or without it (the result is the same up to
+ * rounding); a mismatched plan only balances the work less well. */
+#define PA_PLAN_KV_FP8 0x8u
 
 /* Largest max_kv_total a plan accepts: list entries are addressed with 32-bit
  * byte offsets. */

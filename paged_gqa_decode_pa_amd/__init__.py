@@ -40,6 +40,7 @@ PA_MAX_KV_TOTAL = 1 << 29
 PA_PLAN_NO_XCD_ORDER = 0x1
 PA_PLAN_SPEED_FEEDBACK = 0x2
 PA_PLAN_CASCADE_ALL = 0x4
+PA_PLAN_KV_FP8 = 0x8
 PA_NUM_XCD = 8
 
 

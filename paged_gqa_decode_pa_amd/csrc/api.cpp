@@ -25,7 +25,8 @@ struct pa_plan {
     int32_t max_q_total = 0;
     int32_t num_qo_heads = 0, num_kv_heads = 0, head_dim = 0, group = 0;
     int32_t num_cu = pa::kNumCu, num_xcd = pa::kNumXcd;
-    int32_t max_workgroups = 0;  // decode workgroups resident at once
+    int32_t max_workgroups = 0;  // decode workgroups resident at once (bf16 pools)
+    int32_t max_workgroups_fp8 = 0;  // the same for E4M3 pools (PA_PLAN_KV_FP8)
     int64_t wg_cap = 0, unit_cap = 0, merge_cap = 0, partial_rows_cap = 0;
     int64_t prefix_cap = 0;       // cascade prefix units
     // device: [workgroup offsets | units | merges] packed by the last pa_plan,
@@ -371,8 +372,10 @@ static pa_status plan_impl(pa_plan_t *p, const int32_t *kv_indptr_host, const in
     const size_t units_at = offsets_bytes(p->wg_cap);
     pa_work_unit *units = reinterpret_cast<pa_work_unit *>(stage + units_at);
     pa_merge_unit *merges = reinterpret_cast<pa_merge_unit *>(stage + units_at + (size_t)p->unit_cap * kUnit);
+    // decode workgroups the GPU keeps resident for the pools' element type
+    const int32_t max_wg = (flags & PA_PLAN_KV_FP8) ? p->max_workgroups_fp8 : p->max_workgroups;
     pa::PartitionArgs a{kv_indptr_host, qo_indptr_host, batch, p->num_qo_heads, p->num_kv_heads,
-                        p->head_dim, flags, p->max_workgroups, p->num_xcd,
+                        p->head_dim, flags, max_wg, p->num_xcd,
                         p->xcd_weighted ? p->xcd_weight : nullptr,
                         p->wg_weighted ? p->wg_weight.data() : nullptr, p->n_clock};
     pa::PartitionResult r;
@@ -429,7 +432,7 @@ static pa_status plan_impl(pa_plan_t *p, const int32_t *kv_indptr_host, const in
         p->clock_pending = true;
     }
     // only launches that fill the GPU measure the workgroups' speeds
-    p->clock_record = feedback && r.n_workgroups >= p->max_workgroups &&
+    p->clock_record = feedback && r.n_workgroups >= max_wg &&
                       r.n_workgroups <= p->n_clock;
     p->mode = qo_indptr_host ? pa::PlanMode::kPrefill : pa::PlanMode::kDecode;
     p->batch = batch;
@@ -630,10 +633,14 @@ pa_status pa_plan_create(pa_plan_t **out, int32_t max_batch, int64_t max_kv_tota
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, p->device) == hipSuccess &&
         cus > 0)
         p->num_cu = cus;
-    int per_cu = pa::decode_workgroups_per_cu(head_dim, p->group);
+    int per_cu = pa::decode_workgroups_per_cu(head_dim, p->group, false);
     if (per_cu <= 0)
         per_cu = pa::kDefaultWorkgroupsPerCu;
     p->max_workgroups = p->num_cu * per_cu;
+    // E4M3 pools: as many workgroups as that kernel keeps resident (never
+    // more than the bf16 count the capacities below are sized for)
+    const int per_cu_fp8 = pa::decode_workgroups_per_cu(head_dim, p->group, true);
+    p->max_workgroups_fp8 = per_cu_fp8 > 0 ? std::min(p->max_workgroups, p->num_cu * per_cu_fp8) : p->max_workgroups;
     pa::partition_capacity(max_batch, max_kv_total, max_q_total, num_qo_heads, num_kv_heads,
                            head_dim, p->max_workgroups, p->num_xcd, &p->wg_cap, &p->unit_cap,
                            &p->merge_cap, &p->partial_rows_cap, &p->prefix_cap);

@@ -18,6 +18,9 @@
 //     8c..8c+7), so one wave-wide load instruction fetches RPI = 64/LPR whole
 //     rows (4 rows at D = 128, 2 at D = 256): fully coalesced 128-bit loads,
 //     each lane gathering through its own slot id;
+//     E4M3 pools (one byte per element) take 16 elements a lane for groups of
+//     up to 4 query heads (LPR = D/16; a row of 8 lanes is two quads 8 lanes
+//     apart) and 8 for groups of 8;
 //   * a wave walks the unit in tiles of NI instructions (NI*RPI tokens); the
 //     four waves take every fourth tile; tiles alternate between two register
 //     sets, so one tile's K and V rows are in flight while the other's are
@@ -61,6 +64,8 @@ namespace pa {
 namespace {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -117,16 +122,21 @@ __device__ __forceinline__ float swizzle(float x) {
     return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), AND | (OR << 5) | (XOR << 10)));
 }
 // Sum (max) over the rows of a wave instruction: lanes that hold the same
-// 16-byte chunk of different rows (lane ^ 16, lane ^ 32 at 16 lanes per row;
-// lane ^ 32 at 32).
+// chunk of different rows (lane ^ 16, lane ^ 32 at 16 lanes per row; lane ^
+// 32 at 32; lane ^ 4, ^ 16, ^ 32 at 8, where a row is two quads 8 lanes
+// apart).
 template <int LPR>
 __device__ __forceinline__ float sum_rows(float x) {
+    if constexpr (LPR == 8)
+        x += swizzle<0x1f, 0, 4>(x);
     if constexpr (LPR <= 16)
         x = sum_xor16(x);
     return sum_xor32(x);
 }
 template <int LPR>
 __device__ __forceinline__ float max_rows(float x) {
+    if constexpr (LPR == 8)
+        x = fmaxf(x, swizzle<0x1f, 0, 4>(x));
     if constexpr (LPR <= 16)
         x = max_xor16(x);
     return max_xor32(x);
@@ -189,13 +199,14 @@ __device__ __forceinline__ float group_bcast(float x, int h, int lane) {
 // same head.  In the first step the partner's value is the starting value of
 // the dot-product chain of index 2m, which saves the add and the zeroing of
 // that chain's accumulator.
-template <int G, int LPR>
-__device__ __forceinline__ float row_scores(const uint32_t (&qv)[G][4], const uint4 &k) {
+template <int G, int LPR, int NQ>
+__device__ __forceinline__ float row_scores(const uint32_t (&qv)[G][NQ], const uint32_t (&k)[NQ]) {
     auto chain = [&](int j, float c) {
-        float a = dot2_bf16(qv[j][0], k.x, c);
-        a = dot2_bf16(qv[j][1], k.y, a);
-        a = dot2_bf16(qv[j][2], k.z, a);
-        return dot2_bf16(qv[j][3], k.w, a);
+        float a = c;
+#pragma unroll
+        for (int w = 0; w < NQ; w++)
+            a = dot2_bf16(qv[j][w], k[w], a);
+        return a;
     };
     float x;
     if constexpr (G == 1) {
@@ -218,11 +229,16 @@ __device__ __forceinline__ float row_scores(const uint32_t (&qv)[G][4], const ui
         if constexpr (G == 2)
             x += dpp_mov<kQuadXor2>(x);
     }
-    if constexpr (G <= 4)
-        x += dpp_mov<kRowRor4>(x);
-    x += dpp_mov<kRowRor8>(x);
-    if constexpr (LPR == 32)
-        x = sum_xor16(x);
+    if constexpr (LPR == 8) {
+        // the row's other quad holds the same heads 8 lanes away
+        x += dpp_mov<kRowRor8>(x);
+    } else {
+        if constexpr (G <= 4)
+            x += dpp_mov<kRowRor4>(x);
+        x += dpp_mov<kRowRor8>(x);
+        if constexpr (LPR == 32)
+            x = sum_xor16(x);
+    }
     return x;
 }
 
@@ -266,12 +282,31 @@ __device__ __forceinline__ T load_streamed(const T *p) {
     return __builtin_bit_cast(T, __builtin_nontemporal_load(reinterpret_cast<const V *>(p)));
 }
 
-template <int D>
+// Lane layout of K/V rows: EPL elements of a row per lane (16 bytes of bf16,
+// 8 or 16 bytes of E4M3 codes).
+template <int D, int EPL, int NI_>
 struct Geometry {
-    static constexpr int LPR = D / 8;          // lanes per row
+    static constexpr int LPR = D / EPL;        // lanes per row
     static constexpr int RPI = 64 / LPR;       // rows per wave instruction
-    static constexpr int NI = 4;               // instructions per tile
+    static constexpr int NI = NI_;             // instructions per tile
     static constexpr int TILE = NI * RPI;      // tokens per wave tile
+    // Row (within an instruction) and chunk of a lane.  Rows of 16 or 32
+    // lanes are contiguous.  A row of 8 lanes is two quads 8 lanes apart
+    // (lanes 16a + 4b .. +3 and 16a + 4b + 8 .. +11 for row 2a + b), so
+    // that every exchange of the score reduction stays a DPP move inside a
+    // 16-lane row (quad permutations, then lane ^ 8).
+    static __device__ __forceinline__ int row(int lane) {
+        if constexpr (LPR == 8)
+            return 2 * (lane >> 4) + ((lane >> 2) & 1);
+        else
+            return lane / LPR;
+    }
+    static __device__ __forceinline__ int chunk(int lane) {
+        if constexpr (LPR == 8)
+            return (lane & 3) + ((lane >> 1) & 4);
+        else
+            return lane % LPR;
+    }
 };
 
 // Byte offset of a pool row: 32-bit form or 64-bit form.  The 32-bit form
@@ -297,20 +332,34 @@ struct RowAddr<true> {
     }
 };
 
-// Element type of the pools.  bf16: a lane's 8 elements of a row are one
-// 16-byte load, already in the dot-product and FMA operand formats.  OCP FP8
-// E4M3 (8-bit pools): the same 8 elements are one 8-byte load; K codes are
-// widened to bf16 pairs (exact: every E4M3 value is a bf16 value) for the
-// dot products and V codes to fp32 for the weighted sum, with
-// v_cvt_scalef32_pk_bf16_fp8 / v_cvt_pk_f32_fp8 (scale 1: the pools' scales
-// are applied to the softmax scale and to the output).
-template <bool KV8>
+// Element type of the pools and the lane's part of a row.
+//   * bf16: a lane's 8 elements of a row are one 16-byte load, already in
+//     the dot-product and FMA operand formats.
+//   * OCP FP8 E4M3: 16 codes a lane (one 16-byte load) for groups of up to
+//     4 query heads, 8 (one 8-byte load) for groups of 8, whose 8 x 16 fp32
+//     accumulators would not fit.  K codes are widened to bf16 pairs (exact:
+//     every E4M3 value is a bf16 value, v_cvt_scalef32_pk_bf16_fp8) for the
+//     dot products.  The weighted sum runs on fp16 dot products over two
+//     tokens at once (PAIRED): element e of the lane's rows i, i+1 becomes
+//     one fp16 pair (bytes interleaved with v_perm_b32, then
+//     v_cvt_scalef32_pk_f16_fp8: E4M3 -> fp16 is exact), the two rows'
+//     weights (<= 2^8) are rounded once to an fp16 pair, and one
+//     v_dot2_f32_f16 adds both products with fp32 accumulation: half the
+//     multiply-adds of the fp32 form.  The row sums add the same rounded
+//     weights, so the result is the exact weighted mean of V under them.
+// Scale 1 in the conversions: the pools' scales are applied to the softmax
+// scale and to the output.
+template <bool KV8, int EPL>
 struct PoolRow;
 template <>
-struct PoolRow<false> {
+struct PoolRow<false, 8> {
     using T = uint4;
     static constexpr uint32_t kElemBytes = 2;
-    static __device__ __forceinline__ uint4 k_bf16(const uint4 &x) { return x; }
+    static constexpr int NQ = 4;               // bf16 pairs of the lane's elements
+    static constexpr bool PAIRED = false;
+    static __device__ __forceinline__ void k_words(const uint4 &x, uint32_t (&w)[4]) {
+        w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
+    }
     static __device__ __forceinline__ void v_f32(const uint4 &x, float (&f)[8]) {
         // a bf16 value is the upper half of the fp32 with the same value
         f[0] = __uint_as_float(x.x << 16); f[1] = __uint_as_float(x.x & 0xffff0000u);
@@ -319,26 +368,76 @@ struct PoolRow<false> {
         f[6] = __uint_as_float(x.w << 16); f[7] = __uint_as_float(x.w & 0xffff0000u);
     }
 };
+// two E4M3 codes (the low or high half of w) as a bf16 pair
+__device__ __forceinline__ uint32_t e4m3_pair_bf16(uint32_t w, bool hi) {
+    return hi ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true))
+              : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+}
 template <>
-struct PoolRow<true> {
+struct PoolRow<true, 8> {
     using T = uint2;
     static constexpr uint32_t kElemBytes = 1;
-    static __device__ __forceinline__ uint32_t pair(uint32_t w, bool hi) {
-        return hi ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true))
-                  : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+    static constexpr int NQ = 4;
+    static constexpr bool PAIRED = true;
+    static __device__ __forceinline__ void v_pairs(const uint2 &a, const uint2 &b, f16x2_t (&f)[8]) {
+        const uint32_t wa[2] = {a.x, a.y}, wb[2] = {b.x, b.y};
+#pragma unroll
+        for (int w = 0; w < 2; w++) {
+            const uint32_t lo = __builtin_amdgcn_perm(wb[w], wa[w], 0x05010400u);   // a0 b0 a1 b1
+            const uint32_t hi = __builtin_amdgcn_perm(wb[w], wa[w], 0x07030602u);   // a2 b2 a3 b3
+            f[4 * w] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false);
+            f[4 * w + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true);
+            f[4 * w + 2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false);
+            f[4 * w + 3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true);
+        }
     }
-    static __device__ __forceinline__ uint4 k_bf16(const uint2 &x) {
-        return make_uint4(pair(x.x, false), pair(x.x, true), pair(x.y, false), pair(x.y, true));
-    }
-    static __device__ __forceinline__ void v_f32(const uint2 &x, float (&f)[8]) {
-        const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(x.x, false);
-        const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(x.x, true);
-        const auto c = __builtin_amdgcn_cvt_pk_f32_fp8(x.y, false);
-        const auto d = __builtin_amdgcn_cvt_pk_f32_fp8(x.y, true);
-        f[0] = a[0]; f[1] = a[1]; f[2] = b[0]; f[3] = b[1];
-        f[4] = c[0]; f[5] = c[1]; f[6] = d[0]; f[7] = d[1];
+    static __device__ __forceinline__ void k_words(const uint2 &x, uint32_t (&w)[4]) {
+        w[0] = e4m3_pair_bf16(x.x, false); w[1] = e4m3_pair_bf16(x.x, true);
+        w[2] = e4m3_pair_bf16(x.y, false); w[3] = e4m3_pair_bf16(x.y, true);
     }
 };
+template <>
+struct PoolRow<true, 16> {
+    using T = uint4;
+    static constexpr uint32_t kElemBytes = 1;
+    static constexpr int NQ = 8;
+    static constexpr bool PAIRED = true;
+    static __device__ __forceinline__ void k_words(const uint4 &x, uint32_t (&w)[8]) {
+        w[0] = e4m3_pair_bf16(x.x, false); w[1] = e4m3_pair_bf16(x.x, true);
+        w[2] = e4m3_pair_bf16(x.y, false); w[3] = e4m3_pair_bf16(x.y, true);
+        w[4] = e4m3_pair_bf16(x.z, false); w[5] = e4m3_pair_bf16(x.z, true);
+        w[6] = e4m3_pair_bf16(x.w, false); w[7] = e4m3_pair_bf16(x.w, true);
+    }
+    // f[e] = (element e of row a, element e of row b) as an fp16 pair:
+    // bytes of the two rows interleaved (v_perm_b32), then widened two at a
+    // time.
+    static __device__ __forceinline__ void v_pairs(const uint4 &a, const uint4 &b, f16x2_t (&f)[16]) {
+        const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int w = 0; w < 4; w++) {
+            // byte k of the result = byte sel[k] of {wb (4..7), wa (0..3)}
+            const uint32_t lo = __builtin_amdgcn_perm(wb[w], wa[w], 0x05010400u);   // a0 b0 a1 b1
+            const uint32_t hi = __builtin_amdgcn_perm(wb[w], wa[w], 0x07030602u);   // a2 b2 a3 b3
+            f[4 * w] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false);
+            f[4 * w + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true);
+            f[4 * w + 2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false);
+            f[4 * w + 3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true);
+        }
+    }
+};
+// Elements of a row per lane: 16 E4M3 codes for groups of up to 4 query
+// heads, else 8.
+template <bool KV8, int G>
+constexpr int lane_elems() {
+    return KV8 && G <= 4 ? 16 : 8;
+}
+// Instructions per wave tile: 4 (bf16), 4 (E4M3, 16 codes a lane: 32 tokens)
+// or 8 (E4M3, 8 codes a lane: 32 tokens).  The E4M3 tiles move as many bytes
+// per wave as the bf16 ones, so that as many are in flight.
+template <bool KV8, int G>
+constexpr int tile_instructions() {
+    return KV8 && lane_elems<KV8, G>() == 8 ? 8 : 4;
+}
 
 // Log-sum-exp merge of one merge unit: partial slots [first, first+n) of
 // query rows [q_begin, q_end) of one KV head.  Each slot holds rows_per_slot
@@ -410,16 +509,19 @@ __device__ __forceinline__ void merge_rows(const pa_merge_unit &mu, const float 
 }
 
 // Waves per SIMD the decode kernel is compiled for: three (at most 168
-// VGPRs, room for the rotating K/V registers without spills) for groups of up
-// to four query heads, two for groups of eight.
-template <int G>
+// VGPRs, room for the rotating K/V registers without spills) for bf16 pools
+// and groups of up to four query heads; two for groups of eight and for E4M3
+// pools, whose tiles hold twice the tokens (measured on the batch-64
+// workload: 114-115 us per layer against 125-129 us with three waves and
+// half the tokens per tile, and 118-119 us with 6 instructions a tile).
+template <int G, bool KV8>
 constexpr int decode_waves_per_simd() {
-    return G <= 4 ? 3 : 2;
+    return G <= 4 && !KV8 ? 3 : 2;
 }
 
 template <int D, int G, bool WIDE, bool KV8>
 __global__ __launch_bounds__(kDecodeThreads)
-__attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<G>(), 8))) void decode_kernel(
+__attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<G, KV8>(), 8))) void decode_kernel(
     const int32_t *__restrict__ wg_offsets, const pa_work_unit *__restrict__ units,
     const pa_merge_unit *__restrict__ merges, int32_t *__restrict__ arrivals,
     const uint16_t *__restrict__ q, const char *__restrict__ k_pool,
@@ -427,10 +529,11 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<G>(), 8))) void decode_
     const int32_t *__restrict__ kv_indices, float scale_log2, float out_scale, float *__restrict__ out,
     float *__restrict__ lse, float *__restrict__ part_o, float *__restrict__ part_lse,
     int32_t num_qo_heads, uint64_t *__restrict__ wg_clock) {
-    using Geo = Geometry<D>;
-    using PR = PoolRow<KV8>;
+    constexpr int EPL = lane_elems<KV8, G>();
+    using Geo = Geometry<D, EPL, tile_instructions<KV8, G>()>;
+    using PR = PoolRow<KV8, EPL>;
     using Row = typename PR::T;
-    constexpr int LPR = Geo::LPR, RPI = Geo::RPI, NI = Geo::NI, TILE = Geo::TILE;
+    constexpr int LPR = Geo::LPR, RPI = Geo::RPI, NI = Geo::NI, TILE = Geo::TILE, NQ = PR::NQ;
     constexpr int WAVES = kDecodeWaves;
 
     __shared__ float lds_o[WAVES][G][D];
@@ -480,31 +583,33 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<G>(), 8))) void decode_
     // wave index as a scalar: the tile loop below is uniform per wave
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
-    const int r = lane / LPR;      // row within an instruction
-    const int c = lane % LPR;      // 16-byte chunk of the row
+    const int r = Geo::row(lane);     // row within an instruction
+    const int c = Geo::chunk(lane);   // chunk of the row (elements EPL*c ..)
     const int hsel = lane % G;     // head whose score this lane holds after reduction
 
-    // query rows of the group: qv[j] = q[b, kvh*G + (j ^ hsel), 8c .. 8c+7]
-    uint32_t qv[G][4];
+    // query rows of the group: qv[j] = q[b, kvh*G + (j ^ hsel), EPL*c .. EPL*c + EPL-1]
+    uint32_t qv[G][NQ];
     {
-        const uint16_t *qrow = q + ((int64_t)unit.request * num_qo_heads + (int64_t)unit.kv_head * G) * D + c * 8;
+        const uint16_t *qrow = q + ((int64_t)unit.request * num_qo_heads + (int64_t)unit.kv_head * G) * D + c * EPL;
 #pragma unroll
-        for (int j = 0; j < G; j++) {
-            uint4 t = *reinterpret_cast<const uint4 *>(qrow + (int64_t)(j ^ hsel) * D);
-            qv[j][0] = t.x; qv[j][1] = t.y; qv[j][2] = t.z; qv[j][3] = t.w;
-        }
+        for (int j = 0; j < G; j++)
+#pragma unroll
+            for (int u = 0; u < NQ / 4; u++) {
+                const uint4 t = *reinterpret_cast<const uint4 *>(qrow + (int64_t)(j ^ hsel) * D + 8 * u);
+                qv[j][4 * u] = t.x; qv[j][4 * u + 1] = t.y; qv[j][4 * u + 2] = t.z; qv[j][4 * u + 3] = t.w;
+            }
     }
 
-    const uint32_t lane_off = (uint32_t)(unit.kv_head * D + c * 8) * PR::kElemBytes;
+    const uint32_t lane_off = (uint32_t)(unit.kv_head * D + c * EPL) * PR::kElemBytes;
     const int32_t kv_begin = unit.kv_begin, kv_end = unit.kv_end;
     const int32_t n_tiles = (kv_end - kv_begin + TILE - 1) / TILE;
 
     float m_run = kNoMax, l_run = 0.f;
-    float acc[G][8];
+    float acc[G][EPL];
 #pragma unroll
     for (int h = 0; h < G; h++)
 #pragma unroll
-        for (int e = 0; e < 8; e++)
+        for (int e = 0; e < EPL; e++)
             acc[h][e] = 0.f;
 
     // slot ids of a tile: entries kv_begin + tile*TILE + r + i*RPI of the
@@ -540,7 +645,9 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<G>(), 8))) void decode_
         const int32_t left = kv_end - kv_begin - tile * TILE;
 #pragma unroll
         for (int i = 0; i < NI; i++) {
-            const float sc = row_scores<G, LPR>(qv, PR::k_bf16(k[i])) * scale_log2;
+            uint32_t kw[NQ];
+            PR::k_words(k[i], kw);
+            const float sc = row_scores<G, LPR, NQ>(qv, kw) * scale_log2;
             s[i] = (r + i * RPI < left) ? sc : -INFINITY;
         }
     };
@@ -560,27 +667,48 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<G>(), 8))) void decode_
             for (int h = 0; h < G; h++) {
                 const float ah = group_bcast<G>(alpha, h, lane);
 #pragma unroll
-                for (int e = 0; e < 8; e++)
+                for (int e = 0; e < EPL; e++)
                     acc[h][e] *= ah;
             }
         }
 #pragma unroll
         for (int i = 0; i < NI; i++) {
             p[i] = fast_exp2(s[i] - m_run);
-            l_run += p[i];
+            if constexpr (!PR::PAIRED)
+                l_run += p[i];   // (paired: the rounded weights, in pv)
         }
     };
     auto pv = [&](const Row(&v)[NI], const float(&p)[NI]) {
+        if constexpr (PR::PAIRED) {
+            const f16x2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
-        for (int i = 0; i < NI; i++) {
-            float vf[8];
-            PR::v_f32(v[i], vf);
+            for (int i = 0; i < NI; i += 2) {
+                f16x2_t vp[EPL];
+                PR::v_pairs(v[i], v[i + 1], vp);
+                // weights of rows i, i+1 (<= 2^8) rounded once to fp16
+                const f16x2_t pp = __builtin_convertvector(f32x2_t{p[i], p[i + 1]}, f16x2_t);
+                l_run = __builtin_amdgcn_fdot2(pp, ones, l_run, false);
 #pragma unroll
-            for (int h = 0; h < G; h++) {
-                const float ph = group_bcast<G>(p[i], h, lane);
+                for (int h = 0; h < G; h++) {
+                    const f16x2_t ph =
+                        __builtin_bit_cast(f16x2_t, group_bcast<G>(__builtin_bit_cast(float, pp), h, lane));
 #pragma unroll
-                for (int e = 0; e < 8; e++)
-                    acc[h][e] = fmaf(ph, vf[e], acc[h][e]);
+                    for (int e = 0; e < EPL; e++)
+                        acc[h][e] = __builtin_amdgcn_fdot2(ph, vp[e], acc[h][e], false);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NI; i++) {
+                float vf[8];
+                PR::v_f32(v[i], vf);
+#pragma unroll
+                for (int h = 0; h < G; h++) {
+                    const float ph = group_bcast<G>(p[i], h, lane);
+#pragma unroll
+                    for (int e = 0; e < 8; e++)
+                        acc[h][e] = fmaf(ph, vf[e], acc[h][e]);
+                }
             }
         }
     };
@@ -658,16 +786,17 @@ __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd<G>(), 8))) void decode_
     for (int h = 0; h < G; h++) {
         const float fh = group_bcast<G>(f, h, lane);
 #pragma unroll
-        for (int e = 0; e < 8; e++)
+        for (int e = 0; e < EPL; e++)
             acc[h][e] = sum_rows<LPR>(acc[h][e] * fh);
     }
     // ---- combine the waves through LDS
     if (r == 0) {
 #pragma unroll
         for (int h = 0; h < G; h++) {
-            float4 *dst = reinterpret_cast<float4 *>(&lds_o[wave][h][c * 8]);
-            dst[0] = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
-            dst[1] = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
+            float4 *dst = reinterpret_cast<float4 *>(&lds_o[wave][h][c * EPL]);
+#pragma unroll
+            for (int u = 0; u < EPL / 4; u++)
+                dst[u] = make_float4(acc[h][4 * u], acc[h][4 * u + 1], acc[h][4 * u + 2], acc[h][4 * u + 3]);
         }
         if (c < G) {
             lds_m[wave][c] = mm;
@@ -745,7 +874,7 @@ namespace {
 
 template <int D, int G, bool KV8>
 int launch_decode_dgk(const DecodeLaunch &l, hipStream_t stream) {
-    const uint32_t stride_bytes = (uint32_t)(l.slot_stride * PoolRow<KV8>::kElemBytes);
+    const uint32_t stride_bytes = (uint32_t)(l.slot_stride * (KV8 ? 1 : 2));
     // the 32-bit row address needs every byte offset below 2^31 (it is
     // sign-extended into the address) and 24-bit multiply operands
     const bool wide = !row_offsets_fit_32(l.num_slots, stride_bytes);
@@ -774,30 +903,30 @@ int launch_decode_dg(const DecodeLaunch &l, hipStream_t stream) {
 }
 
 template <int D, int G>
-int occupancy_dg() {
+int occupancy_dg(bool kv_fp8) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<D, G, false, false>, kDecodeThreads, 0) !=
-        hipSuccess)
-        return 0;
-    return n;
+    const hipError_t e =
+        kv_fp8 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<D, G, false, true>, kDecodeThreads, 0)
+               : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<D, G, false, false>, kDecodeThreads, 0);
+    return e == hipSuccess ? n : 0;
 }
 
 }  // namespace
 
-int decode_workgroups_per_cu(int32_t head_dim, int32_t group) {
+int decode_workgroups_per_cu(int32_t head_dim, int32_t group, bool kv_fp8) {
     if (head_dim == 128) {
         switch (group) {
-        case 1: return occupancy_dg<128, 1>();
-        case 2: return occupancy_dg<128, 2>();
-        case 4: return occupancy_dg<128, 4>();
-        case 8: return occupancy_dg<128, 8>();
+        case 1: return occupancy_dg<128, 1>(kv_fp8);
+        case 2: return occupancy_dg<128, 2>(kv_fp8);
+        case 4: return occupancy_dg<128, 4>(kv_fp8);
+        case 8: return occupancy_dg<128, 8>(kv_fp8);
         }
     } else if (head_dim == 256) {
         switch (group) {
-        case 1: return occupancy_dg<256, 1>();
-        case 2: return occupancy_dg<256, 2>();
-        case 4: return occupancy_dg<256, 4>();
-        case 8: return occupancy_dg<256, 8>();
+        case 1: return occupancy_dg<256, 1>(kv_fp8);
+        case 2: return occupancy_dg<256, 2>(kv_fp8);
+        case 4: return occupancy_dg<256, 4>(kv_fp8);
+        case 8: return occupancy_dg<256, 8>(kv_fp8);
         }
     }
     return 0;

@@ -272,7 +272,7 @@ int noalloc_setup(int device, int32_t head_dim, int32_t group, void **scratch_pt
         const hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
         if (e != hipSuccess)
             return (int)e;
-        int per_cu = decode_workgroups_per_cu(head_dim, group);
+        int per_cu = decode_workgroups_per_cu(head_dim, group, false);
         if (per_cu <= 0)
             per_cu = kDefaultWorkgroupsPerCu;
         w = cus * per_cu;

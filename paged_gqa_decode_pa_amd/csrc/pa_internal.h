@@ -185,8 +185,9 @@ int launch_decode(const DecodeLaunch &l, void *stream);   // returns hipError_t
 // Whether a pool of num_slots slots of stride_bytes bytes can be addressed
 // with 32-bit row offsets (every offset below 2^31).
 bool row_offsets_fit_32(int64_t num_slots, uint32_t stride_bytes);
-// Decode workgroups one compute unit holds at once (0 if unknown).
-int decode_workgroups_per_cu(int32_t head_dim, int32_t group);
+// Decode workgroups one compute unit holds at once, for bf16 or E4M3 pools
+// (0 if unknown).
+int decode_workgroups_per_cu(int32_t head_dim, int32_t group, bool kv_fp8);
 int launch_prefill(const DecodeLaunch &l, void *stream);
 
 // Decode without allocation (pa_decode_run_noalloc): the work table,

@@ -408,7 +408,7 @@ pa_status cascade_partition(const PartitionArgs &a, const CascadeArgs &c, Partit
     if (!supported_shape(a.num_qo_heads, a.num_kv_heads, a.head_dim))
         return fail(detail, "unsupported head shape (need Hq/Hkv in {1,2,4,8}, D in {128,256})",
                     PA_ERR_UNSUPPORTED);
-    if ((a.flags & ~(PA_PLAN_NO_XCD_ORDER | PA_PLAN_SPEED_FEEDBACK | PA_PLAN_CASCADE_ALL)) != 0)
+    if ((a.flags & ~(PA_PLAN_NO_XCD_ORDER | PA_PLAN_SPEED_FEEDBACK | PA_PLAN_CASCADE_ALL | PA_PLAN_KV_FP8)) != 0)
         return fail(detail, "unknown flag bits", PA_ERR_INVALID_ARG);
     if (a.num_xcd < 1 || a.num_xcd > kMaxXcd)
         return fail(detail, "XCD count out of range", PA_ERR_INVALID_ARG);
@@ -543,7 +543,7 @@ pa_status partition(const PartitionArgs &a, PartitionScratch *scratch, int32_t *
     if (forced > PA_MAX_FORCED_SPLITS)
         return fail(detail, "forced split count above PA_MAX_FORCED_SPLITS", PA_ERR_INVALID_ARG);
     if ((a.flags & ~(PA_PLAN_FORCE_SPLITS_MASK | PA_PLAN_NO_XCD_ORDER | PA_PLAN_SPEED_FEEDBACK |
-                     PA_PLAN_CASCADE_ALL)) != 0)
+                     PA_PLAN_CASCADE_ALL | PA_PLAN_KV_FP8)) != 0)
         return fail(detail, "unknown flag bits", PA_ERR_INVALID_ARG);
     if (a.num_xcd < 1 || a.num_xcd > kMaxXcd)
         return fail(detail, "XCD count out of range", PA_ERR_INVALID_ARG);
