@@ -90,6 +90,8 @@ pa_status hip_fail(hipError_t e, const char *what) {
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
 constexpr size_t kUnit = sizeof(pa_work_unit);
 constexpr size_t kMerge = sizeof(pa_merge_unit);
 static_assert(kUnit == 48 && kMerge == 32, "table entry sizes");
@@ -373,7 +375,18 @@ static pa_status plan_impl(pa_plan_t *p, const int32_t *kv_indptr_host, const in
     pa_work_unit *units = reinterpret_cast<pa_work_unit *>(stage + units_at);
     pa_merge_unit *merges = reinterpret_cast<pa_merge_unit *>(stage + units_at + (size_t)p->unit_cap * kUnit);
     // decode workgroups the GPU keeps resident for the pools' element type
-    const int32_t max_wg = (flags & PA_PLAN_KV_FP8) ? p->max_workgroups_fp8 : p->max_workgroups;
+    const bool kv_fp8 = (flags & PA_PLAN_KV_FP8) != 0;
+    int32_t max_wg = kv_fp8 ? p->max_workgroups_fp8 : p->max_workgroups;
+    if (auto_decode && p->num_cu > 0 && max_wg >= p->num_cu) {
+        // as many workgroups per compute unit (1 .. resident) as the K/V
+        // bytes need at about kWorkgroupTargetBytes each: a small step's
+        // work in fewer, longer workgroups spends less on each one's fixed
+        // latency chain and merge
+        const int64_t bytes = kv_total * p->num_kv_heads * 2 * p->head_dim * (kv_fp8 ? 1 : 2);
+        const int64_t per_cu = std::max<int64_t>(
+            1, std::min<int64_t>(max_wg / p->num_cu, ceil_div64(bytes, (int64_t)p->num_cu * pa::kWorkgroupTargetBytes)));
+        max_wg = (int32_t)(per_cu * p->num_cu);
+    }
     pa::PartitionArgs a{kv_indptr_host, qo_indptr_host, batch, p->num_qo_heads, p->num_kv_heads,
                         p->head_dim, flags, max_wg, p->num_xcd,
                         p->xcd_weighted ? p->xcd_weight : nullptr,

@@ -47,6 +47,11 @@ constexpr int kPieceOverheadTokens = 128;
 constexpr int kMinPieceTokens = 64;
 // Workgroups per compute unit assumed when the occupancy is not known.
 constexpr int kDefaultWorkgroupsPerCu = 3;
+// pa_plan's automatic decode split gives each compute unit between one and
+// as many workgroups as it holds at once, about this many K+V bytes each
+// (measured on batch 8 x 512-4096 tokens: 24.0 us per layer with one
+// workgroup per unit against 26.0 us with three; batch 64 keeps three).
+constexpr int64_t kWorkgroupTargetBytes = 512 * 1024;
 
 // Prefill kernel geometry: rows of one query tile (chunk tokens x group), one
 // wave per 32 rows; 8 waves (2 per SIMD, one workgroup per compute unit) at
