@@ -53,6 +53,10 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 PREFILL_LAYERS = 8
 CSRC = os.path.join(ROOT, "paged_gqa_decode_pa_amd", "csrc")
 COUNTERS = os.path.join(ROOT, "profiles", "decode_b64_counters.json")
+DECODE_COUNTERS = {
+    "b64_l2048_8192_prefix16x4x1024_36layers": COUNTERS,
+    "b64_l4096_8192_prefix16x4x1024_36layers": os.path.join(ROOT, "profiles", "decode_b64_4k8k_counters.json"),
+}
 DECODE_SOURCES = ("decode.hip", "pa_internal.h")
 PREFILL_COUNTERS = {
     "prefill_8x4096_chunk512": os.path.join(ROOT, "profiles", "prefill_chunk512_counters.json"),
@@ -621,7 +625,10 @@ def main():
     step_bytes = bytes_per_layer * layers
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = bytes_per_layer / (kernel_avg_ms * 1e-3) / 1e9
-    traffic = traffic_per_launch() if spec is W.BATCH64_SHARED_PREFIX and not fp8 else None
+    # HBM bytes per launch from the committed counters of this workload's
+    # plain bf16 decode (none for E4M3 pools or cascade plans)
+    traffic = (traffic_per_launch(DECODE_COUNTERS.get(spec.name))
+               if not fp8 and not args.cascade else None)
 
     G = Hq // Hkv
     result = {

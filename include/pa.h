@@ -52,7 +52,13 @@
  * entry points never allocate and never synchronise, so they can be captured
  * into a HIP graph.  Runs must be ordered after the pa_plan call whose
  * result they read (same stream, or an event); kv_indices must not change
- * between that pa_plan and the last run of the step.
+ * between that pa_plan and the last run of the step.  A captured run keeps
+ * the launch size of the plan current at capture and reads the plan's device
+ * tables, which stay at the same addresses for the life of the plan: its
+ * replays after a later pa_plan of the same plan are valid while that
+ * pa_plan yields the same number of workgroups and of cascade prefix units
+ * (pa_plan_info), as the same lists with the same flags do; otherwise
+ * capture again.
  *
  * Errors: every call returns a pa_status; no exception crosses the ABI.
  * Argument errors are detected on the host before any GPU work is enqueued,

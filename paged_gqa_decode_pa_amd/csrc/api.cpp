@@ -102,12 +102,26 @@ size_t offsets_bytes(int64_t n_workgroups) {
     return (size_t)((n_workgroups + 1 + 15) / 16) * 64;
 }
 
-// Table layout (device and staging): [workgroup offsets | units | merges |
-// prefix workgroup offsets | prefix units]; the last two only in cascade plans.
-size_t table_bytes(const pa_plan_t *p) {
-    return offsets_bytes(p->wg_cap) + (size_t)p->unit_cap * kUnit + (size_t)p->merge_cap * kMerge +
-           offsets_bytes(p->prefix_cap) + (size_t)p->prefix_cap * kUnit;
+// Table layout (device and staging): [workgroup offsets | merge units | work
+// units | prefix workgroup offsets | prefix units], each region at a fixed
+// offset sized by the plan's capacities (the prefix regions are used only by
+// cascade plans).  A launch captured into a HIP graph keeps the region
+// addresses it was given, so they must not move when a later pa_plan of the
+// same plan cuts the lists into a different number of units or merges (the
+// speed feedback does that from step to step).
+struct TableLayout {
+    size_t merges, units, prefix_offsets, prefix_units, end;
+};
+TableLayout table_layout(const pa_plan_t *p) {
+    TableLayout t;
+    t.merges = offsets_bytes(p->wg_cap);
+    t.units = t.merges + (size_t)p->merge_cap * kMerge;
+    t.prefix_offsets = t.units + (size_t)p->unit_cap * kUnit;
+    t.prefix_units = t.prefix_offsets + offsets_bytes(p->prefix_cap);
+    t.end = t.prefix_units + (size_t)p->prefix_cap * kUnit;
+    return t;
 }
+size_t table_bytes(const pa_plan_t *p) { return table_layout(p).end; }
 
 void drop_profile(pa_plan_t *p) {
     for (hipEvent_t e : p->prof_events)
@@ -225,15 +239,14 @@ void update_cu_weights(pa_plan_t *p) {
 }
 
 // The launch of a cascade plan's prefix units: the decode launch l with the
-// prefix workgroup offsets and units of the table (packed after the merges).
+// prefix workgroup offsets and units of the table.
 pa::DecodeLaunch prefix_launch(const pa_plan_t *p, const pa::DecodeLaunch &l) {
     pa::DecodeLaunch x = l;
     const char *tbl = static_cast<const char *>(p->d_table);
-    const size_t at = offsets_bytes(p->n_workgroups) + (size_t)p->n_units * kUnit +
-                      (size_t)p->n_merges * kMerge;
-    x.wg_offsets = reinterpret_cast<const int32_t *>(tbl + at);
+    const TableLayout t = table_layout(p);
+    x.wg_offsets = reinterpret_cast<const int32_t *>(tbl + t.prefix_offsets);
     x.n_workgroups = p->n_prefix_units;
-    x.units = reinterpret_cast<const pa_work_unit *>(tbl + at + offsets_bytes(p->n_prefix_units));
+    x.units = reinterpret_cast<const pa_work_unit *>(tbl + t.prefix_units);
     x.n_units = p->n_prefix_units;
     x.merges = nullptr;
     x.n_merges = 0;
@@ -279,12 +292,12 @@ pa_status prepare_run(const pa_plan_t *p, pa::PlanMode want, const void *q, cons
     if (!std::isfinite(sm_scale))
         return fail(PA_ERR_INVALID_ARG, "sm_scale is not finite");
     const char *tbl = static_cast<const char *>(p->d_table);
-    const size_t off_b = offsets_bytes(p->n_workgroups);
+    const TableLayout t = table_layout(p);
     l->wg_offsets = reinterpret_cast<const int32_t *>(tbl);
     l->n_workgroups = p->n_workgroups;
-    l->units = reinterpret_cast<const pa_work_unit *>(tbl + off_b);
+    l->units = reinterpret_cast<const pa_work_unit *>(tbl + t.units);
     l->n_units = p->n_units;
-    l->merges = reinterpret_cast<const pa_merge_unit *>(tbl + off_b + (size_t)p->n_units * kUnit);
+    l->merges = reinterpret_cast<const pa_merge_unit *>(tbl + t.merges);
     l->n_merges = p->n_merges;
     l->arrivals = p->d_arrivals;
     l->q = q;
@@ -370,10 +383,10 @@ static pa_status plan_impl(pa_plan_t *p, const int32_t *kv_indptr_host, const in
     // partition straight into the staging buffer at capacity offsets, then
     // pack the three lists together and upload them with one copy
     char *stage = static_cast<char *>(p->h_stage[s]);
+    const TableLayout t = table_layout(p);
     int32_t *offsets = reinterpret_cast<int32_t *>(stage);
-    const size_t units_at = offsets_bytes(p->wg_cap);
-    pa_work_unit *units = reinterpret_cast<pa_work_unit *>(stage + units_at);
-    pa_merge_unit *merges = reinterpret_cast<pa_merge_unit *>(stage + units_at + (size_t)p->unit_cap * kUnit);
+    pa_work_unit *units = reinterpret_cast<pa_work_unit *>(stage + t.units);
+    pa_merge_unit *merges = reinterpret_cast<pa_merge_unit *>(stage + t.merges);
     // decode workgroups the GPU keeps resident for the pools' element type
     const bool kv_fp8 = (flags & PA_PLAN_KV_FP8) != 0;
     int32_t max_wg = kv_fp8 ? p->max_workgroups_fp8 : p->max_workgroups;
@@ -394,9 +407,7 @@ static pa_status plan_impl(pa_plan_t *p, const int32_t *kv_indptr_host, const in
     pa::PartitionResult r;
     const char *detail = "";
     auto clamp32 = [](int64_t v) { return (int32_t)std::min<int64_t>(v, 0x7fffffff); };
-    const size_t prefix_at = units_at + (size_t)p->unit_cap * kUnit + (size_t)p->merge_cap * kMerge;
-    pa_work_unit *prefix_units =
-        reinterpret_cast<pa_work_unit *>(stage + prefix_at + offsets_bytes(p->prefix_cap));
+    pa_work_unit *prefix_units = reinterpret_cast<pa_work_unit *>(stage + t.prefix_units);
     pa_status st = casc ? pa::cascade_partition(a, *casc, &p->scratch, offsets, clamp32(p->wg_cap + 1),
                                                 units, clamp32(p->unit_cap), merges,
                                                 clamp32(p->merge_cap), prefix_units,
@@ -409,26 +420,26 @@ static pa_status plan_impl(pa_plan_t *p, const int32_t *kv_indptr_host, const in
     const int64_t rows_per_slot = qo_indptr_host ? pa::prefill_tile_rows(p->head_dim) : p->group;
     if ((int64_t)r.n_partials * rows_per_slot > p->partial_rows_cap)
         return fail(PA_ERR_CAPACITY, "partial storage of the plan exceeded");
-    // pack: [offsets | units | merges | prefix offsets | prefix units]
-    const size_t off_b = offsets_bytes(r.n_workgroups);
-    if (r.n_units > 0)
-        std::memmove(stage + off_b, units, (size_t)r.n_units * kUnit);
-    if (r.n_merges > 0)
-        std::memmove(stage + off_b + (size_t)r.n_units * kUnit, merges, (size_t)r.n_merges * kMerge);
-    size_t bytes = off_b + (size_t)r.n_units * kUnit + (size_t)r.n_merges * kMerge;
+    // upload the used part of each region (the unused capacity of a region
+    // can be far larger than its used part, so each is copied on its own)
     if (r.n_prefix_units > 0) {
-        // one prefix unit per workgroup (packed after the merges, so the
-        // prefix offsets are written last: they may overlap the old units)
-        const size_t pre_off_b = offsets_bytes(r.n_prefix_units);
-        std::memmove(stage + bytes + pre_off_b, prefix_units, (size_t)r.n_prefix_units * kUnit);
-        int32_t *po = reinterpret_cast<int32_t *>(stage + bytes);
+        // one prefix unit per workgroup
+        int32_t *po = reinterpret_cast<int32_t *>(stage + t.prefix_offsets);
         for (int32_t w = 0; w <= r.n_prefix_units; w++)
             po[w] = w;
-        bytes += pre_off_b + (size_t)r.n_prefix_units * kUnit;
     }
-    if ((e = hipMemcpyAsync(p->d_table, stage, bytes, hipMemcpyHostToDevice,
-                            (hipStream_t)stream)) != hipSuccess)
-        return hip_fail(e, "plan upload");
+    const size_t pieces[4][2] = {
+        {0, offsets_bytes(r.n_workgroups)},
+        {t.merges, (size_t)r.n_merges * kMerge},
+        {t.units, (size_t)r.n_units * kUnit},
+        {t.prefix_offsets, r.n_prefix_units > 0 ? t.prefix_units - t.prefix_offsets + (size_t)r.n_prefix_units * kUnit
+                                                : 0},
+    };
+    char *dev_table = static_cast<char *>(p->d_table);
+    for (const auto &pc : pieces)
+        if (pc[1] > 0 && (e = hipMemcpyAsync(dev_table + pc[0], stage + pc[0], pc[1], hipMemcpyHostToDevice,
+                                             (hipStream_t)stream)) != hipSuccess)
+            return hip_fail(e, "plan upload");
     if ((e = hipEventRecord(p->stage_done[s], (hipStream_t)stream)) != hipSuccess)
         return hip_fail(e, "plan upload event");
     p->stage_pending[s] = true;

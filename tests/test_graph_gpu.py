@@ -68,6 +68,63 @@ def test_decode_layers_graph_replay(splits):
         _replay_and_check(step, outs + lses, eager)
 
 
+def test_decode_graph_replay_after_replan_with_other_cuts():
+    """A replay reads the device tables of the plan current at replay time.
+    The same lists re-planned with other budgets (XCD weights here; the speed
+    feedback does the same from step to step) keep the workgroup count but
+    cut the lists into other units and merges: the captured launches must
+    find them at the same table addresses, and the replay must equal an eager
+    run of the new plan bit for bit (regression: the merge table used to
+    follow the units, so its address moved with their count)."""
+    say("graph replay after a re-plan of the same lists with other cuts")
+    dev = device()
+    rng = np.random.Generator(np.random.PCG64(43))
+    B, Hq, Hkv, D, N = 24, 32, 8, 128, 65536
+    ip, idx = W.slot_lists(rng.integers(300, 4097, B), N, rng)
+    q = W.normal_bf16((B, Hq, D), 44, dev)
+    pools = [W.make_pools(N, Hkv, D, 45 + l, dev) for l in range(2)]
+    idx_dev = torch.as_tensor(idx, device=dev)
+    scale = W.softmax_scale(D)
+    outs = [torch.full((B, Hq, D), float("nan"), dtype=torch.float32, device=dev) for _ in range(2)]
+    w_a, w_b = [1.0] * 8, [3.0, 0.3, 1.0, 1.0, 0.5, 2.0, 1.0, 0.7]
+    for mw in (256, 512, 768):
+        a = pa.pa_partition(ip, None, Hq, Hkv, D, max_workgroups=mw, xcd_weights=w_a)
+        b = pa.pa_partition(ip, None, Hq, Hkv, D, max_workgroups=mw, xcd_weights=w_b)
+        say(f"  {mw} workgroups: units {a[0][-1]} -> {b[0][-1]}, merges {len(a[2])} -> {len(b[2])}")
+        assert len(a[0]) == len(b[0]) and (a[0][-1] != b[0][-1] or len(a[2]) != len(b[2]))
+    with pa.Plan(B, int(ip[-1]), Hq, Hkv, D) as plan:
+        pa.pa_plan_set_xcd_weights(plan.handle, w_a)
+        plan.plan(ip)
+
+        def step(stream):
+            for l in range(2):
+                plan.decode(q, pools[l][0], pools[l][1], idx_dev, scale, outs[l], stream=stream)
+
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            step(s)
+        torch.cuda.synchronize()
+        pa.pa_plan_set_xcd_weights(plan.handle, w_b)
+        plan.plan(ip)
+        step(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        eager = [o.cpu().numpy() for o in outs]
+        for l in range(2):
+            ref, _ = oracle_decode(q, pools[l][0], pools[l][1], ip, idx, scale, Hkv)
+            assert max_err(eager[l], ref) <= TOL
+        for rep in range(3):
+            for o in outs:
+                o.fill_(float("nan"))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            for o, e in zip(outs, eager):
+                assert np.array_equal(o.cpu().numpy(), e), f"replay {rep} differs"
+        del g
+
+
 def test_prefill_layers_graph_replay():
     say(f"graph capture: {LAYERS}-layer prefill step with split KV ranges")
     dev = device()
