@@ -8,7 +8,9 @@ layers per step with one pa_plan reused by all of them; every layer has its
 own pools, so caches cannot serve one layer's K/V to the next.  Inputs are
 seeded synthetic data (workloads.py), resident in HBM before timing starts.
 
-A step = pa_plan (host partition + one async upload) + 36 x pa_decode_run.
+A step = pa_plan (host partition + async upload of the tables) + the 36
+pa_decode_run calls, replayed from a HIP graph captured once (`--eager`:
+launched one by one).
 The JSON line reports:
   value            algorithmic HBM bytes of the step / step time (GB/s)
   us_per_step_layer  step time / 36
@@ -27,8 +29,10 @@ entries x 4 (slot ids) + B x Hq x D x 2 (q) + B x Hq x D x 4 (out) + (B+1) x 4.
 Other decode workloads (`--workload single_request | batch8 | hd256`): one
 request of 256 slots; 8 requests of 512..4096 slots (Qwen3-4B head shapes);
 32 requests of 1024..16384 slots at head_dim 256 -- each 36 layers per step
-with per-layer pools.  `--graph` replays each step's 36 layer runs from one
-captured HIP graph (pa_plan stays outside the graph).
+with per-layer pools.  Each step's 36 layer runs are replayed from one
+captured HIP graph (pa_plan stays outside the graph; the CUDA Graph decode
+of the Agent-Infer page, section "CUDA Graph 解码"); `--eager` launches them
+one by one instead.
 `--workload prefill_chunk512 | prefill_chunk64` measures the chunked-prefill
 kernel (MFMA roofline); `--workload copy --copy-gib N` runs a plain device
 copy of N GiB (for calibrating the HBM counters).
@@ -434,8 +438,10 @@ def main():
                              "prefill_chunk512", "prefill_chunk64", "append", "copy"])
     ap.add_argument("--kv", default="bf16", choices=["bf16", "fp8"],
                     help="decode: pool element type (fp8 = OCP E4M3 codes with per-pool scales)")
-    ap.add_argument("--graph", action="store_true",
-                    help="decode: replay each step's layer runs from a captured HIP graph")
+    ap.add_argument("--graph", action="store_true", default=True,
+                    help="decode: replay each step's layer runs from a captured HIP graph (the default)")
+    ap.add_argument("--eager", dest="graph", action="store_false",
+                    help="decode: launch each step's layer runs one by one")
     ap.add_argument("--cascade", action="store_true",
                     help="decode: plan with pa_plan_cascade over the workload's shared-prefix groups")
     ap.add_argument("--copy-gib", type=float, default=4.0)
