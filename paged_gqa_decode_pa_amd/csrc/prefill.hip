@@ -523,9 +523,13 @@ prefill_kernel(const int32_t *__restrict__ wg_offsets, const pa_work_unit *__res
             // compute unit's own L2 (the 8 XCDs do not share one); once they
             // have completed (s_waitcnt vmcnt(0) in every wave, then the
             // barrier) it counts itself in.  The part that arrives last reads
-            // the others with agent-scope coherent loads, issued after it has
-            // seen the count, and merges them with its own rows, still in
-            // registers; it then clears the counter for the next launch.
+            // every part back with agent-scope coherent loads, issued after it
+            // has seen the count, merges them, and clears the counter for the
+            // next launch.  As in the decode kernel's merge, the ordering
+            // rests on gfx950's coherence of sc1 accesses, not on the C++
+            // memory model alone: re-check it on another architecture or
+            // compiler (an acquire-release counter would order it formally,
+            // at the cost of whole-L2 write-back and invalidation).
             constexpr int32_t SLOT_BYTES = TILE_ROWS * D * 4;
             // The lane id passes through an empty asm statement, so that the
             // offsets derived from it are computed here and not hoisted to the
