@@ -29,8 +29,9 @@
 //     v_mfma_f32_32x32x16_f16; the row sum adds the same rounded weights, so
 //     the result is the exact weighted mean of V under them; the V^T operand
 //     is read straight from the row-major LDS tile with the transposing read
-//     ds_read_b64_tr_b16, and the P^T operand is regrouped from the score
-//     layout with two v_permlane32_swap per 16 entries;
+//     ds_read_b64_tr_b16, in the order of list entries in which each lane
+//     already holds its row's weights, so the weights are the P^T operand
+//     as they stand (no exchange between lanes);
 //   * O^T accumulates in the MFMA's fp32 registers: a lane holds D/2 values
 //     of its own row, so rescaling is a per-lane multiply.
 // A unit whose V holds a finite value that fp16 cannot represent runs again
@@ -130,17 +131,6 @@ __device__ __forceinline__ uint32_t bf16_pair_to_f16_scaled(uint32_t u, int shif
 // Smallest magnitude that fp16 rounds to infinity.
 constexpr float kF16Overflow = 65520.0f;
 
-// B operand (P^T, 16 entries x 32 rows) of one k-step from the score layout.
-// x0, x1: this lane's weights of entries 4h..4h+3 of the k-step (h = lane/32)
-// packed in pairs; y0, y1: entries 8+4h..8+4h+3.  Lane l < 32 needs entries
-// 0..7 (its own x and the x of lane l+32), lane l >= 32 entries 8..15 (the y
-// of lane l-32 and its own y): one half-wave swap per dword does both.
-__device__ __forceinline__ uint4 regroup(uint32_t x0, uint32_t x1, uint32_t y0, uint32_t y1) {
-    const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
-    const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
-    return uint4{s0[0], s1[0], s0[1], s1[1]};
-}
-
 // s_waitcnt vmcnt(0): every vector-memory access of this wave has completed.
 __device__ __forceinline__ void wait_vector_memory() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
@@ -209,8 +199,14 @@ prefill_kernel(const int32_t *__restrict__ wg_offsets, const pa_work_unit *__res
     const int srow = tid / TPR, chunk = tid % TPR;
     // LDS byte offsets of this lane's MFMA operands within a stage
     const int k_lane = col * KROW + half * 16;
+    // V^T operand of a k-step over 16 list entries: the matrix core pairs
+    // the 8 k-values of lane half h of its A operand with the 8 of its B
+    // operand, in order.  A lane of half h holds its row's weights of entries
+    // 4h..4h+3 and 8+4h..8+4h+3 of the k-step (the score layout), so the two
+    // transposing reads take V rows 4h+e4 and 8+4h+e4 (e4 = 0..3, the row
+    // within a read's 4-row group), and the weights are the B operand as they are.
     const int gi = lane >> 4, e4 = (lane & 15) >> 2, q4 = lane & 3;
-    const int v_lane = KT * KROW + (8 * (gi >> 1) + e4) * VROW + (16 * (gi & 1) + 4 * q4) * 2;
+    const int v_lane = KT * KROW + (4 * (gi >> 1) + e4) * VROW + (16 * (gi & 1) + 4 * q4) * 2;
     // Scores are scaled after taking their maximum, which needs a positive
     // scale: a negative scale is applied as |scale| to -q (bf16 negation is
     // exact), a zero scale as 1 to q = 0 (every score 0, as it should be).
@@ -369,16 +365,41 @@ prefill_kernel(const int32_t *__restrict__ wg_offsets, const pa_work_unit *__res
                             if (b * 32 + 8 * (i / 4) + (i % 4) > lim)
                                 s[b][i] = -INFINITY;
                 }
-                float tmax = -INFINITY;
+                // Weights relative to the running maximum as it stands, rounded
+                // once to fp16; the row sum adds the rounded weights, so the
+                // result is the exact weighted mean of V under them.  The tile's
+                // own maximum is only needed when a weight does not fit fp16
+                // (a score 16 or more above the running maximum in log2 units,
+                // and always on a unit's first tile): the sum then comes out
+                // infinite (or NaN), and the tile is weighed again after the
+                // maximum has moved, as in the online softmax, to any score that
+                // exceeds it by more than the slack.  Weights stay below 65520.
+                const f16x2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
+                uint32_t ph[SB][8];
+                auto weigh = [&](float lsum) {
 #pragma unroll
-                for (int b = 0; b < SB; b++)
+                    for (int b = 0; b < SB; b++)
 #pragma unroll
-                    for (int i = 0; i < 16; i++)
-                        tmax = fmaxf(tmax, s[b][i]);
-                tmax *= c_exp;
-                tmax = fmaxf(tmax, other_half(tmax));
-                const bool move = tmax > m + kRescaleSlack;
-                if (__builtin_amdgcn_ballot_w64(move)) {
+                        for (int i = 0; i < 16; i += 2) {
+                            const float p0 = fast_exp2(fmaf(s[b][i], c_exp, -m));
+                            const float p1 = fast_exp2(fmaf(s[b][i + 1], c_exp, -m));
+                            ph[b][i / 2] = pack_f16(p0, p1);
+                            lsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, ph[b][i / 2]), ones, lsum,
+                                                          false);
+                        }
+                    return lsum;
+                };
+                float l_new = weigh(l);
+                if (__builtin_amdgcn_ballot_w64(!(l_new <= 3.4028235e38f))) {
+                    float tmax = -INFINITY;
+#pragma unroll
+                    for (int b = 0; b < SB; b++)
+#pragma unroll
+                        for (int i = 0; i < 16; i++)
+                            tmax = fmaxf(tmax, s[b][i]);
+                    tmax *= c_exp;
+                    tmax = fmaxf(tmax, other_half(tmax));
+                    const bool move = tmax > m + kRescaleSlack;
                     const float m_new = move ? tmax : m;
                     const float alpha = fast_exp2(m - m_new);
                     l *= alpha;
@@ -388,33 +409,21 @@ prefill_kernel(const int32_t *__restrict__ wg_offsets, const pa_work_unit *__res
                         for (int i = 0; i < 16; i++)
                             o[b][i] *= alpha;
                     m = m_new;
+                    l_new = weigh(l);
                 }
-                // weights (<= 2^8) rounded once to fp16; the row sum adds the
-                // rounded weights, so the result is the exact weighted mean of V
-                // under them
-                const f16x2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
-                uint32_t ph[SB][8];
-#pragma unroll
-                for (int b = 0; b < SB; b++)
-#pragma unroll
-                    for (int i = 0; i < 16; i += 2) {
-                        const float p0 = fast_exp2(fmaf(s[b][i], c_exp, -m));
-                        const float p1 = fast_exp2(fmaf(s[b][i + 1], c_exp, -m));
-                        ph[b][i / 2] = pack_f16(p0, p1);
-                        l = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, ph[b][i / 2]), ones, l, false);
-                    }
+                l = l_new;
                 // O^T += V^T P^T, 16 entries per k-step
 #pragma unroll
                 for (int k = 0; k < KS; k++) {
                     const int b = k / 2, w0 = 4 * (k % 2);  // dword index of entries 16*(k%2) + 4*half
                     const f16x8_t bh = __builtin_bit_cast(
-                        f16x8_t, regroup(ph[b][w0], ph[b][w0 + 1], ph[b][w0 + 2], ph[b][w0 + 3]));
+                        f16x8_t, uint4{ph[b][w0], ph[b][w0 + 1], ph[b][w0 + 2], ph[b][w0 + 3]});
 #pragma unroll
                     for (int db = 0; db < DB; db++) {
                         const int off = v_lane + k * 16 * VROW + db * 64;
                         const i16x4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(st + off));
                         const i16x4_t hi4 =
-                            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(st + off + 4 * VROW));
+                            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(st + off + 8 * VROW));
                         const f16x8_t a = __builtin_bit_cast(
                             f16x8_t, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
                         o[db] = mfma_f16(a, bh, o[db]);

@@ -65,6 +65,32 @@ def test_prefill_forced_splits(n):
     assert max_err(out, base.astype(np.float64)) <= TOL
 
 
+@pytest.mark.parametrize("D,Hq,Hkv,splits", [(128, 32, 8, 0), (128, 32, 8, 5), (256, 16, 4, 0)])
+def test_prefill_scores_rising_along_the_list(D, Hq, Hkv, splits):
+    """K rows scaled by 1, 4, 16, 64 in bands of 97 list entries (exact in
+    bf16): the scores jump by far more than 16 log2 units inside tiles and
+    between them, so the running maximum must move mid-range (the path that
+    weighs a tile again after an fp16 overflow of its weights)."""
+    say(f"prefill rising scores D={D} Hq={Hq} Hkv={Hkv} splits={splits}")
+    reqs = [(700, 129), (1500, 64), (300, 300)]
+    qo, ip, idx, q, k, v = _case(reqs, Hq, Hkv, D, 8192, seed=43 + D)
+    fac = np.ones(k.shape[0], np.float32)
+    for r in range(len(reqs)):
+        band = np.minimum(np.arange(ip[r + 1] - ip[r]) // 97, 3)
+        fac[idx[ip[r]:ip[r + 1]]] = 4.0 ** band
+    f = torch.as_tensor(fac, device=k.device)[:, None, None]
+    k2 = (k.float() * f).to(torch.bfloat16)
+    assert torch.equal(k2.float(), k.float() * f)   # the scaling is exact
+    idx_dev = torch.as_tensor(idx, device=device())
+    scale = W.softmax_scale(D)
+    flags = pa.PA_PLAN_FORCE_SPLITS(splits) if splits else 0
+    out, lse = run_prefill(q, k2, v, qo, ip, idx_dev, scale, Hkv, flags=flags)
+    ref, ref_lse = oracle_prefill(q, k2, v, qo, ip, idx, scale, Hkv)
+    e_out, e_lse = max_err(out, ref), max_err(lse, ref_lse)
+    say(f"  max|d| out={e_out:.3g} lse={e_lse:.3g} (oracle lse up to {np.abs(ref_lse[np.isfinite(ref_lse)]).max():.1f})")
+    assert e_out <= TOL and e_lse <= TOL
+
+
 def test_prefill_xcd_order_neutral_and_deterministic():
     say("prefill xcd order / determinism")
     reqs = [(500, 200), (1200, 64)]
