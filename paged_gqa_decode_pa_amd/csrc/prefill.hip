@@ -525,10 +525,15 @@ prefill_kernel(const int32_t *__restrict__ wg_offsets, const pa_work_unit *__res
             }
 
             // One of the parts of a cut KV range.  It publishes its normalised
-            // rows and their log2-sum-exp in its partial slot, in register
-            // order (wave w's block of 32 rows, then 8-byte piece k of every
-            // lane in turn: each store and load below is one contiguous 512-byte
-            // run), with agent-scope coherent stores, which write through the
+            // rows in fp16 and their log2-sum-exp in its partial slot, the rows
+            // in register order (wave w's block of 32 rows, then 8-byte piece k
+            // of every lane in turn, four values a piece: each store and load
+            // below is one contiguous 512-byte run).  The rows are stored as
+            // O * 2^-vshift (below 2^15 when vshift > 0, below 65520 otherwise:
+            // fp16 holds them), and vshift after them; fp16 rounds them to
+            // 2^-12 of their size, 8 times finer than the bf16 inputs, and
+            // halves the bytes written here and read back by the merge.  The
+            // stores are agent-scope coherent stores, which write through the
             // compute unit's own L2 (the 8 XCDs do not share one); once they
             // have completed (s_waitcnt vmcnt(0) in every wave, then the
             // barrier) it counts itself in.  The part that arrives last reads
@@ -547,17 +552,23 @@ prefill_kernel(const int32_t *__restrict__ wg_offsets, const pa_work_unit *__res
             uint32_t lid = lane;
             asm volatile("" : "+v"(lid));
             // this lane's byte offset within a slot: its wave's block, its 8 bytes of a piece
-            const uint32_t lane_off = (uint32_t)(wave * (32 * D * 4)) + lid * 8;
+            const uint32_t lane_off = (uint32_t)(wave * (32 * D * 2)) + lid * 8;
+            constexpr int32_t SHIFT_FLOAT = TILE_ROWS * D / 2;   // vshift, after the fp16 rows
             {
-                const __amdgpu_buffer_rsrc_t slot = slot_rsrc(part_o + (int64_t)unit.partial * (TILE_ROWS * D), SLOT_BYTES);
+                float *const base = part_o + (int64_t)unit.partial * (TILE_ROWS * D);
+                const __amdgpu_buffer_rsrc_t slot = slot_rsrc(base, SLOT_BYTES);
                 if (half == 0)
                     store_coherent(part_lse + (int64_t)unit.partial * TILE_ROWS + row, lse2);
+                if (tid == 0)
+                    store_coherent(base + SHIFT_FLOAT, __int_as_float(vshift));
+                const float f = __builtin_amdgcn_ldexpf(inv, -vshift);
 #pragma unroll
                 for (int db = 0; db < DB; db++)
 #pragma unroll
-                    for (int k = 0; k < 8; k++)
-                        store_coherent2(slot, lane_off + (db * 8 + k) * 512, 0, o[db][2 * k] * inv,
-                                        o[db][2 * k + 1] * inv);
+                    for (int k = 0; k < 4; k++)
+                        store_coherent2(slot, lane_off + (db * 4 + k) * 512, 0,
+                                        __uint_as_float(pack_f16(o[db][4 * k] * f, o[db][4 * k + 1] * f)),
+                                        __uint_as_float(pack_f16(o[db][4 * k + 2] * f, o[db][4 * k + 3] * f)));
             }
             wait_vector_memory();
             __syncthreads();
@@ -577,22 +588,33 @@ prefill_kernel(const int32_t *__restrict__ wg_offsets, const pa_work_unit *__res
             for (int db = 0; db < DB; db++)
                 o[db] = f32x16_t{};
             for (int32_t pi = first; pi < first + n_parts; pi++) {
+                float *const base = part_o + (int64_t)pi * (TILE_ROWS * D);
                 const float lp = load_coherent(part_lse + (int64_t)pi * TILE_ROWS + row);
-                const __amdgpu_buffer_rsrc_t src = slot_rsrc(part_o + (int64_t)pi * (TILE_ROWS * D), SLOT_BYTES);
+                const int shift = __float_as_int(load_coherent(base + SHIFT_FLOAT));
+                const __amdgpu_buffer_rsrc_t src = slot_rsrc(base, SLOT_BYTES);
                 const float mx = fmaxf(M, lp);
                 const bool live = mx != -INFINITY;      // some part so far is not empty
                 const float a = live ? fast_exp2(M - mx) : 1.f;   // 0 while M is -inf
                 const float w = live ? fast_exp2(lp - mx) : 0.f;
-                // one column block (16 values of the row) per round trip
+                const float wv = __builtin_amdgcn_ldexpf(w, shift);   // weight of the stored rows
+                // two column blocks (32 values of the row) per round trip
 #pragma unroll
-                for (int db = 0; db < DB; db++) {
+                for (int dp = 0; dp < DB; dp += 2) {
                     f32x2_t v[8];
 #pragma unroll
                     for (int k = 0; k < 8; k++)
-                        v[k] = load_coherent2(src, lane_off + (db * 8 + k) * 512, 0);
+                        v[k] = load_coherent2(src, lane_off + (dp * 4 + k) * 512, 0);
 #pragma unroll
-                    for (int i = 0; i < 16; i++)
-                        o[db][i] = fmaf(w, v[i / 2][i % 2], o[db][i] * a);
+                    for (int j = 0; j < 2; j++)
+#pragma unroll
+                        for (int i = 0; i < 16; i++) {
+                            // the element is copied out before the bit cast: the
+                            // ROCm 7.2 compiler reads element 0 for a bit cast of a
+                            // vector element written in place
+                            const float x = v[4 * j + i / 4][(i / 2) % 2];
+                            const f16x2_t h = __builtin_bit_cast(f16x2_t, x);
+                            o[dp + j][i] = fmaf(wv, (float)h[i % 2], o[dp + j][i] * a);
+                        }
                 }
                 wsum = fmaf(wsum, a, w);
                 M = live ? mx : M;

@@ -168,24 +168,50 @@ def test_prefill_workload_full_rows(spec):
     assert e_out <= TOL and e_lse <= TOL
 
 
-@pytest.mark.parametrize("log2_scale", [16, 100])
-def test_prefill_values_beyond_fp16_range(log2_scale):
+@pytest.mark.parametrize("log2_scale,splits", [(16, 0), (100, 0), (16, 5), (100, 7)])
+def test_prefill_values_beyond_fp16_range(log2_scale, splits):
     """The weighted sum runs on fp16 matrix cores; a unit whose V values
     overflow fp16 is run again with V scaled by a power of two.  V = 2^s x
     N(0, 1) (exact in bf16) must give 2^s x the result for N(0, 1), and the
-    oracle within 2e-3 x 2^s."""
-    say(f"prefill with V scaled by 2^{log2_scale}")
+    oracle within 2e-3 x 2^s; with KV ranges cut into parts, whose fp16
+    partial rows carry that power of two beside them."""
+    say(f"prefill with V scaled by 2^{log2_scale}, splits={splits}")
     reqs = [(300, 64), (700, 129), (40, 33)]
     qo, ip, idx, q, k, v = _case(reqs, 32, 8, 128, 8192, seed=41)
     idx_dev = torch.as_tensor(idx, device=device())
     scale = W.softmax_scale(128)
-    base, base_lse = run_prefill(q, k, v, qo, ip, idx_dev, scale, 8)
+    flags = pa.PA_PLAN_FORCE_SPLITS(splits) if splits else 0
+    base, base_lse = run_prefill(q, k, v, qo, ip, idx_dev, scale, 8, flags=flags)
     f = 2.0 ** log2_scale
     big = (v.float() * f).to(torch.bfloat16)
     assert torch.equal(big.float(), v.float() * f)   # the scaling is exact
-    out, lse = run_prefill(q, k, big, qo, ip, idx_dev, scale, 8)
+    out, lse = run_prefill(q, k, big, qo, ip, idx_dev, scale, 8, flags=flags)
     ref, ref_lse = oracle_prefill(q, k, big, qo, ip, idx, scale, 8)
     e = max_err(out / f, ref / f), max_err(lse, ref_lse)
     say(f"  max|d|/2^s vs oracle {e[0]:.3g}, lse {e[1]:.3g}; vs unscaled {max_err(out / f, base):.3g}")
     assert e[0] <= TOL and e[1] <= TOL
     assert max_err(out / f, base) <= TOL and max_err(lse, base_lse) <= 1e-6
+
+
+@pytest.mark.parametrize("splits", [0, 5])
+def test_prefill_values_beyond_fp16_range_in_part_of_the_list(splits):
+    """Only the V rows of the first 150 list entries of each request scaled by
+    2^16: the parts of a cut range then run with different powers of two, each
+    stored beside its partial rows and undone in the merge."""
+    say(f"prefill with V scaled by 2^16 on the first 150 entries, splits={splits}")
+    reqs = [(300, 64), (700, 129), (40, 33)]
+    qo, ip, idx, q, k, v = _case(reqs, 32, 8, 128, 8192, seed=42)
+    fac = np.ones(v.shape[0], np.float32)
+    for r in range(len(reqs)):
+        fac[idx[ip[r]:ip[r] + 150]] = 65536.0
+    f = torch.as_tensor(fac, device=v.device)[:, None, None]
+    big = (v.float() * f).to(torch.bfloat16)
+    assert torch.equal(big.float(), v.float() * f)   # the scaling is exact
+    idx_dev = torch.as_tensor(idx, device=device())
+    scale = W.softmax_scale(128)
+    flags = pa.PA_PLAN_FORCE_SPLITS(splits) if splits else 0
+    out, lse = run_prefill(q, k, big, qo, ip, idx_dev, scale, 8, flags=flags)
+    ref, ref_lse = oracle_prefill(q, k, big, qo, ip, idx, scale, 8)
+    e = max_err(out / 65536.0, ref / 65536.0), max_err(lse, ref_lse)
+    say(f"  max|d|/2^16 vs oracle {e[0]:.3g}, lse {e[1]:.3g}")
+    assert e[0] <= TOL and e[1] <= TOL
