@@ -50,6 +50,8 @@ CASES = [
     ([50, 900, 3], 64, 8, 128),
     ([17, 1500], 16, 4, 256),
     ([400, 5], 8, 8, 256),
+    ([5, 800, 77], 12, 3, 128),     # odd KV-head count
+    ([300, 40, 1], 8, 2, 128),
 ]
 
 
