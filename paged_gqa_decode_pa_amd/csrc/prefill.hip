@@ -236,12 +236,27 @@ prefill_kernel(const int32_t *__restrict__ wg_offsets, const pa_work_unit *__res
                 qf[s] = __builtin_bit_cast(bf16x8_t, v);
             }
         }
+        const int32_t kv0 = unit.kv_begin, kv1 = unit.kv_end;
+        const int32_t n_tiles = (kv1 - kv0 + KT - 1) / KT;
+        // Entries at or past kv1 (the tail of the last tile) are clamped to the
+        // range's last entry, so every row read is one the unit references and
+        // the loads need no branch; the causal mask gives those entries weight
+        // 0 (their row limit is at most kv1 - 1).
+        const int32_t *const unit_ids = kv_indices + kv0;   // the unit's entries, uniform base
+        int32_t slot[PASSES];
+        auto load_slots = [&](int32_t tile) {
+#pragma unroll
+            for (int p = 0; p < PASSES; p++)
+                slot[p] = unit_ids[(uint32_t)min(tile * KT + p * RPP + srow, kv1 - kv0 - 1)];
+        };
+        // the first tile's slot ids travel with the query loads: one memory
+        // round trip fewer before the first tile
+        if (n_tiles > 0)
+            load_slots(0);
         // the query operand stays in registers for the whole unit; waiting for
         // it here keeps the tile loop from waiting on every load in flight
         wait_vector_memory();
 
-        const int32_t kv0 = unit.kv_begin, kv1 = unit.kv_end;
-        const int32_t n_tiles = (kv1 - kv0 + KT - 1) / KT;
         const uint64_t head_off = (uint64_t)unit.kv_head * D * 2 + chunk * 16;
         // row limit: the last list entry (absolute offset) this row may see
         const int32_t row_last = min(kv1 - 1, unit.diag + tt);
@@ -261,18 +276,7 @@ prefill_kernel(const int32_t *__restrict__ wg_offsets, const pa_work_unit *__res
         auto run_unit = [&](const int vshift, int *retry) -> bool {
             __syncthreads();  // the previous unit's (or pass's) last tile is no longer read
 
-            // Entries at or past kv1 (the tail of the last tile) are clamped
-            // to the range's last entry, so every row read is one the unit
-            // references and the loads need no branch; the causal mask gives
-            // those entries weight 0 (their row limit is at most kv1 - 1).
-            const int32_t *const unit_ids = kv_indices + kv0;   // the unit's entries, uniform base
-            int32_t slot[PASSES];
             u32x4_t kreg[PASSES], vreg[PASSES];
-            auto load_slots = [&](int32_t tile) {
-#pragma unroll
-                for (int p = 0; p < PASSES; p++)
-                    slot[p] = unit_ids[(uint32_t)min(tile * KT + p * RPP + srow, kv1 - kv0 - 1)];
-            };
             auto load_rows = [&]() {
 #pragma unroll
                 for (int p = 0; p < PASSES; p++) {
@@ -323,7 +327,8 @@ prefill_kernel(const int32_t *__restrict__ wg_offsets, const pa_work_unit *__res
                 o[b] = f32x16_t{};
 
             if (n_tiles > 0) {
-                load_slots(0);
+                if (vshift != 0)
+                    load_slots(0);   // a second pass: the first one moved on
                 load_rows();
                 if (n_tiles > 1)
                     load_slots(1);
