@@ -52,6 +52,8 @@ CASES = [
     ([400, 5], 8, 8, 256),
     ([5, 800, 77], 12, 3, 128),     # odd KV-head count
     ([300, 40, 1], 8, 2, 128),
+    ([90, 700], 16, 8, 256),        # group 2
+    ([40, 333, 6], 32, 4, 256),     # group 8: 8 codes a lane, 32 lanes a row
 ]
 
 
@@ -161,19 +163,20 @@ def test_fp8_poisoned_pool():
     assert np.array_equal(clean, dirty)
 
 
-def test_fp8_large_pool_offsets():
+@pytest.mark.parametrize("Hq,Hkv,D", [(32, 8, 128), (16, 4, 256)], ids=["D128", "D256"])
+def test_fp8_large_pool_offsets(Hq, Hkv, D):
     """Rows past 2^31 bytes of an 8-bit pool (64-bit row offsets)."""
-    say("fp8 large pool: 2,300,000 slots x 8 heads x 128")
+    say(f"fp8 large pool: 2,300,000 slots x {Hkv} heads x {D}")
     dev = device()
     N = 2_300_000
     rng = np.random.Generator(np.random.PCG64(101))
     ip, idx = W.slot_lists(np.asarray([700, 260]), N, rng)
     idx[:64] = N - 1 - np.arange(64)
-    q = W.normal_bf16((2, 32, 128), 102, dev)
-    k, v = W.make_pools_e4m3(N, 8, 128, 103, dev)
-    scale = W.softmax_scale(128)
-    out, lse = run_fp8(q, k, v, ip, torch.as_tensor(idx, device=dev), scale, 8)
-    ref, ref_lse = _oracle(q, k, v, ip, idx, scale, 8)
+    q = W.normal_bf16((2, Hq, D), 102, dev)
+    k, v = W.make_pools_e4m3(N, Hkv, D, 103, dev)
+    scale = W.softmax_scale(D)
+    out, lse = run_fp8(q, k, v, ip, torch.as_tensor(idx, device=dev), scale, Hkv)
+    ref, ref_lse = _oracle(q, k, v, ip, idx, scale, Hkv)
     assert max_err(out, ref) <= TOL and max_err(lse, ref_lse) <= TOL
     del k, v
     torch.cuda.empty_cache()

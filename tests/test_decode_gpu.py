@@ -173,9 +173,9 @@ def _slot_tag_pool(num_slots, Hkv, D, dev):
 
 @pytest.mark.parametrize("num_slots,Hq,Hkv,D", [(70000, 32, 8, 128), ((1 << 24) + 1000, 8, 1, 128),
                                                 (2_300_000, 16, 8, 128), (1_048_575, 32, 8, 128),
-                                                (1_600_000, 32, 8, 128)],
+                                                (1_600_000, 32, 8, 128), (1_100_000, 16, 4, 256)],
                          ids=["small_pool", "over_2^24_slots", "over_4GiB", "just_below_2GiB",
-                              "between_2_and_4GiB"])
+                              "between_2_and_4GiB", "head_dim_256_past_2GiB"])
 def test_slot_tags_bit_exact(num_slots, Hq, Hkv, D):
     """Each single-slot request returns its slot id exactly, including the last
     slot of pools on both sides of 2 GiB (where row offsets stop fitting a

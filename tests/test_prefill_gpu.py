@@ -46,6 +46,7 @@ SMALL = [
     ([(50, 50), (400, 100)], 16, 4, 256),
     ([(120, 7), (260, 200)], 8, 8, 256),
     ([(77, 77), (31, 3)], 32, 4, 256),
+    ([(60, 20), (300, 150)], 16, 8, 256),           # group 2
 ]
 
 
@@ -130,9 +131,10 @@ def test_prefill_poisoned_pool():
     assert np.array_equal(clean, dirty)
 
 
-def test_prefill_large_pool_offsets():
+@pytest.mark.parametrize("Hq,Hkv,D", [(32, 8, 128), (16, 4, 256)], ids=["D128", "D256"])
+def test_prefill_large_pool_offsets(Hq, Hkv, D):
     """Slots beyond 2^31 bytes of pool address (64-bit row offsets)."""
-    say("prefill large pool: 2,300,000 slots x 8 heads x 128")
+    say(f"prefill large pool: 2,300,000 slots x {Hkv} heads x {D}")
     num_slots = 2_300_000
     dev = device()
     rng = np.random.Generator(np.random.PCG64(21))
@@ -140,11 +142,11 @@ def test_prefill_large_pool_offsets():
     ip, idx = W.slot_lists(lengths, num_slots, rng)
     idx[:64] = num_slots - 1 - np.arange(64)   # touch the very end of the pool
     qo = np.asarray([0, 200, 330], np.int32)
-    q = W.normal_bf16((330, 32, 128), 22, dev)
-    k, v = W.make_pools(num_slots, 8, 128, 23, dev)
-    scale = W.softmax_scale(128)
-    out, lse = run_prefill(q, k, v, qo, ip, torch.as_tensor(idx, device=dev), scale, 8)
-    ref, ref_lse = oracle_prefill(q, k, v, qo, ip, idx, scale, 8)
+    q = W.normal_bf16((330, Hq, D), 22, dev)
+    k, v = W.make_pools(num_slots, Hkv, D, 23, dev)
+    scale = W.softmax_scale(D)
+    out, lse = run_prefill(q, k, v, qo, ip, torch.as_tensor(idx, device=dev), scale, Hkv)
+    ref, ref_lse = oracle_prefill(q, k, v, qo, ip, idx, scale, Hkv)
     assert max_err(out, ref) <= TOL and max_err(lse, ref_lse) <= TOL
     del k, v
     torch.cuda.empty_cache()
