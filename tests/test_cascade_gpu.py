@@ -69,6 +69,9 @@ CASES = [
     ([800, 950, 1000, 1200, 333, 444], 3, 300, 64, 8, 128),     # 8 query heads per KV head
     ([700, 1900, 1000, 1200], 2, 650, 16, 4, 256),        # head_dim 256
     ([400, 800, 1600, 3200], 1, 0, 32, 8, 128),           # no sharing: plain decode
+    ([500, 600, 700, 800, 900], 5, 400, 8, 8, 128),       # 1 query head per KV head
+    ([900, 1000, 1100, 1300], 4, 500, 16, 8, 128),        # 2 query heads per KV head
+    ([600, 700, 800], 3, 333, 32, 4, 256),                # head_dim 256, 8 query heads per KV head
 ]
 
 
