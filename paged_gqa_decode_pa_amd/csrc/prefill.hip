@@ -15,10 +15,11 @@
 // over 4 waves at 256; wave w owns rows 32w .. 32w+31), and a contiguous
 // range of the list.  Per tile of KT list entries:
 //   * all threads gather the KT K rows and V rows of the KV head (16-byte
-//     loads, one slot id per row) into registers one tile ahead, and write
-//     them into a double-buffered LDS stage (row-major, rows padded so that
-//     the reads below hit distinct banks); K stays bf16, V is converted to
-//     fp16 (exact for bf16 magnitudes in [2^-14, 65520));
+//     loads, one slot id per row) into registers two tiles ahead, and write
+//     them into one of four LDS stages (row-major, rows padded so that the
+//     reads below hit distinct banks; one barrier per two tiles); K stays
+//     bf16, V is converted to fp16 (exact for bf16 magnitudes in [2^-14,
+//     65520));
 //   * each wave computes its 32 x KT score block transposed, S^T = K Q^T,
 //     with v_mfma_f32_32x32x16_bf16 (K rows from LDS as the A operand, the
 //     wave's 32 query rows held in registers as the B operand for the whole
@@ -186,7 +187,7 @@ prefill_kernel(const int32_t *__restrict__ wg_offsets, const pa_work_unit *__res
     constexpr int DS = Geo::DS, DB = Geo::DB, SB = Geo::SB, KS = Geo::KS;
     constexpr int WAVES = prefill_waves<D>(), TILE_ROWS = prefill_tile_rows(D);
 
-    __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+    __shared__ __attribute__((aligned(16))) char smem[4 * STAGE];
     __shared__ float flag_lds[WAVES];
     __shared__ int32_t arrived_lds;
 
@@ -326,6 +327,11 @@ prefill_kernel(const int32_t *__restrict__ wg_offsets, const pa_work_unit *__res
             for (int b = 0; b < DB; b++)
                 o[b] = f32x16_t{};
 
+            // Four LDS stages, tile t in stage t % 4.  Rows are gathered two
+            // tiles ahead and stored at the end of the tile before, so the
+            // barrier before tile t (t even) covers the stores of tiles t and
+            // t+1, and no stage is rewritten while a wave may still read it:
+            // one barrier per two tiles.
             if (n_tiles > 0) {
                 if (vshift != 0)
                     load_slots(0);   // a second pass: the first one moved on
@@ -333,18 +339,25 @@ prefill_kernel(const int32_t *__restrict__ wg_offsets, const pa_work_unit *__res
                 if (n_tiles > 1)
                     load_slots(1);
                 store_rows(0);
+                if (n_tiles > 1) {
+                    load_rows();
+                    if (n_tiles > 2)
+                        load_slots(2);
+                    store_rows(1);
+                }
             }
 
             // one tile: entries kv0 + it*KT ...; MASK: some entry lies beyond a row's limit
             auto step = [&](int32_t it, auto mask_tag) {
                 constexpr bool MASK = decltype(mask_tag)::value;
-                const int buf = it & 1;
-                if (it + 1 < n_tiles) {
-                    load_rows();  // tile it+1, slots fetched one iteration earlier
-                    if (it + 2 < n_tiles)
-                        load_slots(it + 2);
+                const int buf = it & 3;
+                if (it + 2 < n_tiles) {
+                    load_rows();  // tile it+2, slots fetched one iteration earlier
+                    if (it + 3 < n_tiles)
+                        load_slots(it + 3);
                 }
-                __syncthreads();  // stage `buf` written by every thread
+                if ((it & 1) == 0)
+                    __syncthreads();  // stages of tiles it, it+1 written by every thread
 
                 const char *st = smem + buf * STAGE;
                 // S^T = K Q^T, one 32x32 block per 32 entries; entry of s[b][i]:
@@ -434,8 +447,8 @@ prefill_kernel(const int32_t *__restrict__ wg_offsets, const pa_work_unit *__res
                         o[db] = mfma_f16(a, bh, o[db]);
                     }
                 }
-                if (it + 1 < n_tiles)
-                    store_rows(buf ^ 1);
+                if (it + 2 < n_tiles)
+                    store_rows((it + 2) & 3);
             };
             for (int32_t it = 0; it < n_open; it++)
                 step(it, std::false_type{});
