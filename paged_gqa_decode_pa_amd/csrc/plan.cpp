@@ -104,14 +104,6 @@ Groups xcd_order_single(const std::vector<Unit> &units, int num_xcd) {
         for (int32_t m : clusters[c].members)
             queue[x].push_back(m);
     }
-    // Longest units first on each XCD: when there are more workgroups than
-    // run at once, the compute units that finish first take the next ones
-    // in id order, so the short units should come last (a causal chunk's
-    // tiles differ in length by up to a tile per 64 chunk tokens; in request
-    // order the units that finished first drew short ones again).
-    for (auto &q : queue)
-        std::stable_sort(q.begin(), q.end(),
-                         [&](int32_t a, int32_t b) { return units[a].tokens > units[b].tokens; });
     size_t depth = 0;
     for (auto &q : queue)
         depth = std::max(depth, q.size());
