@@ -459,7 +459,9 @@ pa_status pa_plan_workgroup_weights(const pa_plan_t *plan, float *weights, int32
  * pair around their attention kernel, on the run's stream, until the pairs are
  * used up.  pa_profile_end waits for the recorded events, returns the summed
  * kernel time in milliseconds and the number of timed launches, and stops
- * recording.  Merge kernels are not included.  Not for concurrent use.
+ * recording.  A pair spans every kernel of its run (with a cascade plan, the
+ * prefix units and the decode kernel; splits are merged inside the kernels).
+ * Not for concurrent use.
  */
 pa_status pa_profile_begin(pa_plan_t *plan, int32_t capacity);
 pa_status pa_profile_end(pa_plan_t *plan, double *total_ms, int32_t *n_launches);
