@@ -1,5 +1,5 @@
 """fp64 CPU oracle for paged grouped-query decode attention (and the rotary
-position embedding of the rows appended to the pool).
+position embedding and 8-bit encoding of the rows appended to the pool).
 
 TEST INFRASTRUCTURE ONLY: the test-suite, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` are the only code that may import this
@@ -89,6 +89,8 @@ class Oracle:
         lib.pa_oracle_e4m3_to_bf16.argtypes = [ctypes.c_int64, _u8p, _u16p]
         lib.pa_oracle_e4m3_values.restype = ctypes.c_int
         lib.pa_oracle_e4m3_values.argtypes = [ctypes.c_int64, _u8p, _f64p]
+        lib.pa_oracle_e4m3_encode.restype = ctypes.c_int
+        lib.pa_oracle_e4m3_encode.argtypes = [ctypes.c_int64, _f64p, ctypes.c_float, _u8p]
         lib.pa_oracle_decode_e4m3.restype = ctypes.c_int
         lib.pa_oracle_decode_e4m3.argtypes = [
             ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -217,6 +219,33 @@ class Oracle:
         self._check(self._lib.pa_oracle_e4m3_to_bf16(c.size, c.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)),
                                                      _ptr(out, _u16p)))
         return out
+
+    def e4m3_encode(self, x, scale: float = 1.0) -> np.ndarray:
+        """E4M3 codes (uint8) of float64 values divided by a float32 scale:
+        round to nearest even among the finite codes (saturating at +-448),
+        NaN -> 0x7F."""
+        xs = _as(x, np.float64)
+        out = np.zeros(xs.shape, np.uint8)
+        self._check(self._lib.pa_oracle_e4m3_encode(xs.size, _ptr(xs, _f64p), ctypes.c_float(scale),
+                                                    out.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))))
+        return out
+
+    def append_e4m3(self, k_bits, v_bits, positions, theta: float, k_scale: float, v_scale: float):
+        """The rows an append writes into 8-bit pools: K (bf16 [T, Hkv, D])
+        rotated as by ``rope`` when theta > 0 (widened unrotated otherwise),
+        then encoded under k_scale; V (bf16) widened and encoded under
+        v_scale.  Returns (k_codes, v_codes, k_values) with k_values the
+        float64 K rows before encoding."""
+        kb = _as(k_bits, np.uint16)
+        vb = _as(v_bits, np.uint16)
+        if kb.shape != vb.shape or kb.ndim != 3:
+            raise OracleError("k and v rows must both be [T, Hkv, D]")
+        if theta > 0:
+            k_values = self.rope(kb, positions, theta)
+        else:
+            k_values = (kb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        v_values = (vb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        return self.e4m3_encode(k_values, k_scale), self.e4m3_encode(v_values, v_scale), k_values
 
     def decode_fp8(self, q_bits, k_codes, v_codes, kv_indptr, kv_indices, sm_scale: float,
                    k_scale: float, v_scale: float, num_kv_heads: int, sel=None):

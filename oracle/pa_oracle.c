@@ -61,6 +61,13 @@
  *     values unchanged:
  *         s_j = scale * <q, k_scale * value(Kcode[S_j])>
  *         out = sum_j exp(s_j - m) * v_scale * value(Vcode[S_j]) / sum_j exp(s_j - m)
+ *     Writing such a pool (the append step for 8-bit pools): a K row is
+ *     rotated as above in double precision, then each element y is stored as
+ *     the E4M3 code nearest to y / k_scale; a V element x (bf16, widened) as
+ *     the code nearest to x / v_scale.  Reading of "nearest": round to
+ *     nearest, ties to even, among the finite codes, so that magnitudes past
+ *     the largest finite value 448 saturate to +-448 (a KV cache keeps a
+ *     finite value rather than NaN); NaN inputs give the NaN code 0x7F.
  *
  * All arithmetic is in double precision.  bf16 inputs are widened exactly
  * (a bf16 bit pattern is the upper half of an IEEE binary32).  The softmax
@@ -403,6 +410,48 @@ int pa_oracle_e4m3_values(int64_t n, const uint8_t *codes, double *values)
         return ORACLE_BAD_SHAPE;
     for (int64_t i = 0; i < n; i++)
         values[i] = e4m3_value(codes[i]);
+    return ORACLE_OK;
+}
+
+/*
+ * The E4M3 code of one double: the finite code whose value is nearest, a tie
+ * going to the code whose last mantissa bit is 0 (round to nearest even).
+ * Being nearest among the finite codes only, magnitudes at or beyond 448
+ * (infinities included) give +-448; NaN gives 0x7F; the sign of a zero result
+ * is the sign of the input.  Plain search over the 127 finite magnitudes.
+ */
+static uint8_t e4m3_encode(double x)
+{
+    if (isnan(x))
+        return 0x7F;
+    const uint8_t sign = signbit(x) ? 0x80 : 0x00;
+    const double a = fabs(x);
+    if (a >= 448.0)
+        return sign | 0x7E;
+    int best = 0;
+    double best_err = a;              /* distance to code 0 (value 0) */
+    for (int c = 1; c <= 0x7E; c++) {
+        const double err = fabs(e4m3_value((uint8_t)c) - a);
+        if (err < best_err || (err == best_err && (c & 1) == 0)) {
+            best = c;
+            best_err = err;
+        }
+    }
+    return (uint8_t)(sign | best);
+}
+
+/*
+ * Codes of n doubles divided by a scale: codes[i] = E4M3 code of x[i] / scale
+ * (the quotient formed in double precision; the scale is given as a float and
+ * widened).  The write side of the 8-bit pool: a value stored under pool
+ * scale s is the code of value / s, so that s * value(code) approximates it.
+ */
+int pa_oracle_e4m3_encode(int64_t n, const double *x, float scale, uint8_t *codes)
+{
+    if (n < 0 || !(scale > 0.0f) || isinf(scale))
+        return ORACLE_BAD_SHAPE;
+    for (int64_t i = 0; i < n; i++)
+        codes[i] = e4m3_encode(x[i] / (double)scale);
     return ORACLE_OK;
 }
 

@@ -6,7 +6,10 @@ Each ``pin_*`` function takes an oracle handle (``oracle.Oracle``) and raises
     in float64 with grouped-query heads, numpy/scipy reductions),
   * brute force at 50 significant digits (mpmath) on tiny inputs,
   * closed forms (one token, two tokens, zero query, constant values,
-    saturated softmax, empty list; RoPE of unit vectors),
+    saturated softmax, empty list; RoPE of unit vectors; E4M3 saturation and
+    special values),
+  * torch's float8_e4m3fn rounding inside the finite range, and exact
+    rational brute force for the nearest E4M3 code,
   * invariances (slot order, slot relocation, split-and-merge; RoPE's
     relative-position property and pair norms), and for RoPE numpy complex
     multiplication.
@@ -535,6 +538,112 @@ def pin_decode_fp8_unit_scales_equal_bf16(o):
     assert np.abs(out8 - out).max() < TOL and np.abs(lse8 - lse).max() < TOL, "fp8 vs bf16 decode"
 
 
+# ----------------------------------------------------------------------------
+# Writing 8-bit pools: the E4M3 encoder and the append's rows
+# ----------------------------------------------------------------------------
+def _torch_codes(x) -> np.ndarray:
+    """torch's float8_e4m3fn codes of float32 values (nearest even; NaN past 464)."""
+    return torch.as_tensor(np.asarray(x, np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+_FINITE = torch.from_numpy(np.arange(0x7F, dtype=np.uint8)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def _nearest_code(x: float) -> int:
+    """Brute force in exact rationals over torch's table of the 127 finite
+    magnitudes: the nearest one, a tie to the even code, sign kept; past 448
+    the nearest finite value is 448 itself."""
+    if np.isnan(x):
+        return 0x7F
+    sign = 0x80 if np.signbit(x) else 0
+    a = Fraction(448) if np.isinf(x) else abs(Fraction(float(x)))
+    best = min(range(0x7F), key=lambda c: (abs(Fraction(float(_FINITE[c])) - a), c & 1))
+    return sign | best
+
+
+def pin_e4m3_encode_round_trip(o):
+    """Every finite code's own value encodes back to that code (both zeros too)."""
+    codes = np.array([c for c in range(256) if c & 0x7F != 0x7F], np.uint8)
+    assert np.array_equal(o.e4m3_encode(o.e4m3_values(codes)), codes), "E4M3 round trip"
+
+
+def pin_e4m3_encode_matches_torch(o):
+    """Inside the finite range (|x| <= 464, the last tie) the codes equal
+    torch's float8_e4m3fn rounding of float32 inputs: every midpoint between
+    neighbouring codes (ties to even), and log-uniform magnitudes from 2^-12
+    (below the smallest subnormal) to 464 of both signs."""
+    rng = np.random.default_rng(61)
+    mids = ((_FINITE[:-1] + _FINITE[1:]) / 2).tolist() + [464.0]
+    mag = np.exp2(rng.uniform(-12, np.log2(464.0), 20000))
+    x = np.concatenate([mids, -np.array(mids), mag * rng.choice([-1.0, 1.0], mag.size)])
+    x = x.astype(np.float32).astype(np.float64)
+    ours, ref = o.e4m3_encode(x), _torch_codes(x)
+    bad = np.nonzero(ours != ref)[0]
+    assert bad.size == 0, f"E4M3 encode differs from torch at {x[bad[:4]]}: {ours[bad[:4]]} vs {ref[bad[:4]]}"
+
+
+def pin_e4m3_encode_exact_nearest(o):
+    """Doubles off the float32 grid against exact rational brute force: one
+    double-precision step either side of every midpoint (2^-40 relative, far
+    below a float's resolution, so a float-rounded quotient lands on the tie
+    and fails), random doubles, and the subnormal edges."""
+    rng = np.random.default_rng(62)
+    mids = (_FINITE[:-1] + _FINITE[1:]) / 2
+    near = np.concatenate([mids * (1 + 2.0 ** -40), mids * (1 - 2.0 ** -40), mids[:1] * 0.999999])
+    rand = np.exp2(rng.uniform(-11, 8.8, 400)) * rng.choice([-1.0, 1.0], 400) * (1 + rng.uniform(0, 1e-9, 400))
+    x = np.concatenate([near, -near, rand, [2.0 ** -10, 3 * 2.0 ** -10, 2.0 ** -11, -2.0 ** -12]])
+    ours = o.e4m3_encode(x)
+    want = np.array([_nearest_code(v) for v in x], np.uint8)
+    bad = np.nonzero(ours != want)[0]
+    assert bad.size == 0, f"E4M3 encode not nearest at {x[bad[:4]]}: {ours[bad[:4]]} vs {want[bad[:4]]}"
+
+
+def pin_e4m3_encode_saturation_and_specials(o):
+    """448 and beyond (infinity included) saturate to +-448 (0x7E / 0xFE),
+    NaN gives 0x7F, zeros keep their sign, tiny values round to a signed zero."""
+    x = np.array([448.0, 449.0, 463.9, 464.0, 470.0, 480.0, 1e300, np.inf,
+                  -448.0, -470.0, -np.inf, np.nan, 0.0, -0.0, 2.0 ** -11, -2.0 ** -11])
+    want = [0x7E] * 8 + [0xFE] * 3 + [0x7F, 0x00, 0x80, 0x00, 0x80]
+    assert list(o.e4m3_encode(x)) == want, "E4M3 saturation or special values"
+
+
+def pin_e4m3_encode_scale(o):
+    """A power-of-two scale s moves the input exactly, so encode(x, s) equals
+    encode(x / s, 1) (computed here by exact scaling); a value that is
+    s * value(code) for a scale s that is not a power of two encodes back to
+    that code when the product is exact."""
+    rng = np.random.default_rng(63)
+    x = np.exp2(rng.uniform(-8, 6, 2000)) * rng.choice([-1.0, 1.0], 2000)
+    for s in (4.0, 0.25):
+        assert np.array_equal(o.e4m3_encode(x, s), o.e4m3_encode(x / s, 1.0)), f"scale {s}"
+    s = 0.375                                  # 3/8: exact in float, not a power of two
+    codes = np.arange(0x7F, dtype=np.uint8)    # value * 3/8 is exact in double for every code
+    assert np.array_equal(o.e4m3_encode(_FINITE[codes] * s, s), codes), "scale 0.375 round trip"
+
+
+def pin_append_e4m3_rows(o):
+    """The rows the 8-bit append writes: values that are exact multiples of
+    the pool scales (K at scale 2, V at scale 0.5) come back as their codes at
+    position 0 (no rotation), a swap of the scales or of K and V shows; at
+    position p a unit vector e_0 rotates into (cos p, sin p) on the pair
+    (0, D/2), whose codes are the nearest to math.cos / math.sin."""
+    import math
+    rng = np.random.default_rng(64)
+    T, H, D = 3, 2, 8
+    kc = rng.integers(0, 0x7F, (T, H, D)).astype(np.uint8)
+    vc = rng.integers(0x80, 0xFF, (T, H, D)).astype(np.uint8)
+    kb = _bf16_bits(o.e4m3_values(kc) * 2.0)
+    vb = _bf16_bits(o.e4m3_values(vc) * 0.5)
+    k_out, v_out, _ = o.append_e4m3(kb, vb, np.zeros(T, np.int32), 1e4, 2.0, 0.5)
+    assert np.array_equal(k_out, kc) and np.array_equal(v_out, vc), "append codes at position 0"
+    e0 = np.zeros((1, 1, D))
+    e0[0, 0, 0] = 1.0
+    for p in (1, 2, 1000):
+        k_out, _, _ = o.append_e4m3(_bf16_bits(e0), _bf16_bits(e0), np.array([p], np.int32), 1e4, 1.0, 1.0)
+        assert k_out[0, 0, 0] == _nearest_code(math.cos(p)), f"cos({p})"
+        assert k_out[0, 0, D // 2] == _nearest_code(math.sin(p)), f"sin({p})"
+
+
 ALL_PINS = [
     pin_sdpa_decode, pin_bruteforce_tiny, pin_slot_order, pin_single_token, pin_two_tokens,
     pin_zero_query, pin_constant_values, pin_saturated_softmax, pin_empty_list,
@@ -544,4 +653,6 @@ ALL_PINS = [
     pin_rope_relative_position, pin_rope_norm,
     pin_e4m3_matches_torch, pin_e4m3_closed_forms, pin_e4m3_widening_exact, pin_decode_fp8_sdpa,
     pin_decode_fp8_single_token, pin_decode_fp8_unit_scales_equal_bf16,
+    pin_e4m3_encode_round_trip, pin_e4m3_encode_matches_torch, pin_e4m3_encode_exact_nearest,
+    pin_e4m3_encode_saturation_and_specials, pin_e4m3_encode_scale, pin_append_e4m3_rows,
 ]

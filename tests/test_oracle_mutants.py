@@ -68,6 +68,15 @@ MUTANTS = [
     ("fp8_lse_without_max", [("*lse = top + log(total);", "*lse = log(total);", None)]),
     ("fp8_exp_unshifted", [("w[j] = exp(w[j] - top);", "w[j] = exp(w[j]);", None)]),
     ("fp8_gqa_modulo", [("head / per_kv_head, kv_indices", "head % Hkv, kv_indices", None)]),
+    ("e4m3_encode_ties_up", [("(err == best_err && (c & 1) == 0)", "(err == best_err)", None)]),
+    ("e4m3_encode_truncates", [("if (err < best_err || (err == best_err && (c & 1) == 0))",
+                                "if (e4m3_value((uint8_t)c) <= a)", None)]),
+    ("e4m3_encode_saturates_to_nan", [("return sign | 0x7E;", "return 0x7F;", None)]),
+    ("e4m3_encode_sign_dropped", [("return (uint8_t)(sign | best);", "return (uint8_t)best;", None)]),
+    ("e4m3_encode_nan_to_zero", [("if (isnan(x))\n        return 0x7F;", "if (isnan(x))\n        return 0x00;", None)]),
+    ("e4m3_encode_scale_multiplies", [("e4m3_encode(x[i] / (double)scale)", "e4m3_encode(x[i] * (double)scale)", None)]),
+    ("e4m3_encode_float_quotient", [("e4m3_encode(x[i] / (double)scale)",
+                                     "e4m3_encode((double)(float)(x[i] / (double)scale))", None)]),
     ("rope_position_off_by_one", [("(double)positions[t] * inv_freq", "(double)(positions[t] + 1) * inv_freq", None)]),
 ]
 
