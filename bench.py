@@ -339,8 +339,12 @@ def run_append_bench(args):
     import workloads as W
     dev = torch.device("cuda", 0)
     T, Hq, Hkv, D, N, layers = 64, 32, 8, 128, 600_000, args.layers or 36
+    fp8 = args.kv == "fp8"
     rng = np.random.Generator(np.random.PCG64(1006))
-    k_pools = [W.make_pools(N, Hkv, D, 1006 + l, dev) for l in range(min(layers, 4))]
+    if fp8:
+        k_pools = [W.make_pools_e4m3(N, Hkv, D, 1006 + l, dev) for l in range(min(layers, 4))]
+    else:
+        k_pools = [W.make_pools(N, Hkv, D, 1006 + l, dev) for l in range(min(layers, 4))]
     k_new = W.normal_bf16((T, Hkv, D), 7, dev)
     v_new = W.normal_bf16((T, Hkv, D), 8, dev)
     q = W.normal_bf16((T, Hq, D), 9, dev)
@@ -350,8 +354,12 @@ def run_append_bench(args):
     def calls(stream):
         for l in range(layers):
             kp, vp = k_pools[l % len(k_pools)]
-            pa.pa_kv_append(k_new, v_new, loc, kp, vp, positions=pos, rope_theta=1e6, q=q,
-                            stream=stream)
+            if fp8:
+                pa.pa_kv_append_fp8(k_new, v_new, loc, kp, vp, W.FP8_K_SCALE, W.FP8_V_SCALE, positions=pos,
+                                    rope_theta=1e6, q=q, stream=stream)
+            else:
+                pa.pa_kv_append(k_new, v_new, loc, kp, vp, positions=pos, rope_theta=1e6, q=q,
+                                stream=stream)
 
     # the 36 calls of a step replayed from a HIP graph, so the time is the
     # GPU's and not the Python binding's
@@ -373,29 +381,32 @@ def run_append_bench(args):
     end.record()
     torch.cuda.synchronize()
     us = start.elapsed_time(end) * 1e3 / (args.steps * layers)
-    moved = 2 * (2 * T * Hkv * D * 2 + T * Hq * D * 2) + 2 * T * 4   # K, V, Q read + written; ids
+    # K and V read (bf16) and written (bf16, or 1-byte codes), Q read and written; ids
+    moved = 2 * T * Hkv * D * (2 + (1 if fp8 else 2)) + 2 * T * Hq * D * 2 + 2 * T * 4
     log(f"append: {us:.2f} us per call ({moved / (us * 1e-6) / 1e9:.1f} GB/s)")
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline_append(k_new, v_new, q, loc, pos, N, args.cpu_seconds)
+        cpu = cpu_baseline_append(k_new, v_new, q, loc, pos, N, args.cpu_seconds, fp8)
         log(f"cpu baseline {cpu['value']} us per call on {cpu['cores']} threads")
     print(json.dumps({
-        "metric": "append + RoPE µs per layer call, batch-64 decode step", "value": round(us, 3),
+        "metric": f"append + RoPE µs per layer call, batch-64 decode step, {args.kv} KV", "value": round(us, 3),
         "unit": "us", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "higher_is_better": False, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "append_rope_b64_hkv8_hq32_d128", "tokens": T, "layers_per_step": layers},
+        "higher_is_better": False, "dtype": "f64", "data": "synthetic",
+        "config": {"workload": "append_rope_b64_hkv8_hq32_d128" + ("_fp8kv" if fp8 else ""), "tokens": T,
+                   "layers_per_step": layers},
         "bytes_per_call": moved, "vs_baseline": None,
         "roofline": {"bound": "hbm", "achieved": round(moved / (us * 1e-6) / 1e9, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(moved / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 5), "traffic": None,
-                     "kernel": "append_kernel (pa_kv_append)"},
+                     "kernel": "append_kernel<true> (pa_kv_append_fp8)" if fp8 else "append_kernel<false> (pa_kv_append)"},
         "cpu_baseline": cpu,
     }), flush=True)
 
 
-def cpu_baseline_append(k_new, v_new, q, loc, pos, num_slots, seconds):
+def cpu_baseline_append(k_new, v_new, q, loc, pos, num_slots, seconds, fp8=False):
     """The oracle's RoPE of the call's K and query rows, and the K and V rows
-    stored at their slots of host pools (float64, allocated lazily)."""
+    stored at their slots of host pools (float64, allocated lazily; with fp8,
+    the oracle's E4M3 codes into uint8 pools)."""
     import numpy as np
 
     import oracle
@@ -405,13 +416,17 @@ def cpu_baseline_append(k_new, v_new, q, loc, pos, num_slots, seconds):
     slots = loc.cpu().numpy()
     positions = pos.cpu().numpy()
     T, Hkv, D = kb.shape
-    k_pool = np.zeros((num_slots, Hkv, D))
-    v_pool = np.zeros((num_slots, Hkv, D))
+    k_pool = np.zeros((num_slots, Hkv, D), np.uint8 if fp8 else np.float64)
+    v_pool = np.zeros((num_slots, Hkv, D), np.uint8 if fp8 else np.float64)
     reps = 0
     t0 = time.perf_counter()
     while True:
-        k_pool[slots] = ref.rope(kb, positions, 1e6)
-        v_pool[slots] = (vb.astype(np.uint32) << 16).view(np.float32)   # V rows as they are
+        if fp8:
+            k_pool[slots], v_pool[slots], _ = ref.append_e4m3(kb, vb, positions, 1e6, W.FP8_K_SCALE,
+                                                              W.FP8_V_SCALE)
+        else:
+            k_pool[slots] = ref.rope(kb, positions, 1e6)
+            v_pool[slots] = (vb.astype(np.uint32) << 16).view(np.float32)   # V rows as they are
         ref.rope(qb, positions, 1e6)
         reps += 1
         if time.perf_counter() - t0 >= seconds:
@@ -437,7 +452,7 @@ def main():
                     choices=["batch64", "batch64_4k8k", "single_request", "batch8", "hd256", "system_prompt",
                              "prefill_chunk512", "prefill_chunk64", "append", "copy"])
     ap.add_argument("--kv", default="bf16", choices=["bf16", "fp8"],
-                    help="decode: pool element type (fp8 = OCP E4M3 codes with per-pool scales)")
+                    help="decode and append: pool element type (fp8 = OCP E4M3 codes with per-pool scales)")
     ap.add_argument("--graph", action="store_true", default=True,
                     help="decode: replay each step's layer runs from a captured HIP graph (the default)")
     ap.add_argument("--eager", dest="graph", action="store_false",

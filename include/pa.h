@@ -370,6 +370,30 @@ pa_status pa_kv_append(const void *k_new, const void *v_new, void *q, const int3
                        void *v_pool, int64_t num_slots, int64_t slot_stride, pa_stream_t stream);
 
 /*
+ * pa_kv_append_fp8: pa_kv_append into 8-bit pools (the pools of
+ * pa_decode_run_fp8: OCP FP8 E4M3 codes, 1 byte per element, one scale per
+ * pool; quantised KV is on the Agent-Infer page's roadmap, section
+ * "模型支持与发展路线图", the format and its rounding are this library's
+ * reading).  K is rotated as by pa_kv_append, in double precision, and each
+ * rotated value y is stored as the E4M3 code nearest to y / k_scale; each V
+ * value x (bf16) as the code nearest to x / v_scale.  Nearest: the quotient
+ * is formed in double and rounded once to nearest, ties to even, among the
+ * finite codes, so magnitudes at or beyond 448 store +-448 (0x7E / 0xFE),
+ * NaN stores 0x7F, and a zero result keeps the input's sign.  q, if given,
+ * is rotated in place and stays bf16.
+ *   k_pool, v_pool  device E4M3 codes [slots, Hkv, D] (slot_stride in bytes,
+ *                   0 = Hkv*D, a multiple of 8), 16-byte aligned
+ *   k_scale, v_scale  finite and > 0
+ * Other arguments, ownership and errors as pa_kv_append, plus
+ * PA_ERR_INVALID_ARG for a scale that is not finite and positive.
+ */
+pa_status pa_kv_append_fp8(const void *k_new, const void *v_new, void *q, const int32_t *positions,
+                           const int32_t *out_loc, int32_t num_tokens, int32_t num_qo_heads,
+                           int32_t num_kv_heads, int32_t head_dim, float rope_theta, float k_scale,
+                           float v_scale, void *k_pool, void *v_pool, int64_t num_slots,
+                           int64_t slot_stride, pa_stream_t stream);
+
+/*
  * pa_partition: compute the partition pa_plan would upload, into host arrays.
  *   Arguments as in pa_plan_create / pa_plan; max_workgroups is the number of
  *   decode workgroups the GPU holds at once (pa_plan uses the kernel's

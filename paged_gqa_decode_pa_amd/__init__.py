@@ -131,6 +131,8 @@ def _load() -> ctypes.CDLL:
     lib.pa_decode_run_fp8.restype = ctypes.c_int
     lib.pa_kv_append.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp, vp, i64, i64, vp]
     lib.pa_kv_append.restype = ctypes.c_int
+    lib.pa_kv_append_fp8.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, f32, f32, vp, vp, i64, i64, vp]
+    lib.pa_kv_append_fp8.restype = ctypes.c_int
     lib.pa_plan_info.argtypes = [vp, i32p, i32p, i32p, i32p, i32p]
     lib.pa_plan_info.restype = ctypes.c_int
     lib.pa_check_kv_indices.argtypes = [i32p, i32, i32p, i64, ctypes.POINTER(ctypes.c_int64)]
@@ -372,11 +374,8 @@ def pa_prefill_chunk_run(plan, q, k_pool, v_pool, kv_indices, sm_scale, out, lse
          kv_indices, sm_scale, out, lse, num_slots, slot_stride, stream)
 
 
-def pa_kv_append(k_new, v_new, out_loc, k_pool, v_pool, positions=None, rope_theta: float = 0.0,
-                 q=None, num_slots=None, slot_stride=None, stream=None) -> None:
-    """Write the new tokens' K/V rows [T, Hkv, D] to slots out_loc [T] of the
-    pools, K rotated by RoPE (and q [T, Hq, D] rotated in place, if given)
-    when rope_theta > 0."""
+def _append_shapes(k_new, v_new, out_loc, positions, q):
+    """(T, Hq, Hkv, D) of an append call, after the shape and dtype checks."""
     T, Hkv, D = k_new.shape
     if tuple(v_new.shape) != (T, Hkv, D):
         raise ValueError("v_new must have the shape of k_new")
@@ -391,16 +390,48 @@ def pa_kv_append(k_new, v_new, out_loc, k_pool, v_pool, positions=None, rope_the
     for name, t in (("out_loc", out_loc), ("positions", positions)):
         if t is not None and (t.dtype != torch.int32 or t.numel() != T):
             raise TypeError(f"{name} must be int32 with one entry per token")
+    return T, Hq, Hkv, D
+
+
+def pa_kv_append(k_new, v_new, out_loc, k_pool, v_pool, positions=None, rope_theta: float = 0.0,
+                 q=None, num_slots=None, slot_stride=None, stream=None) -> None:
+    """Write the new tokens' K/V rows [T, Hkv, D] to slots out_loc [T] of the
+    pools, K rotated by RoPE (and q [T, Hq, D] rotated in place, if given)
+    when rope_theta > 0."""
+    T, Hq, Hkv, D = _append_shapes(k_new, v_new, out_loc, positions, q)
     if slot_stride is None:
         slot_stride = _pool_stride(k_pool, v_pool, D)
     if num_slots is None:
-        num_slots = k_pool.shape[0]
+        num_slots = min(k_pool.shape[0], v_pool.shape[0])
     _check(_lib.pa_kv_append(_dev_ptr(k_new, "k_new", torch.bfloat16), _dev_ptr(v_new, "v_new", torch.bfloat16),
                              _dev_ptr(q, "q", torch.bfloat16), _dev_ptr(positions, "positions"),
                              _dev_ptr(out_loc, "out_loc"), T, Hq, Hkv, D, float(rope_theta),
                              _dev_ptr(k_pool, "k_pool", torch.bfloat16),
                              _dev_ptr(v_pool, "v_pool", torch.bfloat16), int(num_slots),
                              int(slot_stride), _stream(stream)), "pa_kv_append")
+
+
+def pa_kv_append_fp8(k_new, v_new, out_loc, k_pool, v_pool, k_scale: float, v_scale: float,
+                     positions=None, rope_theta: float = 0.0, q=None, num_slots=None,
+                     slot_stride=None, stream=None) -> None:
+    """pa_kv_append into E4M3 pools (torch.float8_e4m3fn or uint8
+    [slots, Hkv, D]): K rotated in double precision and stored as the code
+    nearest to value / k_scale, V as the code nearest to value / v_scale."""
+    T, Hq, Hkv, D = _append_shapes(k_new, v_new, out_loc, positions, q)
+    for name, t in (("k_pool", k_pool), ("v_pool", v_pool)):
+        if t.dtype not in (torch.float8_e4m3fn, torch.uint8):
+            raise TypeError(f"{name} must hold E4M3 codes (float8_e4m3fn or uint8)")
+    if slot_stride is None:
+        slot_stride = _pool_stride(k_pool, v_pool, D)
+    if num_slots is None:
+        num_slots = min(k_pool.shape[0], v_pool.shape[0])
+    _check(_lib.pa_kv_append_fp8(_dev_ptr(k_new, "k_new", torch.bfloat16),
+                                 _dev_ptr(v_new, "v_new", torch.bfloat16),
+                                 _dev_ptr(q, "q", torch.bfloat16), _dev_ptr(positions, "positions"),
+                                 _dev_ptr(out_loc, "out_loc"), T, Hq, Hkv, D, float(rope_theta),
+                                 float(k_scale), float(v_scale), _dev_ptr(k_pool, "k_pool"),
+                                 _dev_ptr(v_pool, "v_pool"), int(num_slots), int(slot_stride),
+                                 _stream(stream)), "pa_kv_append_fp8")
 
 
 def pa_plan_destroy(plan) -> None:

@@ -736,10 +736,13 @@ pa_status pa_plan_cascade(pa_plan_t *p, const int32_t *kv_indptr_host, int32_t b
     return plan_impl(p, kv_indptr_host, nullptr, batch, flags, stream, &c);
 }
 
-pa_status pa_kv_append(const void *k_new, const void *v_new, void *q, const int32_t *positions,
-                       const int32_t *out_loc, int32_t num_tokens, int32_t num_qo_heads,
-                       int32_t num_kv_heads, int32_t head_dim, float rope_theta, void *k_pool,
-                       void *v_pool, int64_t num_slots, int64_t slot_stride, pa_stream_t stream) {
+static pa_status append_impl(const void *k_new, const void *v_new, void *q, const int32_t *positions,
+                             const int32_t *out_loc, int32_t num_tokens, int32_t num_qo_heads,
+                             int32_t num_kv_heads, int32_t head_dim, float rope_theta, void *k_pool,
+                             void *v_pool, int64_t num_slots, int64_t slot_stride, pa_stream_t stream,
+                             bool kv_fp8, float k_scale, float v_scale) {
+    if (kv_fp8 && !(std::isfinite(k_scale) && std::isfinite(v_scale) && k_scale > 0.f && v_scale > 0.f))
+        return fail(PA_ERR_INVALID_ARG, "k_scale and v_scale must be finite and positive");
     if (num_tokens < 0 || num_qo_heads <= 0 || num_kv_heads <= 0)
         return fail(PA_ERR_INVALID_ARG, "bad token or head count");
     if (head_dim != 128 && head_dim != 256)
@@ -776,10 +779,32 @@ pa_status pa_kv_append(const void *k_new, const void *v_new, void *q, const int3
     l.v_pool = v_pool;
     l.num_slots = num_slots;
     l.slot_stride = slot_stride;
+    l.kv_fp8 = kv_fp8;
+    l.k_scale = k_scale;
+    l.v_scale = v_scale;
     const int rc = pa::launch_append(l, stream);
     if (rc != 0)
         return hip_fail((hipError_t)rc, "append kernel launch");
     return PA_OK;
+}
+
+pa_status pa_kv_append(const void *k_new, const void *v_new, void *q, const int32_t *positions,
+                       const int32_t *out_loc, int32_t num_tokens, int32_t num_qo_heads,
+                       int32_t num_kv_heads, int32_t head_dim, float rope_theta, void *k_pool,
+                       void *v_pool, int64_t num_slots, int64_t slot_stride, pa_stream_t stream) {
+    return append_impl(k_new, v_new, q, positions, out_loc, num_tokens, num_qo_heads, num_kv_heads,
+                       head_dim, rope_theta, k_pool, v_pool, num_slots, slot_stride, stream, false, 1.f,
+                       1.f);
+}
+
+pa_status pa_kv_append_fp8(const void *k_new, const void *v_new, void *q, const int32_t *positions,
+                           const int32_t *out_loc, int32_t num_tokens, int32_t num_qo_heads,
+                           int32_t num_kv_heads, int32_t head_dim, float rope_theta, float k_scale,
+                           float v_scale, void *k_pool, void *v_pool, int64_t num_slots,
+                           int64_t slot_stride, pa_stream_t stream) {
+    return append_impl(k_new, v_new, q, positions, out_loc, num_tokens, num_qo_heads, num_kv_heads,
+                       head_dim, rope_theta, k_pool, v_pool, num_slots, slot_stride, stream, true, k_scale,
+                       v_scale);
 }
 
 pa_status pa_plan_info(const pa_plan_t *p, int32_t *mode, int32_t *rows, int32_t *num_qo_heads,

@@ -15,9 +15,17 @@
 // rounding).  V rows are copied bit for bit.  A token whose slot id is out of
 // [0, num_slots) writes nothing.
 //
+// 8-bit pools (OCP FP8 E4M3 codes with one scale per pool; quantised KV is on
+// the Agent-Infer page's roadmap, section "模型支持与发展路线图"): the rotated K
+// value y (double) is stored as the code nearest to y / k_scale, a V value x
+// as the code nearest to x / v_scale, the quotient formed in double and
+// rounded once: to nearest, ties to even, among the finite codes, so that
+// magnitudes at or beyond the largest finite value 448 store +-448; NaN
+// stores 0x7F.
+//
 // One thread per rotated pair (K, then Q) and one per 16-byte chunk of a V
-// row; consecutive threads take consecutive pairs of a row, so every load and
-// store of a wave is one contiguous run.
+// row (8 values); consecutive threads take consecutive pairs of a row, so
+// every load and store of a wave is one contiguous run.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -42,6 +50,32 @@ __device__ __forceinline__ uint16_t bf16_from_double(double y) {
     return (uint16_t)(u >> 16);
 }
 
+// E4M3 code of a double: nearest among the finite codes, ties to even, NaN
+// to 0x7F, a zero result signed as the input.  At or beyond 448 (the largest
+// finite value, infinities included) the nearest finite code is 448 itself.
+// From 2^-6 up, a = q * 2^(E-3) with E = floor(log2 a) in [-6, 8] and the
+// code is (E + 7) << 3 | (rint(q) - 8); rint(q) = 16 carries into the next
+// exponent by the addition.  Below 2^-6 the codes step by 2^-9 (code 8 is
+// 2^-6 again).  rint rounds half to even; the scalings are exact.
+__device__ __forceinline__ uint32_t e4m3_from_double(double y) {
+    if (__builtin_isnan(y))
+        return 0x7Fu;
+    const uint32_t sign = __builtin_signbit(y) ? 0x80u : 0u;
+    const double a = fabs(y);
+    uint32_t mag;
+    if (a >= 448.0) {
+        mag = 0x7Eu;
+    } else if (a < 0x1p-6) {
+        mag = (uint32_t)rint(a * 0x1p9);
+    } else {
+        int e;
+        (void)frexp(a, &e);           // a = f * 2^e, f in [0.5, 1): E = e - 1
+        const int E = e - 1;
+        mag = (uint32_t)((E + 7) << 3) + ((uint32_t)rint(ldexp(a, 3 - E)) - 8u);
+    }
+    return sign | mag;
+}
+
 struct AppendArgs {
     const uint16_t *k_new, *v_new;
     uint16_t *q;                      // null: no query rotation
@@ -49,22 +83,25 @@ struct AppendArgs {
     int32_t tokens, hq, hkv, d;
     double log2_theta;                // log2(rope_theta), when rotating
     bool rotate;                      // rope_theta > 0
-    uint16_t *k_pool, *v_pool;
+    void *k_pool, *v_pool;            // bf16, or E4M3 codes (1 byte)
+    double k_scale, v_scale;          // E4M3 pools: the pool scales
     int64_t num_slots, slot_stride;   // elements
     int64_t k_pairs, v_chunks, q_pairs;
 };
 
+// Rotation of pair i of token t: inverse frequency theta^(-2i/D) and angle
+// pos * inv_freq, all in double.
 __device__ __forceinline__ void rotate_pair(const AppendArgs &a, int64_t t, int i, uint16_t x1b, uint16_t x2b,
-                                            uint16_t *y1, uint16_t *y2) {
-    // inverse frequency theta^(-2i/D) and angle pos * inv_freq, in double
+                                            double *y1, double *y2) {
     const double inv_freq = exp2(a.log2_theta * (-2.0 * (double)i / (double)a.d));
     double s, c;
     sincos((double)a.positions[t] * inv_freq, &s, &c);
     const double x1 = widen_bf16(x1b), x2 = widen_bf16(x2b);
-    *y1 = bf16_from_double(x1 * c - x2 * s);
-    *y2 = bf16_from_double(x2 * c + x1 * s);
+    *y1 = x1 * c - x2 * s;
+    *y2 = x2 * c + x1 * s;
 }
 
+template <bool KV8>
 __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
     int64_t g = (int64_t)blockIdx.x * kAppendThreads + threadIdx.x;
     const int half = a.d / 2;
@@ -78,12 +115,25 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
         if (slot < 0 || slot >= a.num_slots)
             return;
         const uint16_t *x = a.k_new + row * a.d;
-        uint16_t *dst = a.k_pool + (int64_t)slot * a.slot_stride + (int64_t)h * a.d;
-        if (a.rotate) {
-            rotate_pair(a, t, i, x[i], x[i + half], &dst[i], &dst[i + half]);
+        const int64_t off = (int64_t)slot * a.slot_stride + (int64_t)h * a.d;
+        if constexpr (KV8) {
+            double y1 = widen_bf16(x[i]), y2 = widen_bf16(x[i + half]);
+            if (a.rotate)
+                rotate_pair(a, t, i, x[i], x[i + half], &y1, &y2);
+            uint8_t *dst = static_cast<uint8_t *>(a.k_pool) + off;
+            dst[i] = (uint8_t)e4m3_from_double(y1 / a.k_scale);
+            dst[i + half] = (uint8_t)e4m3_from_double(y2 / a.k_scale);
         } else {
-            dst[i] = x[i];
-            dst[i + half] = x[i + half];
+            uint16_t *dst = static_cast<uint16_t *>(a.k_pool) + off;
+            if (a.rotate) {
+                double y1, y2;
+                rotate_pair(a, t, i, x[i], x[i + half], &y1, &y2);
+                dst[i] = bf16_from_double(y1);
+                dst[i + half] = bf16_from_double(y2);
+            } else {
+                dst[i] = x[i];
+                dst[i + half] = x[i + half];
+            }
         }
         return;
     }
@@ -99,7 +149,19 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
         if (slot < 0 || slot >= a.num_slots)
             return;
         const uint4 v = *reinterpret_cast<const uint4 *>(a.v_new + row * a.d + c * 8);
-        *reinterpret_cast<uint4 *>(a.v_pool + (int64_t)slot * a.slot_stride + (int64_t)h * a.d + c * 8) = v;
+        const int64_t off = (int64_t)slot * a.slot_stride + (int64_t)h * a.d + c * 8;
+        if constexpr (KV8) {
+            // eight bf16 values -> eight codes, one 8-byte store
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+            uint32_t packed[2] = {0u, 0u};
+            for (int e = 0; e < 8; e++) {
+                const uint16_t b = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+                packed[e >> 2] |= e4m3_from_double(widen_bf16(b) / a.v_scale) << (8 * (e & 3));
+            }
+            *reinterpret_cast<uint2 *>(static_cast<uint8_t *>(a.v_pool) + off) = make_uint2(packed[0], packed[1]);
+        } else {
+            *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(a.v_pool) + off) = v;
+        }
         return;
     }
     g -= a.v_chunks;
@@ -109,10 +171,10 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
         const int i = (int)(g % half);
         const int64_t t = row / a.hq;
         uint16_t *x = a.q + row * a.d;
-        uint16_t y1, y2;
+        double y1, y2;
         rotate_pair(a, t, i, x[i], x[i + half], &y1, &y2);
-        x[i] = y1;
-        x[i + half] = y2;
+        x[i] = bf16_from_double(y1);
+        x[i + half] = bf16_from_double(y2);
     }
 }
 
@@ -133,8 +195,10 @@ int launch_append(const AppendLaunch &l, void *stream) {
     a.d = l.head_dim;
     a.rotate = l.rope_theta > 0.f;
     a.log2_theta = a.rotate ? log2((double)l.rope_theta) : 0.0;
-    a.k_pool = static_cast<uint16_t *>(l.k_pool);
-    a.v_pool = static_cast<uint16_t *>(l.v_pool);
+    a.k_pool = l.k_pool;
+    a.v_pool = l.v_pool;
+    a.k_scale = l.kv_fp8 ? (double)l.k_scale : 1.0;
+    a.v_scale = l.kv_fp8 ? (double)l.v_scale : 1.0;
     a.num_slots = l.num_slots;
     a.slot_stride = l.slot_stride;
     const int64_t rows_kv = (int64_t)l.num_tokens * l.num_kv_heads;
@@ -145,7 +209,12 @@ int launch_append(const AppendLaunch &l, void *stream) {
     const int64_t blocks = (total + kAppendThreads - 1) / kAppendThreads;
     if (blocks > 0x7fffffffLL)
         return (int)hipErrorInvalidValue;
-    hipLaunchKernelGGL(append_kernel, dim3((uint32_t)blocks), dim3(kAppendThreads), 0, (hipStream_t)stream, a);
+    if (l.kv_fp8)
+        hipLaunchKernelGGL(append_kernel<true>, dim3((uint32_t)blocks), dim3(kAppendThreads), 0,
+                           (hipStream_t)stream, a);
+    else
+        hipLaunchKernelGGL(append_kernel<false>, dim3((uint32_t)blocks), dim3(kAppendThreads), 0,
+                           (hipStream_t)stream, a);
     return (int)hipGetLastError();
 }
 

@@ -242,8 +242,10 @@ struct AppendLaunch {
     const int32_t *out_loc;     // device [tokens]
     int32_t num_tokens, num_qo_heads, num_kv_heads, head_dim;
     float rope_theta;
-    void *k_pool, *v_pool;
+    void *k_pool, *v_pool;            // bf16, or E4M3 codes when kv_fp8
     int64_t num_slots, slot_stride;   // elements
+    bool kv_fp8 = false;
+    float k_scale = 1.f, v_scale = 1.f;   // E4M3 pools: value = scale * code's value
 };
 int launch_append(const AppendLaunch &l, void *stream);   // returns hipError_t
 
