@@ -97,6 +97,12 @@ class Oracle:
             _u16p, _u8p, _u8p, ctypes.c_int64, ctypes.c_int64,
             _i32p, _i32p, ctypes.c_float, ctypes.c_float, ctypes.c_float,
             _f64p, _f64p, _i32p, ctypes.c_int64]
+        lib.pa_oracle_prefill_e4m3.restype = ctypes.c_int
+        lib.pa_oracle_prefill_e4m3.argtypes = [
+            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+            _u16p, _u8p, _u8p, ctypes.c_int64, ctypes.c_int64,
+            _i32p, _i32p, _i32p, ctypes.c_float, ctypes.c_float, ctypes.c_float,
+            _f64p, _f64p, _i32p, ctypes.c_int64]
         lib.pa_oracle_num_threads.restype = ctypes.c_int
         lib.pa_oracle_num_threads.argtypes = []
         self._lib = lib
@@ -282,6 +288,44 @@ class Oracle:
         rc = self._lib.pa_oracle_decode_e4m3(
             B, Hq, num_kv_heads, D, _ptr(q, _u16p), _ptr(k, u8p), _ptr(v, u8p),
             num_slots, slot_stride, _ptr(indptr, _i32p), _ptr(indices, _i32p),
+            ctypes.c_float(sm_scale), ctypes.c_float(k_scale), ctypes.c_float(v_scale),
+            _ptr(out, _f64p), _ptr(lse, _f64p), sel_p, n_sel)
+        self._check(rc)
+        return out, lse
+
+    def prefill_fp8(self, q_bits, k_codes, v_codes, qo_indptr, kv_indptr, kv_indices, sm_scale: float,
+                    k_scale: float, v_scale: float, num_kv_heads: int, sel=None):
+        """Chunked prefill (as ``prefill``) over E4M3 pools with per-pool
+        scales (the values of ``decode_fp8``).  Returns (out float64
+        [T, Hq, D], lse float64 [T, Hq])."""
+        q = _as(q_bits, np.uint16)
+        k = _as(k_codes, np.uint8)
+        v = _as(v_codes, np.uint8)
+        T, Hq, D = q.shape
+        if v.shape != k.shape:
+            raise OracleError("k and v pools differ in shape")
+        num_slots = k.shape[0]
+        slot_stride = int(np.prod(k.shape[1:])) if k.ndim > 1 else 0
+        qo = _as(qo_indptr, np.int32)
+        indptr = _as(kv_indptr, np.int32)
+        indices = _as(kv_indices, np.int32)
+        B = indptr.shape[0] - 1
+        if qo.shape != (B + 1,) or qo[-1] != T:
+            raise OracleError("qo_indptr must have batch+1 entries ending at T")
+        if indices.size == 0:
+            indices = np.zeros(1, np.int32)
+        out = np.full((T, Hq, D), np.nan)
+        lse = np.full((T, Hq), np.nan)
+        if sel is None:
+            sel_arr, n_sel, sel_p = None, 0, None
+        else:
+            sel_arr = _as(sel, np.int32)
+            n_sel = sel_arr.size
+            sel_p = _ptr(sel_arr, _i32p)
+        u8p = ctypes.POINTER(ctypes.c_uint8)
+        rc = self._lib.pa_oracle_prefill_e4m3(
+            B, Hq, num_kv_heads, D, _ptr(q, _u16p), _ptr(k, u8p), _ptr(v, u8p),
+            num_slots, slot_stride, _ptr(qo, _i32p), _ptr(indptr, _i32p), _ptr(indices, _i32p),
             ctypes.c_float(sm_scale), ctypes.c_float(k_scale), ctypes.c_float(v_scale),
             _ptr(out, _f64p), _ptr(lse, _f64p), sel_p, n_sel)
         self._check(rc)

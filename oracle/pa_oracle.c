@@ -68,6 +68,8 @@
  *     nearest, ties to even, among the finite codes, so that magnitudes past
  *     the largest finite value 448 saturate to +-448 (a KV cache keeps a
  *     finite value rather than NaN); NaN inputs give the NaN code 0x7F.
+ *     Chunked prefill over such pools: the prefill rows above on these
+ *     values.
  *
  * All arithmetic is in double precision.  bf16 inputs are widened exactly
  * (a bf16 bit pattern is the upper half of an IEEE binary32).  The softmax
@@ -545,6 +547,73 @@ int pa_oracle_decode_e4m3(int32_t batch, int32_t Hq, int32_t Hkv, int32_t D,
                                 (int64_t)kv_indptr[b + 1] - kv_indptr[b],
                                 (double)sm_scale, (double)k_scale, (double)v_scale,
                                 w, out + row * D, lse + row);
+        }
+        free(w);
+    }
+    return failed ? ORACLE_NO_MEMORY : ORACLE_OK;
+}
+
+/*
+ * Chunked prefill over E4M3 pools with per-pool scales: the rows of
+ * pa_oracle_prefill (chunk row i of request b sees list positions
+ * 0 .. L - C + i, the chunk being the last C entries of the list) on the
+ * row values of pa_oracle_decode_e4m3 (k_scale * value(code),
+ * v_scale * value(code), in double precision).
+ */
+int pa_oracle_prefill_e4m3(int32_t batch, int32_t Hq, int32_t Hkv, int32_t D,
+                           const uint16_t *q,
+                           const uint8_t *k_codes, const uint8_t *v_codes,
+                           int64_t num_slots, int64_t slot_stride,
+                           const int32_t *qo_indptr,
+                           const int32_t *kv_indptr, const int32_t *kv_indices,
+                           float sm_scale, float k_scale, float v_scale,
+                           double *out, double *lse,
+                           const int32_t *sel, int64_t n_sel)
+{
+    int rc = check_common(batch, Hq, Hkv, D, num_slots, slot_stride, kv_indptr, kv_indices);
+    if (rc != ORACLE_OK)
+        return rc;
+    if (qo_indptr[0] != 0)
+        return ORACLE_BAD_INDPTR;
+    for (int32_t b = 0; b < batch; b++) {
+        if (qo_indptr[b + 1] < qo_indptr[b])
+            return ORACLE_BAD_INDPTR;
+        if (qo_indptr[b + 1] - qo_indptr[b] > kv_indptr[b + 1] - kv_indptr[b])
+            return ORACLE_CHUNK_TOO_LONG;
+    }
+    const int64_t all_rows = (int64_t)qo_indptr[batch] * Hq;
+    const int64_t n_rows = sel ? n_sel : all_rows;
+    for (int64_t r = 0; r < n_rows; r++) {
+        const int64_t row = sel ? sel[r] : r;
+        if (row < 0 || row >= all_rows)
+            return ORACLE_BAD_SHAPE;
+    }
+    const int64_t longest = longest_list(batch, kv_indptr);
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *w = (double *)malloc(sizeof(double) * (size_t)longest);
+        if (!w) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t r = 0; r < n_rows; r++) {
+            if (!w)
+                continue;
+            const int64_t row = sel ? sel[r] : r;
+            const int64_t tok = row / Hq;          /* chunk token (flat over requests) */
+            const int32_t head = (int32_t)(row % Hq);
+            int32_t b = 0;
+            while (qo_indptr[b + 1] <= tok)
+                b++;
+            const int64_t c_len = (int64_t)qo_indptr[b + 1] - qo_indptr[b];
+            const int64_t pos_in_chunk = tok - qo_indptr[b];
+            const int64_t visible = ((int64_t)kv_indptr[b + 1] - kv_indptr[b]) - c_len + pos_in_chunk + 1;
+            attend_one_row_e4m3(D, q + row * D, k_codes, v_codes, slot_stride,
+                                head / (Hq / Hkv),
+                                kv_indices + kv_indptr[b], visible, (double)sm_scale,
+                                (double)k_scale, (double)v_scale, w, out + row * D, lse + row);
         }
         free(w);
     }

@@ -538,6 +538,70 @@ def pin_decode_fp8_unit_scales_equal_bf16(o):
     assert np.abs(out8 - out).max() < TOL and np.abs(lse8 - lse).max() < TOL, "fp8 vs bf16 decode"
 
 
+def _fp8_prefill_case(rng, cached, chunks, Hq, Hkv, D, spare=2):
+    lengths = [p + c for p, c in zip(cached, chunks)]
+    q_dec, kc, vc, indptr, indices = _fp8_case(rng, lengths, Hq, Hkv, D, spare)
+    qo = np.zeros(len(chunks) + 1, np.int32)
+    qo[1:] = np.cumsum(chunks)
+    q = _random_bits(rng, (int(qo[-1]), Hq, D))
+    return q, kc, vc, qo, indptr, indices
+
+
+def pin_prefill_fp8_sdpa(o):
+    """Chunked prefill over E4M3 pools at scales that are not powers of two:
+    torch SDPA (float64) with an explicit bottom-right causal mask on the
+    values scale * torch's float8_e4m3fn value, contiguous slots, to 1e-12."""
+    rng = np.random.default_rng(54)
+    for (Hq, Hkv, D, cached, chunks, k_scale, v_scale) in [(8, 2, 16, [5, 0, 3], [4, 3, 1], 0.37, 1.3),
+                                                           (4, 1, 32, [9], [6], 2.5, 0.07)]:
+        q, kc, vc, qo, indptr, indices = _fp8_prefill_case(rng, cached, chunks, Hq, Hkv, D)
+        scale = workloads.softmax_scale(D)
+        out, lse = o.prefill_fp8(q, kc, vc, qo, indptr, indices, scale, k_scale, v_scale, Hkv)
+        kf = torch.from_numpy(kc.copy()).view(torch.float8_e4m3fn).to(torch.float64) * _f32(k_scale)
+        vf = torch.from_numpy(vc.copy()).view(torch.float8_e4m3fn).to(torch.float64) * _f32(v_scale)
+        for b, (P, C) in enumerate(zip(cached, chunks)):
+            ids = torch.from_numpy(indices[indptr[b]:indptr[b + 1]].astype(np.int64))
+            qt = torch.from_numpy(_widen(q[qo[b]:qo[b + 1]])).permute(1, 0, 2)[None]
+            kt = kf[ids].permute(1, 0, 2)[None].contiguous()
+            vt = vf[ids].permute(1, 0, 2)[None].contiguous()
+            mask = torch.ones(C, P + C, dtype=torch.bool).tril(diagonal=P)
+            ref = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=_f32(scale),
+                                                 enable_gqa=True)
+            err = np.abs(out[qo[b]:qo[b + 1]] - ref[0].permute(1, 0, 2).numpy()).max()
+            assert err < TOL, f"fp8 prefill vs sdpa {err}"
+
+
+def pin_prefill_fp8_rows_are_decodes(o):
+    """Chunk row i over E4M3 pools equals the fp8 decode over the list's first
+    P+i+1 entries (scattered slots, empty cached prefixes included)."""
+    rng = np.random.default_rng(55)
+    Hq, Hkv, D = 8, 2, 16
+    q, kc, vc, qo, indptr, indices = _fp8_prefill_case(rng, [6, 0, 11], [5, 2, 1], Hq, Hkv, D, spare=9)
+    indices = rng.permutation(kc.shape[0])[:indices.size].astype(np.int32)
+    scale, k_scale, v_scale = workloads.softmax_scale(D), 0.37, 1.3
+    out, lse = o.prefill_fp8(q, kc, vc, qo, indptr, indices, scale, k_scale, v_scale, Hkv)
+    for b in range(3):
+        L = indptr[b + 1] - indptr[b]
+        C = qo[b + 1] - qo[b]
+        for i in range(C):
+            n = L - C + i + 1
+            ref, ref_lse = o.decode_fp8(q[qo[b] + i][None], kc, vc, np.array([0, n], np.int32),
+                                        indices[indptr[b]:indptr[b] + n], scale, k_scale, v_scale, Hkv)
+            assert np.abs(out[qo[b] + i] - ref[0]).max() < TOL, "fp8 prefill row vs fp8 decode"
+            assert np.abs(lse[qo[b] + i] - ref_lse[0]).max() < TOL
+
+
+def pin_prefill_fp8_unit_scales_equal_bf16(o):
+    """With unit scales the fp8 prefill equals the bf16 prefill over pools
+    that hold the codes' values."""
+    rng = np.random.default_rng(56)
+    q, kc, vc, qo, indptr, indices = _fp8_prefill_case(rng, [7, 30, 2], [3, 5, 2], 8, 2, 16)
+    scale = workloads.softmax_scale(16)
+    out8, lse8 = o.prefill_fp8(q, kc, vc, qo, indptr, indices, scale, 1.0, 1.0, 2)
+    out, lse = o.prefill(q, o.e4m3_to_bf16(kc), o.e4m3_to_bf16(vc), qo, indptr, indices, scale, 2)
+    assert np.abs(out8 - out).max() < TOL and np.abs(lse8 - lse).max() < TOL, "fp8 vs bf16 prefill"
+
+
 # ----------------------------------------------------------------------------
 # Writing 8-bit pools: the E4M3 encoder and the append's rows
 # ----------------------------------------------------------------------------
@@ -655,4 +719,5 @@ ALL_PINS = [
     pin_decode_fp8_single_token, pin_decode_fp8_unit_scales_equal_bf16,
     pin_e4m3_encode_round_trip, pin_e4m3_encode_matches_torch, pin_e4m3_encode_exact_nearest,
     pin_e4m3_encode_saturation_and_specials, pin_e4m3_encode_scale, pin_append_e4m3_rows,
+    pin_prefill_fp8_sdpa, pin_prefill_fp8_rows_are_decodes, pin_prefill_fp8_unit_scales_equal_bf16,
 ]

@@ -77,6 +77,12 @@ MUTANTS = [
     ("e4m3_encode_scale_multiplies", [("e4m3_encode(x[i] / (double)scale)", "e4m3_encode(x[i] * (double)scale)", None)]),
     ("e4m3_encode_float_quotient", [("e4m3_encode(x[i] / (double)scale)",
                                      "e4m3_encode((double)(float)(x[i] / (double)scale))", None)]),
+    ("fp8_prefill_window_one_short", [("- c_len + pos_in_chunk + 1;", "- c_len + pos_in_chunk;", None)]),
+    ("fp8_prefill_top_left", [("((int64_t)kv_indptr[b + 1] - kv_indptr[b]) - c_len + pos_in_chunk + 1;",
+                               "pos_in_chunk + 1;", None)]),
+    ("fp8_prefill_gqa_modulo", [("head / (Hq / Hkv),", "head % Hkv,", None)]),
+    ("fp8_prefill_scales_swapped", [("(double)k_scale, (double)v_scale, w, out + row * D",
+                                     "(double)v_scale, (double)k_scale, w, out + row * D", None)]),
     ("rope_position_off_by_one", [("(double)positions[t] * inv_freq", "(double)(positions[t] + 1) * inv_freq", None)]),
 ]
 
