@@ -184,23 +184,25 @@ def prefill_flops(spec, qo_indptr, kv_indptr) -> int:
     return total * spec.num_qo_heads * 4 * spec.head_dim
 
 
-def prefill_bytes(spec, qo_indptr, kv_indices) -> int:
+def prefill_bytes(spec, qo_indptr, kv_indices, kv_elem_bytes: int = 2) -> int:
     import numpy as np
     T = int(qo_indptr[-1])
     unique = int(np.unique(kv_indices).size)
     Hq, Hkv, D = spec.num_qo_heads, spec.num_kv_heads, spec.head_dim
-    return unique * Hkv * D * 2 * 2 + int(kv_indices.size) * 4 + T * Hq * D * (2 + 4)
+    return unique * Hkv * D * kv_elem_bytes * 2 + int(kv_indices.size) * 4 + T * Hq * D * (2 + 4)
 
 
-def cpu_baseline_prefill(case, spec, flops_per_row_entry, seconds):
+def cpu_baseline_prefill(case, spec, flops_per_row_entry, seconds, fp8=False):
     """fp64 oracle on a bounded sample of rows: the last chunk token of every
-    request, all heads (the rows that see the most entries), repeated."""
+    request, all heads (the rows that see the most entries), repeated (over
+    the E4M3 codes with fp8)."""
     import numpy as np
 
     import oracle
     import workloads as W
     ref = oracle.load()
-    qb, kb, vb = W.bits(case.q), W.bits(case.k_pool), W.bits(case.v_pool)
+    qb = W.bits(case.q)
+    kb, vb = (W.codes(case.k_pool), W.codes(case.v_pool)) if fp8 else (W.bits(case.k_pool), W.bits(case.v_pool))
     Hq = spec.num_qo_heads
     rows = []
     entries = 0
@@ -213,8 +215,12 @@ def cpu_baseline_prefill(case, spec, flops_per_row_entry, seconds):
     reps = 0
     t0 = time.perf_counter()
     while True:
-        ref.prefill(qb, kb, vb, case.qo_indptr, case.kv_indptr, case.kv_indices, case.sm_scale,
-                    spec.num_kv_heads, sel=rows)
+        if fp8:
+            ref.prefill_fp8(qb, kb, vb, case.qo_indptr, case.kv_indptr, case.kv_indices, case.sm_scale,
+                            W.FP8_K_SCALE, W.FP8_V_SCALE, spec.num_kv_heads, sel=rows)
+        else:
+            ref.prefill(qb, kb, vb, case.qo_indptr, case.kv_indptr, case.kv_indices, case.sm_scale,
+                        spec.num_kv_heads, sel=rows)
         reps += 1
         if time.perf_counter() - t0 >= seconds:
             break
@@ -245,9 +251,14 @@ def run_prefill_bench(args):
     case = W.make_prefill_case(spec, dev)
     T = int(case.qo_indptr[-1])
     B, Hq, Hkv, D = spec.batch, spec.num_qo_heads, spec.num_kv_heads, spec.head_dim
+    fp8 = args.kv == "fp8"
+    if fp8:
+        # the same workload over pools of E4M3 codes (N(0,1) / scale, nearest even)
+        case.k_pool = case.v_pool = None
+        case.k_pool, case.v_pool = W.make_pools_e4m3(spec.num_slots, Hkv, D, W.layer_seed(spec.seed, 0), dev)
     idx = torch.as_tensor(case.kv_indices, device=dev)
     flops = prefill_flops(spec, case.qo_indptr, case.kv_indptr)
-    nbytes = prefill_bytes(spec, case.qo_indptr, case.kv_indices)
+    nbytes = prefill_bytes(spec, case.qo_indptr, case.kv_indices, 1 if fp8 else 2)
     outs = [torch.empty((T, Hq, D), dtype=torch.float32, device=dev) for _ in range(layers)]
     plan = pa.Plan(B, int(case.kv_indptr[-1]), Hq, Hkv, D, max_q_total=T)
     stream = torch.cuda.current_stream(dev)
@@ -255,8 +266,12 @@ def run_prefill_bench(args):
     def step():
         plan.plan(case.kv_indptr, case.qo_indptr, flags=args.flags, stream=stream)
         for layer in range(layers):
-            plan.prefill(case.q, case.k_pool, case.v_pool, idx, case.sm_scale, outs[layer],
-                         stream=stream)
+            if fp8:
+                plan.prefill_fp8(case.q, case.k_pool, case.v_pool, idx, case.sm_scale, W.FP8_K_SCALE,
+                                 W.FP8_V_SCALE, outs[layer], stream=stream)
+            else:
+                plan.prefill(case.q, case.k_pool, case.v_pool, idx, case.sm_scale, outs[layer],
+                             stream=stream)
 
     gc.collect()
     gc.disable()   # no collector pauses while steps are issued (see the decode bench)
@@ -294,10 +309,10 @@ def run_prefill_bench(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8-e4m3 KV widened to bf16/fp16 MFMA" if fp8 else "bf16",
         "data": "synthetic",
         "config": {
-            "workload": spec.name,
+            "workload": spec.name + ("_fp8kv" if fp8 else ""),
             "batch": B, "num_qo_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
             "cached_len": spec.cached_len, "chunk_len": spec.chunk_len,
             "layers_per_step": layers, "pool_slots": spec.num_slots, "plan_flags": args.flags,
@@ -314,15 +329,16 @@ def run_prefill_bench(args):
             "peak": BF16_MFMA_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4),
-            "traffic": traffic_per_launch(PREFILL_COUNTERS.get(spec.name), PREFILL_SOURCES),
-            "kernel": f"prefill_kernel<{D},{Hq // Hkv}> (pa_prefill_chunk_run)",
+            "traffic": None if fp8 else traffic_per_launch(PREFILL_COUNTERS.get(spec.name), PREFILL_SOURCES),
+            "kernel": (f"prefill_kernel<{D},{Hq // Hkv},KV8> (pa_prefill_chunk_run_fp8)" if fp8
+                       else f"prefill_kernel<{D},{Hq // Hkv}> (pa_prefill_chunk_run)"),
             "kernel_avg_us": round(kernel_avg_ms * 1e3, 2),
         },
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
         log(f"cpu baseline: fp64 oracle on sampled rows for ~{args.cpu_seconds:.0f} s")
-        result["cpu_baseline"] = cpu_baseline_prefill(case, spec, 4 * D, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline_prefill(case, spec, 4 * D, args.cpu_seconds, fp8)
     plan.close()
     print(json.dumps(result), flush=True)
 
@@ -452,7 +468,7 @@ def main():
                     choices=["batch64", "batch64_4k8k", "single_request", "batch8", "hd256", "system_prompt",
                              "prefill_chunk512", "prefill_chunk64", "append", "copy"])
     ap.add_argument("--kv", default="bf16", choices=["bf16", "fp8"],
-                    help="decode and append: pool element type (fp8 = OCP E4M3 codes with per-pool scales)")
+                    help="decode, prefill and append: pool element type (fp8 = OCP E4M3 codes with per-pool scales)")
     ap.add_argument("--graph", action="store_true", default=True,
                     help="decode: replay each step's layer runs from a captured HIP graph (the default)")
     ap.add_argument("--eager", dest="graph", action="store_false",

@@ -246,6 +246,21 @@ pa_status pa_prefill_chunk_run(const pa_plan_t *plan, const void *q, const void 
                                float *lse, pa_stream_t stream);
 
 /*
+ * pa_prefill_chunk_run_fp8: pa_prefill_chunk_run over 8-bit pools (the
+ * pools of pa_decode_run_fp8: OCP FP8 E4M3 codes, 1 byte per element, row
+ * values k_scale * code and v_scale * code).  Same plan (any prefill plan;
+ * PA_PLAN_KV_FP8 is not needed), arguments, output and errors as
+ * pa_prefill_chunk_run, plus PA_ERR_INVALID_ARG for a non-finite scale.  The
+ * codes are widened exactly on the way into the matrix cores (every E4M3
+ * value is a bf16 and an fp16 value); a NaN code in a row a query token sees
+ * makes that token's results NaN.
+ */
+pa_status pa_prefill_chunk_run_fp8(const pa_plan_t *plan, const void *q, const void *k_pool,
+                                   const void *v_pool, int64_t num_slots, int64_t slot_stride,
+                                   const int32_t *kv_indices, float sm_scale, float k_scale,
+                                   float v_scale, float *out, float *lse, pa_stream_t stream);
+
+/*
  * pa_decode_run_noalloc: pa_decode_run without a plan object and without any
  * allocation, for callers that cannot allocate device memory (code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc).  The

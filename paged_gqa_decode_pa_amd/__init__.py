@@ -129,6 +129,8 @@ def _load() -> ctypes.CDLL:
     lib.pa_plan_host_timing.restype = ctypes.c_int
     lib.pa_decode_run_fp8.argtypes = [vp, vp, vp, vp, i64, i64, vp, f32, f32, f32, vp, vp, vp]
     lib.pa_decode_run_fp8.restype = ctypes.c_int
+    lib.pa_prefill_chunk_run_fp8.argtypes = [vp, vp, vp, vp, i64, i64, vp, f32, f32, f32, vp, vp, vp]
+    lib.pa_prefill_chunk_run_fp8.restype = ctypes.c_int
     lib.pa_kv_append.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, vp, vp, i64, i64, vp]
     lib.pa_kv_append.restype = ctypes.c_int
     lib.pa_kv_append_fp8.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, f32, f32, vp, vp, i64, i64, vp]
@@ -308,9 +310,8 @@ def pa_decode_run(plan, q, k_pool, v_pool, kv_indices, sm_scale, out, lse=None,
          out, lse, num_slots, slot_stride, stream)
 
 
-def pa_decode_run_fp8(plan, q, k_pool, v_pool, kv_indices, sm_scale, k_scale, v_scale, out, lse=None,
-                      num_slots=None, slot_stride=None, stream=None) -> None:
-    """Decode over E4M3 pools (torch.float8_e4m3fn or uint8 [slots, Hkv, D])."""
+def _run_fp8(fn, where, plan, q, k_pool, v_pool, kv_indices, sm_scale, k_scale, v_scale, out, lse,
+             num_slots, slot_stride, stream):
     head_dim = q.shape[-1]
     for name, t in (("k_pool", k_pool), ("v_pool", v_pool)):
         if t.dtype not in (torch.float8_e4m3fn, torch.uint8):
@@ -326,11 +327,18 @@ def pa_decode_run_fp8(plan, q, k_pool, v_pool, kv_indices, sm_scale, k_scale, v_
     if not q.is_contiguous():
         raise ValueError("q must be contiguous")
     _check_run_shapes(plan, q, k_pool, v_pool, kv_indices, out, lse, num_slots)
-    _check(_lib.pa_decode_run_fp8(plan, _dev_ptr(q, "q", torch.bfloat16), _dev_ptr(k_pool, "k_pool"),
-                                  _dev_ptr(v_pool, "v_pool"), int(num_slots), int(slot_stride),
-                                  _dev_ptr(kv_indices, "kv_indices"), float(sm_scale), float(k_scale),
-                                  float(v_scale), _dev_ptr(out, "out"), _dev_ptr(lse, "lse"),
-                                  _stream(stream)), "pa_decode_run_fp8")
+    _check(fn(plan, _dev_ptr(q, "q", torch.bfloat16), _dev_ptr(k_pool, "k_pool"),
+              _dev_ptr(v_pool, "v_pool"), int(num_slots), int(slot_stride),
+              _dev_ptr(kv_indices, "kv_indices"), float(sm_scale), float(k_scale),
+              float(v_scale), _dev_ptr(out, "out"), _dev_ptr(lse, "lse"),
+              _stream(stream)), where)
+
+
+def pa_decode_run_fp8(plan, q, k_pool, v_pool, kv_indices, sm_scale, k_scale, v_scale, out, lse=None,
+                      num_slots=None, slot_stride=None, stream=None) -> None:
+    """Decode over E4M3 pools (torch.float8_e4m3fn or uint8 [slots, Hkv, D])."""
+    _run_fp8(_lib.pa_decode_run_fp8, "pa_decode_run_fp8", plan, q, k_pool, v_pool, kv_indices, sm_scale,
+             k_scale, v_scale, out, lse, num_slots, slot_stride, stream)
 
 
 def pa_decode_run_noalloc(q, k_pool, v_pool, kv_indptr, kv_indices, sm_scale, out, lse=None,
@@ -372,6 +380,13 @@ def pa_prefill_chunk_run(plan, q, k_pool, v_pool, kv_indices, sm_scale, out, lse
                          num_slots=None, slot_stride=None, stream=None) -> None:
     _run(_lib.pa_prefill_chunk_run, "pa_prefill_chunk_run", plan, q, k_pool, v_pool,
          kv_indices, sm_scale, out, lse, num_slots, slot_stride, stream)
+
+
+def pa_prefill_chunk_run_fp8(plan, q, k_pool, v_pool, kv_indices, sm_scale, k_scale, v_scale, out,
+                             lse=None, num_slots=None, slot_stride=None, stream=None) -> None:
+    """Chunked prefill over E4M3 pools (torch.float8_e4m3fn or uint8 [slots, Hkv, D])."""
+    _run_fp8(_lib.pa_prefill_chunk_run_fp8, "pa_prefill_chunk_run_fp8", plan, q, k_pool, v_pool, kv_indices,
+             sm_scale, k_scale, v_scale, out, lse, num_slots, slot_stride, stream)
 
 
 def _append_shapes(k_new, v_new, out_loc, positions, q):
@@ -603,6 +618,12 @@ class Plan:
     def prefill(self, q, k_pool, v_pool, kv_indices, sm_scale, out, lse=None, **kw) -> None:
         self._debug_check(kv_indices, k_pool, kw)
         pa_prefill_chunk_run(self.handle, q, k_pool, v_pool, kv_indices, sm_scale, out, lse, **kw)
+
+    def prefill_fp8(self, q, k_pool, v_pool, kv_indices, sm_scale, k_scale, v_scale, out, lse=None,
+                    **kw) -> None:
+        self._debug_check(kv_indices, k_pool, kw)
+        pa_prefill_chunk_run_fp8(self.handle, q, k_pool, v_pool, kv_indices, sm_scale, k_scale, v_scale, out,
+                                 lse, **kw)
 
     def close(self) -> None:
         if self.handle is not None and self.handle.value:

@@ -944,6 +944,33 @@ pa_status pa_prefill_chunk_run(const pa_plan_t *p, const void *q, const void *k_
     return PA_OK;
 }
 
+pa_status pa_prefill_chunk_run_fp8(const pa_plan_t *p, const void *q, const void *k_pool,
+                                   const void *v_pool, int64_t num_slots, int64_t slot_stride,
+                                   const int32_t *kv_indices, float sm_scale, float k_scale,
+                                   float v_scale, float *out, float *lse, pa_stream_t stream) {
+    pa::DecodeLaunch l;
+    pa_status st = prepare_run(p, pa::PlanMode::kPrefill, q, k_pool, v_pool, num_slots,
+                               slot_stride, kv_indices, sm_scale, out, lse, &l);
+    if (st != PA_OK)
+        return st;
+    if (!std::isfinite(k_scale) || !std::isfinite(v_scale))
+        return fail(PA_ERR_INVALID_ARG, "k_scale and v_scale must be finite");
+    l.kv_fp8 = true;
+    l.k_scale = k_scale;
+    l.v_scale = v_scale;
+    hipError_t e = profile_mark(p, (hipStream_t)stream, false);
+    if (e != hipSuccess)
+        return hip_fail(e, "profile event");
+    int rc = pa::launch_prefill(l, stream);
+    if (rc == (int)hipErrorNotSupported)
+        return fail(PA_ERR_UNSUPPORTED, "prefill kernel not available in this build");
+    if (rc != 0)
+        return hip_fail((hipError_t)rc, "prefill kernel launch");
+    if ((e = profile_mark(p, (hipStream_t)stream, true)) != hipSuccess)
+        return hip_fail(e, "profile event");
+    return PA_OK;
+}
+
 pa_status pa_decode_run_noalloc(const void *q, const void *k_pool, const void *v_pool,
                                 int64_t num_slots, int64_t slot_stride, const int32_t *kv_indptr,
                                 const int32_t *kv_indices, int32_t batch, int32_t num_qo_heads,

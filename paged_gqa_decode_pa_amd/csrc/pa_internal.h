@@ -181,7 +181,7 @@ struct DecodeLaunch {
     int32_t num_qo_heads;
     int32_t num_kv_heads;
     int32_t head_dim;
-    bool kv_fp8 = false;             // pools of OCP FP8 E4M3 codes (decode only)
+    bool kv_fp8 = false;             // pools of OCP FP8 E4M3 codes (decode and prefill kernels)
     float k_scale = 1.f, v_scale = 1.f;   // their per-pool scales
     uint64_t *wg_clock = nullptr;    // decode: per-workgroup run-time record, or null
 };

@@ -40,6 +40,12 @@
 // final rows; the parts of a cut range publish normalised rows and their
 // log2-sum-exp, and the last part to finish merges them (no second launch);
 // cascade prefix units write partial rows that the decode kernel merges.
+//
+// Pools of OCP FP8 E4M3 codes with one scale per pool (quantised KV is on the
+// Agent-Infer page's roadmap, section "模型支持与发展路线图") take the same
+// path: a staging thread gathers 8 codes (8 bytes) of a row instead of 8 bf16
+// values and widens them exactly, K to bf16 and V to fp16, into the same LDS
+// tiles; k_scale joins the score scale and v_scale multiplies the output rows.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -164,6 +170,23 @@ __device__ __forceinline__ f32x2_t load_coherent2(__amdgpu_buffer_rsrc_t r, uint
     return __builtin_bit_cast(f32x2_t, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kCoherentPolicy));
 }
 
+// Eight E4M3 codes (one 8-byte chunk of a row) widened exactly: every E4M3
+// value is a bf16 value and an fp16 value (3 mantissa bits, exponents
+// 2^-9 .. 2^8), so the K operand goes to the bf16 matrix core and the V
+// operand to the fp16 one unchanged; element order is kept.
+__device__ __forceinline__ u32x4_t e4m3x8_to_bf16(u32x2_t c) {
+    return u32x4_t{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[0], 1.0f, false)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[0], 1.0f, true)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[1], 1.0f, false)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[1], 1.0f, true))};
+}
+__device__ __forceinline__ u32x4_t e4m3x8_to_f16(u32x2_t c) {
+    return u32x4_t{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c[0], 1.0f, false)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c[0], 1.0f, true)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c[1], 1.0f, false)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c[1], 1.0f, true))};
+}
+
 __device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -171,7 +194,10 @@ __device__ __forceinline__ f32x16_t mfma_f16(f16x8_t a, f16x8_t b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
-template <int D, int G, bool WIDE>
+// KV8: pools of OCP FP8 E4M3 codes (one byte per element); the scores carry
+// k_scale inside scale_log2 and the outputs are multiplied by out_scale
+// (v_scale); bf16 pools pass out_scale = 1 and never use it.
+template <int D, int G, bool WIDE, bool KV8>
 __global__ __launch_bounds__(64 * prefill_waves<D>())
 __attribute__((amdgpu_waves_per_eu(prefill_waves_per_simd<D>(), prefill_waves_per_simd<D>()))) void
 prefill_kernel(const int32_t *__restrict__ wg_offsets, const pa_work_unit *__restrict__ units,
@@ -180,8 +206,11 @@ prefill_kernel(const int32_t *__restrict__ wg_offsets, const pa_work_unit *__res
                const int32_t *__restrict__ kv_indices, float scale_log2, float *__restrict__ out,
                float *__restrict__ lse, float *__restrict__ part_o, float *__restrict__ part_lse,
                const pa_merge_unit *__restrict__ merges, int32_t *__restrict__ arrivals,
-               int32_t num_qo_heads) {
+               int32_t num_qo_heads, float out_scale) {
     using Geo = PrefillGeo<D>;
+    // a staging thread's 8 elements of a row: 16 bytes of bf16 or 8 of codes
+    using Chunk = std::conditional_t<KV8, u32x2_t, u32x4_t>;
+    constexpr int EB = KV8 ? 1 : 2;   // bytes per pool element
     constexpr int KT = Geo::KT, KROW = Geo::KROW, VROW = Geo::VROW, STAGE = Geo::STAGE;
     constexpr int TPR = Geo::TPR, RPP = Geo::RPP, PASSES = Geo::PASSES;
     constexpr int DS = Geo::DS, DB = Geo::DB, SB = Geo::SB, KS = Geo::KS;
@@ -258,7 +287,7 @@ prefill_kernel(const int32_t *__restrict__ wg_offsets, const pa_work_unit *__res
         // it here keeps the tile loop from waiting on every load in flight
         wait_vector_memory();
 
-        const uint64_t head_off = (uint64_t)unit.kv_head * D * 2 + chunk * 16;
+        const uint64_t head_off = (uint64_t)unit.kv_head * D * EB + chunk * 8 * EB;
         // row limit: the last list entry (absolute offset) this row may see
         const int32_t row_last = min(kv1 - 1, unit.diag + tt);
         const int32_t unit_last = min(kv1 - 1, unit.diag);  // smallest row limit of the unit
@@ -277,7 +306,7 @@ prefill_kernel(const int32_t *__restrict__ wg_offsets, const pa_work_unit *__res
         auto run_unit = [&](const int vshift, int *retry) -> bool {
             __syncthreads();  // the previous unit's (or pass's) last tile is no longer read
 
-            u32x4_t kreg[PASSES], vreg[PASSES];
+            Chunk kreg[PASSES], vreg[PASSES];
             auto load_rows = [&]() {
 #pragma unroll
                 for (int p = 0; p < PASSES; p++) {
@@ -285,39 +314,49 @@ prefill_kernel(const int32_t *__restrict__ wg_offsets, const pa_work_unit *__res
                     // checks) take a 32-bit offset, shared by the K and V loads
                     if constexpr (WIDE) {
                         const uint64_t off = (uint64_t)(uint32_t)slot[p] * stride_bytes + head_off;
-                        kreg[p] = *reinterpret_cast<const u32x4_t *>(k_pool + off);
-                        vreg[p] = *reinterpret_cast<const u32x4_t *>(v_pool + off);
+                        kreg[p] = *reinterpret_cast<const Chunk *>(k_pool + off);
+                        vreg[p] = *reinterpret_cast<const Chunk *>(v_pool + off);
                     } else {
                         const uint32_t off =
                             __umul24((uint32_t)slot[p], (uint32_t)stride_bytes) + (uint32_t)head_off;
-                        kreg[p] = *reinterpret_cast<const u32x4_t *>(k_pool + off);
-                        vreg[p] = *reinterpret_cast<const u32x4_t *>(v_pool + off);
+                        kreg[p] = *reinterpret_cast<const Chunk *>(k_pool + off);
+                        vreg[p] = *reinterpret_cast<const Chunk *>(v_pool + off);
                     }
                 }
             };
             // K rows as they are (bf16), V rows converted to fp16 (one uniform
-            // branch for the whole stage: the scaled form is the rare retry)
+            // branch for the whole stage: the scaled form is the rare retry);
+            // E4M3 codes widened to the same two forms
             auto store_rows = [&](int buf) {
                 char *st = smem + buf * STAGE;
-                u32x4_t v[PASSES];
-                if (vshift == 0) {
+                if constexpr (KV8) {
 #pragma unroll
-                    for (int p = 0; p < PASSES; p++)
-#pragma unroll
-                        for (int j = 0; j < 4; j++)
-                            v[p][j] = bf16_pair_to_f16(vreg[p][j]);
+                    for (int p = 0; p < PASSES; p++) {
+                        const int r = p * RPP + srow;
+                        *reinterpret_cast<u32x4_t *>(st + r * KROW + chunk * 16) = e4m3x8_to_bf16(kreg[p]);
+                        *reinterpret_cast<u32x4_t *>(st + KT * KROW + r * VROW + chunk * 16) = e4m3x8_to_f16(vreg[p]);
+                    }
                 } else {
+                    u32x4_t v[PASSES];
+                    if (vshift == 0) {
 #pragma unroll
-                    for (int p = 0; p < PASSES; p++)
+                        for (int p = 0; p < PASSES; p++)
 #pragma unroll
-                        for (int j = 0; j < 4; j++)
-                            v[p][j] = bf16_pair_to_f16_scaled(vreg[p][j], vshift);
-                }
+                            for (int j = 0; j < 4; j++)
+                                v[p][j] = bf16_pair_to_f16(vreg[p][j]);
+                    } else {
 #pragma unroll
-                for (int p = 0; p < PASSES; p++) {
-                    const int r = p * RPP + srow;
-                    *reinterpret_cast<u32x4_t *>(st + r * KROW + chunk * 16) = kreg[p];
-                    *reinterpret_cast<u32x4_t *>(st + KT * KROW + r * VROW + chunk * 16) = v[p];
+                        for (int p = 0; p < PASSES; p++)
+#pragma unroll
+                            for (int j = 0; j < 4; j++)
+                                v[p][j] = bf16_pair_to_f16_scaled(vreg[p][j], vshift);
+                    }
+#pragma unroll
+                    for (int p = 0; p < PASSES; p++) {
+                        const int r = p * RPP + srow;
+                        *reinterpret_cast<u32x4_t *>(st + r * KROW + chunk * 16) = kreg[p];
+                        *reinterpret_cast<u32x4_t *>(st + KT * KROW + r * VROW + chunk * 16) = v[p];
+                    }
                 }
             };
 
@@ -455,52 +494,56 @@ prefill_kernel(const int32_t *__restrict__ wg_offsets, const pa_work_unit *__res
             for (int32_t it = n_open; it < n_tiles; it++)
                 step(it, std::true_type{});
 
-            if (vshift == 0) {
-                // a non-finite O or row sum anywhere in the workgroup?
-                float chk = l;
+            // (E4M3 values stay below 448: fp16 holds every V, so a non-finite
+            // result of an 8-bit pool is the right one and needs no check)
+            if constexpr (!KV8) {
+                if (vshift == 0) {
+                    // a non-finite O or row sum anywhere in the workgroup?
+                    float chk = l;
 #pragma unroll
-                for (int db = 0; db < DB; db++)
+                    for (int db = 0; db < DB; db++)
 #pragma unroll
-                    for (int i = 0; i < 16; i++)
-                        chk += o[db][i];
-                const bool bad = !(fabsf(chk) <= 3.4028235e38f);
-                if (lane == 0)
-                    flag_lds[wave] = __builtin_amdgcn_ballot_w64(bad) != 0 ? 1.f : 0.f;
-                __syncthreads();
-                float any_bad = 0.f;
-#pragma unroll
-                for (int w = 0; w < WAVES; w++)
-                    any_bad += flag_lds[w];
-                if (any_bad != 0.f) {
-                    // the unit's largest finite |V| (read again: a rare path)
-                    float vm = 0.f;
-                    for (int32_t tile = 0; tile < n_tiles; tile++) {
-                        load_slots(tile);
-                        load_rows();
-#pragma unroll
-                        for (int p = 0; p < PASSES; p++)
-#pragma unroll
-                            for (int j = 0; j < 4; j++) {
-                                const float a = fabsf(__uint_as_float(vreg[p][j] << 16));
-                                const float b = fabsf(__uint_as_float(vreg[p][j] & 0xffff0000u));
-                                vm = fmaxf(vm, fmaxf(a <= 3.4028235e38f ? a : 0.f, b <= 3.4028235e38f ? b : 0.f));
-                            }
-                    }
-#pragma unroll
-                    for (int off = 32; off > 0; off >>= 1)
-                        vm = fmaxf(vm, __shfl_xor(vm, off));
-                    __syncthreads();   // every wave has read the flags
+                        for (int i = 0; i < 16; i++)
+                            chk += o[db][i];
+                    const bool bad = !(fabsf(chk) <= 3.4028235e38f);
                     if (lane == 0)
-                        flag_lds[wave] = vm;
+                        flag_lds[wave] = __builtin_amdgcn_ballot_w64(bad) != 0 ? 1.f : 0.f;
                     __syncthreads();
-                    float wmax = 0.f;
+                    float any_bad = 0.f;
 #pragma unroll
                     for (int w = 0; w < WAVES; w++)
-                        wmax = fmaxf(wmax, flag_lds[w]);
-                    if (wmax >= kF16Overflow) {
-                        // 2^e <= wmax < 2^(e+1): wmax * 2^-(e-14) < 2^15
-                        *retry = __builtin_amdgcn_readfirstlane((int)((__float_as_uint(wmax) >> 23) & 0xff) - 127 - 14);
-                        return true;
+                        any_bad += flag_lds[w];
+                    if (any_bad != 0.f) {
+                        // the unit's largest finite |V| (read again: a rare path)
+                        float vm = 0.f;
+                        for (int32_t tile = 0; tile < n_tiles; tile++) {
+                            load_slots(tile);
+                            load_rows();
+#pragma unroll
+                            for (int p = 0; p < PASSES; p++)
+#pragma unroll
+                                for (int j = 0; j < 4; j++) {
+                                    const float a = fabsf(__uint_as_float(vreg[p][j] << 16));
+                                    const float b = fabsf(__uint_as_float(vreg[p][j] & 0xffff0000u));
+                                    vm = fmaxf(vm, fmaxf(a <= 3.4028235e38f ? a : 0.f, b <= 3.4028235e38f ? b : 0.f));
+                                }
+                        }
+#pragma unroll
+                        for (int off = 32; off > 0; off >>= 1)
+                            vm = fmaxf(vm, __shfl_xor(vm, off));
+                        __syncthreads();   // every wave has read the flags
+                        if (lane == 0)
+                            flag_lds[wave] = vm;
+                        __syncthreads();
+                        float wmax = 0.f;
+#pragma unroll
+                        for (int w = 0; w < WAVES; w++)
+                            wmax = fmaxf(wmax, flag_lds[w]);
+                        if (wmax >= kF16Overflow) {
+                            // 2^e <= wmax < 2^(e+1): wmax * 2^-(e-14) < 2^15
+                            *retry = __builtin_amdgcn_readfirstlane((int)((__float_as_uint(wmax) >> 23) & 0xff) - 127 - 14);
+                            return true;
+                        }
                     }
                 }
             }
@@ -526,7 +569,7 @@ prefill_kernel(const int32_t *__restrict__ wg_offsets, const pa_work_unit *__res
                 const int64_t orow = (int64_t)(unit.q_begin + tt) * num_qo_heads + unit.kv_head * G + g;
                 if (lse && half == 0)
                     lse[orow] = lse2 * kLn2;
-                write_row(out + orow * D, inv);
+                write_row(out + orow * D, KV8 ? inv * out_scale : inv);
                 return false;
             }
             if (unit.part_stride > 0) {
@@ -538,7 +581,7 @@ prefill_kernel(const int32_t *__restrict__ wg_offsets, const pa_work_unit *__res
                 const int64_t prow = ((int64_t)unit.partial + (int64_t)tt * unit.part_stride) * G + g;
                 if (half == 0)
                     part_lse[prow] = lse2;
-                write_row(part_o + prow * D, inv);
+                write_row(part_o + prow * D, KV8 ? inv * out_scale : inv);
                 return false;
             }
 
@@ -644,7 +687,9 @@ prefill_kernel(const int32_t *__restrict__ wg_offsets, const pa_work_unit *__res
             const int64_t orow = (int64_t)(unit.q_begin + tt) * num_qo_heads + unit.kv_head * G + g;
             if (lse && half == 0)
                 lse[orow] = wsum > 0.f ? (M + fast_log2(wsum)) * kLn2 : -INFINITY;
-            write_row(out + orow * D, wsum > 0.f ? 1.f / wsum : 0.f);
+            // (8-bit pools: the parts hold rows of code values, below 448 and
+            // so within fp16; v_scale is applied here, after the merge)
+            write_row(out + orow * D, wsum > 0.f ? (KV8 ? out_scale / wsum : 1.f / wsum) : 0.f);
             return false;
         };
         // one call site (a loop) keeps the pass inlined once; vshift is
@@ -655,21 +700,29 @@ prefill_kernel(const int32_t *__restrict__ wg_offsets, const pa_work_unit *__res
     }
 }
 
+template <int D, int G, bool KV8>
+int launch_prefill_dgk(const DecodeLaunch &l, hipStream_t stream) {
+    const uint64_t stride_bytes = (uint64_t)l.slot_stride * (KV8 ? 1 : 2);
+    const bool wide = stride_bytes >= (1u << 24) || !row_offsets_fit_32(l.num_slots, (uint32_t)stride_bytes);
+    // 8-bit pools: K = k_scale * code enters the scores, V = v_scale * code the output
+    const float scale_log2 = (KV8 ? l.sm_scale * l.k_scale : l.sm_scale) * kLog2e;
+    const float out_scale = KV8 ? l.v_scale : 1.0f;
+    if (wide)
+        hipLaunchKernelGGL((prefill_kernel<D, G, true, KV8>), dim3(l.n_workgroups), dim3(PrefillGeo<D>::THREADS), 0,
+                           stream, l.wg_offsets, l.units, (const uint16_t *)l.q, (const char *)l.k_pool,
+                           (const char *)l.v_pool, stride_bytes, l.kv_indices, scale_log2, l.out, l.lse,
+                           l.partial_o, l.partial_lse, l.merges, l.arrivals, l.num_qo_heads, out_scale);
+    else
+        hipLaunchKernelGGL((prefill_kernel<D, G, false, KV8>), dim3(l.n_workgroups), dim3(PrefillGeo<D>::THREADS), 0,
+                           stream, l.wg_offsets, l.units, (const uint16_t *)l.q, (const char *)l.k_pool,
+                           (const char *)l.v_pool, stride_bytes, l.kv_indices, scale_log2, l.out, l.lse,
+                           l.partial_o, l.partial_lse, l.merges, l.arrivals, l.num_qo_heads, out_scale);
+    return (int)hipGetLastError();
+}
+
 template <int D, int G>
 int launch_prefill_dg(const DecodeLaunch &l, hipStream_t stream) {
-    const uint64_t stride_bytes = (uint64_t)l.slot_stride * 2;
-    const bool wide = stride_bytes >= (1u << 24) || !row_offsets_fit_32(l.num_slots, (uint32_t)stride_bytes);
-    if (wide)
-        hipLaunchKernelGGL((prefill_kernel<D, G, true>), dim3(l.n_workgroups), dim3(PrefillGeo<D>::THREADS), 0, stream,
-                           l.wg_offsets, l.units, (const uint16_t *)l.q, (const char *)l.k_pool,
-                           (const char *)l.v_pool, stride_bytes, l.kv_indices, l.sm_scale * kLog2e, l.out,
-                           l.lse, l.partial_o, l.partial_lse, l.merges, l.arrivals, l.num_qo_heads);
-    else
-        hipLaunchKernelGGL((prefill_kernel<D, G, false>), dim3(l.n_workgroups), dim3(PrefillGeo<D>::THREADS), 0, stream,
-                           l.wg_offsets, l.units, (const uint16_t *)l.q, (const char *)l.k_pool,
-                           (const char *)l.v_pool, stride_bytes, l.kv_indices, l.sm_scale * kLog2e, l.out,
-                           l.lse, l.partial_o, l.partial_lse, l.merges, l.arrivals, l.num_qo_heads);
-    return (int)hipGetLastError();
+    return l.kv_fp8 ? launch_prefill_dgk<D, G, true>(l, stream) : launch_prefill_dgk<D, G, false>(l, stream);
 }
 
 }  // namespace
