@@ -194,7 +194,9 @@ pa_status pa_plan(pa_plan_t *plan, const int32_t *kv_indptr_host,
  * pa_decode_run under pa_plan up to summation order.  Groups with
  * prefix_len 0 and singleton groups cost nothing extra.  Errors: as pa_plan,
  * plus PA_ERR_INVALID_ARG for inconsistent groups or prefix lengths.
- * pa_decode_run_fp8 does not take cascade plans (PA_ERR_UNSUPPORTED).
+ * pa_decode_run_fp8 runs cascade plans the same way over E4M3 pools (the
+ * prefix units read the codes as pa_prefill_chunk_run_fp8 does; add
+ * PA_PLAN_KV_FP8 to the flags to size the decode part for its kernel).
  */
 pa_status pa_plan_cascade(pa_plan_t *plan, const int32_t *kv_indptr_host, int32_t batch,
                           const int32_t *group_indptr_host, int32_t num_groups,

@@ -867,20 +867,28 @@ pa_status pa_plan_host_timing(const pa_plan_t *p, double *total_us, double *wait
     return PA_OK;
 }
 
-pa_status pa_decode_run(const pa_plan_t *p, const void *q, const void *k_pool, const void *v_pool,
-                        int64_t num_slots, int64_t slot_stride, const int32_t *kv_indices,
-                        float sm_scale, float *out, float *lse, pa_stream_t stream) {
+// One decode layer: a cascade plan's prefix units first (the shared prefixes,
+// on the matrix cores; their partials are complete when the decode kernel's
+// merges read them, same stream), then the decode kernel.  Both kernels take
+// bf16 pools or, with kv_fp8, E4M3 pools and their scales.
+static pa_status decode_run_impl(const pa_plan_t *p, const void *q, const void *k_pool,
+                                 const void *v_pool, int64_t num_slots, int64_t slot_stride,
+                                 const int32_t *kv_indices, float sm_scale, float *out, float *lse,
+                                 pa_stream_t stream, bool kv_fp8, float k_scale, float v_scale) {
     pa::DecodeLaunch l;
     pa_status st = prepare_run(p, pa::PlanMode::kDecode, q, k_pool, v_pool, num_slots, slot_stride,
                                kv_indices, sm_scale, out, lse, &l);
     if (st != PA_OK)
         return st;
+    if (kv_fp8 && (!std::isfinite(k_scale) || !std::isfinite(v_scale)))
+        return fail(PA_ERR_INVALID_ARG, "k_scale and v_scale must be finite");
+    l.kv_fp8 = kv_fp8;
+    l.k_scale = k_scale;
+    l.v_scale = v_scale;
     hipError_t e = profile_mark(p, (hipStream_t)stream, false);
     if (e != hipSuccess)
         return hip_fail(e, "profile event");
     if (p->n_prefix_units > 0) {
-        // cascade: the shared prefixes first; their partials are complete
-        // when the decode kernel's merges read them (same stream)
         int rc = pa::launch_prefill(prefix_launch(p, l), stream);
         if (rc == (int)hipErrorNotSupported)
             return fail(PA_ERR_UNSUPPORTED, "prefill kernel not available in this build");
@@ -895,31 +903,19 @@ pa_status pa_decode_run(const pa_plan_t *p, const void *q, const void *k_pool, c
     return PA_OK;
 }
 
+pa_status pa_decode_run(const pa_plan_t *p, const void *q, const void *k_pool, const void *v_pool,
+                        int64_t num_slots, int64_t slot_stride, const int32_t *kv_indices,
+                        float sm_scale, float *out, float *lse, pa_stream_t stream) {
+    return decode_run_impl(p, q, k_pool, v_pool, num_slots, slot_stride, kv_indices, sm_scale, out, lse,
+                           stream, false, 1.f, 1.f);
+}
+
 pa_status pa_decode_run_fp8(const pa_plan_t *p, const void *q, const void *k_pool, const void *v_pool,
                             int64_t num_slots, int64_t slot_stride, const int32_t *kv_indices,
                             float sm_scale, float k_scale, float v_scale, float *out, float *lse,
                             pa_stream_t stream) {
-    pa::DecodeLaunch l;
-    pa_status st = prepare_run(p, pa::PlanMode::kDecode, q, k_pool, v_pool, num_slots, slot_stride,
-                               kv_indices, sm_scale, out, lse, &l);
-    if (st != PA_OK)
-        return st;
-    if (!std::isfinite(k_scale) || !std::isfinite(v_scale))
-        return fail(PA_ERR_INVALID_ARG, "k_scale and v_scale must be finite");
-    if (p->n_prefix_units > 0)
-        return fail(PA_ERR_UNSUPPORTED, "cascade plans are bf16 only");
-    l.kv_fp8 = true;
-    l.k_scale = k_scale;
-    l.v_scale = v_scale;
-    hipError_t e = profile_mark(p, (hipStream_t)stream, false);
-    if (e != hipSuccess)
-        return hip_fail(e, "profile event");
-    int rc = pa::launch_decode(l, stream);
-    if (rc != 0)
-        return hip_fail((hipError_t)rc, "decode kernel launch");
-    if ((e = profile_mark(p, (hipStream_t)stream, true)) != hipSuccess)
-        return hip_fail(e, "profile event");
-    return PA_OK;
+    return decode_run_impl(p, q, k_pool, v_pool, num_slots, slot_stride, kv_indices, sm_scale, out, lse,
+                           stream, true, k_scale, v_scale);
 }
 
 pa_status pa_prefill_chunk_run(const pa_plan_t *p, const void *q, const void *k_pool,

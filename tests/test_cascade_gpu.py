@@ -163,15 +163,61 @@ def test_plan_modes_alternate():
             o = torch.full((4, 32, 128), float("nan"), dtype=torch.float32, device=device())
             plan.decode(q, k, v, idx_dev, W.softmax_scale(128), o)
             outs.append(o)
-        plan.plan_cascade(ip, gi, pl, flags=pa.PA_PLAN_CASCADE_ALL)
+        # the same cascade plan over E4M3 pools of zero codes: every V is 0
+        plan.plan_cascade(ip, gi, pl, flags=pa.PA_PLAN_CASCADE_ALL | pa.PA_PLAN_KV_FP8)
         k8 = torch.zeros((k.shape[0], 8, 128), dtype=torch.uint8, device=device())
-        o8 = torch.empty((4, 32, 128), dtype=torch.float32, device=device())
-        with pytest.raises(pa.PAError) as e:
-            plan.decode_fp8(q, k8, k8, idx_dev, W.softmax_scale(128), 1.0, 1.0, o8)
-        assert e.value.status == pa.PA_ERR_UNSUPPORTED
+        o8 = torch.full((4, 32, 128), float("nan"), dtype=torch.float32, device=device())
+        plan.decode_fp8(q, k8, k8, idx_dev, W.softmax_scale(128), 1.0, 1.0, o8)
         torch.cuda.synchronize()
+        assert torch.equal(o8, torch.zeros_like(o8))
     a, b, c = (o.cpu().numpy() for o in outs)
     assert np.array_equal(a, c) and max_err(a, b) <= CASCADE_VS_PLAIN
+
+
+def _run_fp8(plan_fn, ip, idx, q, k, v, Hkv, k_scale, v_scale):
+    import paged_gqa_decode_pa_amd as pa
+    B, Hq, D = q.shape
+    out = torch.full((B, Hq, D), float("nan"), dtype=torch.float32, device=q.device)
+    lse = torch.full((B, Hq), float("nan"), dtype=torch.float32, device=q.device)
+    with pa.Plan(B, int(ip[-1]), Hq, Hkv, D) as plan:
+        plan_fn(plan)
+        plan.decode_fp8(q, k, v, torch.as_tensor(idx, device=q.device), W.softmax_scale(D), k_scale, v_scale,
+                        out, lse)
+        torch.cuda.synchronize()
+    return out.cpu().numpy(), lse.cpu().numpy()
+
+
+FP8_CASES = [CASES[0], CASES[2], CASES[3], CASES[4], CASES[5], CASES[9]]
+
+
+@pytest.mark.parametrize("lengths,gsize,plen,Hq,Hkv,D", FP8_CASES,
+                         ids=[f"{c[3]}x{c[4]}x{c[5]}-g{c[1]}-p{c[2]}-{i}" for i, c in enumerate(FP8_CASES)])
+def test_cascade_fp8_parity(lengths, gsize, plen, Hq, Hkv, D):
+    """Cascade plans over E4M3 pools (pa_decode_run_fp8): prefix units read
+    the codes on the matrix cores; scales that are not powers of two."""
+    import oracle
+    import paged_gqa_decode_pa_amd as pa
+    say(f"cascade fp8 parity {Hq}x{Hkv}x{D} groups of {gsize}, prefix {plen}")
+    dev = device()
+    ks, vs = 0.37, 1.3
+    rng = np.random.Generator(np.random.PCG64(80 + len(lengths)))
+    ip, idx = W.slot_lists(np.asarray(lengths), 20000, rng, gsize, plen)
+    q = W.normal_bf16((len(lengths), Hq, D), 81, dev)
+    k, v = W.make_pools_e4m3(20000, Hkv, D, 82, dev, k_scale=ks, v_scale=vs)
+    B = len(lengths)
+    gi = _groups(B, gsize)
+    pl = np.full(gi.size - 1, plen, np.int32)
+    fl = pa.PA_PLAN_KV_FP8
+    cas, cas_lse = _run_fp8(lambda p: p.plan_cascade(ip, gi, pl, flags=pa.PA_PLAN_CASCADE_ALL | fl),
+                            ip, idx, q, k, v, Hkv, ks, vs)
+    plain, plain_lse = _run_fp8(lambda p: p.plan(ip, flags=fl), ip, idx, q, k, v, Hkv, ks, vs)
+    ref, ref_lse = oracle.load().decode_fp8(W.bits(q), W.codes(k), W.codes(v), ip, idx, W.softmax_scale(D),
+                                            ks, vs, Hkv)
+    d_plain = max(max_err(cas, plain), max_err(cas_lse, plain_lse))
+    e = max_err(cas, ref), max_err(cas_lse, ref_lse)
+    say(f"  vs plain {d_plain:.3g}; vs oracle out {e[0]:.3g} lse {e[1]:.3g} (all rows)")
+    assert d_plain <= CASCADE_VS_PLAIN
+    assert e[0] <= TOL and e[1] <= TOL
 
 
 def test_graph_replay():
