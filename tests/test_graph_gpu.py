@@ -125,8 +125,12 @@ def test_decode_graph_replay_after_replan_with_other_cuts():
         del g
 
 
-def test_prefill_layers_graph_replay():
-    say(f"graph capture: {LAYERS}-layer prefill step with split KV ranges")
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_prefill_layers_graph_replay(kv):
+    say(f"graph capture: {LAYERS}-layer prefill step with split KV ranges, {kv} pools")
+    import oracle
+    fp8 = kv == "fp8"
+    ks, vs = W.FP8_K_SCALE, W.FP8_V_SCALE
     dev = device()
     rng = np.random.Generator(np.random.PCG64(37))
     Hq, Hkv, D, N = 32, 8, 128, 16384
@@ -135,7 +139,8 @@ def test_prefill_layers_graph_replay():
     qo = np.concatenate([[0], np.cumsum([C for _, C in reqs])]).astype(np.int32)
     T = int(qo[-1])
     q = W.normal_bf16((T, Hq, D), 38, dev)
-    pools = [W.make_pools(N, Hkv, D, 50 + l, dev) for l in range(LAYERS)]
+    make = W.make_pools_e4m3 if fp8 else W.make_pools
+    pools = [make(N, Hkv, D, 50 + l, dev) for l in range(LAYERS)]
     idx_dev = torch.as_tensor(idx, device=dev)
     scale = W.softmax_scale(D)
     outs = [torch.full((T, Hq, D), float("nan"), dtype=torch.float32, device=dev) for _ in range(LAYERS)]
@@ -145,12 +150,84 @@ def test_prefill_layers_graph_replay():
 
         def step(stream):
             for l in range(LAYERS):
-                plan.prefill(q, pools[l][0], pools[l][1], idx_dev, scale, outs[l], lses[l], stream=stream)
+                if fp8:
+                    plan.prefill_fp8(q, pools[l][0], pools[l][1], idx_dev, scale, ks, vs, outs[l], lses[l],
+                                     stream=stream)
+                else:
+                    plan.prefill(q, pools[l][0], pools[l][1], idx_dev, scale, outs[l], lses[l], stream=stream)
 
         step(torch.cuda.current_stream())
         torch.cuda.synchronize()
         eager = [o.cpu().numpy() for o in outs] + [x.cpu().numpy() for x in lses]
         for l in range(LAYERS):
-            ref, ref_lse = oracle_prefill(q, pools[l][0], pools[l][1], qo, ip, idx, scale, Hkv)
+            if fp8:
+                ref, ref_lse = oracle.load().prefill_fp8(W.bits(q), W.codes(pools[l][0]), W.codes(pools[l][1]),
+                                                         qo, ip, idx, scale, ks, vs, Hkv)
+            else:
+                ref, ref_lse = oracle_prefill(q, pools[l][0], pools[l][1], qo, ip, idx, scale, Hkv)
             assert max_err(eager[l], ref) <= TOL and max_err(eager[LAYERS + l], ref_lse) <= TOL
         _replay_and_check(step, outs + lses, eager)
+
+
+def test_fp8_decode_step_with_append_graph_replay():
+    """A whole decode step over 8-bit pools captured once: per layer, the
+    step's new token of every request appended (K rotated, both encoded) at
+    the end of its list, then the fp8 decode over the lists.  The appended
+    slots are wiped before every replay, so the captured appends must write
+    them again; outputs bit for bit as the eager step's, which match the
+    oracle over the pools the appends produced."""
+    import oracle
+    say(f"graph capture: {LAYERS}-layer fp8 decode step with appends")
+    dev = device()
+    rng = np.random.Generator(np.random.PCG64(39))
+    B, Hq, Hkv, D, N = 8, 32, 8, 128, 65536
+    ks, vs = W.FP8_K_SCALE, W.FP8_V_SCALE
+    lengths = rng.integers(300, 3000, B)
+    ip, idx = W.slot_lists(lengths, N, rng)
+    new_slots = torch.as_tensor(idx[ip[1:] - 1].astype(np.int32), device=dev)
+    positions = torch.as_tensor((lengths - 1).astype(np.int32), device=dev)
+    q = W.normal_bf16((B, Hq, D), 40, dev)
+    k_new = [W.normal_bf16((B, Hkv, D), 41 + 2 * l, dev) for l in range(LAYERS)]
+    v_new = [W.normal_bf16((B, Hkv, D), 42 + 2 * l, dev) for l in range(LAYERS)]
+    pools = [W.make_pools_e4m3(N, Hkv, D, 60 + l, dev) for l in range(LAYERS)]
+    idx_dev = torch.as_tensor(idx, device=dev)
+    scale = W.softmax_scale(D)
+    outs = [torch.full((B, Hq, D), float("nan"), dtype=torch.float32, device=dev) for _ in range(LAYERS)]
+    sel = new_slots.to(torch.int64)
+    with pa.Plan(B, int(ip[-1]), Hq, Hkv, D) as plan:
+        plan.plan(ip, flags=pa.PA_PLAN_KV_FP8)
+
+        def step(stream):
+            for l in range(LAYERS):
+                pa.pa_kv_append_fp8(k_new[l], v_new[l], new_slots, pools[l][0], pools[l][1], ks, vs,
+                                    positions=positions, rope_theta=1e6, stream=stream)
+                plan.decode_fp8(q, pools[l][0], pools[l][1], idx_dev, scale, ks, vs, outs[l], stream=stream)
+
+        step(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        eager = [o.cpu().numpy() for o in outs]
+        for l in range(LAYERS):
+            ref, _ = oracle.load().decode_fp8(W.bits(q), W.codes(pools[l][0]), W.codes(pools[l][1]), ip, idx,
+                                              scale, ks, vs, Hkv)
+            assert max_err(eager[l], ref) <= TOL
+        appended = [(W.codes(pools[l][0].view(torch.uint8)[sel]), W.codes(pools[l][1].view(torch.uint8)[sel]))
+                    for l in range(LAYERS)]
+        s = torch.cuda.Stream()
+        g = torch.cuda.CUDAGraph()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.graph(g, stream=s):
+            step(s)
+        torch.cuda.synchronize()
+        for rep in range(3):
+            for l in range(LAYERS):
+                outs[l].fill_(float("nan"))
+                pools[l][0].view(torch.uint8)[sel] = 0
+                pools[l][1].view(torch.uint8)[sel] = 0
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            for l in range(LAYERS):
+                assert np.array_equal(outs[l].cpu().numpy(), eager[l]), f"replay {rep} layer {l} differs"
+                assert np.array_equal(W.codes(pools[l][0].view(torch.uint8)[sel]), appended[l][0])
+                assert np.array_equal(W.codes(pools[l][1].view(torch.uint8)[sel]), appended[l][1])
+        del g
