@@ -15,14 +15,15 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "pa
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text)) - {"pa_plan_t"})
+    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)) - {"pa_plan_t"})
 
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for required in ("pa_plan_create", "pa_plan", "pa_decode_run", "pa_prefill_chunk_run",
                      "pa_plan_destroy", "pa_strerror", "pa_last_error_detail", "pa_partition",
-                     "pa_version"):
+                     "pa_version", "pa_decode_run_fp8", "pa_prefill_chunk_run_fp8", "pa_kv_append",
+                     "pa_kv_append_fp8", "pa_plan_cascade", "pa_decode_run_noalloc"):
         assert required in names
 
 
