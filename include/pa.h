@@ -101,8 +101,9 @@ typedef enum pa_status {
  * max_batch + max_kv_total / 256.  In prefill mode every (request, KV head,
  * row tile) is cut into n parts: the n * num_kv_heads * sum_b ceil(C_b / t)
  * units (t = 256 / (Hq/Hkv) chunk tokens per tile at head_dim 128, 128 /
- * (Hq/Hkv) at 256) must fit in 1024 + num_kv_heads * (ceil(max_q_total / t)
- * + max_batch), else PA_ERR_CAPACITY (a larger max_q_total makes room). */
+ * (Hq/Hkv) at 256) always fit when they number at most 1024 + num_kv_heads *
+ * (ceil(max_q_total / t) + max_batch) (a larger max_q_total makes room); a
+ * call that needs more units than the plan holds returns PA_ERR_CAPACITY. */
 #define PA_PLAN_FORCE_SPLITS(n) (((uint32_t)(n) & 0xffffu) << PA_PLAN_FORCE_SPLITS_SHIFT)
 #define PA_MAX_FORCED_SPLITS 256
 /* Keep the automatic split but place workgroups in plain order instead of

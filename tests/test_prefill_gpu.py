@@ -217,3 +217,26 @@ def test_prefill_values_beyond_fp16_range_in_part_of_the_list(splits):
     e = max_err(out / 65536.0, ref / 65536.0), max_err(lse, ref_lse)
     say(f"  max|d|/2^16 vs oracle {e[0]:.3g}, lse {e[1]:.3g}")
     assert e[0] <= TOL and e[1] <= TOL
+
+
+def test_prefill_forced_splits_capacity():
+    """The documented room for forced prefill parts: 2 requests of 640 chunk
+    tokens (10 tiles of 64 tokens per KV head, 160 tiles) in a plan with
+    max_q_total 1280 hold 1024 + 8 * (20 + 2) = 1200 units, so 7 parts per
+    tile (1120 units) fit and give the oracle's result; 64 parts per tile
+    (10240 units) are refused with PA_ERR_CAPACITY before anything runs."""
+    say("prefill forced-split capacity")
+    reqs = [(1000, 640), (1000, 640)]
+    qo, ip, idx, q, k, v = _case(reqs, 32, 8, 128, 4096, seed=51)
+    idx_dev = torch.as_tensor(idx, device=device())
+    scale = W.softmax_scale(128)
+    out = torch.full((1280, 32, 128), float("nan"), dtype=torch.float32, device=device())
+    with pa.Plan(2, int(ip[-1]), 32, 8, 128, max_q_total=1280) as plan:
+        plan.plan(ip, qo, flags=pa.PA_PLAN_FORCE_SPLITS(7))
+        plan.prefill(q, k, v, idx_dev, scale, out)
+        torch.cuda.synchronize()
+        with pytest.raises(pa.PAError) as e:
+            plan.plan(ip, qo, flags=pa.PA_PLAN_FORCE_SPLITS(64))
+        assert e.value.status == pa.PA_ERR_CAPACITY
+    ref, _ = oracle_prefill(q, k, v, qo, ip, idx, scale, 8)
+    assert max_err(out.cpu().numpy(), ref) <= TOL
