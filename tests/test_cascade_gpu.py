@@ -220,6 +220,36 @@ def test_cascade_fp8_parity(lengths, gsize, plen, Hq, Hkv, D):
     assert e[0] <= TOL and e[1] <= TOL
 
 
+@pytest.mark.slow
+def test_system_prompt_workload_fp8_full_rows():
+    """The system-prompt workload over E4M3 pools under its cascade plan (as
+    bench.py --workload system_prompt --cascade --kv fp8 runs it): every row
+    against the oracle, and within 5e-4 of the plain E4M3 plan."""
+    import oracle
+    import paged_gqa_decode_pa_amd as pa
+    spec = W.SYSTEM_PROMPT_B64
+    say("cascade system-prompt workload over E4M3 pools (all rows)")
+    dev = device()
+    case = W.make_decode_case(spec, dev, layers=0)
+    k, v = W.make_pools_e4m3(spec.num_slots, spec.num_kv_heads, spec.head_dim, W.layer_seed(spec.seed, 0), dev)
+    ks, vs = W.FP8_K_SCALE, W.FP8_V_SCALE
+    gi = np.array([0, spec.batch], np.int32)
+    pl = np.array([spec.prefix_len], np.int32)
+    fl = pa.PA_PLAN_KV_FP8
+    cas, cas_lse = _run_fp8(lambda p: p.plan_cascade(case.kv_indptr, gi, pl, flags=fl), case.kv_indptr,
+                            case.kv_indices, case.q, k, v, spec.num_kv_heads, ks, vs)
+    plain, plain_lse = _run_fp8(lambda p: p.plan(case.kv_indptr, flags=fl), case.kv_indptr, case.kv_indices,
+                                case.q, k, v, spec.num_kv_heads, ks, vs)
+    assert max_err(cas, plain) <= CASCADE_VS_PLAIN and max_err(cas_lse, plain_lse) <= CASCADE_VS_PLAIN
+    ref, ref_lse = oracle.load().decode_fp8(W.bits(case.q), W.codes(k), W.codes(v), case.kv_indptr,
+                                            case.kv_indices, case.sm_scale, ks, vs, spec.num_kv_heads)
+    e = max_err(cas, ref), max_err(cas_lse, ref_lse)
+    say(f"  vs oracle out {e[0]:.3g} lse {e[1]:.3g}")
+    assert e[0] <= TOL and e[1] <= TOL
+    del case, k, v
+    torch.cuda.empty_cache()
+
+
 def test_graph_replay():
     """A captured cascade run (prefix kernel + decode kernel) replays bit-exactly."""
     import paged_gqa_decode_pa_amd as pa
