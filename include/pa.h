@@ -232,8 +232,9 @@ pa_status pa_decode_run(const pa_plan_t *plan, const void *q, const void *k_pool
  * formats); the
  * format and the per-pool scales are this library's reading.  Same plan,
  * arguments, output and errors as pa_decode_run, plus PA_ERR_INVALID_ARG for
- * a non-finite scale.  Code 0x7F / 0xFF (NaN) in a referenced row makes the
- * results NaN; unreferenced rows are never read.
+ * a non-finite scale or a slot_stride that is not a multiple of 16 (bytes:
+ * rows are read 16 codes at a time).  Code 0x7F / 0xFF (NaN) in a referenced
+ * row makes the results NaN; unreferenced rows are never read.
  */
 pa_status pa_decode_run_fp8(const pa_plan_t *plan, const void *q, const void *k_pool,
                             const void *v_pool, int64_t num_slots, int64_t slot_stride,

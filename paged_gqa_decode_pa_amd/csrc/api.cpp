@@ -882,6 +882,10 @@ static pa_status decode_run_impl(const pa_plan_t *p, const void *q, const void *
         return st;
     if (kv_fp8 && (!std::isfinite(k_scale) || !std::isfinite(v_scale)))
         return fail(PA_ERR_INVALID_ARG, "k_scale and v_scale must be finite");
+    // the E4M3 decode reads up to 16 codes (16 bytes) a lane in one load, so
+    // every slot's rows must start 16-byte aligned
+    if (kv_fp8 && l.slot_stride % 16 != 0)
+        return fail(PA_ERR_INVALID_ARG, "E4M3 pools need a slot_stride that is a multiple of 16 bytes");
     l.kv_fp8 = kv_fp8;
     l.k_scale = k_scale;
     l.v_scale = v_scale;

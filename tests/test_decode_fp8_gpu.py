@@ -201,3 +201,36 @@ def test_fp8_batch64_workload_full_rows(k_scale, v_scale):
     assert e <= TOL and el <= TOL
     del k, v
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("pad,ok", [(16, True), (48, True), (8, False), (24, False)])
+def test_decode_fp8_padded_slot_stride(pad, ok):
+    """E4M3 pools whose slots are padded (slot stride Hkv*D + pad bytes): a
+    stride that keeps every row 16-byte aligned decodes as the compact pool
+    does; any other is refused on the host (rows are read 16 codes a lane)."""
+    say(f"fp8 decode, slot stride Hkv*D + {pad}")
+    Hq, Hkv, D, N = 32, 8, 128, 4096
+    ip, idx, q, k, v = _case([5, 300, 77], Hq, Hkv, D, N, seed=95)
+    stride = Hkv * D + pad
+    dev = q.device
+    kb = torch.zeros((N, stride), dtype=torch.uint8, device=dev)
+    vb = torch.zeros((N, stride), dtype=torch.uint8, device=dev)
+    kb[:, :Hkv * D] = k.view(torch.uint8).reshape(N, Hkv * D)
+    vb[:, :Hkv * D] = v.view(torch.uint8).reshape(N, Hkv * D)
+    kp = torch.as_strided(kb, (N, Hkv, D), (stride, D, 1))
+    vp = torch.as_strided(vb, (N, Hkv, D), (stride, D, 1))
+    idx_dev = torch.as_tensor(idx, device=dev)
+    scale = W.softmax_scale(D)
+    if not ok:
+        out = torch.empty((3, Hq, D), dtype=torch.float32, device=dev)
+        with pa.Plan(3, int(ip[-1]), Hq, Hkv, D) as plan:
+            plan.plan(ip, flags=pa.PA_PLAN_KV_FP8)
+            with pytest.raises(pa.PAError) as e:
+                plan.decode_fp8(q, kp, vp, idx_dev, scale, KS, VS, out)
+            assert e.value.status == pa.PA_ERR_INVALID_ARG
+        return
+    out, lse = run_fp8(q, kp, vp, ip, idx_dev, scale, Hkv)
+    base, base_lse = run_fp8(q, k, v, ip, idx_dev, scale, Hkv)
+    assert np.array_equal(out, base) and np.array_equal(lse, base_lse)
+    ref, ref_lse = _oracle(q, k, v, ip, idx, scale, Hkv)
+    assert max_err(out, ref) <= TOL and max_err(lse, ref_lse) <= TOL
