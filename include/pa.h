@@ -246,7 +246,8 @@ pa_status pa_decode_run_fp8(const pa_plan_t *plan, const void *q, const void *k_
  * prefill plan (pa_plan with qo_indptr_host != NULL).
  *   q [T, Hq, D] bf16 with T = qo_indptr[batch]; pools and kv_indices as in
  *   decode (each request's chunk tokens are the last entries of its list,
- *   already written into the pool); out [T, Hq, D] fp32; lse [T, Hq] or NULL.
+ *   already written into the pool); out [T, Hq, D] fp32, 16-byte aligned
+ *   (rows are written four floats at a time); lse [T, Hq] or NULL.
  */
 pa_status pa_prefill_chunk_run(const pa_plan_t *plan, const void *q, const void *k_pool,
                                const void *v_pool, int64_t num_slots, int64_t slot_stride,

@@ -922,40 +922,22 @@ pa_status pa_decode_run_fp8(const pa_plan_t *p, const void *q, const void *k_poo
                            stream, true, k_scale, v_scale);
 }
 
-pa_status pa_prefill_chunk_run(const pa_plan_t *p, const void *q, const void *k_pool,
-                               const void *v_pool, int64_t num_slots, int64_t slot_stride,
-                               const int32_t *kv_indices, float sm_scale, float *out, float *lse,
-                               pa_stream_t stream) {
+// One chunked-prefill layer over bf16 pools or, with kv_fp8, E4M3 pools.
+static pa_status prefill_run_impl(const pa_plan_t *p, const void *q, const void *k_pool,
+                                  const void *v_pool, int64_t num_slots, int64_t slot_stride,
+                                  const int32_t *kv_indices, float sm_scale, float *out, float *lse,
+                                  pa_stream_t stream, bool kv_fp8, float k_scale, float v_scale) {
     pa::DecodeLaunch l;
     pa_status st = prepare_run(p, pa::PlanMode::kPrefill, q, k_pool, v_pool, num_slots,
                                slot_stride, kv_indices, sm_scale, out, lse, &l);
     if (st != PA_OK)
         return st;
-    hipError_t e = profile_mark(p, (hipStream_t)stream, false);
-    if (e != hipSuccess)
-        return hip_fail(e, "profile event");
-    int rc = pa::launch_prefill(l, stream);
-    if (rc == (int)hipErrorNotSupported)
-        return fail(PA_ERR_UNSUPPORTED, "prefill kernel not available in this build");
-    if (rc != 0)
-        return hip_fail((hipError_t)rc, "prefill kernel launch");
-    if ((e = profile_mark(p, (hipStream_t)stream, true)) != hipSuccess)
-        return hip_fail(e, "profile event");
-    return PA_OK;
-}
-
-pa_status pa_prefill_chunk_run_fp8(const pa_plan_t *p, const void *q, const void *k_pool,
-                                   const void *v_pool, int64_t num_slots, int64_t slot_stride,
-                                   const int32_t *kv_indices, float sm_scale, float k_scale,
-                                   float v_scale, float *out, float *lse, pa_stream_t stream) {
-    pa::DecodeLaunch l;
-    pa_status st = prepare_run(p, pa::PlanMode::kPrefill, q, k_pool, v_pool, num_slots,
-                               slot_stride, kv_indices, sm_scale, out, lse, &l);
-    if (st != PA_OK)
-        return st;
-    if (!std::isfinite(k_scale) || !std::isfinite(v_scale))
+    // the prefill kernel writes each row's outputs four floats at a time
+    if (!aligned(out, 16))
+        return fail(PA_ERR_INVALID_ARG, "out must be 16-byte aligned for chunked prefill");
+    if (kv_fp8 && (!std::isfinite(k_scale) || !std::isfinite(v_scale)))
         return fail(PA_ERR_INVALID_ARG, "k_scale and v_scale must be finite");
-    l.kv_fp8 = true;
+    l.kv_fp8 = kv_fp8;
     l.k_scale = k_scale;
     l.v_scale = v_scale;
     hipError_t e = profile_mark(p, (hipStream_t)stream, false);
@@ -969,6 +951,22 @@ pa_status pa_prefill_chunk_run_fp8(const pa_plan_t *p, const void *q, const void
     if ((e = profile_mark(p, (hipStream_t)stream, true)) != hipSuccess)
         return hip_fail(e, "profile event");
     return PA_OK;
+}
+
+pa_status pa_prefill_chunk_run(const pa_plan_t *p, const void *q, const void *k_pool,
+                               const void *v_pool, int64_t num_slots, int64_t slot_stride,
+                               const int32_t *kv_indices, float sm_scale, float *out, float *lse,
+                               pa_stream_t stream) {
+    return prefill_run_impl(p, q, k_pool, v_pool, num_slots, slot_stride, kv_indices, sm_scale, out, lse,
+                            stream, false, 1.f, 1.f);
+}
+
+pa_status pa_prefill_chunk_run_fp8(const pa_plan_t *p, const void *q, const void *k_pool,
+                                   const void *v_pool, int64_t num_slots, int64_t slot_stride,
+                                   const int32_t *kv_indices, float sm_scale, float k_scale,
+                                   float v_scale, float *out, float *lse, pa_stream_t stream) {
+    return prefill_run_impl(p, q, k_pool, v_pool, num_slots, slot_stride, kv_indices, sm_scale, out, lse,
+                            stream, true, k_scale, v_scale);
 }
 
 pa_status pa_decode_run_noalloc(const void *q, const void *k_pool, const void *v_pool,

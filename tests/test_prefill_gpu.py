@@ -240,3 +240,23 @@ def test_prefill_forced_splits_capacity():
         assert e.value.status == pa.PA_ERR_CAPACITY
     ref, _ = oracle_prefill(q, k, v, qo, ip, idx, scale, 8)
     assert max_err(out.cpu().numpy(), ref) <= TOL
+
+
+def test_prefill_refuses_misaligned_out():
+    """Output rows are written four floats at a time: an out buffer that is
+    only 4-byte aligned is refused on the host, for bf16 and E4M3 pools."""
+    say("prefill with a misaligned out buffer")
+    reqs = [(100, 20)]
+    qo, ip, idx, q, k, v = _case(reqs, 32, 8, 128, 1024, seed=53)
+    idx_dev = torch.as_tensor(idx, device=device())
+    n = 20 * 32 * 128
+    out = torch.empty(n + 4, dtype=torch.float32, device=device())[1:1 + n].view(20, 32, 128)
+    assert out.data_ptr() % 16 == 4
+    k8, v8 = W.make_pools_e4m3(1024, 8, 128, 54, device())
+    with pa.Plan(1, int(ip[-1]), 32, 8, 128, max_q_total=20) as plan:
+        plan.plan(ip, qo)
+        for run in (lambda: plan.prefill(q, k, v, idx_dev, 0.088, out),
+                    lambda: plan.prefill_fp8(q, k8, v8, idx_dev, 0.088, 1.0, 1.0, out)):
+            with pytest.raises(pa.PAError) as e:
+                run()
+            assert e.value.status == pa.PA_ERR_INVALID_ARG
