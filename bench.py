@@ -34,8 +34,12 @@ captured HIP graph (pa_plan stays outside the graph; the CUDA Graph decode
 of the Agent-Infer page, section "CUDA Graph 解码"); `--eager` launches them
 one by one instead.
 `--workload prefill_chunk512 | prefill_chunk64` measures the chunked-prefill
-kernel (MFMA roofline); `--workload copy --copy-gib N` runs a plain device
-copy of N GiB (for calibrating the HBM counters).
+kernel (MFMA roofline); `--workload append` the KV append + RoPE of a
+batch-64 step; `--workload system_prompt --cascade` the cascade decode of 64
+requests sharing a 4096-slot prompt; `--workload copy --copy-gib N` runs a
+plain device copy of N GiB (for calibrating the HBM counters).  `--kv fp8`
+runs a decode, prefill or append workload over pools of OCP FP8 E4M3 codes
+(per-pool scales 0.25 for K and 0.5 for V) instead of bf16.
 """
 from __future__ import annotations
 
