@@ -57,7 +57,8 @@
  * tables, which stay at the same addresses for the life of the plan: its
  * replays after a later pa_plan of the same plan are valid while that
  * pa_plan yields the same number of workgroups and of cascade prefix units
- * (pa_plan_info), as the same lists with the same flags do; otherwise
+ * (pa_plan_launch_shape), as the same lists with the same flags do, and as a
+ * decode step whose work fills the GPU does whatever its lengths; otherwise
  * capture again.
  *
  * Errors: every call returns a pa_status; no exception crosses the ABI.
@@ -521,6 +522,19 @@ pa_status pa_profile_end(pa_plan_t *plan, double *total_ms, int32_t *n_launches)
  * staging buffer is reused).  PA_ERR_INVALID_ARG for null pointers.
  */
 pa_status pa_plan_host_timing(const pa_plan_t *plan, double *total_us, double *wait_us);
+
+/*
+ * pa_plan_launch_shape: the launch sizes of the runs under the last
+ * successful pa_plan / pa_plan_cascade call on this plan: *n_workgroups, the
+ * grid of the attention kernel, and *n_prefix_units, the grid of a cascade
+ * plan's prefix launch (0 without one).  A run captured into a HIP graph
+ * keeps the sizes current at capture, so its replays stay valid after a
+ * later pa_plan of the same plan while both are unchanged: a caller that
+ * keeps one graph per batch size compares them after each pa_plan and
+ * captures again when they differ.  Host only; any output pointer may be
+ * NULL.  PA_ERR_INVALID_ARG for a null plan.
+ */
+pa_status pa_plan_launch_shape(const pa_plan_t *plan, int32_t *n_workgroups, int32_t *n_prefix_units);
 
 /*
  * pa_plan_info: what the last successful pa_plan / pa_plan_cascade call on

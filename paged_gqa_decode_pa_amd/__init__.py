@@ -135,6 +135,8 @@ def _load() -> ctypes.CDLL:
     lib.pa_kv_append.restype = ctypes.c_int
     lib.pa_kv_append_fp8.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, f32, f32, vp, vp, i64, i64, vp]
     lib.pa_kv_append_fp8.restype = ctypes.c_int
+    lib.pa_plan_launch_shape.argtypes = [vp, i32p, i32p]
+    lib.pa_plan_launch_shape.restype = ctypes.c_int
     lib.pa_plan_info.argtypes = [vp, i32p, i32p, i32p, i32p, i32p]
     lib.pa_plan_info.restype = ctypes.c_int
     lib.pa_check_kv_indices.argtypes = [i32p, i32, i32p, i64, ctypes.POINTER(ctypes.c_int64)]
@@ -237,6 +239,14 @@ def pa_plan_cascade(plan, kv_indptr, group_indptr, prefix_len, flags: int = 0,
     ng = 0 if gi is None else gi.size - 1
     _check(_lib.pa_plan_cascade(plan, _i32p(kv), kv.size - 1, _i32p(gi), ng, _i32p(pl), flags,
                                 _stream(stream)), "pa_plan_cascade")
+
+
+def pa_plan_launch_shape(plan):
+    """-> (n_workgroups, n_prefix_units) of the last pa_plan on this plan: the
+    launch sizes a captured run keeps (replays stay valid while they match)."""
+    wg, pre = ctypes.c_int32(), ctypes.c_int32()
+    _check(_lib.pa_plan_launch_shape(plan, ctypes.byref(wg), ctypes.byref(pre)), "pa_plan_launch_shape")
+    return wg.value, pre.value
 
 
 def pa_plan_info(plan):
@@ -618,6 +628,9 @@ class Plan:
     def prefill(self, q, k_pool, v_pool, kv_indices, sm_scale, out, lse=None, **kw) -> None:
         self._debug_check(kv_indices, k_pool, kw)
         pa_prefill_chunk_run(self.handle, q, k_pool, v_pool, kv_indices, sm_scale, out, lse, **kw)
+
+    def launch_shape(self):
+        return pa_plan_launch_shape(self.handle)
 
     def prefill_fp8(self, q, k_pool, v_pool, kv_indices, sm_scale, k_scale, v_scale, out, lse=None,
                     **kw) -> None:

@@ -807,6 +807,16 @@ pa_status pa_kv_append_fp8(const void *k_new, const void *v_new, void *q, const 
                        v_scale);
 }
 
+pa_status pa_plan_launch_shape(const pa_plan_t *p, int32_t *n_workgroups, int32_t *n_prefix_units) {
+    if (!p)
+        return fail(PA_ERR_INVALID_ARG, "plan is null");
+    if (n_workgroups)
+        *n_workgroups = p->mode == pa::PlanMode::kNone ? 0 : p->n_workgroups;
+    if (n_prefix_units)
+        *n_prefix_units = p->mode == pa::PlanMode::kNone ? 0 : p->n_prefix_units;
+    return PA_OK;
+}
+
 pa_status pa_plan_info(const pa_plan_t *p, int32_t *mode, int32_t *rows, int32_t *num_qo_heads,
                        int32_t *num_kv_heads, int32_t *head_dim) {
     if (!p)

@@ -231,3 +231,70 @@ def test_fp8_decode_step_with_append_graph_replay():
                 assert np.array_equal(W.codes(pools[l][0].view(torch.uint8)[sel]), appended[l][0])
                 assert np.array_equal(W.codes(pools[l][1].view(torch.uint8)[sel]), appended[l][1])
         del g
+
+
+def test_one_graph_per_batch_size():
+    """The serving pattern of a captured decode step: one plan, one set of
+    static buffers and one captured step per batch size.  Each step writes
+    its new lists and queries into that batch size's buffers, re-plans, and
+    replays the captured step while pa_plan_launch_shape is unchanged (a step
+    whose work fills the GPU keeps it whatever its lengths), capturing again
+    otherwise.  Every replay equals an eager run of the same plan bit for bit
+    and matches the oracle; batch 32 is captured once for all its steps."""
+    say("one captured decode step per batch size, lists changing every step")
+    dev = device()
+    Hq, Hkv, D, N = 32, 8, 128, 400000
+    rng = np.random.Generator(np.random.PCG64(47))
+    pools = [W.make_pools(N, Hkv, D, 48 + l, dev) for l in range(2)]
+    scale = W.softmax_scale(D)
+    cap_entries = 32 * 4096
+    slots = {}      # batch -> plan, buffers, graph and its launch shape
+    captures = {32: 0, 8: 0}
+    try:
+        for step, B in enumerate([32, 8, 32, 32, 8]):
+            lo, hi = (2048, 4096) if B == 32 else (512, 4096)
+            ip, idx = W.slot_lists(rng.integers(lo, hi + 1, B), N, rng)
+            if B not in slots:
+                slots[B] = {"plan": pa.Plan(B, cap_entries, Hq, Hkv, D),
+                            "q": torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev),
+                            "idx": torch.zeros(cap_entries, dtype=torch.int32, device=dev),
+                            "outs": [torch.empty((B, Hq, D), dtype=torch.float32, device=dev) for _ in range(2)],
+                            "graph": None, "shape": None}
+            sl = slots[B]
+            plan, qb, ib, outs = sl["plan"], sl["q"], sl["idx"], sl["outs"]
+            qb.copy_(W.normal_bf16((B, Hq, D), 49 + step, dev))
+            ib[:idx.size].copy_(torch.as_tensor(idx, device=dev))
+            plan.plan(ip)
+            shape = plan.launch_shape()
+
+            def layers(stream, dst=outs):
+                for l in range(2):
+                    plan.decode(qb, pools[l][0], pools[l][1], ib, scale, dst[l], stream=stream)
+
+            if sl["graph"] is None or sl["shape"] != shape:
+                s = torch.cuda.Stream()
+                s.wait_stream(torch.cuda.current_stream())
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=s):
+                    layers(s)
+                torch.cuda.synchronize()
+                sl["graph"], sl["shape"] = g, shape
+                captures[B] += 1
+            eager = [torch.full_like(o, float("nan")) for o in outs]
+            layers(torch.cuda.current_stream(), eager)
+            for o in outs:
+                o.fill_(float("nan"))
+            torch.cuda.synchronize()
+            sl["graph"].replay()
+            torch.cuda.synchronize()
+            say(f"  step {step}: batch {B}, launch shape {shape}, captures so far {captures}")
+            for l in range(2):
+                got = outs[l].cpu().numpy()
+                assert np.array_equal(got, eager[l].cpu().numpy()), f"step {step} layer {l}: replay differs"
+                ref, _ = oracle_decode(qb, pools[l][0], pools[l][1], ip, idx, scale, Hkv)
+                assert max_err(got, ref) <= TOL
+        assert captures[32] == 1, captures
+    finally:
+        for sl in slots.values():
+            sl["graph"] = None
+            sl["plan"].close()
