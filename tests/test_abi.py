@@ -112,3 +112,19 @@ def test_check_kv_indices_rejects_bad_offsets(ip):
 
 def test_plan_info_null_plan():
     assert pa._lib.pa_plan_info(ctypes.c_void_p(0), None, None, None, None, None) == pa.PA_ERR_INVALID_ARG
+
+
+def test_import_fails_loudly_without_library(tmp_path):
+    """No fallback path: a copy of the package without libpa.so refuses to
+    import, naming the missing library (checked in a child process)."""
+    import shutil
+    import subprocess
+    import sys
+    pkg = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "paged_gqa_decode_pa_amd")
+    dst = tmp_path / "paged_gqa_decode_pa_amd"
+    shutil.copytree(pkg, dst, ignore=shutil.ignore_patterns("*.so", "__pycache__", "csrc"))
+    assert not (dst / "libpa.so").exists()
+    r = subprocess.run([sys.executable, "-c", "import paged_gqa_decode_pa_amd"], cwd=tmp_path,
+                       capture_output=True, text=True, env={**os.environ, "PYTHONPATH": str(tmp_path)})
+    assert r.returncode != 0
+    assert "ImportError" in r.stderr and "libpa.so is missing" in r.stderr, r.stderr[-500:]
