@@ -64,11 +64,14 @@ COUNTERS = os.path.join(ROOT, "profiles", "decode_b64_counters.json")
 DECODE_COUNTERS = {
     "b64_l2048_8192_prefix16x4x1024_36layers": COUNTERS,
     "b64_l4096_8192_prefix16x4x1024_36layers": os.path.join(ROOT, "profiles", "decode_b64_4k8k_counters.json"),
+    "b64_l2048_8192_prefix16x4x1024_36layers_fp8kv": os.path.join(ROOT, "profiles", "decode_b64_fp8_counters.json"),
 }
 DECODE_SOURCES = ("decode.hip", "pa_internal.h")
 PREFILL_COUNTERS = {
     "prefill_8x4096_chunk512": os.path.join(ROOT, "profiles", "prefill_chunk512_counters.json"),
     "prefill_8x4096_chunk64": os.path.join(ROOT, "profiles", "prefill_chunk64_counters.json"),
+    "prefill_8x4096_chunk512_fp8kv": os.path.join(ROOT, "profiles", "prefill_chunk512_fp8_counters.json"),
+    "prefill_8x4096_chunk64_fp8kv": os.path.join(ROOT, "profiles", "prefill_chunk64_fp8_counters.json"),
 }
 # the partition decides how many partial rows a prefill launch writes
 PREFILL_SOURCES = ("prefill.hip", "pa_internal.h", "plan.cpp")
@@ -333,7 +336,8 @@ def run_prefill_bench(args):
             "peak": BF16_MFMA_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4),
-            "traffic": None if fp8 else traffic_per_launch(PREFILL_COUNTERS.get(spec.name), PREFILL_SOURCES),
+            "traffic": traffic_per_launch(PREFILL_COUNTERS.get(spec.name + ("_fp8kv" if fp8 else "")),
+                                          PREFILL_SOURCES),
             "kernel": (f"prefill_kernel<{D},{Hq // Hkv},KV8> (pa_prefill_chunk_run_fp8)" if fp8
                        else f"prefill_kernel<{D},{Hq // Hkv}> (pa_prefill_chunk_run)"),
             "kernel_avg_us": round(kernel_avg_ms * 1e3, 2),
@@ -667,9 +671,9 @@ def main():
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = bytes_per_layer / (kernel_avg_ms * 1e-3) / 1e9
     # HBM bytes per launch from the committed counters of this workload's
-    # plain bf16 decode (none for E4M3 pools or cascade plans)
-    traffic = (traffic_per_launch(DECODE_COUNTERS.get(spec.name))
-               if not fp8 and not args.cascade else None)
+    # plain decode, bf16 or E4M3 (none for cascade plans)
+    traffic = (traffic_per_launch(DECODE_COUNTERS.get(spec.name + ("_fp8kv" if fp8 else "")))
+               if not args.cascade else None)
 
     G = Hq // Hkv
     result = {
