@@ -204,3 +204,21 @@ def test_prefill_fp8_workload_full_rows(spec):
     e_out, e_lse = max_err(out, ref), max_err(lse, ref_lse)
     say(f"  {out.shape[0] * out.shape[1]} rows: max|d| out={e_out:.3g} lse={e_lse:.3g}")
     assert e_out <= TOL and e_lse <= TOL
+
+
+@pytest.mark.parametrize("k_scale,v_scale", [(-0.37, -1.3), (0.0, 0.7), (0.37, 0.0)])
+def test_prefill_fp8_nonpositive_scales(k_scale, v_scale):
+    """Scales of any sign: a negative k_scale runs as |scale| on the negated
+    query, a zero k_scale gives every score 0 (the mean of the visible V
+    rows), a zero v_scale a zero output; against the oracle, with KV cuts."""
+    say(f"prefill fp8 scales k={k_scale} v={v_scale}")
+    reqs = [(300, 64), (700, 129), (40, 33)]
+    qo, ip, idx, q, k, v = _case(reqs, 32, 8, 128, 8192, 96, 0.37, 1.3)
+    scale = W.softmax_scale(128)
+    for flags in (0, pa.PA_PLAN_FORCE_SPLITS(5)):
+        out, lse = run_prefill_fp8(q, k, v, qo, ip, torch.as_tensor(idx, device=device()), scale, 8,
+                                   k_scale, v_scale, flags)
+        ref, ref_lse = _oracle(q, k, v, qo, ip, idx, scale, 8, k_scale, v_scale)
+        e = max_err(out, ref), max_err(lse, ref_lse)
+        say(f"  flags {flags:#x}: max|d| out {e[0]:.3g} lse {e[1]:.3g}")
+        assert e[0] <= TOL and e[1] <= TOL
