@@ -234,3 +234,21 @@ def test_decode_fp8_padded_slot_stride(pad, ok):
     assert np.array_equal(out, base) and np.array_equal(lse, base_lse)
     ref, ref_lse = _oracle(q, k, v, ip, idx, scale, Hkv)
     assert max_err(out, ref) <= TOL and max_err(lse, ref_lse) <= TOL
+
+
+@pytest.mark.parametrize("k_scale,v_scale", [(-0.37, -1.3), (0.0, 0.7), (0.37, 0.0)])
+def test_decode_fp8_nonpositive_scales(k_scale, v_scale):
+    """Scales of any sign through the fp8 decode (the scores carry
+    sm_scale * k_scale, the output v_scale), with the automatic split and
+    with forced parts: against the oracle."""
+    say(f"fp8 decode scales k={k_scale} v={v_scale}")
+    Hq, Hkv, D = 32, 8, 128
+    ip, idx, q, k, v = _case([1, 7, 64, 300, 1025, 0], Hq, Hkv, D, 8192, seed=97)
+    idx_dev = torch.as_tensor(idx, device=q.device)
+    scale = W.softmax_scale(D)
+    ref, ref_lse = _oracle(q, k, v, ip, idx, scale, Hkv, k_scale=k_scale, v_scale=v_scale)
+    for flags in (0, pa.PA_PLAN_FORCE_SPLITS(7)):
+        out, lse = run_fp8(q, k, v, ip, idx_dev, scale, Hkv, flags=flags, k_scale=k_scale, v_scale=v_scale)
+        e = max_err(out, ref), max_err(lse, ref_lse)
+        say(f"  flags {flags:#x}: max|d| out {e[0]:.3g} lse {e[1]:.3g}")
+        assert e[0] <= TOL and e[1] <= TOL
