@@ -185,7 +185,19 @@ def test_fp8_large_pool_offsets(Hq, Hkv, D):
 @pytest.mark.parametrize("k_scale,v_scale", [(KS, VS), (0.37, 1.3)], ids=["pow2_scales", "general_scales"])
 def test_fp8_batch64_workload_full_rows(k_scale, v_scale):
     """The batch-64 shared-prefix workload over 8-bit pools, every row."""
-    spec = W.BATCH64_SHARED_PREFIX
+    _full_rows(W.BATCH64_SHARED_PREFIX, k_scale, v_scale)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("spec", [W.HEADDIM256_BATCH32, W.QWEN3_4B_BATCH8, W.SINGLE_REQUEST_256],
+                         ids=lambda s: s.name)
+def test_fp8_other_workloads_full_rows(spec):
+    """The head_dim-256, batch-8 and single-request workloads over 8-bit
+    pools (as bench.py --kv fp8 runs them), every row."""
+    _full_rows(spec, KS, VS)
+
+
+def _full_rows(spec, k_scale, v_scale):
     say(f"fp8 workload {spec.name}, scales {k_scale}/{v_scale}: all rows")
     dev = device()
     ip, idx = W.decode_lists(spec)
