@@ -222,7 +222,9 @@ pa_status decode_bins(const PartitionArgs &a, PartitionScratch &ws, int32_t *wg_
     auto advance = [&]() {
         p++;
         ws.bin_stream[p] = (int32_t)ws.stream.size();
-        fill = (p < n_seg) ? open_len(p) + ov : 0.0;
+        // bins 0 .. n-1 exist (p reaches n only to close bin_stream), and
+        // only segments below n have an opening piece
+        fill = (p < n && p < n_seg) ? open_len(p) + ov : 0.0;
         if (p < n)
             cap = cap_of(p);
     };
