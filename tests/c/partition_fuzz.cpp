@@ -6,12 +6,16 @@
 // group arrays; and output arrays sized exactly to the counts a first call
 // reports (so any write past them is caught), or one entry short (which must
 // give PA_ERR_CAPACITY).  Every decode partition is checked to cover each
-// (request, KV head) list exactly once.  Test infrastructure, host only: the
-// GPU launchers are stubs that report "not supported".  Exit 0 when every
-// case holds; a failing case is named on stderr.
+// (request, KV head) list exactly once.  With a second argument N the cases
+// run on N threads at once (each with its own random sequence), for a build
+// with ThreadSanitizer.  Test infrastructure, host only: the GPU launchers are
+// stubs that report "not supported".  Exit 0 when every case holds; a failing
+// case is named on stderr.
+#include <atomic>
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
+#include <thread>
 #include <vector>
 
 #include "pa.h"
@@ -30,7 +34,7 @@ int decode_workgroups_per_cu(int32_t, int32_t, bool) { return 3; }
 
 namespace {
 
-uint64_t rng_state = 0x9E3779B97F4A7C15ull;
+thread_local uint64_t rng_state = 0x9E3779B97F4A7C15ull;
 uint32_t next_u32() {   // xorshift64*
     rng_state ^= rng_state >> 12;
     rng_state ^= rng_state << 25;
@@ -39,7 +43,7 @@ uint32_t next_u32() {   // xorshift64*
 }
 int32_t uniform(int32_t lo, int32_t hi) { return lo + (int32_t)(next_u32() % (uint32_t)(hi - lo + 1)); }
 
-int failures = 0;
+std::atomic<int> failures{0};
 #define EXPECT(cond, ...)                                   \
     do {                                                    \
         if (!(cond)) {                                      \
@@ -241,10 +245,8 @@ void bad_offsets_case(int case_id) {
     EXPECT(st == PA_ERR_INVALID_ARG, "offsets not starting at 0: status %d", (int)st);
 }
 
-}  // namespace
-
-int main(int argc, char **argv) {
-    const int cases = argc > 1 ? std::atoi(argv[1]) : 1500;
+void run_cases(int cases, uint64_t seed) {
+    rng_state ^= seed * 0xD1B54A32D192ED03ull;
     for (int c = 0; c < cases; c++) {
         switch (c % 3) {
         case 0: decode_case(c); break;
@@ -253,6 +255,23 @@ int main(int argc, char **argv) {
         }
     }
     bad_offsets_case(cases);
-    std::printf("partition_fuzz: %d cases, %d failures\n", cases + 1, failures);
+}
+
+}  // namespace
+
+int main(int argc, char **argv) {
+    const int cases = argc > 1 ? std::atoi(argv[1]) : 1500;
+    const int threads = argc > 2 ? std::atoi(argv[2]) : 0;
+    if (threads <= 0) {
+        run_cases(cases, 0);
+    } else {
+        std::vector<std::thread> pool;
+        for (int t = 0; t < threads; t++)
+            pool.emplace_back(run_cases, cases, (uint64_t)t + 1);
+        for (auto &th : pool)
+            th.join();
+    }
+    std::printf("partition_fuzz: %d cases, %d failures\n", (cases + 1) * (threads > 0 ? threads : 1),
+                failures.load());
     return failures == 0 ? 0 : 1;
 }
