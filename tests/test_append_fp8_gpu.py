@@ -40,22 +40,24 @@ def _code_pools(N, Hkv, D, seed, dev):
     return k, v
 
 
-def _near_tie(x: np.ndarray, ref: oracle.Oracle) -> np.ndarray:
-    """Where |x| lies within 1e-12 (relative) of a midpoint between two
-    neighbouring finite codes."""
+def _near_tie(x: np.ndarray, ref: oracle.Oracle, abs_window: float = 0.0) -> np.ndarray:
+    """Where |x| lies within 1e-12 (relative), or abs_window, of a midpoint
+    between two neighbouring finite codes."""
     fin = ref.e4m3_values(np.arange(0x7F, dtype=np.uint8))
     mids = (fin[:-1] + fin[1:]) / 2
     a = np.abs(x).ravel()
     j = np.clip(np.searchsorted(mids, a), 1, mids.size - 1)
     d = np.minimum(np.abs(a - mids[j - 1]), np.abs(a - mids[j]))
-    return (d <= 1e-12 * np.maximum(a, 2.0 ** -10)).reshape(x.shape)
+    return (d <= np.maximum(1e-12 * np.maximum(a, 2.0 ** -10), abs_window)).reshape(x.shape)
 
 
-def _check_k_codes(got, want, quotient, ref, what="K"):
-    """Codes equal, or neighbours where the quotient is a near tie."""
+def _check_k_codes(got, want, quotient, ref, what="K", abs_window=0.0):
+    """Codes equal, or neighbours where the quotient is a near tie (within
+    abs_window too: the two sides' rotations differ by about the angle's
+    rounding, pos * 2^-52 radians, times the pair's size)."""
     diff = got != want
     if diff.any():
-        tie = _near_tie(quotient, ref)
+        tie = _near_tie(quotient, ref, abs_window)
         step = np.abs(got.astype(np.int32) - want.astype(np.int32))
         ok = tie & (step == 1) & ((got & 0x80) == (want & 0x80))
         assert np.all(ok[diff]), (f"{what} codes differ away from ties: {np.count_nonzero(diff & ~ok)} "
